@@ -1,0 +1,336 @@
+#!/usr/bin/env python3
+"""all_reduce bandwidth of R logical ranks on one MI355X.
+
+One step is one pass of the measured workload: 8 logical ranks, 16,777,216
+float32 elements (64 MiB) per rank, out of place, all_reduce Sum then
+all_reduce Mean (two launches of the direct R-way kernel).  Inputs are seeded
+synthetic N(0,1) buffers resident in HBM before the timed region.
+
+Printed: one JSON line with the metric (algbw = N * 4 bytes / time per
+all_reduce, in GB/s), the roofline of the dominant kernel (algorithmic HBM
+bytes 2*R*N*4 per launch over its average duration, measured with HIP events
+on the launch stream), the CPU oracle timed on the host cores, and per-row
+context for the other collectives.
+
+    python bench.py [--steps K] [--warmup W] [--no-rows] [--no-cpu-baseline]
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+if str(ROOT) not in sys.path:
+    sys.path.insert(0, str(ROOT))
+
+METRIC = "all_reduce algbw GB/s, fp32, R=8 ranks, 64 MiB/rank; % of HBM peak"
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+KERNEL_SOURCE = ROOT / "rank_reductions_amd" / "csrc" / "kernels.hip"
+TRAFFIC_FILE = ROOT / "profiles" / "traffic_fold_r8_f32_sum_64MiB.txt"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--algo", default="auto", choices=["auto", "direct", "ring"])
+    p.add_argument("--tile-elems", type=int, default=0)
+    p.add_argument("--max-workgroups", type=int, default=0)
+    p.add_argument("--cache-hint", default="auto", choices=["auto", "streaming", "normal"])
+    p.add_argument("--no-rows", action="store_true", help="skip the other collectives")
+    p.add_argument("--full-batched", action="store_true",
+                   help="time the batched all-reduce on the full 32-layer gradient list (211 GB)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+class Timer:
+    """HIP events on torch's current stream, which is the stream every call
+    below is launched on."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def start(self):
+        self.a.record()
+
+    def stop_ms(self):
+        self.b.record()
+        self.b.synchronize()
+        return self.a.elapsed_time(self.b)
+
+
+def time_calls(torch, fn, iters, warmup=2):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t = Timer(torch)
+    t.start()
+    for _ in range(iters):
+        fn()
+    return t.stop_ms() / iters
+
+
+def kernels_sha():
+    return hashlib.sha256(KERNEL_SOURCE.read_bytes()).hexdigest()
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    if not TRAFFIC_FILE.exists():
+        return None
+    vals = {}
+    for line in TRAFFIC_FILE.read_text().splitlines():
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernels_sha256") != kernels_sha():
+        return None
+    try:
+        return int(float(vals["fetch_bytes_per_launch"]) + float(vals["write_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the logical ranks all live in one GPU's HBM, and "
+              f"this build has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import rank_reductions_amd as rr
+    import synth_inputs as si
+
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    lib = rr.library()
+    props = torch.cuda.get_device_properties(0)
+    log(f"bench: device {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
+
+    w = si.WORKLOADS["ranks8_64MiB_f32"]
+    R, N = w["R"], w["N"]
+    log(f"bench: generating inputs R={R} N={N}")
+    xs = si.torch_rank_inputs(R, N, "f32", w["dist"], w["seed"], device=dev)
+    out_sum = [torch.empty_like(x) for x in xs]
+    out_mean = [torch.empty_like(x) for x in xs]
+    rr.register(R, device=0, algo=args.algo, tile_elems=args.tile_elems,
+                max_workgroups=args.max_workgroups, cache_hint=args.cache_hint)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    b_sum = rr.make_bufs([x.data_ptr() for x in xs], [o.data_ptr() for o in out_sum], (N,), rr.RC_F32, rr.RC_SUM)
+    b_mean = rr.make_bufs([x.data_ptr() for x in xs], [o.data_ptr() for o in out_mean], (N,), rr.RC_F32, rr.RC_MEAN)
+    p_sum = ctypes.cast(b_sum, ctypes.c_void_p)
+    p_mean = ctypes.cast(b_mean, ctypes.c_void_p)
+    all_reduce = lib.rc_all_reduce
+
+    def step():
+        if all_reduce(p_sum, stream) or all_reduce(p_mean, stream):
+            raise rr.CollectiveError(1, lib.rc_last_error().decode())
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"bench: timing {args.steps} steps")
+    t = Timer(torch)
+    wall0 = time.perf_counter()
+    t.start()
+    for _ in range(args.steps):
+        step()
+    ms = t.stop_ms()
+    wall = time.perf_counter() - wall0
+    launches_per_call = 2 if args.algo == "ring" else 1
+    ms_per_step = ms / args.steps
+    calls_per_step = 2
+    per_call_s = ms_per_step / calls_per_step / 1e3
+    algbw = N * 4 / per_call_s / 1e9
+    hbm_bytes = 2 * R * N * 4  # read R*N, write R*N elements per all_reduce
+    launch_ms = ms / (args.steps * calls_per_step * launches_per_call)
+    achieved = (hbm_bytes / launches_per_call) / (launch_ms / 1e3) / 1e9
+    same = all(torch.equal(out_sum[0], o) for o in out_sum) and all(torch.equal(out_mean[0], o) for o in out_mean)
+    log(f"bench: {ms_per_step:.4f} ms/step, algbw {algbw:.1f} GB/s, HBM {achieved:.1f} GB/s, "
+        f"{100 * achieved / HBM_PEAK_GBPS:.1f}% of peak; ranks identical: {same}; wall {wall:.3f}s")
+
+    # plain device copy of the same bytes: the practical ceiling, for context
+    src = torch.empty(R * N, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    copy_ms = time_calls(torch, lambda: dst.copy_(src), 20)
+    copy_gbps = 2 * src.numel() * 4 / (copy_ms / 1e3) / 1e9
+    del src, dst
+    log(f"bench: device copy of {R * N * 4 >> 20} MiB: {copy_ms * 1e3:.1f} us, {copy_gbps:.1f} GB/s")
+
+    result = {
+        "metric": METRIC,
+        "value": round(algbw, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "ranks8_64MiB_f32: 8 logical ranks x 16,777,216 fp32 (64 MiB) per rank, "
+                        "N(0,1) seed 1, out of place; step = all_reduce Sum + all_reduce Mean",
+            "ranks": R,
+            "elems_per_rank": N,
+            "algo": args.algo,
+            "tile_elems": args.tile_elems,
+            "max_workgroups": args.max_workgroups,
+            "cache_hint": args.cache_hint,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": read_traffic() if args.algo != "ring" else None,
+            "kernel": "fold_kernel<8, OpSumF32, 2, true>" if args.algo != "ring" else "ring phases",
+            "algorithmic_bytes_per_launch": hbm_bytes // launches_per_call,
+            "avg_launch_us": round(launch_ms * 1e3, 2),
+        },
+        "hbm_frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "ranks_bit_identical": bool(same),
+        "copy_ceiling": {"bytes": 2 * R * N * 4, "us": round(copy_ms * 1e3, 2), "GBps": round(copy_gbps, 1)},
+    }
+
+    if not args.no_rows:
+        rr.finish()
+        result["rows"] = rows(torch, rr, si, dev, xs, args)
+        rr.register(R, device=0)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(torch, xs, out_sum, args.cpu_seconds)
+
+    rr.finish()
+    print(json.dumps(result), flush=True)
+
+
+def _roof(bytes_moved, us):
+    gbps = bytes_moved / (us * 1e-6) / 1e9
+    return {"us": round(us, 2), "hbm_GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
+def rows(torch, rr, si, dev, xs8, args):
+    """Every other collective at its workload's size (context, not the metric)."""
+    out = {}
+    R, N = len(xs8), xs8[0].numel()
+    b = N * 4
+    # ring all-reduce on the metric workload
+    rr.register(R, device=0, algo="ring")
+    o = [torch.empty_like(x) for x in xs8]
+    us = time_calls(torch, lambda: rr.all_reduce(xs8, "sum", out=o), 10) * 1e3
+    out["all_reduce_ring_r8_64MiB_f32_sum"] = _roof(2 * R * b, us)
+    rr.finish()
+    del o
+    rr.register(R, device=0)
+    # reduce_scatter and all_gather, 8 ranks x 256 MiB
+    w = si.WORKLOADS["ranks8_256MiB_f32_rs_ag"]
+    log("bench: rows: reduce_scatter / all_gather 8 x 256 MiB")
+    big = si.torch_rank_inputs(w["R"], w["N"], "f32", w["dist"], w["seed"], device=dev)
+    M = w["N"] // w["R"]
+    shards = [torch.empty(M, dtype=torch.float32, device=dev) for _ in range(w["R"])]
+    gathered = [torch.empty(w["N"], dtype=torch.float32, device=dev) for _ in range(w["R"])]
+    us = time_calls(torch, lambda: rr.reduce_scatter(big, "sum", out=shards), 10) * 1e3
+    out["reduce_scatter_r8_256MiB_f32_sum"] = _roof((w["R"] + 1) * w["N"] * 4, us)
+    us = time_calls(torch, lambda: rr.all_gather(shards, out=gathered), 10) * 1e3
+    out["all_gather_r8_32MiB_shards_f32"] = _roof((w["R"] + 1) * w["N"] * 4, us)
+    rr.finish()
+    del big, shards, gathered
+    torch.cuda.empty_cache()
+    # int32 workload, 4 ranks x 64 MiB
+    w = si.WORKLOADS["ranks4_64MiB_i32"]
+    log("bench: rows: int32 4 x 64 MiB")
+    xi = si.torch_rank_inputs(w["R"], w["N"], "i32", "int", w["seed"], device=dev)
+    R4, N4 = w["R"], w["N"]
+    rr.register(R4, device=0)
+    oi = [torch.empty_like(x) for x in xi]
+    us = time_calls(torch, lambda: rr.all_reduce(xi, "sum", out=oi), 10) * 1e3
+    out["all_reduce_r4_64MiB_i32_sum"] = _roof(2 * R4 * N4 * 4, us)
+    us = time_calls(torch, lambda: rr.all_reduce(xi, "max", out=oi), 10) * 1e3
+    out["all_reduce_r4_64MiB_i32_max"] = _roof(2 * R4 * N4 * 4, us)
+    ro = [oi[r] if r == 2 else None for r in range(R4)]
+    us = time_calls(torch, lambda: rr.reduce(xi, 2, "sum", out=ro), 10) * 1e3
+    out["reduce_r4_64MiB_i32_root2"] = _roof((R4 + 1) * N4 * 4, us)
+    sends = [xi[3] if r == 3 else None for r in range(R4)]
+    bo = [oi[r] if r != 3 else None for r in range(R4)]
+    us = time_calls(torch, lambda: rr.broadcast(sends, out=bo), 10) * 1e3
+    out["broadcast_r4_64MiB_i32_from3"] = _roof(R4 * N4 * 4, us)
+    rr.finish()
+    del xi, oi, ro, bo, sends
+    torch.cuda.empty_cache()
+    # batched gradient all-reduce: the transformer-shaped list
+    layers = 32 if args.full_batched else 2
+    shapes = si.transformer_grad_shapes(layers=layers)
+    log(f"bench: rows: batched Mean over {len(shapes)} tensors ({layers} layers)")
+    w = si.WORKLOADS["ranks4_llama32_grads_f32"]
+    R4 = w["R"]
+    ts = [[si.torch_tensor_for(w["seed"], t, R4, r, shp, device=dev) for r in range(R4)]
+          for t, shp in enumerate(shapes)]
+    os_ = [[torch.empty_like(x) for x in per] for per in ts]
+    elems = sum(x.numel() for x in (per[0] for per in ts))
+    rr.register(R4, device=0)
+    us = time_calls(torch, lambda: rr.all_reduce_many(ts, "mean", out=os_), 3, warmup=1) * 1e3
+    row = _roof(2 * R4 * elems * 4, us)
+    row.update({"tensors": len(shapes), "elems_per_rank": elems, "layers": layers})
+    out[f"all_reduce_many_r4_{layers}layer_grads_f32_mean"] = row
+    rr.finish()
+    del ts, os_
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(torch, xs, out_sum, seconds):
+    """The CPU oracle (ring simulation, NumPy) on the host cores of this machine,
+    on the metric workload's inputs; repeated until about `seconds` of work."""
+    import numpy as np
+
+    import oracle
+
+    hx = [x.cpu().numpy() for x in xs]
+    N = hx[0].size
+    log("bench: timing the CPU oracle")
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        res = oracle.all_reduce(hx, "sum")
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    gpu = out_sum[0].cpu().numpy()
+    match = bool(np.array_equal(res[0].view(np.uint32), gpu.view(np.uint32)))
+    return {
+        "value": round(calls * N * 4 / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{calls} full all_reduce Sum calls of the ring-simulation oracle on the same "
+                  f"8 x 16,777,216 fp32 inputs (host copy), {el:.1f} s; NumPy elementwise, one thread",
+        "seconds": round(el, 2),
+        "matches_gpu_bits": match,
+        "host_cpus_visible": len(os.sched_getaffinity(0)),
+    }
+
+
+if __name__ == "__main__":
+    main()

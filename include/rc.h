@@ -1,0 +1,219 @@
+/*
+ * rc.h - tensor collectives over R logical ranks whose buffers all live in the
+ * HBM of one GPU (gfx950).  C ABI; plain pointers and sizes only.
+ *
+ * The operations are the public tensor collective API of the ruCCL README
+ * (ja), user guide section 2 "Tensor collective API" (register, all_reduce,
+ * reduce, broadcast, finish_collective, reset_collective), with the call
+ * contract of section 3 and the CollectiveError cases of section 4, plus
+ * reduce_scatter_tensor and all_gather_into_tensor from the monarch
+ * `Struct Communicator` page.  Every collective takes a stream, as the
+ * Communicator methods do, and returns a status code.
+ *
+ * One call carries all R ranks' arguments (one rc_buf per logical rank), so
+ * the contract that every rank issues matching collectives in the same order
+ * (ruCCL README section 3; Communicator's Send/Sync safety note) holds by
+ * construction, and mismatches between ranks are detected inside one call.
+ *
+ * Numerics.  Each collective reduces along the ring: for element counts N over
+ * R ranks, the segment length is S = ceil(N/R) and segment c = [c*S,
+ * min((c+1)*S, N)) is folded left in rank order (c+1), (c+2), ..., c (mod R),
+ * the order a ring reduce-scatter leaves at segment c's owner (ruCCL README,
+ * "CUDA tensor example": a ring AllReduce over logical ranks on one GPU).
+ * float32 adds are IEEE round-to-nearest-even with subnormals kept; Mean is
+ * one correctly rounded float32 division of the finished fold by R; int32 Sum
+ * wraps; float32 Max returns the quiet NaN 0x7FC00000 if any operand is NaN
+ * and otherwise the larger value, +0 above -0.  The result therefore does not
+ * depend on the algorithm, tile size or grid, and every rank's output is
+ * bit-identical.
+ *
+ * Errors.  Every argument is checked before anything is enqueued.  On an
+ * error no buffer is touched, nothing is launched, the session stays as it
+ * was, and rc_last_error() describes the failure.  Checks run in this order:
+ *   NOT_REGISTERED; INVALID_ARGUMENT for malformed fields (enum values, ndim,
+ *   negative dims, NULL or misaligned pointers that the op requires);
+ *   DTYPE_MISMATCH; SHAPE_MISMATCH; OP_MISMATCH; INVALID_ARGUMENT for an op the
+ *   dtype lacks (int32 Mean); ROOT_MISMATCH and INVALID_ARGUMENT for a root
+ *   out of range; BROADCAST_SENDERS; INVALID_ARGUMENT for overlapping buffers.
+ *
+ * Threads.  The library keeps one process-wide session behind a mutex; calls
+ * from several threads are serialised.  The caller orders calls on its
+ * streams (the Communicator page leaves issue order to the user).
+ */
+#ifndef RANKRED_RC_H
+#define RANKRED_RC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RC_ABI_VERSION 1
+#define RC_MAX_RANKS 16
+#define RC_MAX_DIMS 8
+
+/* Element types: the backend's float and int types are f32 and i32 (RUDA
+ * "Training and state saving", "Configure training backend"). */
+enum { RC_F32 = 0, RC_I32 = 1 };
+
+/* Reduction operators: Sum and Mean (ruCCL README, "CUDA tensor example" and
+ * section 6, ReduceOperation::Mean); Max (the ReduceOp of the Communicator's
+ * all_reduce).  Mean is float32 only. */
+enum { RC_SUM = 0, RC_MEAN = 1, RC_MAX = 2 };
+
+/* Algorithm for all_reduce: DIRECT reads all R inputs once per element and
+ * writes all R outputs; RING runs a reduce-scatter kernel, then an all-gather
+ * kernel.  Both give the same bits.  AUTO picks DIRECT. */
+enum { RC_ALGO_AUTO = 0, RC_ALGO_DIRECT = 1, RC_ALGO_RING = 2 };
+
+/* Store cache hint for outputs (and load hint for inputs). */
+enum { RC_CACHE_AUTO = 0, RC_CACHE_STREAMING = 1, RC_CACHE_NORMAL = 2 };
+
+/* Status codes.  Codes 1-6 are the CollectiveError cases of the ruCCL README,
+ * section 4 "Errors and lifecycle" (duplicate or missing registration, shape
+ * mismatch, inconsistent reduction op or root, invalid broadcast sender
+ * count); 7-9 are this library's plumbing. */
+typedef enum {
+    RC_OK = 0,
+    RC_ERR_NOT_REGISTERED = 1,
+    RC_ERR_DUPLICATE_REGISTRATION = 2,
+    RC_ERR_SHAPE_MISMATCH = 3,
+    RC_ERR_OP_MISMATCH = 4,
+    RC_ERR_ROOT_MISMATCH = 5,
+    RC_ERR_BROADCAST_SENDERS = 6,
+    RC_ERR_DTYPE_MISMATCH = 7,
+    RC_ERR_INVALID_ARGUMENT = 8,
+    RC_ERR_DEVICE = 9
+} rc_status;
+
+/* One logical rank's side of a collective (cf. the TensorCell argument of the
+ * Communicator methods).  Buffers are dense, contiguous, in device memory of
+ * the registered GPU, and aligned to the element size.  The element count is
+ * the product of dims[0..ndim) (ndim 0 means a scalar, count 1); a count of 0
+ * is a no-op that returns RC_OK once the fields check out.  Buffers of zero
+ * elements may be NULL, except that broadcast still finds its sender as the
+ * one non-NULL send.
+ *   send  input, read only (never written unless recv == send);
+ *   recv  output;
+ *   dtype RC_F32 or RC_I32, equal on all ranks;
+ *   op    RC_SUM / RC_MEAN / RC_MAX, equal on all ranks (reducing ops only;
+ *         ignored by broadcast and all_gather);
+ *   root  reduce: the receiving rank, equal on all ranks.  broadcast: -1 on
+ *         all ranks, or the sender's index on all ranks.  Ignored otherwise.
+ *   dims  shape, equal on all ranks; reduce_scatter: the input's shape (count
+ *         divisible by R; recv holds count/R elements); all_gather: the
+ *         shard's shape (recv holds R*count elements). */
+typedef struct rc_buf {
+    const void* send;
+    void* recv;
+    int32_t dtype;
+    int32_t op;
+    int32_t root;
+    int32_t ndim;
+    int64_t dims[RC_MAX_DIMS];
+} rc_buf;
+
+/* Session configuration (cf. CollectiveConfig::default() and
+ * with_num_devices, ruCCL README section 3; the "strategy" set through the
+ * config maps to algo).  Zero-initialise, set struct_size = sizeof(rc_config),
+ * then set what you need; 0 selects the default of every field but device.
+ *   device         GPU index, or -1 for the device current at rc_register
+ *                  (cfg == NULL also means the current device)
+ *   algo           RC_ALGO_*
+ *   validate_only  nonzero: check arguments and return, never touch the GPU
+ *                  (rc_register then makes no HIP call at all)
+ *   tile_elems     elements per workgroup tile; 0: default; else a multiple
+ *                  of 1024 in [1024, 65536]
+ *   max_workgroups cap on the grid; 0: default (from the CU count)
+ *   cache_hint     RC_CACHE_* */
+typedef struct rc_config {
+    uint32_t struct_size;
+    int32_t device;
+    int32_t algo;
+    int32_t validate_only;
+    int64_t tile_elems;
+    int32_t max_workgroups;
+    int32_t cache_hint;
+} rc_config;
+
+/* register<B> (ruCCL README, section 2; section 3 for the config): open the
+ * process-wide session for num_ranks logical ranks (1..RC_MAX_RANKS) on one
+ * GPU.  cfg may be NULL for defaults; cfg->struct_size must equal
+ * sizeof(rc_config).  Fails with RC_ERR_DUPLICATE_REGISTRATION while a session
+ * is open, RC_ERR_INVALID_ARGUMENT for bad values, RC_ERR_DEVICE if the GPU is
+ * not a gfx950 or cannot be queried.  Allocates nothing on the device. */
+int rc_register(int num_ranks, const rc_config* cfg);
+
+/* all_reduce<B> (ruCCL README section 2: the reduced result is returned to
+ * every participant; Communicator.all_reduce).  bufs[r] for r < num_ranks;
+ * every send and recv non-NULL; recv == send (in place) is allowed.  Every
+ * rank's recv receives the same bits.  Enqueued on `stream` (a hipStream_t;
+ * NULL is the null stream); returns once enqueued. */
+int rc_all_reduce(const rc_buf* bufs, void* stream);
+
+/* reduce<B> (ruCCL README section 2: reduce to the given root; non-root
+ * participants receive nothing; Communicator.reduce).  Every send non-NULL;
+ * the root's recv non-NULL (may equal its send); other ranks' recv may be
+ * NULL and is never written.  The root receives the bits all_reduce gives. */
+int rc_reduce(const rc_buf* bufs, void* stream);
+
+/* broadcast<B> (ruCCL README section 2: the sender passes Some(tensor), the
+ * receivers pass None; section 3: exactly one sender; Communicator.broadcast).
+ * The sender is the one rank with send != NULL; all other sends must be NULL,
+ * else RC_ERR_BROADCAST_SENDERS.  Every receiver's recv must be non-NULL and
+ * receives the sender's bytes; the sender's recv, if non-NULL and not equal to
+ * its send, receives them too. */
+int rc_broadcast(const rc_buf* bufs, void* stream);
+
+/* reduce_scatter_tensor (Communicator page: reduce, then scatter the result).
+ * Each send holds count = R*M elements (dims describe it); rank r's recv
+ * receives the M elements [r*M, (r+1)*M) of the reduction.  In place is
+ * allowed as recv_r == send_r + r*M elements. */
+int rc_reduce_scatter(const rc_buf* bufs, void* stream);
+
+/* all_gather_into_tensor (Communicator page: gather every rank's tensor into
+ * one output).  Each send is a shard of count = M elements; every recv holds
+ * R*M elements and receives shard_0, ..., shard_{R-1} in rank order, bit for
+ * bit.  In place is allowed as send_r == recv_r + r*M elements. */
+int rc_all_gather(const rc_buf* bufs, void* stream);
+
+/* Whole-gradient all-reduce (ruCCL README section 6, "Collective training":
+ * grads.all_reduce_with(communicator, ReduceOperation::Mean) reduces every
+ * gradient of a parameter set, with IDs, shapes, dtype and call order
+ * matching across ranks).  bufs is [num_tensors][num_ranks], row-major: tensor
+ * t's rank r is bufs[t * num_ranks + r].  Every tensor obeys the all_reduce
+ * rules and is reduced with its own segments, so the bits equal num_tensors
+ * separate rc_all_reduce calls.  Tensors are batched into few launches; the
+ * session keeps a descriptor arena for this (allocated on first use, freed by
+ * rc_finish / rc_reset). */
+int rc_all_reduce_many(int num_tensors, const rc_buf* bufs, void* stream);
+
+/* finish_collective<B> (ruCCL README sections 2 and 4: the normal end of the
+ * peer's collective session).  Waits for all work on the session's GPU,
+ * frees the session's scratch and closes the session.
+ * RC_ERR_NOT_REGISTERED if no session is open. */
+int rc_finish(void);
+
+/* reset_collective<B> (ruCCL README sections 2 and 4): discard the
+ * registration and any state of calls in progress, from any state.  It does
+ * not complete, revoke or checkpoint work already enqueued; it waits only for
+ * the kernels that read the session's scratch before freeing it.  Always
+ * returns RC_OK. */
+int rc_reset(void);
+
+/* Text for the last failure on the calling thread (valid until that thread's
+ * next rc_* call); "" after success. */
+const char* rc_last_error(void);
+
+/* Name of a status code ("RC_OK", "RC_ERR_SHAPE_MISMATCH", ...). */
+const char* rc_status_name(int status);
+
+/* RC_ABI_VERSION of the loaded library. */
+int rc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RANKRED_RC_H */

@@ -1,0 +1,352 @@
+"""Python binding of librankred.so: collectives over R logical ranks on one GPU.
+
+Argument marshalling only.  Every collective runs in the library's HIP
+kernels; PyTorch supplies device memory and streams.  The functions mirror the
+public tensor collective API of the ruCCL README (ja), user guide section 2
+(register, all_reduce, reduce, broadcast, finish_collective, reset_collective),
+plus reduce_scatter_tensor and all_gather_into_tensor of the monarch
+Communicator page, and a whole-gradient all_reduce_many (section 6,
+"Collective training").
+
+    import rank_reductions_amd as rr
+    rr.register(4)
+    outs = rr.all_reduce(xs, op="sum")     # xs: 4 CUDA tensors, same shape
+    rr.finish()
+
+Errors from the library raise CollectiveError with the status code and text.
+If librankred.so is not built the module still imports, but every call raises
+(there is no fallback path).
+"""
+
+import ctypes
+from pathlib import Path
+
+import numpy as np
+
+__all__ = [
+    "CollectiveError", "register", "all_reduce", "reduce", "broadcast", "reduce_scatter",
+    "all_gather", "all_reduce_many", "finish", "reset", "library", "library_path",
+    "RC_OK", "RC_ERR_NOT_REGISTERED", "RC_ERR_DUPLICATE_REGISTRATION", "RC_ERR_SHAPE_MISMATCH",
+    "RC_ERR_OP_MISMATCH", "RC_ERR_ROOT_MISMATCH", "RC_ERR_BROADCAST_SENDERS",
+    "RC_ERR_DTYPE_MISMATCH", "RC_ERR_INVALID_ARGUMENT", "RC_ERR_DEVICE",
+]
+
+RC_MAX_RANKS = 16
+RC_MAX_DIMS = 8
+
+RC_F32, RC_I32 = 0, 1
+RC_SUM, RC_MEAN, RC_MAX = 0, 1, 2
+RC_ALGO_AUTO, RC_ALGO_DIRECT, RC_ALGO_RING = 0, 1, 2
+RC_CACHE_AUTO, RC_CACHE_STREAMING, RC_CACHE_NORMAL = 0, 1, 2
+
+RC_OK = 0
+RC_ERR_NOT_REGISTERED = 1
+RC_ERR_DUPLICATE_REGISTRATION = 2
+RC_ERR_SHAPE_MISMATCH = 3
+RC_ERR_OP_MISMATCH = 4
+RC_ERR_ROOT_MISMATCH = 5
+RC_ERR_BROADCAST_SENDERS = 6
+RC_ERR_DTYPE_MISMATCH = 7
+RC_ERR_INVALID_ARGUMENT = 8
+RC_ERR_DEVICE = 9
+
+OPS = {"sum": RC_SUM, "mean": RC_MEAN, "max": RC_MAX}
+ALGOS = {"auto": RC_ALGO_AUTO, "direct": RC_ALGO_DIRECT, "ring": RC_ALGO_RING}
+CACHE_HINTS = {"auto": RC_CACHE_AUTO, "streaming": RC_CACHE_STREAMING, "normal": RC_CACHE_NORMAL}
+
+
+class RcBuf(ctypes.Structure):
+    _fields_ = [
+        ("send", ctypes.c_void_p),
+        ("recv", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32),
+        ("op", ctypes.c_int32),
+        ("root", ctypes.c_int32),
+        ("ndim", ctypes.c_int32),
+        ("dims", ctypes.c_int64 * RC_MAX_DIMS),
+    ]
+
+
+class RcConfig(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("device", ctypes.c_int32),
+        ("algo", ctypes.c_int32),
+        ("validate_only", ctypes.c_int32),
+        ("tile_elems", ctypes.c_int64),
+        ("max_workgroups", ctypes.c_int32),
+        ("cache_hint", ctypes.c_int32),
+    ]
+
+
+# numpy view of rc_buf, for building large batches quickly
+RCBUF_NP = np.dtype([("send", "<u8"), ("recv", "<u8"), ("dtype", "<i4"), ("op", "<i4"),
+                     ("root", "<i4"), ("ndim", "<i4"), ("dims", "<i8", (RC_MAX_DIMS,))])
+assert RCBUF_NP.itemsize == ctypes.sizeof(RcBuf)
+
+
+class CollectiveError(RuntimeError):
+    """A status other than RC_OK from librankred (the CollectiveError cases of
+    the ruCCL README, section 4, plus invalid-argument and device errors)."""
+
+    def __init__(self, code, message):
+        self.code = code
+        self.name = _status_name(code)
+        super().__init__(f"{self.name}: {message}")
+
+
+def library_path():
+    return Path(__file__).resolve().with_name("librankred.so")
+
+
+_lib = None
+
+
+def library():
+    """The loaded librankred.so (ctypes), loading it on first use."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not path.exists():
+        raise RuntimeError(f"{path} is not built: run `python -m rank_reductions_amd.build` "
+                           "(no fallback implementation exists)")
+    lib = ctypes.CDLL(str(path))
+    for name in ("rc_all_reduce", "rc_reduce", "rc_broadcast", "rc_reduce_scatter", "rc_all_gather"):
+        fn = getattr(lib, name)
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        fn.restype = ctypes.c_int
+    lib.rc_register.argtypes = [ctypes.c_int, ctypes.POINTER(RcConfig)]
+    lib.rc_register.restype = ctypes.c_int
+    lib.rc_all_reduce_many.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.rc_all_reduce_many.restype = ctypes.c_int
+    for name in ("rc_finish", "rc_reset", "rc_abi_version"):
+        getattr(lib, name).argtypes = []
+        getattr(lib, name).restype = ctypes.c_int
+    lib.rc_last_error.argtypes = []
+    lib.rc_last_error.restype = ctypes.c_char_p
+    lib.rc_status_name.argtypes = [ctypes.c_int]
+    lib.rc_status_name.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _status_name(code):
+    try:
+        return library().rc_status_name(code).decode()
+    except Exception:  # noqa: BLE001 - naming only
+        return f"status {code}"
+
+
+def check(code):
+    """Raise CollectiveError for a non-RC_OK status."""
+    if code != RC_OK:
+        raise CollectiveError(code, library().rc_last_error().decode())
+    return code
+
+
+# ---------------------------------------------------------------- raw layer
+
+def make_config(device=-1, algo="auto", validate_only=False, tile_elems=0, max_workgroups=0,
+                cache_hint="auto"):
+    cfg = RcConfig()
+    cfg.struct_size = ctypes.sizeof(RcConfig)
+    cfg.device = device
+    cfg.algo = ALGOS[algo] if isinstance(algo, str) else int(algo)
+    cfg.validate_only = 1 if validate_only else 0
+    cfg.tile_elems = tile_elems
+    cfg.max_workgroups = max_workgroups
+    cfg.cache_hint = CACHE_HINTS[cache_hint] if isinstance(cache_hint, str) else int(cache_hint)
+    return cfg
+
+
+def make_bufs(sends, recvs, shape, dtype=RC_F32, op=RC_SUM, root=0):
+    """An rc_buf array from raw addresses (ints or None); shape may be one
+    tuple for all ranks or a list of per-rank tuples."""
+    n = len(sends)
+    arr = (RcBuf * n)()
+    for r in range(n):
+        shp = shape[r] if shape and isinstance(shape[0], (tuple, list)) else shape
+        b = arr[r]
+        b.send = sends[r] if sends[r] else None
+        b.recv = recvs[r] if recvs[r] else None
+        b.dtype = dtype[r] if isinstance(dtype, (list, tuple)) else dtype
+        b.op = op[r] if isinstance(op, (list, tuple)) else op
+        b.root = root[r] if isinstance(root, (list, tuple)) else root
+        b.ndim = len(shp)
+        for d, v in enumerate(shp):
+            b.dims[d] = v
+    return arr
+
+
+def register(num_ranks, device=None, algo="auto", validate_only=False, tile_elems=0,
+             max_workgroups=0, cache_hint="auto"):
+    """register<B>: open the process-wide session for num_ranks logical ranks."""
+    if device is None:
+        device = -1
+    elif not isinstance(device, int):
+        import torch
+        device = torch.device(device).index if torch.device(device).index is not None else -1
+    cfg = make_config(device, algo, validate_only, tile_elems, max_workgroups, cache_hint)
+    return check(library().rc_register(int(num_ranks), ctypes.byref(cfg)))
+
+
+def finish():
+    """finish_collective<B>: wait for the GPU, free scratch, close the session."""
+    return check(library().rc_finish())
+
+
+def reset():
+    """reset_collective<B>: drop the registration and in-flight state."""
+    return check(library().rc_reset())
+
+
+# ---------------------------------------------------------------- torch layer
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return RC_F32
+    if t.dtype == torch.int32:
+        return RC_I32
+    raise TypeError(f"unsupported dtype {t.dtype}; float32 and int32 are supported")
+
+
+# Address passed for a zero-element tensor whose storage pointer is NULL: the
+# library never dereferences it (count 0), but a broadcast sender must be
+# non-NULL to be recognised.
+_EMPTY_ADDR = 256
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on a CUDA (HIP) device")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    p = t.data_ptr()
+    return p if p or t.numel() else _EMPTY_ADDR
+
+
+def _stream(stream, ref):
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    torch = _torch()
+    return torch.cuda.current_stream(ref.device).cuda_stream
+
+
+def _op(op):
+    return OPS[op] if isinstance(op, str) else int(op)
+
+
+def _call(fn, sends, recvs, op=RC_SUM, root=0, stream=None, shapes=None):
+    """One rc_* call: per-rank dtype and shape come from each rank's send
+    tensor (or its recv tensor where send is None), so the library sees and
+    checks every rank's own description."""
+    descr = [s if s is not None else r for s, r in zip(sends, recvs)]
+    ref = next((t for t in descr if t is not None), None)
+    if ref is None:
+        raise ValueError("no tensor given")
+    if shapes is None:
+        shapes = [tuple(t.shape) if t is not None else () for t in descr]
+    dtypes = [_dtype_code(t) if t is not None else RC_F32 for t in descr]
+    bufs = make_bufs([_ptr(s) for s in sends], [_ptr(r) for r in recvs], shapes, dtypes, op, root)
+    check(fn(ctypes.cast(bufs, ctypes.c_void_p), ctypes.c_void_p(_stream(stream, ref))))
+
+
+def all_reduce(xs, op="sum", out=None, stream=None):
+    """all_reduce<B>: every rank receives the reduction of all ranks' tensors.
+    Returns the R output tensors (new ones unless `out` is given; out may be
+    `xs` itself for in place)."""
+    torch = _torch()
+    if out is None:
+        out = [torch.empty_like(x) for x in xs]
+    _call(library().rc_all_reduce, xs, out, _op(op), 0, stream)
+    return out
+
+
+def reduce(xs, root, op="sum", out=None, stream=None):
+    """reduce<B>: only `root` receives the reduction; other entries are None."""
+    torch = _torch()
+    if out is None:
+        out = [torch.empty_like(xs[root]) if r == root else None for r in range(len(xs))]
+    _call(library().rc_reduce, xs, out, _op(op), root, stream)
+    return out
+
+
+def broadcast(sends, out=None, stream=None, root=-1):
+    """broadcast<B>: exactly one entry of `sends` is a tensor (the sender),
+    the others are None; every rank receives the sender's bytes."""
+    torch = _torch()
+    senders = [s for s in sends if s is not None]
+    ref = senders[0] if senders else None
+    if ref is None:
+        raise CollectiveError(RC_ERR_BROADCAST_SENDERS, "broadcast needs one sender tensor")
+    if out is None:
+        out = [torch.empty_like(ref) if s is None else None for s in sends]
+    _call(library().rc_broadcast, sends, out, RC_SUM, root, stream)
+    return out
+
+
+def reduce_scatter(xs, op="sum", out=None, stream=None):
+    """reduce_scatter_tensor: rank r receives shard r (count/R elements) of the
+    reduction of the ranks' flat inputs."""
+    torch = _torch()
+    R = len(xs)
+    if out is None:
+        out = [torch.empty(x.numel() // R, dtype=x.dtype, device=x.device) for x in xs]
+    _call(library().rc_reduce_scatter, xs, out, _op(op), 0, stream)
+    return out
+
+
+def all_gather(shards, out=None, stream=None):
+    """all_gather_into_tensor: every rank receives the R shards concatenated
+    in rank order."""
+    torch = _torch()
+    R = len(shards)
+    if out is None:
+        out = [torch.empty(R * s.numel(), dtype=s.dtype, device=s.device) for s in shards]
+    _call(library().rc_all_gather, shards, out, RC_SUM, 0, stream)
+    return out
+
+
+def batch_bufs(tensors, outs, op):
+    """rc_buf rows [num_tensors][num_ranks] as a numpy structured array."""
+    T = len(tensors)
+    R = len(tensors[0]) if T else 0
+    arr = np.zeros(T * R, dtype=RCBUF_NP)
+    k = 0
+    for t in range(T):
+        for r in range(R):
+            x = tensors[t][r]
+            y = outs[t][r]
+            arr[k]["send"] = _ptr(x)
+            arr[k]["recv"] = _ptr(y)
+            arr[k]["dtype"] = _dtype_code(x)
+            arr[k]["op"] = op
+            arr[k]["ndim"] = x.dim()
+            arr[k]["dims"][:x.dim()] = x.shape
+            k += 1
+    return arr
+
+
+def all_reduce_many(tensors, op="mean", out=None, stream=None):
+    """Whole-gradient all-reduce: tensors[t][r] is rank r's copy of tensor t.
+    Each tensor is reduced as rc_all_reduce would, in few launches.
+    Returns out[t][r]."""
+    torch = _torch()
+    if out is None:
+        out = [[torch.empty_like(x) for x in per_rank] for per_rank in tensors]
+    if not tensors:
+        return out
+    arr = batch_bufs(tensors, out, _op(op))
+    ref = tensors[0][0]
+    check(library().rc_all_reduce_many(len(tensors), ctypes.c_void_p(arr.ctypes.data),
+                                       ctypes.c_void_p(_stream(stream, ref))))
+    return out

@@ -1,0 +1,178 @@
+// HIP side of the session: device query, launches on the caller's stream, and
+// the descriptor arena of the batched all-reduce.
+//
+// The arena holds the job and pointer tables of rc_all_reduce_many.  Tables
+// are written into pinned host staging and copied to device memory with one
+// asynchronous copy on the caller's stream, ahead of the kernel.  Two arenas
+// alternate; before one is rewritten the host waits on the event recorded
+// after the last kernel that read it.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <string>
+
+#include "rc_internal.h"
+
+namespace rc {
+
+hipError_t launch_jobs(const LaunchPlan& p, int grid, hipStream_t stream);
+hipError_t launch_batch(const BatchJob* jobs, int njobs, const void* const* ptrs, const BatchPlan& p,
+                        bool nt, int grid, hipStream_t stream);
+
+namespace {
+
+struct Arena {
+    void* host = nullptr;    // pinned staging
+    void* dev = nullptr;     // device copy read by the kernel
+    size_t cap = 0;
+    hipEvent_t done = nullptr;
+    bool pending = false;    // `done` recorded after the last kernel reading it
+};
+
+struct DeviceState {
+    int device = -1;
+    Arena arena[2];
+    int next = 0;
+} g;
+
+Error hip_fail(const char* what, hipError_t e) {
+    return Error{RC_ERR_DEVICE, std::string(what) + ": " + hipGetErrorName(e) + " (" +
+                                    hipGetErrorString(e) + ")"};
+}
+
+// Makes the session's device current for the scope of a call.
+struct DeviceGuard {
+    int prev = -1;
+    hipError_t err = hipSuccess;
+    DeviceGuard() {
+        err = hipGetDevice(&prev);
+        if (err == hipSuccess && prev != g.device) err = hipSetDevice(g.device);
+        else prev = -1;
+    }
+    ~DeviceGuard() {
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+};
+
+Error wait_arena(Arena& a) {
+    if (a.pending) {
+        hipError_t e = hipEventSynchronize(a.done);
+        if (e != hipSuccess) return hip_fail("hipEventSynchronize", e);
+        a.pending = false;
+    }
+    return {};
+}
+
+void free_arena(Arena& a) {
+    if (a.pending) (void)hipEventSynchronize(a.done);
+    if (a.host) (void)hipHostFree(a.host);
+    if (a.dev) (void)hipFree(a.dev);
+    if (a.done) (void)hipEventDestroy(a.done);
+    a = Arena{};
+}
+
+Error ensure_arena(Arena& a, size_t bytes) {
+    if (a.cap >= bytes) return {};
+    free_arena(a);
+    size_t cap = 64 << 10;
+    while (cap < bytes) cap *= 2;
+    hipError_t e = hipHostMalloc(&a.host, cap, hipHostMallocDefault);
+    if (e != hipSuccess) return hip_fail("hipHostMalloc", e);
+    e = hipMalloc(&a.dev, cap);
+    if (e != hipSuccess) {
+        free_arena(a);
+        return hip_fail("hipMalloc", e);
+    }
+    e = hipEventCreateWithFlags(&a.done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+        free_arena(a);
+        return hip_fail("hipEventCreateWithFlags", e);
+    }
+    a.cap = cap;
+    return {};
+}
+
+}  // namespace
+
+Error device_open(const Config& cfg, DeviceInfo* info) {
+    int count = 0;
+    hipError_t e = hipGetDeviceCount(&count);
+    if (e != hipSuccess) return hip_fail("hipGetDeviceCount", e);
+    if (count <= 0) return Error{RC_ERR_DEVICE, "no GPU visible"};
+    int dev = cfg.device;
+    if (dev < 0) {
+        e = hipGetDevice(&dev);
+        if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+    }
+    if (dev >= count) return Error{RC_ERR_INVALID_ARGUMENT, "device index out of range"};
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail("hipGetDeviceProperties", e);
+    const std::string arch = prop.gcnArchName;
+    if (arch.compare(0, 6, "gfx950") != 0)
+        return Error{RC_ERR_DEVICE, "GPU " + std::to_string(dev) + " is " + arch +
+                                        "; this library is built for gfx950 only"};
+    info->device = dev;
+    info->cu_count = prop.multiProcessorCount;
+    info->l2_bytes = prop.l2CacheSize;
+    info->arch = arch;
+    g.device = dev;
+    g.next = 0;
+    return {};
+}
+
+Error device_launch(const LaunchPlan& p, int grid, void* stream) {
+    DeviceGuard guard;
+    if (guard.err != hipSuccess) return hip_fail("hipSetDevice", guard.err);
+    hipError_t e = launch_jobs(p, grid, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail("kernel launch", e);
+    return {};
+}
+
+Error device_launch_batch(const BatchPlan& p, int grid, void* stream) {
+    if (p.jobs.empty()) return {};
+    DeviceGuard guard;
+    if (guard.err != hipSuccess) return hip_fail("hipSetDevice", guard.err);
+    Arena& a = g.arena[g.next];
+    Error err = wait_arena(a);
+    if (err.code) return err;
+    const size_t job_bytes = p.jobs.size() * sizeof(BatchJob);
+    const size_t ptr_off = (job_bytes + 255) & ~size_t(255);
+    const size_t bytes = ptr_off + p.ptrs.size() * sizeof(void*);
+    err = ensure_arena(a, bytes);
+    if (err.code) return err;
+    std::memcpy(a.host, p.jobs.data(), job_bytes);
+    std::memcpy(static_cast<char*>(a.host) + ptr_off, p.ptrs.data(), p.ptrs.size() * sizeof(void*));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(a.dev, a.host, bytes, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail("hipMemcpyAsync", e);
+    const BatchJob* jobs = static_cast<const BatchJob*>(a.dev);
+    const void* const* ptrs =
+        reinterpret_cast<const void* const*>(static_cast<const char*>(a.dev) + ptr_off);
+    e = launch_batch(jobs, (int)p.jobs.size(), ptrs, p, p.nontemporal != 0, grid, s);
+    if (e != hipSuccess) return hip_fail("kernel launch", e);
+    e = hipEventRecord(a.done, s);
+    if (e != hipSuccess) return hip_fail("hipEventRecord", e);
+    a.pending = true;
+    g.next ^= 1;
+    return {};
+}
+
+Error device_finish() {
+    DeviceGuard guard;
+    if (guard.err != hipSuccess) return hip_fail("hipSetDevice", guard.err);
+    hipError_t e = hipDeviceSynchronize();
+    for (Arena& a : g.arena) free_arena(a);
+    g.device = -1;
+    if (e != hipSuccess) return hip_fail("hipDeviceSynchronize", e);
+    return {};
+}
+
+void device_reset() {
+    if (g.device < 0) return;
+    DeviceGuard guard;
+    for (Arena& a : g.arena) free_arena(a);
+    g.device = -1;
+}
+
+}  // namespace rc

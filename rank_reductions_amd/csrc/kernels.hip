@@ -1,0 +1,426 @@
+// Reduction and fan-out kernels for gfx950 (CDNA4, wave64).
+//
+// Every collective is a list of jobs; a job is one ring segment c of one
+// tensor.  A job either folds R inputs element by element, in the rank order
+// (c+1), (c+2), ..., c that a ring reduce-scatter leaves at segment c's owner
+// (ruCCL README (ja), "CUDA tensor example": ring AllReduce over logical ranks
+// on one GPU), or copies one input bit for bit (broadcast, all-gather, the
+// ring's all-gather phase).  The result is written to a set of ranks' outputs.
+//
+// The work is HBM streaming with no reuse: 16-byte vector loads and stores per
+// lane, R loads in flight per vector, non-temporal hints by default.  A job's
+// elements split into a scalar head (until every pointer of the job is 16-byte
+// aligned), a body of 16-byte vectors, and a scalar tail (fewer than 4
+// elements); head and tail are done by the lanes of the job's first tile.
+// Jobs whose pointers disagree modulo 16 bytes run element by element.
+// Each element is read and written by exactly one lane, and there are no
+// atomics, so the summation order is the documented one whatever the grid.
+#include <hip/hip_runtime.h>
+
+#include "rc_internal.h"
+
+namespace rc {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t as_u(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// ---------------------------------------------------------------- operators
+// Each operator works on raw 32-bit patterns.
+
+struct OpSumF32 {
+    static constexpr bool kCanMean = true;
+    __device__ __forceinline__ static uint32_t apply(uint32_t a, uint32_t b) {
+        return as_u(as_f(a) + as_f(b));
+    }
+    __device__ __forceinline__ static u32x4 apply4(u32x4 a, u32x4 b) {
+        f32x4 r = __builtin_bit_cast(f32x4, a) + __builtin_bit_cast(f32x4, b);
+        return __builtin_bit_cast(u32x4, r);
+    }
+};
+
+struct OpSumI32 {  // two's-complement wrap: unsigned add
+    static constexpr bool kCanMean = false;
+    __device__ __forceinline__ static uint32_t apply(uint32_t a, uint32_t b) { return a + b; }
+    __device__ __forceinline__ static u32x4 apply4(u32x4 a, u32x4 b) { return a + b; }
+};
+
+struct OpMaxI32 {
+    static constexpr bool kCanMean = false;
+    __device__ __forceinline__ static uint32_t apply(uint32_t a, uint32_t b) {
+        int32_t x = (int32_t)a, y = (int32_t)b;
+        return (uint32_t)(x > y ? x : y);
+    }
+    __device__ __forceinline__ static u32x4 apply4(u32x4 a, u32x4 b) {
+        u32x4 r;
+        r.x = apply(a.x, b.x);
+        r.y = apply(a.y, b.y);
+        r.z = apply(a.z, b.z);
+        r.w = apply(a.w, b.w);
+        return r;
+    }
+};
+
+// float32 max: any NaN gives the quiet NaN 0x7FC00000; equal values keep the
+// bitwise AND of their patterns, which picks -0 only when both are -0 and is
+// the identity otherwise; else the larger value.  Commutative and associative,
+// so the fold order does not change it.
+struct OpMaxF32 {
+    static constexpr bool kCanMean = false;
+    __device__ __forceinline__ static uint32_t apply(uint32_t a, uint32_t b) {
+        float x = as_f(a), y = as_f(b);
+        if (x != x || y != y) return 0x7FC00000u;
+        if (x == y) return a & b;
+        return x > y ? a : b;
+    }
+    __device__ __forceinline__ static u32x4 apply4(u32x4 a, u32x4 b) {
+        u32x4 r;
+        r.x = apply(a.x, b.x);
+        r.y = apply(a.y, b.y);
+        r.z = apply(a.z, b.z);
+        r.w = apply(a.w, b.w);
+        return r;
+    }
+};
+
+// Mean: one correctly rounded float32 division of the finished fold by R
+// (hipcc keeps float division IEEE-exact; for R a power of two the compiler
+// may use the exact reciprocal, which gives the same bits).
+template <int R>
+__device__ __forceinline__ uint32_t mean1(uint32_t acc) {
+    return as_u(as_f(acc) / (float)R);
+}
+template <int R>
+__device__ __forceinline__ u32x4 mean4(u32x4 acc) {
+    f32x4 r = __builtin_bit_cast(f32x4, acc) / (float)R;
+    return __builtin_bit_cast(u32x4, r);
+}
+
+// ---------------------------------------------------------------- memory
+
+template <bool NT>
+__device__ __forceinline__ u32x4 ld4(const uint32_t* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    else return *reinterpret_cast<const u32x4*>(p);
+}
+template <bool NT>
+__device__ __forceinline__ void st4(uint32_t* p, u32x4 v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+    else *reinterpret_cast<u32x4*>(p) = v;
+}
+template <bool NT>
+__device__ __forceinline__ uint32_t ld1(const uint32_t* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+template <bool NT>
+__device__ __forceinline__ void st1(uint32_t* p, uint32_t v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+// ---------------------------------------------------------------- one job
+
+// Output addressing: out(o) is rank o's output at the job's first element.
+// Inputs: in[k] is the k-th operand of the fold at the job's first element.
+
+template <int NIN, int NR, class Op, bool NT, class OutF>
+__device__ __forceinline__ void element(const uint32_t* const (&in)[NIN], int64_t e,
+                                        const OutF& out, uint32_t mask, bool mean) {
+    uint32_t x[NIN];
+#pragma unroll
+    for (int k = 0; k < NIN; ++k) x[k] = ld1<NT>(in[k] + e);
+    uint32_t acc = x[0];
+#pragma unroll
+    for (int k = 1; k < NIN; ++k) acc = Op::apply(acc, x[k]);
+    if constexpr (Op::kCanMean) {
+        if (mean) acc = mean1<NIN>(acc);
+    }
+#pragma unroll
+    for (int o = 0; o < NR; ++o)
+        if ((mask >> o) & 1u) st1<NT>(out(o) + e, acc);
+}
+
+// One round of U vectors per lane over vector indices [vb, vb + kBlock*U),
+// clipped to v1 unless FULL.  `base` is the element offset of vector 0.
+template <int NIN, int NR, class Op, int U, bool NT, bool FULL, class OutF>
+__device__ __forceinline__ void vec_round(const uint32_t* const (&in)[NIN], int64_t base, int64_t vb,
+                                          int64_t v1, const OutF& out, uint32_t mask, bool mean) {
+    const int tid = threadIdx.x;
+    u32x4 x[U][NIN];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t v = vb + u * kBlock + tid;
+        ok[u] = FULL || v < v1;
+        if (ok[u]) {
+#pragma unroll
+            for (int k = 0; k < NIN; ++k) x[u][k] = ld4<NT>(in[k] + base + v * kVec);
+        }
+    }
+    u32x4 acc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        acc[u] = x[u][0];
+#pragma unroll
+        for (int k = 1; k < NIN; ++k) acc[u] = Op::apply4(acc[u], x[u][k]);
+        if constexpr (Op::kCanMean) {
+            if (mean) acc[u] = mean4<NIN>(acc[u]);
+        }
+    }
+#pragma unroll
+    for (int o = 0; o < NR; ++o) {
+        if (!((mask >> o) & 1u)) continue;
+        uint32_t* p = out(o) + base;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t v = vb + u * kBlock + tid;
+            if (FULL || ok[u]) st4<NT>(p + v * kVec, acc[u]);
+        }
+    }
+}
+
+// Tile lt of a job of `len` elements.
+template <int NIN, int NR, class Op, int U, bool NT, class OutF>
+__device__ __forceinline__ void job_tile(const uint32_t* const (&in)[NIN], const OutF& out,
+                                         uint32_t mask, int64_t len, int phase, int64_t lt,
+                                         int64_t te, bool mean) {
+    const int tid = threadIdx.x;
+    if (phase == kScalarOnly) {
+        const int64_t e0 = lt * te;
+        const int64_t e1 = e0 + te < len ? e0 + te : len;
+        for (int64_t e = e0 + tid; e < e1; e += kBlock)
+            element<NIN, NR, Op, NT>(in, e, out, mask, mean);
+        return;
+    }
+    const int64_t head = phase < len ? phase : len;
+    const int64_t nvec = (len - head) / kVec;
+    const int64_t tail0 = head + nvec * kVec;
+    const int64_t tv = te / kVec;
+    const int64_t v0 = lt * tv;
+    const int64_t v1 = v0 + tv < nvec ? v0 + tv : nvec;
+    constexpr int64_t kStep = (int64_t)kBlock * U;
+    int64_t vb = v0;
+    for (; vb + kStep <= v1; vb += kStep)
+        vec_round<NIN, NR, Op, U, NT, true>(in, head, vb, v1, out, mask, mean);
+    if (vb < v1) vec_round<NIN, NR, Op, U, NT, false>(in, head, vb, v1, out, mask, mean);
+    if (lt == 0) {
+        const int64_t nscal = head + (len - tail0);  // at most 3 + 3
+        if (tid < nscal) {
+            const int64_t e = tid < head ? tid : tail0 + (tid - head);
+            element<NIN, NR, Op, NT>(in, e, out, mask, mean);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- kernels
+
+// Fold jobs: input k of job c is rank (c+1+k) mod R at element c*in_stride.
+template <int NIN, class Op, int U, bool NT>
+__global__ __launch_bounds__(kBlock) void fold_kernel(JobArgs a) {
+    const int64_t total = a.tile_prefix[a.jobs];
+    for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
+        int c = 0;
+        while (t >= a.tile_prefix[c + 1]) ++c;
+        const int64_t lt = t - a.tile_prefix[c];
+        const int64_t start = (int64_t)c * a.seg;
+        const int64_t len = a.n - start < a.seg ? a.n - start : a.seg;
+        const uint32_t* in[NIN];
+#pragma unroll
+        for (int k = 0; k < NIN; ++k)
+            in[k] = static_cast<const uint32_t*>(a.in[(c + 1 + k) % NIN]) + (int64_t)c * a.in_stride;
+        uint32_t mask = a.out_mask;
+        if (a.out_mode == kOutOwner) mask = 1u << c;
+        else if (a.out_mode == kOutMaskButOwner) mask &= ~(1u << c);
+        const int64_t ooff = (int64_t)c * a.out_stride;
+        auto out = [&](int o) { return static_cast<uint32_t*>(a.out[o]) + ooff; };
+        job_tile<NIN, NIN, Op, U, NT>(in, out, mask, len, a.phase[c], lt, a.tile_elems, a.mean != 0);
+    }
+}
+
+// Copy jobs: job c copies in[c] at element c*in_stride, bit for bit, to the
+// outputs of up to NR ranks.
+template <int NR, int U, bool NT>
+__global__ __launch_bounds__(kBlock) void copy_kernel(JobArgs a) {
+    const int64_t total = a.tile_prefix[a.jobs];
+    for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
+        int c = 0;
+        while (t >= a.tile_prefix[c + 1]) ++c;
+        const int64_t lt = t - a.tile_prefix[c];
+        const int64_t start = (int64_t)c * a.seg;
+        const int64_t len = a.n - start < a.seg ? a.n - start : a.seg;
+        const uint32_t* in[1] = {static_cast<const uint32_t*>(a.in[c]) + (int64_t)c * a.in_stride};
+        uint32_t mask = a.out_mask;
+        if (a.out_mode == kOutOwner) mask = 1u << c;
+        else if (a.out_mode == kOutMaskButOwner) mask &= ~(1u << c);
+        const int64_t ooff = (int64_t)c * a.out_stride;
+        auto out = [&](int o) { return static_cast<uint32_t*>(a.out[o]) + ooff; };
+        job_tile<1, NR, OpSumI32, U, NT>(in, out, mask, len, a.phase[c], lt, a.tile_elems, false);
+    }
+}
+
+// Batched all-reduce: every workgroup takes a contiguous range of tiles and
+// walks the job table from the job that holds its first tile.
+template <int NIN, class Op, int U, bool NT>
+__global__ __launch_bounds__(kBlock) void batch_kernel(const BatchJob* __restrict__ jobs, int njobs,
+                                                       const void* const* __restrict__ ptrs,
+                                                       int64_t total_tiles, int te, int mean) {
+    const int64_t per = (total_tiles + gridDim.x - 1) / gridDim.x;
+    const int64_t t0 = (int64_t)blockIdx.x * per;
+    const int64_t t1 = t0 + per < total_tiles ? t0 + per : total_tiles;
+    if (t0 >= t1) return;
+    int lo = 0, hi = njobs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (jobs[mid].tile_begin <= t0) lo = mid;
+        else hi = mid - 1;
+    }
+    int j = lo;
+    for (int64_t t = t0; t < t1; ++t) {
+        while (j + 1 < njobs && jobs[j + 1].tile_begin <= t) ++j;
+        const BatchJob jb = jobs[j];
+        const void* const* tp = ptrs + (int64_t)jb.tensor * 2 * NIN;
+        const uint32_t* in[NIN];
+#pragma unroll
+        for (int k = 0; k < NIN; ++k)
+            in[k] = static_cast<const uint32_t*>(tp[(jb.c + 1 + k) % NIN]) + jb.start;
+        auto out = [&](int o) {
+            return static_cast<uint32_t*>(const_cast<void*>(tp[NIN + o])) + jb.start;
+        };
+        job_tile<NIN, NIN, Op, U, NT>(in, out, (1u << NIN) - 1u, jb.len, jb.phase, t - jb.tile_begin,
+                                      te, mean != 0);
+    }
+}
+
+// ---------------------------------------------------------------- dispatch
+
+template <int NIN>
+constexpr int kUnroll = unroll_for(NIN);
+
+using FoldFn = void (*)(JobArgs);
+using BatchFn = void (*)(const BatchJob*, int, const void* const*, int64_t, int, int);
+
+template <int NIN, class Op, bool NT>
+FoldFn fold_ptr() { return fold_kernel<NIN, Op, kUnroll<NIN>, NT>; }
+template <int NIN, class Op, bool NT>
+BatchFn batch_ptr() { return batch_kernel<NIN, Op, kUnroll<NIN>, NT>; }
+
+template <int NR, bool NT>
+FoldFn copy_ptr() { return copy_kernel<NR, kUnroll<1>, NT>; }
+
+template <bool NT>
+FoldFn pick_copy(int nranks) {
+    switch (nranks) {
+        case 1: return copy_ptr<1, NT>();
+        case 2: return copy_ptr<2, NT>();
+        case 3: return copy_ptr<3, NT>();
+        case 4: return copy_ptr<4, NT>();
+        case 5: return copy_ptr<5, NT>();
+        case 6: return copy_ptr<6, NT>();
+        case 7: return copy_ptr<7, NT>();
+        case 8: return copy_ptr<8, NT>();
+        case 9: return copy_ptr<9, NT>();
+        case 10: return copy_ptr<10, NT>();
+        case 11: return copy_ptr<11, NT>();
+        case 12: return copy_ptr<12, NT>();
+        case 13: return copy_ptr<13, NT>();
+        case 14: return copy_ptr<14, NT>();
+        case 15: return copy_ptr<15, NT>();
+        case 16: return copy_ptr<16, NT>();
+        default: return nullptr;
+    }
+}
+
+template <class Op, bool NT>
+FoldFn pick_fold(int nin) {
+    switch (nin) {
+        case 1: return fold_ptr<1, Op, NT>();
+        case 2: return fold_ptr<2, Op, NT>();
+        case 3: return fold_ptr<3, Op, NT>();
+        case 4: return fold_ptr<4, Op, NT>();
+        case 5: return fold_ptr<5, Op, NT>();
+        case 6: return fold_ptr<6, Op, NT>();
+        case 7: return fold_ptr<7, Op, NT>();
+        case 8: return fold_ptr<8, Op, NT>();
+        case 9: return fold_ptr<9, Op, NT>();
+        case 10: return fold_ptr<10, Op, NT>();
+        case 11: return fold_ptr<11, Op, NT>();
+        case 12: return fold_ptr<12, Op, NT>();
+        case 13: return fold_ptr<13, Op, NT>();
+        case 14: return fold_ptr<14, Op, NT>();
+        case 15: return fold_ptr<15, Op, NT>();
+        case 16: return fold_ptr<16, Op, NT>();
+        default: return nullptr;
+    }
+}
+
+template <class Op, bool NT>
+BatchFn pick_batch(int nin) {
+    switch (nin) {
+        case 1: return batch_ptr<1, Op, NT>();
+        case 2: return batch_ptr<2, Op, NT>();
+        case 3: return batch_ptr<3, Op, NT>();
+        case 4: return batch_ptr<4, Op, NT>();
+        case 5: return batch_ptr<5, Op, NT>();
+        case 6: return batch_ptr<6, Op, NT>();
+        case 7: return batch_ptr<7, Op, NT>();
+        case 8: return batch_ptr<8, Op, NT>();
+        case 9: return batch_ptr<9, Op, NT>();
+        case 10: return batch_ptr<10, Op, NT>();
+        case 11: return batch_ptr<11, Op, NT>();
+        case 12: return batch_ptr<12, Op, NT>();
+        case 13: return batch_ptr<13, Op, NT>();
+        case 14: return batch_ptr<14, Op, NT>();
+        case 15: return batch_ptr<15, Op, NT>();
+        case 16: return batch_ptr<16, Op, NT>();
+        default: return nullptr;
+    }
+}
+
+template <bool NT>
+FoldFn pick_fold_op(int dtype, int op, int nin) {
+    if (dtype == RC_F32) {
+        if (op == RC_MAX) return pick_fold<OpMaxF32, NT>(nin);
+        return pick_fold<OpSumF32, NT>(nin);
+    }
+    if (op == RC_MAX) return pick_fold<OpMaxI32, NT>(nin);
+    return pick_fold<OpSumI32, NT>(nin);
+}
+
+template <bool NT>
+BatchFn pick_batch_op(int dtype, int op, int nin) {
+    if (dtype == RC_F32) {
+        if (op == RC_MAX) return pick_batch<OpMaxF32, NT>(nin);
+        return pick_batch<OpSumF32, NT>(nin);
+    }
+    if (op == RC_MAX) return pick_batch<OpMaxI32, NT>(nin);
+    return pick_batch<OpSumI32, NT>(nin);
+}
+
+}  // namespace
+
+hipError_t launch_jobs(const LaunchPlan& p, int grid, hipStream_t stream) {
+    const bool nt = p.args.nontemporal != 0;
+    FoldFn fn;
+    if (p.args.in_mode == kInCopy) fn = nt ? pick_copy<true>(p.args.nranks) : pick_copy<false>(p.args.nranks);
+    else fn = nt ? pick_fold_op<true>(p.dtype, p.op, p.nin) : pick_fold_op<false>(p.dtype, p.op, p.nin);
+    if (!fn) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(kBlock), 0, stream, p.args);
+    return hipGetLastError();
+}
+
+hipError_t launch_batch(const BatchJob* jobs, int njobs, const void* const* ptrs, const BatchPlan& p,
+                        bool nt, int grid, hipStream_t stream) {
+    BatchFn fn = nt ? pick_batch_op<true>(p.dtype, p.op, p.nranks)
+                    : pick_batch_op<false>(p.dtype, p.op, p.nranks);
+    if (!fn) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(kBlock), 0, stream, jobs, njobs, ptrs, p.total_tiles,
+                       p.tile_elems, p.op == RC_MEAN ? 1 : 0);
+    return hipGetLastError();
+}
+
+}  // namespace rc

@@ -1,0 +1,283 @@
+// Chunk scheduler: turns a validated collective into launch plans - ring
+// segments (jobs), their alignment phase, tiles per job and the grid.
+//
+// Segmentation follows the ring of the ruCCL README (ja), "CUDA tensor
+// example": S = ceil(N/R) elements per segment, segment c owned by rank c and
+// folded in rank order (c+1), ..., c.  reduce_scatter_tensor and
+// all_gather_into_tensor (monarch Communicator page) use shards of M = N/R
+// elements, which are exactly those segments.  Host-only C++.
+#include <algorithm>
+#include <cstdint>
+#include <vector>
+
+#include "rc_internal.h"
+
+namespace rc {
+
+namespace {
+
+constexpr int64_t kMaxTileElems = 65536;
+
+uintptr_t addr(const void* p, int64_t elem_off, int64_t esize) {
+    return reinterpret_cast<uintptr_t>(p) + (uintptr_t)(elem_off * esize);
+}
+
+// Fill per-job phase and tile counts of a single-launch plan.
+void finish_jobs(LaunchPlan* p, const std::vector<std::vector<uintptr_t>>& job_addrs) {
+    JobArgs& a = p->args;
+    const int64_t es = 4;
+    a.tile_prefix[0] = 0;
+    for (int c = 0; c < a.jobs; ++c) {
+        const int64_t start = (int64_t)c * a.seg;
+        const int64_t len = std::max<int64_t>(0, std::min(a.seg, a.n - start));
+        const auto& ad = job_addrs[c];
+        a.phase[c] = len ? job_phase(ad.data(), (int)ad.size(), es, len) : 0;
+        a.tile_prefix[c + 1] = a.tile_prefix[c] + job_tiles(len, a.phase[c], a.tile_elems);
+    }
+    for (int c = a.jobs; c < kMaxRanks; ++c) {
+        a.tile_prefix[c + 1] = a.tile_prefix[a.jobs];
+        a.phase[c] = 0;
+    }
+    p->total_tiles = a.tile_prefix[a.jobs];
+}
+
+int nontemporal_of(const Config& cfg) {
+    return cfg.cache_hint == RC_CACHE_NORMAL ? 0 : 1;
+}
+
+}  // namespace
+
+int tile_elems_for(int nin, const Config& cfg) {
+    const int64_t step = (int64_t)kBlock * kVec * unroll_for(nin);
+    int64_t te = cfg.tile_elems > 0 ? cfg.tile_elems : step;
+    te = ((te + step - 1) / step) * step;
+    te = std::min<int64_t>(std::max<int64_t>(te, step), std::max<int64_t>(step, kMaxTileElems));
+    return (int)te;
+}
+
+uint8_t job_phase(const uintptr_t* addrs, int naddrs, int64_t esize, int64_t len) {
+    if (naddrs == 0) return 0;
+    const uintptr_t m = addrs[0] % 16;
+    for (int i = 1; i < naddrs; ++i)
+        if (addrs[i] % 16 != m) return kScalarOnly;
+    const int64_t phase = (int64_t)((16 - m) % 16) / esize;
+    (void)len;
+    return (uint8_t)phase;
+}
+
+int64_t job_tiles(int64_t len, uint8_t phase, int64_t te) {
+    if (len <= 0) return 0;
+    if (phase == kScalarOnly) return (len + te - 1) / te;
+    const int64_t head = std::min<int64_t>(phase, len);
+    const int64_t body = ((len - head) / kVec) * kVec;
+    return std::max<int64_t>(1, (body + te - 1) / te);
+}
+
+int grid_for(int64_t total_tiles, const Config& cfg, const DeviceInfo& dev) {
+    const int64_t cap = cfg.max_workgroups > 0 ? cfg.max_workgroups
+                                               : (int64_t)std::max(dev.cu_count, 1) * 8;
+    return (int)std::max<int64_t>(1, std::min(total_tiles, cap));
+}
+
+std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg) {
+    std::vector<LaunchPlan> out;
+    if (ck.count == 0) return out;
+    const int R = ck.nranks;
+    const int64_t es = element_size(ck.dtype);
+    const uint32_t all = (R >= 32) ? 0xFFFFFFFFu : ((1u << R) - 1u);
+
+    LaunchPlan p{};
+    JobArgs& a = p.args;
+    a = JobArgs{};
+    a.nranks = R;
+    a.nontemporal = nontemporal_of(cfg);
+    p.dtype = ck.dtype;
+    p.op = ck.op;
+
+    std::vector<std::vector<uintptr_t>> ad;
+    auto fold_setup = [&](int64_t n, int64_t seg, int64_t in_stride, int64_t out_stride) {
+        p.nin = R;
+        a.in_mode = kInFold;
+        a.n = n;
+        a.seg = seg;
+        a.in_stride = in_stride;
+        a.out_stride = out_stride;
+        a.jobs = R;
+        a.mean = ck.op == RC_MEAN;
+        a.tile_elems = tile_elems_for(R, cfg);
+        for (int r = 0; r < R; ++r) {
+            a.in[r] = ck.send[r];
+            a.out[r] = ck.recv[r];
+        }
+    };
+    auto fold_addrs = [&](uint32_t mask_for_owner_only, bool owner_only) {
+        ad.assign(R, {});
+        for (int c = 0; c < R; ++c) {
+            for (int r = 0; r < R; ++r) ad[c].push_back(addr(a.in[r], (int64_t)c * a.in_stride, es));
+            for (int r = 0; r < R; ++r) {
+                const bool writes = owner_only ? (r == c) : ((mask_for_owner_only >> r) & 1u);
+                if (writes) ad[c].push_back(addr(a.out[r], (int64_t)c * a.out_stride, es));
+            }
+        }
+    };
+
+    switch (ck.coll) {
+        case Coll::AllReduce:
+        case Coll::Reduce: {
+            const int64_t S = (ck.count + R - 1) / R;
+            const bool ring = ck.coll == Coll::AllReduce && cfg.algo == RC_ALGO_RING;
+            fold_setup(ck.count, S, S, S);
+            if (!ring) {
+                a.out_mode = kOutMask;
+                a.out_mask = ck.coll == Coll::Reduce ? (1u << ck.root) : all;
+                fold_addrs(a.out_mask, false);
+                finish_jobs(&p, ad);
+                out.push_back(p);
+                break;
+            }
+            // ring phase 1: the fold of segment c lands in rank c's output
+            a.out_mode = kOutOwner;
+            a.out_mask = all;
+            fold_addrs(0, true);
+            finish_jobs(&p, ad);
+            out.push_back(p);
+            if (R == 1) break;
+            // ring phase 2: rank c's finished segment is copied to every other rank
+            LaunchPlan q{};
+            JobArgs& b = q.args;
+            b = JobArgs{};
+            q.nin = 1;
+            q.dtype = ck.dtype;
+            q.op = ck.op;
+            b.nranks = R;
+            b.nontemporal = a.nontemporal;
+            b.in_mode = kInCopy;
+            b.out_mode = kOutMaskButOwner;
+            b.out_mask = all;
+            b.n = ck.count;
+            b.seg = S;
+            b.in_stride = S;
+            b.out_stride = S;
+            b.jobs = R;
+            b.tile_elems = tile_elems_for(1, cfg);
+            for (int r = 0; r < R; ++r) {
+                b.in[r] = ck.recv[r];
+                b.out[r] = ck.recv[r];
+            }
+            ad.assign(R, {});
+            for (int c = 0; c < R; ++c)
+                for (int r = 0; r < R; ++r) ad[c].push_back(addr(ck.recv[r], (int64_t)c * S, es));
+            finish_jobs(&q, ad);
+            out.push_back(q);
+            break;
+        }
+        case Coll::ReduceScatter: {
+            const int64_t M = ck.count / R;
+            fold_setup(ck.count, M, M, 0);
+            a.out_mode = kOutOwner;
+            a.out_mask = all;
+            fold_addrs(0, true);
+            finish_jobs(&p, ad);
+            out.push_back(p);
+            break;
+        }
+        case Coll::Broadcast: {
+            const int s = ck.root;
+            p.nin = 1;
+            a.in_mode = kInCopy;
+            a.out_mode = kOutMask;
+            a.n = ck.count;
+            a.seg = ck.count;
+            a.in_stride = 0;
+            a.out_stride = 0;
+            a.jobs = 1;
+            a.tile_elems = tile_elems_for(1, cfg);
+            a.in[0] = ck.send[s];
+            uint32_t mask = 0;
+            for (int r = 0; r < R; ++r) {
+                a.out[r] = ck.recv[r];
+                if (ck.recv[r] && !(r == s && ck.recv[r] == ck.send[s])) mask |= 1u << r;
+            }
+            a.out_mask = mask;
+            if (!mask) break;
+            ad.assign(1, {});
+            ad[0].push_back(addr(a.in[0], 0, es));
+            for (int r = 0; r < R; ++r)
+                if ((mask >> r) & 1u) ad[0].push_back(addr(a.out[r], 0, es));
+            finish_jobs(&p, ad);
+            out.push_back(p);
+            break;
+        }
+        case Coll::AllGather: {
+            const int64_t M = ck.count;
+            p.nin = 1;
+            a.in_mode = kInCopy;
+            a.out_mode = kOutMask;
+            a.out_mask = all;
+            a.n = M * R;
+            a.seg = M;
+            a.in_stride = 0;
+            a.out_stride = M;
+            a.jobs = R;
+            a.tile_elems = tile_elems_for(1, cfg);
+            for (int r = 0; r < R; ++r) {
+                a.in[r] = ck.send[r];
+                a.out[r] = ck.recv[r];
+            }
+            // in place: rank c's shard already sits at its place in rank c's output
+            ad.assign(R, {});
+            for (int c = 0; c < R; ++c) {
+                ad[c].push_back(addr(a.in[c], 0, es));
+                for (int r = 0; r < R; ++r) ad[c].push_back(addr(a.out[r], (int64_t)c * M, es));
+            }
+            finish_jobs(&p, ad);
+            out.push_back(p);
+            break;
+        }
+    }
+    return out;
+}
+
+BatchPlan plan_batch(const std::vector<Checked>& tensors, const Config& cfg) {
+    BatchPlan bp;
+    if (tensors.empty()) return bp;
+    const int R = tensors[0].nranks;
+    bp.nranks = R;
+    bp.dtype = tensors[0].dtype;
+    bp.op = tensors[0].op;
+    bp.tile_elems = tile_elems_for(R, cfg);
+    bp.nontemporal = nontemporal_of(cfg);
+    const int64_t es = element_size(bp.dtype);
+    int64_t tiles = 0;
+    int32_t t_index = 0;
+    std::vector<uintptr_t> ad;
+    ad.reserve(2 * R);
+    for (const Checked& ck : tensors) {
+        if (ck.count == 0) continue;
+        for (int r = 0; r < R; ++r) bp.ptrs.push_back(ck.send[r]);
+        for (int r = 0; r < R; ++r) bp.ptrs.push_back(ck.recv[r]);
+        const int64_t S = (ck.count + R - 1) / R;
+        for (int c = 0; c < R; ++c) {
+            const int64_t start = (int64_t)c * S;
+            const int64_t len = std::min(S, ck.count - start);
+            if (len <= 0) continue;
+            ad.clear();
+            for (int r = 0; r < R; ++r) ad.push_back(addr(ck.send[r], start, es));
+            for (int r = 0; r < R; ++r) ad.push_back(addr(ck.recv[r], start, es));
+            BatchJob j{};
+            j.tile_begin = tiles;
+            j.start = start;
+            j.len = len;
+            j.tensor = t_index;
+            j.c = c;
+            j.phase = job_phase(ad.data(), (int)ad.size(), es, len);
+            tiles += job_tiles(len, (uint8_t)j.phase, bp.tile_elems);
+            bp.jobs.push_back(j);
+        }
+        ++t_index;
+    }
+    bp.total_tiles = tiles;
+    return bp;
+}
+
+}  // namespace rc

@@ -1,0 +1,290 @@
+// Argument checks for every collective, producing the CollectiveError cases of
+// the ruCCL README (ja), section 4 "Errors and lifecycle": shape mismatch,
+// inconsistent reduction op or root, invalid broadcast sender count.  The
+// call contract they enforce is section 3 "Registration and call contract":
+// ranks call matching collectives with the same shape, op and root, and each
+// broadcast has exactly one sender.  Host-only C++; nothing here touches HIP.
+#include <algorithm>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "rc_internal.h"
+
+namespace rc {
+namespace {
+
+// Largest element count accepted per buffer (2^44 elements = 64 TiB of f32).
+constexpr int64_t kMaxCount = int64_t(1) << 44;
+
+std::string fmt(const char* f, long long a = 0, long long b = 0, long long c = 0) {
+    char buf[256];
+    std::snprintf(buf, sizeof buf, f, a, b, c);
+    return buf;
+}
+
+Error fail(int code, std::string msg) { return Error{code, std::move(msg)}; }
+
+bool reduces(Coll c) {
+    return c == Coll::AllReduce || c == Coll::Reduce || c == Coll::ReduceScatter;
+}
+
+const char* coll_name(Coll c) {
+    switch (c) {
+        case Coll::AllReduce: return "all_reduce";
+        case Coll::Reduce: return "reduce";
+        case Coll::Broadcast: return "broadcast";
+        case Coll::ReduceScatter: return "reduce_scatter";
+        case Coll::AllGather: return "all_gather";
+    }
+    return "?";
+}
+
+Error count_of(const rc_buf& b, int r, int64_t* count) {
+    if (b.ndim < 0 || b.ndim > RC_MAX_DIMS)
+        return fail(RC_ERR_INVALID_ARGUMENT, fmt("rank %lld: ndim %lld outside [0, 8]", r, b.ndim));
+    int64_t n = 1;
+    for (int d = 0; d < b.ndim; ++d) {
+        if (b.dims[d] < 0)
+            return fail(RC_ERR_INVALID_ARGUMENT, fmt("rank %lld: dims[%lld] is negative", r, d));
+        if (b.dims[d] == 0) n = 0;
+        else if (n != 0) {
+            if (b.dims[d] > kMaxCount || n > kMaxCount / b.dims[d])
+                return fail(RC_ERR_INVALID_ARGUMENT, fmt("rank %lld: element count too large", r));
+            n *= b.dims[d];
+        }
+    }
+    *count = n;
+    return {};
+}
+
+// A byte range [lo, hi) of device memory that one call reads or writes.
+// Reads may overlap reads.  A read may overlap a write only as the exact
+// in-place layout the collective allows: same `tag`, and read.lo - write.lo
+// equal to the read's `delta`.
+struct Range {
+    uintptr_t lo, hi;
+    int tag;        // -1: never in place
+    int64_t delta;  // allowed read.lo - write.lo
+    int owner;      // rank (for messages)
+    int tensor;
+};
+
+Error check_overlaps(std::vector<Range>& writes, const std::vector<Range>& reads) {
+    std::sort(writes.begin(), writes.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+    for (size_t i = 1; i < writes.size(); ++i) {
+        if (writes[i].lo < writes[i - 1].hi)
+            return fail(RC_ERR_INVALID_ARGUMENT,
+                        fmt("output of rank %lld (tensor %lld) overlaps another output",
+                            writes[i].owner, writes[i].tensor));
+    }
+    for (const Range& rd : reads) {
+        // first write that ends after rd.lo
+        auto it = std::upper_bound(writes.begin(), writes.end(), rd.lo,
+                                   [](uintptr_t v, const Range& w) { return v < w.hi; });
+        for (; it != writes.end() && it->lo < rd.hi; ++it) {
+            const bool in_place = rd.tag >= 0 && it->tag == rd.tag &&
+                                  (int64_t)(rd.lo - it->lo) == rd.delta;
+            if (!in_place)
+                return fail(RC_ERR_INVALID_ARGUMENT,
+                            fmt("input of rank %lld (tensor %lld) overlaps an output "
+                                "other than its allowed in-place position",
+                                rd.owner, rd.tensor));
+        }
+    }
+    return {};
+}
+
+bool misaligned(const void* p, int64_t esize) {
+    return (reinterpret_cast<uintptr_t>(p) % (uintptr_t)esize) != 0;
+}
+
+// Collect the ranges of a validated call into reads/writes.
+void ranges_of(const Checked& ck, int tensor, std::vector<Range>* writes, std::vector<Range>* reads) {
+    const int R = ck.nranks;
+    const int64_t b = element_size(ck.dtype);
+    const int64_t n = ck.count;
+    auto at = [](const void* p) { return reinterpret_cast<uintptr_t>(p); };
+    const int tag0 = tensor * kMaxRanks;
+    switch (ck.coll) {
+        case Coll::AllReduce:
+            for (int r = 0; r < R; ++r) {
+                writes->push_back({at(ck.recv[r]), at(ck.recv[r]) + n * b, tag0 + r, 0, r, tensor});
+                reads->push_back({at(ck.send[r]), at(ck.send[r]) + n * b, tag0 + r, 0, r, tensor});
+            }
+            break;
+        case Coll::Reduce:
+            for (int r = 0; r < R; ++r)
+                reads->push_back({at(ck.send[r]), at(ck.send[r]) + n * b, tag0 + r, 0, r, tensor});
+            writes->push_back({at(ck.recv[ck.root]), at(ck.recv[ck.root]) + n * b, tag0 + ck.root, 0,
+                               ck.root, tensor});
+            break;
+        case Coll::Broadcast: {
+            const int s = ck.root;
+            reads->push_back({at(ck.send[s]), at(ck.send[s]) + n * b, -1, 0, s, tensor});
+            for (int r = 0; r < R; ++r) {
+                if (!ck.recv[r] || (r == s && ck.recv[r] == ck.send[s])) continue;
+                writes->push_back({at(ck.recv[r]), at(ck.recv[r]) + n * b, -1, 0, r, tensor});
+            }
+            break;
+        }
+        case Coll::ReduceScatter: {
+            const int64_t m = n / R;
+            for (int r = 0; r < R; ++r) {
+                reads->push_back({at(ck.send[r]), at(ck.send[r]) + n * b, tag0 + r, -(int64_t)r * m * b, r,
+                                  tensor});
+                writes->push_back({at(ck.recv[r]), at(ck.recv[r]) + m * b, tag0 + r, 0, r, tensor});
+            }
+            break;
+        }
+        case Coll::AllGather:
+            for (int r = 0; r < R; ++r) {
+                reads->push_back({at(ck.send[r]), at(ck.send[r]) + n * b, tag0 + r, (int64_t)r * n * b, r,
+                                  tensor});
+                writes->push_back({at(ck.recv[r]), at(ck.recv[r]) + R * n * b, tag0 + r, 0, r, tensor});
+            }
+            break;
+    }
+}
+
+// Every check except the overlap check.
+Error validate_fields(Coll coll, int R, const rc_buf* bufs, Checked* ck) {
+    if (!bufs) return fail(RC_ERR_INVALID_ARGUMENT, "bufs is NULL");
+    ck->coll = coll;
+    ck->nranks = R;
+    // 1. malformed fields and required pointers
+    int64_t count[kMaxRanks];
+    for (int r = 0; r < R; ++r) {
+        const rc_buf& b = bufs[r];
+        if (b.dtype != RC_F32 && b.dtype != RC_I32)
+            return fail(RC_ERR_INVALID_ARGUMENT, fmt("rank %lld: unknown dtype %lld", r, b.dtype));
+        if (reduces(coll) && b.op != RC_SUM && b.op != RC_MEAN && b.op != RC_MAX)
+            return fail(RC_ERR_INVALID_ARGUMENT, fmt("rank %lld: unknown op %lld", r, b.op));
+        Error e = count_of(b, r, &count[r]);
+        if (e.code) return e;
+        const int64_t es = element_size(b.dtype);
+        const bool need_send = coll != Coll::Broadcast;
+        const bool need_recv = coll == Coll::AllReduce || coll == Coll::ReduceScatter ||
+                               coll == Coll::AllGather;
+        // zero-element buffers may be NULL (nothing is read or written)
+        if (need_send && !b.send && count[r] > 0)
+            return fail(RC_ERR_INVALID_ARGUMENT, fmt("rank %lld: send is NULL", r));
+        if (need_recv && !b.recv && count[r] > 0)
+            return fail(RC_ERR_INVALID_ARGUMENT, fmt("rank %lld: recv is NULL", r));
+        if ((b.send && misaligned(b.send, es)) || (b.recv && misaligned(b.recv, es)))
+            return fail(RC_ERR_INVALID_ARGUMENT,
+                        fmt("rank %lld: buffer not aligned to the %lld-byte element", r, es));
+    }
+    // 2. dtype, shape, op agree across ranks
+    for (int r = 1; r < R; ++r)
+        if (bufs[r].dtype != bufs[0].dtype)
+            return fail(RC_ERR_DTYPE_MISMATCH, fmt("rank %lld dtype %lld differs from rank 0's %lld", r,
+                                                   bufs[r].dtype, bufs[0].dtype));
+    for (int r = 1; r < R; ++r) {
+        bool same = bufs[r].ndim == bufs[0].ndim;
+        for (int d = 0; same && d < bufs[0].ndim; ++d) same = bufs[r].dims[d] == bufs[0].dims[d];
+        if (!same) return fail(RC_ERR_SHAPE_MISMATCH, fmt("rank %lld shape differs from rank 0's", r));
+    }
+    if (coll == Coll::ReduceScatter && count[0] % R != 0)
+        return fail(RC_ERR_SHAPE_MISMATCH,
+                    fmt("reduce_scatter input of %lld elements does not split over %lld ranks", count[0], R));
+    if (reduces(coll)) {
+        for (int r = 1; r < R; ++r)
+            if (bufs[r].op != bufs[0].op)
+                return fail(RC_ERR_OP_MISMATCH,
+                            fmt("rank %lld op %lld differs from rank 0's %lld", r, bufs[r].op, bufs[0].op));
+        if (bufs[0].op == RC_MEAN && bufs[0].dtype != RC_F32)
+            return fail(RC_ERR_INVALID_ARGUMENT, "Mean is defined for float32 only");
+    }
+    ck->dtype = bufs[0].dtype;
+    ck->op = reduces(coll) ? bufs[0].op : RC_SUM;
+    ck->count = count[0];
+    // 3. root
+    if (coll == Coll::Reduce || coll == Coll::Broadcast) {
+        for (int r = 1; r < R; ++r)
+            if (bufs[r].root != bufs[0].root)
+                return fail(RC_ERR_ROOT_MISMATCH,
+                            fmt("rank %lld root %lld differs from rank 0's %lld", r, bufs[r].root,
+                                bufs[0].root));
+        const int root = bufs[0].root;
+        if (coll == Coll::Reduce) {
+            if (root < 0 || root >= R)
+                return fail(RC_ERR_INVALID_ARGUMENT, fmt("root %lld outside [0, %lld)", root, R));
+            if (!bufs[root].recv && count[0] > 0)
+                return fail(RC_ERR_INVALID_ARGUMENT, fmt("root rank %lld: recv is NULL", root));
+            ck->root = root;
+        } else {
+            if (root < -1 || root >= R)
+                return fail(RC_ERR_INVALID_ARGUMENT, fmt("broadcast root %lld outside [-1, %lld)", root, R));
+            int senders = 0, sender = -1;
+            for (int r = 0; r < R; ++r)
+                if (bufs[r].send) ++senders, sender = r;
+            if (senders != 1)
+                return fail(RC_ERR_BROADCAST_SENDERS,
+                            fmt("broadcast needs exactly one sender (non-NULL send), got %lld", senders));
+            if (root >= 0 && root != sender)
+                return fail(RC_ERR_ROOT_MISMATCH,
+                            fmt("broadcast root %lld is not the sender %lld", root, sender));
+            for (int r = 0; r < R; ++r)
+                if (r != sender && !bufs[r].recv && count[0] > 0)
+                    return fail(RC_ERR_INVALID_ARGUMENT, fmt("receiver %lld: recv is NULL", r));
+            ck->root = sender;
+        }
+    }
+    for (int r = 0; r < R; ++r) {
+        ck->send[r] = bufs[r].send;
+        ck->recv[r] = bufs[r].recv;
+    }
+    if (coll == Coll::Reduce)
+        for (int r = 0; r < R; ++r)
+            if (r != ck->root) ck->recv[r] = nullptr;  // never written
+    return {};
+}
+
+}  // namespace
+
+int64_t element_size(int /*dtype*/) { return 4; }
+
+Error validate(Coll coll, int R, const rc_buf* bufs, Checked* ck) {
+    Error e = validate_fields(coll, R, bufs, ck);
+    if (e.code) {
+        std::string prefix = std::string(coll_name(coll)) + ": ";
+        e.msg = prefix + e.msg;
+        return e;
+    }
+    if (ck->count == 0) return {};
+    std::vector<Range> writes, reads;
+    ranges_of(*ck, 0, &writes, &reads);
+    e = check_overlaps(writes, reads);
+    if (e.code) e.msg = std::string(coll_name(coll)) + ": " + e.msg;
+    return e;
+}
+
+Error validate_batch(int R, int num_tensors, const rc_buf* bufs, std::vector<Checked>* out) {
+    if (num_tensors < 0)
+        return fail(RC_ERR_INVALID_ARGUMENT, "all_reduce_many: num_tensors is negative");
+    if (num_tensors > 0 && !bufs) return fail(RC_ERR_INVALID_ARGUMENT, "all_reduce_many: bufs is NULL");
+    out->assign(num_tensors, Checked{});
+    for (int t = 0; t < num_tensors; ++t) {
+        Error e = validate_fields(Coll::AllReduce, R, bufs + (int64_t)t * R, &(*out)[t]);
+        if (e.code) {
+            e.msg = fmt("all_reduce_many: tensor %lld: ", t) + e.msg;
+            return e;
+        }
+    }
+    // ops and dtypes must agree across the whole batch: one launch family
+    for (int t = 1; t < num_tensors; ++t) {
+        if ((*out)[t].dtype != (*out)[0].dtype)
+            return fail(RC_ERR_DTYPE_MISMATCH, fmt("all_reduce_many: tensor %lld dtype differs from tensor 0's", t));
+        if ((*out)[t].op != (*out)[0].op)
+            return fail(RC_ERR_OP_MISMATCH, fmt("all_reduce_many: tensor %lld op differs from tensor 0's", t));
+    }
+    std::vector<Range> writes, reads;
+    for (int t = 0; t < num_tensors; ++t)
+        if ((*out)[t].count) ranges_of((*out)[t], t, &writes, &reads);
+    Error e = check_overlaps(writes, reads);
+    if (e.code) e.msg = "all_reduce_many: " + e.msg;
+    return e;
+}
+
+}  // namespace rc
