@@ -124,9 +124,14 @@ typedef struct rc_buf {
  *   validate_only  nonzero: check arguments and return, never touch the GPU
  *                  (rc_register then makes no HIP call at all)
  *   tile_elems     elements per workgroup tile; 0: default; else a multiple
- *                  of 1024 in [1024, 65536]
- *   max_workgroups cap on the grid; 0: default (from the CU count)
- *   cache_hint     RC_CACHE_* */
+ *                  of 256 in [256, 65536]
+ *   max_workgroups 0: one workgroup per tile (batched all-reduce: a
+ *                  persistent grid sized from the CU count); > 0: a
+ *                  persistent grid of at most this many workgroups
+ *   cache_hint     RC_CACHE_*
+ *   waves_per_cu   cap on workgroups (one wave each) resident per compute
+ *                  unit, in [1, 32]; 0: the library's choice per collective
+ *   reserved       must be 0 */
 typedef struct rc_config {
     uint32_t struct_size;
     int32_t device;
@@ -135,6 +140,8 @@ typedef struct rc_config {
     int64_t tile_elems;
     int32_t max_workgroups;
     int32_t cache_hint;
+    int32_t waves_per_cu;
+    int32_t reserved;
 } rc_config;
 
 /* register<B> (ruCCL README, section 2; section 3 for the config): open the

@@ -76,6 +76,8 @@ class RcConfig(ctypes.Structure):
         ("tile_elems", ctypes.c_int64),
         ("max_workgroups", ctypes.c_int32),
         ("cache_hint", ctypes.c_int32),
+        ("waves_per_cu", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -148,7 +150,7 @@ def check(code):
 # ---------------------------------------------------------------- raw layer
 
 def make_config(device=-1, algo="auto", validate_only=False, tile_elems=0, max_workgroups=0,
-                cache_hint="auto"):
+                cache_hint="auto", waves_per_cu=0):
     cfg = RcConfig()
     cfg.struct_size = ctypes.sizeof(RcConfig)
     cfg.device = device
@@ -157,6 +159,7 @@ def make_config(device=-1, algo="auto", validate_only=False, tile_elems=0, max_w
     cfg.tile_elems = tile_elems
     cfg.max_workgroups = max_workgroups
     cfg.cache_hint = CACHE_HINTS[cache_hint] if isinstance(cache_hint, str) else int(cache_hint)
+    cfg.waves_per_cu = waves_per_cu
     return cfg
 
 
@@ -180,14 +183,14 @@ def make_bufs(sends, recvs, shape, dtype=RC_F32, op=RC_SUM, root=0):
 
 
 def register(num_ranks, device=None, algo="auto", validate_only=False, tile_elems=0,
-             max_workgroups=0, cache_hint="auto"):
+             max_workgroups=0, cache_hint="auto", waves_per_cu=0):
     """register<B>: open the process-wide session for num_ranks logical ranks."""
     if device is None:
         device = -1
     elif not isinstance(device, int):
         import torch
         device = torch.device(device).index if torch.device(device).index is not None else -1
-    cfg = make_config(device, algo, validate_only, tile_elems, max_workgroups, cache_hint)
+    cfg = make_config(device, algo, validate_only, tile_elems, max_workgroups, cache_hint, waves_per_cu)
     return check(library().rc_register(int(num_ranks), ctypes.byref(cfg)))
 
 

@@ -15,9 +15,9 @@
 
 namespace rc {
 
-hipError_t launch_jobs(const LaunchPlan& p, int grid, hipStream_t stream);
-hipError_t launch_batch(const BatchJob* jobs, int njobs, const void* const* ptrs, const BatchPlan& p,
-                        bool nt, int grid, hipStream_t stream);
+hipError_t launch_jobs(const LaunchPlan& p, hipStream_t stream);
+hipError_t launch_batch(const BatchJob* jobs, const int32_t* group_job, const void* const* ptrs,
+                        const BatchPlan& p, hipStream_t stream);
 
 namespace {
 
@@ -115,41 +115,50 @@ Error device_open(const Config& cfg, DeviceInfo* info) {
     info->device = dev;
     info->cu_count = prop.multiProcessorCount;
     info->l2_bytes = prop.l2CacheSize;
+    info->lds_per_cu = (int64_t)prop.maxSharedMemoryPerMultiProcessor;
+    info->max_lds_per_block = (int64_t)prop.sharedMemPerBlock;
     info->arch = arch;
     g.device = dev;
     g.next = 0;
     return {};
 }
 
-Error device_launch(const LaunchPlan& p, int grid, void* stream) {
+Error device_launch(const LaunchPlan& p, void* stream) {
     DeviceGuard guard;
     if (guard.err != hipSuccess) return hip_fail("hipSetDevice", guard.err);
-    hipError_t e = launch_jobs(p, grid, static_cast<hipStream_t>(stream));
+    hipError_t e = launch_jobs(p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail("kernel launch", e);
     return {};
 }
 
-Error device_launch_batch(const BatchPlan& p, int grid, void* stream) {
+Error device_launch_batch(const BatchPlan& p, void* stream) {
     if (p.jobs.empty()) return {};
     DeviceGuard guard;
     if (guard.err != hipSuccess) return hip_fail("hipSetDevice", guard.err);
     Arena& a = g.arena[g.next];
     Error err = wait_arena(a);
     if (err.code) return err;
+    // arena layout: [jobs][group index][pointer table], each 256-byte aligned
+    auto align = [](size_t v) { return (v + 255) & ~size_t(255); };
     const size_t job_bytes = p.jobs.size() * sizeof(BatchJob);
-    const size_t ptr_off = (job_bytes + 255) & ~size_t(255);
+    const size_t group_off = align(job_bytes);
+    const size_t group_bytes = p.group_job.size() * sizeof(int32_t);
+    const size_t ptr_off = align(group_off + group_bytes);
     const size_t bytes = ptr_off + p.ptrs.size() * sizeof(void*);
     err = ensure_arena(a, bytes);
     if (err.code) return err;
-    std::memcpy(a.host, p.jobs.data(), job_bytes);
-    std::memcpy(static_cast<char*>(a.host) + ptr_off, p.ptrs.data(), p.ptrs.size() * sizeof(void*));
+    char* host = static_cast<char*>(a.host);
+    std::memcpy(host, p.jobs.data(), job_bytes);
+    std::memcpy(host + group_off, p.group_job.data(), group_bytes);
+    std::memcpy(host + ptr_off, p.ptrs.data(), p.ptrs.size() * sizeof(void*));
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipMemcpyAsync(a.dev, a.host, bytes, hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return hip_fail("hipMemcpyAsync", e);
-    const BatchJob* jobs = static_cast<const BatchJob*>(a.dev);
-    const void* const* ptrs =
-        reinterpret_cast<const void* const*>(static_cast<const char*>(a.dev) + ptr_off);
-    e = launch_batch(jobs, (int)p.jobs.size(), ptrs, p, p.nontemporal != 0, grid, s);
+    const char* dev = static_cast<const char*>(a.dev);
+    const BatchJob* jobs = reinterpret_cast<const BatchJob*>(dev);
+    const int32_t* group_job = reinterpret_cast<const int32_t*>(dev + group_off);
+    const void* const* ptrs = reinterpret_cast<const void* const*>(dev + ptr_off);
+    e = launch_batch(jobs, group_job, ptrs, p, s);
     if (e != hipSuccess) return hip_fail("kernel launch", e);
     e = hipEventRecord(a.done, s);
     if (e != hipSuccess) return hip_fail("hipEventRecord", e);

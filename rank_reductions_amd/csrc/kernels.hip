@@ -263,36 +263,44 @@ __global__ __launch_bounds__(kBlock) void copy_kernel(JobArgs a) {
     }
 }
 
-// Batched all-reduce: every workgroup takes a contiguous range of tiles and
-// walks the job table from the job that holds its first tile.
-template <int NIN, class Op, int U, bool NT>
-__global__ __launch_bounds__(kBlock) void batch_kernel(const BatchJob* __restrict__ jobs, int njobs,
-                                                       const void* const* __restrict__ ptrs,
-                                                       int64_t total_tiles, int te, int mean) {
-    const int64_t per = (total_tiles + gridDim.x - 1) / gridDim.x;
-    const int64_t t0 = (int64_t)blockIdx.x * per;
-    const int64_t t1 = t0 + per < total_tiles ? t0 + per : total_tiles;
-    if (t0 >= t1) return;
-    int lo = 0, hi = njobs - 1;
+// Batched all-reduce over a job table in device memory.  A tile's job lies
+// between the jobs that hold the first tiles of its group and of the next
+// group (group_job); a binary search over that range, usually empty, finds it.
+struct BatchArgs {
+    const BatchJob* jobs;
+    const int32_t* group_job;
+    const void* const* ptrs;  // [job][2R]: fold operands in order, then outputs
+    int64_t total_tiles;
+    int64_t ngroups;
+    int32_t njobs;
+    int32_t tile_elems;
+    int32_t mean;
+};
+
+__device__ __forceinline__ int find_job(const BatchArgs& a, int64_t t) {
+    const int64_t g = t >> kGroupShift;
+    int lo = a.group_job[g];
+    int hi = g + 1 < a.ngroups ? a.group_job[g + 1] : a.njobs - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (jobs[mid].tile_begin <= t0) lo = mid;
+        if (a.jobs[mid].tile_begin <= t) lo = mid;
         else hi = mid - 1;
     }
-    int j = lo;
-    for (int64_t t = t0; t < t1; ++t) {
-        while (j + 1 < njobs && jobs[j + 1].tile_begin <= t) ++j;
-        const BatchJob jb = jobs[j];
-        const void* const* tp = ptrs + (int64_t)jb.tensor * 2 * NIN;
+    return lo;
+}
+
+template <int NIN, class Op, int U, bool NT>
+__global__ __launch_bounds__(kBlock) void batch_kernel(BatchArgs a) {
+    for (int64_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
+        const int j = find_job(a, t);
+        const BatchJob jb = a.jobs[j];
+        const void* const* tp = a.ptrs + (int64_t)j * 2 * NIN;
         const uint32_t* in[NIN];
 #pragma unroll
-        for (int k = 0; k < NIN; ++k)
-            in[k] = static_cast<const uint32_t*>(tp[(jb.c + 1 + k) % NIN]) + jb.start;
-        auto out = [&](int o) {
-            return static_cast<uint32_t*>(const_cast<void*>(tp[NIN + o])) + jb.start;
-        };
+        for (int k = 0; k < NIN; ++k) in[k] = static_cast<const uint32_t*>(tp[k]);
+        auto out = [&](int o) { return static_cast<uint32_t*>(const_cast<void*>(tp[NIN + o])); };
         job_tile<NIN, NIN, Op, U, NT>(in, out, (1u << NIN) - 1u, jb.len, jb.phase, t - jb.tile_begin,
-                                      te, mean != 0);
+                                      a.tile_elems, a.mean != 0);
     }
 }
 
@@ -302,7 +310,7 @@ template <int NIN>
 constexpr int kUnroll = unroll_for(NIN);
 
 using FoldFn = void (*)(JobArgs);
-using BatchFn = void (*)(const BatchJob*, int, const void* const*, int64_t, int, int);
+using BatchFn = void (*)(BatchArgs);
 
 template <int NIN, class Op, bool NT>
 FoldFn fold_ptr() { return fold_kernel<NIN, Op, kUnroll<NIN>, NT>; }
@@ -310,7 +318,7 @@ template <int NIN, class Op, bool NT>
 BatchFn batch_ptr() { return batch_kernel<NIN, Op, kUnroll<NIN>, NT>; }
 
 template <int NR, bool NT>
-FoldFn copy_ptr() { return copy_kernel<NR, kUnroll<1>, NT>; }
+FoldFn copy_ptr() { return copy_kernel<NR, kCopyUnroll, NT>; }
 
 template <bool NT>
 FoldFn pick_copy(int nranks) {
@@ -403,23 +411,32 @@ BatchFn pick_batch_op(int dtype, int op, int nin) {
 
 }  // namespace
 
-hipError_t launch_jobs(const LaunchPlan& p, int grid, hipStream_t stream) {
+hipError_t launch_jobs(const LaunchPlan& p, hipStream_t stream) {
     const bool nt = p.args.nontemporal != 0;
     FoldFn fn;
     if (p.args.in_mode == kInCopy) fn = nt ? pick_copy<true>(p.args.nranks) : pick_copy<false>(p.args.nranks);
     else fn = nt ? pick_fold_op<true>(p.dtype, p.op, p.nin) : pick_fold_op<false>(p.dtype, p.op, p.nin);
     if (!fn) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fn, dim3(grid), dim3(kBlock), 0, stream, p.args);
+    hipLaunchKernelGGL(fn, dim3(p.grid), dim3(kBlock), p.lds_bytes, stream, p.args);
     return hipGetLastError();
 }
 
-hipError_t launch_batch(const BatchJob* jobs, int njobs, const void* const* ptrs, const BatchPlan& p,
-                        bool nt, int grid, hipStream_t stream) {
+hipError_t launch_batch(const BatchJob* jobs, const int32_t* group_job, const void* const* ptrs,
+                        const BatchPlan& p, hipStream_t stream) {
+    const bool nt = p.nontemporal != 0;
     BatchFn fn = nt ? pick_batch_op<true>(p.dtype, p.op, p.nranks)
                     : pick_batch_op<false>(p.dtype, p.op, p.nranks);
     if (!fn) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fn, dim3(grid), dim3(kBlock), 0, stream, jobs, njobs, ptrs, p.total_tiles,
-                       p.tile_elems, p.op == RC_MEAN ? 1 : 0);
+    BatchArgs a;
+    a.jobs = jobs;
+    a.group_job = group_job;
+    a.ptrs = ptrs;
+    a.total_tiles = p.total_tiles;
+    a.ngroups = (int64_t)p.group_job.size();
+    a.njobs = (int32_t)p.jobs.size();
+    a.tile_elems = p.tile_elems;
+    a.mean = p.op == RC_MEAN ? 1 : 0;
+    hipLaunchKernelGGL(fn, dim3(p.grid), dim3(kBlock), p.lds_bytes, stream, a);
     return hipGetLastError();
 }
 

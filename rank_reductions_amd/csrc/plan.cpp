@@ -1,12 +1,22 @@
 // Chunk scheduler: turns a validated collective into launch plans - ring
-// segments (jobs), their alignment phase, tiles per job and the grid.
+// segments (jobs), their alignment phase, tiles per job, the grid and the
+// occupancy cap.
 //
 // Segmentation follows the ring of the ruCCL README (ja), "CUDA tensor
 // example": S = ceil(N/R) elements per segment, segment c owned by rank c and
 // folded in rank order (c+1), ..., c.  reduce_scatter_tensor and
 // all_gather_into_tensor (monarch Communicator page) use shards of M = N/R
 // elements, which are exactly those segments.  Host-only C++.
+//
+// Launch shape.  Every workgroup is one wave and takes one tile, and the
+// workgroups are dispatched in tile order, so the tiles in flight form one
+// compact window of each rank's buffers.  How many waves a CU holds at once is
+// capped through an LDS reservation: on MI355X, HBM efficiency for these
+// many-stream patterns peaks when about 128 KiB of traffic per CU is in
+// flight; more waves open more DRAM rows at once and lose bandwidth, fewer
+// leave it idle.
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <vector>
 
@@ -17,6 +27,7 @@ namespace rc {
 namespace {
 
 constexpr int64_t kMaxTileElems = 65536;
+constexpr double kInFlightKiBPerCU = 128.0;
 
 uintptr_t addr(const void* p, int64_t elem_off, int64_t esize) {
     return reinterpret_cast<uintptr_t>(p) + (uintptr_t)(elem_off * esize);
@@ -47,8 +58,8 @@ int nontemporal_of(const Config& cfg) {
 
 }  // namespace
 
-int tile_elems_for(int nin, const Config& cfg) {
-    const int64_t step = (int64_t)kBlock * kVec * unroll_for(nin);
+int tile_elems_for(int unroll, const Config& cfg) {
+    const int64_t step = (int64_t)kBlock * kVec * unroll;
     int64_t te = cfg.tile_elems > 0 ? cfg.tile_elems : step;
     te = ((te + step - 1) / step) * step;
     te = std::min<int64_t>(std::max<int64_t>(te, step), std::max<int64_t>(step, kMaxTileElems));
@@ -73,18 +84,35 @@ int64_t job_tiles(int64_t len, uint8_t phase, int64_t te) {
     return std::max<int64_t>(1, (body + te - 1) / te);
 }
 
-int grid_for(int64_t total_tiles, const Config& cfg, const DeviceInfo& dev) {
-    const int64_t cap = cfg.max_workgroups > 0 ? cfg.max_workgroups
-                                               : (int64_t)std::max(dev.cu_count, 1) * 8;
-    return (int)std::max<int64_t>(1, std::min(total_tiles, cap));
+int auto_waves_per_cu(int nin, int nout, int unroll) {
+    // each wave moves (nin + nout) * unroll KiB per round (64 lanes x 16 B)
+    const double kib_per_wave = (double)(nin + nout) * unroll;
+    const long w = std::lround(kInFlightKiBPerCU / std::max(kib_per_wave, 1.0));
+    return (int)std::min<long>(16, std::max<long>(2, w));
 }
 
-std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg) {
+void shape_launch(int64_t total_tiles, int nin, int nout, int unroll, const Config& cfg,
+                  const DeviceInfo& dev, int64_t* grid, int* lds_bytes) {
+    const int waves = cfg.waves_per_cu > 0 ? cfg.waves_per_cu : auto_waves_per_cu(nin, nout, unroll);
+    // One workgroup is one wave; reserving lds_per_cu / waves bytes of LDS per
+    // workgroup lets at most `waves` of them sit on a CU at a time.
+    int64_t lds = 0;
+    if (dev.lds_per_cu > 0 && waves < 32) {
+        lds = (dev.lds_per_cu / waves) / 512 * 512;
+        lds = std::min(lds, dev.max_lds_per_block);
+    }
+    *lds_bytes = (int)std::max<int64_t>(lds, 0);
+    int64_t g = total_tiles;
+    if (cfg.max_workgroups > 0) g = std::min<int64_t>(g, cfg.max_workgroups);
+    *grid = std::max<int64_t>(1, std::min<int64_t>(g, 0x7FFFFFFF));
+}
+
+std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceInfo& dev) {
     std::vector<LaunchPlan> out;
     if (ck.count == 0) return out;
     const int R = ck.nranks;
     const int64_t es = element_size(ck.dtype);
-    const uint32_t all = (R >= 32) ? 0xFFFFFFFFu : ((1u << R) - 1u);
+    const uint32_t all = (1u << R) - 1u;
 
     LaunchPlan p{};
     JobArgs& a = p.args;
@@ -97,6 +125,7 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg) {
     std::vector<std::vector<uintptr_t>> ad;
     auto fold_setup = [&](int64_t n, int64_t seg, int64_t in_stride, int64_t out_stride) {
         p.nin = R;
+        p.unroll = unroll_for(R);
         a.in_mode = kInFold;
         a.n = n;
         a.seg = seg;
@@ -104,11 +133,17 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg) {
         a.out_stride = out_stride;
         a.jobs = R;
         a.mean = ck.op == RC_MEAN;
-        a.tile_elems = tile_elems_for(R, cfg);
+        a.tile_elems = tile_elems_for(p.unroll, cfg);
         for (int r = 0; r < R; ++r) {
             a.in[r] = ck.send[r];
             a.out[r] = ck.recv[r];
         }
+    };
+    auto copy_setup = [&](LaunchPlan& q) {
+        q.nin = 1;
+        q.unroll = kCopyUnroll;
+        q.args.in_mode = kInCopy;
+        q.args.tile_elems = tile_elems_for(kCopyUnroll, cfg);
     };
     auto fold_addrs = [&](uint32_t mask_for_owner_only, bool owner_only) {
         ad.assign(R, {});
@@ -146,12 +181,11 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg) {
             LaunchPlan q{};
             JobArgs& b = q.args;
             b = JobArgs{};
-            q.nin = 1;
+            copy_setup(q);
             q.dtype = ck.dtype;
             q.op = ck.op;
             b.nranks = R;
             b.nontemporal = a.nontemporal;
-            b.in_mode = kInCopy;
             b.out_mode = kOutMaskButOwner;
             b.out_mask = all;
             b.n = ck.count;
@@ -159,7 +193,6 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg) {
             b.in_stride = S;
             b.out_stride = S;
             b.jobs = R;
-            b.tile_elems = tile_elems_for(1, cfg);
             for (int r = 0; r < R; ++r) {
                 b.in[r] = ck.recv[r];
                 b.out[r] = ck.recv[r];
@@ -183,15 +216,13 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg) {
         }
         case Coll::Broadcast: {
             const int s = ck.root;
-            p.nin = 1;
-            a.in_mode = kInCopy;
+            copy_setup(p);
             a.out_mode = kOutMask;
             a.n = ck.count;
             a.seg = ck.count;
             a.in_stride = 0;
             a.out_stride = 0;
             a.jobs = 1;
-            a.tile_elems = tile_elems_for(1, cfg);
             a.in[0] = ck.send[s];
             uint32_t mask = 0;
             for (int r = 0; r < R; ++r) {
@@ -210,8 +241,7 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg) {
         }
         case Coll::AllGather: {
             const int64_t M = ck.count;
-            p.nin = 1;
-            a.in_mode = kInCopy;
+            copy_setup(p);
             a.out_mode = kOutMask;
             a.out_mask = all;
             a.n = M * R;
@@ -219,7 +249,6 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg) {
             a.in_stride = 0;
             a.out_stride = M;
             a.jobs = R;
-            a.tile_elems = tile_elems_for(1, cfg);
             for (int r = 0; r < R; ++r) {
                 a.in[r] = ck.send[r];
                 a.out[r] = ck.recv[r];
@@ -235,48 +264,70 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg) {
             break;
         }
     }
+    for (LaunchPlan& lp : out) {
+        const JobArgs& ja = lp.args;
+        const int in_mask = __builtin_popcount(ja.out_mask);
+        lp.nout = ja.out_mode == kOutOwner ? 1 : in_mask - (ja.out_mode == kOutMaskButOwner ? 1 : 0);
+        shape_launch(lp.total_tiles, lp.nin, lp.nout, lp.unroll, cfg, dev, &lp.grid, &lp.lds_bytes);
+    }
     return out;
 }
 
-BatchPlan plan_batch(const std::vector<Checked>& tensors, const Config& cfg) {
+void split_batch(const std::vector<Checked>& tensors, std::vector<Checked>* own,
+                 std::vector<Checked>* batched) {
+    own->clear();
+    batched->clear();
+    for (const Checked& ck : tensors) {
+        if (ck.count == 0) continue;
+        const int64_t moved = 2 * (int64_t)ck.nranks * ck.count * element_size(ck.dtype);
+        (moved >= kOwnLaunchBytes ? own : batched)->push_back(ck);
+    }
+}
+
+BatchPlan plan_batch(const std::vector<Checked>& tensors, const Config& cfg, const DeviceInfo& dev) {
     BatchPlan bp;
     if (tensors.empty()) return bp;
     const int R = tensors[0].nranks;
+    const int unroll = unroll_for(R);
     bp.nranks = R;
     bp.dtype = tensors[0].dtype;
     bp.op = tensors[0].op;
-    bp.tile_elems = tile_elems_for(R, cfg);
+    bp.tile_elems = tile_elems_for(unroll, cfg);
     bp.nontemporal = nontemporal_of(cfg);
     const int64_t es = element_size(bp.dtype);
     int64_t tiles = 0;
-    int32_t t_index = 0;
     std::vector<uintptr_t> ad;
     ad.reserve(2 * R);
     for (const Checked& ck : tensors) {
         if (ck.count == 0) continue;
-        for (int r = 0; r < R; ++r) bp.ptrs.push_back(ck.send[r]);
-        for (int r = 0; r < R; ++r) bp.ptrs.push_back(ck.recv[r]);
         const int64_t S = (ck.count + R - 1) / R;
         for (int c = 0; c < R; ++c) {
             const int64_t start = (int64_t)c * S;
             const int64_t len = std::min(S, ck.count - start);
             if (len <= 0) continue;
             ad.clear();
-            for (int r = 0; r < R; ++r) ad.push_back(addr(ck.send[r], start, es));
+            for (int k = 0; k < R; ++k) ad.push_back(addr(ck.send[(c + 1 + k) % R], start, es));
             for (int r = 0; r < R; ++r) ad.push_back(addr(ck.recv[r], start, es));
             BatchJob j{};
             j.tile_begin = tiles;
-            j.start = start;
             j.len = len;
-            j.tensor = t_index;
-            j.c = c;
             j.phase = job_phase(ad.data(), (int)ad.size(), es, len);
             tiles += job_tiles(len, (uint8_t)j.phase, bp.tile_elems);
             bp.jobs.push_back(j);
+            for (uintptr_t a : ad) bp.ptrs.push_back(reinterpret_cast<const void*>(a));
         }
-        ++t_index;
     }
     bp.total_tiles = tiles;
+    // group index: the job holding the first tile of every group of 2^kGroupShift tiles
+    const int64_t groups = (tiles + (int64_t(1) << kGroupShift) - 1) >> kGroupShift;
+    bp.group_job.resize(groups);
+    size_t j = 0;
+    for (int64_t g = 0; g < groups; ++g) {
+        const int64_t t = g << kGroupShift;
+        while (j + 1 < bp.jobs.size() && bp.jobs[j + 1].tile_begin <= t) ++j;
+        bp.group_job[g] = (int32_t)j;
+    }
+    shape_launch(tiles, R, R, unroll, cfg, dev, &bp.grid, &bp.lds_bytes);
     return bp;
 }
 

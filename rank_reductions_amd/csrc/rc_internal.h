@@ -13,7 +13,7 @@
 namespace rc {
 
 constexpr int kMaxRanks = RC_MAX_RANKS;
-constexpr int kBlock = 256;          // threads per workgroup (4 wave64s)
+constexpr int kBlock = 64;           // threads per workgroup: one wave64
 constexpr int kVec = 4;              // elements per 16-byte vector
 constexpr uint8_t kScalarOnly = 0xFF;  // job phase: pointers not co-aligned
 
@@ -54,13 +54,12 @@ struct JobArgs {
     uint8_t phase[kMaxRanks];            // leading scalar elements, or kScalarOnly
 };
 
-// One segment of one tensor in a batched all-reduce (device descriptor).
+// One segment of one tensor in a batched all-reduce (device descriptor).  Its
+// 2R pointers sit in a parallel table: the R fold operands in fold order,
+// then the R outputs, all already offset to the segment's first element.
 struct BatchJob {
     int64_t tile_begin;  // first tile of this job in the launch's tile space
-    int64_t start;       // element offset of the segment in its tensor
     int64_t len;         // elements in the segment (> 0)
-    int32_t tensor;      // index into the pointer table
-    int32_t c;           // segment index (sets the fold rotation)
     int32_t phase;       // leading scalar elements, or kScalarOnly
     int32_t pad;
 };
@@ -69,6 +68,8 @@ struct DeviceInfo {
     int device = 0;
     int cu_count = 0;
     int64_t l2_bytes = 0;
+    int64_t lds_per_cu = 0;         // bytes of LDS per compute unit
+    int64_t max_lds_per_block = 0;  // largest dynamic LDS one workgroup may take
     std::string arch;
 };
 
@@ -79,6 +80,7 @@ struct Config {
     int64_t tile_elems = 0;
     int max_workgroups = 0;
     int cache_hint = RC_CACHE_AUTO;
+    int waves_per_cu = 0;
 };
 
 // Result of validating one collective call.
@@ -106,11 +108,16 @@ Error validate_batch(int nranks, int num_tensors, const rc_buf* bufs,
 int64_t element_size(int dtype);
 
 // ---------------------------------------------------------------- plan.cpp
-// Unroll (16-byte vectors per lane per round) for a job's input count: about
-// 16 vector loads in flight per lane.  Shared by the planner and the kernels.
-constexpr int unroll_for(int nin) { return nin >= 16 ? 1 : (nin >= 8 ? 2 : 4); }
-// Elements per tile for a job's input count under the session's config.
-int tile_elems_for(int nin, const Config& cfg);
+// Unroll (16-byte vectors per lane per round) of a fold of `nin` inputs: about
+// eight vector loads in flight per lane.  Shared by the planner and kernels.
+constexpr int unroll_for(int nin) { return nin >= 8 ? 1 : (nin >= 4 ? 2 : (nin >= 2 ? 4 : 8)); }
+// Unroll of the copy kernel (one input, up to 16 outputs per element).
+constexpr int kCopyUnroll = 2;
+// Tiles of the batched all-reduce are indexed in groups of 2^kGroupShift: the
+// kernel finds a tile's job from its group's first job.
+constexpr int kGroupShift = 8;
+// Elements per tile for a kernel of the given unroll under the session's config.
+int tile_elems_for(int unroll, const Config& cfg);
 // Job phase: number of scalar elements before every pointer is 16-byte
 // aligned, or kScalarOnly when the pointers disagree modulo 16 bytes.
 uint8_t job_phase(const uintptr_t* addrs, int naddrs, int64_t elem_size, int64_t len);
@@ -120,35 +127,54 @@ int64_t job_tiles(int64_t len, uint8_t phase, int64_t tile_elems);
 struct LaunchPlan {
     JobArgs args;
     int nin = 1;             // inputs folded per element (1 = copy)
+    int nout = 1;            // outputs written per element
+    int unroll = 1;          // vectors per lane per round of the kernel
     int dtype = RC_F32;
     int op = RC_SUM;
     int64_t total_tiles = 0;
+    int64_t grid = 0;        // workgroups launched
+    int lds_bytes = 0;       // dynamic LDS per workgroup: caps workgroups per CU
 };
 
 // Builds the launches of one validated call: one for most collectives, two
 // for the ring all-reduce.  Empty when there is nothing to do.
-std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg);
+std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceInfo& dev);
 
 // Batched all-reduce: job and pointer tables for tensors [t0, t1).
 struct BatchPlan {
     std::vector<BatchJob> jobs;
-    std::vector<const void*> ptrs;  // [tensor][2R]: R inputs, then R outputs
+    std::vector<const void*> ptrs;  // [job][2R]: fold operands in order, then outputs
+    std::vector<int32_t> group_job;  // job holding tile g << kGroupShift, per group g
     int64_t total_tiles = 0;
     int tile_elems = 0;
     int nranks = 0;
     int dtype = RC_F32;
     int op = RC_SUM;
     int nontemporal = 1;
+    int64_t grid = 0;
+    int lds_bytes = 0;
 };
-BatchPlan plan_batch(const std::vector<Checked>& tensors, const Config& cfg);
+BatchPlan plan_batch(const std::vector<Checked>& tensors, const Config& cfg, const DeviceInfo& dev);
 
-int grid_for(int64_t total_tiles, const Config& cfg, const DeviceInfo& dev);
+// A batched all-reduce splits into tensors large enough to run as launches of
+// their own (their kernel time dwarfs a launch boundary, and they avoid the
+// batched kernel's per-tile job lookup) and the rest, batched into one launch.
+constexpr int64_t kOwnLaunchBytes = int64_t(64) << 20;  // HBM bytes moved per tensor
+void split_batch(const std::vector<Checked>& tensors, std::vector<Checked>* own,
+                 std::vector<Checked>* batched);
+
+// Workgroups resident per CU that keep HBM busiest for a kernel streaming
+// `nin` inputs and `nout` outputs per element with `unroll` vectors per lane.
+int auto_waves_per_cu(int nin, int nout, int unroll);
+// Grid and LDS reservation of a launch of `total_tiles` tiles.
+void shape_launch(int64_t total_tiles, int nin, int nout, int unroll, const Config& cfg,
+                  const DeviceInfo& dev, int64_t* grid, int* lds_bytes);
 
 // ---------------------------------------------------------------- device.hip
 // All return RC_OK or RC_ERR_DEVICE with a message.
 Error device_open(const Config& cfg, DeviceInfo* info);
-Error device_launch(const LaunchPlan& p, int grid, void* stream);
-Error device_launch_batch(const BatchPlan& p, int grid, void* stream);
+Error device_launch(const LaunchPlan& p, void* stream);
+Error device_launch_batch(const BatchPlan& p, void* stream);
 Error device_finish();   // wait for the GPU, free scratch
 void device_reset();     // wait for kernels reading scratch, free scratch
 

@@ -48,18 +48,22 @@ Error read_config(const rc_config* in, Config* cfg) {
         return Error{RC_ERR_INVALID_ARGUMENT, "rc_register: unknown algo"};
     if (in->cache_hint < RC_CACHE_AUTO || in->cache_hint > RC_CACHE_NORMAL)
         return Error{RC_ERR_INVALID_ARGUMENT, "rc_register: unknown cache_hint"};
-    if (in->tile_elems < 0 || in->tile_elems > 65536 || in->tile_elems % 1024 != 0)
+    if (in->tile_elems < 0 || in->tile_elems > 65536 || in->tile_elems % 256 != 0)
         return Error{RC_ERR_INVALID_ARGUMENT,
-                     "rc_register: tile_elems must be 0 or a multiple of 1024 up to 65536"};
+                     "rc_register: tile_elems must be 0 or a multiple of 256 up to 65536"};
     if (in->max_workgroups < 0)
         return Error{RC_ERR_INVALID_ARGUMENT, "rc_register: max_workgroups is negative"};
+    if (in->waves_per_cu < 0 || in->waves_per_cu > 32)
+        return Error{RC_ERR_INVALID_ARGUMENT, "rc_register: waves_per_cu must be in [0, 32]"};
     if (in->device < -1) return Error{RC_ERR_INVALID_ARGUMENT, "rc_register: device < -1"};
+    if (in->reserved != 0) return Error{RC_ERR_INVALID_ARGUMENT, "rc_register: reserved must be 0"};
     cfg->device = in->device;
     cfg->algo = in->algo;
     cfg->validate_only = in->validate_only != 0;
     cfg->tile_elems = in->tile_elems;
     cfg->max_workgroups = in->max_workgroups;
     cfg->cache_hint = in->cache_hint;
+    cfg->waves_per_cu = in->waves_per_cu;
     return {};
 }
 
@@ -71,8 +75,8 @@ int collective(Coll coll, const rc_buf* bufs, void* stream) {
     Error e = validate(coll, g_s.nranks, bufs, &ck);
     if (e.code) return report(e);
     if (g_s.cfg.validate_only) return ok();
-    for (const LaunchPlan& p : plan(ck, g_s.cfg)) {
-        e = device_launch(p, grid_for(p.total_tiles, g_s.cfg, g_s.dev), stream);
+    for (const LaunchPlan& p : plan(ck, g_s.cfg, g_s.dev)) {
+        e = device_launch(p, stream);
         if (e.code) return report(e);
     }
     return ok();
@@ -122,9 +126,17 @@ int rc_all_reduce_many(int num_tensors, const rc_buf* bufs, void* stream) {
     Error e = validate_batch(g_s.nranks, num_tensors, bufs, &cks);
     if (e.code) return report(e);
     if (g_s.cfg.validate_only) return ok();
-    const BatchPlan bp = plan_batch(cks, g_s.cfg);
+    std::vector<Checked> own, batched;
+    split_batch(cks, &own, &batched);
+    for (const Checked& ck : own) {
+        for (const LaunchPlan& p : plan(ck, g_s.cfg, g_s.dev)) {
+            e = device_launch(p, stream);
+            if (e.code) return report(e);
+        }
+    }
+    const BatchPlan bp = plan_batch(batched, g_s.cfg, g_s.dev);
     if (bp.total_tiles == 0) return ok();
-    e = device_launch_batch(bp, grid_for(bp.total_tiles, g_s.cfg, g_s.dev), stream);
+    e = device_launch_batch(bp, stream);
     return report(e);
 }
 

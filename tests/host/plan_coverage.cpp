@@ -1,0 +1,275 @@
+// Replays, on the CPU, the index arithmetic the kernels apply to a launch plan
+// (job lookup, scalar head, 16-byte vector body in rounds, scalar tail, the
+// element-by-element path and the batched group lookup) and checks that every
+// element of every job is produced exactly once and that every address read
+// or written lies inside the buffer it belongs to.  Links the host-only
+// planner and validator; no GPU involved.
+#include <algorithm>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <random>
+#include <string>
+#include <vector>
+
+#include "rc_internal.h"
+
+using namespace rc;
+
+namespace {
+
+struct Buffer {
+    uintptr_t lo, hi;
+};
+
+std::vector<Buffer> g_bufs;
+int g_fail = 0;
+
+void fail(const std::string& what) {
+    if (g_fail < 20) std::fprintf(stderr, "FAIL: %s\n", what.c_str());
+    ++g_fail;
+}
+
+// buffers are allocated at increasing addresses, so g_bufs is sorted by lo
+bool inside(uintptr_t a, int64_t bytes) {
+    auto it = std::upper_bound(g_bufs.begin(), g_bufs.end(), a,
+                               [](uintptr_t v, const Buffer& b) { return v < b.lo; });
+    if (it == g_bufs.begin()) return false;
+    --it;
+    return a >= it->lo && a + (uintptr_t)bytes <= it->hi;
+}
+
+// Enumerate the elements tile lt of a job touches, as job_tile does.
+template <class F>
+void tile_elements(int64_t len, int phase, int64_t lt, int64_t te, int unroll, F&& visit) {
+    if (phase == kScalarOnly) {
+        const int64_t e0 = lt * te, e1 = std::min(e0 + te, len);
+        for (int tid = 0; tid < kBlock; ++tid)
+            for (int64_t e = e0 + tid; e < e1; e += kBlock) visit(e, 4);
+        return;
+    }
+    const int64_t head = std::min<int64_t>(phase, len);
+    const int64_t nvec = (len - head) / kVec;
+    const int64_t tail0 = head + nvec * kVec;
+    const int64_t tv = te / kVec;
+    const int64_t v0 = lt * tv, v1 = std::min(v0 + tv, nvec);
+    const int64_t step = (int64_t)kBlock * unroll;
+    for (int64_t vb = v0; vb < v1; vb += step)
+        for (int u = 0; u < unroll; ++u)
+            for (int tid = 0; tid < kBlock; ++tid) {
+                const int64_t v = vb + (int64_t)u * kBlock + tid;
+                if (v < v1) visit(head + v * kVec, 16);
+            }
+    if (lt == 0) {
+        const int64_t nscal = head + (len - tail0);
+        for (int tid = 0; tid < kBlock; ++tid)
+            if (tid < nscal) visit(tid < head ? tid : tail0 + (tid - head), 4);
+    }
+}
+
+void check_plan(const LaunchPlan& p, const std::string& name) {
+    const JobArgs& a = p.args;
+    if (a.tile_elems % (kBlock * kVec * p.unroll)) fail(name + ": tile not a multiple of a round");
+    if (p.grid < 1 || p.grid > 0x7FFFFFFF) fail(name + ": grid out of range");
+    std::vector<std::vector<uint8_t>> seen(a.jobs);
+    for (int c = 0; c < a.jobs; ++c)
+        seen[c].assign((size_t)std::max<int64_t>(0, std::min(a.seg, a.n - (int64_t)c * a.seg)), 0);
+    const int64_t total = a.tile_prefix[a.jobs];
+    for (int64_t t = 0; t < total; ++t) {
+        int c = 0;
+        while (t >= a.tile_prefix[c + 1]) ++c;
+        if (c >= a.jobs) {
+            fail(name + ": job index past the last job");
+            return;
+        }
+        const int64_t lt = t - a.tile_prefix[c];
+        const int64_t start = (int64_t)c * a.seg;
+        const int64_t len = std::min(a.seg, a.n - start);
+        uint32_t mask = a.out_mask;
+        if (a.out_mode == kOutOwner) mask = 1u << c;
+        else if (a.out_mode == kOutMaskButOwner) mask &= ~(1u << c);
+        tile_elements(len, a.phase[c], lt, a.tile_elems, p.unroll, [&](int64_t e, int bytes) {
+            const int n = bytes / 4;
+            for (int i = 0; i < n; ++i) {
+                if (e + i < 0 || e + i >= len) fail(name + ": element outside its job");
+                else seen[c][e + i] += 1;
+            }
+            if (bytes == 16 && e % kVec != (a.phase[c] % kVec) % kVec) {
+                // vector accesses start at head + 4v: aligned by construction
+            }
+            if (a.in_mode == kInFold) {
+                for (int k = 0; k < p.nin; ++k) {
+                    const uintptr_t base = (uintptr_t)a.in[(c + 1 + k) % p.nin] + (uintptr_t)(c * a.in_stride * 4);
+                    const uintptr_t ad = base + (uintptr_t)(e * 4);
+                    if (!inside(ad, bytes)) fail(name + ": input read outside its buffer");
+                    if (bytes == 16 && ad % 16) fail(name + ": misaligned vector read");
+                }
+            } else {
+                const uintptr_t ad = (uintptr_t)a.in[c] + (uintptr_t)(c * a.in_stride * 4) + (uintptr_t)(e * 4);
+                if (!inside(ad, bytes)) fail(name + ": copy read outside its buffer");
+                if (bytes == 16 && ad % 16) fail(name + ": misaligned vector read");
+            }
+            for (int o = 0; o < a.nranks; ++o) {
+                if (!((mask >> o) & 1u)) continue;
+                const uintptr_t ad = (uintptr_t)a.out[o] + (uintptr_t)(c * a.out_stride * 4) + (uintptr_t)(e * 4);
+                if (!inside(ad, bytes)) fail(name + ": write outside its buffer");
+                if (bytes == 16 && ad % 16) fail(name + ": misaligned vector write");
+            }
+        });
+    }
+    for (int c = 0; c < a.jobs; ++c) {
+        const int64_t len = std::max<int64_t>(0, std::min(a.seg, a.n - (int64_t)c * a.seg));
+        for (int64_t e = 0; e < len; ++e) {
+            if (seen[c][e] != 1) {
+                fail(name + ": job " + std::to_string(c) + " element " + std::to_string(e) + " produced " +
+                     std::to_string(seen[c][e]) + " times");
+                return;
+            }
+        }
+    }
+}
+
+uintptr_t g_next = 0x100000;
+
+uintptr_t alloc(int64_t bytes, int misalign_elems) {
+    const uintptr_t a = (g_next + 255) / 256 * 256 + (uintptr_t)misalign_elems * 4;
+    g_next = a + (uintptr_t)bytes + 4096;
+    g_bufs.push_back({a, a + (uintptr_t)bytes});
+    return a;
+}
+
+rc_buf make(const void* s, void* r, int64_t n, int op = RC_SUM, int root = 0) {
+    rc_buf b{};
+    b.send = s;
+    b.recv = r;
+    b.dtype = RC_F32;
+    b.op = op;
+    b.root = root;
+    b.ndim = 1;
+    b.dims[0] = n;
+    return b;
+}
+
+}  // namespace
+
+int main(int argc, char** argv) {
+    const int iters = argc > 1 ? std::atoi(argv[1]) : 300;
+    std::mt19937_64 rng(12345);
+    DeviceInfo dev;
+    dev.cu_count = 256;
+    dev.lds_per_cu = 160 * 1024;
+    dev.max_lds_per_block = 64 * 1024;
+    int plans = 0;
+    for (int it = 0; it < iters; ++it) {
+        g_bufs.clear();
+        const int R = 1 + (int)(rng() % 16);
+        const int sizes[] = {0, 1, 2, 3, 5, 7, 64, 255, 256, 257, 1000, 4099, 20000, 65537};
+        int64_t n = sizes[rng() % 14];
+        if (rng() % 3 == 0) n = (int64_t)(rng() % 50000);
+        Config cfg;
+        cfg.algo = rng() % 2 ? RC_ALGO_RING : RC_ALGO_DIRECT;
+        const int64_t tiles[] = {0, 0, 256, 1024, 4096};
+        cfg.tile_elems = tiles[rng() % 5];
+        cfg.max_workgroups = rng() % 3 == 0 ? (int)(1 + rng() % 50) : 0;
+        cfg.waves_per_cu = (int)(rng() % 9);
+        const int mis_mode = (int)(rng() % 3);  // 0 aligned, 1 common offset, 2 mixed offsets
+        auto mis = [&](int r) { return mis_mode == 0 ? 0 : (mis_mode == 1 ? 1 + (int)(it % 3) : (r * 3 + it) % 4); };
+        const int coll = (int)(rng() % 5);
+        std::vector<rc_buf> bufs(R);
+        if (coll == 3) n = (n / R) * R;  // reduce_scatter needs R | n
+        for (int r = 0; r < R; ++r) {
+            const int64_t out_n = coll == 3 ? n / R : (coll == 4 ? n * R : n);
+            void* s = (void*)alloc(std::max<int64_t>(n, 1) * 4, mis(r));
+            void* o = (void*)alloc(std::max<int64_t>(out_n, 1) * 4, mis(r + 1));
+            bufs[r] = make(s, o, n, RC_SUM, coll == 2 ? -1 : (int)(it % R));
+        }
+        Coll kind = Coll::AllReduce;
+        if (coll == 1) kind = Coll::Reduce;
+        if (coll == 2) {
+            kind = Coll::Broadcast;
+            for (int r = 0; r < R; ++r)
+                if (r != (int)(it % R)) bufs[r].send = nullptr;
+        }
+        if (coll == 3) kind = Coll::ReduceScatter;
+        if (coll == 4) kind = Coll::AllGather;
+        Checked ck;
+        Error e = validate(kind, R, bufs.data(), &ck);
+        if (e.code) {
+            fail("validation rejected a valid call: " + e.msg);
+            continue;
+        }
+        for (const LaunchPlan& p : plan(ck, cfg, dev)) {
+            check_plan(p, "coll " + std::to_string(coll) + " R=" + std::to_string(R) + " n=" + std::to_string(n) +
+                              " mis=" + std::to_string(mis_mode));
+            ++plans;
+        }
+    }
+    // batched plans: job lookup through the group index, and coverage
+    int batches = 0;
+    for (int it = 0; it < iters / 3; ++it) {
+        g_bufs.clear();
+        const int R = 1 + (int)(rng() % 8);
+        const int T = 1 + (int)(rng() % 40);
+        std::vector<rc_buf> rows;
+        for (int t = 0; t < T; ++t) {
+            int64_t n = (int64_t)(rng() % 4) == 0 ? (int64_t)(rng() % 300000) : (int64_t)(rng() % 700);
+            const int mis_mode = (int)(rng() % 3);
+            for (int r = 0; r < R; ++r) {
+                const int m = mis_mode == 0 ? 0 : (mis_mode == 1 ? 2 : (r + t) % 4);
+                void* s = (void*)alloc(std::max<int64_t>(n, 1) * 4, m);
+                void* o = (void*)alloc(std::max<int64_t>(n, 1) * 4, m);
+                rows.push_back(make(s, o, n, RC_MEAN));
+            }
+        }
+        std::vector<Checked> cks;
+        Error e = validate_batch(R, T, rows.data(), &cks);
+        if (e.code) {
+            fail("batch validation rejected a valid call: " + e.msg);
+            continue;
+        }
+        Config cfg;
+        cfg.waves_per_cu = (int)(rng() % 9);
+        const BatchPlan bp = plan_batch(cks, cfg, dev);
+        const int unroll = unroll_for(R);
+        std::vector<std::vector<uint8_t>> seen(bp.jobs.size());
+        for (size_t j = 0; j < bp.jobs.size(); ++j) seen[j].assign((size_t)bp.jobs[j].len, 0);
+        const int64_t ngroups = (int64_t)bp.group_job.size();
+        for (int64_t t = 0; t < bp.total_tiles; ++t) {
+            const int64_t g = t >> kGroupShift;
+            if (g >= ngroups) {
+                fail("group index out of range");
+                break;
+            }
+            int lo = bp.group_job[g];
+            int hi = g + 1 < ngroups ? bp.group_job[g + 1] : (int)bp.jobs.size() - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (bp.jobs[mid].tile_begin <= t) lo = mid;
+                else hi = mid - 1;
+            }
+            const BatchJob& jb = bp.jobs[lo];
+            const int64_t next = lo + 1 < (int)bp.jobs.size() ? bp.jobs[lo + 1].tile_begin : bp.total_tiles;
+            if (!(jb.tile_begin <= t && t < next)) fail("group lookup found the wrong job");
+            tile_elements(jb.len, jb.phase, t - jb.tile_begin, bp.tile_elems, unroll, [&](int64_t e, int bytes) {
+                for (int i = 0; i < bytes / 4; ++i) {
+                    if (e + i >= jb.len) fail("batched element outside its job");
+                    else seen[lo][e + i] += 1;
+                }
+                for (int k = 0; k < 2 * R; ++k) {
+                    const uintptr_t ad = (uintptr_t)bp.ptrs[(size_t)lo * 2 * R + k] + (uintptr_t)(e * 4);
+                    if (!inside(ad, bytes)) fail("batched access outside its buffer");
+                    if (bytes == 16 && ad % 16) fail("batched misaligned vector access");
+                }
+            });
+        }
+        for (size_t j = 0; j < bp.jobs.size(); ++j)
+            for (int64_t e = 0; e < bp.jobs[j].len; ++e)
+                if (seen[j][e] != 1) {
+                    fail("batched job element not produced exactly once");
+                    break;
+                }
+        ++batches;
+    }
+    std::printf("checked %d plans and %d batches: %d failures\n", plans, batches, g_fail);
+    return g_fail ? 1 : 0;
+}

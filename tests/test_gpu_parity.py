@@ -360,6 +360,21 @@ def test_all_reduce_many(R, dtype, op):
                 assert_bits(host(single[r]), host(outs[t][r]), f"batched == single, tensor {t}")
 
 
+@pytest.mark.parametrize("R", [2, 4, 8])
+def test_all_reduce_many_mixed_sizes(R):
+    """Large tensors run as launches of their own and small ones in one batched
+    launch; both kinds in one call, every tensor equal to the oracle."""
+    shapes = [(257,), (2_200_000,), (64, 33), (1_100_000, 3), (4096,), (1,)]
+    tensors = _batch(R, shapes, seed=50 + R)
+    with session(R):
+        outs = rr.all_reduce_many(tensors, "mean")
+        sync()
+        for t, per in enumerate(tensors):
+            want = oracle.all_reduce_closed_form([host(x) for x in per], "mean")
+            for r in range(R):
+                assert_bits(host(outs[t][r]), want, f"tensor {t} {shapes[t]} rank {r}")
+
+
 def test_all_reduce_many_misaligned_and_repeated():
     """Tensors carved out of one buffer at odd offsets, and several batched
     calls in a row (the descriptor arena alternates and grows)."""
