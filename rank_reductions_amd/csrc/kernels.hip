@@ -124,9 +124,23 @@ __device__ __forceinline__ void st1(uint32_t* p, uint32_t v) {
 }
 
 // ---------------------------------------------------------------- one job
+//
+// in[k] is the k-th operand of the fold at the job's first element (the ring
+// order of the job's segment); out(o) is rank o's output at that element.
 
-// Output addressing: out(o) is rank o's output at the job's first element.
-// Inputs: in[k] is the k-th operand of the fold at the job's first element.
+template <class Op>
+__device__ __forceinline__ uint32_t op2(uint32_t a, uint32_t b) { return Op::apply(a, b); }
+template <class Op>
+__device__ __forceinline__ u32x4 op2(u32x4 a, u32x4 b) { return Op::apply4(a, b); }
+
+// Left fold of the operands in the order given.
+template <int NIN, class Op, class V>
+__device__ __forceinline__ V fold(const V (&x)[NIN]) {
+    V acc = x[0];
+#pragma unroll
+    for (int k = 1; k < NIN; ++k) acc = op2<Op>(acc, x[k]);
+    return acc;
+}
 
 template <int NIN, int NR, class Op, bool NT, class OutF>
 __device__ __forceinline__ void element(const uint32_t* const (&in)[NIN], int64_t e,
@@ -134,9 +148,7 @@ __device__ __forceinline__ void element(const uint32_t* const (&in)[NIN], int64_
     uint32_t x[NIN];
 #pragma unroll
     for (int k = 0; k < NIN; ++k) x[k] = ld1<NT>(in[k] + e);
-    uint32_t acc = x[0];
-#pragma unroll
-    for (int k = 1; k < NIN; ++k) acc = Op::apply(acc, x[k]);
+    uint32_t acc = fold<NIN, Op>(x);
     if constexpr (Op::kCanMean) {
         if (mean) acc = mean1<NIN>(acc);
     }
@@ -145,29 +157,28 @@ __device__ __forceinline__ void element(const uint32_t* const (&in)[NIN], int64_
         if ((mask >> o) & 1u) st1<NT>(out(o) + e, acc);
 }
 
-// One round of U vectors per lane over vector indices [vb, vb + kBlock*U),
-// clipped to v1 unless FULL.  `base` is the element offset of vector 0.
+// One round: U vectors per lane.  in[k] + off and out(o) + off are uniform
+// (the round's first element); lane vectors sit at 32-bit offsets from there.
+// Unless FULL, only the first `nv` vectors of the round exist.
 template <int NIN, int NR, class Op, int U, bool NT, bool FULL, class OutF>
-__device__ __forceinline__ void vec_round(const uint32_t* const (&in)[NIN], int64_t base, int64_t vb,
-                                          int64_t v1, const OutF& out, uint32_t mask, bool mean) {
-    const int tid = threadIdx.x;
+__device__ __forceinline__ void vec_round(const uint32_t* const (&in)[NIN], int64_t off,
+                                          uint32_t nv, const OutF& out, uint32_t mask, bool mean) {
+    const uint32_t tid = threadIdx.x;
     u32x4 x[U][NIN];
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int64_t v = vb + u * kBlock + tid;
-        ok[u] = FULL || v < v1;
+        const uint32_t v = (uint32_t)u * kBlock + tid;
+        ok[u] = FULL || v < nv;
         if (ok[u]) {
 #pragma unroll
-            for (int k = 0; k < NIN; ++k) x[u][k] = ld4<NT>(in[k] + base + v * kVec);
+            for (int k = 0; k < NIN; ++k) x[u][k] = ld4<NT>((in[k] + off) + (size_t)(v * kVec));
         }
     }
     u32x4 acc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        acc[u] = x[u][0];
-#pragma unroll
-        for (int k = 1; k < NIN; ++k) acc[u] = Op::apply4(acc[u], x[u][k]);
+        acc[u] = fold<NIN, Op>(x[u]);
         if constexpr (Op::kCanMean) {
             if (mean) acc[u] = mean4<NIN>(acc[u]);
         }
@@ -175,11 +186,11 @@ __device__ __forceinline__ void vec_round(const uint32_t* const (&in)[NIN], int6
 #pragma unroll
     for (int o = 0; o < NR; ++o) {
         if (!((mask >> o) & 1u)) continue;
-        uint32_t* p = out(o) + base;
+        uint32_t* p = out(o) + off;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t v = vb + u * kBlock + tid;
-            if (FULL || ok[u]) st4<NT>(p + v * kVec, acc[u]);
+            const uint32_t v = (uint32_t)u * kBlock + tid;
+            if (FULL || ok[u]) st4<NT>(p + (size_t)(v * kVec), acc[u]);
         }
     }
 }
@@ -204,11 +215,12 @@ __device__ __forceinline__ void job_tile(const uint32_t* const (&in)[NIN], const
     const int64_t v0 = lt * tv;
     const int64_t v1 = v0 + tv < nvec ? v0 + tv : nvec;
     constexpr int64_t kStep = (int64_t)kBlock * U;
-    int64_t vb = v0;
-    for (; vb + kStep <= v1; vb += kStep)
-        vec_round<NIN, NR, Op, U, NT, true>(in, head, vb, v1, out, mask, mean);
-    if (vb < v1) vec_round<NIN, NR, Op, U, NT, false>(in, head, vb, v1, out, mask, mean);
-    if (lt == 0) {
+    for (int64_t vb = v0; vb < v1; vb += kStep) {
+        const int64_t off = head + vb * kVec;
+        if (v1 - vb >= kStep) vec_round<NIN, NR, Op, U, NT, true>(in, off, 0, out, mask, mean);
+        else vec_round<NIN, NR, Op, U, NT, false>(in, off, (uint32_t)(v1 - vb), out, mask, mean);
+    }
+    if (lt == 0 && (head > 0 || tail0 < len)) {
         const int64_t nscal = head + (len - tail0);  // at most 3 + 3
         if (tid < nscal) {
             const int64_t e = tid < head ? tid : tail0 + (tid - head);
@@ -219,26 +231,42 @@ __device__ __forceinline__ void job_tile(const uint32_t* const (&in)[NIN], const
 
 // ---------------------------------------------------------------- kernels
 
+// Job holding tile t: the number of job boundaries at or below t.  Entries of
+// tile_prefix past the last job equal the tile total, which t never reaches.
+__device__ __forceinline__ int job_of(const JobArgs& a, int t) {
+    int c = 0;
+#pragma unroll
+    for (int j = 1; j < kMaxRanks; ++j) c += t >= a.tile_prefix[j] ? 1 : 0;
+    return c;
+}
+
+__device__ __forceinline__ uint32_t out_mask_of(const JobArgs& a, int c) {
+    uint32_t mask = a.out_mask;
+    if (a.out_mode == kOutOwner) mask = 1u << c;
+    else if (a.out_mode == kOutMaskButOwner) mask &= ~(1u << c);
+    return mask;
+}
+
 // Fold jobs: input k of job c is rank (c+1+k) mod R at element c*in_stride.
 template <int NIN, class Op, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void fold_kernel(JobArgs a) {
-    const int64_t total = a.tile_prefix[a.jobs];
-    for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
-        int c = 0;
-        while (t >= a.tile_prefix[c + 1]) ++c;
-        const int64_t lt = t - a.tile_prefix[c];
+    for (int t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
+        const int c = job_of(a, t);
+        const int lt = t - a.tile_prefix[c];
         const int64_t start = (int64_t)c * a.seg;
         const int64_t len = a.n - start < a.seg ? a.n - start : a.seg;
+        const int64_t ioff = (int64_t)c * a.in_stride;
         const uint32_t* in[NIN];
 #pragma unroll
-        for (int k = 0; k < NIN; ++k)
-            in[k] = static_cast<const uint32_t*>(a.in[(c + 1 + k) % NIN]) + (int64_t)c * a.in_stride;
-        uint32_t mask = a.out_mask;
-        if (a.out_mode == kOutOwner) mask = 1u << c;
-        else if (a.out_mode == kOutMaskButOwner) mask &= ~(1u << c);
+        for (int k = 0; k < NIN; ++k) {
+            int r = c + 1 + k;  // c < NIN, so r < 2 * NIN
+            r = r >= NIN ? r - NIN : r;
+            in[k] = static_cast<const uint32_t*>(a.in[r]) + ioff;
+        }
         const int64_t ooff = (int64_t)c * a.out_stride;
         auto out = [&](int o) { return static_cast<uint32_t*>(a.out[o]) + ooff; };
-        job_tile<NIN, NIN, Op, U, NT>(in, out, mask, len, a.phase[c], lt, a.tile_elems, a.mean != 0);
+        job_tile<NIN, NIN, Op, U, NT>(in, out, out_mask_of(a, c), len, a.phase[c], lt, a.tile_elems,
+                                      a.mean != 0);
     }
 }
 
@@ -246,20 +274,16 @@ __global__ __launch_bounds__(kBlock) void fold_kernel(JobArgs a) {
 // outputs of up to NR ranks.
 template <int NR, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void copy_kernel(JobArgs a) {
-    const int64_t total = a.tile_prefix[a.jobs];
-    for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
-        int c = 0;
-        while (t >= a.tile_prefix[c + 1]) ++c;
-        const int64_t lt = t - a.tile_prefix[c];
+    for (int t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
+        const int c = job_of(a, t);
+        const int lt = t - a.tile_prefix[c];
         const int64_t start = (int64_t)c * a.seg;
         const int64_t len = a.n - start < a.seg ? a.n - start : a.seg;
         const uint32_t* in[1] = {static_cast<const uint32_t*>(a.in[c]) + (int64_t)c * a.in_stride};
-        uint32_t mask = a.out_mask;
-        if (a.out_mode == kOutOwner) mask = 1u << c;
-        else if (a.out_mode == kOutMaskButOwner) mask &= ~(1u << c);
         const int64_t ooff = (int64_t)c * a.out_stride;
         auto out = [&](int o) { return static_cast<uint32_t*>(a.out[o]) + ooff; };
-        job_tile<1, NR, OpSumI32, U, NT>(in, out, mask, len, a.phase[c], lt, a.tile_elems, false);
+        job_tile<1, NR, OpSumI32, U, NT>(in, out, out_mask_of(a, c), len, a.phase[c], lt, a.tile_elems,
+                                         false);
     }
 }
 

@@ -33,23 +33,30 @@ uintptr_t addr(const void* p, int64_t elem_off, int64_t esize) {
     return reinterpret_cast<uintptr_t>(p) + (uintptr_t)(elem_off * esize);
 }
 
-// Fill per-job phase and tile counts of a single-launch plan.
+// Fill per-job phase and tile counts of a single-launch plan.  Tile indices
+// are 32-bit in the kernels: tiles grow until the total stays below 2^31.
 void finish_jobs(LaunchPlan* p, const std::vector<std::vector<uintptr_t>>& job_addrs) {
     JobArgs& a = p->args;
     const int64_t es = 4;
-    a.tile_prefix[0] = 0;
     for (int c = 0; c < a.jobs; ++c) {
-        const int64_t start = (int64_t)c * a.seg;
-        const int64_t len = std::max<int64_t>(0, std::min(a.seg, a.n - start));
+        const int64_t len = std::max<int64_t>(0, std::min(a.seg, a.n - (int64_t)c * a.seg));
         const auto& ad = job_addrs[c];
         a.phase[c] = len ? job_phase(ad.data(), (int)ad.size(), es, len) : 0;
-        a.tile_prefix[c + 1] = a.tile_prefix[c] + job_tiles(len, a.phase[c], a.tile_elems);
     }
-    for (int c = a.jobs; c < kMaxRanks; ++c) {
-        a.tile_prefix[c + 1] = a.tile_prefix[a.jobs];
-        a.phase[c] = 0;
+    int64_t prefix[kMaxRanks + 1];
+    for (;;) {
+        prefix[0] = 0;
+        for (int c = 0; c < a.jobs; ++c) {
+            const int64_t len = std::max<int64_t>(0, std::min(a.seg, a.n - (int64_t)c * a.seg));
+            prefix[c + 1] = prefix[c] + job_tiles(len, a.phase[c], a.tile_elems);
+        }
+        if (prefix[a.jobs] < (int64_t(1) << 31)) break;
+        a.tile_elems *= 2;
     }
-    p->total_tiles = a.tile_prefix[a.jobs];
+    for (int c = 0; c <= kMaxRanks; ++c) a.tile_prefix[c] = (int32_t)prefix[std::min(c, a.jobs)];
+    for (int c = a.jobs; c < kMaxRanks; ++c) a.phase[c] = 0;
+    a.total_tiles = (int32_t)prefix[a.jobs];
+    p->total_tiles = prefix[a.jobs];
 }
 
 int nontemporal_of(const Config& cfg) {

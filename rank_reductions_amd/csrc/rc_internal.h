@@ -50,7 +50,8 @@ struct JobArgs {
     uint32_t out_mask;
     int32_t mean;           // divide the finished fold by nranks
     int32_t nontemporal;
-    int64_t tile_prefix[kMaxRanks + 1];  // tiles before job j
+    int32_t total_tiles;                 // tile_prefix[jobs], below 2^31
+    int32_t tile_prefix[kMaxRanks + 1];  // tiles before job j; past the last job: total_tiles
     uint8_t phase[kMaxRanks];            // leading scalar elements, or kScalarOnly
 };
 

@@ -74,11 +74,15 @@ void check_plan(const LaunchPlan& p, const std::string& name) {
     std::vector<std::vector<uint8_t>> seen(a.jobs);
     for (int c = 0; c < a.jobs; ++c)
         seen[c].assign((size_t)std::max<int64_t>(0, std::min(a.seg, a.n - (int64_t)c * a.seg)), 0);
-    const int64_t total = a.tile_prefix[a.jobs];
+    const int64_t total = a.total_tiles;
+    if (total != a.tile_prefix[a.jobs] || total != p.total_tiles) fail(name + ": tile totals disagree");
+    for (int c = a.jobs; c <= kMaxRanks; ++c)
+        if (a.tile_prefix[c] != total) fail(name + ": prefix past the last job is not the total");
     for (int64_t t = 0; t < total; ++t) {
+        // the kernels' lookup: count job boundaries at or below t
         int c = 0;
-        while (t >= a.tile_prefix[c + 1]) ++c;
-        if (c >= a.jobs) {
+        for (int j = 1; j < kMaxRanks; ++j) c += t >= a.tile_prefix[j] ? 1 : 0;
+        if (c >= a.jobs || t < a.tile_prefix[c] || t >= a.tile_prefix[c + 1]) {
             fail(name + ": job index past the last job");
             return;
         }
