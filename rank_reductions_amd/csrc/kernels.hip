@@ -247,43 +247,65 @@ __device__ __forceinline__ uint32_t out_mask_of(const JobArgs& a, int c) {
     return mask;
 }
 
-// Fold jobs: input k of job c is rank (c+1+k) mod R at element c*in_stride.
+// Tile lt of fold job c: input k is rank (c+1+k) mod R at element c*in_stride.
+template <int NIN, class Op, int U, bool NT>
+__device__ __forceinline__ void fold_tile(const JobArgs& a, int c, int lt) {
+    const int64_t start = (int64_t)c * a.seg;
+    const int64_t len = a.n - start < a.seg ? a.n - start : a.seg;
+    const int64_t ioff = (int64_t)c * a.in_stride;
+    const uint32_t* in[NIN];
+#pragma unroll
+    for (int k = 0; k < NIN; ++k) {
+        int r = c + 1 + k;  // c < NIN, so r < 2 * NIN
+        r = r >= NIN ? r - NIN : r;
+        in[k] = static_cast<const uint32_t*>(a.in[r]) + ioff;
+    }
+    const int64_t ooff = (int64_t)c * a.out_stride;
+    auto out = [&](int o) { return static_cast<uint32_t*>(a.out[o]) + ooff; };
+    job_tile<NIN, NIN, Op, U, NT>(in, out, out_mask_of(a, c), len, a.phase[c], lt, a.tile_elems,
+                                  a.mean != 0);
+}
+
+// Tile lt of copy job c: in[c] at element c*in_stride, copied bit for bit to
+// the outputs of up to NR ranks.
+template <int NR, int U, bool NT>
+__device__ __forceinline__ void copy_tile(const JobArgs& a, int c, int lt) {
+    const int64_t start = (int64_t)c * a.seg;
+    const int64_t len = a.n - start < a.seg ? a.n - start : a.seg;
+    const uint32_t* in[1] = {static_cast<const uint32_t*>(a.in[c]) + (int64_t)c * a.in_stride};
+    const int64_t ooff = (int64_t)c * a.out_stride;
+    auto out = [&](int o) { return static_cast<uint32_t*>(a.out[o]) + ooff; };
+    job_tile<1, NR, OpSumI32, U, NT>(in, out, out_mask_of(a, c), len, a.phase[c], lt, a.tile_elems, false);
+}
+
+// Launch shapes: one-shot launches use a 2-D grid, blockIdx.y = job and
+// blockIdx.x = tile of the job (workgroups past a short job's last tile exit);
+// persistent launches use a 1-D grid that strides over all tiles.
 template <int NIN, class Op, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void fold_kernel(JobArgs a) {
+    if (a.grid_2d) {
+        const int c = blockIdx.y;
+        const int lt = blockIdx.x;
+        if (lt < a.tile_prefix[c + 1] - a.tile_prefix[c]) fold_tile<NIN, Op, U, NT>(a, c, lt);
+        return;
+    }
     for (int t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
         const int c = job_of(a, t);
-        const int lt = t - a.tile_prefix[c];
-        const int64_t start = (int64_t)c * a.seg;
-        const int64_t len = a.n - start < a.seg ? a.n - start : a.seg;
-        const int64_t ioff = (int64_t)c * a.in_stride;
-        const uint32_t* in[NIN];
-#pragma unroll
-        for (int k = 0; k < NIN; ++k) {
-            int r = c + 1 + k;  // c < NIN, so r < 2 * NIN
-            r = r >= NIN ? r - NIN : r;
-            in[k] = static_cast<const uint32_t*>(a.in[r]) + ioff;
-        }
-        const int64_t ooff = (int64_t)c * a.out_stride;
-        auto out = [&](int o) { return static_cast<uint32_t*>(a.out[o]) + ooff; };
-        job_tile<NIN, NIN, Op, U, NT>(in, out, out_mask_of(a, c), len, a.phase[c], lt, a.tile_elems,
-                                      a.mean != 0);
+        fold_tile<NIN, Op, U, NT>(a, c, t - a.tile_prefix[c]);
     }
 }
 
-// Copy jobs: job c copies in[c] at element c*in_stride, bit for bit, to the
-// outputs of up to NR ranks.
 template <int NR, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void copy_kernel(JobArgs a) {
+    if (a.grid_2d) {
+        const int c = blockIdx.y;
+        const int lt = blockIdx.x;
+        if (lt < a.tile_prefix[c + 1] - a.tile_prefix[c]) copy_tile<NR, U, NT>(a, c, lt);
+        return;
+    }
     for (int t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
         const int c = job_of(a, t);
-        const int lt = t - a.tile_prefix[c];
-        const int64_t start = (int64_t)c * a.seg;
-        const int64_t len = a.n - start < a.seg ? a.n - start : a.seg;
-        const uint32_t* in[1] = {static_cast<const uint32_t*>(a.in[c]) + (int64_t)c * a.in_stride};
-        const int64_t ooff = (int64_t)c * a.out_stride;
-        auto out = [&](int o) { return static_cast<uint32_t*>(a.out[o]) + ooff; };
-        job_tile<1, NR, OpSumI32, U, NT>(in, out, out_mask_of(a, c), len, a.phase[c], lt, a.tile_elems,
-                                         false);
+        copy_tile<NR, U, NT>(a, c, t - a.tile_prefix[c]);
     }
 }
 
@@ -441,7 +463,7 @@ hipError_t launch_jobs(const LaunchPlan& p, hipStream_t stream) {
     if (p.args.in_mode == kInCopy) fn = nt ? pick_copy<true>(p.args.nranks) : pick_copy<false>(p.args.nranks);
     else fn = nt ? pick_fold_op<true>(p.dtype, p.op, p.nin) : pick_fold_op<false>(p.dtype, p.op, p.nin);
     if (!fn) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fn, dim3(p.grid), dim3(kBlock), p.lds_bytes, stream, p.args);
+    hipLaunchKernelGGL(fn, dim3(p.grid, p.grid_y), dim3(kBlock), p.lds_bytes, stream, p.args);
     return hipGetLastError();
 }
 

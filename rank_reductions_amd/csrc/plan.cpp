@@ -8,13 +8,13 @@
 // all_gather_into_tensor (monarch Communicator page) use shards of M = N/R
 // elements, which are exactly those segments.  Host-only C++.
 //
-// Launch shape.  Every workgroup is one wave and takes one tile, and the
-// workgroups are dispatched in tile order, so the tiles in flight form one
-// compact window of each rank's buffers.  How many waves a CU holds at once is
-// capped through an LDS reservation: on MI355X, HBM efficiency for these
-// many-stream patterns peaks when about 128 KiB of traffic per CU is in
-// flight; more waves open more DRAM rows at once and lose bandwidth, fewer
-// leave it idle.
+// Launch shape.  Every workgroup is one wave and takes one tile.  One-shot
+// launches use a 2-D grid (x: tile of the job, y: job), dispatched in order, so
+// the tiles in flight form one compact window of each rank's buffers.  How
+// many waves a CU holds at once is capped through an LDS reservation: on
+// MI355X, HBM efficiency for these many-stream patterns peaks at about 96 KiB
+// of load traffic per CU in flight, counting stores at half weight; more
+// waves open more DRAM rows at once and lose bandwidth, fewer leave it idle.
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
@@ -27,7 +27,7 @@ namespace rc {
 namespace {
 
 constexpr int64_t kMaxTileElems = 65536;
-constexpr double kInFlightKiBPerCU = 128.0;
+constexpr double kInFlightKiBPerCU = 96.0;
 
 uintptr_t addr(const void* p, int64_t elem_off, int64_t esize) {
     return reinterpret_cast<uintptr_t>(p) + (uintptr_t)(elem_off * esize);
@@ -92,8 +92,9 @@ int64_t job_tiles(int64_t len, uint8_t phase, int64_t te) {
 }
 
 int auto_waves_per_cu(int nin, int nout, int unroll) {
-    // each wave moves (nin + nout) * unroll KiB per round (64 lanes x 16 B)
-    const double kib_per_wave = (double)(nin + nout) * unroll;
+    // each wave moves (nin + nout) * unroll KiB per round (64 lanes x 16 B);
+    // stores are posted and hold the wave only briefly, so they count half
+    const double kib_per_wave = ((double)nin + 0.5 * nout) * unroll;
     const long w = std::lround(kInFlightKiBPerCU / std::max(kib_per_wave, 1.0));
     return (int)std::min<long>(16, std::max<long>(2, w));
 }
@@ -276,6 +277,15 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceI
         const int in_mask = __builtin_popcount(ja.out_mask);
         lp.nout = ja.out_mode == kOutOwner ? 1 : in_mask - (ja.out_mode == kOutMaskButOwner ? 1 : 0);
         shape_launch(lp.total_tiles, lp.nin, lp.nout, lp.unroll, cfg, dev, &lp.grid, &lp.lds_bytes);
+        if (cfg.max_workgroups <= 0) {
+            // one-shot: x = tiles of the longest job, y = jobs
+            int64_t widest = 0;
+            for (int c = 0; c < ja.jobs; ++c)
+                widest = std::max<int64_t>(widest, ja.tile_prefix[c + 1] - ja.tile_prefix[c]);
+            lp.args.grid_2d = 1;
+            lp.grid = std::max<int64_t>(1, widest);
+            lp.grid_y = ja.jobs;
+        }
     }
     return out;
 }

@@ -50,6 +50,7 @@ struct JobArgs {
     uint32_t out_mask;
     int32_t mean;           // divide the finished fold by nranks
     int32_t nontemporal;
+    int32_t grid_2d;                     // one-shot 2-D grid (x: tile of job, y: job)
     int32_t total_tiles;                 // tile_prefix[jobs], below 2^31
     int32_t tile_prefix[kMaxRanks + 1];  // tiles before job j; past the last job: total_tiles
     uint8_t phase[kMaxRanks];            // leading scalar elements, or kScalarOnly
@@ -133,7 +134,8 @@ struct LaunchPlan {
     int dtype = RC_F32;
     int op = RC_SUM;
     int64_t total_tiles = 0;
-    int64_t grid = 0;        // workgroups launched
+    int64_t grid = 0;        // workgroups launched along x
+    int grid_y = 1;          // along y: the jobs, for one-shot launches
     int lds_bytes = 0;       // dynamic LDS per workgroup: caps workgroups per CU
 };
 

@@ -78,15 +78,30 @@ void check_plan(const LaunchPlan& p, const std::string& name) {
     if (total != a.tile_prefix[a.jobs] || total != p.total_tiles) fail(name + ": tile totals disagree");
     for (int c = a.jobs; c <= kMaxRanks; ++c)
         if (a.tile_prefix[c] != total) fail(name + ": prefix past the last job is not the total");
-    for (int64_t t = 0; t < total; ++t) {
-        // the kernels' lookup: count job boundaries at or below t
-        int c = 0;
-        for (int j = 1; j < kMaxRanks; ++j) c += t >= a.tile_prefix[j] ? 1 : 0;
-        if (c >= a.jobs || t < a.tile_prefix[c] || t >= a.tile_prefix[c + 1]) {
-            fail(name + ": job index past the last job");
-            return;
-        }
-        const int64_t lt = t - a.tile_prefix[c];
+    // the (job, tile) pairs the launch visits
+    std::vector<std::pair<int, int64_t>> visits;
+    if (a.grid_2d) {
+        if (p.grid_y != a.jobs) fail(name + ": 2-D grid height is not the job count");
+        for (int c = 0; c < p.grid_y; ++c)
+            for (int64_t lt = 0; lt < p.grid; ++lt)
+                if (lt < a.tile_prefix[c + 1] - a.tile_prefix[c]) visits.push_back({c, lt});
+    } else {
+        if (p.grid_y != 1) fail(name + ": 1-D launch with a 2-D grid");
+        for (int64_t b = 0; b < p.grid; ++b)
+            for (int64_t t = b; t < total; t += p.grid) {
+                // the kernels' lookup: count job boundaries at or below t
+                int c = 0;
+                for (int j = 1; j < kMaxRanks; ++j) c += t >= a.tile_prefix[j] ? 1 : 0;
+                if (c >= a.jobs || t < a.tile_prefix[c] || t >= a.tile_prefix[c + 1]) {
+                    fail(name + ": job index past the last job");
+                    return;
+                }
+                visits.push_back({c, t - a.tile_prefix[c]});
+            }
+    }
+    for (const auto& visit : visits) {
+        const int c = visit.first;
+        const int64_t lt = visit.second;
         const int64_t start = (int64_t)c * a.seg;
         const int64_t len = std::min(a.seg, a.n - start);
         uint32_t mask = a.out_mask;
