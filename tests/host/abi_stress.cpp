@@ -1,0 +1,144 @@
+// Host-only stress of the C ABI in validate-only sessions (no GPU): many
+// threads issue valid and invalid collectives while others register, finish
+// and reset.  Built with AddressSanitizer or ThreadSanitizer by the tests; the
+// program checks that every call returns a documented status and that a
+// valid call in an open session succeeds.  Links session.cpp, validate.cpp,
+// plan.cpp and stub device functions (validate-only sessions never reach them).
+#include <atomic>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <random>
+#include <thread>
+#include <vector>
+
+#include "rc.h"
+#include "rc_internal.h"
+
+namespace rc {
+// validate-only sessions never call into the device layer
+Error device_open(const Config&, DeviceInfo*) { return Error{RC_ERR_DEVICE, "no device in this test"}; }
+Error device_launch(const LaunchPlan&, void*) { return Error{RC_ERR_DEVICE, "no device in this test"}; }
+Error device_launch_batch(const BatchPlan&, void*) { return Error{RC_ERR_DEVICE, "no device in this test"}; }
+Error device_finish() { return {}; }
+void device_reset() {}
+}  // namespace rc
+
+namespace {
+
+std::atomic<int> g_bad{0};
+
+rc_buf buf(uintptr_t s, uintptr_t r, int64_t n, int dtype = RC_F32, int op = RC_SUM, int root = 0) {
+    rc_buf b;
+    std::memset(&b, 0, sizeof b);
+    b.send = reinterpret_cast<const void*>(s);
+    b.recv = reinterpret_cast<void*>(r);
+    b.dtype = dtype;
+    b.op = op;
+    b.root = root;
+    b.ndim = 1;
+    b.dims[0] = n;
+    return b;
+}
+
+void worker(int id, int iters, int R) {
+    std::mt19937 rng(id);
+    std::vector<rc_buf> bufs(R);
+    for (int i = 0; i < iters; ++i) {
+        const int64_t n = 1 + rng() % 100000;
+        const uintptr_t base = 0x100000000ull + (uintptr_t)id * 0x10000000ull;
+        for (int r = 0; r < R; ++r) bufs[r] = buf(base + r * 0x800000ull, base + 0x8000000ull + r * 0x800000ull, n);
+        const int kind = rng() % 6;
+        if (kind == 5) bufs[rng() % R].dims[0] += 1;  // shape mismatch
+        int rc = 0;
+        switch (kind) {
+            case 0: rc = rc_all_reduce(bufs.data(), nullptr); break;
+            case 1: rc = rc_reduce(bufs.data(), nullptr); break;
+            case 2:
+                for (int r = 1; r < R; ++r) bufs[r].send = nullptr;
+                rc = rc_broadcast(bufs.data(), nullptr);
+                break;
+            case 3: rc = rc_all_gather(bufs.data(), nullptr); break;
+            case 4: rc = rc_all_reduce_many(1, bufs.data(), nullptr); break;
+            default: rc = rc_all_reduce(bufs.data(), nullptr); break;
+        }
+        const char* err = rc_last_error();
+        if (rc < 0 || rc > RC_ERR_DEVICE) ++g_bad;
+        if (rc == RC_OK && err[0] != '\0') ++g_bad;
+        if (rc != RC_OK && err[0] == '\0') ++g_bad;
+        if (kind == 5 && rc == RC_OK) ++g_bad;  // a mismatch must never pass
+    }
+}
+
+void lifecycle(int iters, int R) {
+    rc_config cfg;
+    std::memset(&cfg, 0, sizeof cfg);
+    cfg.struct_size = sizeof cfg;
+    cfg.device = -1;
+    cfg.validate_only = 1;
+    for (int i = 0; i < iters; ++i) {
+        const int rc = rc_register(R, &cfg);
+        if (rc != RC_OK && rc != RC_ERR_DUPLICATE_REGISTRATION) ++g_bad;
+        if (i % 3 == 0) {
+            const int f = rc_finish();
+            if (f != RC_OK && f != RC_ERR_NOT_REGISTERED) ++g_bad;
+        } else if (i % 3 == 1) {
+            if (rc_reset() != RC_OK) ++g_bad;
+        }
+    }
+}
+
+// Random field values (pointers are never dereferenced in validate-only
+// sessions): every call must return a documented status without crashing.
+void fuzz(int iters, int R) {
+    std::mt19937_64 rng(99);
+    std::vector<rc_buf> bufs(R * 3);
+    for (int i = 0; i < iters; ++i) {
+        for (rc_buf& b : bufs) {
+            b.send = (rng() % 4) ? reinterpret_cast<const void*>(rng() & 0xFFFFFFFFFFFull) : nullptr;
+            b.recv = (rng() % 4) ? reinterpret_cast<void*>(rng() & 0xFFFFFFFFFFFull) : nullptr;
+            b.dtype = (int32_t)(rng() % 4) - 1;
+            b.op = (int32_t)(rng() % 5) - 1;
+            b.root = (int32_t)(rng() % (R + 3)) - 2;
+            b.ndim = (int32_t)(rng() % 11) - 1;
+            for (int d = 0; d < RC_MAX_DIMS; ++d)
+                b.dims[d] = (rng() % 8 == 0) ? (int64_t)(rng() >> 1) * ((rng() % 2) ? 1 : -1) : (int64_t)(rng() % 70);
+        }
+        int rc;
+        switch (rng() % 6) {
+            case 0: rc = rc_all_reduce(bufs.data(), nullptr); break;
+            case 1: rc = rc_reduce(bufs.data(), nullptr); break;
+            case 2: rc = rc_broadcast(bufs.data(), nullptr); break;
+            case 3: rc = rc_reduce_scatter(bufs.data(), nullptr); break;
+            case 4: rc = rc_all_gather(bufs.data(), nullptr); break;
+            default: rc = rc_all_reduce_many(3, bufs.data(), nullptr); break;
+        }
+        if (rc < 0 || rc > RC_ERR_DEVICE) ++g_bad;
+    }
+}
+
+}  // namespace
+
+int main() {
+    const int R = 8;
+    rc_config cfg;
+    std::memset(&cfg, 0, sizeof cfg);
+    cfg.struct_size = sizeof cfg;
+    cfg.device = -1;
+    cfg.validate_only = 1;
+    if (rc_register(R, &cfg) != RC_OK) return 2;
+    // with the session held open, every valid call must succeed
+    {
+        std::vector<rc_buf> bufs(R);
+        for (int r = 0; r < R; ++r) bufs[r] = buf(0x10000 * (r + 1), 0x1000000 + 0x10000 * r, 1000);
+        if (rc_all_reduce(bufs.data(), nullptr) != RC_OK) return 3;
+    }
+    fuzz(20000, R);
+    std::vector<std::thread> ts;
+    for (int t = 0; t < 6; ++t) ts.emplace_back(worker, t, 3000, R);
+    ts.emplace_back(lifecycle, 2000, R);
+    for (auto& t : ts) t.join();
+    rc_reset();
+    std::printf("abi stress: %d bad results\n", g_bad.load());
+    return g_bad.load() ? 1 : 0;
+}
