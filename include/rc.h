@@ -209,6 +209,49 @@ int rc_finish(void);
  * returns RC_OK. */
 int rc_reset(void);
 
+/* ------------------------------------------------------------------------
+ * Per-rank front end.  Each logical rank registers itself and issues its own
+ * side of every collective, typically from a thread of its own: register<B>
+ * registers one peer (ruCCL README section 2), participants agree on the rank
+ * count and call matching collectives in the same order (section 3), and the
+ * monarch Communicator is created and called once per rank, from a different
+ * thread or process per rank.
+ *
+ * The k-th collective call of every rank forms one collective.  Each call
+ * blocks until all num_ranks ranks have made their k-th call; the last to
+ * arrive checks the R descriptors against each other (the same checks and
+ * codes as the whole-call API; a different collective kind on two ranks is
+ * RC_ERR_OP_MISMATCH) and enqueues the kernels.  Every rank then returns the
+ * same status.  Ordering: the kernels run after the work each rank had
+ * enqueued on its own stream before its call, and each rank's stream waits
+ * for the kernels before any work it enqueues after the call returns.
+ * A rank that never makes its call leaves the others waiting; rc_reset
+ * releases them with RC_ERR_NOT_REGISTERED.  The whole-call entry points
+ * above reject a session opened here with RC_ERR_INVALID_ARGUMENT, and the
+ * per-rank entry points report RC_ERR_NOT_REGISTERED for a rank that has not
+ * registered in a per-rank session. */
+
+/* register<B> for one peer.  The first call opens the session with
+ * num_ranks and cfg; later calls must give the same num_ranks (else
+ * RC_ERR_INVALID_ARGUMENT).  A rank registering twice, or any call while a
+ * whole-call session is open, is RC_ERR_DUPLICATE_REGISTRATION.  rank in
+ * [0, num_ranks). */
+int rc_rank_register(int rank, int num_ranks, const rc_config* cfg);
+
+/* Rank `rank`'s side of all_reduce / reduce / broadcast / reduce_scatter /
+ * all_gather: buf is that rank's rc_buf with the meaning given above for the
+ * whole-call entry point of the same name, stream is that rank's stream. */
+int rc_rank_all_reduce(int rank, const rc_buf* buf, void* stream);
+int rc_rank_reduce(int rank, const rc_buf* buf, void* stream);
+int rc_rank_broadcast(int rank, const rc_buf* buf, void* stream);
+int rc_rank_reduce_scatter(int rank, const rc_buf* buf, void* stream);
+int rc_rank_all_gather(int rank, const rc_buf* buf, void* stream);
+
+/* finish_collective<B> for one peer: the rank leaves the session.  When the
+ * last registered rank has finished, the session waits for the GPU, frees its
+ * scratch and closes.  RC_ERR_NOT_REGISTERED for a rank not registered. */
+int rc_rank_finish(int rank);
+
 /* Text for the last failure on the calling thread (valid until that thread's
  * next rc_* call); "" after success. */
 const char* rc_last_error(void);

@@ -129,6 +129,15 @@ def library():
     lib.rc_last_error.restype = ctypes.c_char_p
     lib.rc_status_name.argtypes = [ctypes.c_int]
     lib.rc_status_name.restype = ctypes.c_char_p
+    lib.rc_rank_register.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(RcConfig)]
+    lib.rc_rank_register.restype = ctypes.c_int
+    for name in ("rc_rank_all_reduce", "rc_rank_reduce", "rc_rank_broadcast", "rc_rank_reduce_scatter",
+                 "rc_rank_all_gather"):
+        fn = getattr(lib, name)
+        fn.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        fn.restype = ctypes.c_int
+    lib.rc_rank_finish.argtypes = [ctypes.c_int]
+    lib.rc_rank_finish.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -352,4 +361,70 @@ def all_reduce_many(tensors, op="mean", out=None, stream=None):
     ref = tensors[0][0]
     check(library().rc_all_reduce_many(len(tensors), ctypes.c_void_p(arr.ctypes.data),
                                        ctypes.c_void_p(_stream(stream, ref))))
+    return out
+
+
+# ---------------------------------------------------------------- per-rank front end
+#
+# Each logical rank calls these from its own thread with its own tensors and
+# stream; the k-th calls of all ranks form one collective (ruCCL README,
+# section 3).  Every call blocks until all ranks have made theirs.
+
+def rank_register(rank, num_ranks, device=None, **cfg):
+    """register<B> for one peer of a per-rank session."""
+    if device is None:
+        device = -1
+    elif not isinstance(device, int):
+        import torch
+        device = torch.device(device).index if torch.device(device).index is not None else -1
+    c = make_config(device, **cfg)
+    return check(library().rc_rank_register(int(rank), int(num_ranks), ctypes.byref(c)))
+
+
+def rank_finish(rank):
+    """finish_collective<B> for one peer; the last one closes the session."""
+    return check(library().rc_rank_finish(int(rank)))
+
+
+def _rank_call(fn, rank, send, recv, op=RC_SUM, root=0, stream=None):
+    ref = send if send is not None else recv
+    bufs = make_bufs([_ptr(send)], [_ptr(recv)], [tuple(ref.shape)], [_dtype_code(ref)], op, root)
+    check(fn(int(rank), ctypes.cast(bufs, ctypes.c_void_p), ctypes.c_void_p(_stream(stream, ref))))
+
+
+def rank_all_reduce(rank, x, op="sum", out=None, stream=None):
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(x)
+    _rank_call(library().rc_rank_all_reduce, rank, x, out, _op(op), 0, stream)
+    return out
+
+
+def rank_reduce(rank, x, root, op="sum", out=None, stream=None):
+    torch = _torch()
+    if out is None and rank == root:
+        out = torch.empty_like(x)
+    _rank_call(library().rc_rank_reduce, rank, x, out, _op(op), root, stream)
+    return out
+
+
+def rank_broadcast(rank, x=None, out=None, stream=None, root=-1):
+    """The sender passes x; receivers pass x=None and an `out` tensor."""
+    _rank_call(library().rc_rank_broadcast, rank, x, out, RC_SUM, root, stream)
+    return out
+
+
+def rank_reduce_scatter(rank, x, num_ranks, op="sum", out=None, stream=None):
+    torch = _torch()
+    if out is None:
+        out = torch.empty(x.numel() // num_ranks, dtype=x.dtype, device=x.device)
+    _rank_call(library().rc_rank_reduce_scatter, rank, x, out, _op(op), 0, stream)
+    return out
+
+
+def rank_all_gather(rank, shard, num_ranks, out=None, stream=None):
+    torch = _torch()
+    if out is None:
+        out = torch.empty(num_ranks * shard.numel(), dtype=shard.dtype, device=shard.device)
+    _rank_call(library().rc_rank_all_gather, rank, shard, out, RC_SUM, 0, stream)
     return out

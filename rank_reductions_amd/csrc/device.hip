@@ -184,4 +184,30 @@ void device_reset() {
     g.device = -1;
 }
 
+Error device_event_create(void** ev) {
+    DeviceGuard guard;
+    if (guard.err != hipSuccess) return hip_fail("hipSetDevice", guard.err);
+    hipEvent_t e = nullptr;
+    hipError_t st = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+    if (st != hipSuccess) return hip_fail("hipEventCreateWithFlags", st);
+    *ev = e;
+    return {};
+}
+
+void device_event_destroy(void* ev) {
+    if (ev) (void)hipEventDestroy(static_cast<hipEvent_t>(ev));
+}
+
+Error device_event_record(void* ev, void* stream) {
+    hipError_t st = hipEventRecord(static_cast<hipEvent_t>(ev), static_cast<hipStream_t>(stream));
+    if (st != hipSuccess) return hip_fail("hipEventRecord", st);
+    return {};
+}
+
+Error device_stream_wait(void* stream, void* ev) {
+    hipError_t st = hipStreamWaitEvent(static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(ev), 0);
+    if (st != hipSuccess) return hip_fail("hipStreamWaitEvent", st);
+    return {};
+}
+
 }  // namespace rc

@@ -180,5 +180,10 @@ Error device_launch(const LaunchPlan& p, void* stream);
 Error device_launch_batch(const BatchPlan& p, void* stream);
 Error device_finish();   // wait for the GPU, free scratch
 void device_reset();     // wait for kernels reading scratch, free scratch
+// Events that order the per-rank front end's streams around a launch.
+Error device_event_create(void** ev);
+void device_event_destroy(void* ev);
+Error device_event_record(void* ev, void* stream);
+Error device_stream_wait(void* stream, void* ev);
 
 }  // namespace rc

@@ -4,9 +4,19 @@
 // 4 "Errors and lifecycle"): register opens the session, finish_collective is
 // the normal end, reset_collective discards the registration and in-flight
 // state without completing, checkpointing or recovering anything.  Duplicate
-// and missing registration are CollectiveError cases.  Host-only C++: the GPU
-// is reached only through the device_* functions.
+// and missing registration are CollectiveError cases.
+//
+// Two front ends share one process-wide session.  The whole-call entry points
+// take all R ranks' arguments at once.  The per-rank entry points take one
+// rank's side per call (section 3: every participant calls matching
+// collectives in the same order; the monarch Communicator page: one thread or
+// process per rank); the k-th calls of all ranks are matched into one
+// collective, checked, and launched by the last rank to arrive.  Host-only
+// C++: the GPU is reached only through the device_* functions.
+#include <condition_variable>
 #include <cstring>
+#include <map>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -16,15 +26,40 @@
 namespace rc {
 namespace {
 
+enum class Mode { None, Whole, PerRank };
+
+// One collective of the per-rank front end, filled in as ranks arrive.
+struct Slot {
+    std::vector<Coll> kinds;
+    std::vector<rc_buf> bufs;
+    std::vector<uint8_t> have_buf;
+    std::vector<void*> streams;
+    std::vector<void*> arrive_ev;  // recorded on each rank's stream at its call
+    void* launch_stream = nullptr;
+    void* done_ev = nullptr;       // recorded after the kernels
+    uint32_t arrived = 0;
+    int left = 0;
+    bool done = false;
+    int status = RC_OK;
+    std::string msg;
+};
+
 struct Session {
-    bool registered = false;
+    Mode mode = Mode::None;
     int nranks = 0;
     Config cfg;
     DeviceInfo dev;
+    // per-rank front end
+    uint32_t reg_mask = 0;
+    uint32_t fin_mask = 0;
+    std::vector<uint64_t> seq;
+    std::map<uint64_t, std::shared_ptr<Slot>> slots;
 };
 
 std::mutex g_mu;
+std::condition_variable g_cv;
 Session g_s;
+uint64_t g_generation = 0;  // bumped when the session is reset or closed
 thread_local std::string t_err;
 
 int report(const Error& e) {
@@ -67,19 +102,160 @@ Error read_config(const rc_config* in, Config* cfg) {
     return {};
 }
 
+// Opens the session (caller holds g_mu and has checked that none is open).
+Error open_session(Mode mode, int num_ranks, const rc_config* cfg) {
+    if (num_ranks < 1 || num_ranks > RC_MAX_RANKS)
+        return Error{RC_ERR_INVALID_ARGUMENT, "register: num_ranks must be in [1, 16]"};
+    Config c;
+    Error e = read_config(cfg, &c);
+    if (e.code) return e;
+    DeviceInfo dev;
+    if (!c.validate_only) {
+        e = device_open(c, &dev);
+        if (e.code) return e;
+    }
+    g_s = Session{};
+    g_s.mode = mode;
+    g_s.nranks = num_ranks;
+    g_s.cfg = c;
+    g_s.dev = dev;
+    g_s.seq.assign(num_ranks, 0);
+    return {};
+}
+
+void release_slot(Slot& s) {
+    for (void* ev : s.arrive_ev) device_event_destroy(ev);
+    device_event_destroy(s.done_ev);
+    s.arrive_ev.assign(s.arrive_ev.size(), nullptr);
+    s.done_ev = nullptr;
+}
+
+// Drops the session; waiting per-rank calls wake up and see the new generation.
+void close_session() {
+    for (auto& kv : g_s.slots) release_slot(*kv.second);
+    g_s = Session{};
+    ++g_generation;
+    g_cv.notify_all();
+}
+
+Error launch(const Checked& ck, void* stream) {
+    for (const LaunchPlan& p : plan(ck, g_s.cfg, g_s.dev)) {
+        Error e = device_launch(p, stream);
+        if (e.code) return e;
+    }
+    return {};
+}
+
 int collective(Coll coll, const rc_buf* bufs, void* stream) {
     std::lock_guard<std::mutex> lock(g_mu);
-    if (!g_s.registered)
+    if (g_s.mode == Mode::None)
         return report(Error{RC_ERR_NOT_REGISTERED, "no session: call rc_register first"});
+    if (g_s.mode == Mode::PerRank)
+        return report(Error{RC_ERR_INVALID_ARGUMENT,
+                            "the session was opened per rank: use the rc_rank_* entry points"});
     Checked ck;
     Error e = validate(coll, g_s.nranks, bufs, &ck);
     if (e.code) return report(e);
     if (g_s.cfg.validate_only) return ok();
-    for (const LaunchPlan& p : plan(ck, g_s.cfg, g_s.dev)) {
-        e = device_launch(p, stream);
-        if (e.code) return report(e);
+    return report(launch(ck, stream));
+}
+
+const char* coll_name(Coll c) {
+    switch (c) {
+        case Coll::AllReduce: return "all_reduce";
+        case Coll::Reduce: return "reduce";
+        case Coll::Broadcast: return "broadcast";
+        case Coll::ReduceScatter: return "reduce_scatter";
+        case Coll::AllGather: return "all_gather";
     }
-    return ok();
+    return "?";
+}
+
+// The last rank of a slot: check the R sides against each other and launch.
+void complete_slot(Slot& s, void* stream) {
+    const int R = g_s.nranks;
+    for (int r = 0; r < R; ++r) {
+        if (!s.have_buf[r]) {
+            s.status = RC_ERR_INVALID_ARGUMENT;
+            s.msg = "rank " + std::to_string(r) + " passed a NULL rc_buf";
+            return;
+        }
+    }
+    for (int r = 1; r < R; ++r) {
+        if (s.kinds[r] != s.kinds[0]) {
+            s.status = RC_ERR_OP_MISMATCH;
+            s.msg = std::string("rank ") + std::to_string(r) + " called " + coll_name(s.kinds[r]) +
+                    " where rank 0 called " + coll_name(s.kinds[0]);
+            return;
+        }
+    }
+    Checked ck;
+    Error e = validate(s.kinds[0], R, s.bufs.data(), &ck);
+    if (!e.code && !g_s.cfg.validate_only) {
+        s.launch_stream = stream;
+        for (int r = 0; r < R && !e.code; ++r)
+            if (s.streams[r] != stream) e = device_stream_wait(stream, s.arrive_ev[r]);
+        if (!e.code) e = launch(ck, stream);
+        if (!e.code) e = device_event_create(&s.done_ev);
+        if (!e.code) e = device_event_record(s.done_ev, stream);
+    }
+    s.status = e.code;
+    s.msg = e.msg;
+}
+
+int rank_collective(Coll coll, int rank, const rc_buf* buf, void* stream) {
+    std::unique_lock<std::mutex> lock(g_mu);
+    if (g_s.mode != Mode::PerRank)
+        return report(Error{RC_ERR_NOT_REGISTERED, "no per-rank session: call rc_rank_register first"});
+    const int R = g_s.nranks;
+    if (rank < 0 || rank >= R)
+        return report(Error{RC_ERR_INVALID_ARGUMENT, "rank outside [0, num_ranks)"});
+    if (!((g_s.reg_mask >> rank) & 1u) || ((g_s.fin_mask >> rank) & 1u))
+        return report(Error{RC_ERR_NOT_REGISTERED, "rank " + std::to_string(rank) + " is not registered"});
+    const uint64_t k = g_s.seq[rank]++;
+    std::shared_ptr<Slot>& sp = g_s.slots[k];
+    if (!sp) {
+        sp = std::make_shared<Slot>();
+        sp->kinds.assign(R, Coll::AllReduce);
+        sp->bufs.assign(R, rc_buf{});
+        sp->have_buf.assign(R, 0);
+        sp->streams.assign(R, nullptr);
+        sp->arrive_ev.assign(R, nullptr);
+    }
+    std::shared_ptr<Slot> s = sp;
+    s->kinds[rank] = coll;
+    if (buf) {
+        s->bufs[rank] = *buf;
+        s->have_buf[rank] = 1;
+    }
+    s->streams[rank] = stream;
+    if (!g_s.cfg.validate_only) {
+        Error e = device_event_create(&s->arrive_ev[rank]);
+        if (!e.code) e = device_event_record(s->arrive_ev[rank], stream);
+        if (e.code && s->status == RC_OK) {
+            s->status = e.code;
+            s->msg = e.msg;
+        }
+    }
+    s->arrived |= 1u << rank;
+    const uint64_t gen = g_generation;
+    if (s->arrived == (uint32_t)((1ull << R) - 1)) {
+        if (s->status == RC_OK) complete_slot(*s, stream);
+        s->done = true;
+        g_cv.notify_all();
+    } else {
+        g_cv.wait(lock, [&] { return s->done || g_generation != gen; });
+        if (g_generation != gen)
+            return report(Error{RC_ERR_NOT_REGISTERED, "the session was reset or closed while rank " +
+                                                           std::to_string(rank) + " waited"});
+    }
+    Error e{s->status, s->msg};
+    if (!e.code && s->done_ev && stream != s->launch_stream) e = device_stream_wait(stream, s->done_ev);
+    if (++s->left == R) {
+        release_slot(*s);
+        g_s.slots.erase(k);
+    }
+    return report(e);
 }
 
 }  // namespace
@@ -91,23 +267,9 @@ extern "C" {
 
 int rc_register(int num_ranks, const rc_config* cfg) {
     std::lock_guard<std::mutex> lock(g_mu);
-    if (g_s.registered)
+    if (g_s.mode != Mode::None)
         return report(Error{RC_ERR_DUPLICATE_REGISTRATION, "rc_register: a session is already open"});
-    if (num_ranks < 1 || num_ranks > RC_MAX_RANKS)
-        return report(Error{RC_ERR_INVALID_ARGUMENT, "rc_register: num_ranks must be in [1, 16]"});
-    Config c;
-    Error e = read_config(cfg, &c);
-    if (e.code) return report(e);
-    DeviceInfo dev;
-    if (!c.validate_only) {
-        e = device_open(c, &dev);
-        if (e.code) return report(e);
-    }
-    g_s.registered = true;
-    g_s.nranks = num_ranks;
-    g_s.cfg = c;
-    g_s.dev = dev;
-    return ok();
+    return report(open_session(Mode::Whole, num_ranks, cfg));
 }
 
 int rc_all_reduce(const rc_buf* bufs, void* stream) { return collective(Coll::AllReduce, bufs, stream); }
@@ -120,8 +282,10 @@ int rc_all_gather(const rc_buf* bufs, void* stream) { return collective(Coll::Al
 
 int rc_all_reduce_many(int num_tensors, const rc_buf* bufs, void* stream) {
     std::lock_guard<std::mutex> lock(g_mu);
-    if (!g_s.registered)
+    if (g_s.mode == Mode::None)
         return report(Error{RC_ERR_NOT_REGISTERED, "no session: call rc_register first"});
+    if (g_s.mode == Mode::PerRank)
+        return report(Error{RC_ERR_INVALID_ARGUMENT, "the session was opened per rank"});
     std::vector<Checked> cks;
     Error e = validate_batch(g_s.nranks, num_tensors, bufs, &cks);
     if (e.code) return report(e);
@@ -129,32 +293,82 @@ int rc_all_reduce_many(int num_tensors, const rc_buf* bufs, void* stream) {
     std::vector<Checked> own, batched;
     split_batch(cks, &own, &batched);
     for (const Checked& ck : own) {
-        for (const LaunchPlan& p : plan(ck, g_s.cfg, g_s.dev)) {
-            e = device_launch(p, stream);
-            if (e.code) return report(e);
-        }
+        e = launch(ck, stream);
+        if (e.code) return report(e);
     }
     const BatchPlan bp = plan_batch(batched, g_s.cfg, g_s.dev);
     if (bp.total_tiles == 0) return ok();
-    e = device_launch_batch(bp, stream);
-    return report(e);
+    return report(device_launch_batch(bp, stream));
 }
 
 int rc_finish(void) {
     std::lock_guard<std::mutex> lock(g_mu);
-    if (!g_s.registered)
+    if (g_s.mode == Mode::None)
         return report(Error{RC_ERR_NOT_REGISTERED, "rc_finish: no session is open"});
+    if (g_s.mode == Mode::PerRank)
+        return report(Error{RC_ERR_INVALID_ARGUMENT, "rc_finish: the session was opened per rank; "
+                                                     "every rank calls rc_rank_finish"});
     Error e;
     if (!g_s.cfg.validate_only) e = device_finish();
-    g_s = Session{};
+    close_session();
     return report(e);
 }
 
 int rc_reset(void) {
     std::lock_guard<std::mutex> lock(g_mu);
-    if (g_s.registered && !g_s.cfg.validate_only) device_reset();
-    g_s = Session{};
+    if (g_s.mode != Mode::None && !g_s.cfg.validate_only) device_reset();
+    close_session();
     return ok();
+}
+
+int rc_rank_register(int rank, int num_ranks, const rc_config* cfg) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (g_s.mode == Mode::Whole)
+        return report(Error{RC_ERR_DUPLICATE_REGISTRATION, "rc_rank_register: a whole-call session is open"});
+    if (g_s.mode == Mode::None) {
+        Error e = open_session(Mode::PerRank, num_ranks, cfg);
+        if (e.code) return report(e);
+    } else if (num_ranks != g_s.nranks) {
+        return report(Error{RC_ERR_INVALID_ARGUMENT, "rc_rank_register: num_ranks " + std::to_string(num_ranks) +
+                                                         " differs from the session's " +
+                                                         std::to_string(g_s.nranks)});
+    }
+    if (rank < 0 || rank >= g_s.nranks)
+        return report(Error{RC_ERR_INVALID_ARGUMENT, "rc_rank_register: rank outside [0, num_ranks)"});
+    if ((g_s.reg_mask >> rank) & 1u)
+        return report(Error{RC_ERR_DUPLICATE_REGISTRATION,
+                            "rc_rank_register: rank " + std::to_string(rank) + " is already registered"});
+    g_s.reg_mask |= 1u << rank;
+    return ok();
+}
+
+int rc_rank_all_reduce(int rank, const rc_buf* buf, void* stream) {
+    return rank_collective(Coll::AllReduce, rank, buf, stream);
+}
+int rc_rank_reduce(int rank, const rc_buf* buf, void* stream) {
+    return rank_collective(Coll::Reduce, rank, buf, stream);
+}
+int rc_rank_broadcast(int rank, const rc_buf* buf, void* stream) {
+    return rank_collective(Coll::Broadcast, rank, buf, stream);
+}
+int rc_rank_reduce_scatter(int rank, const rc_buf* buf, void* stream) {
+    return rank_collective(Coll::ReduceScatter, rank, buf, stream);
+}
+int rc_rank_all_gather(int rank, const rc_buf* buf, void* stream) {
+    return rank_collective(Coll::AllGather, rank, buf, stream);
+}
+
+int rc_rank_finish(int rank) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (g_s.mode != Mode::PerRank || rank < 0 || rank >= g_s.nranks || !((g_s.reg_mask >> rank) & 1u) ||
+        ((g_s.fin_mask >> rank) & 1u))
+        return report(Error{RC_ERR_NOT_REGISTERED, "rc_rank_finish: rank is not registered"});
+    g_s.fin_mask |= 1u << rank;
+    if (g_s.fin_mask != g_s.reg_mask) return ok();
+    Error e;
+    if (!g_s.cfg.validate_only) e = device_finish();
+    close_session();
+    return report(e);
 }
 
 const char* rc_last_error(void) { return t_err.c_str(); }

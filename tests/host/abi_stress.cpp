@@ -22,6 +22,10 @@ Error device_launch(const LaunchPlan&, void*) { return Error{RC_ERR_DEVICE, "no 
 Error device_launch_batch(const BatchPlan&, void*) { return Error{RC_ERR_DEVICE, "no device in this test"}; }
 Error device_finish() { return {}; }
 void device_reset() {}
+Error device_event_create(void**) { return Error{RC_ERR_DEVICE, "no device in this test"}; }
+void device_event_destroy(void*) {}
+Error device_event_record(void*, void*) { return Error{RC_ERR_DEVICE, "no device in this test"}; }
+Error device_stream_wait(void*, void*) { return Error{RC_ERR_DEVICE, "no device in this test"}; }
 }  // namespace rc
 
 namespace {
@@ -117,9 +121,43 @@ void fuzz(int iters, int R) {
     }
 }
 
+// Per-rank front end: one thread per rank, calls matched by issue order; every
+// 7th collective has a shape mismatch on rank 0, which every rank must see.
+void rank_thread(int rank, int R, int iters) {
+    for (int i = 0; i < iters; ++i) {
+        int64_t n = 1 + (i * 7919) % 5000;
+        if (i % 7 == 3 && rank == 0) n += 1;
+        const uintptr_t base = 0x200000000ull + (uintptr_t)rank * 0x1000000ull;
+        rc_buf b = buf(base, base + 0x800000ull, n);
+        int rc;
+        switch (i % 3) {
+            case 0: rc = rc_rank_all_reduce(rank, &b, nullptr); break;
+            case 1: rc = rc_rank_reduce(rank, &b, nullptr); break;
+            default: rc = rc_rank_all_gather(rank, &b, nullptr); break;
+        }
+        const int want = i % 7 == 3 ? RC_ERR_SHAPE_MISMATCH : RC_OK;
+        if (rc != want) ++g_bad;
+    }
+    if (rc_rank_finish(rank) != RC_OK) ++g_bad;
+}
+
+void rank_session(int R, int iters) {
+    rc_config cfg;
+    std::memset(&cfg, 0, sizeof cfg);
+    cfg.struct_size = sizeof cfg;
+    cfg.device = -1;
+    cfg.validate_only = 1;
+    for (int r = 0; r < R; ++r)
+        if (rc_rank_register(r, R, &cfg) != RC_OK) ++g_bad;
+    std::vector<std::thread> ts;
+    for (int r = 0; r < R; ++r) ts.emplace_back(rank_thread, r, R, iters);
+    for (auto& t : ts) t.join();
+}
+
 }  // namespace
 
 int main() {
+    rank_session(6, 3000);
     const int R = 8;
     rc_config cfg;
     std::memset(&cfg, 0, sizeof cfg);

@@ -1,0 +1,149 @@
+"""The per-rank front end on the GPU: one host thread and one stream per
+logical rank.  Each rank produces its input on its own stream right before
+its call and consumes the output on that stream right after, with no host
+synchronisation in between, so the results are only right if the library
+orders the kernels after every rank's producer and every consumer after the
+kernels.  Bits are compared with the CPU oracle."""
+
+import threading
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rank_reductions_amd as rr
+import synth_inputs as si
+from gpu_util import assert_bits, host
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def run_ranks(R, body):
+    out = [None] * R
+    errs = []
+
+    def go(r):
+        try:
+            out[r] = body(r)
+        except BaseException as e:  # noqa: BLE001
+            errs.append(e)
+
+    ts = [threading.Thread(target=go, args=(r,)) for r in range(R)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join(timeout=120)
+    assert not errs, errs
+    assert all(not t.is_alive() for t in ts)
+    return out
+
+
+def slow_copy(src):
+    """src, rebuilt through a chain of exact float32 ops (x*2-x = x, x/1 = x),
+    so the producer is still running when the rank's call is issued."""
+    x = src.clone()
+    for _ in range(6):
+        x = (x * 2.0 - x) / 1.0
+    return x
+
+
+@pytest.mark.parametrize("R", [2, 4, 8])
+def test_rank_threads_all_reduce(R):
+    N = 4_000_037
+    srcs = si.torch_rank_inputs(R, N, "f32", "normal", 70 + R, device=DEV)
+    torch.cuda.synchronize()
+    hx = [host(x) for x in srcs]
+    streams = [torch.cuda.Stream() for _ in range(R)]
+    for r in range(R):
+        rr.rank_register(r, R)
+
+    def body(r):
+        got = {}
+        with torch.cuda.stream(streams[r]):
+            for op in ("sum", "mean", "max"):
+                x = slow_copy(srcs[r])
+                out = rr.rank_all_reduce(r, x, op, stream=streams[r])
+                got[op] = out.clone()  # consumer on the rank's stream
+                x.mul_(0)              # overwrite the input right after the call
+        return got
+
+    try:
+        got = run_ranks(R, body)
+        torch.cuda.synchronize()
+        for op in ("sum", "mean", "max"):
+            want = oracle.all_reduce_closed_form(hx, op)
+            for r in range(R):
+                assert_bits(host(got[r][op]), want, f"R={R} {op} rank {r}")
+    finally:
+        for r in range(R):
+            rr.rank_finish(r)
+
+
+def test_rank_threads_every_collective():
+    R = 4
+    M = 250_007
+    N = R * M
+    srcs = si.torch_rank_inputs(R, N, "i32", "int", 81, device=DEV)
+    torch.cuda.synchronize()
+    hx = [host(x) for x in srcs]
+    streams = [torch.cuda.Stream() for _ in range(R)]
+    for r in range(R):
+        rr.rank_register(r, R)
+
+    def body(r):
+        s = streams[r]
+        res = {}
+        with torch.cuda.stream(s):
+            x = srcs[r].clone()
+            out = rr.rank_reduce(r, x, 2, "sum", stream=s)
+            res["reduce"] = out.clone() if out is not None else None
+            b_out = torch.empty_like(x) if r != 1 else None
+            res["broadcast"] = rr.rank_broadcast(r, x if r == 1 else None, out=b_out, stream=s)
+            if r != 1:
+                res["broadcast"] = res["broadcast"].clone()
+            res["rs"] = rr.rank_reduce_scatter(r, x, R, "max", stream=s).clone()
+            shard = (x[:M] + 0).contiguous()
+            res["ag"] = rr.rank_all_gather(r, shard, R, stream=s).clone()
+        return res
+
+    try:
+        got = run_ranks(R, body)
+        torch.cuda.synchronize()
+        assert_bits(host(got[2]["reduce"]), oracle.reduce(hx, 2, "sum")[2], "reduce root 2")
+        for r in (0, 2, 3):
+            assert_bits(host(got[r]["broadcast"]), hx[1], f"broadcast rank {r}")
+        want_rs = oracle.reduce_scatter(hx, "max")
+        want_ag = np.concatenate([h[:M] for h in hx])
+        for r in range(R):
+            assert_bits(host(got[r]["rs"]), want_rs[r], f"reduce_scatter rank {r}")
+            assert_bits(host(got[r]["ag"]), want_ag, f"all_gather rank {r}")
+    finally:
+        for r in range(R):
+            rr.rank_finish(r)
+
+
+def test_rank_mismatch_on_gpu_launches_nothing():
+    R = 2
+    xs = si.torch_rank_inputs(R, 1000, "f32", "normal", 5, device=DEV)
+    outs = [torch.full_like(x, 7.0) for x in xs]
+    for r in range(R):
+        rr.rank_register(r, R)
+
+    def body(r):
+        op = "sum" if r == 0 else "max"
+        try:
+            rr.rank_all_reduce(r, xs[r], op, out=outs[r])
+        except rr.CollectiveError as e:
+            return e.code
+        return rr.RC_OK
+
+    try:
+        assert run_ranks(R, body) == [rr.RC_ERR_OP_MISMATCH] * R
+        torch.cuda.synchronize()
+        for o in outs:
+            assert torch.all(o == 7.0).item(), "an output was written despite the error"
+    finally:
+        for r in range(R):
+            rr.rank_finish(r)
