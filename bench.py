@@ -241,6 +241,10 @@ def rows(torch, rr, si, dev, xs8, args):
     us = time_calls(torch, lambda: rr.all_reduce(xs8, "sum", out=o), 10) * 1e3
     out["all_reduce_ring_r8_64MiB_f32_sum"] = _roof(2 * R * b, us)
     rr.finish()
+    # the same all-reduce through the per-rank front end: one host thread and
+    # one stream per rank, calls matched by issue order
+    out["all_reduce_per_rank_threads_r8_64MiB_f32_sum_shared_stream"] = per_rank_row(torch, rr, xs8, o, 1)
+    out["all_reduce_per_rank_threads_r8_64MiB_f32_sum_8_streams"] = per_rank_row(torch, rr, xs8, o, R)
     del o
     rr.register(R, device=0)
     # reduce_scatter and all_gather, 8 ranks x 256 MiB
@@ -297,6 +301,66 @@ def rows(torch, rr, si, dev, xs8, args):
     del ts, os_
     torch.cuda.empty_cache()
     return out
+
+
+def per_rank_row(torch, rr, xs, outs, n_streams, calls=100):
+    """Wall time of `calls` all-reduce Sum collectives issued by R rank threads
+    on n_streams streams (rank r on stream r mod n_streams), from a released
+    barrier to the device's drain.  Each distinct stream beyond the launching
+    rank's costs an event join per collective."""
+    import threading
+
+    R, N = len(xs), xs[0].numel()
+    lib = rr.library()
+    ref = outs[0].clone()  # the ring schedule's result of the same inputs
+    for o in outs:
+        o.fill_(float("nan"))
+    torch.cuda.synchronize()
+    pool = [torch.cuda.Stream() for _ in range(n_streams)]
+    streams = [pool[r % n_streams] for r in range(R)]
+    bufs = [rr.make_bufs([x.data_ptr()], [o.data_ptr()], (N,), rr.RC_F32, rr.RC_SUM) for x, o in zip(xs, outs)]
+    warmed = threading.Barrier(R + 1)
+    go = threading.Barrier(R + 1)
+    bad = []
+
+    def rank(r):
+        p = ctypes.cast(bufs[r], ctypes.c_void_p)
+        s = ctypes.c_void_p(streams[r].cuda_stream)
+        for k in range(2 * calls):
+            if k == calls:  # an untimed pass, then the timed one
+                warmed.wait()
+                go.wait()
+            if lib.rc_rank_all_reduce(r, p, s):
+                bad.append(lib.rc_last_error().decode())
+                warmed.abort()
+                go.abort()
+                return
+
+    for r in range(R):
+        rr.rank_register(r, R, device=0)
+    ts = [threading.Thread(target=rank, args=(r,)) for r in range(R)]
+    for t in ts:
+        t.start()
+    try:
+        warmed.wait()
+        torch.cuda.synchronize()
+        go.wait()
+    except threading.BrokenBarrierError:
+        pass
+    t0 = time.perf_counter()
+    for t in ts:
+        t.join()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for r in range(R):
+        rr.rank_finish(r)
+    if bad:
+        raise rr.CollectiveError(1, bad[0])
+    row = _roof(2 * R * N * 4, wall / calls * 1e6)
+    row.update({"calls": calls, "threads": R, "streams": n_streams,
+                "matches_ring_bits": all(torch.equal(ref, o) for o in outs),
+                "timing": "host wall clock from the released barrier to device drain"})
+    return row
 
 
 def cpu_baseline(torch, xs, out_sum, seconds):

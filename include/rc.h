@@ -224,9 +224,15 @@ int rc_reset(void);
  * RC_ERR_OP_MISMATCH) and enqueues the kernels.  Every rank then returns the
  * same status.  Ordering: the kernels run after the work each rank had
  * enqueued on its own stream before its call, and each rank's stream waits
- * for the kernels before any work it enqueues after the call returns.
- * A rank that never makes its call leaves the others waiting; rc_reset
- * releases them with RC_ERR_NOT_REGISTERED.  The whole-call entry points
+ * for the kernels before any work it enqueues after the call returns.  The
+ * join is made when the last rank arrives, so work that another thread puts
+ * on a waiting rank's stream in the meantime also precedes the kernels.
+ * Ranks that pass the same stream as the launching rank cost no events.
+ * A rank issues its calls one at a time: a call for a rank that already has
+ * one in progress (on another thread) is RC_ERR_INVALID_ARGUMENT and joins
+ * no collective.  A rank that never makes its call leaves the others
+ * waiting; rc_reset releases them with RC_ERR_NOT_REGISTERED.  The
+ * whole-call entry points
  * above reject a session opened here with RC_ERR_INVALID_ARGUMENT, and the
  * per-rank entry points report RC_ERR_NOT_REGISTERED for a rank that has not
  * registered in a per-rank session. */

@@ -13,6 +13,7 @@
 // process per rank); the k-th calls of all ranks are matched into one
 // collective, checked, and launched by the last rank to arrive.  Host-only
 // C++: the GPU is reached only through the device_* functions.
+#include <algorithm>
 #include <condition_variable>
 #include <cstring>
 #include <map>
@@ -34,14 +35,23 @@ struct Slot {
     std::vector<rc_buf> bufs;
     std::vector<uint8_t> have_buf;
     std::vector<void*> streams;
-    std::vector<void*> arrive_ev;  // recorded on each rank's stream at its call
-    void* launch_stream = nullptr;
-    void* done_ev = nullptr;       // recorded after the kernels
     uint32_t arrived = 0;
     int left = 0;
     bool done = false;
     int status = RC_OK;
     std::string msg;
+};
+
+// The per-rank session's events, used only by the launching rank under the
+// session lock and reused by every collective (each wait is enqueued right
+// after the record it reads, before the event can be recorded again).
+struct RankEvents {
+    std::vector<void*> arrive;  // one per distinct stream other than the launch stream
+    void* done = nullptr;
+    ~RankEvents() {
+        for (void* ev : arrive) device_event_destroy(ev);
+        device_event_destroy(done);
+    }
 };
 
 struct Session {
@@ -52,8 +62,10 @@ struct Session {
     // per-rank front end
     uint32_t reg_mask = 0;
     uint32_t fin_mask = 0;
+    uint32_t busy_mask = 0;  // ranks with a call in progress
     std::vector<uint64_t> seq;
     std::map<uint64_t, std::shared_ptr<Slot>> slots;
+    std::shared_ptr<RankEvents> events;
 };
 
 std::mutex g_mu;
@@ -114,25 +126,25 @@ Error open_session(Mode mode, int num_ranks, const rc_config* cfg) {
         e = device_open(c, &dev);
         if (e.code) return e;
     }
+    auto events = std::make_shared<RankEvents>();
+    if (mode == Mode::PerRank && !c.validate_only) {
+        events->arrive.assign(num_ranks, nullptr);
+        for (int r = 0; r < num_ranks && !e.code; ++r) e = device_event_create(&events->arrive[r]);
+        if (!e.code) e = device_event_create(&events->done);
+        if (e.code) return e;
+    }
     g_s = Session{};
     g_s.mode = mode;
     g_s.nranks = num_ranks;
     g_s.cfg = c;
     g_s.dev = dev;
     g_s.seq.assign(num_ranks, 0);
+    g_s.events = std::move(events);
     return {};
-}
-
-void release_slot(Slot& s) {
-    for (void* ev : s.arrive_ev) device_event_destroy(ev);
-    device_event_destroy(s.done_ev);
-    s.arrive_ev.assign(s.arrive_ev.size(), nullptr);
-    s.done_ev = nullptr;
 }
 
 // Drops the session; waiting per-rank calls wake up and see the new generation.
 void close_session() {
-    for (auto& kv : g_s.slots) release_slot(*kv.second);
     g_s = Session{};
     ++g_generation;
     g_cv.notify_all();
@@ -171,6 +183,29 @@ const char* coll_name(Coll c) {
     return "?";
 }
 
+// Launches one matched collective on `stream` (the last rank's), ordered
+// against every rank's stream.  Every other rank is blocked inside its call
+// and has enqueued nothing since making it, so an event recorded on its
+// stream now marks that rank's call point; after the kernels, the same
+// streams wait on `done` before anything the ranks enqueue once they return.
+// Each distinct stream is joined once, and a stream shared with the launching
+// rank needs no event at all.
+Error launch_joined(const Checked& ck, const std::vector<void*>& streams, void* stream) {
+    RankEvents& ev = *g_s.events;
+    std::vector<void*> others;
+    for (void* s : streams)
+        if (s != stream && std::find(others.begin(), others.end(), s) == others.end()) others.push_back(s);
+    Error e;
+    for (size_t i = 0; i < others.size() && !e.code; ++i) {
+        e = device_event_record(ev.arrive[i], others[i]);
+        if (!e.code) e = device_stream_wait(stream, ev.arrive[i]);
+    }
+    if (!e.code) e = launch(ck, stream);
+    if (!e.code && !others.empty()) e = device_event_record(ev.done, stream);
+    for (size_t i = 0; i < others.size() && !e.code; ++i) e = device_stream_wait(others[i], ev.done);
+    return e;
+}
+
 // The last rank of a slot: check the R sides against each other and launch.
 void complete_slot(Slot& s, void* stream) {
     const int R = g_s.nranks;
@@ -191,14 +226,7 @@ void complete_slot(Slot& s, void* stream) {
     }
     Checked ck;
     Error e = validate(s.kinds[0], R, s.bufs.data(), &ck);
-    if (!e.code && !g_s.cfg.validate_only) {
-        s.launch_stream = stream;
-        for (int r = 0; r < R && !e.code; ++r)
-            if (s.streams[r] != stream) e = device_stream_wait(stream, s.arrive_ev[r]);
-        if (!e.code) e = launch(ck, stream);
-        if (!e.code) e = device_event_create(&s.done_ev);
-        if (!e.code) e = device_event_record(s.done_ev, stream);
-    }
+    if (!e.code && !g_s.cfg.validate_only) e = launch_joined(ck, s.streams, stream);
     s.status = e.code;
     s.msg = e.msg;
 }
@@ -212,6 +240,12 @@ int rank_collective(Coll coll, int rank, const rc_buf* buf, void* stream) {
         return report(Error{RC_ERR_INVALID_ARGUMENT, "rank outside [0, num_ranks)"});
     if (!((g_s.reg_mask >> rank) & 1u) || ((g_s.fin_mask >> rank) & 1u))
         return report(Error{RC_ERR_NOT_REGISTERED, "rank " + std::to_string(rank) + " is not registered"});
+    const uint32_t bit = 1u << rank;
+    if (g_s.busy_mask & bit)
+        return report(Error{RC_ERR_INVALID_ARGUMENT, "rank " + std::to_string(rank) +
+                                                         " already has a call in progress on another thread"});
+    g_s.busy_mask |= bit;
+    const uint64_t gen = g_generation;
     const uint64_t k = g_s.seq[rank]++;
     std::shared_ptr<Slot>& sp = g_s.slots[k];
     if (!sp) {
@@ -220,7 +254,6 @@ int rank_collective(Coll coll, int rank, const rc_buf* buf, void* stream) {
         sp->bufs.assign(R, rc_buf{});
         sp->have_buf.assign(R, 0);
         sp->streams.assign(R, nullptr);
-        sp->arrive_ev.assign(R, nullptr);
     }
     std::shared_ptr<Slot> s = sp;
     s->kinds[rank] = coll;
@@ -229,18 +262,9 @@ int rank_collective(Coll coll, int rank, const rc_buf* buf, void* stream) {
         s->have_buf[rank] = 1;
     }
     s->streams[rank] = stream;
-    if (!g_s.cfg.validate_only) {
-        Error e = device_event_create(&s->arrive_ev[rank]);
-        if (!e.code) e = device_event_record(s->arrive_ev[rank], stream);
-        if (e.code && s->status == RC_OK) {
-            s->status = e.code;
-            s->msg = e.msg;
-        }
-    }
-    s->arrived |= 1u << rank;
-    const uint64_t gen = g_generation;
+    s->arrived |= bit;
     if (s->arrived == (uint32_t)((1ull << R) - 1)) {
-        if (s->status == RC_OK) complete_slot(*s, stream);
+        complete_slot(*s, stream);
         s->done = true;
         g_cv.notify_all();
     } else {
@@ -249,12 +273,9 @@ int rank_collective(Coll coll, int rank, const rc_buf* buf, void* stream) {
             return report(Error{RC_ERR_NOT_REGISTERED, "the session was reset or closed while rank " +
                                                            std::to_string(rank) + " waited"});
     }
-    Error e{s->status, s->msg};
-    if (!e.code && s->done_ev && stream != s->launch_stream) e = device_stream_wait(stream, s->done_ev);
-    if (++s->left == R) {
-        release_slot(*s);
-        g_s.slots.erase(k);
-    }
+    g_s.busy_mask &= ~bit;
+    const Error e{s->status, s->msg};
+    if (++s->left == R) g_s.slots.erase(k);
     return report(e);
 }
 

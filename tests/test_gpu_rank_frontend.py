@@ -49,13 +49,16 @@ def slow_copy(src):
     return x
 
 
-@pytest.mark.parametrize("R", [2, 4, 8])
-def test_rank_threads_all_reduce(R):
+@pytest.mark.parametrize("R,n_streams", [(2, 2), (4, 4), (8, 8), (8, 1), (6, 3)])
+def test_rank_threads_all_reduce(R, n_streams):
+    """Rank r on stream r mod n_streams: own streams, one shared stream (no
+    events), and pairs of ranks sharing a stream."""
     N = 4_000_037
     srcs = si.torch_rank_inputs(R, N, "f32", "normal", 70 + R, device=DEV)
     torch.cuda.synchronize()
     hx = [host(x) for x in srcs]
-    streams = [torch.cuda.Stream() for _ in range(R)]
+    pool = [torch.cuda.Stream() for _ in range(n_streams)]
+    streams = [pool[r % n_streams] for r in range(R)]
     for r in range(R):
         rr.rank_register(r, R)
 

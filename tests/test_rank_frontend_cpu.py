@@ -159,6 +159,32 @@ def test_null_buf_is_reported_to_all(lib):
     assert run_ranks(R, body) == [rr.RC_ERR_INVALID_ARGUMENT] * R
 
 
+def test_second_call_of_a_busy_rank_is_refused(lib):
+    R = 2
+    for r in range(R):
+        assert lib.rc_rank_register(r, R, ctypes.byref(cfg())) == rr.RC_OK
+    first = {}
+
+    def rank0():
+        b = one(send_addr(0), recv_addr(0))
+        first["rc"] = lib.rc_rank_all_reduce(0, ctypes.cast(b, ctypes.c_void_p), None)
+
+    t = threading.Thread(target=rank0)
+    t.start()
+    time.sleep(0.2)  # rank 0's call is now waiting for rank 1
+    b = one(send_addr(0), recv_addr(0))
+    assert lib.rc_rank_all_reduce(0, ctypes.cast(b, ctypes.c_void_p), None) == rr.RC_ERR_INVALID_ARGUMENT
+    assert "in progress" in lib.rc_last_error().decode()
+    b = one(send_addr(1), recv_addr(1))
+    assert lib.rc_rank_all_reduce(1, ctypes.cast(b, ctypes.c_void_p), None) == rr.RC_OK
+    t.join(timeout=30)
+    assert first["rc"] == rr.RC_OK
+    # the refused call joined no collective: the next calls still pair up
+    res = run_ranks(R, lambda r: lib.rc_rank_all_reduce(
+        r, ctypes.cast(one(send_addr(r), recv_addr(r)), ctypes.c_void_p), None))
+    assert res == [rr.RC_OK] * R
+
+
 def test_single_rank_does_not_wait(lib):
     assert lib.rc_rank_register(0, 1, ctypes.byref(cfg())) == rr.RC_OK
     b = one(send_addr(0), recv_addr(0))
