@@ -213,9 +213,9 @@ int rc_reset(void);
  * Per-rank front end.  Each logical rank registers itself and issues its own
  * side of every collective, typically from a thread of its own: register<B>
  * registers one peer (ruCCL README section 2), participants agree on the rank
- * count and call matching collectives in the same order (section 3), and the
- * monarch Communicator is created and called once per rank, from a different
- * thread or process per rank.
+ * count and call matching collectives in the same order (section 3), and on
+ * the monarch Communicator page each rank builds and drives its own
+ * communicator on its own thread or in its own process.
  *
  * The k-th collective call of every rank forms one collective.  Each call
  * blocks until all num_ranks ranks have made their k-th call; the last to
