@@ -11,4 +11,5 @@ from .ring import (  # noqa: F401
     ring_reduce_scatter_phase, ring_all_gather_phase,
     all_reduce, reduce, broadcast, reduce_scatter, all_gather, all_reduce_many,
     all_reduce_closed_form, all_reduce_at, all_reduce_at_many,
+    ParamMismatch, all_reduce_params, accumulate,
 )

@@ -19,6 +19,10 @@ What it computes, and where that is defined
 * RUDA "Training and state saving", section "Configure training backend": the
   backend element types are f32 and i32, so the dtypes here are float32 and
   int32 and all float arithmetic is float32 (the pages fix that precision).
+* ruCCL README (ja), section 6 "Collective training": the whole gradient set,
+  keyed by parameter ID, is reduced with Mean; IDs, shapes and dtype must
+  agree on every rank.  RUDA "Training and state saving", gradient
+  accumulation: accumulate adds without averaging.
 
 Readings where the pages are silent (each restated where it is used):
 * Segments: S = ceil(N / R); segment c is [c*S, min((c+1)*S, N)), possibly
@@ -274,6 +278,69 @@ def all_reduce_many(tensors, op=MEAN):
     rank r's copy of tensor t; each tensor is reduced on its own, with its own
     ring segments.  Returns out[t][r]."""
     return [all_reduce(list(per_rank), op) for per_rank in tensors]
+
+
+# --------------------------------------------------------------------------
+# Gradient synchronisation keyed by parameter ID
+# --------------------------------------------------------------------------
+
+class ParamMismatch(OracleError):
+    """The ranks' gradient maps disagree.  kind is "ids" (the ID sets differ),
+    "dtype" or "shape" (one ID's tensors differ between ranks)."""
+
+    def __init__(self, kind, msg):
+        super().__init__(msg)
+        self.kind = kind
+
+
+def all_reduce_params(grads, op=MEAN):
+    """Whole-gradient sync of ruCCL README section 6, "Collective training":
+    every rank holds a map from parameter ID to gradient and reduces it with
+    ReduceOperation::Mean; the IDs, each gradient's shape and the dtype must
+    agree on every rank.
+
+    grads[r] is rank r's map {id: array}.  Readings: entries are paired across
+    ranks by ID (a map has no order, so the order a rank lists its entries in
+    does not matter); each parameter is reduced on its own, exactly as one
+    all_reduce of that parameter's R tensors; mismatches are checked IDs
+    first, then per parameter (in ID order) dtype before shape.  Returns R
+    maps {id: reduced array}, every rank's values identical."""
+    R = len(grads)
+    if R == 0:
+        raise OracleError("need at least one rank")
+    ids = set(grads[0])
+    for r in range(1, R):
+        if set(grads[r]) != ids:
+            only0 = sorted(ids - set(grads[r]))
+            onlyr = sorted(set(grads[r]) - ids)
+            raise ParamMismatch("ids", f"rank {r}: missing {only0[:3]}, extra {onlyr[:3]}")
+    for pid in sorted(ids):
+        per_rank = [np.asarray(grads[r][pid]) for r in range(R)]
+        if any(a.dtype != per_rank[0].dtype for a in per_rank):
+            raise ParamMismatch("dtype", f"parameter {pid}: dtype differs between ranks")
+        if any(a.shape != per_rank[0].shape for a in per_rank):
+            raise ParamMismatch("shape", f"parameter {pid}: shape differs between ranks")
+    out = [{} for _ in range(R)]
+    for pid in ids:
+        reduced = all_reduce([grads[r][pid] for r in range(R)], op)
+        for r in range(R):
+            out[r][pid] = reduced[r]
+    return out
+
+
+def accumulate(acc, grad):
+    """GradientsAccumulator.accumulate (RUDA "Training and state saving",
+    gradient accumulation): gradients are added without averaging.  acc is None
+    for an empty accumulator, which then takes a copy of grad.  One float32
+    add per element (int32 wraps)."""
+    grad = np.asarray(grad)
+    _check_dtype(grad)
+    if acc is None:
+        return grad.copy()
+    acc = np.asarray(acc)
+    if acc.dtype != grad.dtype or acc.shape != grad.shape:
+        raise OracleError("accumulate: dtype or shape differs from the accumulator")
+    return combine(_flat(acc), _flat(grad), SUM).reshape(acc.shape)
 
 
 # --------------------------------------------------------------------------

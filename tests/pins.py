@@ -319,6 +319,110 @@ def pin_invariants(orc):
                 assert_bits_equal(xs[r], keep[r], "input modified")
 
 
+def _param_maps(rng, R, specs, int_valued=True, seed_order=0):
+    """R maps {id: array}; rank r inserts its entries in its own order."""
+    order_rng = _rng(1000 + seed_order)
+    maps = []
+    for r in range(R):
+        entries = {}
+        for pid, shape in specs:
+            n = int(np.prod(shape)) if shape else 1
+            if int_valued:
+                v = rng.integers(-(1 << 20), (1 << 20) + 1, size=n).astype(np.float32)
+            else:
+                v = rng.standard_normal(n).astype(np.float32)
+            entries[pid] = v.reshape(shape)
+        keys = list(entries)
+        order_rng.shuffle(keys)
+        maps.append({k: entries[k] for k in keys})
+    return maps
+
+
+PARAM_SPECS = [(7, (3, 5)), (3, (257,)), (11, (0,)), (0, ()), (42, (64,)), (5, (2, 2, 3))]
+
+
+def pin_params(orc):
+    """Whole-gradient sync keyed by parameter ID (ruCCL README section 6):
+    entries pair by ID whatever order each rank lists them in, every
+    parameter gets the exact reduction of its own R tensors (integer-valued
+    float32 sums are exact in any order, so they must equal numpy's int64
+    sum; Mean is that sum divided by R and rounded once), all ranks agree,
+    inputs are unchanged, and ID, dtype and shape disagreements are reported
+    as such (IDs first, then dtype before shape)."""
+    rng = _rng(23)
+    for R in (1, 2, 3, 5, 8):
+        maps = _param_maps(rng, R, PARAM_SPECS, seed_order=R)
+        keep = [{k: v.copy() for k, v in m.items()} for m in maps]
+        for op in (orc.SUM, orc.MEAN):
+            out = orc.all_reduce_params(maps, op)
+            assert len(out) == R
+            for pid, shape in PARAM_SPECS:
+                exact = np.sum(np.stack([maps[r][pid].astype(np.int64) for r in range(R)]), axis=0)
+                want = exact.astype(np.float32) if op == orc.SUM else \
+                    (exact.astype(np.float64) / R).astype(np.float32)
+                for r in range(R):
+                    assert set(out[r]) == {p for p, _ in PARAM_SPECS}, "ID set changed"
+                    assert_bits_equal(out[r][pid], want.reshape(shape), f"R={R} {op} id {pid} rank {r}")
+        for r in range(R):
+            for pid in keep[r]:
+                assert_bits_equal(maps[r][pid], keep[r][pid], "input modified")
+
+    def expect(kind, maps):
+        try:
+            orc.all_reduce_params(maps, orc.MEAN)
+        except orc.ParamMismatch as e:
+            assert e.kind == kind, f"reported {e.kind!r}, expected {kind!r}"
+            return
+        raise AssertionError(f"{kind} mismatch not reported")
+
+    base = _param_maps(rng, 3, PARAM_SPECS, seed_order=99)
+    missing = [dict(m) for m in base]
+    del missing[2][42]
+    expect("ids", missing)
+    extra = [dict(m) for m in base]
+    extra[1][99] = np.zeros(4, np.float32)
+    expect("ids", extra)
+    renamed = [dict(m) for m in base]
+    renamed[0][43] = renamed[0].pop(42)
+    expect("ids", renamed)
+    shape = [dict(m) for m in base]
+    shape[1][7] = shape[1][7].reshape(5, 3)
+    expect("shape", shape)
+    dtype = [dict(m) for m in base]
+    dtype[2][3] = dtype[2][3].astype(np.int32)
+    expect("dtype", dtype)
+    both = [dict(m) for m in base]
+    both[2][5] = np.zeros((12,), np.int32)
+    expect("dtype", both)
+
+
+def pin_accumulate(orc):
+    """GradientsAccumulator.accumulate (RUDA "Training and state saving"):
+    adds without averaging, so integer-valued float32 gradients accumulate to
+    their exact int64 sum; the first gradient is copied, not aliased; int32
+    wraps; a shape change is refused."""
+    rng = _rng(29)
+    grads = [rng.integers(-(1 << 20), (1 << 20) + 1, size=(4, 33)).astype(np.float32) for _ in range(6)]
+    acc = None
+    for k, g in enumerate(grads):
+        acc = orc.accumulate(acc, g)
+        exact = np.sum(np.stack([x.astype(np.int64) for x in grads[:k + 1]]), axis=0)
+        assert_bits_equal(acc, exact.astype(np.float32), f"after {k + 1} microbatches")
+    first = np.ones(5, np.float32)
+    acc = orc.accumulate(None, first)
+    acc[0] = 7.0
+    assert first[0] == 1.0, "the accumulator aliases the caller's gradient"
+    top = np.array([2 ** 31 - 1, -2 ** 31], np.int32)
+    assert_bits_equal(orc.accumulate(top, np.array([1, -1], np.int32)),
+                      np.array([-2 ** 31, 2 ** 31 - 1], np.int32), "int32 wraps")
+    try:
+        orc.accumulate(np.zeros(4, np.float32), np.zeros(5, np.float32))
+    except orc.OracleError:
+        pass
+    else:
+        raise AssertionError("shape change accepted")
+
+
 ALL_PINS = [
     pin_segments,
     pin_worked_examples,
@@ -331,4 +435,6 @@ ALL_PINS = [
     pin_broadcast,
     pin_all_gather,
     pin_invariants,
+    pin_params,
+    pin_accumulate,
 ]

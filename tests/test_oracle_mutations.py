@@ -58,6 +58,24 @@ MUTATIONS = {
                               "return [(c - k) % num_ranks for k in range(1, num_ranks + 1)]"),
     "at_many_wrong_segment": ("seg = indices // s", "seg = indices // max(s - 1, 1)"),
     "at_wrong_segment": ("c = index // segment_length(n, R)", "c = index // (segment_length(n, R) + 1)"),
+    "params_pair_by_position": ("reduced = all_reduce([grads[r][pid] for r in range(R)], op)",
+                                "reduced = all_reduce([list(grads[r].values())[sorted(ids).index(pid)] "
+                                "for r in range(R)], op)"),
+    "params_no_id_check": ("        if set(grads[r]) != ids:\n", "        if False:\n"),
+    "params_no_shape_check": ('            raise ParamMismatch("shape", f"parameter {pid}: shape differs between ranks")',
+                              "            pass"),
+    "params_shape_before_dtype": ("        if any(a.dtype != per_rank[0].dtype for a in per_rank):\n"
+                                  '            raise ParamMismatch("dtype"',
+                                  "        if any(a.shape != per_rank[0].shape for a in per_rank):\n"
+                                  '            raise ParamMismatch("shape"'),
+    "params_op_ignored": ("reduced = all_reduce([grads[r][pid] for r in range(R)], op)",
+                          "reduced = all_reduce([grads[r][pid] for r in range(R)], SUM)"),
+    "params_rank0_everywhere": ("            out[r][pid] = reduced[r]", "            out[r][pid] = grads[0][pid]"),
+    "accumulate_averages": ("return combine(_flat(acc), _flat(grad), SUM).reshape(acc.shape)",
+                            "return (combine(_flat(acc), _flat(grad), SUM) / np.float32(2)).reshape(acc.shape)"),
+    "accumulate_aliases": ("        return grad.copy()", "        return grad"),
+    "accumulate_replaces": ("return combine(_flat(acc), _flat(grad), SUM).reshape(acc.shape)",
+                            "return grad.copy()"),
 }
 
 
