@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define RC_ABI_VERSION 1
+#define RC_ABI_VERSION 2
 #define RC_MAX_RANKS 16
 #define RC_MAX_DIMS 8
 
@@ -73,7 +73,8 @@ enum { RC_CACHE_AUTO = 0, RC_CACHE_STREAMING = 1, RC_CACHE_NORMAL = 2 };
 /* Status codes.  Codes 1-6 are the CollectiveError cases of the ruCCL README,
  * section 4 "Errors and lifecycle" (duplicate or missing registration, shape
  * mismatch, inconsistent reduction op or root, invalid broadcast sender
- * count); 7-9 are this library's plumbing. */
+ * count); 7-9 are this library's plumbing; 10 is the parameter-ID agreement
+ * that section 6 "Collective training" requires of a gradient sync. */
 typedef enum {
     RC_OK = 0,
     RC_ERR_NOT_REGISTERED = 1,
@@ -84,7 +85,8 @@ typedef enum {
     RC_ERR_BROADCAST_SENDERS = 6,
     RC_ERR_DTYPE_MISMATCH = 7,
     RC_ERR_INVALID_ARGUMENT = 8,
-    RC_ERR_DEVICE = 9
+    RC_ERR_DEVICE = 9,
+    RC_ERR_PARAM_MISMATCH = 10  /* gradient maps with different parameter IDs */
 } rc_status;
 
 /* One logical rank's side of a collective (cf. the TensorCell argument of the
@@ -196,6 +198,25 @@ int rc_all_gather(const rc_buf* bufs, void* stream);
  * rc_finish / rc_reset). */
 int rc_all_reduce_many(int num_tensors, const rc_buf* bufs, void* stream);
 
+/* Whole-gradient all-reduce keyed by parameter ID (ruCCL README section 6,
+ * "Collective training": each rank's gradients form a map from parameter ID
+ * to gradient, reduced with ReduceOperation::Mean; IDs, shapes and dtype
+ * must agree on every rank).  Rank r lists num_params[r] entries, in any
+ * order: entry i is (ids[r][i], bufs[r][i]), an rc_buf with the all_reduce
+ * meaning (send: that rank's gradient, recv: its output, op: normally
+ * RC_MEAN).  Entries are paired across ranks by ID and each parameter is
+ * reduced on its own, so its bits equal rc_all_reduce of its R buffers; the
+ * batch runs as rc_all_reduce_many does.  The arrays are read during the
+ * call only.
+ * Errors, in this order, nothing enqueued: a negative count, NULL arrays
+ * with a positive count, or an ID listed twice by one rank:
+ * RC_ERR_INVALID_ARGUMENT; the ranks' ID sets differ (including their
+ * sizes): RC_ERR_PARAM_MISMATCH; then each parameter, in ascending ID order,
+ * gets the rc_all_reduce checks, and dtype and op must be the same for the
+ * whole batch (as in rc_all_reduce_many). */
+int rc_all_reduce_params(const int* num_params, const uint64_t* const* ids, const rc_buf* const* bufs,
+                         void* stream);
+
 /* finish_collective<B> (ruCCL README sections 2 and 4: the normal end of the
  * peer's collective session).  Waits for all work on the session's GPU,
  * frees the session's scratch and closes the session.
@@ -252,6 +273,13 @@ int rc_rank_reduce(int rank, const rc_buf* buf, void* stream);
 int rc_rank_broadcast(int rank, const rc_buf* buf, void* stream);
 int rc_rank_reduce_scatter(int rank, const rc_buf* buf, void* stream);
 int rc_rank_all_gather(int rank, const rc_buf* buf, void* stream);
+
+/* Rank `rank`'s side of rc_all_reduce_params: its own num_params entries
+ * (ids[i], bufs[i]), in any order.  The gradient sync as the pages call it,
+ * once per rank with that rank's parameter map.  The arrays are read before
+ * the call returns. */
+int rc_rank_all_reduce_params(int rank, int num_params, const uint64_t* ids, const rc_buf* bufs,
+                              void* stream);
 
 /* finish_collective<B> for one peer: the rank leaves the session.  When the
  * last registered rank has finished, the session waits for the GPU, frees its

@@ -5,8 +5,10 @@ kernels; PyTorch supplies device memory and streams.  The functions mirror the
 public tensor collective API of the ruCCL README (ja), user guide section 2
 (register, all_reduce, reduce, broadcast, finish_collective, reset_collective),
 plus reduce_scatter_tensor and all_gather_into_tensor of the monarch
-Communicator page, and a whole-gradient all_reduce_many (section 6,
-"Collective training").
+Communicator page, a whole-gradient all_reduce_many and the parameter-keyed
+gradient sync all_reduce_params (section 6, "Collective training"), and a
+per-rank front end (rank_*) in which each logical rank calls from its own
+thread.
 
     import rank_reductions_amd as rr
     rr.register(4)
@@ -28,7 +30,9 @@ __all__ = [
     "all_gather", "all_reduce_many", "finish", "reset", "library", "library_path",
     "RC_OK", "RC_ERR_NOT_REGISTERED", "RC_ERR_DUPLICATE_REGISTRATION", "RC_ERR_SHAPE_MISMATCH",
     "RC_ERR_OP_MISMATCH", "RC_ERR_ROOT_MISMATCH", "RC_ERR_BROADCAST_SENDERS",
-    "RC_ERR_DTYPE_MISMATCH", "RC_ERR_INVALID_ARGUMENT", "RC_ERR_DEVICE",
+    "RC_ERR_DTYPE_MISMATCH", "RC_ERR_INVALID_ARGUMENT", "RC_ERR_DEVICE", "RC_ERR_PARAM_MISMATCH",
+    "all_reduce_params", "rank_register", "rank_finish", "rank_all_reduce", "rank_reduce",
+    "rank_broadcast", "rank_reduce_scatter", "rank_all_gather", "rank_all_reduce_params",
 ]
 
 RC_MAX_RANKS = 16
@@ -49,6 +53,7 @@ RC_ERR_BROADCAST_SENDERS = 6
 RC_ERR_DTYPE_MISMATCH = 7
 RC_ERR_INVALID_ARGUMENT = 8
 RC_ERR_DEVICE = 9
+RC_ERR_PARAM_MISMATCH = 10
 
 OPS = {"sum": RC_SUM, "mean": RC_MEAN, "max": RC_MAX}
 ALGOS = {"auto": RC_ALGO_AUTO, "direct": RC_ALGO_DIRECT, "ring": RC_ALGO_RING}
@@ -136,6 +141,11 @@ def library():
         fn = getattr(lib, name)
         fn.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
         fn.restype = ctypes.c_int
+    lib.rc_all_reduce_params.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.rc_all_reduce_params.restype = ctypes.c_int
+    lib.rc_rank_all_reduce_params.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p]
+    lib.rc_rank_all_reduce_params.restype = ctypes.c_int
     lib.rc_rank_finish.argtypes = [ctypes.c_int]
     lib.rc_rank_finish.restype = ctypes.c_int
     _lib = lib
@@ -364,6 +374,43 @@ def all_reduce_many(tensors, op="mean", out=None, stream=None):
     return out
 
 
+def _param_entries(grads, outs, op):
+    """One rank's map as (count, ids array, rc_buf array), in the map's order."""
+    keys = list(grads)
+    n = len(keys)
+    ids = (ctypes.c_uint64 * max(n, 1))(*[int(k) for k in keys])
+    if not n:
+        return 0, ids, (RcBuf * 1)()
+    bufs = make_bufs([_ptr(grads[k]) for k in keys], [_ptr(outs[k]) for k in keys],
+                     [tuple(grads[k].shape) for k in keys], [_dtype_code(grads[k]) for k in keys], op)
+    return n, ids, bufs
+
+
+def _first_tensor(maps):
+    return next((v for m in maps for v in m.values()), None)
+
+
+def all_reduce_params(grads, op="mean", out=None, stream=None):
+    """Gradient sync keyed by parameter ID (ruCCL README section 6,
+    grads.all_reduce_with(communicator, ReduceOperation::Mean)).  grads[r] is
+    rank r's map {parameter id: CUDA tensor}; entries pair across ranks by ID,
+    whatever order each map lists them in.  Returns out: one map per rank with
+    the reduced tensors (allocated when out is None).  Different ID sets raise
+    CollectiveError with RC_ERR_PARAM_MISMATCH."""
+    torch = _torch()
+    R = len(grads)
+    if out is None:
+        out = [{k: torch.empty_like(v) for k, v in g.items()} for g in grads]
+    entries = [_param_entries(g, o, _op(op)) for g, o in zip(grads, out)]
+    counts = (ctypes.c_int * R)(*[e[0] for e in entries])
+    ids = (ctypes.c_void_p * R)(*[ctypes.addressof(e[1]) for e in entries])
+    bufs = (ctypes.c_void_p * R)(*[ctypes.addressof(e[2]) for e in entries])
+    ref = _first_tensor(grads)
+    s = _stream(stream, ref) if ref is not None else (_stream(stream, None) if stream is not None else 0)
+    check(library().rc_all_reduce_params(counts, ids, bufs, ctypes.c_void_p(s)))
+    return out
+
+
 # ---------------------------------------------------------------- per-rank front end
 #
 # Each logical rank calls these from its own thread with its own tensors and
@@ -427,4 +474,17 @@ def rank_all_gather(rank, shard, num_ranks, out=None, stream=None):
     if out is None:
         out = torch.empty(num_ranks * shard.numel(), dtype=shard.dtype, device=shard.device)
     _rank_call(library().rc_rank_all_gather, rank, shard, out, RC_SUM, 0, stream)
+    return out
+
+
+def rank_all_reduce_params(rank, grads, op="mean", out=None, stream=None):
+    """Rank `rank`'s side of all_reduce_params: its own map {id: tensor}."""
+    torch = _torch()
+    if out is None:
+        out = {k: torch.empty_like(v) for k, v in grads.items()}
+    n, ids, bufs = _param_entries(grads, out, _op(op))
+    ref = _first_tensor([grads])
+    s = _stream(stream, ref) if ref is not None else (_stream(stream, None) if stream is not None else 0)
+    check(library().rc_rank_all_reduce_params(int(rank), n, ctypes.addressof(ids), ctypes.addressof(bufs),
+                                              ctypes.c_void_p(s)))
     return out

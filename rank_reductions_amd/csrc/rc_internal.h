@@ -104,9 +104,15 @@ struct Error {
 
 // ---------------------------------------------------------------- validate.cpp
 Error validate(Coll coll, int nranks, const rc_buf* bufs, Checked* out);
-// Tensor t of a batched all-reduce; messages name the tensor index.
+// Tensor t of a batched all-reduce; messages name the tensor index, or
+// ids[t] when ids is given (a gradient sync's parameter IDs).
 Error validate_batch(int nranks, int num_tensors, const rc_buf* bufs,
-                     std::vector<Checked>* out);
+                     std::vector<Checked>* out, const uint64_t* ids = nullptr);
+// Pairs the ranks' gradient entries by parameter ID: rank r has counts[r]
+// entries (ids[r][i], bufs[r][i]).  On success tensor_major[t*R + r] is rank
+// r's buffer of the t-th smallest ID, order[t].
+Error match_params(int nranks, const int* counts, const uint64_t* const* ids, const rc_buf* const* bufs,
+                   std::vector<rc_buf>* tensor_major, std::vector<uint64_t>* order);
 int64_t element_size(int dtype);
 
 // ---------------------------------------------------------------- plan.cpp

@@ -35,6 +35,11 @@ struct Slot {
     std::vector<rc_buf> bufs;
     std::vector<uint8_t> have_buf;
     std::vector<void*> streams;
+    // gradient sync (all_reduce_params): each rank's entries
+    std::vector<uint8_t> is_params;
+    std::vector<int> pcount;
+    std::vector<std::vector<uint64_t>> pids;
+    std::vector<std::vector<rc_buf>> pbufs;
     uint32_t arrived = 0;
     int left = 0;
     bool done = false;
@@ -183,14 +188,29 @@ const char* coll_name(Coll c) {
     return "?";
 }
 
-// Launches one matched collective on `stream` (the last rank's), ordered
-// against every rank's stream.  Every other rank is blocked inside its call
-// and has enqueued nothing since making it, so an event recorded on its
-// stream now marks that rank's call point; after the kernels, the same
-// streams wait on `done` before anything the ranks enqueue once they return.
-// Each distinct stream is joined once, and a stream shared with the launching
-// rank needs no event at all.
-Error launch_joined(const Checked& ck, const std::vector<void*>& streams, void* stream) {
+// A validated batch of all-reduces: tensors large enough get launches of
+// their own, the rest share one batched launch.
+Error launch_batch(const std::vector<Checked>& cks, void* stream) {
+    std::vector<Checked> own, batched;
+    split_batch(cks, &own, &batched);
+    for (const Checked& ck : own) {
+        Error e = launch(ck, stream);
+        if (e.code) return e;
+    }
+    const BatchPlan bp = plan_batch(batched, g_s.cfg, g_s.dev);
+    if (bp.total_tiles == 0) return {};
+    return device_launch_batch(bp, stream);
+}
+
+// Runs `enqueue` (the kernels of one matched collective) on `stream`, the
+// last rank's, ordered against every rank's stream.  Every other rank is
+// blocked inside its call and has enqueued nothing since making it, so an
+// event recorded on its stream now marks that rank's call point; after the
+// kernels, the same streams wait on `done` before anything the ranks enqueue
+// once they return.  Each distinct stream is joined once, and a stream shared
+// with the launching rank needs no event at all.
+template <class Enqueue>
+Error launch_joined(const std::vector<void*>& streams, void* stream, Enqueue enqueue) {
     RankEvents& ev = *g_s.events;
     std::vector<void*> others;
     for (void* s : streams)
@@ -200,38 +220,78 @@ Error launch_joined(const Checked& ck, const std::vector<void*>& streams, void* 
         e = device_event_record(ev.arrive[i], others[i]);
         if (!e.code) e = device_stream_wait(stream, ev.arrive[i]);
     }
-    if (!e.code) e = launch(ck, stream);
+    if (!e.code) e = enqueue();
     if (!e.code && !others.empty()) e = device_event_record(ev.done, stream);
     for (size_t i = 0; i < others.size() && !e.code; ++i) e = device_stream_wait(others[i], ev.done);
     return e;
 }
 
+const char* kind_name(const Slot& s, int r) {
+    return s.is_params[r] ? "all_reduce_params" : coll_name(s.kinds[r]);
+}
+
+// Pairs a gradient sync's entries by parameter ID and validates the batch.
+Error check_params(int R, const std::vector<int>& counts, const std::vector<const uint64_t*>& ids,
+                   const std::vector<const rc_buf*>& bufs, std::vector<Checked>* cks) {
+    std::vector<rc_buf> tensor_major;
+    std::vector<uint64_t> order;
+    Error e = match_params(R, counts.data(), ids.data(), bufs.data(), &tensor_major, &order);
+    if (e.code) return e;
+    return validate_batch(R, (int)order.size(), tensor_major.data(), cks, order.data());
+}
+
 // The last rank of a slot: check the R sides against each other and launch.
 void complete_slot(Slot& s, void* stream) {
+    if (s.status != RC_OK) return;  // an argument error recorded at arrival
     const int R = g_s.nranks;
-    for (int r = 0; r < R; ++r) {
-        if (!s.have_buf[r]) {
-            s.status = RC_ERR_INVALID_ARGUMENT;
-            s.msg = "rank " + std::to_string(r) + " passed a NULL rc_buf";
-            return;
-        }
-    }
     for (int r = 1; r < R; ++r) {
-        if (s.kinds[r] != s.kinds[0]) {
+        if (s.kinds[r] != s.kinds[0] || s.is_params[r] != s.is_params[0]) {
             s.status = RC_ERR_OP_MISMATCH;
-            s.msg = std::string("rank ") + std::to_string(r) + " called " + coll_name(s.kinds[r]) +
-                    " where rank 0 called " + coll_name(s.kinds[0]);
+            s.msg = std::string("rank ") + std::to_string(r) + " called " + kind_name(s, r) +
+                    " where rank 0 called " + kind_name(s, 0);
             return;
         }
     }
-    Checked ck;
-    Error e = validate(s.kinds[0], R, s.bufs.data(), &ck);
-    if (!e.code && !g_s.cfg.validate_only) e = launch_joined(ck, s.streams, stream);
+    Error e;
+    if (s.is_params[0]) {
+        std::vector<const uint64_t*> ids(R);
+        std::vector<const rc_buf*> bufs(R);
+        for (int r = 0; r < R; ++r) {
+            ids[r] = s.pids[r].data();
+            bufs[r] = s.pbufs[r].data();
+        }
+        std::vector<Checked> cks;
+        e = check_params(R, s.pcount, ids, bufs, &cks);
+        if (!e.code && !g_s.cfg.validate_only)
+            e = launch_joined(s.streams, stream, [&] { return launch_batch(cks, stream); });
+    } else {
+        for (int r = 0; r < R; ++r) {
+            if (!s.have_buf[r]) {
+                s.status = RC_ERR_INVALID_ARGUMENT;
+                s.msg = "rank " + std::to_string(r) + " passed a NULL rc_buf";
+                return;
+            }
+        }
+        Checked ck;
+        e = validate(s.kinds[0], R, s.bufs.data(), &ck);
+        if (!e.code && !g_s.cfg.validate_only)
+            e = launch_joined(s.streams, stream, [&] { return launch(ck, stream); });
+    }
     s.status = e.code;
     s.msg = e.msg;
 }
 
-int rank_collective(Coll coll, int rank, const rc_buf* buf, void* stream) {
+// One rank's side of a collective (params == nullptr) or of a gradient sync.
+struct RankArgs {
+    Coll coll = Coll::AllReduce;
+    const rc_buf* buf = nullptr;
+    bool params = false;
+    int count = 0;
+    const uint64_t* ids = nullptr;
+    const rc_buf* bufs = nullptr;
+};
+
+int rank_collective(const RankArgs& a, int rank, void* stream) {
     std::unique_lock<std::mutex> lock(g_mu);
     if (g_s.mode != Mode::PerRank)
         return report(Error{RC_ERR_NOT_REGISTERED, "no per-rank session: call rc_rank_register first"});
@@ -254,11 +314,29 @@ int rank_collective(Coll coll, int rank, const rc_buf* buf, void* stream) {
         sp->bufs.assign(R, rc_buf{});
         sp->have_buf.assign(R, 0);
         sp->streams.assign(R, nullptr);
+        sp->is_params.assign(R, 0);
+        sp->pcount.assign(R, 0);
+        sp->pids.assign(R, {});
+        sp->pbufs.assign(R, {});
     }
     std::shared_ptr<Slot> s = sp;
-    s->kinds[rank] = coll;
-    if (buf) {
-        s->bufs[rank] = *buf;
+    s->kinds[rank] = a.coll;
+    s->is_params[rank] = a.params;
+    if (a.params) {
+        // copied now: the caller's arrays need only live through the call
+        if (a.count < 0 || (a.count > 0 && (!a.ids || !a.bufs))) {
+            if (s->status == RC_OK) {
+                s->status = RC_ERR_INVALID_ARGUMENT;
+                s->msg = "rank " + std::to_string(rank) +
+                         ": all_reduce_params needs num_params >= 0 and non-NULL ids and bufs";
+            }
+        } else {
+            s->pcount[rank] = a.count;
+            s->pids[rank].assign(a.ids, a.ids + a.count);
+            s->pbufs[rank].assign(a.bufs, a.bufs + a.count);
+        }
+    } else if (a.buf) {
+        s->bufs[rank] = *a.buf;
         s->have_buf[rank] = 1;
     }
     s->streams[rank] = stream;
@@ -311,15 +389,26 @@ int rc_all_reduce_many(int num_tensors, const rc_buf* bufs, void* stream) {
     Error e = validate_batch(g_s.nranks, num_tensors, bufs, &cks);
     if (e.code) return report(e);
     if (g_s.cfg.validate_only) return ok();
-    std::vector<Checked> own, batched;
-    split_batch(cks, &own, &batched);
-    for (const Checked& ck : own) {
-        e = launch(ck, stream);
-        if (e.code) return report(e);
-    }
-    const BatchPlan bp = plan_batch(batched, g_s.cfg, g_s.dev);
-    if (bp.total_tiles == 0) return ok();
-    return report(device_launch_batch(bp, stream));
+    return report(launch_batch(cks, stream));
+}
+
+int rc_all_reduce_params(const int* num_params, const uint64_t* const* ids, const rc_buf* const* bufs,
+                         void* stream) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (g_s.mode == Mode::None)
+        return report(Error{RC_ERR_NOT_REGISTERED, "no session: call rc_register first"});
+    if (g_s.mode == Mode::PerRank)
+        return report(Error{RC_ERR_INVALID_ARGUMENT, "the session was opened per rank"});
+    const int R = g_s.nranks;
+    if (!num_params || !ids || !bufs)
+        return report(Error{RC_ERR_INVALID_ARGUMENT, "all_reduce_params: NULL num_params, ids or bufs"});
+    std::vector<int> counts(num_params, num_params + R);
+    std::vector<Checked> cks;
+    Error e = check_params(R, counts, std::vector<const uint64_t*>(ids, ids + R),
+                           std::vector<const rc_buf*>(bufs, bufs + R), &cks);
+    if (e.code) return report(e);
+    if (g_s.cfg.validate_only) return ok();
+    return report(launch_batch(cks, stream));
 }
 
 int rc_finish(void) {
@@ -363,20 +452,33 @@ int rc_rank_register(int rank, int num_ranks, const rc_config* cfg) {
     return ok();
 }
 
+static int rank_call(Coll coll, int rank, const rc_buf* buf, void* stream) {
+    RankArgs a;
+    a.coll = coll;
+    a.buf = buf;
+    return rank_collective(a, rank, stream);
+}
+
 int rc_rank_all_reduce(int rank, const rc_buf* buf, void* stream) {
-    return rank_collective(Coll::AllReduce, rank, buf, stream);
+    return rank_call(Coll::AllReduce, rank, buf, stream);
 }
-int rc_rank_reduce(int rank, const rc_buf* buf, void* stream) {
-    return rank_collective(Coll::Reduce, rank, buf, stream);
-}
+int rc_rank_reduce(int rank, const rc_buf* buf, void* stream) { return rank_call(Coll::Reduce, rank, buf, stream); }
 int rc_rank_broadcast(int rank, const rc_buf* buf, void* stream) {
-    return rank_collective(Coll::Broadcast, rank, buf, stream);
+    return rank_call(Coll::Broadcast, rank, buf, stream);
 }
 int rc_rank_reduce_scatter(int rank, const rc_buf* buf, void* stream) {
-    return rank_collective(Coll::ReduceScatter, rank, buf, stream);
+    return rank_call(Coll::ReduceScatter, rank, buf, stream);
 }
 int rc_rank_all_gather(int rank, const rc_buf* buf, void* stream) {
-    return rank_collective(Coll::AllGather, rank, buf, stream);
+    return rank_call(Coll::AllGather, rank, buf, stream);
+}
+int rc_rank_all_reduce_params(int rank, int num_params, const uint64_t* ids, const rc_buf* bufs, void* stream) {
+    RankArgs a;
+    a.params = true;
+    a.count = num_params;
+    a.ids = ids;
+    a.bufs = bufs;
+    return rank_collective(a, rank, stream);
 }
 
 int rc_rank_finish(int rank) {
@@ -406,6 +508,7 @@ const char* rc_status_name(int status) {
         case RC_ERR_DTYPE_MISMATCH: return "RC_ERR_DTYPE_MISMATCH";
         case RC_ERR_INVALID_ARGUMENT: return "RC_ERR_INVALID_ARGUMENT";
         case RC_ERR_DEVICE: return "RC_ERR_DEVICE";
+        case RC_ERR_PARAM_MISMATCH: return "RC_ERR_PARAM_MISMATCH";
         default: return "RC_UNKNOWN_STATUS";
     }
 }

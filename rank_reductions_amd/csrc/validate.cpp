@@ -260,31 +260,87 @@ Error validate(Coll coll, int R, const rc_buf* bufs, Checked* ck) {
     return e;
 }
 
-Error validate_batch(int R, int num_tensors, const rc_buf* bufs, std::vector<Checked>* out) {
-    if (num_tensors < 0)
-        return fail(RC_ERR_INVALID_ARGUMENT, "all_reduce_many: num_tensors is negative");
-    if (num_tensors > 0 && !bufs) return fail(RC_ERR_INVALID_ARGUMENT, "all_reduce_many: bufs is NULL");
+Error validate_batch(int R, int num_tensors, const rc_buf* bufs, std::vector<Checked>* out,
+                     const uint64_t* ids) {
+    const char* who = ids ? "all_reduce_params" : "all_reduce_many";
+    auto name = [&](int t) {
+        return ids ? "parameter " + std::to_string(ids[t]) : "tensor " + std::to_string(t);
+    };
+    if (num_tensors < 0) return fail(RC_ERR_INVALID_ARGUMENT, std::string(who) + ": num_tensors is negative");
+    if (num_tensors > 0 && !bufs) return fail(RC_ERR_INVALID_ARGUMENT, std::string(who) + ": bufs is NULL");
     out->assign(num_tensors, Checked{});
     for (int t = 0; t < num_tensors; ++t) {
         Error e = validate_fields(Coll::AllReduce, R, bufs + (int64_t)t * R, &(*out)[t]);
         if (e.code) {
-            e.msg = fmt("all_reduce_many: tensor %lld: ", t) + e.msg;
+            e.msg = std::string(who) + ": " + name(t) + ": " + e.msg;
             return e;
         }
     }
     // ops and dtypes must agree across the whole batch: one launch family
     for (int t = 1; t < num_tensors; ++t) {
         if ((*out)[t].dtype != (*out)[0].dtype)
-            return fail(RC_ERR_DTYPE_MISMATCH, fmt("all_reduce_many: tensor %lld dtype differs from tensor 0's", t));
+            return fail(RC_ERR_DTYPE_MISMATCH,
+                        std::string(who) + ": " + name(t) + " dtype differs from " + name(0) + "'s");
         if ((*out)[t].op != (*out)[0].op)
-            return fail(RC_ERR_OP_MISMATCH, fmt("all_reduce_many: tensor %lld op differs from tensor 0's", t));
+            return fail(RC_ERR_OP_MISMATCH, std::string(who) + ": " + name(t) + " op differs from " + name(0) + "'s");
     }
     std::vector<Range> writes, reads;
     for (int t = 0; t < num_tensors; ++t)
         if ((*out)[t].count) ranges_of((*out)[t], t, &writes, &reads);
     Error e = check_overlaps(writes, reads);
-    if (e.code) e.msg = "all_reduce_many: " + e.msg;
+    if (e.code) e.msg = std::string(who) + ": " + e.msg;
     return e;
+}
+
+// Gradient sync keyed by parameter ID (ruCCL README section 6, "Collective
+// training": IDs, shapes and dtype agree on every rank).  Each rank's entries
+// are sorted by ID; a repeated ID within a rank is an argument error, and ID
+// lists that differ between ranks are a parameter mismatch named by the first
+// ID that one side lacks.
+Error match_params(int R, const int* counts, const uint64_t* const* ids, const rc_buf* const* bufs,
+                   std::vector<rc_buf>* tensor_major, std::vector<uint64_t>* order) {
+    std::vector<std::vector<int>> perm(R);
+    for (int r = 0; r < R; ++r) {
+        if (counts[r] < 0)
+            return fail(RC_ERR_INVALID_ARGUMENT, fmt("all_reduce_params: rank %lld: num_params is negative", r));
+        if (counts[r] > 0 && (!ids[r] || !bufs[r]))
+            return fail(RC_ERR_INVALID_ARGUMENT, fmt("all_reduce_params: rank %lld: ids or bufs is NULL", r));
+        perm[r].resize(counts[r]);
+        for (int i = 0; i < counts[r]; ++i) perm[r][i] = i;
+        const uint64_t* id = ids[r];
+        std::sort(perm[r].begin(), perm[r].end(), [id](int a, int b) { return id[a] < id[b]; });
+        for (int i = 1; i < counts[r]; ++i)
+            if (id[perm[r][i]] == id[perm[r][i - 1]])
+                return fail(RC_ERR_INVALID_ARGUMENT, "all_reduce_params: rank " + std::to_string(r) +
+                                                         " lists parameter " + std::to_string(id[perm[r][i]]) +
+                                                         " twice");
+    }
+    for (int r = 1; r < R; ++r) {
+        // walk both sorted lists to the first ID present on one side only
+        int i = 0, j = 0;
+        while (i < counts[0] || j < counts[r]) {
+            const bool has0 = i < counts[0], hasr = j < counts[r];
+            const uint64_t a = has0 ? ids[0][perm[0][i]] : 0, b = hasr ? ids[r][perm[r][j]] : 0;
+            if (has0 && hasr && a == b) {
+                ++i, ++j;
+                continue;
+            }
+            const bool missing_on_r = has0 && (!hasr || a < b);
+            const uint64_t pid = missing_on_r ? a : b;
+            return fail(RC_ERR_PARAM_MISMATCH,
+                        "all_reduce_params: parameter " + std::to_string(pid) +
+                            (missing_on_r ? " is on rank 0 but not on rank " + std::to_string(r)
+                                          : " is on rank " + std::to_string(r) + " but not on rank 0"));
+        }
+    }
+    const int P = R ? counts[0] : 0;
+    order->resize(P);
+    tensor_major->assign((size_t)P * R, rc_buf{});
+    for (int t = 0; t < P; ++t) {
+        (*order)[t] = ids[0][perm[0][t]];
+        for (int r = 0; r < R; ++r) (*tensor_major)[(size_t)t * R + r] = bufs[r][perm[r][t]];
+    }
+    return {};
 }
 
 }  // namespace rc

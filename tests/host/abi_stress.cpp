@@ -67,7 +67,7 @@ void worker(int id, int iters, int R) {
             default: rc = rc_all_reduce(bufs.data(), nullptr); break;
         }
         const char* err = rc_last_error();
-        if (rc < 0 || rc > RC_ERR_DEVICE) ++g_bad;
+        if (rc < 0 || rc > RC_ERR_PARAM_MISMATCH) ++g_bad;
         if (rc == RC_OK && err[0] != '\0') ++g_bad;
         if (rc != RC_OK && err[0] == '\0') ++g_bad;
         if (kind == 5 && rc == RC_OK) ++g_bad;  // a mismatch must never pass
@@ -117,7 +117,7 @@ void fuzz(int iters, int R) {
             case 4: rc = rc_all_gather(bufs.data(), nullptr); break;
             default: rc = rc_all_reduce_many(3, bufs.data(), nullptr); break;
         }
-        if (rc < 0 || rc > RC_ERR_DEVICE) ++g_bad;
+        if (rc < 0 || rc > RC_ERR_PARAM_MISMATCH) ++g_bad;
     }
 }
 

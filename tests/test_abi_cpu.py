@@ -58,7 +58,7 @@ def test_library_exports_every_declared_symbol(lib):
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (rc_\w+)", out))
     assert set(declared_functions()) <= exported
-    assert lib.rc_abi_version() == 1
+    assert lib.rc_abi_version() == 2
 
 
 def test_struct_layout_matches_a_c_compiler(tmp_path):

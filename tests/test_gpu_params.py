@@ -1,0 +1,142 @@
+"""The parameter-keyed gradient sync on the GPU, bit for bit against the CPU
+oracle's all_reduce_params: per-rank maps listed in different orders, empty
+and scalar parameters, a parameter large enough for a launch of its own, in
+place, from one thread and from one thread per rank."""
+
+import random
+import threading
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rank_reductions_amd as rr
+import synth_inputs as si
+from gpu_util import SENTINEL, assert_bits, host, session
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+# parameter id -> shape: several tiles, ragged tails, empty, scalar
+SMALL = {101: (512, 33), 7: (257,), 9000: (0,), 3: (), 42: (4096,), 5: (3, 1000, 7), 77: (65_537,)}
+
+
+def make_maps(R, specs, seed, sigma=1e-3):
+    """R maps {id: tensor}, each rank listing its IDs in its own order."""
+    maps = []
+    for r in range(R):
+        keys = list(specs)
+        random.Random(seed * 31 + r).shuffle(keys)
+        maps.append({k: si.torch_tensor_for(seed, k, R, r, specs[k], device=DEV) for k in keys})
+    return maps
+
+
+def host_maps(maps):
+    return [{k: host(v) for k, v in m.items()} for m in maps]
+
+
+def check(got, want, what):
+    for r, (g, w) in enumerate(zip(got, want)):
+        assert set(g) == set(w), f"{what}: rank {r} IDs"
+        for k in w:
+            assert_bits(host(g[k]), w[k], f"{what}: rank {r} parameter {k}")
+
+
+@pytest.mark.parametrize("R", [1, 2, 4, 8])
+@pytest.mark.parametrize("op", ["mean", "sum"])
+def test_params_whole_call(R, op):
+    maps = make_maps(R, SMALL, seed=50 + R)
+    torch.cuda.synchronize()
+    want = oracle.all_reduce_params(host_maps(maps), op)
+    with session(R, device=0):
+        got = rr.all_reduce_params(maps, op)
+        torch.cuda.synchronize()
+    check(got, want, f"R={R} {op}")
+
+
+def test_params_with_own_launch_tensor_and_in_place():
+    """A 64 MiB parameter takes its own fold launch, the rest share the
+    batched launch; in place (out = grads) as an optimizer would use it."""
+    R = 4
+    specs = dict(SMALL)
+    specs[1 << 40] = (4096, 4096)  # 64 MiB per rank
+    maps = make_maps(R, specs, seed=61)
+    torch.cuda.synchronize()
+    want = oracle.all_reduce_params(host_maps(maps), "mean")
+    with session(R, device=0):
+        rr.all_reduce_params(maps, "mean", out=maps)
+        torch.cuda.synchronize()
+    check(maps, want, "in place")
+
+
+def test_params_mismatch_touches_nothing():
+    R = 3
+    maps = make_maps(R, SMALL, seed=62)
+    del maps[1][42]
+    outs = [{k: torch.full(v.shape, SENTINEL, dtype=torch.int32, device=DEV).view(torch.float32)
+             for k, v in m.items()} for m in maps]
+    with session(R, device=0):
+        with pytest.raises(rr.CollectiveError) as ei:
+            rr.all_reduce_params(maps, "mean", out=outs)
+        assert ei.value.code == rr.RC_ERR_PARAM_MISMATCH
+        torch.cuda.synchronize()
+    for m in outs:
+        for v in m.values():
+            assert torch.all(v.view(torch.int32) == SENTINEL).item()
+
+
+@pytest.mark.parametrize("n_streams", [1, 4])
+def test_params_rank_threads(n_streams):
+    """The pages' calling pattern: each rank's thread syncs its own map on
+    its own stream; the producer runs right before the call and the
+    consumer right after, with no host synchronisation."""
+    R = 4
+    maps = make_maps(R, SMALL, seed=63 + n_streams)
+    torch.cuda.synchronize()
+    want = oracle.all_reduce_params(host_maps(maps), "mean")
+    pool = [torch.cuda.Stream() for _ in range(n_streams)]
+    for r in range(R):
+        rr.rank_register(r, R, device=0)
+    errs = []
+    got = [None] * R
+
+    def rank(r):
+        try:
+            s = pool[r % n_streams]
+            with torch.cuda.stream(s):
+                grads = {k: (v * 2.0 - v) / 1.0 for k, v in maps[r].items()}  # exact copy, on s
+                out = rr.rank_all_reduce_params(r, grads, "mean", stream=s)
+                got[r] = {k: v.clone() for k, v in out.items()}
+                for v in grads.values():
+                    v.mul_(0)
+        except BaseException as e:  # noqa: BLE001
+            errs.append(e)
+
+    try:
+        ts = [threading.Thread(target=rank, args=(r,)) for r in range(R)]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join(timeout=120)
+        assert not errs, errs
+        torch.cuda.synchronize()
+        check(got, want, f"rank threads, {n_streams} streams")
+    finally:
+        for r in range(R):
+            rr.rank_finish(r)
+
+
+def test_params_equal_all_reduce_many_bits():
+    """The same tensors through all_reduce_many in ID order give the same bits."""
+    R = 4
+    maps = make_maps(R, SMALL, seed=64)
+    order = sorted(SMALL)
+    with session(R, device=0):
+        a = rr.all_reduce_params(maps, "mean")
+        b = rr.all_reduce_many([[maps[r][k] for r in range(R)] for k in order], "mean")
+        torch.cuda.synchronize()
+    for t, k in enumerate(order):
+        for r in range(R):
+            assert torch.equal(a[r][k].view(-1).view(torch.int32), b[t][r].view(-1).view(torch.int32))
+    assert np.all([set(m) == set(SMALL) for m in a])
