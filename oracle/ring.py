@@ -293,7 +293,7 @@ class ParamMismatch(OracleError):
         self.kind = kind
 
 
-def all_reduce_params(grads, op=MEAN):
+def all_reduce_params(grads, op=MEAN, acc=None):
     """Whole-gradient sync of ruCCL README section 6, "Collective training":
     every rank holds a map from parameter ID to gradient and reduces it with
     ReduceOperation::Mean; the IDs, each gradient's shape and the dtype must
@@ -304,7 +304,14 @@ def all_reduce_params(grads, op=MEAN):
     does not matter); each parameter is reduced on its own, exactly as one
     all_reduce of that parameter's R tensors; mismatches are checked IDs
     first, then per parameter (in ID order) dtype before shape.  Returns R
-    maps {id: reduced array}, every rank's values identical."""
+    maps {id: reduced array}, every rank's values identical.
+
+    acc, if given, is one map per rank of accumulated gradients (RUDA
+    "Training and state saving": the accumulator sums microbatch gradients
+    and hands the sum to the sync).  A parameter with an accumulator is
+    reduced over accumulate(acc, grad), the last microbatch added first.
+    Readings: a non-empty parameter has an accumulator on every rank or on
+    none; accumulated gradients are reduced with Sum or Mean only."""
     R = len(grads)
     if R == 0:
         raise OracleError("need at least one rank")
@@ -322,7 +329,16 @@ def all_reduce_params(grads, op=MEAN):
             raise ParamMismatch("shape", f"parameter {pid}: shape differs between ranks")
     out = [{} for _ in range(R)]
     for pid in ids:
-        reduced = all_reduce([grads[r][pid] for r in range(R)], op)
+        operands = [grads[r][pid] for r in range(R)]
+        if acc is not None and np.asarray(operands[0]).size:
+            given = [pid in acc[r] for r in range(R)]
+            if any(given) and not all(given):
+                raise OracleError(f"parameter {pid}: accumulator on some ranks only")
+            if all(given):
+                if op == MAX:
+                    raise OracleError(f"parameter {pid}: accumulated gradients reduce with Sum or Mean")
+                operands = [accumulate(acc[r][pid], operands[r]) for r in range(R)]
+        reduced = all_reduce(operands, op)
         for r in range(R):
             out[r][pid] = reduced[r]
     return out

@@ -396,6 +396,37 @@ def pin_params(orc):
     expect("dtype", both)
 
 
+def pin_params_accumulated(orc):
+    """The sync of accumulated gradients (ruCCL README section 6 with the
+    GradientsAccumulator of RUDA "Training and state saving"): integer-valued
+    accumulators and gradients reduce to the exact int64 sum of acc + grad
+    over ranks (Mean: divided by R, rounded once); parameters without
+    accumulators keep the plain result; an accumulator on some ranks only, or
+    with Max, is refused."""
+    rng = _rng(31)
+    R = 4
+    grads = _param_maps(rng, R, PARAM_SPECS, seed_order=7)
+    accs = [{pid: rng.integers(-(1 << 20), (1 << 20) + 1, size=np.shape(m[pid])).astype(np.float32)
+             for pid in (7, 3, 42)} for m in grads]
+    for op in (orc.SUM, orc.MEAN):
+        out = orc.all_reduce_params(grads, op, acc=accs)
+        for pid, shape in PARAM_SPECS:
+            terms = [grads[r][pid].astype(np.int64) + (accs[r][pid].astype(np.int64) if pid in accs[r] else 0)
+                     for r in range(R)]
+            exact = np.sum(np.stack(terms), axis=0)
+            want = exact.astype(np.float32) if op == orc.SUM else (exact.astype(np.float64) / R).astype(np.float32)
+            for r in range(R):
+                assert_bits_equal(out[r][pid], want.reshape(shape), f"{op} id {pid} rank {r} with accumulators")
+    partial = [dict(a) for a in accs]
+    del partial[2][3]
+    for bad, op in ((partial, orc.MEAN), (accs, orc.MAX)):
+        try:
+            orc.all_reduce_params(grads, op, acc=bad)
+        except orc.OracleError:
+            continue
+        raise AssertionError("an invalid accumulator set was accepted")
+
+
 def pin_accumulate(orc):
     """GradientsAccumulator.accumulate (RUDA "Training and state saving"):
     adds without averaging, so integer-valued float32 gradients accumulate to
@@ -436,5 +467,6 @@ ALL_PINS = [
     pin_all_gather,
     pin_invariants,
     pin_params,
+    pin_params_accumulated,
     pin_accumulate,
 ]

@@ -58,9 +58,8 @@ MUTATIONS = {
                               "return [(c - k) % num_ranks for k in range(1, num_ranks + 1)]"),
     "at_many_wrong_segment": ("seg = indices // s", "seg = indices // max(s - 1, 1)"),
     "at_wrong_segment": ("c = index // segment_length(n, R)", "c = index // (segment_length(n, R) + 1)"),
-    "params_pair_by_position": ("reduced = all_reduce([grads[r][pid] for r in range(R)], op)",
-                                "reduced = all_reduce([list(grads[r].values())[sorted(ids).index(pid)] "
-                                "for r in range(R)], op)"),
+    "params_pair_by_position": ("operands = [grads[r][pid] for r in range(R)]",
+                                "operands = [list(grads[r].values())[sorted(ids).index(pid)] for r in range(R)]"),
     "params_no_id_check": ("        if set(grads[r]) != ids:\n", "        if False:\n"),
     "params_no_shape_check": ('            raise ParamMismatch("shape", f"parameter {pid}: shape differs between ranks")',
                               "            pass"),
@@ -68,9 +67,13 @@ MUTATIONS = {
                                   '            raise ParamMismatch("dtype"',
                                   "        if any(a.shape != per_rank[0].shape for a in per_rank):\n"
                                   '            raise ParamMismatch("shape"'),
-    "params_op_ignored": ("reduced = all_reduce([grads[r][pid] for r in range(R)], op)",
-                          "reduced = all_reduce([grads[r][pid] for r in range(R)], SUM)"),
+    "params_op_ignored": ("reduced = all_reduce(operands, op)", "reduced = all_reduce(operands, SUM)"),
     "params_rank0_everywhere": ("            out[r][pid] = reduced[r]", "            out[r][pid] = grads[0][pid]"),
+    "params_acc_ignored": ("                operands = [accumulate(acc[r][pid], operands[r]) for r in range(R)]",
+                           "                pass"),
+    "params_acc_from_rank0": ("                operands = [accumulate(acc[r][pid], operands[r]) for r in range(R)]",
+                              "                operands = [accumulate(acc[0][pid], operands[r]) for r in range(R)]"),
+    "params_acc_partial_accepted": ("            if any(given) and not all(given):", "            if False:"),
     "accumulate_averages": ("return combine(_flat(acc), _flat(grad), SUM).reshape(acc.shape)",
                             "return (combine(_flat(acc), _flat(grad), SUM) / np.float32(2)).reshape(acc.shape)"),
     "accumulate_aliases": ("        return grad.copy()", "        return grad"),
