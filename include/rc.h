@@ -198,24 +198,43 @@ int rc_all_gather(const rc_buf* bufs, void* stream);
  * rc_finish / rc_reset). */
 int rc_all_reduce_many(int num_tensors, const rc_buf* bufs, void* stream);
 
+/* One rank's entry of a gradient sync keyed by parameter ID.
+ *   id   the parameter ID;
+ *   acc  NULL, or that rank's gradients accumulated over earlier microbatches
+ *        (the GradientsAccumulator of RUDA "Training and state saving":
+ *        accumulate adds without averaging, grads() hands the sum over).
+ *        Same shape and dtype as buf.send, read only.  The parameter is then
+ *        reduced over acc + send, one add per element (float32 round to
+ *        nearest even, int32 wrap) before the fold: the bits of adding the
+ *        last microbatch with a separate accumulate and then syncing, in one
+ *        pass over memory.  recv may equal acc (the accumulator's storage
+ *        receives the result) as it may equal send.  Sum and Mean only.
+ *   buf  the parameter's rc_buf with the all_reduce meaning (send: the
+ *        rank's gradient, recv: its output, op: normally RC_MEAN). */
+typedef struct rc_param {
+    uint64_t id;
+    const void* acc;
+    rc_buf buf;
+} rc_param;
+
 /* Whole-gradient all-reduce keyed by parameter ID (ruCCL README section 6,
  * "Collective training": each rank's gradients form a map from parameter ID
  * to gradient, reduced with ReduceOperation::Mean; IDs, shapes and dtype
- * must agree on every rank).  Rank r lists num_params[r] entries, in any
- * order: entry i is (ids[r][i], bufs[r][i]), an rc_buf with the all_reduce
- * meaning (send: that rank's gradient, recv: its output, op: normally
- * RC_MEAN).  Entries are paired across ranks by ID and each parameter is
- * reduced on its own, so its bits equal rc_all_reduce of its R buffers; the
+ * must agree on every rank).  Rank r lists num_params[r] entries
+ * params[r][0 .. num_params[r]), in any order.  Entries are paired across
+ * ranks by ID and each parameter is reduced on its own, so its bits equal
+ * rc_all_reduce of its R buffers (of acc + send where acc is given); the
  * batch runs as rc_all_reduce_many does.  The arrays are read during the
  * call only.
- * Errors, in this order, nothing enqueued: a negative count, NULL arrays
+ * Errors, in this order, nothing enqueued: a negative count, a NULL array
  * with a positive count, or an ID listed twice by one rank:
  * RC_ERR_INVALID_ARGUMENT; the ranks' ID sets differ (including their
  * sizes): RC_ERR_PARAM_MISMATCH; then each parameter, in ascending ID order,
  * gets the rc_all_reduce checks, and dtype and op must be the same for the
- * whole batch (as in rc_all_reduce_many). */
-int rc_all_reduce_params(const int* num_params, const uint64_t* const* ids, const rc_buf* const* bufs,
-                         void* stream);
+ * whole batch (as in rc_all_reduce_many); an acc given on some ranks only,
+ * misaligned, overlapping an output other than its own rank's recv, or with
+ * RC_MAX: RC_ERR_INVALID_ARGUMENT. */
+int rc_all_reduce_params(const int* num_params, const rc_param* const* params, void* stream);
 
 /* finish_collective<B> (ruCCL README sections 2 and 4: the normal end of the
  * peer's collective session).  Waits for all work on the session's GPU,
@@ -274,12 +293,10 @@ int rc_rank_broadcast(int rank, const rc_buf* buf, void* stream);
 int rc_rank_reduce_scatter(int rank, const rc_buf* buf, void* stream);
 int rc_rank_all_gather(int rank, const rc_buf* buf, void* stream);
 
-/* Rank `rank`'s side of rc_all_reduce_params: its own num_params entries
- * (ids[i], bufs[i]), in any order.  The gradient sync as the pages call it,
- * once per rank with that rank's parameter map.  The arrays are read before
- * the call returns. */
-int rc_rank_all_reduce_params(int rank, int num_params, const uint64_t* ids, const rc_buf* bufs,
-                              void* stream);
+/* Rank `rank`'s side of rc_all_reduce_params: its own num_params entries,
+ * in any order.  The gradient sync as the pages call it, once per rank with
+ * that rank's parameter map.  The array is read before the call returns. */
+int rc_rank_all_reduce_params(int rank, int num_params, const rc_param* params, void* stream);
 
 /* finish_collective<B> for one peer: the rank leaves the session.  When the
  * last registered rank has finished, the session waits for the GPU, frees its

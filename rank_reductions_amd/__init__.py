@@ -86,6 +86,12 @@ class RcConfig(ctypes.Structure):
     ]
 
 
+class RcParam(ctypes.Structure):
+    """One rank's entry of a gradient sync: parameter ID, optional
+    accumulator, and the gradient's rc_buf."""
+    _fields_ = [("id", ctypes.c_uint64), ("acc", ctypes.c_void_p), ("buf", RcBuf)]
+
+
 # numpy view of rc_buf, for building large batches quickly
 RCBUF_NP = np.dtype([("send", "<u8"), ("recv", "<u8"), ("dtype", "<i4"), ("op", "<i4"),
                      ("root", "<i4"), ("ndim", "<i4"), ("dims", "<i8", (RC_MAX_DIMS,))])
@@ -141,10 +147,9 @@ def library():
         fn = getattr(lib, name)
         fn.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
         fn.restype = ctypes.c_int
-    lib.rc_all_reduce_params.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.rc_all_reduce_params.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.rc_all_reduce_params.restype = ctypes.c_int
-    lib.rc_rank_all_reduce_params.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
-                                              ctypes.c_void_p]
+    lib.rc_rank_all_reduce_params.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.rc_rank_all_reduce_params.restype = ctypes.c_int
     lib.rc_rank_finish.argtypes = [ctypes.c_int]
     lib.rc_rank_finish.restype = ctypes.c_int
@@ -374,40 +379,52 @@ def all_reduce_many(tensors, op="mean", out=None, stream=None):
     return out
 
 
-def _param_entries(grads, outs, op):
-    """One rank's map as (count, ids array, rc_buf array), in the map's order."""
+def _param_entries(grads, outs, op, acc=None):
+    """One rank's map as an rc_param array (in the map's order) and its length."""
     keys = list(grads)
     n = len(keys)
-    ids = (ctypes.c_uint64 * max(n, 1))(*[int(k) for k in keys])
-    if not n:
-        return 0, ids, (RcBuf * 1)()
-    bufs = make_bufs([_ptr(grads[k]) for k in keys], [_ptr(outs[k]) for k in keys],
-                     [tuple(grads[k].shape) for k in keys], [_dtype_code(grads[k]) for k in keys], op)
-    return n, ids, bufs
+    arr = (RcParam * max(n, 1))()
+    if n:
+        bufs = make_bufs([_ptr(grads[k]) for k in keys], [_ptr(outs[k]) for k in keys],
+                         [tuple(grads[k].shape) for k in keys], [_dtype_code(grads[k]) for k in keys], op)
+        for i, k in enumerate(keys):
+            arr[i].id = int(k)
+            a = acc.get(k) if acc else None
+            arr[i].acc = _ptr(a) if a is not None else None
+            arr[i].buf = bufs[i]
+    return n, arr
 
 
 def _first_tensor(maps):
     return next((v for m in maps for v in m.values()), None)
 
 
-def all_reduce_params(grads, op="mean", out=None, stream=None):
+def _stream_for(stream, ref):
+    if ref is not None:
+        return _stream(stream, ref)
+    return _stream(stream, None) if stream is not None else 0
+
+
+def all_reduce_params(grads, op="mean", out=None, stream=None, acc=None):
     """Gradient sync keyed by parameter ID (ruCCL README section 6,
     grads.all_reduce_with(communicator, ReduceOperation::Mean)).  grads[r] is
     rank r's map {parameter id: CUDA tensor}; entries pair across ranks by ID,
-    whatever order each map lists them in.  Returns out: one map per rank with
-    the reduced tensors (allocated when out is None).  Different ID sets raise
-    CollectiveError with RC_ERR_PARAM_MISMATCH."""
+    whatever order each map lists them in.  acc, if given, is one map per rank
+    of accumulated gradients (a GradientsAccumulator's sum over earlier
+    microbatches): a parameter with one is reduced over acc + grad, fused into
+    the same pass.  Returns out: one map per rank with the reduced tensors
+    (allocated when out is None; out may be grads or acc, in place).
+    Different ID sets raise CollectiveError with RC_ERR_PARAM_MISMATCH."""
     torch = _torch()
     R = len(grads)
     if out is None:
         out = [{k: torch.empty_like(v) for k, v in g.items()} for g in grads]
-    entries = [_param_entries(g, o, _op(op)) for g, o in zip(grads, out)]
+    accs = acc if acc is not None else [None] * R
+    entries = [_param_entries(g, o, _op(op), a) for g, o, a in zip(grads, out, accs)]
     counts = (ctypes.c_int * R)(*[e[0] for e in entries])
-    ids = (ctypes.c_void_p * R)(*[ctypes.addressof(e[1]) for e in entries])
-    bufs = (ctypes.c_void_p * R)(*[ctypes.addressof(e[2]) for e in entries])
-    ref = _first_tensor(grads)
-    s = _stream(stream, ref) if ref is not None else (_stream(stream, None) if stream is not None else 0)
-    check(library().rc_all_reduce_params(counts, ids, bufs, ctypes.c_void_p(s)))
+    params = (ctypes.c_void_p * R)(*[ctypes.addressof(e[1]) for e in entries])
+    s = _stream_for(stream, _first_tensor(grads))
+    check(library().rc_all_reduce_params(counts, params, ctypes.c_void_p(s)))
     return out
 
 
@@ -477,14 +494,13 @@ def rank_all_gather(rank, shard, num_ranks, out=None, stream=None):
     return out
 
 
-def rank_all_reduce_params(rank, grads, op="mean", out=None, stream=None):
-    """Rank `rank`'s side of all_reduce_params: its own map {id: tensor}."""
+def rank_all_reduce_params(rank, grads, op="mean", out=None, stream=None, acc=None):
+    """Rank `rank`'s side of all_reduce_params: its own map {id: tensor}, and
+    optionally its map of accumulated gradients."""
     torch = _torch()
     if out is None:
         out = {k: torch.empty_like(v) for k, v in grads.items()}
-    n, ids, bufs = _param_entries(grads, out, _op(op))
-    ref = _first_tensor([grads])
-    s = _stream(stream, ref) if ref is not None else (_stream(stream, None) if stream is not None else 0)
-    check(library().rc_rank_all_reduce_params(int(rank), n, ctypes.addressof(ids), ctypes.addressof(bufs),
-                                              ctypes.c_void_p(s)))
+    n, arr = _param_entries(grads, out, _op(op), acc)
+    s = _stream_for(stream, _first_tensor([grads]))
+    check(library().rc_rank_all_reduce_params(int(rank), n, ctypes.addressof(arr), ctypes.c_void_p(s)))
     return out

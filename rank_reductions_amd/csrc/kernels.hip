@@ -142,12 +142,21 @@ __device__ __forceinline__ V fold(const V (&x)[NIN]) {
     return acc;
 }
 
-template <int NIN, int NR, class Op, bool NT, class OutF>
-__device__ __forceinline__ void element(const uint32_t* const (&in)[NIN], int64_t e,
-                                        const OutF& out, uint32_t mask, bool mean) {
+// With ACC, operand k is acc[k] + in[k] (an accumulator plus the last
+// gradient, one add per element with the reduction's Sum), added before the fold.
+template <int NIN, int NR, class Op, bool NT, bool ACC, class OutF>
+__device__ __forceinline__ void element(const uint32_t* const (&in)[NIN], const uint32_t* const (&ac)[NIN],
+                                        int64_t e, const OutF& out, uint32_t mask, bool mean) {
     uint32_t x[NIN];
 #pragma unroll
     for (int k = 0; k < NIN; ++k) x[k] = ld1<NT>(in[k] + e);
+    if constexpr (ACC) {
+        uint32_t y[NIN];
+#pragma unroll
+        for (int k = 0; k < NIN; ++k) y[k] = ld1<NT>(ac[k] + e);
+#pragma unroll
+        for (int k = 0; k < NIN; ++k) x[k] = op2<Op>(y[k], x[k]);
+    }
     uint32_t acc = fold<NIN, Op>(x);
     if constexpr (Op::kCanMean) {
         if (mean) acc = mean1<NIN>(acc);
@@ -160,11 +169,14 @@ __device__ __forceinline__ void element(const uint32_t* const (&in)[NIN], int64_
 // One round: U vectors per lane.  in[k] + off and out(o) + off are uniform
 // (the round's first element); lane vectors sit at 32-bit offsets from there.
 // Unless FULL, only the first `nv` vectors of the round exist.
-template <int NIN, int NR, class Op, int U, bool NT, bool FULL, class OutF>
-__device__ __forceinline__ void vec_round(const uint32_t* const (&in)[NIN], int64_t off,
-                                          uint32_t nv, const OutF& out, uint32_t mask, bool mean) {
+template <int NIN, int NR, class Op, int U, bool NT, bool ACC, bool FULL, class OutF>
+__device__ __forceinline__ void vec_round(const uint32_t* const (&in)[NIN], const uint32_t* const (&ac)[NIN],
+                                          int64_t off, uint32_t nv, const OutF& out, uint32_t mask,
+                                          bool mean) {
     const uint32_t tid = threadIdx.x;
+    constexpr int NA = ACC ? NIN : 1;
     u32x4 x[U][NIN];
+    u32x4 y[U][NA];
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -173,11 +185,19 @@ __device__ __forceinline__ void vec_round(const uint32_t* const (&in)[NIN], int6
         if (ok[u]) {
 #pragma unroll
             for (int k = 0; k < NIN; ++k) x[u][k] = ld4<NT>((in[k] + off) + (size_t)(v * kVec));
+            if constexpr (ACC) {
+#pragma unroll
+                for (int k = 0; k < NIN; ++k) y[u][k] = ld4<NT>((ac[k] + off) + (size_t)(v * kVec));
+            }
         }
     }
     u32x4 acc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+        if constexpr (ACC) {
+#pragma unroll
+            for (int k = 0; k < NIN; ++k) x[u][k] = op2<Op>(y[u][k], x[u][k]);
+        }
         acc[u] = fold<NIN, Op>(x[u]);
         if constexpr (Op::kCanMean) {
             if (mean) acc[u] = mean4<NIN>(acc[u]);
@@ -196,16 +216,16 @@ __device__ __forceinline__ void vec_round(const uint32_t* const (&in)[NIN], int6
 }
 
 // Tile lt of a job of `len` elements.
-template <int NIN, int NR, class Op, int U, bool NT, class OutF>
-__device__ __forceinline__ void job_tile(const uint32_t* const (&in)[NIN], const OutF& out,
-                                         uint32_t mask, int64_t len, int phase, int64_t lt,
+template <int NIN, int NR, class Op, int U, bool NT, bool ACC, class OutF>
+__device__ __forceinline__ void job_tile(const uint32_t* const (&in)[NIN], const uint32_t* const (&ac)[NIN],
+                                         const OutF& out, uint32_t mask, int64_t len, int phase, int64_t lt,
                                          int64_t te, bool mean) {
     const int tid = threadIdx.x;
     if (phase == kScalarOnly) {
         const int64_t e0 = lt * te;
         const int64_t e1 = e0 + te < len ? e0 + te : len;
         for (int64_t e = e0 + tid; e < e1; e += kBlock)
-            element<NIN, NR, Op, NT>(in, e, out, mask, mean);
+            element<NIN, NR, Op, NT, ACC>(in, ac, e, out, mask, mean);
         return;
     }
     const int64_t head = phase < len ? phase : len;
@@ -217,14 +237,14 @@ __device__ __forceinline__ void job_tile(const uint32_t* const (&in)[NIN], const
     constexpr int64_t kStep = (int64_t)kBlock * U;
     for (int64_t vb = v0; vb < v1; vb += kStep) {
         const int64_t off = head + vb * kVec;
-        if (v1 - vb >= kStep) vec_round<NIN, NR, Op, U, NT, true>(in, off, 0, out, mask, mean);
-        else vec_round<NIN, NR, Op, U, NT, false>(in, off, (uint32_t)(v1 - vb), out, mask, mean);
+        if (v1 - vb >= kStep) vec_round<NIN, NR, Op, U, NT, ACC, true>(in, ac, off, 0, out, mask, mean);
+        else vec_round<NIN, NR, Op, U, NT, ACC, false>(in, ac, off, (uint32_t)(v1 - vb), out, mask, mean);
     }
     if (lt == 0 && (head > 0 || tail0 < len)) {
         const int64_t nscal = head + (len - tail0);  // at most 3 + 3
         if (tid < nscal) {
             const int64_t e = tid < head ? tid : tail0 + (tid - head);
-            element<NIN, NR, Op, NT>(in, e, out, mask, mean);
+            element<NIN, NR, Op, NT, ACC>(in, ac, e, out, mask, mean);
         }
     }
 }
@@ -247,23 +267,26 @@ __device__ __forceinline__ uint32_t out_mask_of(const JobArgs& a, int c) {
     return mask;
 }
 
-// Tile lt of fold job c: input k is rank (c+1+k) mod R at element c*in_stride.
-template <int NIN, class Op, int U, bool NT>
+// Tile lt of fold job c: input k is rank (c+1+k) mod R at element c*in_stride
+// (with ACC, plus that rank's accumulator at the same element).
+template <int NIN, class Op, int U, bool NT, bool ACC>
 __device__ __forceinline__ void fold_tile(const JobArgs& a, int c, int lt) {
     const int64_t start = (int64_t)c * a.seg;
     const int64_t len = a.n - start < a.seg ? a.n - start : a.seg;
     const int64_t ioff = (int64_t)c * a.in_stride;
     const uint32_t* in[NIN];
+    const uint32_t* ac[NIN];
 #pragma unroll
     for (int k = 0; k < NIN; ++k) {
         int r = c + 1 + k;  // c < NIN, so r < 2 * NIN
         r = r >= NIN ? r - NIN : r;
         in[k] = static_cast<const uint32_t*>(a.in[r]) + ioff;
+        ac[k] = ACC ? static_cast<const uint32_t*>(a.acc[r]) + ioff : nullptr;
     }
     const int64_t ooff = (int64_t)c * a.out_stride;
     auto out = [&](int o) { return static_cast<uint32_t*>(a.out[o]) + ooff; };
-    job_tile<NIN, NIN, Op, U, NT>(in, out, out_mask_of(a, c), len, a.phase[c], lt, a.tile_elems,
-                                  a.mean != 0);
+    job_tile<NIN, NIN, Op, U, NT, ACC>(in, ac, out, out_mask_of(a, c), len, a.phase[c], lt, a.tile_elems,
+                                       a.mean != 0);
 }
 
 // Tile lt of copy job c: in[c] at element c*in_stride, copied bit for bit to
@@ -273,25 +296,27 @@ __device__ __forceinline__ void copy_tile(const JobArgs& a, int c, int lt) {
     const int64_t start = (int64_t)c * a.seg;
     const int64_t len = a.n - start < a.seg ? a.n - start : a.seg;
     const uint32_t* in[1] = {static_cast<const uint32_t*>(a.in[c]) + (int64_t)c * a.in_stride};
+    const uint32_t* none[1] = {nullptr};
     const int64_t ooff = (int64_t)c * a.out_stride;
     auto out = [&](int o) { return static_cast<uint32_t*>(a.out[o]) + ooff; };
-    job_tile<1, NR, OpSumI32, U, NT>(in, out, out_mask_of(a, c), len, a.phase[c], lt, a.tile_elems, false);
+    job_tile<1, NR, OpSumI32, U, NT, false>(in, none, out, out_mask_of(a, c), len, a.phase[c], lt,
+                                            a.tile_elems, false);
 }
 
 // Launch shapes: one-shot launches use a 2-D grid, blockIdx.y = job and
 // blockIdx.x = tile of the job (workgroups past a short job's last tile exit);
 // persistent launches use a 1-D grid that strides over all tiles.
-template <int NIN, class Op, int U, bool NT>
+template <int NIN, class Op, int U, bool NT, bool ACC>
 __global__ __launch_bounds__(kBlock) void fold_kernel(JobArgs a) {
     if (a.grid_2d) {
         const int c = blockIdx.y;
         const int lt = blockIdx.x;
-        if (lt < a.tile_prefix[c + 1] - a.tile_prefix[c]) fold_tile<NIN, Op, U, NT>(a, c, lt);
+        if (lt < a.tile_prefix[c + 1] - a.tile_prefix[c]) fold_tile<NIN, Op, U, NT, ACC>(a, c, lt);
         return;
     }
     for (int t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
         const int c = job_of(a, t);
-        fold_tile<NIN, Op, U, NT>(a, c, t - a.tile_prefix[c]);
+        fold_tile<NIN, Op, U, NT, ACC>(a, c, t - a.tile_prefix[c]);
     }
 }
 
@@ -315,7 +340,7 @@ __global__ __launch_bounds__(kBlock) void copy_kernel(JobArgs a) {
 struct BatchArgs {
     const BatchJob* jobs;
     const int32_t* group_job;
-    const void* const* ptrs;  // [job][2R]: fold operands in order, then outputs
+    const void* const* ptrs;  // [job][2R], or [job][3R] with ACC: operands, accumulators, outputs
     int64_t total_tiles;
     int64_t ngroups;
     int32_t njobs;
@@ -335,33 +360,41 @@ __device__ __forceinline__ int find_job(const BatchArgs& a, int64_t t) {
     return lo;
 }
 
-template <int NIN, class Op, int U, bool NT>
+template <int NIN, class Op, int U, bool NT, bool ACC>
 __global__ __launch_bounds__(kBlock) void batch_kernel(BatchArgs a) {
+    constexpr int kPtrs = (ACC ? 3 : 2) * NIN;
+    constexpr int kOut = (ACC ? 2 : 1) * NIN;
     for (int64_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
         const int j = find_job(a, t);
         const BatchJob jb = a.jobs[j];
-        const void* const* tp = a.ptrs + (int64_t)j * 2 * NIN;
+        const void* const* tp = a.ptrs + (int64_t)j * kPtrs;
         const uint32_t* in[NIN];
+        const uint32_t* ac[NIN];
 #pragma unroll
-        for (int k = 0; k < NIN; ++k) in[k] = static_cast<const uint32_t*>(tp[k]);
-        auto out = [&](int o) { return static_cast<uint32_t*>(const_cast<void*>(tp[NIN + o])); };
-        job_tile<NIN, NIN, Op, U, NT>(in, out, (1u << NIN) - 1u, jb.len, jb.phase, t - jb.tile_begin,
-                                      a.tile_elems, a.mean != 0);
+        for (int k = 0; k < NIN; ++k) {
+            in[k] = static_cast<const uint32_t*>(tp[k]);
+            ac[k] = ACC ? static_cast<const uint32_t*>(tp[NIN + k]) : nullptr;
+        }
+        auto out = [&](int o) { return static_cast<uint32_t*>(const_cast<void*>(tp[kOut + o])); };
+        job_tile<NIN, NIN, Op, U, NT, ACC>(in, ac, out, (1u << NIN) - 1u, jb.len, jb.phase, t - jb.tile_begin,
+                                           a.tile_elems, a.mean != 0);
     }
 }
 
 // ---------------------------------------------------------------- dispatch
 
-template <int NIN>
-constexpr int kUnroll = unroll_for(NIN);
+// Vectors per lane per round: about eight 16-byte loads in flight per lane,
+// counting an accumulator's loads with the operands'.
+template <int NIN, bool ACC>
+constexpr int kUnroll = unroll_for(ACC ? 2 * NIN : NIN);
 
 using FoldFn = void (*)(JobArgs);
 using BatchFn = void (*)(BatchArgs);
 
-template <int NIN, class Op, bool NT>
-FoldFn fold_ptr() { return fold_kernel<NIN, Op, kUnroll<NIN>, NT>; }
-template <int NIN, class Op, bool NT>
-BatchFn batch_ptr() { return batch_kernel<NIN, Op, kUnroll<NIN>, NT>; }
+template <int NIN, class Op, bool NT, bool ACC>
+FoldFn fold_ptr() { return fold_kernel<NIN, Op, kUnroll<NIN, ACC>, NT, ACC>; }
+template <int NIN, class Op, bool NT, bool ACC>
+BatchFn batch_ptr() { return batch_kernel<NIN, Op, kUnroll<NIN, ACC>, NT, ACC>; }
 
 template <int NR, bool NT>
 FoldFn copy_ptr() { return copy_kernel<NR, kCopyUnroll, NT>; }
@@ -389,70 +422,85 @@ FoldFn pick_copy(int nranks) {
     }
 }
 
-template <class Op, bool NT>
-FoldFn pick_fold(int nin) {
+// Kernel for nin = 1..16 ranks; Make<NIN>::get() names the instantiation.
+template <template <int> class Make, class Fn>
+Fn pick_nin(int nin) {
     switch (nin) {
-        case 1: return fold_ptr<1, Op, NT>();
-        case 2: return fold_ptr<2, Op, NT>();
-        case 3: return fold_ptr<3, Op, NT>();
-        case 4: return fold_ptr<4, Op, NT>();
-        case 5: return fold_ptr<5, Op, NT>();
-        case 6: return fold_ptr<6, Op, NT>();
-        case 7: return fold_ptr<7, Op, NT>();
-        case 8: return fold_ptr<8, Op, NT>();
-        case 9: return fold_ptr<9, Op, NT>();
-        case 10: return fold_ptr<10, Op, NT>();
-        case 11: return fold_ptr<11, Op, NT>();
-        case 12: return fold_ptr<12, Op, NT>();
-        case 13: return fold_ptr<13, Op, NT>();
-        case 14: return fold_ptr<14, Op, NT>();
-        case 15: return fold_ptr<15, Op, NT>();
-        case 16: return fold_ptr<16, Op, NT>();
+        case 1: return Make<1>::get();
+        case 2: return Make<2>::get();
+        case 3: return Make<3>::get();
+        case 4: return Make<4>::get();
+        case 5: return Make<5>::get();
+        case 6: return Make<6>::get();
+        case 7: return Make<7>::get();
+        case 8: return Make<8>::get();
+        case 9: return Make<9>::get();
+        case 10: return Make<10>::get();
+        case 11: return Make<11>::get();
+        case 12: return Make<12>::get();
+        case 13: return Make<13>::get();
+        case 14: return Make<14>::get();
+        case 15: return Make<15>::get();
+        case 16: return Make<16>::get();
         default: return nullptr;
     }
 }
 
-template <class Op, bool NT>
-BatchFn pick_batch(int nin) {
-    switch (nin) {
-        case 1: return batch_ptr<1, Op, NT>();
-        case 2: return batch_ptr<2, Op, NT>();
-        case 3: return batch_ptr<3, Op, NT>();
-        case 4: return batch_ptr<4, Op, NT>();
-        case 5: return batch_ptr<5, Op, NT>();
-        case 6: return batch_ptr<6, Op, NT>();
-        case 7: return batch_ptr<7, Op, NT>();
-        case 8: return batch_ptr<8, Op, NT>();
-        case 9: return batch_ptr<9, Op, NT>();
-        case 10: return batch_ptr<10, Op, NT>();
-        case 11: return batch_ptr<11, Op, NT>();
-        case 12: return batch_ptr<12, Op, NT>();
-        case 13: return batch_ptr<13, Op, NT>();
-        case 14: return batch_ptr<14, Op, NT>();
-        case 15: return batch_ptr<15, Op, NT>();
-        case 16: return batch_ptr<16, Op, NT>();
-        default: return nullptr;
-    }
-}
+template <class Op, bool NT, bool ACC>
+struct FoldOf {
+    template <int NIN>
+    struct At {
+        static FoldFn get() { return fold_ptr<NIN, Op, NT, ACC>(); }
+    };
+};
+template <class Op, bool NT, bool ACC>
+struct BatchOf {
+    template <int NIN>
+    struct At {
+        static BatchFn get() { return batch_ptr<NIN, Op, NT, ACC>(); }
+    };
+};
 
-template <bool NT>
+// Accumulators exist for Sum and Mean only (validation refuses Max).
+template <bool NT, bool ACC>
 FoldFn pick_fold_op(int dtype, int op, int nin) {
     if (dtype == RC_F32) {
-        if (op == RC_MAX) return pick_fold<OpMaxF32, NT>(nin);
-        return pick_fold<OpSumF32, NT>(nin);
+        if (op == RC_MAX) {
+            if constexpr (ACC) return nullptr;
+            else return pick_nin<FoldOf<OpMaxF32, NT, false>::template At, FoldFn>(nin);
+        }
+        return pick_nin<FoldOf<OpSumF32, NT, ACC>::template At, FoldFn>(nin);
     }
-    if (op == RC_MAX) return pick_fold<OpMaxI32, NT>(nin);
-    return pick_fold<OpSumI32, NT>(nin);
+    if (op == RC_MAX) {
+        if constexpr (ACC) return nullptr;
+        else return pick_nin<FoldOf<OpMaxI32, NT, false>::template At, FoldFn>(nin);
+    }
+    return pick_nin<FoldOf<OpSumI32, NT, ACC>::template At, FoldFn>(nin);
+}
+
+template <bool NT, bool ACC>
+BatchFn pick_batch_op(int dtype, int op, int nin) {
+    if (dtype == RC_F32) {
+        if (op == RC_MAX) {
+            if constexpr (ACC) return nullptr;
+            else return pick_nin<BatchOf<OpMaxF32, NT, false>::template At, BatchFn>(nin);
+        }
+        return pick_nin<BatchOf<OpSumF32, NT, ACC>::template At, BatchFn>(nin);
+    }
+    if (op == RC_MAX) {
+        if constexpr (ACC) return nullptr;
+        else return pick_nin<BatchOf<OpMaxI32, NT, false>::template At, BatchFn>(nin);
+    }
+    return pick_nin<BatchOf<OpSumI32, NT, ACC>::template At, BatchFn>(nin);
 }
 
 template <bool NT>
-BatchFn pick_batch_op(int dtype, int op, int nin) {
-    if (dtype == RC_F32) {
-        if (op == RC_MAX) return pick_batch<OpMaxF32, NT>(nin);
-        return pick_batch<OpSumF32, NT>(nin);
-    }
-    if (op == RC_MAX) return pick_batch<OpMaxI32, NT>(nin);
-    return pick_batch<OpSumI32, NT>(nin);
+FoldFn pick_fold_any(int dtype, int op, int nin, bool acc) {
+    return acc ? pick_fold_op<NT, true>(dtype, op, nin) : pick_fold_op<NT, false>(dtype, op, nin);
+}
+template <bool NT>
+BatchFn pick_batch_any(int dtype, int op, int nin, bool acc) {
+    return acc ? pick_batch_op<NT, true>(dtype, op, nin) : pick_batch_op<NT, false>(dtype, op, nin);
 }
 
 }  // namespace
@@ -461,7 +509,8 @@ hipError_t launch_jobs(const LaunchPlan& p, hipStream_t stream) {
     const bool nt = p.args.nontemporal != 0;
     FoldFn fn;
     if (p.args.in_mode == kInCopy) fn = nt ? pick_copy<true>(p.args.nranks) : pick_copy<false>(p.args.nranks);
-    else fn = nt ? pick_fold_op<true>(p.dtype, p.op, p.nin) : pick_fold_op<false>(p.dtype, p.op, p.nin);
+    else fn = nt ? pick_fold_any<true>(p.dtype, p.op, p.nin, p.acc)
+                 : pick_fold_any<false>(p.dtype, p.op, p.nin, p.acc);
     if (!fn) return hipErrorInvalidValue;
     hipLaunchKernelGGL(fn, dim3(p.grid, p.grid_y), dim3(kBlock), p.lds_bytes, stream, p.args);
     return hipGetLastError();
@@ -470,8 +519,8 @@ hipError_t launch_jobs(const LaunchPlan& p, hipStream_t stream) {
 hipError_t launch_batch(const BatchJob* jobs, const int32_t* group_job, const void* const* ptrs,
                         const BatchPlan& p, hipStream_t stream) {
     const bool nt = p.nontemporal != 0;
-    BatchFn fn = nt ? pick_batch_op<true>(p.dtype, p.op, p.nranks)
-                    : pick_batch_op<false>(p.dtype, p.op, p.nranks);
+    BatchFn fn = nt ? pick_batch_any<true>(p.dtype, p.op, p.nranks, p.acc)
+                    : pick_batch_any<false>(p.dtype, p.op, p.nranks, p.acc);
     if (!fn) return hipErrorInvalidValue;
     BatchArgs a;
     a.jobs = jobs;

@@ -133,7 +133,8 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceI
     std::vector<std::vector<uintptr_t>> ad;
     auto fold_setup = [&](int64_t n, int64_t seg, int64_t in_stride, int64_t out_stride) {
         p.nin = R;
-        p.unroll = unroll_for(R);
+        p.acc = ck.has_acc;
+        p.unroll = unroll_for(ck.has_acc ? 2 * R : R);
         a.in_mode = kInFold;
         a.n = n;
         a.seg = seg;
@@ -145,6 +146,7 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceI
         for (int r = 0; r < R; ++r) {
             a.in[r] = ck.send[r];
             a.out[r] = ck.recv[r];
+            a.acc[r] = ck.has_acc ? ck.acc[r] : nullptr;
         }
     };
     auto copy_setup = [&](LaunchPlan& q) {
@@ -157,6 +159,8 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceI
         ad.assign(R, {});
         for (int c = 0; c < R; ++c) {
             for (int r = 0; r < R; ++r) ad[c].push_back(addr(a.in[r], (int64_t)c * a.in_stride, es));
+            if (p.acc)
+                for (int r = 0; r < R; ++r) ad[c].push_back(addr(a.acc[r], (int64_t)c * a.in_stride, es));
             for (int r = 0; r < R; ++r) {
                 const bool writes = owner_only ? (r == c) : ((mask_for_owner_only >> r) & 1u);
                 if (writes) ad[c].push_back(addr(a.out[r], (int64_t)c * a.out_stride, es));
@@ -276,7 +280,8 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceI
         const JobArgs& ja = lp.args;
         const int in_mask = __builtin_popcount(ja.out_mask);
         lp.nout = ja.out_mode == kOutOwner ? 1 : in_mask - (ja.out_mode == kOutMaskButOwner ? 1 : 0);
-        shape_launch(lp.total_tiles, lp.nin, lp.nout, lp.unroll, cfg, dev, &lp.grid, &lp.lds_bytes);
+        const int loads = lp.acc ? 2 * lp.nin : lp.nin;
+        shape_launch(lp.total_tiles, loads, lp.nout, lp.unroll, cfg, dev, &lp.grid, &lp.lds_bytes);
         if (cfg.max_workgroups <= 0) {
             // one-shot: x = tiles of the longest job, y = jobs
             int64_t widest = 0;
@@ -296,7 +301,7 @@ void split_batch(const std::vector<Checked>& tensors, std::vector<Checked>* own,
     batched->clear();
     for (const Checked& ck : tensors) {
         if (ck.count == 0) continue;
-        const int64_t moved = 2 * (int64_t)ck.nranks * ck.count * element_size(ck.dtype);
+        const int64_t moved = (ck.has_acc ? 3 : 2) * (int64_t)ck.nranks * ck.count * element_size(ck.dtype);
         (moved >= kOwnLaunchBytes ? own : batched)->push_back(ck);
     }
 }
@@ -305,7 +310,9 @@ BatchPlan plan_batch(const std::vector<Checked>& tensors, const Config& cfg, con
     BatchPlan bp;
     if (tensors.empty()) return bp;
     const int R = tensors[0].nranks;
-    const int unroll = unroll_for(R);
+    bp.acc = tensors[0].has_acc;  // the caller batches tensors with and without accumulators apart
+    const int loads = bp.acc ? 2 * R : R;
+    const int unroll = unroll_for(loads);
     bp.nranks = R;
     bp.dtype = tensors[0].dtype;
     bp.op = tensors[0].op;
@@ -314,7 +321,7 @@ BatchPlan plan_batch(const std::vector<Checked>& tensors, const Config& cfg, con
     const int64_t es = element_size(bp.dtype);
     int64_t tiles = 0;
     std::vector<uintptr_t> ad;
-    ad.reserve(2 * R);
+    ad.reserve(3 * R);
     for (const Checked& ck : tensors) {
         if (ck.count == 0) continue;
         const int64_t S = (ck.count + R - 1) / R;
@@ -324,6 +331,8 @@ BatchPlan plan_batch(const std::vector<Checked>& tensors, const Config& cfg, con
             if (len <= 0) continue;
             ad.clear();
             for (int k = 0; k < R; ++k) ad.push_back(addr(ck.send[(c + 1 + k) % R], start, es));
+            if (bp.acc)
+                for (int k = 0; k < R; ++k) ad.push_back(addr(ck.acc[(c + 1 + k) % R], start, es));
             for (int r = 0; r < R; ++r) ad.push_back(addr(ck.recv[r], start, es));
             BatchJob j{};
             j.tile_begin = tiles;
@@ -344,7 +353,7 @@ BatchPlan plan_batch(const std::vector<Checked>& tensors, const Config& cfg, con
         while (j + 1 < bp.jobs.size() && bp.jobs[j + 1].tile_begin <= t) ++j;
         bp.group_job[g] = (int32_t)j;
     }
-    shape_launch(tiles, R, R, unroll, cfg, dev, &bp.grid, &bp.lds_bytes);
+    shape_launch(tiles, loads, R, unroll, cfg, dev, &bp.grid, &bp.lds_bytes);
     return bp;
 }
 

@@ -54,6 +54,9 @@ struct JobArgs {
     int32_t total_tiles;                 // tile_prefix[jobs], below 2^31
     int32_t tile_prefix[kMaxRanks + 1];  // tiles before job j; past the last job: total_tiles
     uint8_t phase[kMaxRanks];            // leading scalar elements, or kScalarOnly
+    // fold jobs with accumulators: operand k of a job is acc[r] + in[r] for
+    // its rank r, added before the fold (kernels instantiated for it only)
+    const void* acc[kMaxRanks];
 };
 
 // One segment of one tensor in a batched all-reduce (device descriptor).  Its
@@ -95,6 +98,9 @@ struct Checked {
     int64_t count = 0;        // element count described by dims
     const void* send[kMaxRanks] = {};
     void* recv[kMaxRanks] = {};
+    // all_reduce over acc[r] + send[r] (a gradient sync's accumulators)
+    bool has_acc = false;
+    const void* acc[kMaxRanks] = {};
 };
 
 struct Error {
@@ -105,14 +111,16 @@ struct Error {
 // ---------------------------------------------------------------- validate.cpp
 Error validate(Coll coll, int nranks, const rc_buf* bufs, Checked* out);
 // Tensor t of a batched all-reduce; messages name the tensor index, or
-// ids[t] when ids is given (a gradient sync's parameter IDs).
+// ids[t] when ids is given (a gradient sync's parameter IDs).  accs, when
+// given, holds tensor t's accumulators at [t*R + r] (NULL: none).
 Error validate_batch(int nranks, int num_tensors, const rc_buf* bufs,
-                     std::vector<Checked>* out, const uint64_t* ids = nullptr);
+                     std::vector<Checked>* out, const uint64_t* ids = nullptr,
+                     const void* const* accs = nullptr);
 // Pairs the ranks' gradient entries by parameter ID: rank r has counts[r]
-// entries (ids[r][i], bufs[r][i]).  On success tensor_major[t*R + r] is rank
-// r's buffer of the t-th smallest ID, order[t].
-Error match_params(int nranks, const int* counts, const uint64_t* const* ids, const rc_buf* const* bufs,
-                   std::vector<rc_buf>* tensor_major, std::vector<uint64_t>* order);
+// entries params[r][i].  On success bufs[t*R + r] and accs[t*R + r] are rank
+// r's buffer and accumulator of the t-th smallest ID, order[t].
+Error match_params(int nranks, const int* counts, const rc_param* const* params,
+                   std::vector<rc_buf>* bufs, std::vector<const void*>* accs, std::vector<uint64_t>* order);
 int64_t element_size(int dtype);
 
 // ---------------------------------------------------------------- plan.cpp
@@ -135,6 +143,7 @@ int64_t job_tiles(int64_t len, uint8_t phase, int64_t tile_elems);
 struct LaunchPlan {
     JobArgs args;
     int nin = 1;             // inputs folded per element (1 = copy)
+    bool acc = false;        // each folded input is an accumulator plus a send
     int nout = 1;            // outputs written per element
     int unroll = 1;          // vectors per lane per round of the kernel
     int dtype = RC_F32;
@@ -152,7 +161,10 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceI
 // Batched all-reduce: job and pointer tables for tensors [t0, t1).
 struct BatchPlan {
     std::vector<BatchJob> jobs;
-    std::vector<const void*> ptrs;  // [job][2R]: fold operands in order, then outputs
+    // [job][2R] or, with accumulators, [job][3R]: fold operands in order,
+    // their accumulators in the same order, then the outputs
+    std::vector<const void*> ptrs;
+    bool acc = false;
     std::vector<int32_t> group_job;  // job holding tile g << kGroupShift, per group g
     int64_t total_tiles = 0;
     int tile_elems = 0;

@@ -38,8 +38,7 @@ struct Slot {
     // gradient sync (all_reduce_params): each rank's entries
     std::vector<uint8_t> is_params;
     std::vector<int> pcount;
-    std::vector<std::vector<uint64_t>> pids;
-    std::vector<std::vector<rc_buf>> pbufs;
+    std::vector<std::vector<rc_param>> params;
     uint32_t arrived = 0;
     int left = 0;
     bool done = false;
@@ -189,7 +188,8 @@ const char* coll_name(Coll c) {
 }
 
 // A validated batch of all-reduces: tensors large enough get launches of
-// their own, the rest share one batched launch.
+// their own, the rest share one batched launch (one for tensors with
+// accumulators and one for tensors without, when both occur).
 Error launch_batch(const std::vector<Checked>& cks, void* stream) {
     std::vector<Checked> own, batched;
     split_batch(cks, &own, &batched);
@@ -197,9 +197,16 @@ Error launch_batch(const std::vector<Checked>& cks, void* stream) {
         Error e = launch(ck, stream);
         if (e.code) return e;
     }
-    const BatchPlan bp = plan_batch(batched, g_s.cfg, g_s.dev);
-    if (bp.total_tiles == 0) return {};
-    return device_launch_batch(bp, stream);
+    for (const bool acc : {false, true}) {
+        std::vector<Checked> part;
+        for (const Checked& ck : batched)
+            if (ck.has_acc == acc) part.push_back(ck);
+        const BatchPlan bp = plan_batch(part, g_s.cfg, g_s.dev);
+        if (bp.total_tiles == 0) continue;
+        Error e = device_launch_batch(bp, stream);
+        if (e.code) return e;
+    }
+    return {};
 }
 
 // Runs `enqueue` (the kernels of one matched collective) on `stream`, the
@@ -231,13 +238,14 @@ const char* kind_name(const Slot& s, int r) {
 }
 
 // Pairs a gradient sync's entries by parameter ID and validates the batch.
-Error check_params(int R, const std::vector<int>& counts, const std::vector<const uint64_t*>& ids,
-                   const std::vector<const rc_buf*>& bufs, std::vector<Checked>* cks) {
-    std::vector<rc_buf> tensor_major;
+Error check_params(int R, const std::vector<int>& counts, const std::vector<const rc_param*>& params,
+                   std::vector<Checked>* cks) {
+    std::vector<rc_buf> bufs;
+    std::vector<const void*> accs;
     std::vector<uint64_t> order;
-    Error e = match_params(R, counts.data(), ids.data(), bufs.data(), &tensor_major, &order);
+    Error e = match_params(R, counts.data(), params.data(), &bufs, &accs, &order);
     if (e.code) return e;
-    return validate_batch(R, (int)order.size(), tensor_major.data(), cks, order.data());
+    return validate_batch(R, (int)order.size(), bufs.data(), cks, order.data(), accs.data());
 }
 
 // The last rank of a slot: check the R sides against each other and launch.
@@ -254,14 +262,10 @@ void complete_slot(Slot& s, void* stream) {
     }
     Error e;
     if (s.is_params[0]) {
-        std::vector<const uint64_t*> ids(R);
-        std::vector<const rc_buf*> bufs(R);
-        for (int r = 0; r < R; ++r) {
-            ids[r] = s.pids[r].data();
-            bufs[r] = s.pbufs[r].data();
-        }
+        std::vector<const rc_param*> params(R);
+        for (int r = 0; r < R; ++r) params[r] = s.params[r].data();
         std::vector<Checked> cks;
-        e = check_params(R, s.pcount, ids, bufs, &cks);
+        e = check_params(R, s.pcount, params, &cks);
         if (!e.code && !g_s.cfg.validate_only)
             e = launch_joined(s.streams, stream, [&] { return launch_batch(cks, stream); });
     } else {
@@ -287,8 +291,7 @@ struct RankArgs {
     const rc_buf* buf = nullptr;
     bool params = false;
     int count = 0;
-    const uint64_t* ids = nullptr;
-    const rc_buf* bufs = nullptr;
+    const rc_param* entries = nullptr;
 };
 
 int rank_collective(const RankArgs& a, int rank, void* stream) {
@@ -316,24 +319,22 @@ int rank_collective(const RankArgs& a, int rank, void* stream) {
         sp->streams.assign(R, nullptr);
         sp->is_params.assign(R, 0);
         sp->pcount.assign(R, 0);
-        sp->pids.assign(R, {});
-        sp->pbufs.assign(R, {});
+        sp->params.assign(R, {});
     }
     std::shared_ptr<Slot> s = sp;
     s->kinds[rank] = a.coll;
     s->is_params[rank] = a.params;
     if (a.params) {
         // copied now: the caller's arrays need only live through the call
-        if (a.count < 0 || (a.count > 0 && (!a.ids || !a.bufs))) {
+        if (a.count < 0 || (a.count > 0 && !a.entries)) {
             if (s->status == RC_OK) {
                 s->status = RC_ERR_INVALID_ARGUMENT;
                 s->msg = "rank " + std::to_string(rank) +
-                         ": all_reduce_params needs num_params >= 0 and non-NULL ids and bufs";
+                         ": all_reduce_params needs num_params >= 0 and a non-NULL params array";
             }
         } else {
             s->pcount[rank] = a.count;
-            s->pids[rank].assign(a.ids, a.ids + a.count);
-            s->pbufs[rank].assign(a.bufs, a.bufs + a.count);
+            s->params[rank].assign(a.entries, a.entries + a.count);
         }
     } else if (a.buf) {
         s->bufs[rank] = *a.buf;
@@ -392,20 +393,18 @@ int rc_all_reduce_many(int num_tensors, const rc_buf* bufs, void* stream) {
     return report(launch_batch(cks, stream));
 }
 
-int rc_all_reduce_params(const int* num_params, const uint64_t* const* ids, const rc_buf* const* bufs,
-                         void* stream) {
+int rc_all_reduce_params(const int* num_params, const rc_param* const* params, void* stream) {
     std::lock_guard<std::mutex> lock(g_mu);
     if (g_s.mode == Mode::None)
         return report(Error{RC_ERR_NOT_REGISTERED, "no session: call rc_register first"});
     if (g_s.mode == Mode::PerRank)
         return report(Error{RC_ERR_INVALID_ARGUMENT, "the session was opened per rank"});
     const int R = g_s.nranks;
-    if (!num_params || !ids || !bufs)
-        return report(Error{RC_ERR_INVALID_ARGUMENT, "all_reduce_params: NULL num_params, ids or bufs"});
+    if (!num_params || !params)
+        return report(Error{RC_ERR_INVALID_ARGUMENT, "all_reduce_params: NULL num_params or params"});
     std::vector<int> counts(num_params, num_params + R);
     std::vector<Checked> cks;
-    Error e = check_params(R, counts, std::vector<const uint64_t*>(ids, ids + R),
-                           std::vector<const rc_buf*>(bufs, bufs + R), &cks);
+    Error e = check_params(R, counts, std::vector<const rc_param*>(params, params + R), &cks);
     if (e.code) return report(e);
     if (g_s.cfg.validate_only) return ok();
     return report(launch_batch(cks, stream));
@@ -472,12 +471,11 @@ int rc_rank_reduce_scatter(int rank, const rc_buf* buf, void* stream) {
 int rc_rank_all_gather(int rank, const rc_buf* buf, void* stream) {
     return rank_call(Coll::AllGather, rank, buf, stream);
 }
-int rc_rank_all_reduce_params(int rank, int num_params, const uint64_t* ids, const rc_buf* bufs, void* stream) {
+int rc_rank_all_reduce_params(int rank, int num_params, const rc_param* params, void* stream) {
     RankArgs a;
     a.params = true;
     a.count = num_params;
-    a.ids = ids;
-    a.bufs = bufs;
+    a.entries = params;
     return rank_collective(a, rank, stream);
 }
 

@@ -111,6 +111,9 @@ void ranges_of(const Checked& ck, int tensor, std::vector<Range>* writes, std::v
             for (int r = 0; r < R; ++r) {
                 writes->push_back({at(ck.recv[r]), at(ck.recv[r]) + n * b, tag0 + r, 0, r, tensor});
                 reads->push_back({at(ck.send[r]), at(ck.send[r]) + n * b, tag0 + r, 0, r, tensor});
+                // an accumulator may be its own rank's output, like send
+                if (ck.has_acc)
+                    reads->push_back({at(ck.acc[r]), at(ck.acc[r]) + n * b, tag0 + r, 0, r, tensor});
             }
             break;
         case Coll::Reduce:
@@ -261,7 +264,7 @@ Error validate(Coll coll, int R, const rc_buf* bufs, Checked* ck) {
 }
 
 Error validate_batch(int R, int num_tensors, const rc_buf* bufs, std::vector<Checked>* out,
-                     const uint64_t* ids) {
+                     const uint64_t* ids, const void* const* accs) {
     const char* who = ids ? "all_reduce_params" : "all_reduce_many";
     auto name = [&](int t) {
         return ids ? "parameter " + std::to_string(ids[t]) : "tensor " + std::to_string(t);
@@ -284,6 +287,28 @@ Error validate_batch(int R, int num_tensors, const rc_buf* bufs, std::vector<Che
         if ((*out)[t].op != (*out)[0].op)
             return fail(RC_ERR_OP_MISMATCH, std::string(who) + ": " + name(t) + " op differs from " + name(0) + "'s");
     }
+    // accumulators (RUDA "Training and state saving": accumulate adds without
+    // averaging), on every rank or on none, for Sum and Mean
+    for (int t = 0; accs && t < num_tensors; ++t) {
+        Checked& ck = (*out)[t];
+        if (ck.count == 0) continue;
+        int given = 0;
+        for (int r = 0; r < R; ++r) given += accs[(int64_t)t * R + r] != nullptr;
+        if (given == 0) continue;
+        if (given != R)
+            return fail(RC_ERR_INVALID_ARGUMENT, std::string(who) + ": " + name(t) +
+                                                     ": acc is given on some ranks only");
+        if (ck.op == RC_MAX)
+            return fail(RC_ERR_INVALID_ARGUMENT, std::string(who) + ": " + name(t) +
+                                                     ": accumulated gradients reduce with Sum or Mean");
+        for (int r = 0; r < R; ++r) {
+            ck.acc[r] = accs[(int64_t)t * R + r];
+            if (misaligned(ck.acc[r], element_size(ck.dtype)))
+                return fail(RC_ERR_INVALID_ARGUMENT, std::string(who) + ": " + name(t) + ": rank " +
+                                                         std::to_string(r) + ": acc is misaligned");
+        }
+        ck.has_acc = true;
+    }
     std::vector<Range> writes, reads;
     for (int t = 0; t < num_tensors; ++t)
         if ((*out)[t].count) ranges_of((*out)[t], t, &writes, &reads);
@@ -297,22 +322,23 @@ Error validate_batch(int R, int num_tensors, const rc_buf* bufs, std::vector<Che
 // are sorted by ID; a repeated ID within a rank is an argument error, and ID
 // lists that differ between ranks are a parameter mismatch named by the first
 // ID that one side lacks.
-Error match_params(int R, const int* counts, const uint64_t* const* ids, const rc_buf* const* bufs,
-                   std::vector<rc_buf>* tensor_major, std::vector<uint64_t>* order) {
+Error match_params(int R, const int* counts, const rc_param* const* params, std::vector<rc_buf>* bufs,
+                   std::vector<const void*>* accs, std::vector<uint64_t>* order) {
     std::vector<std::vector<int>> perm(R);
+    auto id_of = [&](int r, int i) { return params[r][perm[r][i]].id; };
     for (int r = 0; r < R; ++r) {
         if (counts[r] < 0)
             return fail(RC_ERR_INVALID_ARGUMENT, fmt("all_reduce_params: rank %lld: num_params is negative", r));
-        if (counts[r] > 0 && (!ids[r] || !bufs[r]))
-            return fail(RC_ERR_INVALID_ARGUMENT, fmt("all_reduce_params: rank %lld: ids or bufs is NULL", r));
+        if (counts[r] > 0 && !params[r])
+            return fail(RC_ERR_INVALID_ARGUMENT, fmt("all_reduce_params: rank %lld: params is NULL", r));
         perm[r].resize(counts[r]);
         for (int i = 0; i < counts[r]; ++i) perm[r][i] = i;
-        const uint64_t* id = ids[r];
-        std::sort(perm[r].begin(), perm[r].end(), [id](int a, int b) { return id[a] < id[b]; });
+        const rc_param* pr = params[r];
+        std::sort(perm[r].begin(), perm[r].end(), [pr](int a, int b) { return pr[a].id < pr[b].id; });
         for (int i = 1; i < counts[r]; ++i)
-            if (id[perm[r][i]] == id[perm[r][i - 1]])
+            if (id_of(r, i) == id_of(r, i - 1))
                 return fail(RC_ERR_INVALID_ARGUMENT, "all_reduce_params: rank " + std::to_string(r) +
-                                                         " lists parameter " + std::to_string(id[perm[r][i]]) +
+                                                         " lists parameter " + std::to_string(id_of(r, i)) +
                                                          " twice");
     }
     for (int r = 1; r < R; ++r) {
@@ -320,7 +346,7 @@ Error match_params(int R, const int* counts, const uint64_t* const* ids, const r
         int i = 0, j = 0;
         while (i < counts[0] || j < counts[r]) {
             const bool has0 = i < counts[0], hasr = j < counts[r];
-            const uint64_t a = has0 ? ids[0][perm[0][i]] : 0, b = hasr ? ids[r][perm[r][j]] : 0;
+            const uint64_t a = has0 ? id_of(0, i) : 0, b = hasr ? id_of(r, j) : 0;
             if (has0 && hasr && a == b) {
                 ++i, ++j;
                 continue;
@@ -335,10 +361,15 @@ Error match_params(int R, const int* counts, const uint64_t* const* ids, const r
     }
     const int P = R ? counts[0] : 0;
     order->resize(P);
-    tensor_major->assign((size_t)P * R, rc_buf{});
+    bufs->assign((size_t)P * R, rc_buf{});
+    accs->assign((size_t)P * R, nullptr);
     for (int t = 0; t < P; ++t) {
-        (*order)[t] = ids[0][perm[0][t]];
-        for (int r = 0; r < R; ++r) (*tensor_major)[(size_t)t * R + r] = bufs[r][perm[r][t]];
+        (*order)[t] = id_of(0, t);
+        for (int r = 0; r < R; ++r) {
+            const rc_param& e = params[r][perm[r][t]];
+            (*bufs)[(size_t)t * R + r] = e.buf;
+            (*accs)[(size_t)t * R + r] = e.acc;
+        }
     }
     return {};
 }

@@ -122,6 +122,12 @@ void check_plan(const LaunchPlan& p, const std::string& name) {
                     const uintptr_t ad = base + (uintptr_t)(e * 4);
                     if (!inside(ad, bytes)) fail(name + ": input read outside its buffer");
                     if (bytes == 16 && ad % 16) fail(name + ": misaligned vector read");
+                    if (p.acc) {
+                        const uintptr_t aa = (uintptr_t)a.acc[(c + 1 + k) % p.nin] +
+                                             (uintptr_t)(c * a.in_stride * 4) + (uintptr_t)(e * 4);
+                        if (!inside(aa, bytes)) fail(name + ": accumulator read outside its buffer");
+                        if (bytes == 16 && aa % 16) fail(name + ": misaligned accumulator read");
+                    }
                 }
             } else {
                 const uintptr_t ad = (uintptr_t)a.in[c] + (uintptr_t)(c * a.in_stride * 4) + (uintptr_t)(e * 4);
@@ -217,9 +223,13 @@ int main(int argc, char** argv) {
             fail("validation rejected a valid call: " + e.msg);
             continue;
         }
+        if (kind == Coll::AllReduce && rng() % 2) {  // a gradient sync's accumulators
+            ck.has_acc = true;
+            for (int r = 0; r < R; ++r) ck.acc[r] = (const void*)alloc(std::max<int64_t>(n, 1) * 4, mis(r + 2));
+        }
         for (const LaunchPlan& p : plan(ck, cfg, dev)) {
             check_plan(p, "coll " + std::to_string(coll) + " R=" + std::to_string(R) + " n=" + std::to_string(n) +
-                              " mis=" + std::to_string(mis_mode));
+                              " mis=" + std::to_string(mis_mode) + (ck.has_acc ? " acc" : ""));
             ++plans;
         }
     }
@@ -229,7 +239,9 @@ int main(int argc, char** argv) {
         g_bufs.clear();
         const int R = 1 + (int)(rng() % 8);
         const int T = 1 + (int)(rng() % 40);
+        const bool with_acc = rng() % 2;  // every tensor with accumulators, or none
         std::vector<rc_buf> rows;
+        std::vector<const void*> accs;
         for (int t = 0; t < T; ++t) {
             int64_t n = (int64_t)(rng() % 4) == 0 ? (int64_t)(rng() % 300000) : (int64_t)(rng() % 700);
             const int mis_mode = (int)(rng() % 3);
@@ -238,18 +250,26 @@ int main(int argc, char** argv) {
                 void* s = (void*)alloc(std::max<int64_t>(n, 1) * 4, m);
                 void* o = (void*)alloc(std::max<int64_t>(n, 1) * 4, m);
                 rows.push_back(make(s, o, n, RC_MEAN));
+                accs.push_back(with_acc ? (const void*)alloc(std::max<int64_t>(n, 1) * 4, mis_mode == 2 ? (r + t + 1) % 4 : m)
+                                        : nullptr);
             }
         }
         std::vector<Checked> cks;
-        Error e = validate_batch(R, T, rows.data(), &cks);
+        Error e = validate_batch(R, T, rows.data(), &cks, nullptr, accs.data());
         if (e.code) {
             fail("batch validation rejected a valid call: " + e.msg);
             continue;
         }
         Config cfg;
         cfg.waves_per_cu = (int)(rng() % 9);
-        const BatchPlan bp = plan_batch(cks, cfg, dev);
-        const int unroll = unroll_for(R);
+        std::vector<Checked> nonempty;
+        for (const Checked& ck : cks)
+            if (ck.count) nonempty.push_back(ck);
+        const BatchPlan bp = plan_batch(nonempty, cfg, dev);
+        if (!nonempty.empty() && bp.acc != with_acc) fail("batched plan lost the accumulators");
+        const int unroll = unroll_for(with_acc ? 2 * R : R);
+        const int ptrs_per_job = (with_acc ? 3 : 2) * R;
+        if (bp.ptrs.size() != bp.jobs.size() * (size_t)ptrs_per_job) fail("batched pointer table has the wrong size");
         std::vector<std::vector<uint8_t>> seen(bp.jobs.size());
         for (size_t j = 0; j < bp.jobs.size(); ++j) seen[j].assign((size_t)bp.jobs[j].len, 0);
         const int64_t ngroups = (int64_t)bp.group_job.size();
@@ -274,8 +294,8 @@ int main(int argc, char** argv) {
                     if (e + i >= jb.len) fail("batched element outside its job");
                     else seen[lo][e + i] += 1;
                 }
-                for (int k = 0; k < 2 * R; ++k) {
-                    const uintptr_t ad = (uintptr_t)bp.ptrs[(size_t)lo * 2 * R + k] + (uintptr_t)(e * 4);
+                for (int k = 0; k < ptrs_per_job; ++k) {
+                    const uintptr_t ad = (uintptr_t)bp.ptrs[(size_t)lo * ptrs_per_job + k] + (uintptr_t)(e * 4);
                     if (!inside(ad, bytes)) fail("batched access outside its buffer");
                     if (bytes == 16 && ad % 16) fail("batched misaligned vector access");
                 }

@@ -65,26 +65,29 @@ def test_struct_layout_matches_a_c_compiler(tmp_path):
     src = tmp_path / "layout.c"
     src.write_text(
         '#include <stdio.h>\n#include <stddef.h>\n#include "rc.h"\n'
-        "int main(void){printf(\"%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n\","
+        "int main(void){printf(\"%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n\","
         "sizeof(rc_buf), offsetof(rc_buf, recv), offsetof(rc_buf, dtype), offsetof(rc_buf, root),"
         "offsetof(rc_buf, dims), sizeof(rc_config), offsetof(rc_config, algo),"
         "offsetof(rc_config, tile_elems), offsetof(rc_config, max_workgroups),"
-        "offsetof(rc_config, waves_per_cu));return 0;}\n")
+        "offsetof(rc_config, waves_per_cu), sizeof(rc_param), offsetof(rc_param, acc),"
+        "offsetof(rc_param, buf));return 0;}\n")
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", f"-I{ROOT / 'include'}", str(src), "-o", str(exe)],
                    check=True)
     got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
     want = [ctypes.sizeof(rr.RcBuf), rr.RcBuf.recv.offset, rr.RcBuf.dtype.offset, rr.RcBuf.root.offset,
             rr.RcBuf.dims.offset, ctypes.sizeof(rr.RcConfig), rr.RcConfig.algo.offset,
-            rr.RcConfig.tile_elems.offset, rr.RcConfig.max_workgroups.offset, rr.RcConfig.waves_per_cu.offset]
+            rr.RcConfig.tile_elems.offset, rr.RcConfig.max_workgroups.offset, rr.RcConfig.waves_per_cu.offset,
+            ctypes.sizeof(rr.RcParam), rr.RcParam.acc.offset, rr.RcParam.buf.offset]
     assert got == want
 
 
 def test_status_names(lib):
-    names = {c: lib.rc_status_name(c).decode() for c in range(10)}
+    names = {c: lib.rc_status_name(c).decode() for c in range(11)}
     assert names[0] == "RC_OK"
     assert names[3] == "RC_ERR_SHAPE_MISMATCH"
     assert names[6] == "RC_ERR_BROADCAST_SENDERS"
+    assert names[10] == "RC_ERR_PARAM_MISMATCH"
     assert lib.rc_status_name(99).decode() == "RC_UNKNOWN_STATUS"
 
 

@@ -140,3 +140,106 @@ def test_params_equal_all_reduce_many_bits():
         for r in range(R):
             assert torch.equal(a[r][k].view(-1).view(torch.int32), b[t][r].view(-1).view(torch.int32))
     assert np.all([set(m) == set(SMALL) for m in a])
+
+
+# ---------------------------------------------------------------- accumulators
+
+def make_accs(maps, ids, seed):
+    """Per-rank accumulators for the parameters in ids (every rank)."""
+    R = len(maps)
+    return [{k: si.torch_tensor_for(seed, k, R, r, tuple(maps[r][k].shape), device=DEV) for k in ids}
+            for r in range(R)]
+
+
+@pytest.mark.parametrize("R", [2, 4, 8])
+@pytest.mark.parametrize("op", ["mean", "sum"])
+def test_params_accumulated(R, op):
+    """Some parameters carry accumulators, some do not: the batch splits into
+    an accumulating and a plain launch, and both match the oracle."""
+    maps = make_maps(R, SMALL, seed=70 + R)
+    accs = make_accs(maps, [101, 7, 3, 77], seed=90 + R)
+    torch.cuda.synchronize()
+    want = oracle.all_reduce_params(host_maps(maps), op, acc=host_maps(accs))
+    with session(R, device=0):
+        got = rr.all_reduce_params(maps, op, acc=accs)
+        torch.cuda.synchronize()
+    check(got, want, f"accumulated R={R} {op}")
+
+
+@pytest.mark.parametrize("algo", ["direct", "ring"])
+def test_params_accumulated_own_launch_in_place(algo):
+    """A parameter large enough for its own fold launch (direct, or the ring's
+    two launches), written in place into the accumulators' storage."""
+    R = 4
+    specs = {5: (2_000_003,), 6: (1000,)}
+    maps = make_maps(R, specs, seed=81)
+    accs = make_accs(maps, [5, 6], seed=82)
+    torch.cuda.synchronize()
+    want = oracle.all_reduce_params(host_maps(maps), "mean", acc=host_maps(accs))
+    with session(R, device=0, algo=algo):
+        rr.all_reduce_params(maps, "mean", out=accs, acc=accs)
+        torch.cuda.synchronize()
+    check(accs, want, f"accumulated own launch {algo}, in place")
+
+
+def test_params_accumulated_i32_sum():
+    R = 4
+    specs = {1: (70_001,), 2: (33,)}
+    maps = [{k: si.torch_tensor_for(83, k, R, r, specs[k], dtype="i32", device=DEV) for k in specs} for r in range(R)]
+    accs = [{k: si.torch_tensor_for(84, k, R, r, specs[k], dtype="i32", device=DEV) for k in specs} for r in range(R)]
+    torch.cuda.synchronize()
+    want = oracle.all_reduce_params(host_maps(maps), "sum", acc=host_maps(accs))
+    with session(R, device=0):
+        got = rr.all_reduce_params(maps, "sum", acc=accs)
+        torch.cuda.synchronize()
+    check(got, want, "accumulated int32")
+
+
+def test_fused_equals_accumulate_then_sync():
+    """The fused pass gives the bits of adding the last microbatch with a
+    separate elementwise add and then syncing."""
+    R = 4
+    maps = make_maps(R, SMALL, seed=85)
+    accs = make_accs(maps, list(SMALL), seed=86)
+    with session(R, device=0):
+        fused = rr.all_reduce_params(maps, "mean", acc=accs)
+        summed = [{k: accs[r][k] + maps[r][k] for k in SMALL} for r in range(R)]
+        plain = rr.all_reduce_params(summed, "mean")
+        torch.cuda.synchronize()
+    for r in range(R):
+        for k in SMALL:
+            assert torch.equal(fused[r][k].view(-1).view(torch.int32), plain[r][k].view(-1).view(torch.int32)), k
+
+
+def test_params_accumulated_rank_threads():
+    R = 4
+    maps = make_maps(R, SMALL, seed=87)
+    accs = make_accs(maps, [101, 42, 77], seed=88)
+    torch.cuda.synchronize()
+    want = oracle.all_reduce_params(host_maps(maps), "mean", acc=host_maps(accs))
+    pool = [torch.cuda.Stream() for _ in range(R)]
+    for r in range(R):
+        rr.rank_register(r, R, device=0)
+    errs = []
+    got = [None] * R
+
+    def rank(r):
+        try:
+            with torch.cuda.stream(pool[r]):
+                out = rr.rank_all_reduce_params(r, maps[r], "mean", stream=pool[r], acc=accs[r])
+                got[r] = {k: v.clone() for k, v in out.items()}
+        except BaseException as e:  # noqa: BLE001
+            errs.append(e)
+
+    try:
+        ts = [threading.Thread(target=rank, args=(r,)) for r in range(R)]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join(timeout=120)
+        assert not errs, errs
+        torch.cuda.synchronize()
+        check(got, want, "accumulated, rank threads")
+    finally:
+        for r in range(R):
+            rr.rank_finish(r)

@@ -28,9 +28,10 @@ def cfg():
     return rr.make_config(validate_only=True)
 
 
-def rank_entries(r, specs=SPECS, order_seed=None, dtype=rr.RC_F32, op=rr.RC_MEAN, edits=None):
-    """(count, ids array, bufs array) of rank r: each parameter at its own
-    fake send/recv range, listed in a per-rank shuffled order."""
+def rank_entries(r, specs=SPECS, order_seed=None, dtype=rr.RC_F32, op=rr.RC_MEAN, edits=None, accs=None):
+    """(count, rc_param array) of rank r: each parameter at its own fake
+    send/recv range, listed in a per-rank shuffled order; accs maps an ID to
+    its accumulator address."""
     keys = list(specs)
     random.Random(order_seed if order_seed is not None else r).shuffle(keys)
     shapes, sends, recvs, dts, ops = [], [], [], [], []
@@ -43,17 +44,25 @@ def rank_entries(r, specs=SPECS, order_seed=None, dtype=rr.RC_F32, op=rr.RC_MEAN
     if edits:
         edits(keys, shapes, sends, recvs, dts, ops)
     n = len(keys)
-    ids = (ctypes.c_uint64 * max(n, 1))(*keys)
-    bufs = rr.make_bufs(sends, recvs, shapes, dts, ops) if n else (rr.RcBuf * 1)()
-    return n, ids, bufs
+    arr = (rr.RcParam * max(n, 1))()
+    if n:
+        bufs = rr.make_bufs(sends, recvs, shapes, dts, ops)
+        for i, k in enumerate(keys):
+            arr[i].id = k
+            arr[i].buf = bufs[i]
+            arr[i].acc = (accs or {}).get(k)
+    return n, arr
+
+
+def acc_addr(r, k):
+    return 0x1000000000 + r * 256 * MiB + k * MiB
 
 
 def whole_call(lib, entries):
     R = len(entries)
     counts = (ctypes.c_int * R)(*[e[0] for e in entries])
-    ids = (ctypes.c_void_p * R)(*[ctypes.addressof(e[1]) for e in entries])
-    bufs = (ctypes.c_void_p * R)(*[ctypes.addressof(e[2]) for e in entries])
-    code = lib.rc_all_reduce_params(counts, ids, bufs, None)
+    params = (ctypes.c_void_p * R)(*[ctypes.addressof(e[1]) for e in entries])
+    code = lib.rc_all_reduce_params(counts, params, None)
     return code, lib.rc_last_error().decode()
 
 
@@ -130,13 +139,13 @@ def test_argument_errors(lib):
     assert code == rr.RC_ERR_INVALID_ARGUMENT and "twice" in msg, msg
     e0 = rank_entries(0)
     counts = (ctypes.c_int * R)(-1, e0[0])
-    ids = (ctypes.c_void_p * R)(ctypes.addressof(e0[1]), ctypes.addressof(e0[1]))
-    bufs = (ctypes.c_void_p * R)(ctypes.addressof(e0[2]), ctypes.addressof(e0[2]))
-    assert lib.rc_all_reduce_params(counts, ids, bufs, None) == rr.RC_ERR_INVALID_ARGUMENT
+    params = (ctypes.c_void_p * R)(ctypes.addressof(e0[1]), ctypes.addressof(e0[1]))
+    assert lib.rc_all_reduce_params(counts, params, None) == rr.RC_ERR_INVALID_ARGUMENT
     counts = (ctypes.c_int * R)(e0[0], e0[0])
-    ids = (ctypes.c_void_p * R)(ctypes.addressof(e0[1]), None)
-    assert lib.rc_all_reduce_params(counts, ids, bufs, None) == rr.RC_ERR_INVALID_ARGUMENT
-    assert lib.rc_all_reduce_params(None, ids, bufs, None) == rr.RC_ERR_INVALID_ARGUMENT
+    params = (ctypes.c_void_p * R)(ctypes.addressof(e0[1]), None)
+    assert lib.rc_all_reduce_params(counts, params, None) == rr.RC_ERR_INVALID_ARGUMENT
+    assert lib.rc_all_reduce_params(None, params, None) == rr.RC_ERR_INVALID_ARGUMENT
+    assert lib.rc_all_reduce_params(counts, None, None) == rr.RC_ERR_INVALID_ARGUMENT
     # nothing to sync is fine
     code, msg = whole_call(lib, [rank_entries(0, {}), rank_entries(1, {})])
     assert code == rr.RC_OK, msg
@@ -173,8 +182,8 @@ def run_ranks(R, body):
 
 
 def rank_params(lib, r, entry):
-    n, ids, bufs = entry
-    return lib.rc_rank_all_reduce_params(r, n, ctypes.addressof(ids), ctypes.addressof(bufs), None)
+    n, arr = entry
+    return lib.rc_rank_all_reduce_params(r, n, ctypes.addressof(arr), None)
 
 
 def test_per_rank_sync(lib):
@@ -193,7 +202,7 @@ def test_per_rank_sync(lib):
         else:
             res.append(rank_params(lib, r, rank_entries(r)))
         if r == 2:
-            res.append(lib.rc_rank_all_reduce_params(r, 3, None, None, None))
+            res.append(lib.rc_rank_all_reduce_params(r, 3, None, None))
         else:
             res.append(rank_params(lib, r, rank_entries(r)))
         res.append(rank_params(lib, r, rank_entries(r)))
@@ -207,3 +216,43 @@ def test_per_rank_sync(lib):
         assert res[22] == rr.RC_ERR_INVALID_ARGUMENT
         assert res[23] == rr.RC_OK
         assert res[24] == rr.RC_OK
+
+
+def test_accumulators(lib):
+    """acc on every rank or none, Sum/Mean only, aligned, and overlapping
+    nothing but its own rank's output."""
+    R = 3
+    assert lib.rc_register(R, ctypes.byref(cfg())) == rr.RC_OK
+    every = [rank_entries(r, accs={k: acc_addr(r, k) for k in SPECS}) for r in range(R)]
+    code, msg = whole_call(lib, every)
+    assert code == rr.RC_OK, msg
+    # only some parameters carry accumulators: fine, they are batched apart
+    some = [rank_entries(r, accs={k: acc_addr(r, k) for k in (3, 99)}) for r in range(R)]
+    code, msg = whole_call(lib, some)
+    assert code == rr.RC_OK, msg
+    partial = [rank_entries(r, accs={99: acc_addr(r, 99)} if r != 1 else {}) for r in range(R)]
+    code, msg = whole_call(lib, partial)
+    assert code == rr.RC_ERR_INVALID_ARGUMENT and "parameter 99" in msg and "some ranks" in msg, msg
+    mx = [rank_entries(r, op=rr.RC_MAX, accs={3: acc_addr(r, 3)}) for r in range(R)]
+    code, msg = whole_call(lib, mx)
+    assert code == rr.RC_ERR_INVALID_ARGUMENT and "Sum or Mean" in msg, msg
+    mis = [rank_entries(r, accs={3: acc_addr(r, 3) + (2 if r == 2 else 0)}) for r in range(R)]
+    code, msg = whole_call(lib, mis)
+    assert code == rr.RC_ERR_INVALID_ARGUMENT and "misaligned" in msg, msg
+    # in place into the accumulator: recv == acc on every rank
+    def recv_is_acc(r):
+        def edit(keys, shapes, sends, recvs, dts, ops):
+            recvs[keys.index(99)] = acc_addr(r, 99)
+        return edit
+    inplace = [rank_entries(r, edits=recv_is_acc(r), accs={99: acc_addr(r, 99)}) for r in range(R)]
+    code, msg = whole_call(lib, inplace)
+    assert code == rr.RC_OK, msg
+    # an accumulator that is another rank's output
+    clash = [rank_entries(r, accs={99: (0x800000000 + 256 * MiB + 99 * MiB) if r == 0 else acc_addr(r, 99)})
+             for r in range(R)]
+    code, msg = whole_call(lib, clash)
+    assert code == rr.RC_ERR_INVALID_ARGUMENT, msg
+    # and an empty parameter ignores its accumulator fields entirely
+    empty = [rank_entries(r, accs={40: acc_addr(r, 40)} if r == 0 else {}) for r in range(R)]
+    code, msg = whole_call(lib, empty)
+    assert code == rr.RC_OK, msg
