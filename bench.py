@@ -204,7 +204,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": read_traffic() if args.algo != "ring" else None,
-            "kernel": "fold_kernel<8, OpSumF32, 1, true>" if args.algo != "ring" else "ring phases",
+            "kernel": "fold_kernel<8, OpSumF32, 1, true, false>" if args.algo != "ring" else "ring phases",
             "algorithmic_bytes_per_launch": hbm_bytes // launches_per_call,
             "avg_launch_us": round(launch_ms * 1e3, 2),
         },
@@ -297,8 +297,43 @@ def rows(torch, rr, si, dev, xs8, args):
     row = _roof(2 * R4 * elems * 4, us)
     row.update({"tensors": len(shapes), "elems_per_rank": elems, "layers": layers})
     out[f"all_reduce_many_r4_{layers}layer_grads_f32_mean"] = row
+    # the same list as per-rank maps keyed by parameter ID, each rank listing
+    # its IDs in its own order
+    import random
+    grads = []
+    for r in range(R4):
+        ids = list(range(len(shapes)))
+        random.Random(r).shuffle(ids)
+        grads.append({t: ts[t][r] for t in ids})
+    outs = [{t: os_[t][r] for t in range(len(shapes))} for r in range(R4)]
+    us = time_calls(torch, lambda: rr.all_reduce_params(grads, "mean", out=outs), 3, warmup=1) * 1e3
+    row = _roof(2 * R4 * elems * 4, us)
+    row.update({"tensors": len(shapes), "elems_per_rank": elems})
+    out[f"all_reduce_params_r4_{layers}layer_grads_f32_mean"] = row
+    # gradient accumulation: the last microbatch added to the accumulators
+    # inside the sync (one pass) against a separate elementwise add and then
+    # the sync (two passes); both give the same bits
+    log("bench: rows: accumulated gradient sync, fused and separate")
+    accs = [{t: torch.empty_like(ts[t][r]).normal_(0.0, 1e-3) for t in range(len(shapes))} for r in range(R4)]
+    us = time_calls(torch, lambda: rr.all_reduce_params(grads, "mean", out=outs, acc=accs), 3, warmup=1) * 1e3
+    row = _roof(3 * R4 * elems * 4, us)
+    row.update({"tensors": len(shapes), "elems_per_rank": elems,
+                "bytes": "read acc and grad, write the output: 3*R*N*4"})
+    out[f"all_reduce_params_acc_fused_r4_{layers}layer_grads_f32_mean"] = row
+
+    def separate():
+        for r in range(R4):
+            for t in range(len(shapes)):
+                accs[r][t].add_(grads[r][t])
+        rr.all_reduce_params(accs, "mean", out=outs)
+
+    us = time_calls(torch, separate, 3, warmup=1) * 1e3
+    row = _roof(5 * R4 * elems * 4, us)
+    row.update({"tensors": len(shapes), "elems_per_rank": elems,
+                "bytes": "torch add (2 reads, 1 write) then the sync (1 read, 1 write): 5*R*N*4"})
+    out[f"accumulate_then_sync_r4_{layers}layer_grads_f32_mean"] = row
     rr.finish()
-    del ts, os_
+    del ts, os_, grads, outs, accs
     torch.cuda.empty_cache()
     return out
 
