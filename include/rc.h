@@ -10,10 +10,14 @@
  * `Struct Communicator` page.  Every collective takes a stream, as the
  * Communicator methods do, and returns a status code.
  *
- * One call carries all R ranks' arguments (one rc_buf per logical rank), so
- * the contract that every rank issues matching collectives in the same order
- * (ruCCL README section 3; Communicator's Send/Sync safety note) holds by
- * construction, and mismatches between ranks are detected inside one call.
+ * Two ways to call.  The whole-call entry points take all R ranks' arguments
+ * at once (one rc_buf per logical rank), so the contract that every rank
+ * issues matching collectives in the same order (ruCCL README section 3;
+ * Communicator's Send/Sync safety note) holds by construction and mismatches
+ * between ranks are detected inside one call.  The per-rank entry points
+ * (rc_rank_*, below) take one rank's side per call, from that rank's own
+ * thread, and match the ranks' calls by issue order.  Gradient syncs keyed by
+ * parameter ID (ruCCL README section 6) come in both forms.
  *
  * Numerics.  Each collective reduces along the ring: for element counts N over
  * R ranks, the segment length is S = ceil(N/R) and segment c = [c*S,
