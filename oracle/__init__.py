@@ -12,4 +12,5 @@ from .ring import (  # noqa: F401
     all_reduce, reduce, broadcast, reduce_scatter, all_gather, all_reduce_many,
     all_reduce_closed_form, all_reduce_at, all_reduce_at_many,
     ParamMismatch, all_reduce_params, accumulate,
+    all_gather_list, all_to_all_single, send_recv,
 )

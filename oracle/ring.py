@@ -281,6 +281,48 @@ def all_reduce_many(tensors, op=MEAN):
 
 
 # --------------------------------------------------------------------------
+# Copies between ranks (monarch Communicator page)
+# --------------------------------------------------------------------------
+
+def all_gather_list(shards):
+    """Communicator.all_gather, the list form: every rank receives one output
+    tensor per source rank, the k-th being rank k's input.  Returns out[r][k]
+    (copies)."""
+    _validate_ranks(shards)
+    R = len(shards)
+    return [[np.array(shards[k], copy=True) for k in range(R)] for _ in range(R)]
+
+
+def all_to_all_single(xs):
+    """Communicator.all_to_all_single: each rank's input is split into R equal
+    chunks, chunk d is scattered to rank d, and each rank concatenates the
+    chunks it receives in source-rank order.  An input length not divisible by
+    R is an error (the page's form has no split sizes, so the chunks are
+    equal).  Returns R arrays shaped like the inputs."""
+    _validate_ranks(xs)
+    R = len(xs)
+    shape = np.shape(xs[0])
+    flat = [_flat(x) for x in xs]
+    n = flat[0].size
+    if n % R:
+        raise OracleError("all_to_all_single input length must be a multiple of R")
+    m = n // R
+    out = [np.empty_like(flat[0]) for _ in range(R)]
+    for src in range(R):
+        for dst in range(R):
+            out[dst][src * m:(src + 1) * m] = flat[src][dst * m:(dst + 1) * m]
+    return [o.reshape(shape) for o in out]
+
+
+def send_recv(x):
+    """Communicator.send on the source rank and recv on the destination: the
+    receiver's tensor gets the sender's bytes."""
+    x = np.asarray(x)
+    _check_dtype(x)
+    return x.copy()
+
+
+# --------------------------------------------------------------------------
 # Gradient synchronisation keyed by parameter ID
 # --------------------------------------------------------------------------
 

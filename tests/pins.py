@@ -319,6 +319,75 @@ def pin_invariants(orc):
                 assert_bits_equal(xs[r], keep[r], "input modified")
 
 
+def load_all_to_all_example():
+    ex = {"in": {}, "out": {}}
+    for line in (GOLDEN / "all_to_all_example.txt").read_text().splitlines():
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, *rest = line.split()
+        if key == "R":
+            ex["R"] = int(rest[0])
+        else:
+            ex[key][int(rest[0])] = np.array([int(v) for v in rest[1:]], dtype=np.int32)
+    return ex
+
+
+def pin_all_to_all(orc):
+    """all_to_all_single (Communicator page): the hand-derived worked example
+    in tests/golden; applying it twice gives back the inputs (chunk d of rank
+    s goes to chunk s of rank d, and back); every element keeps its bits
+    (a permutation: the multiset of all ranks' values is unchanged); R = 1 is
+    a copy; a length not divisible by R is refused."""
+    ex = load_all_to_all_example()
+    R = ex["R"]
+    got = orc.all_to_all_single([ex["in"][r] for r in range(R)])
+    for r in range(R):
+        assert_bits_equal(got[r], ex["out"][r], f"worked example rank {r}")
+    rng = _rng(37)
+    for R in (1, 2, 3, 5, 8):
+        for m in (0, 1, 3, 64):
+            xs = [rng.standard_normal((R * m,)).astype(np.float32) for _ in range(R)]
+            once = orc.all_to_all_single(xs)
+            twice = orc.all_to_all_single(once)
+            for r in range(R):
+                assert_bits_equal(twice[r], xs[r], f"R={R} m={m}: twice is not the identity")
+            a = np.sort(np.concatenate([bits(x).reshape(-1) for x in xs]))
+            b = np.sort(np.concatenate([bits(x).reshape(-1) for x in once]))
+            assert np.array_equal(a, b), "values changed"
+            if R == 1:
+                assert_bits_equal(once[0], xs[0], "single rank is a copy")
+    try:
+        orc.all_to_all_single([np.zeros(5, np.float32)] * 2)
+    except orc.OracleError:
+        pass
+    else:
+        raise AssertionError("a length not divisible by R was accepted")
+
+
+def pin_all_gather_list(orc):
+    """The list form of all_gather (Communicator.all_gather) holds, rank by
+    rank, the pieces of the single-tensor form (all_gather_into_tensor, pinned
+    to numpy.concatenate): output k of every rank is rank k's input, bit for
+    bit, as a copy; shapes are kept."""
+    rng = _rng(41)
+    for R in (1, 2, 4, 7):
+        shards = [rng.standard_normal((3, 5)).astype(np.float32) for _ in range(R)]
+        out = orc.all_gather_list(shards)
+        flat = np.concatenate([s.reshape(-1) for s in shards])
+        assert len(out) == R
+        for r in range(R):
+            assert len(out[r]) == R
+            assert_bits_equal(np.concatenate([o.reshape(-1) for o in out[r]]), flat, f"R={R} rank {r}")
+            for k in range(R):
+                assert out[r][k].shape == (3, 5)
+                assert not np.shares_memory(out[r][k], shards[k]), "output aliases an input"
+    x = np.arange(7, dtype=np.int32)
+    y = orc.send_recv(x)
+    assert_bits_equal(y, x, "send/recv copies")
+    assert not np.shares_memory(x, y)
+
+
 def _param_maps(rng, R, specs, int_valued=True, seed_order=0):
     """R maps {id: array}; rank r inserts its entries in its own order."""
     order_rng = _rng(1000 + seed_order)
@@ -469,4 +538,6 @@ ALL_PINS = [
     pin_params,
     pin_params_accumulated,
     pin_accumulate,
+    pin_all_to_all,
+    pin_all_gather_list,
 ]

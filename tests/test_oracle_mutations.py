@@ -74,6 +74,16 @@ MUTATIONS = {
     "params_acc_from_rank0": ("                operands = [accumulate(acc[r][pid], operands[r]) for r in range(R)]",
                               "                operands = [accumulate(acc[0][pid], operands[r]) for r in range(R)]"),
     "params_acc_partial_accepted": ("            if any(given) and not all(given):", "            if False:"),
+    "a2a_transposed": ("out[dst][src * m:(src + 1) * m] = flat[src][dst * m:(dst + 1) * m]",
+                       "out[src][dst * m:(dst + 1) * m] = flat[src][dst * m:(dst + 1) * m]"),
+    "a2a_wrong_chunk": ("out[dst][src * m:(src + 1) * m] = flat[src][dst * m:(dst + 1) * m]",
+                        "out[dst][src * m:(src + 1) * m] = flat[src][src * m:(src + 1) * m]"),
+    "a2a_reversed_sources": ("out[dst][src * m:(src + 1) * m] = flat[src][dst * m:(dst + 1) * m]",
+                             "out[dst][(R - 1 - src) * m:(R - src) * m] = flat[src][dst * m:(dst + 1) * m]"),
+    "gather_list_own_shard": ("return [[np.array(shards[k], copy=True) for k in range(R)] for _ in range(R)]",
+                              "return [[np.array(shards[r], copy=True) for k in range(R)] for r in range(R)]"),
+    "gather_list_aliases": ("return [[np.array(shards[k], copy=True) for k in range(R)] for _ in range(R)]",
+                            "return [[shards[k] for k in range(R)] for _ in range(R)]"),
     "accumulate_averages": ("return combine(_flat(acc), _flat(grad), SUM).reshape(acc.shape)",
                             "return (combine(_flat(acc), _flat(grad), SUM) / np.float32(2)).reshape(acc.shape)"),
     "accumulate_aliases": ("        return grad.copy()", "        return grad"),
