@@ -191,6 +191,36 @@ int rc_reduce_scatter(const rc_buf* bufs, void* stream);
  * bit.  In place is allowed as send_r == recv_r + r*M elements. */
 int rc_all_gather(const rc_buf* bufs, void* stream);
 
+/* all_gather, list form (Communicator.all_gather: one output tensor per
+ * source rank).  bufs[r].send is rank r's shard of count M elements (dims
+ * describe it); bufs[r].recv is not used.  recvs[r * num_ranks + k] is rank
+ * r's output for rank k's shard (M elements), receiving it bit for bit.  The
+ * output a rank keeps for its own shard may be the shard itself
+ * (recvs[r * num_ranks + r] == bufs[r].send); any other overlap is
+ * RC_ERR_INVALID_ARGUMENT.  recvs is read during the call only. */
+int rc_all_gather_list(const rc_buf* bufs, void* const* recvs, void* stream);
+
+/* all_to_all_single (Communicator page: split the input, scatter the splits
+ * to all ranks, concatenate what is received).  Each send holds count = R*M
+ * elements and each recv the same count; rank d's recv receives, at [s*M,
+ * (s+1)*M), the elements [d*M, (d+1)*M) of rank s's send, bit for bit.  A
+ * count not divisible by R is RC_ERR_SHAPE_MISMATCH; no in-place layout
+ * exists (recv overlapping any send is RC_ERR_INVALID_ARGUMENT). */
+int rc_all_to_all_single(const rc_buf* bufs, void* stream);
+
+/* Communicator.send on rank src together with Communicator.recv on rank dst,
+ * as one call: bufs[0] is the sender's side (send used), bufs[1] the
+ * receiver's (recv used); dtype and shape must agree (RC_ERR_DTYPE_MISMATCH,
+ * RC_ERR_SHAPE_MISMATCH); src and dst are different ranks in [0, num_ranks).
+ * recv == send moves nothing. */
+int rc_send_recv(int src, int dst, const rc_buf* bufs, void* stream);
+
+/* Communicator.barrier.  With every rank's work issued on the one stream of
+ * the whole-call entry points, it is already in order: this checks the
+ * session and enqueues nothing.  The per-rank form below joins the ranks'
+ * streams. */
+int rc_barrier(void* stream);
+
 /* Whole-gradient all-reduce (ruCCL README section 6, "Collective training":
  * grads.all_reduce_with(communicator, ReduceOperation::Mean) reduces every
  * gradient of a parameter set, with IDs, shapes, dtype and call order
@@ -296,6 +326,29 @@ int rc_rank_reduce(int rank, const rc_buf* buf, void* stream);
 int rc_rank_broadcast(int rank, const rc_buf* buf, void* stream);
 int rc_rank_reduce_scatter(int rank, const rc_buf* buf, void* stream);
 int rc_rank_all_gather(int rank, const rc_buf* buf, void* stream);
+
+/* Rank `rank`'s side of rc_all_gather_list: buf describes its shard and
+ * recvs[k], k < num_ranks, are its outputs for rank k's shard. */
+int rc_rank_all_gather_list(int rank, const rc_buf* buf, void* const* recvs, void* stream);
+
+/* Rank `rank`'s side of rc_all_to_all_single. */
+int rc_rank_all_to_all_single(int rank, const rc_buf* buf, void* stream);
+
+/* Communicator.send and recv on logical ranks.  Unlike the collectives, a
+ * send from rank a to rank b is matched only with recvs on b from a: the k-th
+ * such send meets the k-th such recv, whatever the other ranks call.  Each
+ * call blocks until its peer's call arrives (a send and a recv that wait on
+ * each other in opposite orders never complete, as with unbuffered
+ * point-to-point).  buf.send is the sender's tensor, buf.recv the receiver's;
+ * checks as rc_send_recv, reported to both sides.  A peer out of range or
+ * equal to the rank: RC_ERR_INVALID_ARGUMENT, nothing matched. */
+int rc_rank_send(int rank, const rc_buf* buf, int dst, void* stream);
+int rc_rank_recv(int rank, const rc_buf* buf, int src, void* stream);
+
+/* Communicator.barrier: the k-th barrier of every rank forms one barrier.
+ * Work each rank enqueues after it is ordered after the work every rank had
+ * enqueued before it; nothing else is launched. */
+int rc_rank_barrier(int rank, void* stream);
 
 /* Rank `rank`'s side of rc_all_reduce_params: its own num_params entries,
  * in any order.  The gradient sync as the pages call it, once per rank with

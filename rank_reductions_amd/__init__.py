@@ -33,6 +33,8 @@ __all__ = [
     "RC_ERR_DTYPE_MISMATCH", "RC_ERR_INVALID_ARGUMENT", "RC_ERR_DEVICE", "RC_ERR_PARAM_MISMATCH",
     "all_reduce_params", "rank_register", "rank_finish", "rank_all_reduce", "rank_reduce",
     "rank_broadcast", "rank_reduce_scatter", "rank_all_gather", "rank_all_reduce_params",
+    "all_gather_list", "all_to_all_single", "send_recv", "barrier", "rank_all_gather_list",
+    "rank_all_to_all_single", "rank_send", "rank_recv", "rank_barrier",
 ]
 
 RC_MAX_RANKS = 16
@@ -151,6 +153,23 @@ def library():
     lib.rc_all_reduce_params.restype = ctypes.c_int
     lib.rc_rank_all_reduce_params.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.rc_rank_all_reduce_params.restype = ctypes.c_int
+    lib.rc_all_gather_list.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.rc_all_gather_list.restype = ctypes.c_int
+    lib.rc_all_to_all_single.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.rc_all_to_all_single.restype = ctypes.c_int
+    lib.rc_send_recv.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.rc_send_recv.restype = ctypes.c_int
+    lib.rc_barrier.argtypes = [ctypes.c_void_p]
+    lib.rc_barrier.restype = ctypes.c_int
+    lib.rc_rank_all_gather_list.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.rc_rank_all_gather_list.restype = ctypes.c_int
+    lib.rc_rank_all_to_all_single.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.rc_rank_all_to_all_single.restype = ctypes.c_int
+    for name in ("rc_rank_send", "rc_rank_recv"):
+        getattr(lib, name).argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+        getattr(lib, name).restype = ctypes.c_int
+    lib.rc_rank_barrier.argtypes = [ctypes.c_int, ctypes.c_void_p]
+    lib.rc_rank_barrier.restype = ctypes.c_int
     lib.rc_rank_finish.argtypes = [ctypes.c_int]
     lib.rc_rank_finish.restype = ctypes.c_int
     _lib = lib
@@ -379,6 +398,50 @@ def all_reduce_many(tensors, op="mean", out=None, stream=None):
     return out
 
 
+def all_gather_list(shards, out=None, stream=None):
+    """Communicator.all_gather, the list form: out[r][k] receives rank k's
+    shard on every rank r (allocated when out is None)."""
+    torch = _torch()
+    R = len(shards)
+    if out is None:
+        out = [[torch.empty_like(shards[k]) for k in range(R)] for _ in range(R)]
+    bufs = make_bufs([_ptr(x) for x in shards], [None] * R, [tuple(x.shape) for x in shards],
+                     [_dtype_code(x) for x in shards])
+    recvs = (ctypes.c_void_p * (R * R))(*[_ptr(out[r][k]) for r in range(R) for k in range(R)])
+    check(library().rc_all_gather_list(ctypes.cast(bufs, ctypes.c_void_p), recvs,
+                                       ctypes.c_void_p(_stream(stream, shards[0]))))
+    return out
+
+
+def all_to_all_single(xs, out=None, stream=None):
+    """Communicator.all_to_all_single: rank d's output holds, in source-rank
+    order, split d of every rank's input (equal splits of N/R elements)."""
+    torch = _torch()
+    if out is None:
+        out = [torch.empty_like(x) for x in xs]
+    _call(library().rc_all_to_all_single, xs, out, stream=stream)
+    return out
+
+
+def send_recv(x, src, dst, out=None, stream=None):
+    """Communicator.send on rank src and recv on rank dst, as one call: out
+    (rank dst's tensor) receives x (rank src's)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(x)
+    bufs = make_bufs([_ptr(x), None], [None, _ptr(out)], [tuple(x.shape), tuple(out.shape)],
+                     [_dtype_code(x), _dtype_code(out)])
+    check(library().rc_send_recv(int(src), int(dst), ctypes.cast(bufs, ctypes.c_void_p),
+                                 ctypes.c_void_p(_stream(stream, x))))
+    return out
+
+
+def barrier(stream=None):
+    """Communicator.barrier for the whole-call form (one stream: nothing to join)."""
+    s = stream.cuda_stream if hasattr(stream, "cuda_stream") else (int(stream) if stream else 0)
+    return check(library().rc_barrier(ctypes.c_void_p(s)))
+
+
 def _param_entries(grads, outs, op, acc=None):
     """One rank's map as an rc_param array (in the map's order) and its length."""
     keys = list(grads)
@@ -504,3 +567,48 @@ def rank_all_reduce_params(rank, grads, op="mean", out=None, stream=None, acc=No
     s = _stream_for(stream, _first_tensor([grads]))
     check(library().rc_rank_all_reduce_params(int(rank), n, ctypes.addressof(arr), ctypes.c_void_p(s)))
     return out
+
+
+def rank_all_gather_list(rank, shard, num_ranks, out=None, stream=None):
+    """Rank `rank`'s side of all_gather_list: out[k] receives rank k's shard."""
+    torch = _torch()
+    if out is None:
+        out = [torch.empty_like(shard) for _ in range(num_ranks)]
+    bufs = make_bufs([_ptr(shard)], [None], [tuple(shard.shape)], [_dtype_code(shard)])
+    recvs = (ctypes.c_void_p * num_ranks)(*[_ptr(o) for o in out])
+    check(library().rc_rank_all_gather_list(int(rank), ctypes.cast(bufs, ctypes.c_void_p), recvs,
+                                            ctypes.c_void_p(_stream(stream, shard))))
+    return out
+
+
+def rank_all_to_all_single(rank, x, out=None, stream=None):
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(x)
+    _rank_call(library().rc_rank_all_to_all_single, rank, x, out, RC_SUM, 0, stream)
+    return out
+
+
+def rank_send(rank, x, dst, stream=None):
+    """Communicator.send from logical rank `rank` to `dst`; blocks until dst's
+    matching recv arrives."""
+    bufs = make_bufs([_ptr(x)], [None], [tuple(x.shape)], [_dtype_code(x)])
+    check(library().rc_rank_send(int(rank), ctypes.cast(bufs, ctypes.c_void_p), int(dst),
+                                 ctypes.c_void_p(_stream(stream, x))))
+
+
+def rank_recv(rank, out, src, stream=None):
+    """Communicator.recv on logical rank `rank` from `src` into out."""
+    bufs = make_bufs([None], [_ptr(out)], [tuple(out.shape)], [_dtype_code(out)])
+    check(library().rc_rank_recv(int(rank), ctypes.cast(bufs, ctypes.c_void_p), int(src),
+                                 ctypes.c_void_p(_stream(stream, out))))
+    return out
+
+
+def rank_barrier(rank, stream=None):
+    """Communicator.barrier for logical rank `rank`."""
+    if stream is None:
+        s = _torch().cuda.current_stream().cuda_stream
+    else:
+        s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    check(library().rc_rank_barrier(int(rank), ctypes.c_void_p(s)))

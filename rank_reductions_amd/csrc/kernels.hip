@@ -381,6 +381,22 @@ __global__ __launch_bounds__(kBlock) void batch_kernel(BatchArgs a) {
     }
 }
 
+// Batched copies over a job table (all_to_all_single, the list form of
+// all_gather): job j copies tp[0] to the NR destinations tp[1..NR], bit for bit.
+template <int NR, int U, bool NT>
+__global__ __launch_bounds__(kBlock) void copy_batch_kernel(BatchArgs a) {
+    for (int64_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
+        const int j = find_job(a, t);
+        const BatchJob jb = a.jobs[j];
+        const void* const* tp = a.ptrs + (int64_t)j * (1 + NR);
+        const uint32_t* in[1] = {static_cast<const uint32_t*>(tp[0])};
+        const uint32_t* none[1] = {nullptr};
+        auto out = [&](int o) { return static_cast<uint32_t*>(const_cast<void*>(tp[1 + o])); };
+        job_tile<1, NR, OpSumI32, U, NT, false>(in, none, out, (1u << NR) - 1u, jb.len, jb.phase,
+                                                t - jb.tile_begin, a.tile_elems, false);
+    }
+}
+
 // ---------------------------------------------------------------- dispatch
 
 // Vectors per lane per round: about eight 16-byte loads in flight per lane,
@@ -495,6 +511,14 @@ BatchFn pick_batch_op(int dtype, int op, int nin) {
 }
 
 template <bool NT>
+struct CopyBatchOf {
+    template <int NR>
+    struct At {
+        static BatchFn get() { return copy_batch_kernel<NR, kCopyUnroll, NT>; }
+    };
+};
+
+template <bool NT>
 FoldFn pick_fold_any(int dtype, int op, int nin, bool acc) {
     return acc ? pick_fold_op<NT, true>(dtype, op, nin) : pick_fold_op<NT, false>(dtype, op, nin);
 }
@@ -519,8 +543,11 @@ hipError_t launch_jobs(const LaunchPlan& p, hipStream_t stream) {
 hipError_t launch_batch(const BatchJob* jobs, const int32_t* group_job, const void* const* ptrs,
                         const BatchPlan& p, hipStream_t stream) {
     const bool nt = p.nontemporal != 0;
-    BatchFn fn = nt ? pick_batch_any<true>(p.dtype, p.op, p.nranks, p.acc)
-                    : pick_batch_any<false>(p.dtype, p.op, p.nranks, p.acc);
+    BatchFn fn;
+    if (p.copy) fn = nt ? pick_nin<CopyBatchOf<true>::template At, BatchFn>(p.nout)
+                        : pick_nin<CopyBatchOf<false>::template At, BatchFn>(p.nout);
+    else fn = nt ? pick_batch_any<true>(p.dtype, p.op, p.nranks, p.acc)
+                 : pick_batch_any<false>(p.dtype, p.op, p.nranks, p.acc);
     if (!fn) return hipErrorInvalidValue;
     BatchArgs a;
     a.jobs = jobs;

@@ -63,6 +63,19 @@ int nontemporal_of(const Config& cfg) {
     return cfg.cache_hint == RC_CACHE_NORMAL ? 0 : 1;
 }
 
+// Group index of a batch: the job holding the first tile of every group of
+// 2^kGroupShift tiles.
+void build_groups(BatchPlan* bp) {
+    const int64_t groups = (bp->total_tiles + (int64_t(1) << kGroupShift) - 1) >> kGroupShift;
+    bp->group_job.resize(groups);
+    size_t j = 0;
+    for (int64_t g = 0; g < groups; ++g) {
+        const int64_t t = g << kGroupShift;
+        while (j + 1 < bp->jobs.size() && bp->jobs[j + 1].tile_begin <= t) ++j;
+        bp->group_job[g] = (int32_t)j;
+    }
+}
+
 }  // namespace
 
 int tile_elems_for(int unroll, const Config& cfg) {
@@ -251,6 +264,29 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceI
             out.push_back(p);
             break;
         }
+        case Coll::SendRecv: {
+            // one job: the sender's buffer to the receiver's (nothing when they coincide)
+            copy_setup(p);
+            a.nranks = 1;
+            a.out_mode = kOutMask;
+            a.n = ck.count;
+            a.seg = ck.count;
+            a.in_stride = 0;
+            a.out_stride = 0;
+            a.jobs = 1;
+            a.in[0] = ck.send[0];
+            a.out[0] = ck.recv[0];
+            a.out_mask = ck.send[0] != ck.recv[0] ? 1u : 0u;
+            if (!a.out_mask) break;
+            ad.assign(1, {addr(a.in[0], 0, es), addr(a.out[0], 0, es)});
+            finish_jobs(&p, ad);
+            out.push_back(p);
+            break;
+        }
+        case Coll::AllToAll:
+        case Coll::AllGatherList:  // batches of copies: plan_copies
+        case Coll::Barrier:        // no kernel
+            break;
         case Coll::AllGather: {
             const int64_t M = ck.count;
             copy_setup(p);
@@ -344,16 +380,56 @@ BatchPlan plan_batch(const std::vector<Checked>& tensors, const Config& cfg, con
         }
     }
     bp.total_tiles = tiles;
-    // group index: the job holding the first tile of every group of 2^kGroupShift tiles
-    const int64_t groups = (tiles + (int64_t(1) << kGroupShift) - 1) >> kGroupShift;
-    bp.group_job.resize(groups);
-    size_t j = 0;
-    for (int64_t g = 0; g < groups; ++g) {
-        const int64_t t = g << kGroupShift;
-        while (j + 1 < bp.jobs.size() && bp.jobs[j + 1].tile_begin <= t) ++j;
-        bp.group_job[g] = (int32_t)j;
-    }
+    build_groups(&bp);
     shape_launch(tiles, loads, R, unroll, cfg, dev, &bp.grid, &bp.lds_bytes);
+    return bp;
+}
+
+// all_to_all_single (Communicator page: split, scatter, concatenate): job
+// (d, s) copies chunk d of rank s's input to chunk s of rank d's output.  The
+// list form of all_gather: job k copies rank k's shard to every rank's output
+// for shard k.
+BatchPlan plan_copies(const Checked& ck, const Config& cfg, const DeviceInfo& dev) {
+    BatchPlan bp;
+    if (ck.count == 0) return bp;
+    const int R = ck.nranks;
+    const int64_t es = element_size(ck.dtype);
+    bp.copy = true;
+    bp.nranks = R;
+    bp.dtype = ck.dtype;
+    bp.op = RC_SUM;
+    bp.nontemporal = nontemporal_of(cfg);
+    bp.tile_elems = tile_elems_for(kCopyUnroll, cfg);
+    std::vector<uintptr_t> ad;
+    int64_t tiles = 0;
+    auto add_job = [&](int64_t len) {
+        BatchJob j{};
+        j.tile_begin = tiles;
+        j.len = len;
+        j.phase = job_phase(ad.data(), (int)ad.size(), es, len);
+        tiles += job_tiles(len, (uint8_t)j.phase, bp.tile_elems);
+        bp.jobs.push_back(j);
+        for (uintptr_t a : ad) bp.ptrs.push_back(reinterpret_cast<const void*>(a));
+    };
+    if (ck.coll == Coll::AllToAll) {
+        const int64_t m = ck.count / R;
+        bp.nout = 1;
+        for (int d = 0; d < R; ++d)
+            for (int s = 0; s < R; ++s) {
+                ad.assign({addr(ck.send[s], (int64_t)d * m, es), addr(ck.recv[d], (int64_t)s * m, es)});
+                add_job(m);
+            }
+    } else {
+        bp.nout = R;
+        for (int k = 0; k < R; ++k) {
+            ad.assign(1, addr(ck.send[k], 0, es));
+            for (int r = 0; r < R; ++r) ad.push_back(addr(ck.recv_list[(size_t)r * R + k], 0, es));
+            add_job(ck.count);
+        }
+    }
+    bp.total_tiles = tiles;
+    build_groups(&bp);
+    shape_launch(tiles, 1, bp.nout, kCopyUnroll, cfg, dev, &bp.grid, &bp.lds_bytes);
     return bp;
 }
 

@@ -17,7 +17,9 @@ constexpr int kBlock = 64;           // threads per workgroup: one wave64
 constexpr int kVec = 4;              // elements per 16-byte vector
 constexpr uint8_t kScalarOnly = 0xFF;  // job phase: pointers not co-aligned
 
-enum class Coll { AllReduce, Reduce, Broadcast, ReduceScatter, AllGather };
+// The first five are reductions or fan-outs over ring segments; the rest are
+// the Communicator page's other methods: copies between ranks and a barrier.
+enum class Coll { AllReduce, Reduce, Broadcast, ReduceScatter, AllGather, AllToAll, AllGatherList, SendRecv, Barrier };
 
 // How a job's inputs are formed.
 enum InMode : int32_t {
@@ -101,6 +103,8 @@ struct Checked {
     // all_reduce over acc[r] + send[r] (a gradient sync's accumulators)
     bool has_acc = false;
     const void* acc[kMaxRanks] = {};
+    // all_gather, list form: rank r's output for rank k's shard at [r*R + k]
+    std::vector<void*> recv_list;
 };
 
 struct Error {
@@ -109,7 +113,12 @@ struct Error {
 };
 
 // ---------------------------------------------------------------- validate.cpp
-Error validate(Coll coll, int nranks, const rc_buf* bufs, Checked* out);
+Error validate(Coll coll, int nranks, const rc_buf* bufs, Checked* out, void* const* recv_list = nullptr);
+// send on rank src and recv on rank dst as one copy: bufs[0] is the sender's
+// side, bufs[1] the receiver's.  The result is a SendRecv with send[0] and
+// recv[0] set and root = src.
+Error validate_send_recv(int nranks, int src, int dst, const rc_buf* bufs, Checked* out);
+const char* coll_name(Coll c);
 // Tensor t of a batched all-reduce; messages name the tensor index, or
 // ids[t] when ids is given (a gradient sync's parameter IDs).  accs, when
 // given, holds tensor t's accumulators at [t*R + r] (NULL: none).
@@ -165,6 +174,10 @@ struct BatchPlan {
     // their accumulators in the same order, then the outputs
     std::vector<const void*> ptrs;
     bool acc = false;
+    // a batch of copies instead of folds: ptrs is [job][1 + nout], the
+    // source then nout destinations, all at the job's first element
+    bool copy = false;
+    int nout = 0;
     std::vector<int32_t> group_job;  // job holding tile g << kGroupShift, per group g
     int64_t total_tiles = 0;
     int tile_elems = 0;
@@ -176,6 +189,11 @@ struct BatchPlan {
     int lds_bytes = 0;
 };
 BatchPlan plan_batch(const std::vector<Checked>& tensors, const Config& cfg, const DeviceInfo& dev);
+// The copy jobs of all_to_all_single and of the list form of all_gather.
+BatchPlan plan_copies(const Checked& ck, const Config& cfg, const DeviceInfo& dev);
+// Whether a validated call runs as a batch of copies (plan_copies) rather
+// than through plan().
+inline bool runs_as_copies(Coll c) { return c == Coll::AllToAll || c == Coll::AllGatherList; }
 
 // A batched all-reduce splits into tensors large enough to run as launches of
 // their own (their kernel time dwarfs a launch boundary, and they avoid the

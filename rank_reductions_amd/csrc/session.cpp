@@ -20,6 +20,7 @@
 #include <memory>
 #include <mutex>
 #include <string>
+#include <tuple>
 #include <vector>
 
 #include "rc_internal.h"
@@ -39,6 +40,8 @@ struct Slot {
     std::vector<uint8_t> is_params;
     std::vector<int> pcount;
     std::vector<std::vector<rc_param>> params;
+    // all_gather, list form: each rank's R outputs
+    std::vector<std::vector<void*>> recvs;
     uint32_t arrived = 0;
     int left = 0;
     bool done = false;
@@ -58,6 +61,19 @@ struct RankEvents {
     }
 };
 
+// One send/recv pair of the per-rank front end: side 0 is the sender's, side 1
+// the receiver's.
+struct PairSlot {
+    rc_buf bufs[2] = {};
+    bool have[2] = {false, false};
+    bool null_buf = false;
+    void* streams[2] = {nullptr, nullptr};
+    bool done = false;
+    int left = 0;
+    int status = RC_OK;
+    std::string msg;
+};
+
 struct Session {
     Mode mode = Mode::None;
     int nranks = 0;
@@ -70,6 +86,9 @@ struct Session {
     std::vector<uint64_t> seq;
     std::map<uint64_t, std::shared_ptr<Slot>> slots;
     std::shared_ptr<RankEvents> events;
+    // point-to-point: the k-th send from src to dst meets the k-th recv on dst from src
+    std::map<std::pair<int, int>, uint64_t> sends_posted, recvs_posted;
+    std::map<std::tuple<int, int, uint64_t>, std::shared_ptr<struct PairSlot>> pairs;
 };
 
 std::mutex g_mu;
@@ -155,6 +174,10 @@ void close_session() {
 }
 
 Error launch(const Checked& ck, void* stream) {
+    if (runs_as_copies(ck.coll)) {
+        const BatchPlan bp = plan_copies(ck, g_s.cfg, g_s.dev);
+        return bp.total_tiles ? device_launch_batch(bp, stream) : Error{};
+    }
     for (const LaunchPlan& p : plan(ck, g_s.cfg, g_s.dev)) {
         Error e = device_launch(p, stream);
         if (e.code) return e;
@@ -162,29 +185,23 @@ Error launch(const Checked& ck, void* stream) {
     return {};
 }
 
-int collective(Coll coll, const rc_buf* bufs, void* stream) {
-    std::lock_guard<std::mutex> lock(g_mu);
-    if (g_s.mode == Mode::None)
-        return report(Error{RC_ERR_NOT_REGISTERED, "no session: call rc_register first"});
+// Registration checks of the whole-call entry points.
+Error whole_call_session() {
+    if (g_s.mode == Mode::None) return Error{RC_ERR_NOT_REGISTERED, "no session: call rc_register first"};
     if (g_s.mode == Mode::PerRank)
-        return report(Error{RC_ERR_INVALID_ARGUMENT,
-                            "the session was opened per rank: use the rc_rank_* entry points"});
+        return Error{RC_ERR_INVALID_ARGUMENT, "the session was opened per rank: use the rc_rank_* entry points"};
+    return {};
+}
+
+int collective(Coll coll, const rc_buf* bufs, void* stream, void* const* recv_list = nullptr) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    Error reg = whole_call_session();
+    if (reg.code) return report(reg);
     Checked ck;
-    Error e = validate(coll, g_s.nranks, bufs, &ck);
+    Error e = validate(coll, g_s.nranks, bufs, &ck, recv_list);
     if (e.code) return report(e);
     if (g_s.cfg.validate_only) return ok();
     return report(launch(ck, stream));
-}
-
-const char* coll_name(Coll c) {
-    switch (c) {
-        case Coll::AllReduce: return "all_reduce";
-        case Coll::Reduce: return "reduce";
-        case Coll::Broadcast: return "broadcast";
-        case Coll::ReduceScatter: return "reduce_scatter";
-        case Coll::AllGather: return "all_gather";
-    }
-    return "?";
 }
 
 // A validated batch of all-reduces: tensors large enough get launches of
@@ -261,7 +278,10 @@ void complete_slot(Slot& s, void* stream) {
         }
     }
     Error e;
-    if (s.is_params[0]) {
+    if (s.kinds[0] == Coll::Barrier) {
+        // Communicator.barrier: no data, only the stream join
+        if (!g_s.cfg.validate_only) e = launch_joined(s.streams, stream, [] { return Error{}; });
+    } else if (s.is_params[0]) {
         std::vector<const rc_param*> params(R);
         for (int r = 0; r < R; ++r) params[r] = s.params[r].data();
         std::vector<Checked> cks;
@@ -276,8 +296,11 @@ void complete_slot(Slot& s, void* stream) {
                 return;
             }
         }
+        std::vector<void*> recv_list;
+        if (s.kinds[0] == Coll::AllGatherList)
+            for (int r = 0; r < R; ++r) recv_list.insert(recv_list.end(), s.recvs[r].begin(), s.recvs[r].end());
         Checked ck;
-        e = validate(s.kinds[0], R, s.bufs.data(), &ck);
+        e = validate(s.kinds[0], R, s.bufs.data(), &ck, recv_list.empty() ? nullptr : recv_list.data());
         if (!e.code && !g_s.cfg.validate_only)
             e = launch_joined(s.streams, stream, [&] { return launch(ck, stream); });
     }
@@ -292,6 +315,7 @@ struct RankArgs {
     bool params = false;
     int count = 0;
     const rc_param* entries = nullptr;
+    void* const* recvs = nullptr;  // all_gather list form: R outputs
 };
 
 int rank_collective(const RankArgs& a, int rank, void* stream) {
@@ -320,6 +344,7 @@ int rank_collective(const RankArgs& a, int rank, void* stream) {
         sp->is_params.assign(R, 0);
         sp->pcount.assign(R, 0);
         sp->params.assign(R, {});
+        sp->recvs.assign(R, {});
     }
     std::shared_ptr<Slot> s = sp;
     s->kinds[rank] = a.coll;
@@ -339,6 +364,16 @@ int rank_collective(const RankArgs& a, int rank, void* stream) {
     } else if (a.buf) {
         s->bufs[rank] = *a.buf;
         s->have_buf[rank] = 1;
+    } else if (a.coll == Coll::Barrier) {
+        s->have_buf[rank] = 1;  // nothing to describe
+    }
+    if (a.coll == Coll::AllGatherList) {
+        if (a.recvs) {
+            s->recvs[rank].assign(a.recvs, a.recvs + R);
+        } else if (s->status == RC_OK) {
+            s->status = RC_ERR_INVALID_ARGUMENT;
+            s->msg = "rank " + std::to_string(rank) + ": all_gather_list needs its recvs array";
+        }
     }
     s->streams[rank] = stream;
     s->arrived |= bit;
@@ -355,6 +390,63 @@ int rank_collective(const RankArgs& a, int rank, void* stream) {
     g_s.busy_mask &= ~bit;
     const Error e{s->status, s->msg};
     if (++s->left == R) g_s.slots.erase(k);
+    return report(e);
+}
+
+// Communicator.send / recv on logical ranks: pairs are matched per ordered
+// (src, dst) in issue order, independently of the other ranks' calls.  The
+// first side to arrive waits for its peer; the second validates both sides
+// and copies on its stream, joined with the peer's.
+int rank_p2p(bool is_send, int rank, int peer, const rc_buf* buf, void* stream) {
+    std::unique_lock<std::mutex> lock(g_mu);
+    if (g_s.mode != Mode::PerRank)
+        return report(Error{RC_ERR_NOT_REGISTERED, "no per-rank session: call rc_rank_register first"});
+    const int R = g_s.nranks;
+    if (rank < 0 || rank >= R) return report(Error{RC_ERR_INVALID_ARGUMENT, "rank outside [0, num_ranks)"});
+    if (!((g_s.reg_mask >> rank) & 1u) || ((g_s.fin_mask >> rank) & 1u))
+        return report(Error{RC_ERR_NOT_REGISTERED, "rank " + std::to_string(rank) + " is not registered"});
+    if (peer < 0 || peer >= R || peer == rank)
+        return report(Error{RC_ERR_INVALID_ARGUMENT, std::string(is_send ? "send: dst " : "recv: src ") +
+                                                         std::to_string(peer) + " is not another rank"});
+    const uint32_t bit = 1u << rank;
+    if (g_s.busy_mask & bit)
+        return report(Error{RC_ERR_INVALID_ARGUMENT, "rank " + std::to_string(rank) +
+                                                         " already has a call in progress on another thread"});
+    g_s.busy_mask |= bit;
+    const uint64_t gen = g_generation;
+    const int src = is_send ? rank : peer, dst = is_send ? peer : rank;
+    const int side = is_send ? 0 : 1;
+    const uint64_t k = (is_send ? g_s.sends_posted : g_s.recvs_posted)[{src, dst}]++;
+    const auto key = std::make_tuple(src, dst, k);
+    std::shared_ptr<PairSlot>& sp = g_s.pairs[key];
+    if (!sp) sp = std::make_shared<PairSlot>();
+    std::shared_ptr<PairSlot> s = sp;
+    s->have[side] = true;
+    if (buf) s->bufs[side] = *buf;
+    else s->null_buf = true;
+    s->streams[side] = stream;
+    if (s->have[0] && s->have[1]) {
+        Error e;
+        if (s->null_buf) e = Error{RC_ERR_INVALID_ARGUMENT, "send_recv: a side passed a NULL rc_buf"};
+        Checked ck;
+        if (!e.code) e = validate_send_recv(R, src, dst, s->bufs, &ck);
+        if (!e.code && !g_s.cfg.validate_only) {
+            const std::vector<void*> streams = {s->streams[0], s->streams[1]};
+            e = launch_joined(streams, stream, [&] { return launch(ck, stream); });
+        }
+        s->status = e.code;
+        s->msg = e.msg;
+        s->done = true;
+        g_cv.notify_all();
+    } else {
+        g_cv.wait(lock, [&] { return s->done || g_generation != gen; });
+        if (g_generation != gen)
+            return report(Error{RC_ERR_NOT_REGISTERED, "the session was reset or closed while rank " +
+                                                           std::to_string(rank) + " waited"});
+    }
+    g_s.busy_mask &= ~bit;
+    const Error e{s->status, s->msg};
+    if (++s->left == 2) g_s.pairs.erase(key);
     return report(e);
 }
 
@@ -379,6 +471,27 @@ int rc_reduce_scatter(const rc_buf* bufs, void* stream) {
     return collective(Coll::ReduceScatter, bufs, stream);
 }
 int rc_all_gather(const rc_buf* bufs, void* stream) { return collective(Coll::AllGather, bufs, stream); }
+int rc_all_gather_list(const rc_buf* bufs, void* const* recvs, void* stream) {
+    return collective(Coll::AllGatherList, bufs, stream, recvs);
+}
+int rc_all_to_all_single(const rc_buf* bufs, void* stream) { return collective(Coll::AllToAll, bufs, stream); }
+
+int rc_send_recv(int src, int dst, const rc_buf* bufs, void* stream) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    Error e = whole_call_session();
+    if (e.code) return report(e);
+    Checked ck;
+    e = validate_send_recv(g_s.nranks, src, dst, bufs, &ck);
+    if (e.code) return report(e);
+    if (g_s.cfg.validate_only) return ok();
+    return report(launch(ck, stream));
+}
+
+int rc_barrier(void* stream) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    // every rank's work is on the one stream of the calls, already in order
+    return report(whole_call_session());
+}
 
 int rc_all_reduce_many(int num_tensors, const rc_buf* bufs, void* stream) {
     std::lock_guard<std::mutex> lock(g_mu);
@@ -470,6 +583,23 @@ int rc_rank_reduce_scatter(int rank, const rc_buf* buf, void* stream) {
 }
 int rc_rank_all_gather(int rank, const rc_buf* buf, void* stream) {
     return rank_call(Coll::AllGather, rank, buf, stream);
+}
+int rc_rank_all_gather_list(int rank, const rc_buf* buf, void* const* recvs, void* stream) {
+    RankArgs a;
+    a.coll = Coll::AllGatherList;
+    a.buf = buf;
+    a.recvs = recvs;
+    return rank_collective(a, rank, stream);
+}
+int rc_rank_all_to_all_single(int rank, const rc_buf* buf, void* stream) {
+    return rank_call(Coll::AllToAll, rank, buf, stream);
+}
+int rc_rank_send(int rank, const rc_buf* buf, int dst, void* stream) { return rank_p2p(true, rank, dst, buf, stream); }
+int rc_rank_recv(int rank, const rc_buf* buf, int src, void* stream) { return rank_p2p(false, rank, src, buf, stream); }
+int rc_rank_barrier(int rank, void* stream) {
+    RankArgs a;
+    a.coll = Coll::Barrier;
+    return rank_collective(a, rank, stream);
 }
 int rc_rank_all_reduce_params(int rank, int num_params, const rc_param* params, void* stream) {
     RankArgs a;

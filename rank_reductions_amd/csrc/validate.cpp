@@ -29,17 +29,6 @@ bool reduces(Coll c) {
     return c == Coll::AllReduce || c == Coll::Reduce || c == Coll::ReduceScatter;
 }
 
-const char* coll_name(Coll c) {
-    switch (c) {
-        case Coll::AllReduce: return "all_reduce";
-        case Coll::Reduce: return "reduce";
-        case Coll::Broadcast: return "broadcast";
-        case Coll::ReduceScatter: return "reduce_scatter";
-        case Coll::AllGather: return "all_gather";
-    }
-    return "?";
-}
-
 Error count_of(const rc_buf& b, int r, int64_t* count) {
     if (b.ndim < 0 || b.ndim > RC_MAX_DIMS)
         return fail(RC_ERR_INVALID_ARGUMENT, fmt("rank %lld: ndim %lld outside [0, 8]", r, b.ndim));
@@ -147,6 +136,28 @@ void ranges_of(const Checked& ck, int tensor, std::vector<Range>* writes, std::v
                 writes->push_back({at(ck.recv[r]), at(ck.recv[r]) + R * n * b, tag0 + r, 0, r, tensor});
             }
             break;
+        case Coll::AllToAll:  // no in-place layout: chunks move between ranks
+            for (int r = 0; r < R; ++r) {
+                reads->push_back({at(ck.send[r]), at(ck.send[r]) + n * b, -1, 0, r, tensor});
+                writes->push_back({at(ck.recv[r]), at(ck.recv[r]) + n * b, -1, 0, r, tensor});
+            }
+            break;
+        case Coll::AllGatherList:
+            // rank k's output for its own shard may be the shard itself
+            for (int k = 0; k < R; ++k) {
+                reads->push_back({at(ck.send[k]), at(ck.send[k]) + n * b, tag0 + k, 0, k, tensor});
+                for (int r = 0; r < R; ++r) {
+                    const uintptr_t o = at(ck.recv_list[(size_t)r * R + k]);
+                    writes->push_back({o, o + n * b, r == k ? tag0 + k : -1, 0, r, tensor});
+                }
+            }
+            break;
+        case Coll::SendRecv:
+            reads->push_back({at(ck.send[0]), at(ck.send[0]) + n * b, tag0, 0, ck.root, tensor});
+            writes->push_back({at(ck.recv[0]), at(ck.recv[0]) + n * b, tag0, 0, ck.root, tensor});
+            break;
+        case Coll::Barrier:
+            break;
     }
 }
 
@@ -168,7 +179,7 @@ Error validate_fields(Coll coll, int R, const rc_buf* bufs, Checked* ck) {
         const int64_t es = element_size(b.dtype);
         const bool need_send = coll != Coll::Broadcast;
         const bool need_recv = coll == Coll::AllReduce || coll == Coll::ReduceScatter ||
-                               coll == Coll::AllGather;
+                               coll == Coll::AllGather || coll == Coll::AllToAll;
         // zero-element buffers may be NULL (nothing is read or written)
         if (need_send && !b.send && count[r] > 0)
             return fail(RC_ERR_INVALID_ARGUMENT, fmt("rank %lld: send is NULL", r));
@@ -188,9 +199,9 @@ Error validate_fields(Coll coll, int R, const rc_buf* bufs, Checked* ck) {
         for (int d = 0; same && d < bufs[0].ndim; ++d) same = bufs[r].dims[d] == bufs[0].dims[d];
         if (!same) return fail(RC_ERR_SHAPE_MISMATCH, fmt("rank %lld shape differs from rank 0's", r));
     }
-    if (coll == Coll::ReduceScatter && count[0] % R != 0)
+    if ((coll == Coll::ReduceScatter || coll == Coll::AllToAll) && count[0] % R != 0)
         return fail(RC_ERR_SHAPE_MISMATCH,
-                    fmt("reduce_scatter input of %lld elements does not split over %lld ranks", count[0], R));
+                    fmt("input of %lld elements does not split over %lld ranks", count[0], R));
     if (reduces(coll)) {
         for (int r = 1; r < R; ++r)
             if (bufs[r].op != bufs[0].op)
@@ -248,8 +259,40 @@ Error validate_fields(Coll coll, int R, const rc_buf* bufs, Checked* ck) {
 
 int64_t element_size(int /*dtype*/) { return 4; }
 
-Error validate(Coll coll, int R, const rc_buf* bufs, Checked* ck) {
+const char* coll_name(Coll c) {
+    switch (c) {
+        case Coll::AllReduce: return "all_reduce";
+        case Coll::Reduce: return "reduce";
+        case Coll::Broadcast: return "broadcast";
+        case Coll::ReduceScatter: return "reduce_scatter";
+        case Coll::AllGather: return "all_gather";
+        case Coll::AllToAll: return "all_to_all_single";
+        case Coll::AllGatherList: return "all_gather_list";
+        case Coll::SendRecv: return "send_recv";
+        case Coll::Barrier: return "barrier";
+    }
+    return "?";
+}
+
+Error validate(Coll coll, int R, const rc_buf* bufs, Checked* ck, void* const* recv_list) {
     Error e = validate_fields(coll, R, bufs, ck);
+    if (!e.code && coll == Coll::AllGatherList) {
+        // the list form's outputs: R per rank, each a shard's size
+        if (!recv_list) {
+            e = fail(RC_ERR_INVALID_ARGUMENT, "recvs is NULL");
+        } else {
+            ck->recv_list.assign(recv_list, recv_list + (size_t)R * R);
+            for (int i = 0; i < R * R && !e.code; ++i) {
+                void* o = ck->recv_list[i];
+                if (!o && ck->count > 0)
+                    e = fail(RC_ERR_INVALID_ARGUMENT,
+                             fmt("rank %lld: output for rank %lld's shard is NULL", i / R, i % R));
+                else if (o && misaligned(o, element_size(ck->dtype)))
+                    e = fail(RC_ERR_INVALID_ARGUMENT,
+                             fmt("rank %lld: output for rank %lld's shard is misaligned", i / R, i % R));
+            }
+        }
+    }
     if (e.code) {
         std::string prefix = std::string(coll_name(coll)) + ": ";
         e.msg = prefix + e.msg;
@@ -260,6 +303,51 @@ Error validate(Coll coll, int R, const rc_buf* bufs, Checked* ck) {
     ranges_of(*ck, 0, &writes, &reads);
     e = check_overlaps(writes, reads);
     if (e.code) e.msg = std::string(coll_name(coll)) + ": " + e.msg;
+    return e;
+}
+
+// Communicator.send on rank src and recv on rank dst.  The two sides must
+// describe the same dtype and shape; the sender's send and the receiver's
+// recv are required (when non-empty), and they may be the same buffer (then
+// nothing moves) but must not overlap otherwise.
+Error validate_send_recv(int R, int src, int dst, const rc_buf* bufs, Checked* ck) {
+    if (!bufs) return fail(RC_ERR_INVALID_ARGUMENT, "send_recv: bufs is NULL");
+    if (src < 0 || src >= R || dst < 0 || dst >= R)
+        return fail(RC_ERR_INVALID_ARGUMENT, fmt("send_recv: src %lld or dst %lld outside [0, %lld)", src, dst, R));
+    if (src == dst) return fail(RC_ERR_INVALID_ARGUMENT, "send_recv: a rank cannot send to itself");
+    int64_t count[2];
+    for (int i = 0; i < 2; ++i) {
+        const rc_buf& b = bufs[i];
+        const int rank = i ? dst : src;
+        if (b.dtype != RC_F32 && b.dtype != RC_I32)
+            return fail(RC_ERR_INVALID_ARGUMENT, fmt("send_recv: rank %lld: unknown dtype %lld", rank, b.dtype));
+        Error e = count_of(b, rank, &count[i]);
+        if (e.code) return e;
+        const void* p = i ? static_cast<const void*>(b.recv) : b.send;
+        if (!p && count[i] > 0)
+            return fail(RC_ERR_INVALID_ARGUMENT,
+                        fmt(i ? "send_recv: receiver %lld: recv is NULL" : "send_recv: sender %lld: send is NULL", rank));
+        if (p && misaligned(p, element_size(b.dtype)))
+            return fail(RC_ERR_INVALID_ARGUMENT, fmt("send_recv: rank %lld: buffer not aligned", rank));
+    }
+    if (bufs[1].dtype != bufs[0].dtype)
+        return fail(RC_ERR_DTYPE_MISMATCH, fmt("send_recv: receiver %lld dtype differs from sender %lld's", dst, src));
+    bool same = bufs[1].ndim == bufs[0].ndim;
+    for (int d = 0; same && d < bufs[0].ndim; ++d) same = bufs[1].dims[d] == bufs[0].dims[d];
+    if (!same) return fail(RC_ERR_SHAPE_MISMATCH, fmt("send_recv: receiver %lld shape differs from sender %lld's", dst, src));
+    ck->coll = Coll::SendRecv;
+    ck->nranks = 2;
+    ck->dtype = bufs[0].dtype;
+    ck->op = RC_SUM;
+    ck->root = src;
+    ck->count = count[0];
+    ck->send[0] = bufs[0].send;
+    ck->recv[0] = bufs[1].recv;
+    if (ck->count == 0) return {};
+    std::vector<Range> writes, reads;
+    ranges_of(*ck, 0, &writes, &reads);
+    Error e = check_overlaps(writes, reads);
+    if (e.code) e.msg = "send_recv: " + e.msg;
     return e;
 }
 

@@ -108,13 +108,18 @@ void fuzz(int iters, int R) {
             for (int d = 0; d < RC_MAX_DIMS; ++d)
                 b.dims[d] = (rng() % 8 == 0) ? (int64_t)(rng() >> 1) * ((rng() % 2) ? 1 : -1) : (int64_t)(rng() % 70);
         }
+        std::vector<void*> recvs(R * R);
+        for (void*& p : recvs) p = (rng() % 8) ? reinterpret_cast<void*>(rng() & 0xFFFFFFFFFFFull) : nullptr;
         int rc;
-        switch (rng() % 6) {
+        switch (rng() % 9) {
             case 0: rc = rc_all_reduce(bufs.data(), nullptr); break;
             case 1: rc = rc_reduce(bufs.data(), nullptr); break;
             case 2: rc = rc_broadcast(bufs.data(), nullptr); break;
             case 3: rc = rc_reduce_scatter(bufs.data(), nullptr); break;
             case 4: rc = rc_all_gather(bufs.data(), nullptr); break;
+            case 5: rc = rc_all_to_all_single(bufs.data(), nullptr); break;
+            case 6: rc = rc_all_gather_list(bufs.data(), (rng() % 5) ? recvs.data() : nullptr, nullptr); break;
+            case 7: rc = rc_send_recv((int)(rng() % (R + 2)) - 1, (int)(rng() % (R + 2)) - 1, bufs.data(), nullptr); break;
             default: rc = rc_all_reduce_many(3, bufs.data(), nullptr); break;
         }
         if (rc < 0 || rc > RC_ERR_PARAM_MISMATCH) ++g_bad;

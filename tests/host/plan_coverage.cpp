@@ -309,6 +309,86 @@ int main(int argc, char** argv) {
                 }
         ++batches;
     }
-    std::printf("checked %d plans and %d batches: %d failures\n", plans, batches, g_fail);
+    // copy batches: all_to_all_single and the list form of all_gather; every
+    // destination element written exactly once, every access in bounds
+    int copies = 0;
+    for (int it = 0; it < iters / 2; ++it) {
+        g_bufs.clear();
+        const int R = 1 + (int)(rng() % 16);
+        const bool a2a = rng() % 2;
+        int64_t m = (int64_t)(rng() % 3 == 0 ? rng() % 40000 : rng() % 300);
+        const int mis_mode = (int)(rng() % 3);
+        auto mis = [&](int r) { return mis_mode == 0 ? 0 : (mis_mode == 1 ? 1 : (r * 3 + it) % 4); };
+        std::vector<rc_buf> bufs(R);
+        std::vector<void*> recv_list;
+        // destination buffers, with per-element write counts
+        struct Dst {
+            uintptr_t lo;
+            int64_t n;
+            std::vector<uint8_t> hits;
+        };
+        std::vector<Dst> dsts;
+        const int64_t n = a2a ? m * R : m;
+        for (int r = 0; r < R; ++r) {
+            void* s = (void*)alloc(std::max<int64_t>(n, 1) * 4, mis(r));
+            void* o = nullptr;
+            if (a2a) {
+                o = (void*)alloc(std::max<int64_t>(n, 1) * 4, mis(r + 1));
+                dsts.push_back({(uintptr_t)o, n, std::vector<uint8_t>((size_t)n, 0)});
+            }
+            bufs[r] = make(s, o, n);
+        }
+        if (!a2a)
+            for (int i = 0; i < R * R; ++i) {
+                void* o = (void*)alloc(std::max<int64_t>(m, 1) * 4, mis(i + 2));
+                recv_list.push_back(o);
+                dsts.push_back({(uintptr_t)o, m, std::vector<uint8_t>((size_t)m, 0)});
+            }
+        Checked ck;
+        Error e = validate(a2a ? Coll::AllToAll : Coll::AllGatherList, R, bufs.data(), &ck,
+                           a2a ? nullptr : recv_list.data());
+        if (e.code) {
+            fail("copy validation rejected a valid call: " + e.msg);
+            continue;
+        }
+        Config cfg;
+        cfg.waves_per_cu = (int)(rng() % 9);
+        const BatchPlan bp = plan_copies(ck, cfg, dev);
+        const int per_job = 1 + bp.nout;
+        if (ck.count > 0 && (!bp.copy || bp.ptrs.size() != bp.jobs.size() * (size_t)per_job))
+            fail("copy plan has the wrong shape");
+        const int64_t ngroups = (int64_t)bp.group_job.size();
+        for (int64_t t = 0; t < bp.total_tiles; ++t) {
+            const int64_t g = t >> kGroupShift;
+            int lo = bp.group_job[g];
+            int hi = g + 1 < ngroups ? bp.group_job[g + 1] : (int)bp.jobs.size() - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (bp.jobs[mid].tile_begin <= t) lo = mid;
+                else hi = mid - 1;
+            }
+            const BatchJob& jb = bp.jobs[lo];
+            tile_elements(jb.len, jb.phase, t - jb.tile_begin, bp.tile_elems, kCopyUnroll, [&](int64_t el, int bytes) {
+                for (int k = 0; k < per_job; ++k) {
+                    const uintptr_t ad = (uintptr_t)bp.ptrs[(size_t)lo * per_job + k] + (uintptr_t)(el * 4);
+                    if (!inside(ad, bytes)) fail("copy access outside its buffer");
+                    if (bytes == 16 && ad % 16) fail("copy misaligned vector access");
+                    if (k == 0) continue;
+                    for (Dst& d : dsts)
+                        if (ad >= d.lo && ad < d.lo + (uintptr_t)d.n * 4)
+                            for (int i = 0; i < bytes / 4; ++i) d.hits[(ad - d.lo) / 4 + i] += 1;
+                }
+            });
+        }
+        for (const Dst& d : dsts)
+            for (int64_t i = 0; i < d.n; ++i)
+                if (d.hits[i] != 1) {
+                    fail(std::string(a2a ? "all_to_all" : "all_gather_list") + ": destination element written " +
+                         std::to_string(d.hits[i]) + " times");
+                    i = d.n;
+                }
+        ++copies;
+    }
+    std::printf("checked %d plans, %d batches and %d copy batches: %d failures\n", plans, batches, copies, g_fail);
     return g_fail ? 1 : 0;
 }

@@ -1,0 +1,214 @@
+"""The Communicator page's copies on the GPU, bit for bit against the CPU
+oracle: list-form all_gather, all_to_all_single and send/recv from one call
+and from one thread per rank, and barrier ordering between the ranks'
+streams."""
+
+import threading
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rank_reductions_amd as rr
+import synth_inputs as si
+from gpu_util import assert_bits, host, session
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def view_at(n, offset, dtype=torch.float32, fill=None):
+    """A tensor of n elements starting `offset` elements into a fresh buffer
+    (misaligned for offset % 4 != 0)."""
+    base = torch.empty(n + offset + 4, dtype=dtype, device=DEV)
+    t = base[offset:offset + n]
+    if fill is not None:
+        t.copy_(fill)
+    return t
+
+
+def inputs(R, n, dtype, seed, offsets=None):
+    xs = si.torch_rank_inputs(R, n, "i32" if dtype == torch.int32 else "f32", "normal", seed, device=DEV)
+    if offsets:
+        xs = [view_at(n, offsets[r % len(offsets)], dtype, x) for r, x in enumerate(xs)]
+    return xs
+
+
+@pytest.mark.parametrize("R", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("m", [0, 1, 257, 65_537])
+def test_all_gather_list(R, m):
+    xs = inputs(R, m, torch.float32, 200 + R, offsets=[0, 1, 2, 3] if m > 1 else None)
+    with session(R, device=0):
+        out = rr.all_gather_list(xs)
+        torch.cuda.synchronize()
+    want = oracle.all_gather_list([host(x) for x in xs])
+    for r in range(R):
+        for k in range(R):
+            assert_bits(host(out[r][k]), want[r][k], f"R={R} m={m} rank {r} shard {k}")
+
+
+def test_all_gather_list_own_slot_in_place_i32():
+    R = 4
+    m = 10_001
+    xs = inputs(R, m, torch.int32, 211)
+    keep = [host(x).copy() for x in xs]
+    out = [[xs[k] if k == r else torch.empty_like(xs[k]) for k in range(R)] for r in range(R)]
+    with session(R, device=0):
+        rr.all_gather_list(xs, out=out)
+        torch.cuda.synchronize()
+    for r in range(R):
+        for k in range(R):
+            assert_bits(host(out[r][k]), keep[k], f"rank {r} shard {k}")
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 8, 16])
+@pytest.mark.parametrize("m", [0, 1, 3, 257, 40_000])
+def test_all_to_all_single(R, m):
+    n = R * m
+    xs = inputs(R, n, torch.float32, 300 + R, offsets=[0, 3, 1] if n > 1 else None)
+    with session(R, device=0):
+        out = rr.all_to_all_single(xs)
+        torch.cuda.synchronize()
+    want = oracle.all_to_all_single([host(x) for x in xs])
+    for r in range(R):
+        assert_bits(host(out[r]), want[r], f"R={R} m={m} rank {r}")
+
+
+def test_all_to_all_single_2d_i32():
+    R = 4
+    xs = [si.torch_tensor_for(7, 0, R, r, (8, 1000), dtype="i32", device=DEV) for r in range(R)]
+    with session(R, device=0):
+        out = rr.all_to_all_single(xs)
+        torch.cuda.synchronize()
+    want = oracle.all_to_all_single([host(x) for x in xs])
+    for r in range(R):
+        assert out[r].shape == (8, 1000)
+        assert_bits(host(out[r]), want[r], f"rank {r}")
+
+
+@pytest.mark.parametrize("n", [0, 1, 7, 1_000_003])
+def test_send_recv_whole_call(n):
+    R = 4
+    x = inputs(1, n, torch.float32, 400 + n)[0]
+    with session(R, device=0):
+        y = rr.send_recv(x, 3, 1)
+        z = rr.send_recv(x, 0, 2, out=view_at(n, 1))
+        rr.barrier()
+        torch.cuda.synchronize()
+    assert_bits(host(y), oracle.send_recv(host(x)), "send_recv")
+    assert_bits(host(z), oracle.send_recv(host(x)), "send_recv into a misaligned view")
+
+
+# ---------------------------------------------------------------- per rank
+
+def run_ranks(R, body):
+    out = [None] * R
+    errs = []
+
+    def go(r):
+        try:
+            out[r] = body(r)
+        except BaseException as e:  # noqa: BLE001
+            errs.append(e)
+
+    ts = [threading.Thread(target=go, args=(r,)) for r in range(R)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join(timeout=120)
+    assert not errs, errs
+    assert all(not t.is_alive() for t in ts)
+    return out
+
+
+def slow_copy(src):
+    """An exact copy built through a chain of kernels, still running when the
+    next call is issued."""
+    x = src.clone()
+    for _ in range(6):
+        x = (x * 2.0 - x) / 1.0
+    return x
+
+
+@pytest.mark.parametrize("n_streams", [1, 4])
+def test_rank_threads_copies(n_streams):
+    R = 4
+    m = 300_001
+    xs = inputs(R, R * m, torch.float32, 500)
+    shards = inputs(R, m, torch.float32, 501)
+    torch.cuda.synchronize()
+    hx = [host(x) for x in xs]
+    hs = [host(s) for s in shards]
+    pool = [torch.cuda.Stream() for _ in range(n_streams)]
+    for r in range(R):
+        rr.rank_register(r, R, device=0)
+
+    def body(r):
+        s = pool[r % n_streams]
+        res = {}
+        with torch.cuda.stream(s):
+            x = slow_copy(xs[r])
+            res["a2a"] = rr.rank_all_to_all_single(r, x, stream=s).clone()
+            x.mul_(0)
+            sh = slow_copy(shards[r])
+            res["list"] = [o.clone() for o in rr.rank_all_gather_list(r, sh, R, stream=s)]
+            sh.mul_(0)
+            # ring exchange: even ranks send first, odd ranks receive first
+            nxt, prv = (r + 1) % R, (r - 1) % R
+            mine = slow_copy(shards[r])
+            got = torch.empty_like(mine)
+            if r % 2 == 0:
+                rr.rank_send(r, mine, nxt, stream=s)
+                rr.rank_recv(r, got, prv, stream=s)
+            else:
+                rr.rank_recv(r, got, prv, stream=s)
+                rr.rank_send(r, mine, nxt, stream=s)
+            res["p2p"] = got.clone()
+            mine.mul_(0)
+        return res
+
+    try:
+        got = run_ranks(R, body)
+        torch.cuda.synchronize()
+        want_a2a = oracle.all_to_all_single(hx)
+        want_list = oracle.all_gather_list(hs)
+        for r in range(R):
+            assert_bits(host(got[r]["a2a"]), want_a2a[r], f"a2a rank {r}")
+            for k in range(R):
+                assert_bits(host(got[r]["list"][k]), want_list[r][k], f"list rank {r} shard {k}")
+            assert_bits(host(got[r]["p2p"]), oracle.send_recv(hs[(r - 1) % R]), f"p2p rank {r}")
+    finally:
+        for r in range(R):
+            rr.rank_finish(r)
+
+
+def test_rank_barrier_orders_streams():
+    """Each rank fills its slot of a shared buffer on its own stream, then
+    calls the barrier; afterwards every rank copies the whole buffer on its
+    stream.  Only the barrier's stream join orders those reads after the
+    other ranks' fills."""
+    R = 4
+    n = 2_000_000
+    src = inputs(R, n, torch.float32, 600)
+    shared = torch.zeros(R, n, dtype=torch.float32, device=DEV)
+    torch.cuda.synchronize()
+    pool = [torch.cuda.Stream() for _ in range(R)]
+    for r in range(R):
+        rr.rank_register(r, R, device=0)
+
+    def body(r):
+        with torch.cuda.stream(pool[r]):
+            shared[r].copy_(slow_copy(src[r]))
+            rr.rank_barrier(r, stream=pool[r])
+            return shared.clone()
+
+    try:
+        seen = run_ranks(R, body)
+        torch.cuda.synchronize()
+        want = np.stack([host(x) for x in src])
+        for r in range(R):
+            assert_bits(host(seen[r]), want, f"rank {r} after the barrier")
+    finally:
+        for r in range(R):
+            rr.rank_finish(r)
