@@ -247,6 +247,21 @@ def rows(torch, rr, si, dev, xs8, args):
     out["all_reduce_per_rank_threads_r8_64MiB_f32_sum_8_streams"] = per_rank_row(torch, rr, xs8, o, R)
     del o
     rr.register(R, device=0)
+    # the Communicator's copies on the metric workload's buffers
+    log("bench: rows: all_to_all_single, all_gather list form, send/recv")
+    o = [torch.empty_like(x) for x in xs8]
+    us = time_calls(torch, lambda: rr.all_to_all_single(xs8, out=o), 10) * 1e3
+    out["all_to_all_single_r8_64MiB_f32"] = _roof(2 * R * b, us)
+    M = N // R
+    shards = [x[:M] for x in xs8]
+    lst = [[o[r][k * M:(k + 1) * M] for k in range(R)] for r in range(R)]
+    us = time_calls(torch, lambda: rr.all_gather_list(shards, out=lst), 10) * 1e3
+    row = _roof((R + R * R) * M * 4, us)
+    row["shard_MiB"] = M * 4 >> 20
+    out["all_gather_list_r8_8MiB_shards_f32"] = row
+    us = time_calls(torch, lambda: rr.send_recv(xs8[0], 0, 1, out=o[1]), 10) * 1e3
+    out["send_recv_64MiB_f32"] = _roof(2 * b, us)
+    del o, lst, shards
     # reduce_scatter and all_gather, 8 ranks x 256 MiB
     w = si.WORKLOADS["ranks8_256MiB_f32_rs_ag"]
     log("bench: rows: reduce_scatter / all_gather 8 x 256 MiB")

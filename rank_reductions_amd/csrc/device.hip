@@ -1,11 +1,13 @@
 // HIP side of the session: device query, launches on the caller's stream, and
 // the descriptor arena of the batched all-reduce.
 //
-// The arena holds the job and pointer tables of rc_all_reduce_many.  Tables
-// are written into pinned host staging and copied to device memory with one
-// asynchronous copy on the caller's stream, ahead of the kernel.  Two arenas
-// alternate; before one is rewritten the host waits on the event recorded
-// after the last kernel that read it.
+// The arena holds the job and pointer tables of batched launches (the
+// gradient all-reduces, and copy batches too large for kernel arguments).
+// Tables are written into pinned host staging and copied to device memory
+// with one asynchronous copy on the caller's stream, ahead of the kernel.  Two
+// arenas alternate; before one is rewritten the host waits on the event
+// recorded after the last kernel that read it.  Copy batches that fit travel
+// in the kernel arguments instead and need no upload.
 #include <hip/hip_runtime.h>
 
 #include <cstring>
@@ -16,6 +18,7 @@
 namespace rc {
 
 hipError_t launch_jobs(const LaunchPlan& p, hipStream_t stream);
+hipError_t launch_copy_args(const BatchPlan& p, hipStream_t stream);
 hipError_t launch_batch(const BatchJob* jobs, const int32_t* group_job, const void* const* ptrs,
                         const BatchPlan& p, hipStream_t stream);
 
@@ -135,6 +138,11 @@ Error device_launch_batch(const BatchPlan& p, void* stream) {
     if (p.jobs.empty()) return {};
     DeviceGuard guard;
     if (guard.err != hipSuccess) return hip_fail("hipSetDevice", guard.err);
+    if (p.by_value) {
+        const hipError_t e = launch_copy_args(p, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return hip_fail("kernel launch", e);
+        return {};
+    }
     Arena& a = g.arena[g.next];
     Error err = wait_arena(a);
     if (err.code) return err;

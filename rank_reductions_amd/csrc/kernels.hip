@@ -346,6 +346,7 @@ struct BatchArgs {
     int32_t njobs;
     int32_t tile_elems;
     int32_t mean;
+    int32_t grid_2d;  // copies: y = job, x = tile of the job
 };
 
 __device__ __forceinline__ int find_job(const BatchArgs& a, int64_t t) {
@@ -384,17 +385,61 @@ __global__ __launch_bounds__(kBlock) void batch_kernel(BatchArgs a) {
 // Batched copies over a job table (all_to_all_single, the list form of
 // all_gather): job j copies tp[0] to the NR destinations tp[1..NR], bit for bit.
 template <int NR, int U, bool NT>
+__device__ __forceinline__ void copy_job_tile(const BatchArgs& a, int j, int64_t lt) {
+    const BatchJob jb = a.jobs[j];
+    const void* const* tp = a.ptrs + (int64_t)j * (1 + NR);
+    const uint32_t* in[1] = {static_cast<const uint32_t*>(tp[0])};
+    const uint32_t* none[1] = {nullptr};
+    auto out = [&](int o) { return static_cast<uint32_t*>(const_cast<void*>(tp[1 + o])); };
+    job_tile<1, NR, OpSumI32, U, NT, false>(in, none, out, (1u << NR) - 1u, jb.len, jb.phase, lt, a.tile_elems,
+                                            false);
+}
+
+// Tiles of a job of `len` elements with alignment phase `phase` (as planned).
+__device__ __forceinline__ int64_t tiles_of(int64_t len, int phase, int64_t te) {
+    if (phase == kScalarOnly) return (len + te - 1) / te;
+    const int64_t head = phase < len ? phase : len;
+    const int64_t body = ((len - head) / kVec) * kVec;
+    const int64_t t = (body + te - 1) / te;
+    return t > 1 ? t : 1;
+}
+
+template <int NR, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void copy_batch_kernel(BatchArgs a) {
+    if (a.grid_2d) {
+        const int j = blockIdx.y;
+        const BatchJob jb = a.jobs[j];
+        if (blockIdx.x < tiles_of(jb.len, jb.phase, a.tile_elems)) copy_job_tile<NR, U, NT>(a, j, blockIdx.x);
+        return;
+    }
     for (int64_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
         const int j = find_job(a, t);
-        const BatchJob jb = a.jobs[j];
-        const void* const* tp = a.ptrs + (int64_t)j * (1 + NR);
-        const uint32_t* in[1] = {static_cast<const uint32_t*>(tp[0])};
-        const uint32_t* none[1] = {nullptr};
-        auto out = [&](int o) { return static_cast<uint32_t*>(const_cast<void*>(tp[1 + o])); };
-        job_tile<1, NR, OpSumI32, U, NT, false>(in, none, out, (1u << NR) - 1u, jb.len, jb.phase,
-                                                t - jb.tile_begin, a.tile_elems, false);
+        copy_job_tile<NR, U, NT>(a, j, t - a.jobs[j].tile_begin);
     }
+}
+
+// A copy batch whose table travels in the kernel arguments: job j =
+// blockIdx.y copies ptrs[j*(1+NR)] to the next NR pointers; every job has
+// len elements.
+struct CopyArgs {
+    const void* ptrs[kMaxCopyArgPtrs];
+    int64_t len;
+    int32_t tile_elems;
+    int32_t pad;
+    uint8_t phase[kMaxCopyArgJobs];
+};
+
+template <int NR, int U, bool NT>
+__global__ __launch_bounds__(kBlock) void copy_args_kernel(CopyArgs a) {
+    const int j = blockIdx.y;
+    const int phase = a.phase[j];
+    if (blockIdx.x >= tiles_of(a.len, phase, a.tile_elems)) return;
+    const void* const* tp = a.ptrs + j * (1 + NR);
+    const uint32_t* in[1] = {static_cast<const uint32_t*>(tp[0])};
+    const uint32_t* none[1] = {nullptr};
+    auto out = [&](int o) { return static_cast<uint32_t*>(const_cast<void*>(tp[1 + o])); };
+    job_tile<1, NR, OpSumI32, U, NT, false>(in, none, out, (1u << NR) - 1u, a.len, phase, blockIdx.x,
+                                            a.tile_elems, false);
 }
 
 // ---------------------------------------------------------------- dispatch
@@ -518,6 +563,15 @@ struct CopyBatchOf {
     };
 };
 
+using CopyArgsFn = void (*)(CopyArgs);
+template <bool NT>
+struct CopyArgsOf {
+    template <int NR>
+    struct At {
+        static CopyArgsFn get() { return copy_args_kernel<NR, kCopyUnroll, NT>; }
+    };
+};
+
 template <bool NT>
 FoldFn pick_fold_any(int dtype, int op, int nin, bool acc) {
     return acc ? pick_fold_op<NT, true>(dtype, op, nin) : pick_fold_op<NT, false>(dtype, op, nin);
@@ -558,7 +612,27 @@ hipError_t launch_batch(const BatchJob* jobs, const int32_t* group_job, const vo
     a.njobs = (int32_t)p.jobs.size();
     a.tile_elems = p.tile_elems;
     a.mean = p.op == RC_MEAN ? 1 : 0;
-    hipLaunchKernelGGL(fn, dim3(p.grid), dim3(kBlock), p.lds_bytes, stream, a);
+    a.grid_2d = p.grid_2d;
+    hipLaunchKernelGGL(fn, dim3(p.grid, p.grid_y), dim3(kBlock), p.lds_bytes, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_args(const BatchPlan& p, hipStream_t stream) {
+    if (!p.by_value || p.jobs.size() > (size_t)kMaxCopyArgJobs || p.ptrs.size() > (size_t)kMaxCopyArgPtrs)
+        return hipErrorInvalidValue;
+    const bool nt = p.nontemporal != 0;
+    CopyArgsFn fn = nt ? pick_nin<CopyArgsOf<true>::template At, CopyArgsFn>(p.nout)
+                       : pick_nin<CopyArgsOf<false>::template At, CopyArgsFn>(p.nout);
+    if (!fn) return hipErrorInvalidValue;
+    CopyArgs a{};
+    for (size_t i = 0; i < p.ptrs.size(); ++i) a.ptrs[i] = p.ptrs[i];
+    a.len = p.jobs[0].len;
+    a.tile_elems = p.tile_elems;
+    for (size_t j = 0; j < p.jobs.size(); ++j) {
+        if (p.jobs[j].len != a.len) return hipErrorInvalidValue;  // equal lengths only
+        a.phase[j] = (uint8_t)p.jobs[j].phase;
+    }
+    hipLaunchKernelGGL(fn, dim3(p.grid, p.grid_y), dim3(kBlock), p.lds_bytes, stream, a);
     return hipGetLastError();
 }
 

@@ -109,7 +109,7 @@ int auto_waves_per_cu(int nin, int nout, int unroll) {
     // stores are posted and hold the wave only briefly, so they count half
     const double kib_per_wave = ((double)nin + 0.5 * nout) * unroll;
     const long w = std::lround(kInFlightKiBPerCU / std::max(kib_per_wave, 1.0));
-    return (int)std::min<long>(16, std::max<long>(2, w));
+    return (int)std::min<long>(32, std::max<long>(2, w));
 }
 
 void shape_launch(int64_t total_tiles, int nin, int nout, int unroll, const Config& cfg,
@@ -430,6 +430,18 @@ BatchPlan plan_copies(const Checked& ck, const Config& cfg, const DeviceInfo& de
     bp.total_tiles = tiles;
     build_groups(&bp);
     shape_launch(tiles, 1, bp.nout, kCopyUnroll, cfg, dev, &bp.grid, &bp.lds_bytes);
+    if (cfg.max_workgroups <= 0 && !bp.jobs.empty()) {
+        // every job has the same length: a one-shot 2-D grid needs no job lookup
+        int64_t widest = 0;
+        for (size_t j = 0; j < bp.jobs.size(); ++j) {
+            const int64_t next = j + 1 < bp.jobs.size() ? bp.jobs[j + 1].tile_begin : tiles;
+            widest = std::max(widest, next - bp.jobs[j].tile_begin);
+        }
+        bp.grid_2d = 1;
+        bp.grid = std::max<int64_t>(1, widest);
+        bp.grid_y = (int)bp.jobs.size();
+        bp.by_value = bp.jobs.size() <= (size_t)kMaxCopyArgJobs && bp.ptrs.size() <= (size_t)kMaxCopyArgPtrs;
+    }
     return bp;
 }
 

@@ -186,8 +186,17 @@ struct BatchPlan {
     int op = RC_SUM;
     int nontemporal = 1;
     int64_t grid = 0;
+    int grid_y = 1;     // copies of equal-length jobs: y = job, x = tile of the job
+    int grid_2d = 0;
     int lds_bytes = 0;
+    // a copy batch small enough to pass its table in the kernel arguments
+    // (no descriptor upload before the launch)
+    bool by_value = false;
 };
+// Capacity of the by-value copy table: all_to_all_single up to 12 ranks
+// (R*R jobs of 2 pointers) and every list-form all_gather (R jobs of 1+R).
+constexpr int kMaxCopyArgJobs = 256;
+constexpr int kMaxCopyArgPtrs = 288;
 BatchPlan plan_batch(const std::vector<Checked>& tensors, const Config& cfg, const DeviceInfo& dev);
 // The copy jobs of all_to_all_single and of the list form of all_gather.
 BatchPlan plan_copies(const Checked& ck, const Config& cfg, const DeviceInfo& dev);

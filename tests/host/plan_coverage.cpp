@@ -353,22 +353,43 @@ int main(int argc, char** argv) {
         }
         Config cfg;
         cfg.waves_per_cu = (int)(rng() % 9);
+        cfg.max_workgroups = rng() % 3 == 0 ? (int)(1 + rng() % 50) : 0;
+        const int64_t tes[] = {0, 0, 2048, 8192};
+        cfg.tile_elems = tes[rng() % 4];
         const BatchPlan bp = plan_copies(ck, cfg, dev);
         const int per_job = 1 + bp.nout;
         if (ck.count > 0 && (!bp.copy || bp.ptrs.size() != bp.jobs.size() * (size_t)per_job))
             fail("copy plan has the wrong shape");
-        const int64_t ngroups = (int64_t)bp.group_job.size();
-        for (int64_t t = 0; t < bp.total_tiles; ++t) {
-            const int64_t g = t >> kGroupShift;
-            int lo = bp.group_job[g];
-            int hi = g + 1 < ngroups ? bp.group_job[g + 1] : (int)bp.jobs.size() - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (bp.jobs[mid].tile_begin <= t) lo = mid;
-                else hi = mid - 1;
+        // the (job, tile) pairs the launch visits: one-shot 2-D grid (y = job,
+        // tiles past the job's own count exit) or the 1-D group lookup
+        std::vector<std::pair<int, int64_t>> visits;
+        if (bp.grid_2d) {
+            if (bp.grid_y != (int)bp.jobs.size()) fail("copy 2-D grid height is not the job count");
+            for (int j = 0; j < bp.grid_y; ++j) {
+                const BatchJob& jb = bp.jobs[j];
+                const int64_t own = job_tiles(jb.len, (uint8_t)jb.phase, bp.tile_elems);
+                if (own > bp.grid) fail("copy 2-D grid narrower than a job");
+                for (int64_t lt = 0; lt < bp.grid; ++lt)
+                    if (lt < own) visits.push_back({j, lt});
             }
+        } else {
+            const int64_t ngroups = (int64_t)bp.group_job.size();
+            for (int64_t t = 0; t < bp.total_tiles; ++t) {
+                const int64_t g = t >> kGroupShift;
+                int lo = bp.group_job[g];
+                int hi = g + 1 < ngroups ? bp.group_job[g + 1] : (int)bp.jobs.size() - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (bp.jobs[mid].tile_begin <= t) lo = mid;
+                    else hi = mid - 1;
+                }
+                visits.push_back({lo, t - bp.jobs[lo].tile_begin});
+            }
+        }
+        for (const auto& v : visits) {
+            const int lo = v.first;
             const BatchJob& jb = bp.jobs[lo];
-            tile_elements(jb.len, jb.phase, t - jb.tile_begin, bp.tile_elems, kCopyUnroll, [&](int64_t el, int bytes) {
+            tile_elements(jb.len, jb.phase, v.second, bp.tile_elems, kCopyUnroll, [&](int64_t el, int bytes) {
                 for (int k = 0; k < per_job; ++k) {
                     const uintptr_t ad = (uintptr_t)bp.ptrs[(size_t)lo * per_job + k] + (uintptr_t)(el * 4);
                     if (!inside(ad, bytes)) fail("copy access outside its buffer");

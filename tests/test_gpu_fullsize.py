@@ -158,3 +158,33 @@ def test_ranks4_llama32_grads_all_reduce_many():
             del single
     del ts, outs
     free()
+
+
+def test_ranks8_64MiB_copies_as_benchmarked():
+    """all_to_all_single over the metric workload's buffers, the list form of
+    all_gather on 8 MiB shards written into views of 64 MiB outputs, and a
+    64 MiB send/recv: the shapes the benchmark rows time, whole outputs
+    against the oracle."""
+    w = si.WORKLOADS["ranks8_64MiB_f32"]
+    R, N = w["R"], w["N"]
+    xs = si.torch_rank_inputs(R, N, "f32", w["dist"], w["seed"], device=DEV)
+    hx = [host(x).copy() for x in xs]
+    with session(R):
+        o = rr.all_to_all_single(xs)
+        sync()
+        want = oracle.all_to_all_single(hx)
+        for r in range(R):
+            assert_bits(host(o[r]), want[r], f"all_to_all rank {r}")
+        M = N // R
+        shards = [x[:M] for x in xs]
+        lst = [[o[r][k * M:(k + 1) * M] for k in range(R)] for r in range(R)]
+        rr.all_gather_list(shards, out=lst)
+        sync()
+        want_flat = np.concatenate([h[:M] for h in hx])
+        for r in range(R):
+            assert_bits(host(o[r]), want_flat, f"all_gather_list rank {r}")
+        y = rr.send_recv(xs[0], 0, 1, out=o[1])
+        sync()
+        assert_bits(host(y), hx[0], "send_recv")
+    del xs, o
+    free()
