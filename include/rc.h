@@ -355,9 +355,31 @@ int rc_rank_barrier(int rank, void* stream);
  * that rank's parameter map.  The array is read before the call returns. */
 int rc_rank_all_reduce_params(int rank, int num_params, const rc_param* params, void* stream);
 
+/* Communicator.split_all / split_from: a collective on rank's communicator
+ * that makes a new communicator of some of its members.  Each rank that is
+ * to be a member passes the same list of num_members distinct ranks of the
+ * current communicator, in the new communicator's rank order (all ranks, in
+ * order, is split_all); a rank that passes num_members = 0 stays out and
+ * needs not know the list (the page's empty-ranks case).  *new_rank receives
+ * the member's endpoint in the new communicator, or -1 for a rank left out.
+ *
+ * Endpoints.  The rank argument of every rc_rank_* call is an endpoint: a
+ * registered rank's index in [0, num_ranks) addresses the world, and the
+ * endpoints rc_rank_split returns address the new communicators (each is
+ * comm_id * RC_MAX_RANKS + the member's rank in it).  Every collective,
+ * gradient sync, send/recv and barrier works on any communicator, with ranks,
+ * roots and peers counted within it.  A rank calls from one thread at a time
+ * whichever endpoint it uses.
+ * Errors: lists that differ between ranks, a listed rank that passed no
+ * list, members out of range or listed twice, or new_rank NULL:
+ * RC_ERR_INVALID_ARGUMENT for every rank. */
+int rc_rank_split(int rank, int num_members, const int* members, int* new_rank);
+
 /* finish_collective<B> for one peer: the rank leaves the session.  When the
  * last registered rank has finished, the session waits for the GPU, frees its
- * scratch and closes.  RC_ERR_NOT_REGISTERED for a rank not registered. */
+ * scratch and closes.  On a split-off communicator's endpoint it leaves that
+ * communicator, which is dropped once all its members have left.
+ * RC_ERR_NOT_REGISTERED for a rank not registered. */
 int rc_rank_finish(int rank);
 
 /* Text for the last failure on the calling thread (valid until that thread's

@@ -34,7 +34,7 @@ __all__ = [
     "all_reduce_params", "rank_register", "rank_finish", "rank_all_reduce", "rank_reduce",
     "rank_broadcast", "rank_reduce_scatter", "rank_all_gather", "rank_all_reduce_params",
     "all_gather_list", "all_to_all_single", "send_recv", "barrier", "rank_all_gather_list",
-    "rank_all_to_all_single", "rank_send", "rank_recv", "rank_barrier",
+    "rank_all_to_all_single", "rank_send", "rank_recv", "rank_barrier", "rank_split", "rank_split_all",
 ]
 
 RC_MAX_RANKS = 16
@@ -170,6 +170,8 @@ def library():
         getattr(lib, name).restype = ctypes.c_int
     lib.rc_rank_barrier.argtypes = [ctypes.c_int, ctypes.c_void_p]
     lib.rc_rank_barrier.restype = ctypes.c_int
+    lib.rc_rank_split.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(ctypes.c_int)]
+    lib.rc_rank_split.restype = ctypes.c_int
     lib.rc_rank_finish.argtypes = [ctypes.c_int]
     lib.rc_rank_finish.restype = ctypes.c_int
     _lib = lib
@@ -528,8 +530,9 @@ def rank_all_reduce(rank, x, op="sum", out=None, stream=None):
 
 
 def rank_reduce(rank, x, root, op="sum", out=None, stream=None):
+    """root counts within rank's communicator (an endpoint's low part)."""
     torch = _torch()
-    if out is None and rank == root:
+    if out is None and int(rank) % RC_MAX_RANKS == root:
         out = torch.empty_like(x)
     _rank_call(library().rc_rank_reduce, rank, x, out, _op(op), root, stream)
     return out
@@ -612,3 +615,20 @@ def rank_barrier(rank, stream=None):
     else:
         s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     check(library().rc_rank_barrier(int(rank), ctypes.c_void_p(s)))
+
+
+def rank_split(rank, members):
+    """Communicator.split_from for logical rank `rank` (an endpoint): members
+    lists the ranks of rank's communicator that form the new one, in order;
+    a rank that passes an empty list stays out.  Returns the rank's endpoint
+    in the new communicator, or None when it is not a member."""
+    members = [int(m) for m in members]
+    arr = (ctypes.c_int * max(len(members), 1))(*members)
+    out = ctypes.c_int(-1)
+    check(library().rc_rank_split(int(rank), len(members), arr, ctypes.byref(out)))
+    return out.value if out.value >= 0 else None
+
+
+def rank_split_all(rank, size):
+    """Communicator.split_all: a new communicator of the same `size` ranks."""
+    return rank_split(rank, range(size))

@@ -30,18 +30,27 @@ namespace {
 
 enum class Mode { None, Whole, PerRank };
 
+// What a per-rank call is: one of the collectives (its Coll kind), a gradient
+// sync, or a communicator split.
+enum Form : uint8_t { kCollective = 0, kParams = 1, kSplit = 2 };
+
 // One collective of the per-rank front end, filled in as ranks arrive.
 struct Slot {
     std::vector<Coll> kinds;
     std::vector<rc_buf> bufs;
     std::vector<uint8_t> have_buf;
     std::vector<void*> streams;
+    std::vector<uint8_t> form;  // per rank: kCollective, kParams or kSplit
     // gradient sync (all_reduce_params): each rank's entries
-    std::vector<uint8_t> is_params;
     std::vector<int> pcount;
     std::vector<std::vector<rc_param>> params;
     // all_gather, list form: each rank's R outputs
     std::vector<std::vector<void*>> recvs;
+    // split: each rank's member list (has_list 0: the rank gave none) and,
+    // once matched, its endpoint in the new communicator or -1
+    std::vector<uint8_t> has_list;
+    std::vector<std::vector<int>> members;
+    std::vector<int> result;
     uint32_t arrived = 0;
     int left = 0;
     bool done = false;
@@ -74,21 +83,33 @@ struct PairSlot {
     std::string msg;
 };
 
+// A communicator of the per-rank front end: the registered world (id 0), or
+// one split off another (the Communicator page's split_all and split_from).
+// A member is addressed by its endpoint, id * RC_MAX_RANKS + its rank in the
+// communicator, so the world's endpoints are its rank indices.
+struct Comm {
+    std::vector<int> world;     // world rank of each member, in communicator rank order
+    uint32_t fin_mask = 0;      // members that have finished
+    std::vector<uint64_t> seq;  // calls issued per member
+    std::map<uint64_t, std::shared_ptr<Slot>> slots;
+    // point-to-point: the k-th send from src to dst meets the k-th recv on dst from src
+    std::map<std::pair<int, int>, uint64_t> sends_posted, recvs_posted;
+    std::map<std::tuple<int, int, uint64_t>, std::shared_ptr<PairSlot>> pairs;
+    int size() const { return (int)world.size(); }
+};
+
 struct Session {
     Mode mode = Mode::None;
     int nranks = 0;
     Config cfg;
     DeviceInfo dev;
     // per-rank front end
-    uint32_t reg_mask = 0;
-    uint32_t fin_mask = 0;
-    uint32_t busy_mask = 0;  // ranks with a call in progress
-    std::vector<uint64_t> seq;
-    std::map<uint64_t, std::shared_ptr<Slot>> slots;
+    uint32_t reg_mask = 0;   // world ranks registered
+    uint32_t fin_mask = 0;   // world ranks finished
+    uint32_t busy_mask = 0;  // world ranks with a call in progress
+    std::map<int, Comm> comms;
+    int next_comm = 1;
     std::shared_ptr<RankEvents> events;
-    // point-to-point: the k-th send from src to dst meets the k-th recv on dst from src
-    std::map<std::pair<int, int>, uint64_t> sends_posted, recvs_posted;
-    std::map<std::tuple<int, int, uint64_t>, std::shared_ptr<struct PairSlot>> pairs;
 };
 
 std::mutex g_mu;
@@ -161,7 +182,11 @@ Error open_session(Mode mode, int num_ranks, const rc_config* cfg) {
     g_s.nranks = num_ranks;
     g_s.cfg = c;
     g_s.dev = dev;
-    g_s.seq.assign(num_ranks, 0);
+    if (mode == Mode::PerRank) {
+        Comm& world = g_s.comms[0];
+        for (int r = 0; r < num_ranks; ++r) world.world.push_back(r);
+        world.seq.assign(num_ranks, 0);
+    }
     g_s.events = std::move(events);
     return {};
 }
@@ -251,7 +276,9 @@ Error launch_joined(const std::vector<void*>& streams, void* stream, Enqueue enq
 }
 
 const char* kind_name(const Slot& s, int r) {
-    return s.is_params[r] ? "all_reduce_params" : coll_name(s.kinds[r]);
+    if (s.form[r] == kParams) return "all_reduce_params";
+    if (s.form[r] == kSplit) return "split";
+    return coll_name(s.kinds[r]);
 }
 
 // Pairs a gradient sync's entries by parameter ID and validates the batch.
@@ -265,12 +292,47 @@ Error check_params(int R, const std::vector<int>& counts, const std::vector<cons
     return validate_batch(R, (int)order.size(), bufs.data(), cks, order.data(), accs.data());
 }
 
+// Communicator.split_all / split_from: the members named by the ranks that
+// pass a list form a new communicator in that order; ranks that pass none are
+// left out (the page's empty-list case) and get -1.  Every rank that passes a
+// list must pass the same one, and every listed rank must pass it.
+Error complete_split(Slot& s, const Comm& parent) {
+    const int R = parent.size();
+    int first = -1;
+    for (int r = 0; r < R; ++r)
+        if (s.has_list[r]) {
+            if (first < 0) first = r;
+            else if (s.members[r] != s.members[first])
+                return Error{RC_ERR_INVALID_ARGUMENT, "split: ranks " + std::to_string(first) + " and " +
+                                                          std::to_string(r) + " pass different member lists"};
+        }
+    s.result.assign(R, -1);
+    if (first < 0) return {};  // nobody named a member: no communicator
+    const std::vector<int>& list = s.members[first];
+    std::vector<uint8_t> seen(R, 0);
+    for (int m : list) {
+        if (m < 0 || m >= R) return Error{RC_ERR_INVALID_ARGUMENT, "split: member " + std::to_string(m) + " outside the communicator"};
+        if (seen[m]++) return Error{RC_ERR_INVALID_ARGUMENT, "split: member " + std::to_string(m) + " listed twice"};
+        if (!s.has_list[m])
+            return Error{RC_ERR_INVALID_ARGUMENT, "split: rank " + std::to_string(m) + " is listed but passed no list"};
+    }
+    if (g_s.next_comm >= (1 << 26)) return Error{RC_ERR_INVALID_ARGUMENT, "split: too many communicators"};
+    const int id = g_s.next_comm++;
+    Comm& c = g_s.comms[id];
+    for (size_t i = 0; i < list.size(); ++i) {
+        c.world.push_back(parent.world[list[i]]);
+        s.result[list[i]] = id * RC_MAX_RANKS + (int)i;
+    }
+    c.seq.assign(list.size(), 0);
+    return {};
+}
+
 // The last rank of a slot: check the R sides against each other and launch.
-void complete_slot(Slot& s, void* stream) {
+void complete_slot(Slot& s, const Comm& cm, void* stream) {
     if (s.status != RC_OK) return;  // an argument error recorded at arrival
-    const int R = g_s.nranks;
+    const int R = cm.size();
     for (int r = 1; r < R; ++r) {
-        if (s.kinds[r] != s.kinds[0] || s.is_params[r] != s.is_params[0]) {
+        if (s.kinds[r] != s.kinds[0] || s.form[r] != s.form[0]) {
             s.status = RC_ERR_OP_MISMATCH;
             s.msg = std::string("rank ") + std::to_string(r) + " called " + kind_name(s, r) +
                     " where rank 0 called " + kind_name(s, 0);
@@ -278,10 +340,12 @@ void complete_slot(Slot& s, void* stream) {
         }
     }
     Error e;
-    if (s.kinds[0] == Coll::Barrier) {
+    if (s.form[0] == kSplit) {
+        e = complete_split(s, cm);
+    } else if (s.kinds[0] == Coll::Barrier && s.form[0] == kCollective) {
         // Communicator.barrier: no data, only the stream join
         if (!g_s.cfg.validate_only) e = launch_joined(s.streams, stream, [] { return Error{}; });
-    } else if (s.is_params[0]) {
+    } else if (s.form[0] == kParams) {
         std::vector<const rc_param*> params(R);
         for (int r = 0; r < R; ++r) params[r] = s.params[r].data();
         std::vector<Checked> cks;
@@ -304,62 +368,100 @@ void complete_slot(Slot& s, void* stream) {
         if (!e.code && !g_s.cfg.validate_only)
             e = launch_joined(s.streams, stream, [&] { return launch(ck, stream); });
     }
+    if (e.code) s.result.assign(R, -1);
     s.status = e.code;
     s.msg = e.msg;
 }
 
-// One rank's side of a collective (params == nullptr) or of a gradient sync.
+// One rank's side of a per-rank call.
 struct RankArgs {
     Coll coll = Coll::AllReduce;
+    Form form = kCollective;
     const rc_buf* buf = nullptr;
-    bool params = false;
-    int count = 0;
+    int count = 0;                     // all_reduce_params entries, or split members
     const rc_param* entries = nullptr;
-    void* const* recvs = nullptr;  // all_gather list form: R outputs
+    const int* members = nullptr;
+    bool missing_out = false;          // split without a place for its result
+    void* const* recvs = nullptr;      // all_gather list form: R outputs
 };
 
-int rank_collective(const RankArgs& a, int rank, void* stream) {
-    std::unique_lock<std::mutex> lock(g_mu);
+// Resolves an endpoint of the per-rank front end (the caller holds g_mu).
+Error resolve(int ep, int* id, int* local, int* world) {
     if (g_s.mode != Mode::PerRank)
-        return report(Error{RC_ERR_NOT_REGISTERED, "no per-rank session: call rc_rank_register first"});
-    const int R = g_s.nranks;
-    if (rank < 0 || rank >= R)
-        return report(Error{RC_ERR_INVALID_ARGUMENT, "rank outside [0, num_ranks)"});
-    if (!((g_s.reg_mask >> rank) & 1u) || ((g_s.fin_mask >> rank) & 1u))
-        return report(Error{RC_ERR_NOT_REGISTERED, "rank " + std::to_string(rank) + " is not registered"});
-    const uint32_t bit = 1u << rank;
+        return Error{RC_ERR_NOT_REGISTERED, "no per-rank session: call rc_rank_register first"};
+    if (ep < 0) return Error{RC_ERR_INVALID_ARGUMENT, "rank outside [0, num_ranks)"};
+    *id = ep / RC_MAX_RANKS;
+    *local = ep % RC_MAX_RANKS;
+    auto it = g_s.comms.find(*id);
+    if (it == g_s.comms.end() || *local >= it->second.size()) {
+        if (*id == 0) return Error{RC_ERR_INVALID_ARGUMENT, "rank outside [0, num_ranks)"};
+        return Error{RC_ERR_NOT_REGISTERED, "endpoint " + std::to_string(ep) + " names no communicator"};
+    }
+    *world = it->second.world[*local];
+    if (!((g_s.reg_mask >> *world) & 1u) || ((g_s.fin_mask >> *world) & 1u) ||
+        ((it->second.fin_mask >> *local) & 1u))
+        return Error{RC_ERR_NOT_REGISTERED, "rank " + std::to_string(ep) + " is not registered"};
+    return {};
+}
+
+Error claim(int world) {
+    const uint32_t bit = 1u << world;
     if (g_s.busy_mask & bit)
-        return report(Error{RC_ERR_INVALID_ARGUMENT, "rank " + std::to_string(rank) +
-                                                         " already has a call in progress on another thread"});
+        return Error{RC_ERR_INVALID_ARGUMENT,
+                     "rank " + std::to_string(world) + " already has a call in progress on another thread"};
     g_s.busy_mask |= bit;
+    return {};
+}
+
+int rank_collective(const RankArgs& a, int ep, void* stream, int* split_result = nullptr) {
+    std::unique_lock<std::mutex> lock(g_mu);
+    int id = 0, rank = 0, world = 0;
+    Error e0 = resolve(ep, &id, &rank, &world);
+    if (!e0.code) e0 = claim(world);
+    if (e0.code) return report(e0);
+    Comm& cm = g_s.comms[id];
+    const int R = cm.size();
     const uint64_t gen = g_generation;
-    const uint64_t k = g_s.seq[rank]++;
-    std::shared_ptr<Slot>& sp = g_s.slots[k];
+    const uint64_t k = cm.seq[rank]++;
+    std::shared_ptr<Slot>& sp = cm.slots[k];
     if (!sp) {
         sp = std::make_shared<Slot>();
         sp->kinds.assign(R, Coll::AllReduce);
         sp->bufs.assign(R, rc_buf{});
         sp->have_buf.assign(R, 0);
         sp->streams.assign(R, nullptr);
-        sp->is_params.assign(R, 0);
+        sp->form.assign(R, kCollective);
         sp->pcount.assign(R, 0);
         sp->params.assign(R, {});
         sp->recvs.assign(R, {});
+        sp->has_list.assign(R, 0);
+        sp->members.assign(R, {});
     }
     std::shared_ptr<Slot> s = sp;
     s->kinds[rank] = a.coll;
-    s->is_params[rank] = a.params;
-    if (a.params) {
+    s->form[rank] = a.form;
+    auto arg_error = [&](const std::string& msg) {
+        if (s->status == RC_OK) {
+            s->status = RC_ERR_INVALID_ARGUMENT;
+            s->msg = "rank " + std::to_string(rank) + ": " + msg;
+        }
+    };
+    if (a.form == kParams) {
         // copied now: the caller's arrays need only live through the call
         if (a.count < 0 || (a.count > 0 && !a.entries)) {
-            if (s->status == RC_OK) {
-                s->status = RC_ERR_INVALID_ARGUMENT;
-                s->msg = "rank " + std::to_string(rank) +
-                         ": all_reduce_params needs num_params >= 0 and a non-NULL params array";
-            }
+            arg_error("all_reduce_params needs num_params >= 0 and a non-NULL params array");
         } else {
             s->pcount[rank] = a.count;
             s->params[rank].assign(a.entries, a.entries + a.count);
+        }
+    } else if (a.form == kSplit) {
+        if (a.missing_out) {
+            arg_error("split needs somewhere to return the new rank");
+        } else if (a.count < 0 || (a.count > 0 && !a.members)) {
+            arg_error("split needs num_members >= 0 and a non-NULL members array");
+        } else if (a.count > 0) {
+            s->has_list[rank] = 1;
+            s->members[rank].assign(a.members, a.members + a.count);
         }
     } else if (a.buf) {
         s->bufs[rank] = *a.buf;
@@ -367,58 +469,53 @@ int rank_collective(const RankArgs& a, int rank, void* stream) {
     } else if (a.coll == Coll::Barrier) {
         s->have_buf[rank] = 1;  // nothing to describe
     }
-    if (a.coll == Coll::AllGatherList) {
-        if (a.recvs) {
-            s->recvs[rank].assign(a.recvs, a.recvs + R);
-        } else if (s->status == RC_OK) {
-            s->status = RC_ERR_INVALID_ARGUMENT;
-            s->msg = "rank " + std::to_string(rank) + ": all_gather_list needs its recvs array";
-        }
+    if (a.form == kCollective && a.coll == Coll::AllGatherList) {
+        if (a.recvs) s->recvs[rank].assign(a.recvs, a.recvs + R);
+        else arg_error("all_gather_list needs its recvs array");
     }
     s->streams[rank] = stream;
-    s->arrived |= bit;
+    s->arrived |= 1u << rank;
     if (s->arrived == (uint32_t)((1ull << R) - 1)) {
-        complete_slot(*s, stream);
+        complete_slot(*s, cm, stream);
         s->done = true;
         g_cv.notify_all();
     } else {
         g_cv.wait(lock, [&] { return s->done || g_generation != gen; });
         if (g_generation != gen)
             return report(Error{RC_ERR_NOT_REGISTERED, "the session was reset or closed while rank " +
-                                                           std::to_string(rank) + " waited"});
+                                                           std::to_string(ep) + " waited"});
     }
-    g_s.busy_mask &= ~bit;
+    g_s.busy_mask &= ~(1u << world);
     const Error e{s->status, s->msg};
-    if (++s->left == R) g_s.slots.erase(k);
+    if (split_result) *split_result = s->result.empty() ? -1 : s->result[rank];
+    // the communicator outlives every call in progress on it (a member cannot
+    // finish while it is inside a call), so cm is still valid here
+    if (++s->left == R) cm.slots.erase(k);
     return report(e);
 }
 
 // Communicator.send / recv on logical ranks: pairs are matched per ordered
-// (src, dst) in issue order, independently of the other ranks' calls.  The
-// first side to arrive waits for its peer; the second validates both sides
-// and copies on its stream, joined with the peer's.
-int rank_p2p(bool is_send, int rank, int peer, const rc_buf* buf, void* stream) {
+// (src, dst) of one communicator in issue order, independently of the other
+// ranks' calls.  The first side to arrive waits for its peer; the second
+// validates both sides and copies on its stream, joined with the peer's.
+int rank_p2p(bool is_send, int ep, int peer, const rc_buf* buf, void* stream) {
     std::unique_lock<std::mutex> lock(g_mu);
-    if (g_s.mode != Mode::PerRank)
-        return report(Error{RC_ERR_NOT_REGISTERED, "no per-rank session: call rc_rank_register first"});
-    const int R = g_s.nranks;
-    if (rank < 0 || rank >= R) return report(Error{RC_ERR_INVALID_ARGUMENT, "rank outside [0, num_ranks)"});
-    if (!((g_s.reg_mask >> rank) & 1u) || ((g_s.fin_mask >> rank) & 1u))
-        return report(Error{RC_ERR_NOT_REGISTERED, "rank " + std::to_string(rank) + " is not registered"});
+    int id = 0, rank = 0, world = 0;
+    Error e0 = resolve(ep, &id, &rank, &world);
+    if (e0.code) return report(e0);
+    Comm& cm = g_s.comms[id];
+    const int R = cm.size();
     if (peer < 0 || peer >= R || peer == rank)
         return report(Error{RC_ERR_INVALID_ARGUMENT, std::string(is_send ? "send: dst " : "recv: src ") +
                                                          std::to_string(peer) + " is not another rank"});
-    const uint32_t bit = 1u << rank;
-    if (g_s.busy_mask & bit)
-        return report(Error{RC_ERR_INVALID_ARGUMENT, "rank " + std::to_string(rank) +
-                                                         " already has a call in progress on another thread"});
-    g_s.busy_mask |= bit;
+    e0 = claim(world);
+    if (e0.code) return report(e0);
     const uint64_t gen = g_generation;
     const int src = is_send ? rank : peer, dst = is_send ? peer : rank;
     const int side = is_send ? 0 : 1;
-    const uint64_t k = (is_send ? g_s.sends_posted : g_s.recvs_posted)[{src, dst}]++;
+    const uint64_t k = (is_send ? cm.sends_posted : cm.recvs_posted)[{src, dst}]++;
     const auto key = std::make_tuple(src, dst, k);
-    std::shared_ptr<PairSlot>& sp = g_s.pairs[key];
+    std::shared_ptr<PairSlot>& sp = cm.pairs[key];
     if (!sp) sp = std::make_shared<PairSlot>();
     std::shared_ptr<PairSlot> s = sp;
     s->have[side] = true;
@@ -442,11 +539,11 @@ int rank_p2p(bool is_send, int rank, int peer, const rc_buf* buf, void* stream) 
         g_cv.wait(lock, [&] { return s->done || g_generation != gen; });
         if (g_generation != gen)
             return report(Error{RC_ERR_NOT_REGISTERED, "the session was reset or closed while rank " +
-                                                           std::to_string(rank) + " waited"});
+                                                           std::to_string(ep) + " waited"});
     }
-    g_s.busy_mask &= ~bit;
+    g_s.busy_mask &= ~(1u << world);
     const Error e{s->status, s->msg};
-    if (++s->left == 2) g_s.pairs.erase(key);
+    if (++s->left == 2) cm.pairs.erase(key);
     return report(e);
 }
 
@@ -603,18 +700,37 @@ int rc_rank_barrier(int rank, void* stream) {
 }
 int rc_rank_all_reduce_params(int rank, int num_params, const rc_param* params, void* stream) {
     RankArgs a;
-    a.params = true;
+    a.form = kParams;
     a.count = num_params;
     a.entries = params;
     return rank_collective(a, rank, stream);
 }
 
+int rc_rank_split(int rank, int num_members, const int* members, int* new_rank) {
+    RankArgs a;
+    a.form = kSplit;
+    a.count = num_members;
+    a.members = members;
+    a.missing_out = new_rank == nullptr;
+    int result = -1;
+    const int rc = rank_collective(a, rank, nullptr, &result);
+    if (new_rank) *new_rank = rc == RC_OK ? result : -1;
+    return rc;
+}
+
 int rc_rank_finish(int rank) {
     std::lock_guard<std::mutex> lock(g_mu);
-    if (g_s.mode != Mode::PerRank || rank < 0 || rank >= g_s.nranks || !((g_s.reg_mask >> rank) & 1u) ||
-        ((g_s.fin_mask >> rank) & 1u))
+    int id = 0, local = 0, world = 0;
+    if (resolve(rank, &id, &local, &world).code)
         return report(Error{RC_ERR_NOT_REGISTERED, "rc_rank_finish: rank is not registered"});
-    g_s.fin_mask |= 1u << rank;
+    if (id != 0) {
+        // a split-off communicator goes away when all its members have finished
+        Comm& c = g_s.comms[id];
+        c.fin_mask |= 1u << local;
+        if (c.fin_mask == (uint32_t)((1ull << c.size()) - 1)) g_s.comms.erase(id);
+        return ok();
+    }
+    g_s.fin_mask |= 1u << world;
     if (g_s.fin_mask != g_s.reg_mask) return ok();
     Error e;
     if (!g_s.cfg.validate_only) e = device_finish();

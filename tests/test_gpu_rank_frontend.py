@@ -150,3 +150,50 @@ def test_rank_mismatch_on_gpu_launches_nothing():
     finally:
         for r in range(R):
             rr.rank_finish(r)
+
+
+def test_split_groups_reduce_in_their_own_rank_order():
+    """Eight rank threads split into two communicators (world ranks 0,2,4,6
+    and 7,5,3,1, in those orders); each group all-reduces its members'
+    tensors concurrently with the other, folding in the group's own ring
+    order, and reduces to its rank 1."""
+    R = 8
+    N = 1_000_003
+    xs = si.torch_rank_inputs(R, N, "f32", "normal", 90, device=DEV)
+    torch.cuda.synchronize()
+    hx = [host(x) for x in xs]
+    groups = [[0, 2, 4, 6], [7, 5, 3, 1]]
+    streams = [torch.cuda.Stream() for _ in range(R)]
+    for r in range(R):
+        rr.rank_register(r, R, device=0)
+
+    def body(r):
+        g = 0 if r % 2 == 0 else 1
+        eps = [rr.rank_split(r, groups[i] if i == g else []) for i in range(2)]
+        ep = eps[g]
+        assert eps[1 - g] is None
+        s = streams[r]
+        with torch.cuda.stream(s):
+            out = rr.rank_all_reduce(ep, xs[r], "sum", stream=s).clone()
+            red = rr.rank_reduce(ep, xs[r], 1, "mean", stream=s)
+            red = red.clone() if red is not None else None
+        rr.rank_finish(ep)
+        return g, out, red
+
+    try:
+        got = run_ranks(R, body)
+        torch.cuda.synchronize()
+        for g, members in enumerate(groups):
+            gx = [hx[w] for w in members]
+            want = oracle.all_reduce_closed_form(gx, "sum")
+            want_mean = oracle.reduce(gx, 1, "mean")[1]
+            for i, w in enumerate(members):
+                assert got[w][0] == g
+                assert_bits(host(got[w][1]), want, f"group {g} world rank {w}")
+                if i == 1:
+                    assert_bits(host(got[w][2]), want_mean, f"group {g} reduce at its rank 1")
+                else:
+                    assert got[w][2] is None
+    finally:
+        for r in range(R):
+            rr.rank_finish(r)
