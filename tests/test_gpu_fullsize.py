@@ -188,3 +188,51 @@ def test_ranks8_64MiB_copies_as_benchmarked():
         assert_bits(host(y), hx[0], "send_recv")
     del xs, o
     free()
+
+
+def test_beyond_2pow31_elements():
+    """Buffers of more than 2^31 elements: all_reduce of 3 ranks x
+    2,147,483,649 fp32 (8 GiB each; ring segments of 715,827,883 elements,
+    whose starts sit 0, 12 and 8 bytes past a 16-byte boundary), and an
+    int32 all_gather of 5 shards into outputs of 2,684,354,575 elements.
+    Sampled elements, every segment's ends included, against the oracle."""
+    R = 3
+    N = 3 * 715_827_883
+    assert N > 2 ** 31
+    xs = si.torch_rank_inputs(R, N, "f32", "normal", 77, device=DEV)
+    with session(R):
+        outs = rr.all_reduce(xs, "sum")
+        sync()
+        idx = sample_indices(N, R, k=20000, seed=5)
+        # the elements on both sides of 2^31 (N - 1 == 2^31 is the last one)
+        idx = np.unique(np.concatenate([idx, np.array([2 ** 31 - 2, 2 ** 31 - 1, 2 ** 31])]))
+        assert idx.min() >= 0 and idx.max() <= N - 1
+        it = torch.from_numpy(idx).to(DEV)
+        vals = np.stack([host(x[it]) for x in xs])
+        want = oracle.all_reduce_at_many(vals, idx, N, "sum")
+        for r in range(R):
+            assert_bits(host(outs[r][it]), want, f"all_reduce > 2^31 rank {r}")
+    del xs, outs
+    free()
+
+    R = 5
+    M = 2 ** 29 + 3
+    shards = si.torch_rank_inputs(R, M, "i32", "int", 78, device=DEV)
+    with session(R):
+        outs = rr.all_gather(shards)
+        sync()
+        rng = np.random.default_rng(6)
+        idx = np.unique(np.concatenate([rng.integers(0, R * M, 20000),
+                                        np.array([k * M + d for k in range(R) for d in (0, 1, M - 1)])]))
+        assert idx.min() >= 0 and idx.max() <= R * M - 1
+        it = torch.from_numpy(idx).to(DEV)
+        src = torch.from_numpy(idx // M).to(DEV)
+        off = torch.from_numpy(idx % M).to(DEV)
+        want = torch.stack(shards)[src, off]  # shard k's element j, gathered on the GPU
+        for r in range(R):
+            assert torch.equal(outs[r][it], want), f"all_gather > 2^31 rank {r}"
+        # and the host sees the same: shard values at those offsets
+        hw = np.array([host(shards[k][j:j + 1])[0] for k, j in zip((idx // M)[:50], (idx % M)[:50])])
+        assert_bits(host(outs[0][it[:50]]), hw, "all_gather > 2^31 (host check)")
+    del shards, outs
+    free()
