@@ -723,6 +723,8 @@ int rc_rank_finish(int rank) {
     int id = 0, local = 0, world = 0;
     if (resolve(rank, &id, &local, &world).code)
         return report(Error{RC_ERR_NOT_REGISTERED, "rc_rank_finish: rank is not registered"});
+    if ((g_s.busy_mask >> world) & 1u)  // a call of this rank is still waiting on another thread
+        return report(Error{RC_ERR_INVALID_ARGUMENT, "rc_rank_finish: the rank has a call in progress"});
     if (id != 0) {
         // a split-off communicator goes away when all its members have finished
         Comm& c = g_s.comms[id];

@@ -159,10 +159,62 @@ void rank_session(int R, int iters) {
     for (auto& t : ts) t.join();
 }
 
+// Communicator splits under threads: the six ranks split into two groups of
+// three over and over, run collectives, a send/recv ring and a barrier inside
+// their group, and leave it.
+void group_thread(int rank, int rounds) {
+    const int evens[3] = {0, 2, 4}, odds[3] = {5, 3, 1};
+    const int parity = rank % 2;
+    const uintptr_t base = 0x400000000ull + (uintptr_t)rank * 0x1000000ull;
+    for (int it = 0; it < rounds; ++it) {
+        int ep_even = -2, ep_odd = -2;
+        if (rc_rank_split(rank, parity ? 0 : 3, evens, &ep_even) != RC_OK) ++g_bad;
+        if (rc_rank_split(rank, parity ? 3 : 0, odds, &ep_odd) != RC_OK) ++g_bad;
+        const int ep = parity ? ep_odd : ep_even;
+        if (ep < RC_MAX_RANKS || (parity ? ep_even : ep_odd) != -1) {
+            ++g_bad;
+            return;
+        }
+        const int local = ep % RC_MAX_RANKS, size = 3;
+        for (int j = 0; j < 12; ++j) {
+            rc_buf b = buf(base, base + 0x800000ull, 1 + (j * 131) % 3000);
+            if (rc_rank_all_reduce(ep, &b, nullptr) != RC_OK) ++g_bad;
+        }
+        rc_buf s = buf(base, 0, 64), d = buf(0, base + 0x800000ull, 64);
+        const int nxt = (local + 1) % size, prv = (local + size - 1) % size;
+        int a, c;
+        if (local % 2 == 0) {
+            a = rc_rank_send(ep, &s, nxt, nullptr);
+            c = rc_rank_recv(ep, &d, prv, nullptr);
+        } else {
+            c = rc_rank_recv(ep, &d, prv, nullptr);
+            a = rc_rank_send(ep, &s, nxt, nullptr);
+        }
+        if (a != RC_OK || c != RC_OK) ++g_bad;
+        if (rc_rank_barrier(ep, nullptr) != RC_OK) ++g_bad;
+        if (rc_rank_finish(ep) != RC_OK) ++g_bad;
+    }
+    if (rc_rank_finish(rank) != RC_OK) ++g_bad;
+}
+
+void group_session(int rounds) {
+    rc_config cfg;
+    std::memset(&cfg, 0, sizeof cfg);
+    cfg.struct_size = sizeof cfg;
+    cfg.device = -1;
+    cfg.validate_only = 1;
+    for (int r = 0; r < 6; ++r)
+        if (rc_rank_register(r, 6, &cfg) != RC_OK) ++g_bad;
+    std::vector<std::thread> ts;
+    for (int r = 0; r < 6; ++r) ts.emplace_back(group_thread, r, rounds);
+    for (auto& t : ts) t.join();
+}
+
 }  // namespace
 
 int main() {
     rank_session(6, 3000);
+    group_session(200);
     const int R = 8;
     rc_config cfg;
     std::memset(&cfg, 0, sizeof cfg);

@@ -185,6 +185,27 @@ def test_second_call_of_a_busy_rank_is_refused(lib):
     assert res == [rr.RC_OK] * R
 
 
+def test_finish_refused_while_the_rank_waits(lib):
+    R = 2
+    for r in range(R):
+        assert lib.rc_rank_register(r, R, ctypes.byref(cfg())) == rr.RC_OK
+    first = {}
+
+    def rank0():
+        b = one(send_addr(0), recv_addr(0))
+        first["rc"] = lib.rc_rank_all_reduce(0, ctypes.cast(b, ctypes.c_void_p), None)
+
+    t = threading.Thread(target=rank0)
+    t.start()
+    time.sleep(0.2)
+    assert lib.rc_rank_finish(0) == rr.RC_ERR_INVALID_ARGUMENT
+    b = one(send_addr(1), recv_addr(1))
+    assert lib.rc_rank_all_reduce(1, ctypes.cast(b, ctypes.c_void_p), None) == rr.RC_OK
+    t.join(timeout=30)
+    assert first["rc"] == rr.RC_OK
+    assert lib.rc_rank_finish(0) == rr.RC_OK
+
+
 def test_single_rank_does_not_wait(lib):
     assert lib.rc_rank_register(0, 1, ctypes.byref(cfg())) == rr.RC_OK
     b = one(send_addr(0), recv_addr(0))
