@@ -379,7 +379,8 @@ int rc_rank_split(int rank, int num_members, const int* members, int* new_rank);
  * last registered rank has finished, the session waits for the GPU, frees its
  * scratch and closes.  On a split-off communicator's endpoint it leaves that
  * communicator, which is dropped once all its members have left.
- * RC_ERR_NOT_REGISTERED for a rank not registered. */
+ * RC_ERR_NOT_REGISTERED for a rank not registered; RC_ERR_INVALID_ARGUMENT
+ * while the rank still has a call in progress on another thread. */
 int rc_rank_finish(int rank);
 
 /* Text for the last failure on the calling thread (valid until that thread's
