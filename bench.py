@@ -140,8 +140,9 @@ def main():
     all_reduce = lib.rc_all_reduce
 
     def step():
-        if all_reduce(p_sum, stream) or all_reduce(p_mean, stream):
-            raise rr.CollectiveError(1, lib.rc_last_error().decode())
+        rc = all_reduce(p_sum, stream) or all_reduce(p_mean, stream)
+        if rc:
+            raise rr.CollectiveError(rc, lib.rc_last_error().decode())
 
     for _ in range(args.warmup):
         step()
@@ -230,11 +231,57 @@ def _roof(bytes_moved, us):
     return {"us": round(us, 2), "hbm_GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
 
 
+def small_latency(torch, rr, si, dev, calls=200):
+    """The pages' own example size (4 ranks x 257 fp32): launch-bound, so
+    microseconds per call, device-side (HIP events over back-to-back calls)
+    and host-side (time to issue one call through the C ABI)."""
+    import ctypes
+
+    w = si.WORKLOADS["ranks4_257_f32"]
+    R, n = w["R"], w["N"]
+    xs = si.torch_rank_inputs(R, n, "f32", w["dist"], w["seed"], device=dev)
+    outs = [torch.empty_like(x) for x in xs]
+    lib = rr.library()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    s_ptr = [x.data_ptr() for x in xs]
+    o_ptr = [o.data_ptr() for o in outs]
+    calls_of = {
+        "all_reduce_sum": (lib.rc_all_reduce, rr.make_bufs(s_ptr, o_ptr, (n,), rr.RC_F32, rr.RC_SUM)),
+        "all_reduce_mean": (lib.rc_all_reduce, rr.make_bufs(s_ptr, o_ptr, (n,), rr.RC_F32, rr.RC_MEAN)),
+        "reduce_sum_to_0": (lib.rc_reduce, rr.make_bufs(s_ptr, [o_ptr[0], None, None, None], (n,), rr.RC_F32,
+                                                       rr.RC_SUM, 0)),
+        "broadcast_from_1": (lib.rc_broadcast, rr.make_bufs([None, s_ptr[1], None, None],
+                                                            [o_ptr[0], None, o_ptr[2], o_ptr[3]], (n,),
+                                                            rr.RC_F32, rr.RC_SUM, 1)),
+    }
+    rr.register(R, device=0)
+    res = {}
+    for name, (fn, bufs) in calls_of.items():
+        p = ctypes.cast(bufs, ctypes.c_void_p)
+
+        def call():
+            rc = fn(p, stream)
+            if rc:
+                raise rr.CollectiveError(rc, lib.rc_last_error().decode())
+
+        dev_us = time_calls(torch, call, calls, warmup=10) * 1e3
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(calls):
+            call()
+        host_us = (time.perf_counter() - t0) / calls * 1e6
+        torch.cuda.synchronize()
+        res[name] = {"us_per_call": round(dev_us, 2), "host_issue_us": round(host_us, 2)}
+    rr.finish()
+    return res
+
+
 def rows(torch, rr, si, dev, xs8, args):
     """Every other collective at its workload's size (context, not the metric)."""
     out = {}
     R, N = len(xs8), xs8[0].numel()
     b = N * 4
+    out["latency_r4_257_f32"] = small_latency(torch, rr, si, dev)
     # ring all-reduce on the metric workload
     rr.register(R, device=0, algo="ring")
     o = [torch.empty_like(x) for x in xs8]
@@ -380,8 +427,9 @@ def per_rank_row(torch, rr, xs, outs, n_streams, calls=100):
             if k == calls:  # an untimed pass, then the timed one
                 warmed.wait()
                 go.wait()
-            if lib.rc_rank_all_reduce(r, p, s):
-                bad.append(lib.rc_last_error().decode())
+            rc = lib.rc_rank_all_reduce(r, p, s)
+            if rc:
+                bad.append((rc, lib.rc_last_error().decode()))
                 warmed.abort()
                 go.abort()
                 return
@@ -405,7 +453,7 @@ def per_rank_row(torch, rr, xs, outs, n_streams, calls=100):
     for r in range(R):
         rr.rank_finish(r)
     if bad:
-        raise rr.CollectiveError(1, bad[0])
+        raise rr.CollectiveError(*bad[0])
     row = _roof(2 * R * N * 4, wall / calls * 1e6)
     row.update({"calls": calls, "threads": R, "streams": n_streams,
                 "matches_ring_bits": all(torch.equal(ref, o) for o in outs),
