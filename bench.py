@@ -375,9 +375,13 @@ def rows(torch, rr, si, dev, xs8, args):
     # gradient accumulation: the last microbatch added to the accumulators
     # inside the sync (one pass) against a separate elementwise add and then
     # the sync (two passes); both give the same bits
+    # (results go in place into the accumulators' storage, so the full
+    # 32-layer list needs only gradients plus accumulators: 211 GB)
     log("bench: rows: accumulated gradient sync, fused and separate")
+    del outs, os_
+    torch.cuda.empty_cache()
     accs = [{t: torch.empty_like(ts[t][r]).normal_(0.0, 1e-3) for t in range(len(shapes))} for r in range(R4)]
-    us = time_calls(torch, lambda: rr.all_reduce_params(grads, "mean", out=outs, acc=accs), 3, warmup=1) * 1e3
+    us = time_calls(torch, lambda: rr.all_reduce_params(grads, "mean", out=accs, acc=accs), 3, warmup=1) * 1e3
     row = _roof(3 * R4 * elems * 4, us)
     row.update({"tensors": len(shapes), "elems_per_rank": elems,
                 "bytes": "read acc and grad, write the output: 3*R*N*4"})
@@ -387,7 +391,7 @@ def rows(torch, rr, si, dev, xs8, args):
         for r in range(R4):
             for t in range(len(shapes)):
                 accs[r][t].add_(grads[r][t])
-        rr.all_reduce_params(accs, "mean", out=outs)
+        rr.all_reduce_params(accs, "mean", out=accs)
 
     us = time_calls(torch, separate, 3, warmup=1) * 1e3
     row = _roof(5 * R4 * elems * 4, us)
@@ -395,7 +399,7 @@ def rows(torch, rr, si, dev, xs8, args):
                 "bytes": "torch add (2 reads, 1 write) then the sync (1 read, 1 write): 5*R*N*4"})
     out[f"accumulate_then_sync_r4_{layers}layer_grads_f32_mean"] = row
     rr.finish()
-    del ts, os_, grads, outs, accs
+    del ts, grads, accs
     torch.cuda.empty_cache()
     return out
 
