@@ -41,8 +41,10 @@
  *   out of range; BROADCAST_SENDERS; INVALID_ARGUMENT for overlapping buffers.
  *
  * Threads.  The library keeps one process-wide session behind a mutex; calls
- * from several threads are serialised.  The caller orders calls on its
- * streams (the Communicator page leaves issue order to the user).
+ * from several threads are serialised.  A per-rank call blocks its thread,
+ * without holding the mutex, until its peers' matching calls arrive.  The
+ * caller orders whole-call collectives on its streams (the Communicator page
+ * leaves issue order to the user).
  */
 #ifndef RANKRED_RC_H
 #define RANKRED_RC_H
