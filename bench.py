@@ -128,7 +128,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the logical ranks all live in one GPU's HBM, and "
-              f"this build has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+              f"the library has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
     import torch
