@@ -40,6 +40,16 @@
  *   dtype lacks (int32 Mean); ROOT_MISMATCH and INVALID_ARGUMENT for a root
  *   out of range; BROADCAST_SENDERS; INVALID_ARGUMENT for overlapping buffers.
  *
+ * Graphs.  Single collectives (all_reduce, reduce, broadcast, reduce_scatter,
+ * all_gather, send/recv) and the copy batches of all_to_all_single and the
+ * list-form all_gather (up to 12 and 16 ranks) enqueue nothing but kernels,
+ * so they can be captured into a HIP graph and replayed.  Batched all-reduces
+ * (rc_all_reduce_many, rc_all_reduce_params) with tensors under 64 MiB of
+ * traffic, and copy batches beyond those sizes, upload descriptor tables
+ * from reused host staging; on a capturing stream they return
+ * RC_ERR_INVALID_ARGUMENT before enqueuing anything.  Per-rank calls join
+ * several streams and are not meant for capture.
+ *
  * Threads.  The library keeps one process-wide session behind a mutex; calls
  * from several threads are serialised.  A per-rank call blocks its thread,
  * without holding the mutex, until its peers' matching calls arrive.  The

@@ -218,4 +218,12 @@ Error device_stream_wait(void* stream, void* ev) {
     return {};
 }
 
+Error device_stream_capturing(void* stream, bool* capturing) {
+    hipStreamCaptureStatus status = hipStreamCaptureStatusNone;
+    hipError_t st = hipStreamIsCapturing(static_cast<hipStream_t>(stream), &status);
+    if (st != hipSuccess) return hip_fail("hipStreamIsCapturing", st);
+    *capturing = status != hipStreamCaptureStatusNone;
+    return {};
+}
+
 }  // namespace rc

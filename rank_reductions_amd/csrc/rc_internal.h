@@ -234,5 +234,7 @@ Error device_event_create(void** ev);
 void device_event_destroy(void* ev);
 Error device_event_record(void* ev, void* stream);
 Error device_stream_wait(void* stream, void* ev);
+// Whether work enqueued on `stream` is being captured into a graph.
+Error device_stream_capturing(void* stream, bool* capturing);
 
 }  // namespace rc

@@ -201,7 +201,16 @@ void close_session() {
 Error launch(const Checked& ck, void* stream) {
     if (runs_as_copies(ck.coll)) {
         const BatchPlan bp = plan_copies(ck, g_s.cfg, g_s.dev);
-        return bp.total_tiles ? device_launch_batch(bp, stream) : Error{};
+        if (!bp.total_tiles) return {};
+        if (!bp.by_value) {  // tables through the arena: not capturable (see launch_batch)
+            bool capturing = false;
+            Error e = device_stream_capturing(stream, &capturing);
+            if (e.code) return e;
+            if (capturing)
+                return Error{RC_ERR_INVALID_ARGUMENT, std::string(coll_name(ck.coll)) +
+                                                          " with this many ranks cannot be captured into a graph"};
+        }
+        return device_launch_batch(bp, stream);
     }
     for (const LaunchPlan& p : plan(ck, g_s.cfg, g_s.dev)) {
         Error e = device_launch(p, stream);
@@ -235,6 +244,18 @@ int collective(Coll coll, const rc_buf* bufs, void* stream, void* const* recv_li
 Error launch_batch(const std::vector<Checked>& cks, void* stream) {
     std::vector<Checked> own, batched;
     split_batch(cks, &own, &batched);
+    if (!batched.empty()) {
+        // the batched launch uploads its tables from host staging that later
+        // calls reuse, so a graph replay would read stale tables: refuse
+        // capture before anything is enqueued
+        bool capturing = false;
+        Error e = device_stream_capturing(stream, &capturing);
+        if (e.code) return e;
+        if (capturing)
+            return Error{RC_ERR_INVALID_ARGUMENT,
+                         "the batched all-reduce cannot be captured into a graph (its descriptor tables are "
+                         "uploaded from reused host staging); tensors of 64 MiB and more can be"};
+    }
     for (const Checked& ck : own) {
         Error e = launch(ck, stream);
         if (e.code) return e;

@@ -1,0 +1,76 @@
+"""Collectives captured into a HIP graph (torch.cuda.CUDAGraph) and replayed:
+single collectives and copy batches whose tables travel in the kernel
+arguments enqueue nothing but kernels, so every replay recomputes from the
+current inputs.  Each replay follows eager work that rewrites the inputs and
+a synchronisation, and is checked against the CPU oracle.  The batched
+all-reduce, whose tables come from reused host staging, refuses capture
+before enqueuing anything."""
+
+import pytest
+import torch
+
+import oracle
+import rank_reductions_amd as rr
+import synth_inputs as si
+from gpu_util import assert_bits, host, session
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def test_replays_follow_the_inputs():
+    R = 4
+    M = 250_007
+    N = R * M
+    xs = si.torch_rank_inputs(R, N, "f32", "normal", 700, device=DEV)
+    sums = [torch.empty_like(x) for x in xs]
+    shards = [torch.empty(M, device=DEV) for _ in range(R)]
+    swapped = [torch.empty_like(x) for x in xs]
+    with session(R, device=0):
+        # warm up outside the capture (first launches load code objects)
+        rr.all_reduce(xs, "sum", out=sums)
+        rr.reduce_scatter(xs, "max", out=shards)
+        rr.all_to_all_single(xs, out=swapped)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            rr.all_reduce(xs, "sum", out=sums)
+            rr.reduce_scatter(xs, "max", out=shards)
+            rr.all_to_all_single(xs, out=swapped)
+        for rep in range(4):
+            fresh = si.torch_rank_inputs(R, N, "f32", "normal", 710 + rep, device=DEV)
+            for x, f in zip(xs, fresh):
+                x.copy_(f)  # eager work between replays
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            hx = [host(x) for x in xs]
+            want = oracle.all_reduce_closed_form(hx, "sum")
+            want_rs = oracle.reduce_scatter(hx, "max")
+            want_a2a = oracle.all_to_all_single(hx)
+            for r in range(R):
+                assert_bits(host(sums[r]), want, f"replay {rep} all_reduce rank {r}")
+                assert_bits(host(shards[r]), want_rs[r], f"replay {rep} reduce_scatter rank {r}")
+                assert_bits(host(swapped[r]), want_a2a[r], f"replay {rep} all_to_all rank {r}")
+
+
+def test_batched_all_reduce_refuses_capture():
+    R = 2
+    ts = [[si.torch_tensor_for(9, t, R, r, (1000 + t,), device=DEV) for r in range(R)] for t in range(3)]
+    outs = [[torch.empty_like(x) for x in per] for per in ts]
+    with session(R, device=0):
+        rr.all_reduce_many(ts, "mean", out=outs)  # fine outside a capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with pytest.raises(rr.CollectiveError) as ei:
+            with torch.cuda.graph(g):
+                rr.all_reduce_many(ts, "mean", out=outs)
+        assert ei.value.code == rr.RC_ERR_INVALID_ARGUMENT
+        assert "graph" in str(ei.value)
+        torch.cuda.synchronize()
+        # the session and the stream are still usable
+        got = rr.all_reduce_many(ts, "mean")
+        torch.cuda.synchronize()
+        for t in range(3):
+            want = oracle.all_reduce_closed_form([host(x) for x in ts[t]], "mean")
+            assert_bits(host(got[t][0]), want, f"tensor {t} after the refused capture")
