@@ -35,6 +35,7 @@ __all__ = [
     "rank_broadcast", "rank_reduce_scatter", "rank_all_gather", "rank_all_reduce_params",
     "all_gather_list", "all_to_all_single", "send_recv", "barrier", "rank_all_gather_list",
     "rank_all_to_all_single", "rank_send", "rank_recv", "rank_barrier", "rank_split", "rank_split_all",
+    "Communicator",
 ]
 
 RC_MAX_RANKS = 16
@@ -632,3 +633,85 @@ def rank_split(rank, members):
 def rank_split_all(rank, size):
     """Communicator.split_all: a new communicator of the same `size` ranks."""
     return rank_split(rank, range(size))
+
+
+class Communicator:
+    """One logical rank's communicator, with the method set of the monarch
+    `Struct Communicator` page: created once per rank (from that rank's own
+    thread), collectives in place on that rank's tensor, a stream per call,
+    split_all / split_from for sub-communicators.  Argument marshalling over
+    the rank_* functions; errors raise CollectiveError."""
+
+    def __init__(self, rank, world_size, device=None, **cfg):
+        rank_register(rank, world_size, device, **cfg)
+        self._ep, self._size = int(rank), int(world_size)
+
+    @classmethod
+    def _from_endpoint(cls, endpoint, size):
+        c = cls.__new__(cls)
+        c._ep, c._size = endpoint, size
+        return c
+
+    @property
+    def rank(self):
+        """This rank's index within the communicator."""
+        return self._ep % RC_MAX_RANKS
+
+    @property
+    def world_size(self):
+        return self._size
+
+    def split_all(self):
+        """A new communicator of the same ranks (collective over this one)."""
+        return Communicator._from_endpoint(rank_split_all(self._ep, self._size), self._size)
+
+    def split_from(self, ranks):
+        """A new communicator of `ranks` (in that order); None for a rank left
+        out, which may pass an empty list."""
+        ranks = list(ranks)
+        ep = rank_split(self._ep, ranks)
+        return None if ep is None else Communicator._from_endpoint(ep, len(ranks))
+
+    def all_reduce(self, tensor, op="sum", stream=None):
+        """Reduce across all ranks, the result in place on every rank."""
+        rank_all_reduce(self._ep, tensor, op, out=tensor, stream=stream)
+
+    def broadcast(self, tensor, root, stream=None):
+        """The root's tensor to every other rank's tensor."""
+        if self.rank == root:
+            rank_broadcast(self._ep, tensor, None, stream=stream, root=root)
+        else:
+            rank_broadcast(self._ep, None, tensor, stream=stream, root=root)
+
+    def reduce(self, tensor, op, root, stream=None):
+        """Reduce across all ranks into the root's tensor (in place)."""
+        rank_reduce(self._ep, tensor, root, op, out=tensor if self.rank == root else None, stream=stream)
+
+    def all_gather(self, output_tensors, input_tensor, stream=None):
+        """Every rank's input into this rank's list of outputs, one per rank."""
+        rank_all_gather_list(self._ep, input_tensor, self._size, out=list(output_tensors), stream=stream)
+
+    def all_gather_into_tensor(self, output, input, stream=None):
+        rank_all_gather(self._ep, input, self._size, out=output, stream=stream)
+
+    def reduce_scatter_tensor(self, output, input, op="sum", stream=None):
+        rank_reduce_scatter(self._ep, input, self._size, op, out=output, stream=stream)
+
+    def send(self, tensor, dst, stream=None):
+        rank_send(self._ep, tensor, dst, stream=stream)
+
+    def recv(self, tensor, src, stream=None):
+        rank_recv(self._ep, tensor, src, stream=stream)
+
+    def all_to_all_single(self, output, input, stream=None):
+        rank_all_to_all_single(self._ep, input, out=output, stream=stream)
+
+    def barrier(self, stream=None):
+        rank_barrier(self._ep, stream=stream)
+
+    def all_reduce_params(self, grads, op="mean", out=None, stream=None, acc=None):
+        """The gradient sync keyed by parameter ID for this rank's map."""
+        return rank_all_reduce_params(self._ep, grads, op, out=out, stream=stream, acc=acc)
+
+    def finish(self):
+        rank_finish(self._ep)
