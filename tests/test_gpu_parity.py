@@ -421,3 +421,32 @@ def test_lifecycle_on_gpu():
     assert rr.reset() == rr.RC_OK
     rr.register(2)
     rr.finish()
+
+
+@pytest.mark.parametrize("shape", [(), (0,), (2, 3, 4), (1, 2, 1, 3, 1, 2, 1, 5), (3, 0, 7)])
+def test_shapes_are_flattened(shape):
+    """Scalars, empty shapes, and up to 8 dimensions: every collective works on
+    the flattened elements in row-major order, so the bits equal those of the
+    same data as 1-D tensors."""
+    R = 3
+    n = int(np.prod(shape)) if shape else 1
+    xs = [si.torch_tensor_for(11, 0, R, r, shape, device=DEV) for r in range(R)]
+    hx = [host(x) for x in xs]
+    with session(R):
+        ar = rr.all_reduce(xs, "sum")
+        ag = rr.all_gather(xs)
+        red = rr.reduce(xs, 2, "mean")
+        torch.cuda.synchronize()
+    want = oracle.all_reduce_closed_form([h.reshape(-1) for h in hx], "sum").reshape(shape)
+    for r in range(R):
+        assert ar[r].shape == torch.Size(shape)
+        assert_bits(host(ar[r]), want, f"{shape} all_reduce rank {r}")
+        assert_bits(host(ag[r]), np.concatenate([h.reshape(-1) for h in hx]), f"{shape} all_gather rank {r}")
+    assert_bits(host(red[2]), oracle.reduce([h.reshape(-1) for h in hx], 2, "mean")[2], f"{shape} reduce")
+    if n % R == 0:
+        with session(R):
+            rs = rr.reduce_scatter(xs, "max")
+            torch.cuda.synchronize()
+        want_rs = oracle.reduce_scatter([h.reshape(-1) for h in hx], "max")
+        for r in range(R):
+            assert_bits(host(rs[r]), want_rs[r], f"{shape} reduce_scatter rank {r}")
