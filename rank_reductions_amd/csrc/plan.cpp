@@ -12,8 +12,8 @@
 // launches use a 2-D grid (x: tile of the job, y: job), dispatched in order, so
 // the tiles in flight form one compact window of each rank's buffers.  How
 // many waves a CU holds at once is capped through an LDS reservation: on
-// MI355X, HBM efficiency for these many-stream patterns peaks at about 96 KiB
-// of load traffic per CU in flight, counting stores at half weight; more
+// MI355X, HBM efficiency for these many-stream patterns peaks at about 110 KiB
+// of load traffic per CU in flight, counting a store as 0.65 of a load; more
 // waves open more DRAM rows at once and lose bandwidth, fewer leave it idle.
 #include <algorithm>
 #include <cmath>
@@ -103,18 +103,17 @@ int64_t job_tiles(int64_t len, uint8_t phase, int64_t te) {
     return std::max<int64_t>(1, (body + te - 1) / te);
 }
 
-int auto_waves_per_cu(int nin, int nout, int unroll, double kib_in_flight) {
+int auto_waves_per_cu(int nin, int nout, int unroll, const InFlightRule& rule) {
     // each wave moves (nin + nout) * unroll KiB per round (64 lanes x 16 B);
-    // stores are posted and hold the wave only briefly, so they count half
-    const double kib_per_wave = ((double)nin + 0.5 * nout) * unroll;
-    const long w = std::lround(kib_in_flight / std::max(kib_per_wave, 1.0));
+    // stores are posted and hold the wave only part of the time
+    const double kib_per_wave = ((double)nin + rule.store_weight * nout) * unroll;
+    const long w = std::lround(rule.kib / std::max(kib_per_wave, 1.0));
     return (int)std::min<long>(32, std::max<long>(2, w));
 }
 
 void shape_launch(int64_t total_tiles, int nin, int nout, int unroll, const Config& cfg,
-                  const DeviceInfo& dev, int64_t* grid, int* lds_bytes, double kib_in_flight) {
-    const int waves =
-        cfg.waves_per_cu > 0 ? cfg.waves_per_cu : auto_waves_per_cu(nin, nout, unroll, kib_in_flight);
+                  const DeviceInfo& dev, int64_t* grid, int* lds_bytes, const InFlightRule& rule) {
+    const int waves = cfg.waves_per_cu > 0 ? cfg.waves_per_cu : auto_waves_per_cu(nin, nout, unroll, rule);
     // One workgroup is one wave; reserving lds_per_cu / waves bytes of LDS per
     // workgroup lets at most `waves` of them sit on a CU at a time.
     int64_t lds = 0;
@@ -431,7 +430,7 @@ BatchPlan plan_copies(const Checked& ck, const Config& cfg, const DeviceInfo& de
     build_groups(&bp);
     // measured: the batched copies peak at less traffic in flight than the
     // single-collective kernels (all_to_all and the list all_gather alike)
-    shape_launch(tiles, 1, bp.nout, kCopyUnroll, cfg, dev, &bp.grid, &bp.lds_bytes, kInFlightKiBPerCUCopy);
+    shape_launch(tiles, 1, bp.nout, kCopyUnroll, cfg, dev, &bp.grid, &bp.lds_bytes, kCopyBatchRule);
     if (cfg.max_workgroups <= 0 && !bp.jobs.empty()) {
         // every job has the same length: a one-shot 2-D grid needs no job lookup
         int64_t widest = 0;

@@ -212,15 +212,20 @@ void split_batch(const std::vector<Checked>& tensors, std::vector<Checked>* own,
                  std::vector<Checked>* batched);
 
 // Workgroups resident per CU that keep HBM busiest for a kernel streaming
-// `nin` inputs and `nout` outputs per element with `unroll` vectors per lane,
-// aiming at `kib_in_flight` KiB of traffic in flight per CU.
-constexpr double kInFlightKiBPerCU = 96.0;      // folds and single-collective copies
-constexpr double kInFlightKiBPerCUCopy = 60.0;  // batched copies (by-value table)
-int auto_waves_per_cu(int nin, int nout, int unroll, double kib_in_flight = kInFlightKiBPerCU);
+// `nin` inputs and `nout` outputs per element with `unroll` vectors per lane:
+// the rule aims at `kib` KiB of traffic in flight per CU, a store counting
+// `store_weight` of a load.
+struct InFlightRule {
+    double kib;
+    double store_weight;
+};
+constexpr InFlightRule kFoldRule{110.0, 0.65};     // folds and single-collective copies
+constexpr InFlightRule kCopyBatchRule{60.0, 0.5};  // batched copies (by-value table)
+int auto_waves_per_cu(int nin, int nout, int unroll, const InFlightRule& rule = kFoldRule);
 // Grid and LDS reservation of a launch of `total_tiles` tiles.
 void shape_launch(int64_t total_tiles, int nin, int nout, int unroll, const Config& cfg,
                   const DeviceInfo& dev, int64_t* grid, int* lds_bytes,
-                  double kib_in_flight = kInFlightKiBPerCU);
+                  const InFlightRule& rule = kFoldRule);
 
 // ---------------------------------------------------------------- device.hip
 // All return RC_OK or RC_ERR_DEVICE with a message.
