@@ -390,7 +390,12 @@ int rc_rank_split(int rank, int num_members, const int* members, int* new_rank);
 /* finish_collective<B> for one peer: the rank leaves the session.  When the
  * last registered rank has finished, the session waits for the GPU, frees its
  * scratch and closes.  On a split-off communicator's endpoint it leaves that
- * communicator, which is dropped once all its members have left.
+ * communicator, which is dropped once all its members have left.  A world
+ * rank that finishes leaves every communicator it belongs to.  Calls of other
+ * members that wait for a rank that has left could never complete: they
+ * return RC_ERR_NOT_REGISTERED at once, and so do later calls on a
+ * communicator with a member that has left (send and recv only when the peer
+ * has left).
  * RC_ERR_NOT_REGISTERED for a rank not registered; RC_ERR_INVALID_ARGUMENT
  * while the rank still has a call in progress on another thread. */
 int rc_rank_finish(int rank);

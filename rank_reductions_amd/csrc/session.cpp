@@ -54,6 +54,7 @@ struct Slot {
     uint32_t arrived = 0;
     int left = 0;
     bool done = false;
+    bool abandoned = false;  // a member finished before arriving: the ranks that came get an error
     int status = RC_OK;
     std::string msg;
 };
@@ -78,6 +79,7 @@ struct PairSlot {
     bool null_buf = false;
     void* streams[2] = {nullptr, nullptr};
     bool done = false;
+    bool abandoned = false;
     int left = 0;
     int status = RC_OK;
     std::string msg;
@@ -425,6 +427,44 @@ Error resolve(int ep, int* id, int* local, int* world) {
     return {};
 }
 
+// Whether member `local` of `cm` has left: it finished its endpoint in a
+// split-off communicator, or its world rank, which ends all its endpoints.
+bool member_left(const Comm& cm, int local) {
+    return ((cm.fin_mask >> local) & 1u) || ((g_s.fin_mask >> cm.world[local]) & 1u);
+}
+
+Error check_members(const Comm& cm) {
+    for (int i = 0; i < cm.size(); ++i)
+        if (member_left(cm, i))
+            return Error{RC_ERR_NOT_REGISTERED, "rank " + std::to_string(i) +
+                                                    " of this communicator has finished: the call cannot complete"};
+    return {};
+}
+
+// Member `local` of `cm` is leaving: the calls of other members that wait for
+// it could never complete, so they end now with RC_ERR_NOT_REGISTERED (later
+// calls are refused by check_members).  The caller holds g_mu and notifies.
+void abandon_waits(Comm& cm, int local) {
+    const std::string why = "rank " + std::to_string(local) + " of the communicator finished before joining this ";
+    for (auto& kv : cm.slots) {
+        Slot& s = *kv.second;
+        if (s.done || ((s.arrived >> local) & 1u)) continue;
+        s.status = RC_ERR_NOT_REGISTERED;
+        s.msg = why + "call";
+        s.abandoned = true;
+        s.done = true;
+    }
+    for (auto& kv : cm.pairs) {
+        PairSlot& p = *kv.second;
+        const int src = std::get<0>(kv.first), dst = std::get<1>(kv.first);
+        if (p.done || !((src == local && !p.have[0]) || (dst == local && !p.have[1]))) continue;
+        p.status = RC_ERR_NOT_REGISTERED;
+        p.msg = why + (src == local ? "send" : "recv");
+        p.abandoned = true;
+        p.done = true;
+    }
+}
+
 Error claim(int world) {
     const uint32_t bit = 1u << world;
     if (g_s.busy_mask & bit)
@@ -438,6 +478,7 @@ int rank_collective(const RankArgs& a, int ep, void* stream, int* split_result =
     std::unique_lock<std::mutex> lock(g_mu);
     int id = 0, rank = 0, world = 0;
     Error e0 = resolve(ep, &id, &rank, &world);
+    if (!e0.code) e0 = check_members(g_s.comms[id]);
     if (!e0.code) e0 = claim(world);
     if (e0.code) return report(e0);
     Comm& cm = g_s.comms[id];
@@ -510,8 +551,9 @@ int rank_collective(const RankArgs& a, int ep, void* stream, int* split_result =
     const Error e{s->status, s->msg};
     if (split_result) *split_result = s->result.empty() ? -1 : s->result[rank];
     // the communicator outlives every call in progress on it (a member cannot
-    // finish while it is inside a call), so cm is still valid here
-    if (++s->left == R) cm.slots.erase(k);
+    // finish while it is inside a call), so cm is still valid here; nobody
+    // joins an abandoned slot after it ended
+    if (++s->left == (s->abandoned ? __builtin_popcount(s->arrived) : R)) cm.slots.erase(k);
     return report(e);
 }
 
@@ -529,6 +571,9 @@ int rank_p2p(bool is_send, int ep, int peer, const rc_buf* buf, void* stream) {
     if (peer < 0 || peer >= R || peer == rank)
         return report(Error{RC_ERR_INVALID_ARGUMENT, std::string(is_send ? "send: dst " : "recv: src ") +
                                                          std::to_string(peer) + " is not another rank"});
+    if (member_left(cm, peer))
+        return report(Error{RC_ERR_NOT_REGISTERED, std::string(is_send ? "send: dst " : "recv: src ") +
+                                                       std::to_string(peer) + " has finished"});
     e0 = claim(world);
     if (e0.code) return report(e0);
     const uint64_t gen = g_generation;
@@ -564,7 +609,7 @@ int rank_p2p(bool is_send, int ep, int peer, const rc_buf* buf, void* stream) {
     }
     g_s.busy_mask &= ~(1u << world);
     const Error e{s->status, s->msg};
-    if (++s->left == 2) cm.pairs.erase(key);
+    if (++s->left == (s->abandoned ? (int)s->have[0] + (int)s->have[1] : 2)) cm.pairs.erase(key);
     return report(e);
 }
 
@@ -750,10 +795,19 @@ int rc_rank_finish(int rank) {
         // a split-off communicator goes away when all its members have finished
         Comm& c = g_s.comms[id];
         c.fin_mask |= 1u << local;
+        abandon_waits(c, local);
+        g_cv.notify_all();
         if (c.fin_mask == (uint32_t)((1ull << c.size()) - 1)) g_s.comms.erase(id);
         return ok();
     }
     g_s.fin_mask |= 1u << world;
+    // the world rank leaves every communicator it belongs to
+    for (auto& kv : g_s.comms) {
+        Comm& c = kv.second;
+        const auto it = std::find(c.world.begin(), c.world.end(), world);
+        if (it != c.world.end()) abandon_waits(c, (int)(it - c.world.begin()));
+    }
+    g_cv.notify_all();
     if (g_s.fin_mask != g_s.reg_mask) return ok();
     Error e;
     if (!g_s.cfg.validate_only) e = device_finish();

@@ -214,11 +214,47 @@ void group_session(int rounds) {
     for (auto& t : ts) t.join();
 }
 
+// A rank leaving early: in each round one rank finishes after `stop` calls
+// while the others keep calling.  Their next call must end with
+// RC_ERR_NOT_REGISTERED, released from its wait or refused at once, and the
+// session must close once they have finished too.
+void leave_thread(int rank, int R, int round) {
+    const int leaver = round % R, stop = round % 5;
+    const uintptr_t base = 0x600000000ull + (uintptr_t)rank * 0x1000000ull;
+    for (int i = 0; !(rank == leaver && i == stop); ++i) {
+        rc_buf b = buf(base, base + 0x800000ull, 1 + (i * 37) % 2000);
+        const int rc = (i % 2) ? rc_rank_all_reduce(rank, &b, nullptr) : rc_rank_barrier(rank, nullptr);
+        if (i < stop) {
+            if (rc != RC_OK) ++g_bad;
+            continue;
+        }
+        if (rc != RC_ERR_NOT_REGISTERED) ++g_bad;
+        break;
+    }
+    if (rc_rank_finish(rank) != RC_OK) ++g_bad;
+}
+
+void leave_session(int R, int rounds) {
+    rc_config cfg;
+    std::memset(&cfg, 0, sizeof cfg);
+    cfg.struct_size = sizeof cfg;
+    cfg.device = -1;
+    cfg.validate_only = 1;
+    for (int round = 0; round < rounds; ++round) {
+        for (int r = 0; r < R; ++r)
+            if (rc_rank_register(r, R, &cfg) != RC_OK) ++g_bad;  // a new session each round
+        std::vector<std::thread> ts;
+        for (int r = 0; r < R; ++r) ts.emplace_back(leave_thread, r, R, round);
+        for (auto& t : ts) t.join();
+    }
+}
+
 }  // namespace
 
 int main() {
     rank_session(6, 3000);
     group_session(200);
+    leave_session(6, 300);
     const int R = 8;
     rc_config cfg;
     std::memset(&cfg, 0, sizeof cfg);

@@ -211,3 +211,58 @@ def test_single_rank_does_not_wait(lib):
     b = one(send_addr(0), recv_addr(0))
     assert lib.rc_rank_all_reduce(0, ctypes.cast(b, ctypes.c_void_p), None) == rr.RC_OK
     assert lib.rc_rank_finish(0) == rr.RC_OK
+
+
+def test_finish_releases_ranks_waiting_for_it(lib):
+    # rank 2 finishes instead of joining the all_reduce the others wait in
+    R = 3
+    for r in range(R):
+        assert lib.rc_rank_register(r, R, ctypes.byref(cfg())) == rr.RC_OK
+
+    def body(r):
+        if r == 2:
+            time.sleep(0.3)
+            return lib.rc_rank_finish(2)
+        b = one(send_addr(r), recv_addr(r))
+        rc = lib.rc_rank_all_reduce(r, ctypes.cast(b, ctypes.c_void_p), None)
+        return rc, lib.rc_last_error().decode()
+
+    res = run_ranks(R, body)
+    assert res[2] == rr.RC_OK
+    for r in range(2):
+        assert res[r][0] == rr.RC_ERR_NOT_REGISTERED
+        assert "rank 2" in res[r][1] and "finished" in res[r][1]
+    # later calls on the world are refused at once rather than waiting
+    b = one(send_addr(0), recv_addr(0))
+    assert lib.rc_rank_all_reduce(0, ctypes.cast(b, ctypes.c_void_p), None) == rr.RC_ERR_NOT_REGISTERED
+    assert lib.rc_rank_barrier(1, None) == rr.RC_ERR_NOT_REGISTERED
+    # the ranks left can still finish, which closes the session
+    assert lib.rc_rank_finish(0) == rr.RC_OK
+    assert lib.rc_rank_finish(1) == rr.RC_OK
+    assert lib.rc_rank_register(0, 2, ctypes.byref(cfg())) == rr.RC_OK
+
+
+def test_finish_releases_a_waiting_send_and_refuses_later_ones(lib):
+    R = 3
+    for r in range(R):
+        assert lib.rc_rank_register(r, R, ctypes.byref(cfg())) == rr.RC_OK
+
+    def body(r):
+        if r == 1:
+            time.sleep(0.3)
+            return lib.rc_rank_finish(1)
+        if r == 0:
+            b = one(send_addr(0), recv_addr(0))
+            return lib.rc_rank_send(0, ctypes.cast(b, ctypes.c_void_p), 1, None)
+        return rr.RC_OK
+
+    assert run_ranks(R, body) == [rr.RC_ERR_NOT_REGISTERED, rr.RC_OK, rr.RC_OK]
+    b = one(send_addr(2), recv_addr(2))
+    assert lib.rc_rank_recv(2, ctypes.cast(b, ctypes.c_void_p), 1, None) == rr.RC_ERR_NOT_REGISTERED
+    assert "has finished" in lib.rc_last_error().decode()
+    # pairs between ranks still registered are unaffected
+    res = run_ranks(R, lambda r: (
+        lib.rc_rank_send(0, ctypes.cast(one(send_addr(0), recv_addr(0)), ctypes.c_void_p), 2, None) if r == 0 else
+        lib.rc_rank_recv(2, ctypes.cast(one(send_addr(2), recv_addr(2)), ctypes.c_void_p), 0, None) if r == 2 else
+        rr.RC_OK))
+    assert res == [rr.RC_OK] * R

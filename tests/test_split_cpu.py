@@ -4,6 +4,7 @@ communicators with ranks counted inside them, nesting, errors, and finish."""
 
 import ctypes
 import threading
+import time
 
 import pytest
 
@@ -150,3 +151,43 @@ def test_unknown_endpoints(lib):
     assert ar(lib, 5 * rr.RC_MAX_RANKS, 0) == rr.RC_ERR_NOT_REGISTERED
     assert ar(lib, R, 0) == rr.RC_ERR_INVALID_ARGUMENT
     assert lib.rc_rank_finish(3 * rr.RC_MAX_RANKS + 1) == rr.RC_ERR_NOT_REGISTERED
+
+
+def test_leaving_a_split_communicator_releases_its_members(lib):
+    # world of 4; {0, 1, 2} split off.  Member 2 leaves the split communicator
+    # while 0 and 1 wait in it; then world rank 3 finishes, which releases
+    # world rank 0's wait on the world.
+    R = 4
+    for r in range(R):
+        assert lib.rc_rank_register(r, R, ctypes.byref(cfg())) == rr.RC_OK
+    eps = run_ranks(R, lambda r: split(lib, r, [0, 1, 2] if r < 3 else []))
+    assert [rc for rc, _ in eps] == [rr.RC_OK] * R
+    sub = [ep for _, ep in eps]
+    assert sub[3] == -1
+
+    def body(r):
+        if r == 2:
+            time.sleep(0.3)
+            return lib.rc_rank_finish(sub[2])
+        if r == 3:
+            return rr.RC_OK
+        return ar(lib, sub[r], r)
+
+    assert run_ranks(R, body) == [rr.RC_ERR_NOT_REGISTERED, rr.RC_ERR_NOT_REGISTERED, rr.RC_OK, rr.RC_OK]
+    # the split communicator refuses further calls; the world still works
+    assert ar(lib, sub[0], 0) == rr.RC_ERR_NOT_REGISTERED
+    assert run_ranks(R, lambda r: ar(lib, r, r)) == [rr.RC_OK] * R
+
+    def body2(r):
+        if r == 3:
+            time.sleep(0.3)
+            return lib.rc_rank_finish(3)
+        if r == 0:
+            return ar(lib, 0, 0)
+        return rr.RC_OK
+
+    assert run_ranks(R, body2) == [rr.RC_ERR_NOT_REGISTERED, rr.RC_OK, rr.RC_OK, rr.RC_OK]
+    for ep in (sub[0], sub[1]):
+        assert lib.rc_rank_finish(ep) == rr.RC_OK
+    for r in range(3):
+        assert lib.rc_rank_finish(r) == rr.RC_OK
