@@ -47,7 +47,8 @@ def parse():
     p.add_argument("--tile-elems", type=int, default=0)
     p.add_argument("--max-workgroups", type=int, default=0)
     p.add_argument("--cache-hint", default="auto", choices=["auto", "streaming", "normal"])
-    p.add_argument("--no-rows", action="store_true", help="skip the other collectives")
+    p.add_argument("--no-rows", action="store_true",
+                   help="skip the other collectives and the flushed per-call timing")
     p.add_argument("--full-batched", action="store_true",
                    help="time the batched all-reduce on the full 32-layer gradient list (211 GB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -84,11 +85,10 @@ def time_calls(torch, fn, iters, warmup=2):
     return t.stop_ms() / iters
 
 
-def time_cold(torch, fn, iters, scratch, warmup=2):
-    """Device time per call with the 256 MB Infinity Cache flushed first: an
-    untimed 512 MiB scratch write precedes every call, and HIP events bracket
-    the call alone.  For rows small enough to stay cache-resident between
-    back-to-back calls."""
+def cold_samples(torch, fn, iters, scratch, warmup=2):
+    """Device time in ms of each of `iters` calls with the 256 MB Infinity
+    Cache flushed first: an untimed 512 MiB scratch write precedes every call,
+    and HIP events bracket the call alone."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -99,7 +99,13 @@ def time_cold(torch, fn, iters, scratch, warmup=2):
         fn()
         b.record()
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in evs) / iters
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def time_cold(torch, fn, iters, scratch, warmup=2):
+    """Mean of cold_samples: for rows small enough to stay cache-resident
+    between back-to-back calls."""
+    return sum(cold_samples(torch, fn, iters, scratch, warmup)) / iters
 
 
 def kernels_sha():
@@ -122,6 +128,12 @@ def read_traffic():
         return int(float(vals["fetch_bytes_per_launch"]) + float(vals["write_bytes_per_launch"]))
     except (KeyError, ValueError):
         return None
+
+
+def step_one(call, bufs, stream, lib, rr):
+    rc = call(bufs, stream)
+    if rc:
+        raise rr.CollectiveError(rc, lib.rc_last_error().decode())
 
 
 def main():
@@ -193,6 +205,17 @@ def main():
     del src, dst
     log(f"bench: device copy of {R * N * 4 >> 20} MiB: {copy_ms * 1e3:.1f} us, {copy_gbps:.1f} GB/s")
 
+    # the same call timed one at a time after a cache flush: median and best
+    # (skipped with --no-rows, so that a profiled run holds only the timed steps)
+    cold = []
+    if not args.no_rows:
+        scratch = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+        cold = sorted(cold_samples(torch, lambda: step_one(all_reduce, p_sum, stream, lib, rr), 30, scratch))
+        del scratch
+        cold_med, cold_best = cold[len(cold) // 2], cold[0]
+        log(f"bench: one call at a time, cache flushed: median {cold_med * 1e3:.1f} us, "
+            f"best {cold_best * 1e3:.1f} us")
+
     result = {
         "metric": METRIC,
         "value": round(algbw, 2),
@@ -231,6 +254,15 @@ def main():
         "ranks_bit_identical": bool(same),
         "copy_ceiling": {"bytes": 2 * R * N * 4, "us": round(copy_ms * 1e3, 2), "GBps": round(copy_gbps, 1)},
     }
+    if cold:
+        result["per_call_flushed"] = {
+            "op": "all_reduce Sum", "calls": len(cold),
+            "timing": "HIP events around each call, after an untimed 512 MiB scratch write that evicts the Infinity Cache",
+            "median_us": round(cold_med * 1e3, 2), "best_us": round(cold_best * 1e3, 2),
+            "median_algbw_GBps": round(N * 4 / (cold_med / 1e3) / 1e9, 1),
+            "best_algbw_GBps": round(N * 4 / (cold_best / 1e3) / 1e9, 1),
+            "median_frac": round(hbm_bytes / (cold_med / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+        }
 
     if not args.no_rows:
         rr.finish()
