@@ -21,6 +21,7 @@ If librankred.so is not built the module still imports, but every call raises
 """
 
 import ctypes
+import threading
 from pathlib import Path
 
 import numpy as np
@@ -39,6 +40,7 @@ __all__ = [
 ]
 
 RC_MAX_RANKS = 16
+RC_ABI_VERSION = 2  # the include/rc.h this binding is written against
 RC_MAX_DIMS = 8
 
 RC_F32, RC_I32 = 0, 1
@@ -116,18 +118,32 @@ def library_path():
 
 
 _lib = None
+_lib_lock = threading.Lock()
 
 
 def library():
-    """The loaded librankred.so (ctypes), loading it on first use."""
+    """The loaded librankred.so (ctypes), loading it on first use.  Raises if
+    it is not built or was built from another version of include/rc.h."""
     global _lib
     if _lib is not None:
         return _lib
+    with _lib_lock:
+        if _lib is None:
+            _lib = _load()
+    return _lib
+
+
+def _load():
     path = library_path()
     if not path.exists():
         raise RuntimeError(f"{path} is not built: run `python -m rank_reductions_amd.build` "
                            "(no fallback implementation exists)")
     lib = ctypes.CDLL(str(path))
+    lib.rc_abi_version.argtypes = []
+    lib.rc_abi_version.restype = ctypes.c_int
+    if lib.rc_abi_version() != RC_ABI_VERSION:
+        raise RuntimeError(f"{path} reports ABI version {lib.rc_abi_version()}, this binding expects "
+                           f"{RC_ABI_VERSION}: rebuild with `python -m rank_reductions_amd.build`")
     for name in ("rc_all_reduce", "rc_reduce", "rc_broadcast", "rc_reduce_scatter", "rc_all_gather"):
         fn = getattr(lib, name)
         fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
@@ -175,7 +191,6 @@ def library():
     lib.rc_rank_split.restype = ctypes.c_int
     lib.rc_rank_finish.argtypes = [ctypes.c_int]
     lib.rc_rank_finish.restype = ctypes.c_int
-    _lib = lib
     return lib
 
 
