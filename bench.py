@@ -337,7 +337,12 @@ def rows(torch, rr, si, dev, xs8, args):
     rr.register(R, device=0, algo="ring")
     o = [torch.empty_like(x) for x in xs8]
     us = time_calls(torch, lambda: rr.all_reduce(xs8, "sum", out=o), 10) * 1e3
-    out["all_reduce_ring_r8_64MiB_f32_sum"] = _roof(2 * R * b, us)
+    # the ring moves (R+1)*N*4 bytes in and R*N*4 out: its reduce-scatter
+    # phase reads every input and writes the owner's segment, the all-gather
+    # phase reads that segment back and writes the other R-1 copies
+    out["all_reduce_ring_r8_64MiB_f32_sum"] = {
+        **_roof((2 * R + 1) * b, us), "bytes": "read (R+1)*N*4, write R*N*4",
+        "algbw_GBps": round(b / (us * 1e-6) / 1e9, 1)}
     rr.finish()
     # the same all-reduce through the per-rank front end: one host thread and
     # one stream per rank, calls matched by issue order
