@@ -349,6 +349,17 @@ def rows(torch, rr, si, dev, xs8, args):
     out["all_reduce_per_rank_threads_r8_64MiB_f32_sum_shared_stream"] = per_rank_row(torch, rr, xs8, o, 1)
     out["all_reduce_per_rank_threads_r8_64MiB_f32_sum_8_streams"] = per_rank_row(torch, rr, xs8, o, R)
     del o
+    # a length whose ring segments start 4 bytes past a 256-byte boundary:
+    # every job then begins with a short lead tile
+    n_odd = N + R
+    xo = si.torch_rank_inputs(R, n_odd, "f32", "normal", 1, device=dev)
+    oo = [torch.empty_like(x) for x in xo]
+    rr.register(R, device=0)
+    us = time_calls(torch, lambda: rr.all_reduce(xo, "sum", out=oo), 10) * 1e3
+    out["all_reduce_r8_64MiB_plus_8_f32_sum"] = {**_roof(2 * R * n_odd * 4, us), "elems_per_rank": n_odd,
+                                                 "segment_offset_mod_256_bytes": (-(-n_odd // R) * 4) % 256}
+    rr.finish()
+    del xo, oo
     rr.register(R, device=0)
     # the Communicator's copies on the metric workload's buffers
     log("bench: rows: all_to_all_single, all_gather list form, send/recv")

@@ -228,12 +228,18 @@ __device__ __forceinline__ void job_tile(const uint32_t* const (&in)[NIN], const
             element<NIN, NR, Op, NT, ACC>(in, ac, e, out, mask, mean);
         return;
     }
-    const int64_t head = phase < len ? phase : len;
+    const int64_t h = phase_head((uint8_t)phase);
+    const int64_t head = h < len ? h : len;
     const int64_t nvec = (len - head) / kVec;
     const int64_t tail0 = head + nvec * kVec;
     const int64_t tv = te / kVec;
-    const int64_t v0 = lt * tv;
-    const int64_t v1 = v0 + tv < nvec ? v0 + tv : nvec;
+    // a non-zero lead makes tile 0 the lead vectors alone; tile t >= 1 starts
+    // at vector lead + (t-1)*tv, on a kTileAlignBytes boundary
+    const int64_t l = phase_lead((uint8_t)phase);
+    const int64_t lead = l < nvec ? l : nvec;
+    const int64_t shift = lead > 0 ? lead - tv : 0;
+    const int64_t v0 = lt * tv + shift > 0 ? lt * tv + shift : 0;
+    const int64_t v1 = (lt + 1) * tv + shift < nvec ? (lt + 1) * tv + shift : nvec;
     constexpr int64_t kStep = (int64_t)kBlock * U;
     for (int64_t vb = v0; vb < v1; vb += kStep) {
         const int64_t off = head + vb * kVec;
@@ -398,9 +404,13 @@ __device__ __forceinline__ void copy_job_tile(const BatchArgs& a, int j, int64_t
 // Tiles of a job of `len` elements with alignment phase `phase` (as planned).
 __device__ __forceinline__ int64_t tiles_of(int64_t len, int phase, int64_t te) {
     if (phase == kScalarOnly) return (len + te - 1) / te;
-    const int64_t head = phase < len ? phase : len;
-    const int64_t body = ((len - head) / kVec) * kVec;
-    const int64_t t = (body + te - 1) / te;
+    const int64_t h = phase_head((uint8_t)phase);
+    const int64_t head = h < len ? h : len;
+    const int64_t nvec = (len - head) / kVec;
+    const int64_t l = phase_lead((uint8_t)phase);
+    const int64_t lead = l < nvec ? l : nvec;
+    const int64_t tv = te / kVec;
+    const int64_t t = (lead > 0 ? 1 : 0) + (nvec - lead + tv - 1) / tv;
     return t > 1 ? t : 1;
 }
 

@@ -90,17 +90,21 @@ uint8_t job_phase(const uintptr_t* addrs, int naddrs, int64_t esize, int64_t len
     const uintptr_t m = addrs[0] % 16;
     for (int i = 1; i < naddrs; ++i)
         if (addrs[i] % 16 != m) return kScalarOnly;
-    const int64_t phase = (int64_t)((16 - m) % 16) / esize;
+    const int head = (int)(((16 - m) % 16) / (uintptr_t)esize);
+    const uintptr_t first_vec = addrs[0] + (uintptr_t)(head * esize);
+    const int lead = (int)(((kTileAlignBytes - first_vec % kTileAlignBytes) % kTileAlignBytes) / 16);
     (void)len;
-    return (uint8_t)phase;
+    return phase_code(head, lead);
 }
 
 int64_t job_tiles(int64_t len, uint8_t phase, int64_t te) {
     if (len <= 0) return 0;
     if (phase == kScalarOnly) return (len + te - 1) / te;
-    const int64_t head = std::min<int64_t>(phase, len);
-    const int64_t body = ((len - head) / kVec) * kVec;
-    return std::max<int64_t>(1, (body + te - 1) / te);
+    const int64_t head = std::min<int64_t>(phase_head(phase), len);
+    const int64_t nvec = (len - head) / kVec;
+    const int64_t lead = std::min<int64_t>(phase_lead(phase), nvec);
+    const int64_t tv = te / kVec;
+    return std::max<int64_t>(1, (lead > 0 ? 1 : 0) + (nvec - lead + tv - 1) / tv);
 }
 
 int auto_waves_per_cu(int nin, int nout, int unroll, const InFlightRule& rule) {

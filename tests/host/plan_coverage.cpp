@@ -48,11 +48,14 @@ void tile_elements(int64_t len, int phase, int64_t lt, int64_t te, int unroll, F
             for (int64_t e = e0 + tid; e < e1; e += kBlock) visit(e, 4);
         return;
     }
-    const int64_t head = std::min<int64_t>(phase, len);
+    const int64_t head = std::min<int64_t>(phase_head((uint8_t)phase), len);
     const int64_t nvec = (len - head) / kVec;
     const int64_t tail0 = head + nvec * kVec;
     const int64_t tv = te / kVec;
-    const int64_t v0 = lt * tv, v1 = std::min(v0 + tv, nvec);
+    // a lead of L vectors is tile 0 on its own; tile t >= 1 starts at L + (t-1)*tv
+    const int64_t lead = std::min<int64_t>(phase_lead((uint8_t)phase), nvec);
+    const int64_t v0 = lead > 0 ? (lt == 0 ? 0 : lead + (lt - 1) * tv) : lt * tv;
+    const int64_t v1 = std::min(lead > 0 ? (lt == 0 ? lead : lead + lt * tv) : (lt + 1) * tv, nvec);
     const int64_t step = (int64_t)kBlock * unroll;
     for (int64_t vb = v0; vb < v1; vb += step)
         for (int u = 0; u < unroll; ++u)
@@ -185,6 +188,17 @@ int main(int argc, char** argv) {
     dev.lds_per_cu = 160 * 1024;
     dev.max_lds_per_block = 64 * 1024;
     int plans = 0;
+    // job_phase: the head reaches a 16-byte boundary, the lead a 256-byte one
+    for (int i = 0; i < 20000; ++i) {
+        const uintptr_t base = 0x10000 + (uintptr_t)(rng() % 8192) * 4;
+        uintptr_t addrs[3] = {base, base + 4096 * (1 + rng() % 5), base + 16 * (rng() % 1000)};
+        const uint8_t ph = job_phase(addrs, 3, 4, 1000);
+        const uintptr_t v = base + (uintptr_t)phase_head(ph) * 4;
+        if (ph == kScalarOnly || v % 16 || (v + (uintptr_t)phase_lead(ph) * 16) % kTileAlignBytes)
+            fail("job_phase: wrong head or lead for base " + std::to_string(base));
+        addrs[2] += 4;
+        if (job_phase(addrs, 3, 4, 1000) != kScalarOnly) fail("job_phase: mixed alignment not scalar-only");
+    }
     for (int it = 0; it < iters; ++it) {
         g_bufs.clear();
         const int R = 1 + (int)(rng() % 16);
