@@ -166,6 +166,40 @@ __device__ __forceinline__ void element(const uint32_t* const (&in)[NIN], const 
         if ((mask >> o) & 1u) st1<NT>(out(o) + e, acc);
 }
 
+// The element-by-element path in rounds: J elements per lane, kBlock apart
+// (each a coalesced 256-byte run across the wave), all loads issued before
+// the folds, so that as many bytes are in flight as in a vector round.
+template <int NIN, int NR, class Op, int J, bool NT, bool ACC, class OutF>
+__device__ __forceinline__ void element_round(const uint32_t* const (&in)[NIN], const uint32_t* const (&ac)[NIN],
+                                              int64_t e, const OutF& out, uint32_t mask, bool mean) {
+    constexpr int NA = ACC ? NIN : 1;
+    uint32_t x[J][NIN];
+    uint32_t y[J][NA];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+#pragma unroll
+        for (int k = 0; k < NIN; ++k) x[j][k] = ld1<NT>(in[k] + e + j * kBlock);
+        if constexpr (ACC) {
+#pragma unroll
+            for (int k = 0; k < NIN; ++k) y[j][k] = ld1<NT>(ac[k] + e + j * kBlock);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        if constexpr (ACC) {
+#pragma unroll
+            for (int k = 0; k < NIN; ++k) x[j][k] = op2<Op>(y[j][k], x[j][k]);
+        }
+        uint32_t acc = fold<NIN, Op>(x[j]);
+        if constexpr (Op::kCanMean) {
+            if (mean) acc = mean1<NIN>(acc);
+        }
+#pragma unroll
+        for (int o = 0; o < NR; ++o)
+            if ((mask >> o) & 1u) st1<NT>(out(o) + e + j * kBlock, acc);
+    }
+}
+
 // One round: U vectors per lane.  in[k] + off and out(o) + off are uniform
 // (the round's first element); lane vectors sit at 32-bit offsets from there.
 // Unless FULL, only the first `nv` vectors of the round exist.
@@ -222,10 +256,15 @@ __device__ __forceinline__ void job_tile(const uint32_t* const (&in)[NIN], const
                                          int64_t te, bool mean) {
     const int tid = threadIdx.x;
     if (phase == kScalarOnly) {
+        // full rounds of 4U elements per lane (a tile holds a whole number of
+        // them), then the last tile's remainder one element per lane at a time
+        constexpr int J = 4 * U;
         const int64_t e0 = lt * te;
         const int64_t e1 = e0 + te < len ? e0 + te : len;
-        for (int64_t e = e0 + tid; e < e1; e += kBlock)
-            element<NIN, NR, Op, NT, ACC>(in, ac, e, out, mask, mean);
+        int64_t e = e0;
+        for (; e + (int64_t)J * kBlock <= e1; e += (int64_t)J * kBlock)
+            element_round<NIN, NR, Op, J, NT, ACC>(in, ac, e + tid, out, mask, mean);
+        for (e += tid; e < e1; e += kBlock) element<NIN, NR, Op, NT, ACC>(in, ac, e, out, mask, mean);
         return;
     }
     const int64_t h = phase_head((uint8_t)phase);

@@ -43,9 +43,15 @@ bool inside(uintptr_t a, int64_t bytes) {
 template <class F>
 void tile_elements(int64_t len, int phase, int64_t lt, int64_t te, int unroll, F&& visit) {
     if (phase == kScalarOnly) {
+        // rounds of 4*unroll elements per lane, kBlock apart, then the remainder
         const int64_t e0 = lt * te, e1 = std::min(e0 + te, len);
+        const int64_t J = 4 * unroll;
+        int64_t e = e0;
+        for (; e + J * kBlock <= e1; e += J * kBlock)
+            for (int tid = 0; tid < kBlock; ++tid)
+                for (int64_t j = 0; j < J; ++j) visit(e + tid + j * kBlock, 4);
         for (int tid = 0; tid < kBlock; ++tid)
-            for (int64_t e = e0 + tid; e < e1; e += kBlock) visit(e, 4);
+            for (int64_t x = e + tid; x < e1; x += kBlock) visit(x, 4);
         return;
     }
     const int64_t head = std::min<int64_t>(phase_head((uint8_t)phase), len);

@@ -243,3 +243,33 @@ def test_params_accumulated_rank_threads():
     finally:
         for r in range(R):
             rr.rank_finish(r)
+
+
+@pytest.mark.parametrize("R", [2, 4])
+def test_params_accumulated_misaligned_views(R):
+    """Gradients and accumulators carved out of larger buffers at offsets of
+    0-3 elements that differ between ranks: every job runs element by element
+    (in rounds of several elements per lane), with and without accumulators,
+    and the bits still equal the oracle's."""
+    specs = {11: (40_003,), 12: (1_001,), 13: (5_000,)}
+    grads, accs = [], []
+    for r in range(R):
+        g, a = {}, {}
+        for k, shape in specs.items():
+            n = shape[0]
+            og, oa = (r + k) % 4, (r * 3 + k) % 4
+            g[k] = si.torch_tensor_for(70, k, R, r, (n + 4,), device=DEV)[og:og + n]
+            a[k] = si.torch_tensor_for(71, k, R, r, (n + 4,), device=DEV)[oa:oa + n]
+        grads.append(g)
+        accs.append(a)
+    torch.cuda.synchronize()
+    for use_acc in (False, True):
+        want = oracle.all_reduce_params(host_maps(grads), "mean", acc=host_maps(accs) if use_acc else None)
+        outs = []
+        for r in range(R):
+            outs.append({k: torch.empty(v.numel() + 4, device=DEV)[(r + 1) % 4:(r + 1) % 4 + v.numel()]
+                         for k, v in grads[r].items()})
+        with session(R, device=0):
+            rr.all_reduce_params(grads, "mean", out=outs, acc=accs if use_acc else None)
+            torch.cuda.synchronize()
+        check(outs, want, f"R={R} acc={use_acc}")
