@@ -246,7 +246,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": read_traffic() if args.algo != "ring" else None,
-            "kernel": "fold_kernel<8, OpSumF32, 1, true, false>" if args.algo != "ring" else "ring phases",
+            "kernel": "fold_full_kernel<8, OpSumF32, 1, true, false>" if args.algo != "ring" else "ring phases",
             "algorithmic_bytes_per_launch": hbm_bytes // launches_per_call,
             "avg_launch_us": round(launch_ms * 1e3, 2),
         },

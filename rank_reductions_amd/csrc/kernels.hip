@@ -126,7 +126,8 @@ __device__ __forceinline__ void st1(uint32_t* p, uint32_t v) {
 // ---------------------------------------------------------------- one job
 //
 // in[k] is the k-th operand of the fold at the job's first element (the ring
-// order of the job's segment); out(o) is rank o's output at that element.
+// order of the job's segment); out(o) is rank o's output at that element
+// (an Outs).
 
 template <class Op>
 __device__ __forceinline__ uint32_t op2(uint32_t a, uint32_t b) { return Op::apply(a, b); }
@@ -140,6 +141,31 @@ __device__ __forceinline__ V fold(const V (&x)[NIN]) {
 #pragma unroll
     for (int k = 1; k < NIN; ++k) acc = op2<Op>(acc, x[k]);
     return acc;
+}
+
+// Output pointers of up to NR ranks, all read when the struct is built.  A
+// pointer read inside each output's store branch would cost one dependent
+// scalar load per output after the data has arrived, and a wave holds its
+// slot on the CU all that time.  pin() makes the values live at that point,
+// so the loads are issued together and their wait overlaps the HBM loads.
+template <int NR>
+struct Outs {
+    uint32_t* base[NR];
+    int64_t off;  // element offset added to every rank's pointer
+    __device__ __forceinline__ uint32_t* operator()(int o) const { return base[o] + off; }
+    __device__ __forceinline__ void pin() const {
+#pragma unroll
+        for (int o = 0; o < NR; ++o) asm volatile("" ::"s"(base[o]));
+    }
+};
+
+template <int NR>
+__device__ __forceinline__ Outs<NR> outs_of(void* const* ptrs, int64_t off) {
+    Outs<NR> r;
+#pragma unroll
+    for (int o = 0; o < NR; ++o) r.base[o] = static_cast<uint32_t*>(ptrs[o]);
+    r.off = off;
+    return r;
 }
 
 // With ACC, operand k is acc[k] + in[k] (an accumulator plus the last
@@ -225,6 +251,7 @@ __device__ __forceinline__ void vec_round(const uint32_t* const (&in)[NIN], cons
             }
         }
     }
+    out.pin();
     u32x4 acc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -328,8 +355,7 @@ __device__ __forceinline__ void fold_tile(const JobArgs& a, int c, int lt) {
         in[k] = static_cast<const uint32_t*>(a.in[r]) + ioff;
         ac[k] = ACC ? static_cast<const uint32_t*>(a.acc[r]) + ioff : nullptr;
     }
-    const int64_t ooff = (int64_t)c * a.out_stride;
-    auto out = [&](int o) { return static_cast<uint32_t*>(a.out[o]) + ooff; };
+    const Outs<NIN> out = outs_of<NIN>(a.out, (int64_t)c * a.out_stride);
     job_tile<NIN, NIN, Op, U, NT, ACC>(in, ac, out, out_mask_of(a, c), len, a.phase[c], lt, a.tile_elems,
                                        a.mean != 0);
 }
@@ -342,10 +368,43 @@ __device__ __forceinline__ void copy_tile(const JobArgs& a, int c, int lt) {
     const int64_t len = a.n - start < a.seg ? a.n - start : a.seg;
     const uint32_t* in[1] = {static_cast<const uint32_t*>(a.in[c]) + (int64_t)c * a.in_stride};
     const uint32_t* none[1] = {nullptr};
-    const int64_t ooff = (int64_t)c * a.out_stride;
-    auto out = [&](int o) { return static_cast<uint32_t*>(a.out[o]) + ooff; };
+    const Outs<NR> out = outs_of<NR>(a.out, (int64_t)c * a.out_stride);
     job_tile<1, NR, OpSumI32, U, NT, false>(in, none, out, out_mask_of(a, c), len, a.phase[c], lt,
                                             a.tile_elems, false);
+}
+
+// Whole-tile launches (full_tiles): every job has phase 0 and exactly
+// gridDim.x tiles of one round (kBlock*kVec*U elements), so workgroup
+// (x, y) = (tile, job) does one full round with no head, lead, tail or
+// tile-count logic.  These are kernels of their own: the same round inside
+// the general kernel, whose other paths shape its register and scalar-load
+// scheduling, measured 2-3% slower on the 8-rank fold.
+template <int NIN, class Op, int U, bool NT, bool ACC>
+__global__ __launch_bounds__(kBlock) void fold_full_kernel(JobArgs a) {
+    const int c = blockIdx.y;
+    const int64_t e0 = (int64_t)blockIdx.x * (kBlock * kVec * U);
+    const int64_t ioff = (int64_t)c * a.in_stride + e0;
+    const uint32_t* in[NIN];
+    const uint32_t* ac[NIN];
+#pragma unroll
+    for (int k = 0; k < NIN; ++k) {
+        int r = c + 1 + k;
+        r = r >= NIN ? r - NIN : r;
+        in[k] = static_cast<const uint32_t*>(a.in[r]) + ioff;
+        ac[k] = ACC ? static_cast<const uint32_t*>(a.acc[r]) + ioff : nullptr;
+    }
+    const Outs<NIN> out = outs_of<NIN>(a.out, (int64_t)c * a.out_stride + e0);
+    vec_round<NIN, NIN, Op, U, NT, ACC, true>(in, ac, 0, 0, out, out_mask_of(a, c), a.mean != 0);
+}
+
+template <int NR, int U, bool NT>
+__global__ __launch_bounds__(kBlock) void copy_full_kernel(JobArgs a) {
+    const int c = blockIdx.y;
+    const int64_t e0 = (int64_t)blockIdx.x * (kBlock * kVec * U);
+    const uint32_t* in[1] = {static_cast<const uint32_t*>(a.in[c]) + (int64_t)c * a.in_stride + e0};
+    const uint32_t* none[1] = {nullptr};
+    const Outs<NR> out = outs_of<NR>(a.out, (int64_t)c * a.out_stride + e0);
+    vec_round<1, NR, OpSumI32, U, NT, false, true>(in, none, 0, 0, out, out_mask_of(a, c), false);
 }
 
 // Launch shapes: one-shot launches use a 2-D grid, blockIdx.y = job and
@@ -421,7 +480,7 @@ __global__ __launch_bounds__(kBlock) void batch_kernel(BatchArgs a) {
             in[k] = static_cast<const uint32_t*>(tp[k]);
             ac[k] = ACC ? static_cast<const uint32_t*>(tp[NIN + k]) : nullptr;
         }
-        auto out = [&](int o) { return static_cast<uint32_t*>(const_cast<void*>(tp[kOut + o])); };
+        const Outs<NIN> out = outs_of<NIN>(const_cast<void* const*>(tp + kOut), 0);
         job_tile<NIN, NIN, Op, U, NT, ACC>(in, ac, out, (1u << NIN) - 1u, jb.len, jb.phase, t - jb.tile_begin,
                                            a.tile_elems, a.mean != 0);
     }
@@ -435,7 +494,7 @@ __device__ __forceinline__ void copy_job_tile(const BatchArgs& a, int j, int64_t
     const void* const* tp = a.ptrs + (int64_t)j * (1 + NR);
     const uint32_t* in[1] = {static_cast<const uint32_t*>(tp[0])};
     const uint32_t* none[1] = {nullptr};
-    auto out = [&](int o) { return static_cast<uint32_t*>(const_cast<void*>(tp[1 + o])); };
+    const Outs<NR> out = outs_of<NR>(const_cast<void* const*>(tp + 1), 0);
     job_tile<1, NR, OpSumI32, U, NT, false>(in, none, out, (1u << NR) - 1u, jb.len, jb.phase, lt, a.tile_elems,
                                             false);
 }
@@ -486,7 +545,7 @@ __global__ __launch_bounds__(kBlock) void copy_args_kernel(CopyArgs a) {
     const void* const* tp = a.ptrs + j * (1 + NR);
     const uint32_t* in[1] = {static_cast<const uint32_t*>(tp[0])};
     const uint32_t* none[1] = {nullptr};
-    auto out = [&](int o) { return static_cast<uint32_t*>(const_cast<void*>(tp[1 + o])); };
+    const Outs<NR> out = outs_of<NR>(const_cast<void* const*>(tp + 1), 0);
     job_tile<1, NR, OpSumI32, U, NT, false>(in, none, out, (1u << NR) - 1u, a.len, phase, blockIdx.x,
                                             a.tile_elems, false);
 }
@@ -501,36 +560,24 @@ constexpr int kUnroll = unroll_for(ACC ? 2 * NIN : NIN);
 using FoldFn = void (*)(JobArgs);
 using BatchFn = void (*)(BatchArgs);
 
-template <int NIN, class Op, bool NT, bool ACC>
-FoldFn fold_ptr() { return fold_kernel<NIN, Op, kUnroll<NIN, ACC>, NT, ACC>; }
+template <int NIN, class Op, bool NT, bool ACC, bool FULL>
+FoldFn fold_ptr() {
+    if constexpr (FULL) return fold_full_kernel<NIN, Op, kUnroll<NIN, ACC>, NT, ACC>;
+    else return fold_kernel<NIN, Op, kUnroll<NIN, ACC>, NT, ACC>;
+}
 template <int NIN, class Op, bool NT, bool ACC>
 BatchFn batch_ptr() { return batch_kernel<NIN, Op, kUnroll<NIN, ACC>, NT, ACC>; }
 
-template <int NR, bool NT>
-FoldFn copy_ptr() { return copy_kernel<NR, kCopyUnroll, NT>; }
-
-template <bool NT>
-FoldFn pick_copy(int nranks) {
-    switch (nranks) {
-        case 1: return copy_ptr<1, NT>();
-        case 2: return copy_ptr<2, NT>();
-        case 3: return copy_ptr<3, NT>();
-        case 4: return copy_ptr<4, NT>();
-        case 5: return copy_ptr<5, NT>();
-        case 6: return copy_ptr<6, NT>();
-        case 7: return copy_ptr<7, NT>();
-        case 8: return copy_ptr<8, NT>();
-        case 9: return copy_ptr<9, NT>();
-        case 10: return copy_ptr<10, NT>();
-        case 11: return copy_ptr<11, NT>();
-        case 12: return copy_ptr<12, NT>();
-        case 13: return copy_ptr<13, NT>();
-        case 14: return copy_ptr<14, NT>();
-        case 15: return copy_ptr<15, NT>();
-        case 16: return copy_ptr<16, NT>();
-        default: return nullptr;
-    }
-}
+template <bool NT, bool FULL>
+struct CopyOf {
+    template <int NR>
+    struct At {
+        static FoldFn get() {
+            if constexpr (FULL) return copy_full_kernel<NR, kCopyUnroll, NT>;
+            else return copy_kernel<NR, kCopyUnroll, NT>;
+        }
+    };
+};
 
 // Kernel for nin = 1..16 ranks; Make<NIN>::get() names the instantiation.
 template <template <int> class Make, class Fn>
@@ -556,11 +603,16 @@ Fn pick_nin(int nin) {
     }
 }
 
-template <class Op, bool NT, bool ACC>
+template <bool NT, bool FULL>
+FoldFn pick_copy(int nranks) {
+    return pick_nin<CopyOf<NT, FULL>::template At, FoldFn>(nranks);
+}
+
+template <class Op, bool NT, bool ACC, bool FULL>
 struct FoldOf {
     template <int NIN>
     struct At {
-        static FoldFn get() { return fold_ptr<NIN, Op, NT, ACC>(); }
+        static FoldFn get() { return fold_ptr<NIN, Op, NT, ACC, FULL>(); }
     };
 };
 template <class Op, bool NT, bool ACC>
@@ -572,20 +624,20 @@ struct BatchOf {
 };
 
 // Accumulators exist for Sum and Mean only (validation refuses Max).
-template <bool NT, bool ACC>
+template <bool NT, bool ACC, bool FULL>
 FoldFn pick_fold_op(int dtype, int op, int nin) {
     if (dtype == RC_F32) {
         if (op == RC_MAX) {
             if constexpr (ACC) return nullptr;
-            else return pick_nin<FoldOf<OpMaxF32, NT, false>::template At, FoldFn>(nin);
+            else return pick_nin<FoldOf<OpMaxF32, NT, false, FULL>::template At, FoldFn>(nin);
         }
-        return pick_nin<FoldOf<OpSumF32, NT, ACC>::template At, FoldFn>(nin);
+        return pick_nin<FoldOf<OpSumF32, NT, ACC, FULL>::template At, FoldFn>(nin);
     }
     if (op == RC_MAX) {
         if constexpr (ACC) return nullptr;
-        else return pick_nin<FoldOf<OpMaxI32, NT, false>::template At, FoldFn>(nin);
+        else return pick_nin<FoldOf<OpMaxI32, NT, false, FULL>::template At, FoldFn>(nin);
     }
-    return pick_nin<FoldOf<OpSumI32, NT, ACC>::template At, FoldFn>(nin);
+    return pick_nin<FoldOf<OpSumI32, NT, ACC, FULL>::template At, FoldFn>(nin);
 }
 
 template <bool NT, bool ACC>
@@ -621,9 +673,9 @@ struct CopyArgsOf {
     };
 };
 
-template <bool NT>
+template <bool NT, bool FULL>
 FoldFn pick_fold_any(int dtype, int op, int nin, bool acc) {
-    return acc ? pick_fold_op<NT, true>(dtype, op, nin) : pick_fold_op<NT, false>(dtype, op, nin);
+    return acc ? pick_fold_op<NT, true, FULL>(dtype, op, nin) : pick_fold_op<NT, false, FULL>(dtype, op, nin);
 }
 template <bool NT>
 BatchFn pick_batch_any(int dtype, int op, int nin, bool acc) {
@@ -634,10 +686,18 @@ BatchFn pick_batch_any(int dtype, int op, int nin, bool acc) {
 
 hipError_t launch_jobs(const LaunchPlan& p, hipStream_t stream) {
     const bool nt = p.args.nontemporal != 0;
+    const bool full = p.args.full_tiles != 0;
     FoldFn fn;
-    if (p.args.in_mode == kInCopy) fn = nt ? pick_copy<true>(p.args.nranks) : pick_copy<false>(p.args.nranks);
-    else fn = nt ? pick_fold_any<true>(p.dtype, p.op, p.nin, p.acc)
-                 : pick_fold_any<false>(p.dtype, p.op, p.nin, p.acc);
+    if (p.args.in_mode == kInCopy) {
+        const int nr = p.args.nranks;
+        fn = nt ? (full ? pick_copy<true, true>(nr) : pick_copy<true, false>(nr))
+                : (full ? pick_copy<false, true>(nr) : pick_copy<false, false>(nr));
+    } else {
+        fn = nt ? (full ? pick_fold_any<true, true>(p.dtype, p.op, p.nin, p.acc)
+                        : pick_fold_any<true, false>(p.dtype, p.op, p.nin, p.acc))
+                : (full ? pick_fold_any<false, true>(p.dtype, p.op, p.nin, p.acc)
+                        : pick_fold_any<false, false>(p.dtype, p.op, p.nin, p.acc));
+    }
     if (!fn) return hipErrorInvalidValue;
     hipLaunchKernelGGL(fn, dim3(p.grid, p.grid_y), dim3(kBlock), p.lds_bytes, stream, p.args);
     return hipGetLastError();

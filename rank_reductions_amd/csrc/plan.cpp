@@ -320,16 +320,26 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceI
         const int in_mask = __builtin_popcount(ja.out_mask);
         lp.nout = ja.out_mode == kOutOwner ? 1 : in_mask - (ja.out_mode == kOutMaskButOwner ? 1 : 0);
         const int loads = lp.acc ? 2 * lp.nin : lp.nin;
-        shape_launch(lp.total_tiles, loads, lp.nout, lp.unroll, cfg, dev, &lp.grid, &lp.lds_bytes);
-        if (cfg.max_workgroups <= 0) {
-            // one-shot: x = tiles of the longest job, y = jobs
-            int64_t widest = 0;
-            for (int c = 0; c < ja.jobs; ++c)
-                widest = std::max<int64_t>(widest, ja.tile_prefix[c + 1] - ja.tile_prefix[c]);
-            lp.args.grid_2d = 1;
-            lp.grid = std::max<int64_t>(1, widest);
-            lp.grid_y = ja.jobs;
+        if (cfg.max_workgroups > 0) {
+            shape_launch(lp.total_tiles, loads, lp.nout, lp.unroll, cfg, dev, &lp.grid, &lp.lds_bytes);
+            continue;
         }
+        // one-shot: x = tiles of the longest job, y = jobs
+        int64_t widest = 0;
+        for (int c = 0; c < ja.jobs; ++c) widest = std::max<int64_t>(widest, ja.tile_prefix[c + 1] - ja.tile_prefix[c]);
+        bool full = widest > 0 && ja.tile_elems == (int64_t)kBlock * kVec * lp.unroll;
+        for (int c = 0; c < ja.jobs && full; ++c) {
+            const int64_t len = std::max<int64_t>(0, std::min(ja.seg, ja.n - (int64_t)c * ja.seg));
+            full = ja.phase[c] == 0 && ja.tile_prefix[c + 1] - ja.tile_prefix[c] == widest &&
+                   len == widest * (int64_t)ja.tile_elems;
+        }
+        // whole-tile kernels carry their own occupancy rules (fitted per shape)
+        const InFlightRule& rule = !full ? kFoldRule : (ja.in_mode == kInCopy ? kCopyBatchRule : kFullFoldRule);
+        shape_launch(lp.total_tiles, loads, lp.nout, lp.unroll, cfg, dev, &lp.grid, &lp.lds_bytes, rule);
+        lp.args.grid_2d = 1;
+        lp.args.full_tiles = full ? 1 : 0;
+        lp.grid = std::max<int64_t>(1, widest);
+        lp.grid_y = ja.jobs;
     }
     return out;
 }

@@ -64,6 +64,11 @@ struct JobArgs {
     int32_t mean;           // divide the finished fold by nranks
     int32_t nontemporal;
     int32_t grid_2d;                     // one-shot 2-D grid (x: tile of job, y: job)
+    // 2-D grid whose every tile is one whole round: each job has phase 0 and
+    // exactly gridDim.x tiles of tile_elems = kBlock*kVec*unroll elements.
+    // Such launches run the whole-tile kernels, which skip the head, lead,
+    // tail and tile-count logic.
+    int32_t full_tiles;
     int32_t total_tiles;                 // tile_prefix[jobs], below 2^31
     int32_t tile_prefix[kMaxRanks + 1];  // tiles before job j; past the last job: total_tiles
     uint8_t phase[kMaxRanks];            // job phase (phase_code), or kScalarOnly
@@ -230,8 +235,9 @@ struct InFlightRule {
     double kib;
     double store_weight;
 };
-constexpr InFlightRule kFoldRule{110.0, 0.65};     // folds and single-collective copies
-constexpr InFlightRule kCopyBatchRule{60.0, 0.5};  // batched copies (by-value table)
+constexpr InFlightRule kFoldRule{110.0, 0.65};     // general fold and copy kernels
+constexpr InFlightRule kCopyBatchRule{60.0, 0.5};  // batched copies; whole-tile copies
+constexpr InFlightRule kFullFoldRule{85.0, 0.52};  // whole-tile folds
 int auto_waves_per_cu(int nin, int nout, int unroll, const InFlightRule& rule = kFoldRule);
 // Grid and LDS reservation of a launch of `total_tiles` tiles.
 void shape_launch(int64_t total_tiles, int nin, int nout, int unroll, const Config& cfg,

@@ -93,7 +93,17 @@ void check_plan(const LaunchPlan& p, const std::string& name) {
         if (p.grid_y != a.jobs) fail(name + ": 2-D grid height is not the job count");
         for (int c = 0; c < p.grid_y; ++c)
             for (int64_t lt = 0; lt < p.grid; ++lt)
-                if (lt < a.tile_prefix[c + 1] - a.tile_prefix[c]) visits.push_back({c, lt});
+                if (a.full_tiles || lt < a.tile_prefix[c + 1] - a.tile_prefix[c]) visits.push_back({c, lt});
+        if (a.full_tiles) {
+            // the kernels then take every tile as whole: check that it is
+            for (int c = 0; c < a.jobs; ++c) {
+                const int64_t len = std::max<int64_t>(0, std::min(a.seg, a.n - (int64_t)c * a.seg));
+                if (a.tile_elems != kBlock * kVec * p.unroll || a.phase[c] != 0 ||
+                    a.tile_prefix[c + 1] - a.tile_prefix[c] != p.grid ||
+                    len != p.grid * (int64_t)a.tile_elems)
+                    fail(name + ": full_tiles set on a job that is not whole tiles");
+            }
+        }
     } else {
         if (p.grid_y != 1) fail(name + ": 1-D launch with a 2-D grid");
         for (int64_t b = 0; b < p.grid; ++b)
@@ -116,7 +126,16 @@ void check_plan(const LaunchPlan& p, const std::string& name) {
         uint32_t mask = a.out_mask;
         if (a.out_mode == kOutOwner) mask = 1u << c;
         else if (a.out_mode == kOutMaskButOwner) mask &= ~(1u << c);
-        tile_elements(len, a.phase[c], lt, a.tile_elems, p.unroll, [&](int64_t e, int bytes) {
+        auto visit_tile = [&](auto&& visit) {
+            if (a.full_tiles) {
+                // fold_full_kernel / copy_full_kernel: one round of whole 16-byte vectors
+                // from lt*tile_elems
+                for (int64_t e = lt * a.tile_elems; e < (lt + 1) * a.tile_elems; e += kVec) visit(e, 16);
+            } else {
+                tile_elements(len, a.phase[c], lt, a.tile_elems, p.unroll, visit);
+            }
+        };
+        visit_tile([&](int64_t e, int bytes) {
             const int n = bytes / 4;
             for (int i = 0; i < n; ++i) {
                 if (e + i < 0 || e + i >= len) fail(name + ": element outside its job");
@@ -194,6 +213,7 @@ int main(int argc, char** argv) {
     dev.lds_per_cu = 160 * 1024;
     dev.max_lds_per_block = 64 * 1024;
     int plans = 0;
+    int full_plans = 0;  // plans whose kernels take the whole-tile path
     // job_phase: the head reaches a 16-byte boundary, the lead a 256-byte one
     for (int i = 0; i < 20000; ++i) {
         const uintptr_t base = 0x10000 + (uintptr_t)(rng() % 8192) * 4;
@@ -211,6 +231,7 @@ int main(int argc, char** argv) {
         const int sizes[] = {0, 1, 2, 3, 5, 7, 64, 255, 256, 257, 1000, 4099, 20000, 65537};
         int64_t n = sizes[rng() % 14];
         if (rng() % 3 == 0) n = (int64_t)(rng() % 50000);
+        if (rng() % 4 == 0) n = (int64_t)R * 4096 * (int64_t)(1 + rng() % 3);  // whole tiles per segment
         Config cfg;
         cfg.algo = rng() % 2 ? RC_ALGO_RING : RC_ALGO_DIRECT;
         const int64_t tiles[] = {0, 0, 256, 1024, 4096};
@@ -251,6 +272,7 @@ int main(int argc, char** argv) {
             check_plan(p, "coll " + std::to_string(coll) + " R=" + std::to_string(R) + " n=" + std::to_string(n) +
                               " mis=" + std::to_string(mis_mode) + (ck.has_acc ? " acc" : ""));
             ++plans;
+            if (p.args.full_tiles) ++full_plans;
         }
     }
     // batched plans: job lookup through the group index, and coverage
@@ -430,6 +452,8 @@ int main(int argc, char** argv) {
                 }
         ++copies;
     }
-    std::printf("checked %d plans, %d batches and %d copy batches: %d failures\n", plans, batches, copies, g_fail);
+    if (iters >= 100 && full_plans == 0) fail("no plan took the whole-tile path");
+    std::printf("checked %d plans (%d whole-tile), %d batches and %d copy batches: %d failures\n", plans, full_plans,
+                batches, copies, g_fail);
     return g_fail ? 1 : 0;
 }
