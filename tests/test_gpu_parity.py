@@ -375,6 +375,34 @@ def test_all_reduce_many_mixed_sizes(R):
                 assert_bits(host(outs[t][r]), want, f"tensor {t} {shapes[t]} rank {r}")
 
 
+@pytest.mark.parametrize("R,dtype,op", [(4, "f32", "mean"), (4, "i32", "sum"), (8, "f32", "sum"),
+                                         (8, "f32", "max"), (3, "f32", "mean")])
+def test_all_reduce_many_own_launches(R, dtype, op):
+    """Tensors large enough for launches of their own: whole-tile segments
+    (the whole-tile kernel), a ragged one and a misaligned view (the general
+    kernel), next to small batched ones.  Every tensor equals the ring-order
+    oracle and the single-tensor call."""
+    tile = 256 * (2 if R < 8 else 1)  # 64 lanes x 4 elements x unroll
+    own = (64 << 20) // (2 * R * 4)   # elements per rank for a launch of its own
+    whole = -(-own // (R * tile)) * R * tile
+    shapes = [(whole,), (whole,), (2 * whole,), (whole + 3,), (whole,), (257,), (whole // R, R)]
+    tensors = _batch(R, shapes, seed=70 + R, dtype=dtype)
+    # tensor 4: views one element into larger buffers (not on a 256-byte boundary)
+    big = gen(R, whole + 1, dtype, "normal", seed=90 + R)
+    tensors[4] = [b[1:] for b in big]
+    with session(R):
+        outs = rr.all_reduce_many(tensors, op)
+        sync()
+        for t, per in enumerate(tensors):
+            hx = [host(x) for x in per]
+            want = oracle.all_reduce(hx, op)
+            single = rr.all_reduce(per, op)
+            sync()
+            for r in range(R):
+                assert_bits(host(outs[t][r]), want[r], f"tensor {t} {shapes[t]} rank {r}")
+                assert_bits(host(single[r]), host(outs[t][r]), f"batched == single, tensor {t}")
+
+
 def test_all_reduce_many_misaligned_and_repeated():
     """Tensors carved out of one buffer at odd offsets, and several batched
     calls in a row (the descriptor arena alternates and grows)."""
