@@ -74,7 +74,7 @@ class Timer:
         return self.a.elapsed_time(self.b)
 
 
-def time_calls(torch, fn, iters, warmup=2):
+def time_calls(torch, fn, iters, warmup=8):
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -85,7 +85,7 @@ def time_calls(torch, fn, iters, warmup=2):
     return t.stop_ms() / iters
 
 
-def cold_samples(torch, fn, iters, scratch, warmup=2):
+def cold_samples(torch, fn, iters, scratch, warmup=8):
     """Device time in ms of each of `iters` calls with the 256 MB Infinity
     Cache flushed first: an untimed 512 MiB scratch write precedes every call,
     and HIP events bracket the call alone."""
@@ -102,7 +102,7 @@ def cold_samples(torch, fn, iters, scratch, warmup=2):
     return [a.elapsed_time(b) for a, b in evs]
 
 
-def time_cold(torch, fn, iters, scratch, warmup=2):
+def time_cold(torch, fn, iters, scratch, warmup=8):
     """Mean of cold_samples: for rows small enough to stay cache-resident
     between back-to-back calls."""
     return sum(cold_samples(torch, fn, iters, scratch, warmup)) / iters
@@ -423,7 +423,7 @@ def rows(torch, rr, si, dev, xs8, args):
     os_ = [[torch.empty_like(x) for x in per] for per in ts]
     elems = sum(x.numel() for x in (per[0] for per in ts))
     rr.register(R4, device=0)
-    us = time_calls(torch, lambda: rr.all_reduce_many(ts, "mean", out=os_), 3, warmup=1) * 1e3
+    us = time_calls(torch, lambda: rr.all_reduce_many(ts, "mean", out=os_), 3, warmup=6) * 1e3
     row = _roof(2 * R4 * elems * 4, us)
     row.update({"tensors": len(shapes), "elems_per_rank": elems, "layers": layers})
     out[f"all_reduce_many_r4_{layers}layer_grads_f32_mean"] = row
@@ -436,7 +436,7 @@ def rows(torch, rr, si, dev, xs8, args):
         random.Random(r).shuffle(ids)
         grads.append({t: ts[t][r] for t in ids})
     outs = [{t: os_[t][r] for t in range(len(shapes))} for r in range(R4)]
-    us = time_calls(torch, lambda: rr.all_reduce_params(grads, "mean", out=outs), 3, warmup=1) * 1e3
+    us = time_calls(torch, lambda: rr.all_reduce_params(grads, "mean", out=outs), 3, warmup=6) * 1e3
     row = _roof(2 * R4 * elems * 4, us)
     row.update({"tensors": len(shapes), "elems_per_rank": elems})
     out[f"all_reduce_params_r4_{layers}layer_grads_f32_mean"] = row
@@ -449,7 +449,7 @@ def rows(torch, rr, si, dev, xs8, args):
     del outs, os_
     torch.cuda.empty_cache()
     accs = [{t: torch.empty_like(ts[t][r]).normal_(0.0, 1e-3) for t in range(len(shapes))} for r in range(R4)]
-    us = time_calls(torch, lambda: rr.all_reduce_params(grads, "mean", out=accs, acc=accs), 3, warmup=1) * 1e3
+    us = time_calls(torch, lambda: rr.all_reduce_params(grads, "mean", out=accs, acc=accs), 3, warmup=6) * 1e3
     row = _roof(3 * R4 * elems * 4, us)
     row.update({"tensors": len(shapes), "elems_per_rank": elems,
                 "bytes": "read acc and grad, write the output: 3*R*N*4"})
@@ -461,7 +461,7 @@ def rows(torch, rr, si, dev, xs8, args):
                 accs[r][t].add_(grads[r][t])
         rr.all_reduce_params(accs, "mean", out=accs)
 
-    us = time_calls(torch, separate, 3, warmup=1) * 1e3
+    us = time_calls(torch, separate, 3, warmup=6) * 1e3
     row = _roof(5 * R4 * elems * 4, us)
     row.update({"tensors": len(shapes), "elems_per_rank": elems,
                 "bytes": "torch add (2 reads, 1 write) then the sync (1 read, 1 write): 5*R*N*4"})

@@ -148,7 +148,13 @@ typedef struct rc_buf {
  *                  persistent grid of at most this many workgroups
  *   cache_hint     RC_CACHE_*
  *   waves_per_cu   cap on workgroups (one wave each) resident per compute
- *                  unit, in [1, 32]; 0: the library's choice per collective
+ *                  unit, in [1, 32]; 0: the library's choice per collective.
+ *                  With 0, launches that move 256 MiB or more are tuned
+ *                  online: the first launches of each launch shape and size
+ *                  class try three caps (two timed launches each, HIP events
+ *                  read once complete, never waited on; none while the stream
+ *                  is being captured) and later ones use the fastest.  The
+ *                  cap changes timing only, never the results.
  *   reserved       must be 0 */
 typedef struct rc_config {
     uint32_t struct_size;

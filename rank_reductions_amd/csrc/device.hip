@@ -12,6 +12,7 @@
 
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "rc_internal.h"
 
@@ -32,11 +33,27 @@ struct Arena {
     bool pending = false;    // `done` recorded after the last kernel reading it
 };
 
+// A launch timer of the occupancy tuner: start and stop events, reused.
+struct Timer {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+    bool used = false;
+};
+
 struct DeviceState {
     int device = -1;
     Arena arena[2];
     int next = 0;
+    std::vector<Timer> timers;
 } g;
+
+void free_timers() {
+    for (Timer& t : g.timers) {
+        if (t.start) (void)hipEventDestroy(t.start);
+        if (t.stop) (void)hipEventDestroy(t.stop);
+    }
+    g.timers.clear();
+}
 
 Error hip_fail(const char* what, hipError_t e) {
     return Error{RC_ERR_DEVICE, std::string(what) + ": " + hipGetErrorName(e) + " (" +
@@ -180,6 +197,7 @@ Error device_finish() {
     if (guard.err != hipSuccess) return hip_fail("hipSetDevice", guard.err);
     hipError_t e = hipDeviceSynchronize();
     for (Arena& a : g.arena) free_arena(a);
+    free_timers();
     g.device = -1;
     if (e != hipSuccess) return hip_fail("hipDeviceSynchronize", e);
     return {};
@@ -189,6 +207,7 @@ void device_reset() {
     if (g.device < 0) return;
     DeviceGuard guard;
     for (Arena& a : g.arena) free_arena(a);
+    free_timers();  // destroying a pending event is allowed: the runtime defers it
     g.device = -1;
 }
 
@@ -223,6 +242,57 @@ Error device_stream_capturing(void* stream, bool* capturing) {
     hipError_t st = hipStreamIsCapturing(static_cast<hipStream_t>(stream), &status);
     if (st != hipSuccess) return hip_fail("hipStreamIsCapturing", st);
     *capturing = status != hipStreamCaptureStatusNone;
+    return {};
+}
+
+}  // namespace rc
+
+namespace rc {
+
+Error device_timer_start(void* stream, int* ticket) {
+    DeviceGuard guard;
+    if (guard.err != hipSuccess) return hip_fail("hipSetDevice", guard.err);
+    size_t i = 0;
+    while (i < g.timers.size() && g.timers[i].used) ++i;
+    if (i == g.timers.size()) {
+        Timer t;
+        hipError_t e = hipEventCreate(&t.start);
+        if (e == hipSuccess) e = hipEventCreate(&t.stop);
+        if (e != hipSuccess) {
+            if (t.start) (void)hipEventDestroy(t.start);
+            return hip_fail("hipEventCreate", e);
+        }
+        g.timers.push_back(t);
+    }
+    const hipError_t e = hipEventRecord(g.timers[i].start, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail("hipEventRecord", e);
+    g.timers[i].used = true;
+    *ticket = (int)i;
+    return {};
+}
+
+Error device_timer_stop(int ticket, void* stream) {
+    if (ticket < 0 || ticket >= (int)g.timers.size() || !g.timers[ticket].used)
+        return Error{RC_ERR_DEVICE, "device_timer_stop: unknown ticket"};
+    const hipError_t e = hipEventRecord(g.timers[ticket].stop, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail("hipEventRecord", e);
+    return {};
+}
+
+Error device_timer_read(int ticket, bool* done, float* us) {
+    *done = false;
+    if (ticket < 0 || ticket >= (int)g.timers.size() || !g.timers[ticket].used)
+        return Error{RC_ERR_DEVICE, "device_timer_read: unknown ticket"};
+    Timer& t = g.timers[ticket];
+    hipError_t e = hipEventQuery(t.stop);
+    if (e == hipErrorNotReady) return {};
+    if (e != hipSuccess) return hip_fail("hipEventQuery", e);
+    float ms = 0.0f;
+    e = hipEventElapsedTime(&ms, t.start, t.stop);
+    if (e != hipSuccess) return hip_fail("hipEventElapsedTime", e);
+    t.used = false;
+    *done = true;
+    *us = ms * 1000.0f;
     return {};
 }
 

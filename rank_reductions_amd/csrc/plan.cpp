@@ -115,17 +115,50 @@ int auto_waves_per_cu(int nin, int nout, int unroll, const InFlightRule& rule) {
     return (int)std::min<long>(32, std::max<long>(2, w));
 }
 
-void shape_launch(int64_t total_tiles, int nin, int nout, int unroll, const Config& cfg,
-                  const DeviceInfo& dev, int64_t* grid, int* lds_bytes, const InFlightRule& rule) {
-    const int waves = cfg.waves_per_cu > 0 ? cfg.waves_per_cu : auto_waves_per_cu(nin, nout, unroll, rule);
+int lds_for_waves(const DeviceInfo& dev, int waves) {
     // One workgroup is one wave; reserving lds_per_cu / waves bytes of LDS per
     // workgroup lets at most `waves` of them sit on a CU at a time.
     int64_t lds = 0;
-    if (dev.lds_per_cu > 0 && waves < 32) {
+    if (dev.lds_per_cu > 0 && waves > 0 && waves < 32) {
         lds = (dev.lds_per_cu / waves) / 512 * 512;
         lds = std::min(lds, dev.max_lds_per_block);
     }
-    *lds_bytes = (int)std::max<int64_t>(lds, 0);
+    return (int)std::max<int64_t>(lds, 0);
+}
+
+int tune_pick(TuneEntry& t, int rule_waves, int* cand) {
+    *cand = -1;
+    if (t.ncand == 0) {
+        for (int w = rule_waves; w >= std::max(2, rule_waves - (kTuneCands - 1)); --w) t.cand[t.ncand++] = w;
+        for (int i = 0; i < t.ncand; ++i) t.best_us[i] = 0.0f;
+    }
+    if (t.chosen) return t.chosen;
+    // candidates in turn, the one with the fewest timed launches first
+    int pick = -1;
+    for (int i = 0; i < t.ncand; ++i)
+        if (t.issued[i] < kTuneSamples && (pick < 0 || t.issued[i] < t.issued[pick])) pick = i;
+    if (pick < 0) return t.cand[0];  // every sample issued, some not read yet
+    ++t.issued[pick];
+    *cand = pick;
+    return t.cand[pick];
+}
+
+void tune_record(TuneEntry& t, int cand, float us) {
+    if (cand < 0 || cand >= t.ncand || t.chosen) return;
+    if (t.got[cand] == 0 || us < t.best_us[cand]) t.best_us[cand] = us;
+    ++t.got[cand];
+    for (int i = 0; i < t.ncand; ++i)
+        if (t.got[i] < kTuneSamples) return;
+    int best = 0;  // ties keep the rule's value
+    for (int i = 1; i < t.ncand; ++i)
+        if (t.best_us[i] < t.best_us[best]) best = i;
+    t.chosen = t.cand[best];
+}
+
+void shape_launch(int64_t total_tiles, int nin, int nout, int unroll, const Config& cfg,
+                  const DeviceInfo& dev, int64_t* grid, int* lds_bytes, const InFlightRule& rule) {
+    const int waves = cfg.waves_per_cu > 0 ? cfg.waves_per_cu : auto_waves_per_cu(nin, nout, unroll, rule);
+    *lds_bytes = lds_for_waves(dev, waves);
     int64_t g = total_tiles;
     if (cfg.max_workgroups > 0) g = std::min<int64_t>(g, cfg.max_workgroups);
     *grid = std::max<int64_t>(1, std::min<int64_t>(g, 0x7FFFFFFF));
@@ -322,6 +355,7 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceI
         const int loads = lp.acc ? 2 * lp.nin : lp.nin;
         if (cfg.max_workgroups > 0) {
             shape_launch(lp.total_tiles, loads, lp.nout, lp.unroll, cfg, dev, &lp.grid, &lp.lds_bytes);
+            lp.waves = cfg.waves_per_cu > 0 ? cfg.waves_per_cu : auto_waves_per_cu(loads, lp.nout, lp.unroll);
             continue;
         }
         // one-shot: x = tiles of the longest job, y = jobs
@@ -336,6 +370,7 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceI
         // whole-tile kernels carry their own occupancy rules (fitted per shape)
         const InFlightRule& rule = !full ? kFoldRule : (ja.in_mode == kInCopy ? kCopyBatchRule : kFullFoldRule);
         shape_launch(lp.total_tiles, loads, lp.nout, lp.unroll, cfg, dev, &lp.grid, &lp.lds_bytes, rule);
+        lp.waves = cfg.waves_per_cu > 0 ? cfg.waves_per_cu : auto_waves_per_cu(loads, lp.nout, lp.unroll, rule);
         lp.args.grid_2d = 1;
         lp.args.full_tiles = full ? 1 : 0;
         lp.grid = std::max<int64_t>(1, widest);

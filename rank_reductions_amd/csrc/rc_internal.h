@@ -177,6 +177,7 @@ struct LaunchPlan {
     int64_t grid = 0;        // workgroups launched along x
     int grid_y = 1;          // along y: the jobs, for one-shot launches
     int lds_bytes = 0;       // dynamic LDS per workgroup: caps workgroups per CU
+    int waves = 0;           // workgroups (waves) per CU that lds_bytes allows; 0: no cap
 };
 
 // Builds the launches of one validated call: one for most collectives, two
@@ -244,6 +245,39 @@ void shape_launch(int64_t total_tiles, int nin, int nout, int unroll, const Conf
                   const DeviceInfo& dev, int64_t* grid, int* lds_bytes,
                   const InFlightRule& rule = kFoldRule);
 
+// LDS reservation per one-wave workgroup that lets `waves` of them share a CU.
+int lds_for_waves(const DeviceInfo& dev, int waves);
+
+// Occupancy tuner.  The fastest waves per CU for a launch shape differs
+// between otherwise identical boxes (5 on some, 7 on others for the 8-rank
+// all-reduce: 161 against 167 us and the reverse), and the wave count changes
+// timing only, never results.  So the first launches of each large shape try
+// the rule's W and the two values below it, kTuneSamples timed launches each
+// (HIP events read once they have completed, never waited on), and every
+// later launch of that shape uses the fastest.  Used when waves_per_cu is
+// left to the library, for launches that move at least kTuneMinBytes.
+constexpr int kTuneCands = 3;
+constexpr int kTuneSamples = 2;
+constexpr int64_t kTuneMinBytes = int64_t(256) << 20;
+struct TunePending {
+    int ticket;     // device timer
+    int cand;       // candidate index
+    int64_t bytes;  // bytes the timed launch moves
+};
+struct TuneEntry {
+    int ncand = 0;
+    int cand[kTuneCands] = {};
+    int issued[kTuneCands] = {};
+    int got[kTuneCands] = {};
+    float best_us[kTuneCands] = {};
+    std::vector<TunePending> pending;  // timed launches not read yet
+    int chosen = 0;  // 0 until every candidate has kTuneSamples times
+};
+// Waves per CU for the next launch of a shape whose rule gives rule_waves;
+// *cand >= 0 asks the caller to time this launch and report it to tune_record.
+int tune_pick(TuneEntry& t, int rule_waves, int* cand);
+void tune_record(TuneEntry& t, int cand, float us);
+
 // ---------------------------------------------------------------- device.hip
 // All return RC_OK or RC_ERR_DEVICE with a message.
 Error device_open(const Config& cfg, DeviceInfo* info);
@@ -258,5 +292,12 @@ Error device_event_record(void* ev, void* stream);
 Error device_stream_wait(void* stream, void* ev);
 // Whether work enqueued on `stream` is being captured into a graph.
 Error device_stream_capturing(void* stream, bool* capturing);
+// Launch timers for the occupancy tuner: a start and a stop event around
+// kernels on `stream`.  timer_read never blocks: *done stays false while
+// either event is pending; once both completed it gives the time between
+// them and releases the ticket.  device_finish / device_reset free them all.
+Error device_timer_start(void* stream, int* ticket);
+Error device_timer_stop(int ticket, void* stream);
+Error device_timer_read(int ticket, bool* done, float* us);
 
 }  // namespace rc

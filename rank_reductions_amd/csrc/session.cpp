@@ -112,7 +112,17 @@ struct Session {
     std::map<int, Comm> comms;
     int next_comm = 1;
     std::shared_ptr<RankEvents> events;
+    // occupancy tuner, per launch shape (tune_key)
+    std::map<std::tuple<int, int, int, int, int, int, int>, TuneEntry> tune;
 };
+
+// Launch shape for the occupancy tuner: kernel family, memory streams, and
+// the power of two of the bytes the launch moves.
+std::tuple<int, int, int, int, int, int, int> tune_key(const LaunchPlan& p, int64_t moved) {
+    const int size_class = 63 - __builtin_clzll((unsigned long long)std::max<int64_t>(moved, 1));
+    return std::make_tuple((int)p.args.in_mode, (int)p.args.full_tiles, p.nin, p.acc ? 1 : 0, p.nout, p.unroll,
+                           size_class);
+}
 
 std::mutex g_mu;
 std::condition_variable g_cv;
@@ -214,9 +224,53 @@ Error launch(const Checked& ck, void* stream) {
         }
         return device_launch_batch(bp, stream);
     }
-    for (const LaunchPlan& p : plan(ck, g_s.cfg, g_s.dev)) {
-        Error e = device_launch(p, stream);
+    int capturing = -1;  // asked once, when a launch could be tuned
+    for (LaunchPlan& p : plan(ck, g_s.cfg, g_s.dev)) {
+        const int64_t moved = (int64_t)(p.nin * (p.acc ? 2 : 1) + p.nout) * ck.count * element_size(ck.dtype);
+        if (g_s.cfg.waves_per_cu > 0 || g_s.cfg.max_workgroups > 0 || !p.args.grid_2d || p.waves <= 0 ||
+            moved < kTuneMinBytes) {
+            Error e = device_launch(p, stream);
+            if (e.code) return e;
+            continue;
+        }
+        if (capturing < 0) {
+            bool c = false;
+            Error e = device_stream_capturing(stream, &c);
+            if (e.code) return e;
+            capturing = c ? 1 : 0;
+        }
+        TuneEntry& t = g_s.tune[tune_key(p, moved)];
+        // read the timed launches that have completed, without waiting
+        for (size_t i = 0; i < t.pending.size();) {
+            bool done = false;
+            float us = 0.0f;
+            Error e = device_timer_read(t.pending[i].ticket, &done, &us);
+            if (e.code) return e;
+            if (done) {  // launches of one size class differ by up to 2x: compare time per GiB
+                tune_record(t, t.pending[i].cand, (float)(us * (double)(int64_t(1) << 30) / (double)t.pending[i].bytes));
+                t.pending.erase(t.pending.begin() + (std::ptrdiff_t)i);
+            } else {
+                ++i;
+            }
+        }
+        int cand = -1;
+        const int waves = tune_pick(t, p.waves, &cand);
+        if (capturing && cand >= 0) {  // a captured launch is replayed later: not timed here
+            --t.issued[cand];
+            cand = -1;
+        }
+        if (waves != p.waves) p.lds_bytes = lds_for_waves(g_s.dev, waves);
+        if (cand < 0) {
+            Error e = device_launch(p, stream);
+            if (e.code) return e;
+            continue;
+        }
+        int ticket = -1;
+        Error e = device_timer_start(stream, &ticket);
+        if (!e.code) e = device_launch(p, stream);
+        if (!e.code) e = device_timer_stop(ticket, stream);
         if (e.code) return e;
+        t.pending.push_back(TunePending{ticket, cand, moved});
     }
     return {};
 }

@@ -26,6 +26,12 @@ Error device_event_create(void**) { return Error{RC_ERR_DEVICE, "no device in th
 void device_event_destroy(void*) {}
 Error device_event_record(void*, void*) { return Error{RC_ERR_DEVICE, "no device in this test"}; }
 Error device_stream_wait(void*, void*) { return Error{RC_ERR_DEVICE, "no device in this test"}; }
+Error device_timer_start(void*, int*) { return Error{RC_ERR_DEVICE, "no device in this test"}; }
+Error device_timer_stop(int, void*) { return Error{RC_ERR_DEVICE, "no device in this test"}; }
+Error device_timer_read(int, bool* done, float*) {
+    *done = false;
+    return Error{RC_ERR_DEVICE, "no device in this test"};
+}
 Error device_stream_capturing(void*, bool* c) {
     *c = false;
     return Error{RC_ERR_DEVICE, "no device in this test"};

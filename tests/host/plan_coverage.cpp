@@ -453,6 +453,50 @@ int main(int argc, char** argv) {
         ++copies;
     }
     if (iters >= 100 && full_plans == 0) fail("no plan took the whole-tile path");
+    // occupancy tuner: candidates are the rule's W and the two below (never
+    // under 2), each timed kTuneSamples times in turn, and the fastest wins
+    // (ties keep the rule's value); nothing is timed once a value is chosen
+    for (int rule : {2, 3, 7, 10, 32}) {
+        for (int fastest = 0; fastest < kTuneCands; ++fastest) {
+            TuneEntry t;
+            std::vector<std::pair<int, int>> issued;  // (W, cand)
+            for (int call = 0; call < 3 * kTuneCands * kTuneSamples; ++call) {
+                int cand = -1;
+                const int w = tune_pick(t, rule, &cand);
+                if (w < 2 || w > rule) fail("tuner picked a wave count outside [2, rule]");
+                if (cand >= 0) {
+                    if (t.cand[cand] != w) fail("tuner candidate and wave count disagree");
+                    issued.push_back({w, cand});
+                } else if (!t.chosen && w != rule) {
+                    fail("untimed launch before the choice does not use the rule's value");
+                }
+                // read the oldest timed launch two calls late
+                if (issued.size() > 2 || (cand < 0 && !issued.empty())) {
+                    const auto s0 = issued.front();
+                    issued.erase(issued.begin());
+                    const int pos = rule - s0.first;  // 0 = rule
+                    tune_record(t, s0.second, pos == fastest ? 100.0f : 120.0f + (float)pos);
+                }
+            }
+            const int expect_n = std::min(kTuneCands, rule - 1);
+            if (t.ncand != expect_n) fail("tuner candidate count");
+            const int want = fastest < t.ncand ? rule - fastest : rule;
+            if (t.chosen != want)
+                fail("tuner chose " + std::to_string(t.chosen) + " for rule " + std::to_string(rule) + ", want " +
+                     std::to_string(want));
+            int c2 = 0;
+            if (tune_pick(t, rule, &c2) != want || c2 != -1) fail("tuner still timing after its choice");
+        }
+    }
+    {
+        TuneEntry t;  // equal times: the rule's value stays
+        int c = 0;
+        for (int i = 0; i < kTuneCands * kTuneSamples; ++i) {
+            tune_pick(t, 7, &c);
+            tune_record(t, c, 50.0f);
+        }
+        if (t.chosen != 7) fail("tuner left the rule's value on a tie");
+    }
     std::printf("checked %d plans (%d whole-tile), %d batches and %d copy batches: %d failures\n", plans, full_plans,
                 batches, copies, g_fail);
     return g_fail ? 1 : 0;

@@ -403,6 +403,22 @@ def test_all_reduce_many_own_launches(R, dtype, op):
                 assert_bits(host(single[r]), host(outs[t][r]), f"batched == single, tensor {t}")
 
 
+def test_occupancy_tuning_keeps_bits():
+    """Launches large enough for the occupancy tuner try several wave counts
+    while it measures; every call's result equals the oracle's bits, before,
+    during and after the choice, for the direct and the ring algorithm."""
+    R, N = 8, 4 * 2**20  # 2*R*N*4 = 256 MiB per all-reduce: tuned
+    xs = gen(R, N, "f32", "normal", seed=31)
+    want = oracle.all_reduce([host(x) for x in xs], "sum")
+    for algo in ("auto", "ring"):
+        with session(R, algo=algo):
+            for call in range(3 * 3 * 2 + 4):
+                outs = rr.all_reduce(xs, "sum")
+                sync()  # lets the next call read the timers
+                for r in (0, call % R):
+                    assert_bits(host(outs[r]), want[r], f"{algo} call {call} rank {r}")
+
+
 def test_all_reduce_many_misaligned_and_repeated():
     """Tensors carved out of one buffer at odd offsets, and several batched
     calls in a row (the descriptor arena alternates and grows)."""
