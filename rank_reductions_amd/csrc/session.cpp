@@ -240,8 +240,9 @@ Error launch(const Checked& ck, void* stream) {
             capturing = c ? 1 : 0;
         }
         TuneEntry& t = g_s.tune[tune_key(p, moved)];
-        // read the timed launches that have completed, without waiting
-        for (size_t i = 0; i < t.pending.size();) {
+        // read the timed launches that have completed, without waiting; a
+        // capturing call makes no event calls at all
+        for (size_t i = 0; !capturing && i < t.pending.size();) {
             bool done = false;
             float us = 0.0f;
             Error e = device_timer_read(t.pending[i].ticket, &done, &us);

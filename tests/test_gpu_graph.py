@@ -54,6 +54,35 @@ def test_replays_follow_the_inputs():
                 assert_bits(host(swapped[r]), want_a2a[r], f"replay {rep} all_to_all rank {r}")
 
 
+def test_capture_during_occupancy_tuning():
+    """An all-reduce large enough for the occupancy tuner, captured while the
+    tuner still has timed launches outstanding: the capture makes no event
+    calls, replays recompute from the current inputs, and eager calls between
+    the replays (which go on tuning) give the same bits."""
+    R, N = 8, 4 * 2**20  # 2*R*N*4 = 256 MiB moved: tuned
+    xs = si.torch_rank_inputs(R, N, "f32", "normal", 720, device=DEV)
+    outs = [torch.empty_like(x) for x in xs]
+    eager = [torch.empty_like(x) for x in xs]
+    with session(R, device=0):
+        rr.all_reduce(xs, "sum", out=outs)  # first timed launches, not read yet
+        rr.all_reduce(xs, "sum", out=outs)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            rr.all_reduce(xs, "sum", out=outs)
+        for rep in range(6):
+            fresh = si.torch_rank_inputs(R, N, "f32", "normal", 730 + rep, device=DEV)
+            for x, f in zip(xs, fresh):
+                x.copy_(f)
+            torch.cuda.synchronize()
+            g.replay()
+            rr.all_reduce(xs, "sum", out=eager)  # eager, tuning goes on
+            torch.cuda.synchronize()
+            want = oracle.all_reduce([host(x) for x in xs], "sum")
+            for r in (0, rep % R, R - 1):
+                assert_bits(host(outs[r]), want[r], f"replay {rep} rank {r}")
+                assert_bits(host(eager[r]), want[r], f"eager {rep} rank {r}")
+
+
 def test_batched_all_reduce_refuses_capture():
     R = 2
     ts = [[si.torch_tensor_for(9, t, R, r, (1000 + t,), device=DEV) for r in range(R)] for t in range(3)]
