@@ -550,6 +550,18 @@ __global__ __launch_bounds__(kBlock) void copy_args_kernel(CopyArgs a) {
                                             a.tile_elems, false);
 }
 
+// The whole-tile form of copy_args_kernel (full_tiles): job j = blockIdx.y,
+// one full round at element blockIdx.x * kBlock*kVec*U of the job.
+template <int NR, int U, bool NT>
+__global__ __launch_bounds__(kBlock) void copy_args_full_kernel(CopyArgs a) {
+    const void* const* tp = a.ptrs + blockIdx.y * (1 + NR);
+    const int64_t e0 = (int64_t)blockIdx.x * (kBlock * kVec * U);
+    const uint32_t* in[1] = {static_cast<const uint32_t*>(tp[0]) + e0};
+    const uint32_t* none[1] = {nullptr};
+    const Outs<NR> out = outs_of<NR>(const_cast<void* const*>(tp + 1), e0);
+    vec_round<1, NR, OpSumI32, U, NT, false, true>(in, none, 0, 0, out, 0xFFFFFFFFu >> (32 - NR), false);
+}
+
 // ---------------------------------------------------------------- dispatch
 
 // Vectors per lane per round: about eight 16-byte loads in flight per lane,
@@ -665,11 +677,14 @@ struct CopyBatchOf {
 };
 
 using CopyArgsFn = void (*)(CopyArgs);
-template <bool NT>
+template <bool NT, bool FULL>
 struct CopyArgsOf {
     template <int NR>
     struct At {
-        static CopyArgsFn get() { return copy_args_kernel<NR, kCopyUnroll, NT>; }
+        static CopyArgsFn get() {
+            if constexpr (FULL) return copy_args_full_kernel<NR, kCopyUnroll, NT>;
+            else return copy_args_kernel<NR, kCopyUnroll, NT>;
+        }
     };
 };
 
@@ -730,8 +745,11 @@ hipError_t launch_copy_args(const BatchPlan& p, hipStream_t stream) {
     if (!p.by_value || p.jobs.size() > (size_t)kMaxCopyArgJobs || p.ptrs.size() > (size_t)kMaxCopyArgPtrs)
         return hipErrorInvalidValue;
     const bool nt = p.nontemporal != 0;
-    CopyArgsFn fn = nt ? pick_nin<CopyArgsOf<true>::template At, CopyArgsFn>(p.nout)
-                       : pick_nin<CopyArgsOf<false>::template At, CopyArgsFn>(p.nout);
+    const bool full = p.full_tiles;
+    CopyArgsFn fn = nt ? (full ? pick_nin<CopyArgsOf<true, true>::template At, CopyArgsFn>(p.nout)
+                               : pick_nin<CopyArgsOf<true, false>::template At, CopyArgsFn>(p.nout))
+                       : (full ? pick_nin<CopyArgsOf<false, true>::template At, CopyArgsFn>(p.nout)
+                               : pick_nin<CopyArgsOf<false, false>::template At, CopyArgsFn>(p.nout));
     if (!fn) return hipErrorInvalidValue;
     CopyArgs a{};
     for (size_t i = 0; i < p.ptrs.size(); ++i) a.ptrs[i] = p.ptrs[i];

@@ -480,6 +480,7 @@ BatchPlan plan_copies(const Checked& ck, const Config& cfg, const DeviceInfo& de
     // measured: the batched copies peak at less traffic in flight than the
     // single-collective kernels (all_to_all and the list all_gather alike)
     shape_launch(tiles, 1, bp.nout, kCopyUnroll, cfg, dev, &bp.grid, &bp.lds_bytes, kCopyBatchRule);
+    bp.waves = cfg.waves_per_cu > 0 ? cfg.waves_per_cu : auto_waves_per_cu(1, bp.nout, kCopyUnroll, kCopyBatchRule);
     if (cfg.max_workgroups <= 0 && !bp.jobs.empty()) {
         // every job has the same length: a one-shot 2-D grid needs no job lookup
         int64_t widest = 0;
@@ -491,6 +492,10 @@ BatchPlan plan_copies(const Checked& ck, const Config& cfg, const DeviceInfo& de
         bp.grid = std::max<int64_t>(1, widest);
         bp.grid_y = (int)bp.jobs.size();
         bp.by_value = bp.jobs.size() <= (size_t)kMaxCopyArgJobs && bp.ptrs.size() <= (size_t)kMaxCopyArgPtrs;
+        bool full = bp.by_value && bp.tile_elems == kBlock * kVec * kCopyUnroll;
+        for (const BatchJob& jb : bp.jobs)
+            full = full && jb.phase == 0 && jb.len == bp.grid * (int64_t)bp.tile_elems;
+        bp.full_tiles = full;
     }
     return bp;
 }

@@ -206,9 +206,13 @@ struct BatchPlan {
     int grid_y = 1;     // copies of equal-length jobs: y = job, x = tile of the job
     int grid_2d = 0;
     int lds_bytes = 0;
+    int waves = 0;  // workgroups (waves) per CU that lds_bytes allows; 0: no cap
     // a copy batch small enough to pass its table in the kernel arguments
     // (no descriptor upload before the launch)
     bool by_value = false;
+    // by value, and every job whole one-round tiles on a 256-byte boundary
+    // (phase 0, len = grid * tile_elems): the whole-tile copy kernel
+    bool full_tiles = false;
 };
 // Capacity of the by-value copy table: all_to_all_single up to 12 ranks
 // (R*R jobs of 2 pointers) and every list-form all_gather (R jobs of 1+R).

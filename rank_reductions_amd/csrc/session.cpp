@@ -100,6 +100,10 @@ struct Comm {
     int size() const { return (int)world.size(); }
 };
 
+// Launch shape for the occupancy tuner: kernel family (fold, copy, copy
+// batch), whole tiles, inputs, accumulators, outputs, unroll and size class.
+using TuneKey = std::tuple<int, int, int, int, int, int, int>;
+
 struct Session {
     Mode mode = Mode::None;
     int nranks = 0;
@@ -113,16 +117,11 @@ struct Session {
     int next_comm = 1;
     std::shared_ptr<RankEvents> events;
     // occupancy tuner, per launch shape (tune_key)
-    std::map<std::tuple<int, int, int, int, int, int, int>, TuneEntry> tune;
+    std::map<TuneKey, TuneEntry> tune;
 };
 
-// Launch shape for the occupancy tuner: kernel family, memory streams, and
-// the power of two of the bytes the launch moves.
-std::tuple<int, int, int, int, int, int, int> tune_key(const LaunchPlan& p, int64_t moved) {
-    const int size_class = 63 - __builtin_clzll((unsigned long long)std::max<int64_t>(moved, 1));
-    return std::make_tuple((int)p.args.in_mode, (int)p.args.full_tiles, p.nin, p.acc ? 1 : 0, p.nout, p.unroll,
-                           size_class);
-}
+// The power of two of the bytes a launch moves (the tuner's size class).
+int size_class(int64_t moved) { return 63 - __builtin_clzll((unsigned long long)std::max<int64_t>(moved, 1)); }
 
 std::mutex g_mu;
 std::condition_variable g_cv;
@@ -210,68 +209,91 @@ void close_session() {
     g_cv.notify_all();
 }
 
+// Runs `run(lds_bytes)`, one launch whose rule allows rule_waves waves per
+// CU, under the occupancy tuner when it applies: the entry `key` picks the
+// wave count, and a launch chosen for timing is bracketed by a timer.
+// run(-1) keeps the plan's own reservation.  `capturing` caches whether
+// `stream` is being captured (-1: not asked yet).
+template <class Run>
+Error launch_tuned(const TuneKey& key, int rule_waves, int64_t moved, void* stream, int* capturing, Run run) {
+    if (g_s.cfg.waves_per_cu > 0 || g_s.cfg.max_workgroups > 0 || rule_waves <= 0 || moved < kTuneMinBytes)
+        return run(-1);
+    if (*capturing < 0) {
+        bool c = false;
+        Error e = device_stream_capturing(stream, &c);
+        if (e.code) return e;
+        *capturing = c ? 1 : 0;
+    }
+    TuneEntry& t = g_s.tune[key];
+    // read the timed launches that have completed, without waiting; a
+    // capturing call makes no event calls at all
+    for (size_t i = 0; !*capturing && i < t.pending.size();) {
+        bool done = false;
+        float us = 0.0f;
+        Error e = device_timer_read(t.pending[i].ticket, &done, &us);
+        if (e.code) return e;
+        if (done) {  // launches of one size class differ by up to 2x: compare time per GiB
+            tune_record(t, t.pending[i].cand, (float)(us * (double)(int64_t(1) << 30) / (double)t.pending[i].bytes));
+            t.pending.erase(t.pending.begin() + (std::ptrdiff_t)i);
+        } else {
+            ++i;
+        }
+    }
+    int cand = -1;
+    const int waves = tune_pick(t, rule_waves, &cand);
+    if (*capturing && cand >= 0) {  // a captured launch is replayed later: not timed here
+        --t.issued[cand];
+        cand = -1;
+    }
+    const int lds = waves == rule_waves ? -1 : lds_for_waves(g_s.dev, waves);
+    if (cand < 0) return run(lds);
+    int ticket = -1;
+    Error e = device_timer_start(stream, &ticket);
+    if (!e.code) e = run(lds);
+    if (!e.code) e = device_timer_stop(ticket, stream);
+    if (e.code) return e;
+    t.pending.push_back(TunePending{ticket, cand, moved});
+    return {};
+}
+
 Error launch(const Checked& ck, void* stream) {
+    const int64_t es = element_size(ck.dtype);
+    int capturing = -1;  // asked once, when a launch could be tuned
     if (runs_as_copies(ck.coll)) {
-        const BatchPlan bp = plan_copies(ck, g_s.cfg, g_s.dev);
+        BatchPlan bp = plan_copies(ck, g_s.cfg, g_s.dev);
         if (!bp.total_tiles) return {};
         if (!bp.by_value) {  // tables through the arena: not capturable (see launch_batch)
-            bool capturing = false;
-            Error e = device_stream_capturing(stream, &capturing);
-            if (e.code) return e;
-            if (capturing)
-                return Error{RC_ERR_INVALID_ARGUMENT, std::string(coll_name(ck.coll)) +
-                                                          " with this many ranks cannot be captured into a graph"};
-        }
-        return device_launch_batch(bp, stream);
-    }
-    int capturing = -1;  // asked once, when a launch could be tuned
-    for (LaunchPlan& p : plan(ck, g_s.cfg, g_s.dev)) {
-        const int64_t moved = (int64_t)(p.nin * (p.acc ? 2 : 1) + p.nout) * ck.count * element_size(ck.dtype);
-        if (g_s.cfg.waves_per_cu > 0 || g_s.cfg.max_workgroups > 0 || !p.args.grid_2d || p.waves <= 0 ||
-            moved < kTuneMinBytes) {
-            Error e = device_launch(p, stream);
-            if (e.code) return e;
-            continue;
-        }
-        if (capturing < 0) {
             bool c = false;
             Error e = device_stream_capturing(stream, &c);
             if (e.code) return e;
-            capturing = c ? 1 : 0;
+            if (c)
+                return Error{RC_ERR_INVALID_ARGUMENT, std::string(coll_name(ck.coll)) +
+                                                          " with this many ranks cannot be captured into a graph"};
+            return device_launch_batch(bp, stream);
         }
-        TuneEntry& t = g_s.tune[tune_key(p, moved)];
-        // read the timed launches that have completed, without waiting; a
-        // capturing call makes no event calls at all
-        for (size_t i = 0; !capturing && i < t.pending.size();) {
-            bool done = false;
-            float us = 0.0f;
-            Error e = device_timer_read(t.pending[i].ticket, &done, &us);
-            if (e.code) return e;
-            if (done) {  // launches of one size class differ by up to 2x: compare time per GiB
-                tune_record(t, t.pending[i].cand, (float)(us * (double)(int64_t(1) << 30) / (double)t.pending[i].bytes));
-                t.pending.erase(t.pending.begin() + (std::ptrdiff_t)i);
-            } else {
-                ++i;
-            }
-        }
-        int cand = -1;
-        const int waves = tune_pick(t, p.waves, &cand);
-        if (capturing && cand >= 0) {  // a captured launch is replayed later: not timed here
-            --t.issued[cand];
-            cand = -1;
-        }
-        if (waves != p.waves) p.lds_bytes = lds_for_waves(g_s.dev, waves);
-        if (cand < 0) {
+        int64_t elems = 0;  // every job reads len elements and writes them nout times
+        for (const BatchJob& jb : bp.jobs) elems += jb.len;
+        const int64_t moved = (1 + bp.nout) * elems * es;
+        const TuneKey key{2, bp.full_tiles ? 1 : 0, 1, 0, bp.nout, kCopyUnroll, size_class(moved)};
+        return launch_tuned(key, bp.waves, moved, stream, &capturing, [&](int lds) {
+            if (lds >= 0) bp.lds_bytes = lds;
+            return device_launch_batch(bp, stream);
+        });
+    }
+    for (LaunchPlan& p : plan(ck, g_s.cfg, g_s.dev)) {
+        const int64_t moved = (int64_t)(p.nin * (p.acc ? 2 : 1) + p.nout) * ck.count * es;
+        if (!p.args.grid_2d) {
             Error e = device_launch(p, stream);
             if (e.code) return e;
             continue;
         }
-        int ticket = -1;
-        Error e = device_timer_start(stream, &ticket);
-        if (!e.code) e = device_launch(p, stream);
-        if (!e.code) e = device_timer_stop(ticket, stream);
+        const TuneKey key{(int)p.args.in_mode, (int)p.args.full_tiles, p.nin, p.acc ? 1 : 0, p.nout, p.unroll,
+                          size_class(moved)};
+        Error e = launch_tuned(key, p.waves, moved, stream, &capturing, [&](int lds) {
+            if (lds >= 0) p.lds_bytes = lds;
+            return device_launch(p, stream);
+        });
         if (e.code) return e;
-        t.pending.push_back(TunePending{ticket, cand, moved});
     }
     return {};
 }

@@ -354,11 +354,13 @@ int main(int argc, char** argv) {
     // copy batches: all_to_all_single and the list form of all_gather; every
     // destination element written exactly once, every access in bounds
     int copies = 0;
+    int full_copy_batches = 0;  // copy batches on the whole-tile kernel
     for (int it = 0; it < iters / 2; ++it) {
         g_bufs.clear();
         const int R = 1 + (int)(rng() % 16);
         const bool a2a = rng() % 2;
         int64_t m = (int64_t)(rng() % 3 == 0 ? rng() % 40000 : rng() % 300);
+        if (rng() % 4 == 0) m = 2048 * (1 + (int64_t)(rng() % 3));  // whole tiles for every tile size tried
         const int mis_mode = (int)(rng() % 3);
         auto mis = [&](int r) { return mis_mode == 0 ? 0 : (mis_mode == 1 ? 1 : (r * 3 + it) % 4); };
         std::vector<rc_buf> bufs(R);
@@ -411,9 +413,13 @@ int main(int argc, char** argv) {
                 const BatchJob& jb = bp.jobs[j];
                 const int64_t own = job_tiles(jb.len, (uint8_t)jb.phase, bp.tile_elems);
                 if (own > bp.grid) fail("copy 2-D grid narrower than a job");
+                if (bp.full_tiles && (!bp.by_value || jb.phase != 0 || bp.tile_elems != kBlock * kVec * kCopyUnroll ||
+                                      jb.len != bp.grid * (int64_t)bp.tile_elems))
+                    fail("whole-tile copy batch on a job that is not whole tiles");
                 for (int64_t lt = 0; lt < bp.grid; ++lt)
-                    if (lt < own) visits.push_back({j, lt});
+                    if (bp.full_tiles || lt < own) visits.push_back({j, lt});
             }
+            if (bp.full_tiles) ++full_copy_batches;
         } else {
             const int64_t ngroups = (int64_t)bp.group_job.size();
             for (int64_t t = 0; t < bp.total_tiles; ++t) {
@@ -431,7 +437,15 @@ int main(int argc, char** argv) {
         for (const auto& v : visits) {
             const int lo = v.first;
             const BatchJob& jb = bp.jobs[lo];
-            tile_elements(jb.len, jb.phase, v.second, bp.tile_elems, kCopyUnroll, [&](int64_t el, int bytes) {
+            auto visit_copy_tile = [&](auto&& visit) {
+                if (bp.full_tiles) {  // copy_args_full_kernel: one whole round from lt*tile_elems
+                    for (int64_t el = v.second * bp.tile_elems; el < (v.second + 1) * bp.tile_elems; el += kVec)
+                        visit(el, 16);
+                } else {
+                    tile_elements(jb.len, jb.phase, v.second, bp.tile_elems, kCopyUnroll, visit);
+                }
+            };
+            visit_copy_tile([&](int64_t el, int bytes) {
                 for (int k = 0; k < per_job; ++k) {
                     const uintptr_t ad = (uintptr_t)bp.ptrs[(size_t)lo * per_job + k] + (uintptr_t)(el * 4);
                     if (!inside(ad, bytes)) fail("copy access outside its buffer");
@@ -453,6 +467,7 @@ int main(int argc, char** argv) {
         ++copies;
     }
     if (iters >= 100 && full_plans == 0) fail("no plan took the whole-tile path");
+    if (iters >= 100 && full_copy_batches == 0) fail("no copy batch took the whole-tile path");
     // occupancy tuner: candidates are the rule's W and the two below (never
     // under 2), each timed kTuneSamples times in turn, and the fastest wins
     // (ties keep the rule's value); nothing is timed once a value is chosen
@@ -497,7 +512,7 @@ int main(int argc, char** argv) {
         }
         if (t.chosen != 7) fail("tuner left the rule's value on a tie");
     }
-    std::printf("checked %d plans (%d whole-tile), %d batches and %d copy batches: %d failures\n", plans, full_plans,
-                batches, copies, g_fail);
+    std::printf("checked %d plans (%d whole-tile), %d batches and %d copy batches (%d whole-tile): %d failures\n",
+                plans, full_plans, batches, copies, full_copy_batches, g_fail);
     return g_fail ? 1 : 0;
 }

@@ -48,6 +48,46 @@ def test_all_gather_list(R, m):
             assert_bits(host(out[r][k]), want[r][k], f"R={R} m={m} rank {r} shard {k}")
 
 
+@pytest.mark.parametrize("R", [2, 8, 16])
+def test_copy_batches_whole_tiles(R):
+    """Shards of whole 512-element tiles on aligned buffers: the copy batches
+    passed by value run the whole-tile copy kernel (the all_to_all of 16 ranks
+    has too many pointers for the kernel arguments and keeps the table path)."""
+    m = 65_536
+    xs = inputs(R, m, torch.float32, 230 + R)
+    ys = inputs(R, R * m, torch.int32, 240 + R)
+    with session(R, device=0):
+        gl = rr.all_gather_list(xs)
+        a2a = rr.all_to_all_single(ys)
+        torch.cuda.synchronize()
+    want = oracle.all_gather_list([host(x) for x in xs])
+    want_a2a = oracle.all_to_all_single([host(y) for y in ys])
+    for r in range(R):
+        assert_bits(host(a2a[r]), want_a2a[r], f"all_to_all R={R} rank {r}")
+        for k in range(R):
+            assert_bits(host(gl[r][k]), want[r][k], f"all_gather_list R={R} rank {r} shard {k}")
+
+
+def test_copy_batches_keep_bits_while_tuned():
+    """Copy batches large enough for the occupancy tuner (the list all_gather
+    of 8 shards of 8 MiB, all_to_all_single of 8 x 32 MiB) through and past
+    its calibration launches: every call equals the oracle bit for bit."""
+    R, M = 8, 2 * 2**20
+    xs = inputs(R, M, torch.float32, 250)
+    ys = inputs(R, 4 * M, torch.int32, 251)
+    want = oracle.all_gather_list([host(x) for x in xs])
+    want_a2a = oracle.all_to_all_single([host(y) for y in ys])
+    with session(R, device=0):
+        for call in range(10):
+            gl = rr.all_gather_list(xs)
+            a2a = rr.all_to_all_single(ys)
+            torch.cuda.synchronize()
+            r = call % R
+            assert_bits(host(a2a[r]), want_a2a[r], f"call {call} all_to_all rank {r}")
+            for k in (0, R - 1):
+                assert_bits(host(gl[r][k]), want[r][k], f"call {call} all_gather_list rank {r} shard {k}")
+
+
 def test_all_gather_list_own_slot_in_place_i32():
     R = 4
     m = 10_001
