@@ -202,8 +202,13 @@ def main():
     dst = torch.empty_like(src)
     copy_ms = time_calls(torch, lambda: dst.copy_(src), 20)
     copy_gbps = 2 * src.numel() * 4 / (copy_ms / 1e3) / 1e9
+    # the library's own 1 -> 1 copy of the same bytes (send/recv between two
+    # ranks: the whole-tile copy kernel), on torch's current stream like the rest
+    lib_copy_ms = time_calls(torch, lambda: rr.send_recv(src, 0, 1, out=dst), 20)
+    lib_copy_gbps = 2 * src.numel() * 4 / (lib_copy_ms / 1e3) / 1e9
     del src, dst
-    log(f"bench: device copy of {R * N * 4 >> 20} MiB: {copy_ms * 1e3:.1f} us, {copy_gbps:.1f} GB/s")
+    log(f"bench: device copy of {R * N * 4 >> 20} MiB: {copy_ms * 1e3:.1f} us, {copy_gbps:.1f} GB/s; "
+        f"the library's send/recv: {lib_copy_ms * 1e3:.1f} us, {lib_copy_gbps:.1f} GB/s")
 
     # the same call timed one at a time after a cache flush: median and best
     # (skipped with --no-rows, so that a profiled run holds only the timed steps)
@@ -252,7 +257,12 @@ def main():
         },
         "hbm_frac": round(achieved / HBM_PEAK_GBPS, 4),
         "ranks_bit_identical": bool(same),
-        "copy_ceiling": {"bytes": 2 * R * N * 4, "us": round(copy_ms * 1e3, 2), "GBps": round(copy_gbps, 1)},
+        "copy_ceiling": {"bytes": 2 * R * N * 4, "us": round(copy_ms * 1e3, 2), "GBps": round(copy_gbps, 1),
+                         "what": "torch device-to-device copy of R*N fp32"},
+        "copy_ceiling_library": {"bytes": 2 * R * N * 4, "us": round(lib_copy_ms * 1e3, 2),
+                                 "GBps": round(lib_copy_gbps, 1),
+                                 "what": "send_recv of the same R*N fp32 (copy_full_kernel<1>)",
+                                 "metric_over_copy": round(achieved / lib_copy_gbps, 4)},
     }
     if cold:
         result["per_call_flushed"] = {
