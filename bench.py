@@ -25,6 +25,8 @@ import time
 from pathlib import Path
 
 ROOT = Path(__file__).resolve().parent
+# the library reports each occupancy-tuner choice on stderr
+os.environ.setdefault("RC_TUNE_LOG", "1")
 if str(ROOT) not in sys.path:
     sys.path.insert(0, str(ROOT))
 

@@ -154,7 +154,9 @@ typedef struct rc_buf {
  *                  class try three caps (two timed launches each, HIP events
  *                  read once complete, never waited on; none while the stream
  *                  is being captured) and later ones use the fastest.  The
- *                  cap changes timing only, never the results.
+ *                  cap changes timing only, never the results.  With
+ *                  RC_TUNE_LOG=1 in the environment each choice is printed
+ *                  on stderr.
  *   reserved       must be 0 */
 typedef struct rc_config {
     uint32_t struct_size;

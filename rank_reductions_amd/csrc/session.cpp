@@ -15,6 +15,8 @@
 // C++: the GPU is reached only through the device_* functions.
 #include <algorithm>
 #include <condition_variable>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <memory>
@@ -209,6 +211,30 @@ void close_session() {
     g_cv.notify_all();
 }
 
+// With RC_TUNE_LOG=1 in the environment, each choice of the occupancy tuner
+// is reported on stderr: the launch shape, the rule's wave count, and each
+// candidate's best time per GiB moved.
+void log_tune_choice(const TuneKey& key, int rule_waves, const TuneEntry& t) {
+    static const bool on = [] {
+        const char* v = std::getenv("RC_TUNE_LOG");
+        return v && std::strcmp(v, "0") != 0 && *v;
+    }();
+    if (!on) return;
+    static const char* const kinds[] = {"fold", "copy", "copy batch"};
+    const int kind = std::get<0>(key);
+    std::string line = std::string("rankred tune: ") + (kind >= 0 && kind < 3 ? kinds[kind] : "?") + " whole-tile " +
+                       std::to_string(std::get<1>(key)) + " in " + std::to_string(std::get<2>(key)) + " acc " +
+                       std::to_string(std::get<3>(key)) + " out " + std::to_string(std::get<4>(key)) + " unroll " +
+                       std::to_string(std::get<5>(key)) + " 2^" + std::to_string(std::get<6>(key)) +
+                       " B: rule W=" + std::to_string(rule_waves) + ", chose W=" + std::to_string(t.chosen) + " (";
+    for (int i = 0; i < t.ncand; ++i) {
+        char buf[64];
+        std::snprintf(buf, sizeof buf, "%sW=%d %.1f us/GiB", i ? ", " : "", t.cand[i], (double)t.best_us[i]);
+        line += buf;
+    }
+    std::fprintf(stderr, "%s)\n", line.c_str());
+}
+
 // Runs `run(lds_bytes)`, one launch whose rule allows rule_waves waves per
 // CU, under the occupancy tuner when it applies: the entry `key` picks the
 // wave count, and a launch chosen for timing is bracketed by a timer.
@@ -233,7 +259,9 @@ Error launch_tuned(const TuneKey& key, int rule_waves, int64_t moved, void* stre
         Error e = device_timer_read(t.pending[i].ticket, &done, &us);
         if (e.code) return e;
         if (done) {  // launches of one size class differ by up to 2x: compare time per GiB
+            const bool open = !t.chosen;
             tune_record(t, t.pending[i].cand, (float)(us * (double)(int64_t(1) << 30) / (double)t.pending[i].bytes));
+            if (open && t.chosen) log_tune_choice(key, rule_waves, t);
             t.pending.erase(t.pending.begin() + (std::ptrdiff_t)i);
         } else {
             ++i;
@@ -281,7 +309,10 @@ Error launch(const Checked& ck, void* stream) {
         });
     }
     for (LaunchPlan& p : plan(ck, g_s.cfg, g_s.dev)) {
-        const int64_t moved = (int64_t)(p.nin * (p.acc ? 2 : 1) + p.nout) * ck.count * es;
+        int64_t elems = 0;  // the launch's jobs: every element read from nin inputs, written nout times
+        for (int c = 0; c < p.args.jobs; ++c)
+            elems += std::max<int64_t>(0, std::min(p.args.seg, p.args.n - (int64_t)c * p.args.seg));
+        const int64_t moved = (int64_t)(p.nin * (p.acc ? 2 : 1) + p.nout) * elems * es;
         if (!p.args.grid_2d) {
             Error e = device_launch(p, stream);
             if (e.code) return e;
