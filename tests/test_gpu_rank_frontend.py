@@ -49,6 +49,39 @@ def slow_copy(src):
     return x
 
 
+def test_rank_threads_through_tuner_calibration():
+    """Eight rank threads on eight streams, calls large enough for the
+    occupancy tuner (256 MiB moved), ten in a row: the timed launches sit on
+    the launching rank's stream between the joins, and every call's result
+    is the oracle's, consumed on each rank's own stream."""
+    R, N = 8, 4 * 2**20
+    srcs = si.torch_rank_inputs(R, N, "f32", "normal", 90, device=DEV)
+    torch.cuda.synchronize()
+    want = oracle.all_reduce([host(x) for x in srcs], "sum")
+    streams = [torch.cuda.Stream() for _ in range(R)]
+    for r in range(R):
+        rr.rank_register(r, R)
+
+    def body(r):
+        outs = []
+        with torch.cuda.stream(streams[r]):
+            for _ in range(10):
+                x = slow_copy(srcs[r])
+                out = rr.rank_all_reduce(r, x, "sum", stream=streams[r])
+                outs.append(out.clone())  # consumer on the rank's stream
+        return outs
+
+    try:
+        got = run_ranks(R, body)
+        torch.cuda.synchronize()
+        for r in range(R):
+            for k, o in enumerate(got[r]):
+                assert_bits(host(o), want[r], f"call {k} rank {r}")
+    finally:
+        for r in range(R):
+            rr.rank_finish(r)
+
+
 @pytest.mark.parametrize("R,n_streams", [(2, 2), (4, 4), (8, 8), (8, 1), (6, 3)])
 def test_rank_threads_all_reduce(R, n_streams):
     """Rank r on stream r mod n_streams: own streams, one shared stream (no
