@@ -91,6 +91,43 @@ def test_all_reduce_sweep(R, dtype, op, algo):
             check_unchanged(xs, hx, f"R={R} N={N}")
 
 
+@pytest.mark.parametrize("R", RANKS)
+@pytest.mark.parametrize("dtype,op", OPS)
+def test_whole_tile_collectives(R, dtype, op):
+    """Sizes whose ring segments are whole tiles on 256-byte boundaries (every
+    unroll the ranks use): all_reduce (direct and ring), reduce, reduce_scatter,
+    all_gather and broadcast run the whole-tile kernels; bits against the
+    oracle, inputs unchanged."""
+    N = R * 8192  # a multiple of 256 * U elements per segment for every U
+    dist = "int" if dtype == "i32" else "normal"
+    xs = gen(R, N, dtype, dist, seed=4000 + 10 * R + OPS.index((dtype, op)))
+    hx = [host(x).copy() for x in xs]
+    want = oracle.all_reduce_closed_form(hx, op)
+    for algo in ("direct", "ring"):
+        with session(R, algo=algo):
+            outs = rr.all_reduce(xs, op)
+            sync()
+            for r in range(R):
+                assert_bits(host(outs[r]), want, f"all_reduce {algo} R={R} {dtype} {op} rank {r}")
+    with session(R):
+        root = R // 2
+        red = rr.reduce(xs, root, op)
+        shards = rr.reduce_scatter(xs, op)
+        sync()
+        assert_bits(host(red[root]), want, f"reduce R={R} {dtype} {op}")
+        for r in range(R):
+            assert_bits(host(shards[r]), want[r * 8192:(r + 1) * 8192], f"reduce_scatter R={R} {op} rank {r}")
+        gathered = rr.all_gather(shards)
+        sends = [xs[r] if r == R - 1 else None for r in range(R)]
+        bc = rr.broadcast(sends)
+        sync()
+        for r in range(R):
+            assert_bits(host(gathered[r]), want, f"all_gather R={R} {op} rank {r}")
+            if r != R - 1:  # the sender's own output is not asked for
+                assert_bits(host(bc[r]), hx[R - 1], f"broadcast R={R} rank {r}")
+    check_unchanged(xs, hx, f"whole tiles R={R}")
+
+
 @pytest.mark.parametrize("R", [2, 4, 8])
 def test_all_reduce_matches_ring_simulation(R):
     """The closed form used above equals the oracle's message-by-message ring."""
