@@ -166,6 +166,23 @@ def test_params_accumulated(R, op):
     check(got, want, f"accumulated R={R} {op}")
 
 
+@pytest.mark.parametrize("R", [2, 3, 8])
+def test_params_accumulated_whole_tiles(R):
+    """Parameters large enough for launches of their own whose ring segments
+    are whole tiles (the whole-tile fold with accumulators) next to one that
+    is not, for rank counts whose unroll differs from 4 ranks'."""
+    seg = {2: 2**21, 3: 2**20, 8: 2**17}[R]  # elements per segment: whole tiles, 64 MiB+ moved
+    specs = {11: (R * seg,), 12: (R, seg), 13: (R * seg + 5,), 14: (300,)}
+    maps = make_maps(R, specs, seed=120 + R)
+    accs = make_accs(maps, [11, 12, 13, 14], seed=130 + R)
+    torch.cuda.synchronize()
+    want = oracle.all_reduce_params(host_maps(maps), "mean", acc=host_maps(accs))
+    with session(R, device=0):
+        got = rr.all_reduce_params(maps, "mean", acc=accs)
+        torch.cuda.synchronize()
+    check(got, want, f"accumulated whole tiles R={R}")
+
+
 @pytest.mark.parametrize("algo", ["direct", "ring"])
 def test_params_accumulated_own_launch_in_place(algo):
     """A parameter large enough for its own fold launch (direct, or the ring's
