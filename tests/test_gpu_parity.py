@@ -194,6 +194,24 @@ def test_schedule_invariance():
                     assert_bits(host(outs[r]), want[op], f"{cfg} {op} rank {r}")
 
 
+def test_schedule_invariance_whole_tiles():
+    """At a whole-tile size the default launch runs the whole-tile kernels
+    (non-temporal or, with cache_hint normal, cached accesses), larger tiles
+    or a workgroup cap the general ones: the same bits from each."""
+    R, N = 8, 8 * 65536
+    xs = gen(R, N, "f32", "normal", seed=19)
+    hx = [host(x) for x in xs]
+    want = {op: oracle.all_reduce_closed_form(hx, op) for op in ("sum", "mean", "max")}
+    for cfg in (dict(), dict(cache_hint="normal"), dict(tile_elems=4096), dict(max_workgroups=7),
+                dict(algo="ring"), dict(algo="ring", cache_hint="normal"), dict(waves_per_cu=3)):
+        with session(R, **cfg):
+            for op in ("sum", "mean", "max"):
+                outs = rr.all_reduce(xs, op)
+                sync()
+                for r in range(R):
+                    assert_bits(host(outs[r]), want[op], f"{cfg} {op} rank {r}")
+
+
 def test_special_values():
     """Subnormals are kept (no flush to zero); Max follows the NaN and signed
     zero rules."""
