@@ -572,9 +572,12 @@ constexpr int kUnroll = unroll_for(ACC ? 2 * NIN : NIN);
 using FoldFn = void (*)(JobArgs);
 using BatchFn = void (*)(BatchArgs);
 
-template <int NIN, class Op, bool NT, bool ACC, bool FULL>
+// U1: the whole-tile 4-rank all-reduce with one vector per lane (the planner
+// halves its tiles); every other launch uses kUnroll.
+template <int NIN, class Op, bool NT, bool ACC, bool FULL, bool U1>
 FoldFn fold_ptr() {
-    if constexpr (FULL) return fold_full_kernel<NIN, Op, kUnroll<NIN, ACC>, NT, ACC>;
+    if constexpr (FULL && U1 && NIN == 4 && !ACC) return fold_full_kernel<NIN, Op, 1, NT, ACC>;
+    else if constexpr (FULL) return fold_full_kernel<NIN, Op, kUnroll<NIN, ACC>, NT, ACC>;
     else return fold_kernel<NIN, Op, kUnroll<NIN, ACC>, NT, ACC>;
 }
 template <int NIN, class Op, bool NT, bool ACC>
@@ -620,11 +623,11 @@ FoldFn pick_copy(int nranks) {
     return pick_nin<CopyOf<NT, FULL>::template At, FoldFn>(nranks);
 }
 
-template <class Op, bool NT, bool ACC, bool FULL>
+template <class Op, bool NT, bool ACC, bool FULL, bool U1>
 struct FoldOf {
     template <int NIN>
     struct At {
-        static FoldFn get() { return fold_ptr<NIN, Op, NT, ACC, FULL>(); }
+        static FoldFn get() { return fold_ptr<NIN, Op, NT, ACC, FULL, U1>(); }
     };
 };
 template <class Op, bool NT, bool ACC>
@@ -636,20 +639,20 @@ struct BatchOf {
 };
 
 // Accumulators exist for Sum and Mean only (validation refuses Max).
-template <bool NT, bool ACC, bool FULL>
+template <bool NT, bool ACC, bool FULL, bool U1>
 FoldFn pick_fold_op(int dtype, int op, int nin) {
     if (dtype == RC_F32) {
         if (op == RC_MAX) {
             if constexpr (ACC) return nullptr;
-            else return pick_nin<FoldOf<OpMaxF32, NT, false, FULL>::template At, FoldFn>(nin);
+            else return pick_nin<FoldOf<OpMaxF32, NT, false, FULL, U1>::template At, FoldFn>(nin);
         }
-        return pick_nin<FoldOf<OpSumF32, NT, ACC, FULL>::template At, FoldFn>(nin);
+        return pick_nin<FoldOf<OpSumF32, NT, ACC, FULL, U1>::template At, FoldFn>(nin);
     }
     if (op == RC_MAX) {
         if constexpr (ACC) return nullptr;
-        else return pick_nin<FoldOf<OpMaxI32, NT, false, FULL>::template At, FoldFn>(nin);
+        else return pick_nin<FoldOf<OpMaxI32, NT, false, FULL, U1>::template At, FoldFn>(nin);
     }
-    return pick_nin<FoldOf<OpSumI32, NT, ACC, FULL>::template At, FoldFn>(nin);
+    return pick_nin<FoldOf<OpSumI32, NT, ACC, FULL, U1>::template At, FoldFn>(nin);
 }
 
 template <bool NT, bool ACC>
@@ -689,8 +692,12 @@ struct CopyArgsOf {
 };
 
 template <bool NT, bool FULL>
-FoldFn pick_fold_any(int dtype, int op, int nin, bool acc) {
-    return acc ? pick_fold_op<NT, true, FULL>(dtype, op, nin) : pick_fold_op<NT, false, FULL>(dtype, op, nin);
+FoldFn pick_fold_any(int dtype, int op, int nin, bool acc, bool u1) {
+    if (acc) return pick_fold_op<NT, true, FULL, false>(dtype, op, nin);
+    if constexpr (FULL) {
+        if (u1) return pick_fold_op<NT, false, true, true>(dtype, op, nin);
+    }
+    return pick_fold_op<NT, false, FULL, false>(dtype, op, nin);
 }
 template <bool NT>
 BatchFn pick_batch_any(int dtype, int op, int nin, bool acc) {
@@ -708,10 +715,13 @@ hipError_t launch_jobs(const LaunchPlan& p, hipStream_t stream) {
         fn = nt ? (full ? pick_copy<true, true>(nr) : pick_copy<true, false>(nr))
                 : (full ? pick_copy<false, true>(nr) : pick_copy<false, false>(nr));
     } else {
-        fn = nt ? (full ? pick_fold_any<true, true>(p.dtype, p.op, p.nin, p.acc)
-                        : pick_fold_any<true, false>(p.dtype, p.op, p.nin, p.acc))
-                : (full ? pick_fold_any<false, true>(p.dtype, p.op, p.nin, p.acc)
-                        : pick_fold_any<false, false>(p.dtype, p.op, p.nin, p.acc));
+        // the one-vector 4-rank whole-tile all-reduce (see plan)
+        const bool u1 = full && !p.acc && p.nin == 4 && p.unroll == 1;
+        if (!full && p.unroll != kUnroll<4, false> && p.nin == 4 && !p.acc) return hipErrorInvalidValue;
+        fn = nt ? (full ? pick_fold_any<true, true>(p.dtype, p.op, p.nin, p.acc, u1)
+                        : pick_fold_any<true, false>(p.dtype, p.op, p.nin, p.acc, false))
+                : (full ? pick_fold_any<false, true>(p.dtype, p.op, p.nin, p.acc, u1)
+                        : pick_fold_any<false, false>(p.dtype, p.op, p.nin, p.acc, false));
     }
     if (!fn) return hipErrorInvalidValue;
     hipLaunchKernelGGL(fn, dim3(p.grid, p.grid_y), dim3(kBlock), p.lds_bytes, stream, p.args);

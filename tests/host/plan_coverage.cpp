@@ -275,6 +275,24 @@ int main(int argc, char** argv) {
             if (p.args.full_tiles) ++full_plans;
         }
     }
+    {
+        // the 4-rank whole-tile all-reduce runs one vector per lane: its plan
+        // replays like any other, with tiles of 256 elements
+        g_bufs.clear();
+        const int R = 4;
+        const int64_t n = (int64_t)R * 4096 * 3;
+        std::vector<rc_buf> bufs(R);
+        for (int r = 0; r < R; ++r) bufs[r] = make((void*)alloc(n * 4, 0), (void*)alloc(n * 4, 0), n);
+        Checked ck;
+        if (validate(Coll::AllReduce, R, bufs.data(), &ck).code) fail("4-rank all-reduce rejected");
+        Config cfg;
+        for (const LaunchPlan& p : plan(ck, cfg, dev)) {
+            check_plan(p, "4-rank whole-tile all-reduce");
+            ++plans;
+            if (!p.args.full_tiles || p.unroll != 1 || p.args.tile_elems != kBlock * kVec)
+                fail("4-rank whole-tile all-reduce does not run one vector per lane");
+        }
+    }
     // batched plans: job lookup through the group index, and coverage
     int batches = 0;
     for (int it = 0; it < iters / 3; ++it) {
