@@ -572,11 +572,11 @@ constexpr int kUnroll = unroll_for(ACC ? 2 * NIN : NIN);
 using FoldFn = void (*)(JobArgs);
 using BatchFn = void (*)(BatchArgs);
 
-// U1: the whole-tile 4-rank all-reduce with one vector per lane (the planner
-// halves its tiles); every other launch uses kUnroll.
+// U1: the whole-tile all-reduce of 4-7 ranks with one vector per lane (the
+// planner halves its tiles); every other launch uses kUnroll.
 template <int NIN, class Op, bool NT, bool ACC, bool FULL, bool U1>
 FoldFn fold_ptr() {
-    if constexpr (FULL && U1 && NIN == 4 && !ACC) return fold_full_kernel<NIN, Op, 1, NT, ACC>;
+    if constexpr (FULL && U1 && NIN >= 4 && NIN < 8 && !ACC) return fold_full_kernel<NIN, Op, 1, NT, ACC>;
     else if constexpr (FULL) return fold_full_kernel<NIN, Op, kUnroll<NIN, ACC>, NT, ACC>;
     else return fold_kernel<NIN, Op, kUnroll<NIN, ACC>, NT, ACC>;
 }
@@ -715,9 +715,10 @@ hipError_t launch_jobs(const LaunchPlan& p, hipStream_t stream) {
         fn = nt ? (full ? pick_copy<true, true>(nr) : pick_copy<true, false>(nr))
                 : (full ? pick_copy<false, true>(nr) : pick_copy<false, false>(nr));
     } else {
-        // the one-vector 4-rank whole-tile all-reduce (see plan)
-        const bool u1 = full && !p.acc && p.nin == 4 && p.unroll == 1;
-        if (!full && p.unroll != kUnroll<4, false> && p.nin == 4 && !p.acc) return hipErrorInvalidValue;
+        // the one-vector whole-tile all-reduce of 4-7 ranks (see plan)
+        const bool mid = !p.acc && p.nin >= 4 && p.nin < 8;
+        const bool u1 = full && mid && p.unroll == 1;
+        if (mid && !full && p.unroll != 2) return hipErrorInvalidValue;  // no general kernel with one vector
         fn = nt ? (full ? pick_fold_any<true, true>(p.dtype, p.op, p.nin, p.acc, u1)
                         : pick_fold_any<true, false>(p.dtype, p.op, p.nin, p.acc, false))
                 : (full ? pick_fold_any<false, true>(p.dtype, p.op, p.nin, p.acc, u1)

@@ -371,12 +371,15 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceI
         const InFlightRule& rule = !full ? kFoldRule : (ja.in_mode == kInCopy ? kCopyBatchRule : kFullFoldRule);
         shape_launch(lp.total_tiles, loads, lp.nout, lp.unroll, cfg, dev, &lp.grid, &lp.lds_bytes, rule);
         lp.waves = cfg.waves_per_cu > 0 ? cfg.waves_per_cu : auto_waves_per_cu(loads, lp.nout, lp.unroll, rule);
-        // A whole-tile 4-rank all-reduce runs one vector per lane: measured on
-        // three boxes, 82.1-82.2 us per 4 x 64 MiB at W=7 against 83.3-83.6
-        // at the best W with two.  Whole tiles of two vectors are whole tiles
-        // of one; the wave count stays the two-vector rule's (7).
-        if (full && ja.in_mode == kInFold && !lp.acc && lp.nin == 4 && lp.nout == 4 && lp.unroll == 2 &&
-            cfg.tile_elems <= 0) {
+        // A whole-tile all-reduce of 4-7 ranks runs one vector per lane:
+        // 4 x 64 MiB 82.1-82.2 us at W=7 against 83.3-83.6 at the best W with
+        // two (three boxes); 5, 6 and 7 ranks of 2^21 elements per segment
+        // 64.2 / 93.0 / 126.6 us against 66.8 / 96.7 / 131.9.  Whole tiles of
+        // two vectors are whole tiles of one, and the two-vector rule's wave
+        // count (7, 6, 5, 4) is where one vector peaks.  A reduce to one
+        // output stays at two (26.5 against 27.8 us for 4 ranks).
+        if (full && ja.in_mode == kInFold && !lp.acc && lp.nin >= 4 && lp.nin < 8 && lp.nout == lp.nin &&
+            lp.unroll == 2 && cfg.tile_elems <= 0) {
             lp.unroll = 1;
             lp.args.tile_elems /= 2;
             for (int c = 0; c <= kMaxRanks; ++c) lp.args.tile_prefix[c] *= 2;

@@ -276,21 +276,22 @@ int main(int argc, char** argv) {
         }
     }
     {
-        // the 4-rank whole-tile all-reduce runs one vector per lane: its plan
-        // replays like any other, with tiles of 256 elements
+        // whole-tile all-reduces of 4-7 ranks run one vector per lane: their
+        // plans replay like any other, with tiles of 256 elements
+        for (int R = 4; R < 8; ++R) {
         g_bufs.clear();
-        const int R = 4;
         const int64_t n = (int64_t)R * 4096 * 3;
         std::vector<rc_buf> bufs(R);
         for (int r = 0; r < R; ++r) bufs[r] = make((void*)alloc(n * 4, 0), (void*)alloc(n * 4, 0), n);
         Checked ck;
-        if (validate(Coll::AllReduce, R, bufs.data(), &ck).code) fail("4-rank all-reduce rejected");
+        if (validate(Coll::AllReduce, R, bufs.data(), &ck).code) fail("all-reduce rejected");
         Config cfg;
         for (const LaunchPlan& p : plan(ck, cfg, dev)) {
-            check_plan(p, "4-rank whole-tile all-reduce");
+            check_plan(p, "whole-tile all-reduce of " + std::to_string(R) + " ranks");
             ++plans;
             if (!p.args.full_tiles || p.unroll != 1 || p.args.tile_elems != kBlock * kVec)
-                fail("4-rank whole-tile all-reduce does not run one vector per lane");
+                fail("whole-tile all-reduce of 4-7 ranks does not run one vector per lane");
+        }
         }
     }
     // batched plans: job lookup through the group index, and coverage
