@@ -32,7 +32,11 @@ if str(ROOT) not in sys.path:
 
 METRIC = "all_reduce algbw GB/s, fp32, R=8 ranks, 64 MiB/rank; % of HBM peak"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
-KERNEL_SOURCE = ROOT / "rank_reductions_amd" / "csrc" / "kernels.hip"
+CSRC = ROOT / "rank_reductions_amd" / "csrc"
+# the sources that decide what the kernels compile to (a traffic summary
+# applies to the kernels it was taken on only)
+KERNEL_SOURCES = [CSRC / n for n in ("tiling.h", "kernels_impl.h", "kernels_fold.hip", "kernels_batch.hip",
+                                     "kernels_copy.hip")]
 TRAFFIC_FILE = ROOT / "profiles" / "traffic_fold_r8_f32_sum_64MiB.txt"
 
 
@@ -111,7 +115,10 @@ def time_cold(torch, fn, iters, scratch, warmup=8):
 
 
 def kernels_sha():
-    return hashlib.sha256(KERNEL_SOURCE.read_bytes()).hexdigest()
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(p.name.encode() + b"\0" + p.read_bytes())
+    return h.hexdigest()
 
 
 def read_traffic():

@@ -298,6 +298,29 @@ def _ptr(t):
     return p if p or t.numel() else _EMPTY_ADDR
 
 
+def _expect(out, ref, numel, what):
+    """Checks an output tensor the library writes `numel` elements of ref's
+    dtype into: the C ABI carries the input's shape only, so an undersized or
+    mistyped output would be written past its end or misread.  Raises
+    CollectiveError before anything is launched."""
+    if out is None:
+        raise CollectiveError(RC_ERR_INVALID_ARGUMENT, f"{what}: no output tensor")
+    if out.dtype != ref.dtype:
+        raise CollectiveError(RC_ERR_DTYPE_MISMATCH, f"{what}: output dtype {out.dtype}, input dtype {ref.dtype}")
+    if out.numel() != numel:
+        raise CollectiveError(RC_ERR_SHAPE_MISMATCH,
+                              f"{what}: output holds {out.numel()} elements, the call writes {numel}")
+    if out.device != ref.device:
+        raise CollectiveError(RC_ERR_INVALID_ARGUMENT, f"{what}: output on {out.device}, input on {ref.device}")
+    if not out.is_contiguous():
+        raise CollectiveError(RC_ERR_INVALID_ARGUMENT, f"{what}: output is not contiguous")
+
+
+def _expect_list(outs, n, what):
+    if len(outs) != n:
+        raise CollectiveError(RC_ERR_INVALID_ARGUMENT, f"{what}: {len(outs)} outputs for {n} ranks")
+
+
 def _stream(stream, ref):
     if stream is not None:
         return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -331,6 +354,9 @@ def all_reduce(xs, op="sum", out=None, stream=None):
     torch = _torch()
     if out is None:
         out = [torch.empty_like(x) for x in xs]
+    _expect_list(out, len(xs), "all_reduce")
+    for r, (x, o) in enumerate(zip(xs, out)):
+        _expect(o, x, x.numel(), f"all_reduce rank {r}")
     _call(library().rc_all_reduce, xs, out, _op(op), 0, stream)
     return out
 
@@ -340,6 +366,9 @@ def reduce(xs, root, op="sum", out=None, stream=None):
     torch = _torch()
     if out is None:
         out = [torch.empty_like(xs[root]) if r == root else None for r in range(len(xs))]
+    _expect_list(out, len(xs), "reduce")
+    if 0 <= root < len(xs):  # a root out of range is the library's to report
+        _expect(out[root], xs[root], xs[root].numel(), f"reduce root {root}")
     _call(library().rc_reduce, xs, out, _op(op), root, stream)
     return out
 
@@ -354,6 +383,10 @@ def broadcast(sends, out=None, stream=None, root=-1):
         raise CollectiveError(RC_ERR_BROADCAST_SENDERS, "broadcast needs one sender tensor")
     if out is None:
         out = [torch.empty_like(ref) if s is None else None for s in sends]
+    _expect_list(out, len(sends), "broadcast")
+    for r, (snd, o) in enumerate(zip(sends, out)):
+        if o is not None and (snd is None or o is not snd):
+            _expect(o, ref, ref.numel(), f"broadcast rank {r}")
     _call(library().rc_broadcast, sends, out, RC_SUM, root, stream)
     return out
 
@@ -365,6 +398,10 @@ def reduce_scatter(xs, op="sum", out=None, stream=None):
     R = len(xs)
     if out is None:
         out = [torch.empty(x.numel() // R, dtype=x.dtype, device=x.device) for x in xs]
+    _expect_list(out, R, "reduce_scatter")
+    for r, (x, o) in enumerate(zip(xs, out)):
+        if x.numel() % R == 0:  # an indivisible count is the library's to report
+            _expect(o, x, x.numel() // R, f"reduce_scatter rank {r}")
     _call(library().rc_reduce_scatter, xs, out, _op(op), 0, stream)
     return out
 
@@ -376,14 +413,23 @@ def all_gather(shards, out=None, stream=None):
     R = len(shards)
     if out is None:
         out = [torch.empty(R * s.numel(), dtype=s.dtype, device=s.device) for s in shards]
+    _expect_list(out, R, "all_gather")
+    for r, (x, o) in enumerate(zip(shards, out)):
+        _expect(o, x, R * x.numel(), f"all_gather rank {r}")
     _call(library().rc_all_gather, shards, out, RC_SUM, 0, stream)
     return out
 
 
 def batch_bufs(tensors, outs, op):
-    """rc_buf rows [num_tensors][num_ranks] as a numpy structured array."""
+    """rc_buf rows [num_tensors][num_ranks] as a numpy structured array; every
+    output is checked against its input first."""
     T = len(tensors)
     R = len(tensors[0]) if T else 0
+    _expect_list(outs, T, "batched all_reduce (tensors)")
+    for t in range(T):
+        _expect_list(outs[t], len(tensors[t]), f"batched all_reduce tensor {t}")
+        for r in range(len(tensors[t])):
+            _expect(outs[t][r], tensors[t][r], tensors[t][r].numel(), f"batched all_reduce tensor {t} rank {r}")
     arr = np.zeros(T * R, dtype=RCBUF_NP)
     k = 0
     for t in range(T):
@@ -423,6 +469,11 @@ def all_gather_list(shards, out=None, stream=None):
     R = len(shards)
     if out is None:
         out = [[torch.empty_like(shards[k]) for k in range(R)] for _ in range(R)]
+    _expect_list(out, R, "all_gather_list")
+    for r in range(R):
+        _expect_list(out[r], R, f"all_gather_list rank {r}")
+        for k in range(R):
+            _expect(out[r][k], shards[k], shards[k].numel(), f"all_gather_list rank {r} shard {k}")
     bufs = make_bufs([_ptr(x) for x in shards], [None] * R, [tuple(x.shape) for x in shards],
                      [_dtype_code(x) for x in shards])
     recvs = (ctypes.c_void_p * (R * R))(*[_ptr(out[r][k]) for r in range(R) for k in range(R)])
@@ -437,6 +488,9 @@ def all_to_all_single(xs, out=None, stream=None):
     torch = _torch()
     if out is None:
         out = [torch.empty_like(x) for x in xs]
+    _expect_list(out, len(xs), "all_to_all_single")
+    for r, (x, o) in enumerate(zip(xs, out)):
+        _expect(o, x, x.numel(), f"all_to_all_single rank {r}")
     _call(library().rc_all_to_all_single, xs, out, stream=stream)
     return out
 
@@ -447,6 +501,7 @@ def send_recv(x, src, dst, out=None, stream=None):
     torch = _torch()
     if out is None:
         out = torch.empty_like(x)
+    _expect(out, x, x.numel(), "send_recv")
     bufs = make_bufs([_ptr(x), None], [None, _ptr(out)], [tuple(x.shape), tuple(out.shape)],
                      [_dtype_code(x), _dtype_code(out)])
     check(library().rc_send_recv(int(src), int(dst), ctypes.cast(bufs, ctypes.c_void_p),
@@ -461,9 +516,17 @@ def barrier(stream=None):
 
 
 def _param_entries(grads, outs, op, acc=None):
-    """One rank's map as an rc_param array (in the map's order) and its length."""
+    """One rank's map as an rc_param array (in the map's order) and its length;
+    outputs and accumulators are checked against their gradients first."""
     keys = list(grads)
     n = len(keys)
+    for k in keys:
+        if k not in outs:
+            raise CollectiveError(RC_ERR_INVALID_ARGUMENT, f"all_reduce_params: no output for parameter {k}")
+        _expect(outs[k], grads[k], grads[k].numel(), f"all_reduce_params output of parameter {k}")
+        a = acc.get(k) if acc else None
+        if a is not None:
+            _expect(a, grads[k], grads[k].numel(), f"all_reduce_params accumulator of parameter {k}")
     arr = (RcParam * max(n, 1))()
     if n:
         bufs = make_bufs([_ptr(grads[k]) for k in keys], [_ptr(outs[k]) for k in keys],
@@ -541,6 +604,7 @@ def rank_all_reduce(rank, x, op="sum", out=None, stream=None):
     torch = _torch()
     if out is None:
         out = torch.empty_like(x)
+    _expect(out, x, x.numel(), "rank_all_reduce")
     _rank_call(library().rc_rank_all_reduce, rank, x, out, _op(op), 0, stream)
     return out
 
@@ -550,12 +614,16 @@ def rank_reduce(rank, x, root, op="sum", out=None, stream=None):
     torch = _torch()
     if out is None and int(rank) % RC_MAX_RANKS == root:
         out = torch.empty_like(x)
+    if out is not None and int(rank) % RC_MAX_RANKS == root:
+        _expect(out, x, x.numel(), "rank_reduce root")
     _rank_call(library().rc_rank_reduce, rank, x, out, _op(op), root, stream)
     return out
 
 
 def rank_broadcast(rank, x=None, out=None, stream=None, root=-1):
-    """The sender passes x; receivers pass x=None and an `out` tensor."""
+    """The sender passes x; receivers pass x=None and an `out` tensor (its
+    size and dtype are checked against the sender's by the library only
+    through the shapes the ranks pass, which must agree)."""
     _rank_call(library().rc_rank_broadcast, rank, x, out, RC_SUM, root, stream)
     return out
 
@@ -564,6 +632,8 @@ def rank_reduce_scatter(rank, x, num_ranks, op="sum", out=None, stream=None):
     torch = _torch()
     if out is None:
         out = torch.empty(x.numel() // num_ranks, dtype=x.dtype, device=x.device)
+    if x.numel() % num_ranks == 0:
+        _expect(out, x, x.numel() // num_ranks, "rank_reduce_scatter")
     _rank_call(library().rc_rank_reduce_scatter, rank, x, out, _op(op), 0, stream)
     return out
 
@@ -572,6 +642,7 @@ def rank_all_gather(rank, shard, num_ranks, out=None, stream=None):
     torch = _torch()
     if out is None:
         out = torch.empty(num_ranks * shard.numel(), dtype=shard.dtype, device=shard.device)
+    _expect(out, shard, num_ranks * shard.numel(), "rank_all_gather")
     _rank_call(library().rc_rank_all_gather, rank, shard, out, RC_SUM, 0, stream)
     return out
 
@@ -593,6 +664,9 @@ def rank_all_gather_list(rank, shard, num_ranks, out=None, stream=None):
     torch = _torch()
     if out is None:
         out = [torch.empty_like(shard) for _ in range(num_ranks)]
+    _expect_list(out, num_ranks, "rank_all_gather_list")
+    for k, o in enumerate(out):
+        _expect(o, shard, shard.numel(), f"rank_all_gather_list output {k}")
     bufs = make_bufs([_ptr(shard)], [None], [tuple(shard.shape)], [_dtype_code(shard)])
     recvs = (ctypes.c_void_p * num_ranks)(*[_ptr(o) for o in out])
     check(library().rc_rank_all_gather_list(int(rank), ctypes.cast(bufs, ctypes.c_void_p), recvs,
@@ -604,6 +678,7 @@ def rank_all_to_all_single(rank, x, out=None, stream=None):
     torch = _torch()
     if out is None:
         out = torch.empty_like(x)
+    _expect(out, x, x.numel(), "rank_all_to_all_single")
     _rank_call(library().rc_rank_all_to_all_single, rank, x, out, RC_SUM, 0, stream)
     return out
 

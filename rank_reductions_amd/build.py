@@ -21,7 +21,19 @@ BUILD = PKG / "_build"
 LIB = PKG / "librankred.so"
 
 HOST_SOURCES = ["session.cpp", "validate.cpp", "plan.cpp"]
-HIP_SOURCES = ["kernels.hip", "device.hip"]
+# (source, object, defines): the fold and batch kernels are built once per
+# element type and cache hint, so that their instantiations compile in parallel
+RC_F32, RC_I32 = 0, 1
+HIP_SOURCES = [
+    ("kernels_fold.hip", "kernels_fold_f32_nt", {"RC_KDT": RC_F32, "RC_KNT": 1}),
+    ("kernels_fold.hip", "kernels_fold_f32_cached", {"RC_KDT": RC_F32, "RC_KNT": 0}),
+    ("kernels_fold.hip", "kernels_fold_i32_nt", {"RC_KDT": RC_I32, "RC_KNT": 1}),
+    ("kernels_fold.hip", "kernels_fold_i32_cached", {"RC_KDT": RC_I32, "RC_KNT": 0}),
+    ("kernels_batch.hip", "kernels_batch_nt", {"RC_KNT": 1}),
+    ("kernels_batch.hip", "kernels_batch_cached", {"RC_KNT": 0}),
+    ("kernels_copy.hip", "kernels_copy", {}),
+    ("device.hip", "device", {}),
+]
 
 ARCH = "gfx950"
 
@@ -66,11 +78,14 @@ def build(verbose=False, extra_hip_flags=()):
         obj = BUILD / (src + ".o")
         jobs.append([cxx, *HOST_FLAGS, *inc, "-c", CSRC / src, "-o", obj])
         objs.append(obj)
-    for src in HIP_SOURCES:
-        obj = BUILD / (src + ".o")
-        jobs.append([hipcc, *HIP_FLAGS, *extra_hip_flags, *inc, "-c", CSRC / src, "-o", obj])
+    for src, name, defines in HIP_SOURCES:
+        obj = BUILD / (name + ".o")
+        dflags = [f"-D{k}={v}" for k, v in defines.items()]
+        jobs.append([hipcc, *HIP_FLAGS, *extra_hip_flags, *dflags, *inc, "-c", CSRC / src, "-o", obj])
         objs.append(obj)
-    with ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as ex:
+    # the largest objects first, so the pool ends together
+    jobs.sort(key=lambda c: 0 if "kernels_fold.hip" in str(c) else 1)
+    with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 8, 16)) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))
     tmp = LIB.with_suffix(".so.tmp")
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)

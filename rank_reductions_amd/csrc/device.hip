@@ -10,6 +10,7 @@
 // in the kernel arguments instead and need no upload.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -18,12 +19,67 @@
 
 namespace rc {
 
-hipError_t launch_jobs(const LaunchPlan& p, hipStream_t stream);
-hipError_t launch_copy_args(const BatchPlan& p, hipStream_t stream);
-hipError_t launch_batch(const BatchJob* jobs, const int32_t* group_job, const void* const* ptrs,
-                        const BatchPlan& p, hipStream_t stream);
-
 namespace {
+
+// ---------------------------------------------------------------- launches
+
+hipError_t launch_jobs(const LaunchPlan& p, hipStream_t stream) {
+    const bool nt = p.args.nontemporal != 0;
+    const bool full = p.args.full_tiles != 0;
+    FoldFn fn;
+    if (p.args.in_mode == kInCopy) {
+        fn = copy_fn(nt, full, p.args.nranks);
+    } else {
+        // the one-vector whole-tile all-reduce of 4-7 ranks (see plan)
+        const bool mid = !p.acc && p.nin >= 4 && p.nin < 8;
+        const bool u1 = full && mid && p.unroll == 1;
+        if (mid && !full && p.unroll != 2) return hipErrorInvalidValue;  // no general kernel with one vector
+        if (p.dtype == RC_F32) fn = nt ? fold_fn_f32_nt(p.op, p.acc, full, u1, p.nin)
+                                       : fold_fn_f32_cached(p.op, p.acc, full, u1, p.nin);
+        else fn = nt ? fold_fn_i32_nt(p.op, p.acc, full, u1, p.nin) : fold_fn_i32_cached(p.op, p.acc, full, u1, p.nin);
+    }
+    if (!fn) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fn, dim3(p.grid, p.grid_y), dim3(kBlock), p.lds_bytes, stream, p.args);
+    return hipGetLastError();
+}
+
+hipError_t launch_batch(const BatchJob* jobs, const int32_t* group_job, const void* const* ptrs,
+                        const BatchPlan& p, hipStream_t stream) {
+    const bool nt = p.nontemporal != 0;
+    BatchFn fn;
+    if (p.copy) fn = copy_batch_fn(nt, p.nout);
+    else fn = nt ? batch_fn_nt(p.dtype, p.op, p.acc, p.nranks) : batch_fn_cached(p.dtype, p.op, p.acc, p.nranks);
+    if (!fn) return hipErrorInvalidValue;
+    BatchArgs a;
+    a.jobs = jobs;
+    a.group_job = group_job;
+    a.ptrs = ptrs;
+    a.total_tiles = p.total_tiles;
+    a.ngroups = (int64_t)p.group_job.size();
+    a.njobs = (int32_t)p.jobs.size();
+    a.tile_elems = p.tile_elems;
+    a.mean = p.op == RC_MEAN ? 1 : 0;
+    a.grid_2d = p.grid_2d;
+    hipLaunchKernelGGL(fn, dim3(p.grid, p.grid_y), dim3(kBlock), p.lds_bytes, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_args(const BatchPlan& p, hipStream_t stream) {
+    if (!p.by_value || p.jobs.size() > (size_t)kMaxCopyArgJobs || p.ptrs.size() > (size_t)kMaxCopyArgPtrs)
+        return hipErrorInvalidValue;
+    CopyArgsFn fn = copy_args_fn(p.nontemporal != 0, p.full_tiles, p.nout);
+    if (!fn) return hipErrorInvalidValue;
+    CopyArgs a{};
+    for (size_t i = 0; i < p.ptrs.size(); ++i) a.ptrs[i] = p.ptrs[i];
+    a.len = p.jobs[0].len;
+    a.tile_elems = p.tile_elems;
+    for (size_t j = 0; j < p.jobs.size(); ++j) {
+        if (p.jobs[j].len != a.len) return hipErrorInvalidValue;  // equal lengths only
+        a.phase[j] = (uint8_t)p.jobs[j].phase;
+    }
+    hipLaunchKernelGGL(fn, dim3(p.grid, p.grid_y), dim3(kBlock), p.lds_bytes, stream, a);
+    return hipGetLastError();
+}
 
 struct Arena {
     void* host = nullptr;    // pinned staging
@@ -112,6 +168,41 @@ Error ensure_arena(Arena& a, size_t bytes) {
     return {};
 }
 
+// Where a batch's tables sit in its descriptor block: [jobs][group index]
+// [pointer table], each 256-byte aligned.
+struct TableLayout {
+    size_t group_off;
+    size_t ptr_off;
+    size_t bytes;
+};
+
+TableLayout table_layout(const BatchPlan& p) {
+    auto align = [](size_t v) { return (v + 255) & ~size_t(255); };
+    TableLayout t;
+    t.group_off = align(p.jobs.size() * sizeof(BatchJob));
+    t.ptr_off = align(t.group_off + p.group_job.size() * sizeof(int32_t));
+    t.bytes = t.ptr_off + p.ptrs.size() * sizeof(void*);
+    return t;
+}
+
+// Bytes [off, off + n) of a batch's descriptor block into dst (the gaps
+// between the tables are zero).
+void read_tables(const BatchPlan& p, const TableLayout& t, size_t off, size_t n, char* dst) {
+    std::memset(dst, 0, n);
+    const struct {
+        const void* src;
+        size_t at, len;
+    } parts[3] = {{p.jobs.data(), 0, p.jobs.size() * sizeof(BatchJob)},
+                  {p.group_job.data(), t.group_off, p.group_job.size() * sizeof(int32_t)},
+                  {p.ptrs.data(), t.ptr_off, p.ptrs.size() * sizeof(void*)}};
+    for (const auto& q : parts) {
+        const size_t lo = std::max(off, q.at), hi = std::min(off + n, q.at + q.len);
+        if (lo < hi) std::memcpy(dst + (lo - off), static_cast<const char*>(q.src) + (lo - q.at), hi - lo);
+    }
+}
+
+void write_tables(const BatchPlan& p, const TableLayout& t, char* dst) { read_tables(p, t, 0, t.bytes, dst); }
+
 }  // namespace
 
 Error device_open(const Config& cfg, DeviceInfo* info) {
@@ -163,27 +254,16 @@ Error device_launch_batch(const BatchPlan& p, void* stream) {
     Arena& a = g.arena[g.next];
     Error err = wait_arena(a);
     if (err.code) return err;
-    // arena layout: [jobs][group index][pointer table], each 256-byte aligned
-    auto align = [](size_t v) { return (v + 255) & ~size_t(255); };
-    const size_t job_bytes = p.jobs.size() * sizeof(BatchJob);
-    const size_t group_off = align(job_bytes);
-    const size_t group_bytes = p.group_job.size() * sizeof(int32_t);
-    const size_t ptr_off = align(group_off + group_bytes);
-    const size_t bytes = ptr_off + p.ptrs.size() * sizeof(void*);
-    err = ensure_arena(a, bytes);
+    const TableLayout t = table_layout(p);
+    err = ensure_arena(a, t.bytes);
     if (err.code) return err;
-    char* host = static_cast<char*>(a.host);
-    std::memcpy(host, p.jobs.data(), job_bytes);
-    std::memcpy(host + group_off, p.group_job.data(), group_bytes);
-    std::memcpy(host + ptr_off, p.ptrs.data(), p.ptrs.size() * sizeof(void*));
+    write_tables(p, t, static_cast<char*>(a.host));
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = hipMemcpyAsync(a.dev, a.host, bytes, hipMemcpyHostToDevice, s);
+    hipError_t e = hipMemcpyAsync(a.dev, a.host, t.bytes, hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return hip_fail("hipMemcpyAsync", e);
     const char* dev = static_cast<const char*>(a.dev);
-    const BatchJob* jobs = reinterpret_cast<const BatchJob*>(dev);
-    const int32_t* group_job = reinterpret_cast<const int32_t*>(dev + group_off);
-    const void* const* ptrs = reinterpret_cast<const void* const*>(dev + ptr_off);
-    e = launch_batch(jobs, group_job, ptrs, p, s);
+    e = launch_batch(reinterpret_cast<const BatchJob*>(dev), reinterpret_cast<const int32_t*>(dev + t.group_off),
+                     reinterpret_cast<const void* const*>(dev + t.ptr_off), p, s);
     if (e != hipSuccess) return hip_fail("kernel launch", e);
     e = hipEventRecord(a.done, s);
     if (e != hipSuccess) return hip_fail("hipEventRecord", e);

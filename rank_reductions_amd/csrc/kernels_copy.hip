@@ -1,0 +1,59 @@
+// Copy kernels (broadcast, all_gather, the ring's all-gather phase,
+// send/recv, all_to_all_single, the list form of all_gather).
+#include "kernels_impl.h"
+
+namespace rc {
+namespace {
+
+template <bool NT, bool FULL>
+struct CopyOf {
+    template <int NR>
+    struct At {
+        static FoldFn get() {
+            if constexpr (FULL) return copy_full_kernel<NR, kCopyUnroll, NT>;
+            else return copy_kernel<NR, kCopyUnroll, NT>;
+        }
+    };
+};
+
+template <bool NT>
+struct CopyBatchOf {
+    template <int NR>
+    struct At {
+        static BatchFn get() { return copy_batch_kernel<NR, kCopyUnroll, NT>; }
+    };
+};
+
+template <bool NT, bool FULL>
+struct CopyArgsOf {
+    template <int NR>
+    struct At {
+        static CopyArgsFn get() {
+            if constexpr (FULL) return copy_args_full_kernel<NR, kCopyUnroll, NT>;
+            else return copy_args_kernel<NR, kCopyUnroll, NT>;
+        }
+    };
+};
+
+}  // namespace
+
+FoldFn copy_fn(bool nt, bool full, int nr) {
+    if (nt) return full ? pick_nin<CopyOf<true, true>::template At, FoldFn>(nr)
+                        : pick_nin<CopyOf<true, false>::template At, FoldFn>(nr);
+    return full ? pick_nin<CopyOf<false, true>::template At, FoldFn>(nr)
+                : pick_nin<CopyOf<false, false>::template At, FoldFn>(nr);
+}
+
+BatchFn copy_batch_fn(bool nt, int nr) {
+    return nt ? pick_nin<CopyBatchOf<true>::template At, BatchFn>(nr)
+              : pick_nin<CopyBatchOf<false>::template At, BatchFn>(nr);
+}
+
+CopyArgsFn copy_args_fn(bool nt, bool full, int nr) {
+    if (nt) return full ? pick_nin<CopyArgsOf<true, true>::template At, CopyArgsFn>(nr)
+                        : pick_nin<CopyArgsOf<true, false>::template At, CopyArgsFn>(nr);
+    return full ? pick_nin<CopyArgsOf<false, true>::template At, CopyArgsFn>(nr)
+                : pick_nin<CopyArgsOf<false, false>::template At, CopyArgsFn>(nr);
+}
+
+}  // namespace rc

@@ -1,4 +1,5 @@
-// Reduction and fan-out kernels for gfx950 (CDNA4, wave64).
+// Reduction and fan-out kernels for gfx950 (CDNA4, wave64): device code shared
+// by the kernel translation units, each of which instantiates one family.
 //
 // Every collective is a list of jobs; a job is one ring segment c of one
 // tensor.  A job either folds R inputs element by element, in the rank order
@@ -9,12 +10,16 @@
 //
 // The work is HBM streaming with no reuse: 16-byte vector loads and stores per
 // lane, R loads in flight per vector, non-temporal hints by default.  A job's
-// elements split into a scalar head (until every pointer of the job is 16-byte
+// elements split into a scalar head (until its reference stream is 16-byte
 // aligned), a body of 16-byte vectors, and a scalar tail (fewer than 4
-// elements); head and tail are done by the lanes of the job's first tile.
-// Jobs whose pointers disagree modulo 16 bytes run element by element.
-// Each element is read and written by exactly one lane, and there are no
-// atomics, so the summation order is the documented one whatever the grid.
+// elements); head and tail are done by the lanes of the job's first tile
+// (tiling.h).  Streams that are not aligned like the reference are accessed
+// with the same 16-byte instructions at 4-byte aligned addresses, which the
+// HSA runtime's unaligned access mode serves.  Each element is read and
+// written by exactly one lane, and there are no atomics, so the summation
+// order is the documented one whatever the grid.
+#pragma once
+
 #include <hip/hip_runtime.h>
 
 #include "rc_internal.h"
@@ -24,7 +29,9 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+// the memory view of a 16-byte vector: 4-byte alignment, so that streams off
+// the reference's 16-byte grid use the same instructions
+typedef uint32_t u32x4m __attribute__((ext_vector_type(4), aligned(4)));
 
 __device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t as_u(float f) { return __builtin_bit_cast(uint32_t, f); }
@@ -34,9 +41,7 @@ __device__ __forceinline__ uint32_t as_u(float f) { return __builtin_bit_cast(ui
 
 struct OpSumF32 {
     static constexpr bool kCanMean = true;
-    __device__ __forceinline__ static uint32_t apply(uint32_t a, uint32_t b) {
-        return as_u(as_f(a) + as_f(b));
-    }
+    __device__ __forceinline__ static uint32_t apply(uint32_t a, uint32_t b) { return as_u(as_f(a) + as_f(b)); }
     __device__ __forceinline__ static u32x4 apply4(u32x4 a, u32x4 b) {
         f32x4 r = __builtin_bit_cast(f32x4, a) + __builtin_bit_cast(f32x4, b);
         return __builtin_bit_cast(u32x4, r);
@@ -52,7 +57,7 @@ struct OpSumI32 {  // two's-complement wrap: unsigned add
 struct OpMaxI32 {
     static constexpr bool kCanMean = false;
     __device__ __forceinline__ static uint32_t apply(uint32_t a, uint32_t b) {
-        int32_t x = (int32_t)a, y = (int32_t)b;
+        const int32_t x = (int32_t)a, y = (int32_t)b;
         return (uint32_t)(x > y ? x : y);
     }
     __device__ __forceinline__ static u32x4 apply4(u32x4 a, u32x4 b) {
@@ -72,7 +77,7 @@ struct OpMaxI32 {
 struct OpMaxF32 {
     static constexpr bool kCanMean = false;
     __device__ __forceinline__ static uint32_t apply(uint32_t a, uint32_t b) {
-        float x = as_f(a), y = as_f(b);
+        const float x = as_f(a), y = as_f(b);
         if (x != x || y != y) return 0x7FC00000u;
         if (x == y) return a & b;
         return x > y ? a : b;
@@ -104,13 +109,14 @@ __device__ __forceinline__ u32x4 mean4(u32x4 acc) {
 
 template <bool NT>
 __device__ __forceinline__ u32x4 ld4(const uint32_t* p) {
-    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    else return *reinterpret_cast<const u32x4*>(p);
+    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4m*>(p));
+    else return *reinterpret_cast<const u32x4m*>(p);
 }
 template <bool NT>
 __device__ __forceinline__ void st4(uint32_t* p, u32x4 v) {
-    if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
-    else *reinterpret_cast<u32x4*>(p) = v;
+    const u32x4m w = v;
+    if constexpr (NT) __builtin_nontemporal_store(w, reinterpret_cast<u32x4m*>(p));
+    else *reinterpret_cast<u32x4m*>(p) = w;
 }
 template <bool NT>
 __device__ __forceinline__ uint32_t ld1(const uint32_t* p) {
@@ -168,8 +174,9 @@ __device__ __forceinline__ Outs<NR> outs_of(void* const* ptrs, int64_t off) {
     return r;
 }
 
-// With ACC, operand k is acc[k] + in[k] (an accumulator plus the last
-// gradient, one add per element with the reduction's Sum), added before the fold.
+// One scalar element.  With ACC, operand k is acc[k] + in[k] (an accumulator
+// plus the last gradient, one add per element with the reduction's Sum),
+// added before the fold.
 template <int NIN, int NR, class Op, bool NT, bool ACC, class OutF>
 __device__ __forceinline__ void element(const uint32_t* const (&in)[NIN], const uint32_t* const (&ac)[NIN],
                                         int64_t e, const OutF& out, uint32_t mask, bool mean) {
@@ -190,40 +197,6 @@ __device__ __forceinline__ void element(const uint32_t* const (&in)[NIN], const 
 #pragma unroll
     for (int o = 0; o < NR; ++o)
         if ((mask >> o) & 1u) st1<NT>(out(o) + e, acc);
-}
-
-// The element-by-element path in rounds: J elements per lane, kBlock apart
-// (each a coalesced 256-byte run across the wave), all loads issued before
-// the folds, so that as many bytes are in flight as in a vector round.
-template <int NIN, int NR, class Op, int J, bool NT, bool ACC, class OutF>
-__device__ __forceinline__ void element_round(const uint32_t* const (&in)[NIN], const uint32_t* const (&ac)[NIN],
-                                              int64_t e, const OutF& out, uint32_t mask, bool mean) {
-    constexpr int NA = ACC ? NIN : 1;
-    uint32_t x[J][NIN];
-    uint32_t y[J][NA];
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-#pragma unroll
-        for (int k = 0; k < NIN; ++k) x[j][k] = ld1<NT>(in[k] + e + j * kBlock);
-        if constexpr (ACC) {
-#pragma unroll
-            for (int k = 0; k < NIN; ++k) y[j][k] = ld1<NT>(ac[k] + e + j * kBlock);
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-        if constexpr (ACC) {
-#pragma unroll
-            for (int k = 0; k < NIN; ++k) x[j][k] = op2<Op>(y[j][k], x[j][k]);
-        }
-        uint32_t acc = fold<NIN, Op>(x[j]);
-        if constexpr (Op::kCanMean) {
-            if (mean) acc = mean1<NIN>(acc);
-        }
-#pragma unroll
-        for (int o = 0; o < NR; ++o)
-            if ((mask >> o) & 1u) st1<NT>(out(o) + e + j * kBlock, acc);
-    }
 }
 
 // One round: U vectors per lane.  in[k] + off and out(o) + off are uniform
@@ -276,101 +249,58 @@ __device__ __forceinline__ void vec_round(const uint32_t* const (&in)[NIN], cons
     }
 }
 
-// Tile lt of a job of `len` elements.
+// Tile lt of a job of `len` elements: its vectors in rounds of U per lane,
+// and on tile 0 the job's scalar head and tail.
 template <int NIN, int NR, class Op, int U, bool NT, bool ACC, class OutF>
 __device__ __forceinline__ void job_tile(const uint32_t* const (&in)[NIN], const uint32_t* const (&ac)[NIN],
-                                         const OutF& out, uint32_t mask, int64_t len, int phase, int64_t lt,
+                                         const OutF& out, uint32_t mask, int64_t len, uint8_t phase, int64_t lt,
                                          int64_t te, bool mean) {
-    const int tid = threadIdx.x;
-    if (phase == kScalarOnly) {
-        // full rounds of 4U elements per lane (a tile holds a whole number of
-        // them), then the last tile's remainder one element per lane at a time
-        constexpr int J = 4 * U;
-        const int64_t e0 = lt * te;
-        const int64_t e1 = e0 + te < len ? e0 + te : len;
-        int64_t e = e0;
-        for (; e + (int64_t)J * kBlock <= e1; e += (int64_t)J * kBlock)
-            element_round<NIN, NR, Op, J, NT, ACC>(in, ac, e + tid, out, mask, mean);
-        for (e += tid; e < e1; e += kBlock) element<NIN, NR, Op, NT, ACC>(in, ac, e, out, mask, mean);
-        return;
-    }
-    const int64_t h = phase_head((uint8_t)phase);
-    const int64_t head = h < len ? h : len;
-    const int64_t nvec = (len - head) / kVec;
-    const int64_t tail0 = head + nvec * kVec;
-    const int64_t tv = te / kVec;
-    // a non-zero lead makes tile 0 the lead vectors alone; tile t >= 1 starts
-    // at vector lead + (t-1)*tv, on a kTileAlignBytes boundary
-    const int64_t l = phase_lead((uint8_t)phase);
-    const int64_t lead = l < nvec ? l : nvec;
-    const int64_t shift = lead > 0 ? lead - tv : 0;
-    const int64_t v0 = lt * tv + shift > 0 ? lt * tv + shift : 0;
-    const int64_t v1 = (lt + 1) * tv + shift < nvec ? (lt + 1) * tv + shift : nvec;
+    const JobSplit s = job_split(len, phase, te);
+    int64_t v0, v1;
+    tile_vectors(s, lt, &v0, &v1);
     constexpr int64_t kStep = (int64_t)kBlock * U;
     for (int64_t vb = v0; vb < v1; vb += kStep) {
-        const int64_t off = head + vb * kVec;
+        const int64_t off = s.head + vb * kVec;
         if (v1 - vb >= kStep) vec_round<NIN, NR, Op, U, NT, ACC, true>(in, ac, off, 0, out, mask, mean);
         else vec_round<NIN, NR, Op, U, NT, ACC, false>(in, ac, off, (uint32_t)(v1 - vb), out, mask, mean);
     }
-    if (lt == 0 && (head > 0 || tail0 < len)) {
-        const int64_t nscal = head + (len - tail0);  // at most 3 + 3
-        if (tid < nscal) {
-            const int64_t e = tid < head ? tid : tail0 + (tid - head);
-            element<NIN, NR, Op, NT, ACC>(in, ac, e, out, mask, mean);
-        }
+    if (lt == 0) {
+        const int64_t lane = threadIdx.x;
+        if (lane < scalars_of(s, len)) element<NIN, NR, Op, NT, ACC>(in, ac, scalar_elem(s, lane), out, mask, mean);
     }
 }
 
 // ---------------------------------------------------------------- kernels
 
-// Job holding tile t: the number of job boundaries at or below t.  Entries of
-// tile_prefix past the last job equal the tile total, which t never reaches.
-__device__ __forceinline__ int job_of(const JobArgs& a, int t) {
-    int c = 0;
-#pragma unroll
-    for (int j = 1; j < kMaxRanks; ++j) c += t >= a.tile_prefix[j] ? 1 : 0;
-    return c;
-}
-
-__device__ __forceinline__ uint32_t out_mask_of(const JobArgs& a, int c) {
-    uint32_t mask = a.out_mask;
-    if (a.out_mode == kOutOwner) mask = 1u << c;
-    else if (a.out_mode == kOutMaskButOwner) mask &= ~(1u << c);
-    return mask;
-}
-
-// Tile lt of fold job c: input k is rank (c+1+k) mod R at element c*in_stride
-// (with ACC, plus that rank's accumulator at the same element).
+// Tile lt of fold job c: operand k is rank fold_rank(c, k) at element
+// c*in_stride (with ACC, plus that rank's accumulator at the same element).
 template <int NIN, class Op, int U, bool NT, bool ACC>
 __device__ __forceinline__ void fold_tile(const JobArgs& a, int c, int lt) {
-    const int64_t start = (int64_t)c * a.seg;
-    const int64_t len = a.n - start < a.seg ? a.n - start : a.seg;
+    const int64_t len = job_len(a.n, a.seg, c);
     const int64_t ioff = (int64_t)c * a.in_stride;
     const uint32_t* in[NIN];
     const uint32_t* ac[NIN];
 #pragma unroll
     for (int k = 0; k < NIN; ++k) {
-        int r = c + 1 + k;  // c < NIN, so r < 2 * NIN
-        r = r >= NIN ? r - NIN : r;
+        const int r = fold_rank(c, k, NIN);
         in[k] = static_cast<const uint32_t*>(a.in[r]) + ioff;
         ac[k] = ACC ? static_cast<const uint32_t*>(a.acc[r]) + ioff : nullptr;
     }
     const Outs<NIN> out = outs_of<NIN>(a.out, (int64_t)c * a.out_stride);
-    job_tile<NIN, NIN, Op, U, NT, ACC>(in, ac, out, out_mask_of(a, c), len, a.phase[c], lt, a.tile_elems,
-                                       a.mean != 0);
+    job_tile<NIN, NIN, Op, U, NT, ACC>(in, ac, out, out_mask_of(a.out_mode, a.out_mask, c), len, a.phase[c], lt,
+                                       a.tile_elems, a.mean != 0);
 }
 
 // Tile lt of copy job c: in[c] at element c*in_stride, copied bit for bit to
 // the outputs of up to NR ranks.
 template <int NR, int U, bool NT>
 __device__ __forceinline__ void copy_tile(const JobArgs& a, int c, int lt) {
-    const int64_t start = (int64_t)c * a.seg;
-    const int64_t len = a.n - start < a.seg ? a.n - start : a.seg;
+    const int64_t len = job_len(a.n, a.seg, c);
     const uint32_t* in[1] = {static_cast<const uint32_t*>(a.in[c]) + (int64_t)c * a.in_stride};
     const uint32_t* none[1] = {nullptr};
     const Outs<NR> out = outs_of<NR>(a.out, (int64_t)c * a.out_stride);
-    job_tile<1, NR, OpSumI32, U, NT, false>(in, none, out, out_mask_of(a, c), len, a.phase[c], lt,
-                                            a.tile_elems, false);
+    job_tile<1, NR, OpSumI32, U, NT, false>(in, none, out, out_mask_of(a.out_mode, a.out_mask, c), len, a.phase[c],
+                                            lt, a.tile_elems, false);
 }
 
 // Whole-tile launches (full_tiles): every job has phase 0 and exactly
@@ -388,13 +318,13 @@ __global__ __launch_bounds__(kBlock) void fold_full_kernel(JobArgs a) {
     const uint32_t* ac[NIN];
 #pragma unroll
     for (int k = 0; k < NIN; ++k) {
-        int r = c + 1 + k;
-        r = r >= NIN ? r - NIN : r;
+        const int r = fold_rank(c, k, NIN);
         in[k] = static_cast<const uint32_t*>(a.in[r]) + ioff;
         ac[k] = ACC ? static_cast<const uint32_t*>(a.acc[r]) + ioff : nullptr;
     }
     const Outs<NIN> out = outs_of<NIN>(a.out, (int64_t)c * a.out_stride + e0);
-    vec_round<NIN, NIN, Op, U, NT, ACC, true>(in, ac, 0, 0, out, out_mask_of(a, c), a.mean != 0);
+    vec_round<NIN, NIN, Op, U, NT, ACC, true>(in, ac, 0, 0, out, out_mask_of(a.out_mode, a.out_mask, c),
+                                             a.mean != 0);
 }
 
 template <int NR, int U, bool NT>
@@ -404,7 +334,8 @@ __global__ __launch_bounds__(kBlock) void copy_full_kernel(JobArgs a) {
     const uint32_t* in[1] = {static_cast<const uint32_t*>(a.in[c]) + (int64_t)c * a.in_stride + e0};
     const uint32_t* none[1] = {nullptr};
     const Outs<NR> out = outs_of<NR>(a.out, (int64_t)c * a.out_stride + e0);
-    vec_round<1, NR, OpSumI32, U, NT, false, true>(in, none, 0, 0, out, out_mask_of(a, c), false);
+    vec_round<1, NR, OpSumI32, U, NT, false, true>(in, none, 0, 0, out, out_mask_of(a.out_mode, a.out_mask, c),
+                                                   false);
 }
 
 // Launch shapes: one-shot launches use a 2-D grid, blockIdx.y = job and
@@ -419,7 +350,7 @@ __global__ __launch_bounds__(kBlock) void fold_kernel(JobArgs a) {
         return;
     }
     for (int t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
-        const int c = job_of(a, t);
+        const int c = job_of(a.tile_prefix, t);
         fold_tile<NIN, Op, U, NT, ACC>(a, c, t - a.tile_prefix[c]);
     }
 }
@@ -433,44 +364,18 @@ __global__ __launch_bounds__(kBlock) void copy_kernel(JobArgs a) {
         return;
     }
     for (int t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
-        const int c = job_of(a, t);
+        const int c = job_of(a.tile_prefix, t);
         copy_tile<NR, U, NT>(a, c, t - a.tile_prefix[c]);
     }
 }
 
-// Batched all-reduce over a job table in device memory.  A tile's job lies
-// between the jobs that hold the first tiles of its group and of the next
-// group (group_job); a binary search over that range, usually empty, finds it.
-struct BatchArgs {
-    const BatchJob* jobs;
-    const int32_t* group_job;
-    const void* const* ptrs;  // [job][2R], or [job][3R] with ACC: operands, accumulators, outputs
-    int64_t total_tiles;
-    int64_t ngroups;
-    int32_t njobs;
-    int32_t tile_elems;
-    int32_t mean;
-    int32_t grid_2d;  // copies: y = job, x = tile of the job
-};
-
-__device__ __forceinline__ int find_job(const BatchArgs& a, int64_t t) {
-    const int64_t g = t >> kGroupShift;
-    int lo = a.group_job[g];
-    int hi = g + 1 < a.ngroups ? a.group_job[g + 1] : a.njobs - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (a.jobs[mid].tile_begin <= t) lo = mid;
-        else hi = mid - 1;
-    }
-    return lo;
-}
-
+// Batched all-reduce over a job table in device memory (find_job, tiling.h).
 template <int NIN, class Op, int U, bool NT, bool ACC>
 __global__ __launch_bounds__(kBlock) void batch_kernel(BatchArgs a) {
     constexpr int kPtrs = (ACC ? 3 : 2) * NIN;
     constexpr int kOut = (ACC ? 2 : 1) * NIN;
     for (int64_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
-        const int j = find_job(a, t);
+        const int j = find_job(a.jobs, a.group_job, a.ngroups, a.njobs, t);
         const BatchJob jb = a.jobs[j];
         const void* const* tp = a.ptrs + (int64_t)j * kPtrs;
         const uint32_t* in[NIN];
@@ -481,8 +386,8 @@ __global__ __launch_bounds__(kBlock) void batch_kernel(BatchArgs a) {
             ac[k] = ACC ? static_cast<const uint32_t*>(tp[NIN + k]) : nullptr;
         }
         const Outs<NIN> out = outs_of<NIN>(const_cast<void* const*>(tp + kOut), 0);
-        job_tile<NIN, NIN, Op, U, NT, ACC>(in, ac, out, (1u << NIN) - 1u, jb.len, jb.phase, t - jb.tile_begin,
-                                           a.tile_elems, a.mean != 0);
+        job_tile<NIN, NIN, Op, U, NT, ACC>(in, ac, out, (1u << NIN) - 1u, jb.len, (uint8_t)jb.phase,
+                                           t - jb.tile_begin, a.tile_elems, a.mean != 0);
     }
 }
 
@@ -495,21 +400,8 @@ __device__ __forceinline__ void copy_job_tile(const BatchArgs& a, int j, int64_t
     const uint32_t* in[1] = {static_cast<const uint32_t*>(tp[0])};
     const uint32_t* none[1] = {nullptr};
     const Outs<NR> out = outs_of<NR>(const_cast<void* const*>(tp + 1), 0);
-    job_tile<1, NR, OpSumI32, U, NT, false>(in, none, out, (1u << NR) - 1u, jb.len, jb.phase, lt, a.tile_elems,
-                                            false);
-}
-
-// Tiles of a job of `len` elements with alignment phase `phase` (as planned).
-__device__ __forceinline__ int64_t tiles_of(int64_t len, int phase, int64_t te) {
-    if (phase == kScalarOnly) return (len + te - 1) / te;
-    const int64_t h = phase_head((uint8_t)phase);
-    const int64_t head = h < len ? h : len;
-    const int64_t nvec = (len - head) / kVec;
-    const int64_t l = phase_lead((uint8_t)phase);
-    const int64_t lead = l < nvec ? l : nvec;
-    const int64_t tv = te / kVec;
-    const int64_t t = (lead > 0 ? 1 : 0) + (nvec - lead + tv - 1) / tv;
-    return t > 1 ? t : 1;
+    job_tile<1, NR, OpSumI32, U, NT, false>(in, none, out, (1u << NR) - 1u, jb.len, (uint8_t)jb.phase, lt,
+                                            a.tile_elems, false);
 }
 
 template <int NR, int U, bool NT>
@@ -517,11 +409,11 @@ __global__ __launch_bounds__(kBlock) void copy_batch_kernel(BatchArgs a) {
     if (a.grid_2d) {
         const int j = blockIdx.y;
         const BatchJob jb = a.jobs[j];
-        if (blockIdx.x < tiles_of(jb.len, jb.phase, a.tile_elems)) copy_job_tile<NR, U, NT>(a, j, blockIdx.x);
+        if (blockIdx.x < tiles_of(jb.len, (uint8_t)jb.phase, a.tile_elems)) copy_job_tile<NR, U, NT>(a, j, blockIdx.x);
         return;
     }
     for (int64_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
-        const int j = find_job(a, t);
+        const int j = find_job(a.jobs, a.group_job, a.ngroups, a.njobs, t);
         copy_job_tile<NR, U, NT>(a, j, t - a.jobs[j].tile_begin);
     }
 }
@@ -529,18 +421,10 @@ __global__ __launch_bounds__(kBlock) void copy_batch_kernel(BatchArgs a) {
 // A copy batch whose table travels in the kernel arguments: job j =
 // blockIdx.y copies ptrs[j*(1+NR)] to the next NR pointers; every job has
 // len elements.
-struct CopyArgs {
-    const void* ptrs[kMaxCopyArgPtrs];
-    int64_t len;
-    int32_t tile_elems;
-    int32_t pad;
-    uint8_t phase[kMaxCopyArgJobs];
-};
-
 template <int NR, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void copy_args_kernel(CopyArgs a) {
     const int j = blockIdx.y;
-    const int phase = a.phase[j];
+    const uint8_t phase = a.phase[j];
     if (blockIdx.x >= tiles_of(a.len, phase, a.tile_elems)) return;
     const void* const* tp = a.ptrs + j * (1 + NR);
     const uint32_t* in[1] = {static_cast<const uint32_t*>(tp[0])};
@@ -562,37 +446,12 @@ __global__ __launch_bounds__(kBlock) void copy_args_full_kernel(CopyArgs a) {
     vec_round<1, NR, OpSumI32, U, NT, false, true>(in, none, 0, 0, out, 0xFFFFFFFFu >> (32 - NR), false);
 }
 
-// ---------------------------------------------------------------- dispatch
+// ---------------------------------------------------------------- dispatch helpers
 
 // Vectors per lane per round: about eight 16-byte loads in flight per lane,
 // counting an accumulator's loads with the operands'.
 template <int NIN, bool ACC>
 constexpr int kUnroll = unroll_for(ACC ? 2 * NIN : NIN);
-
-using FoldFn = void (*)(JobArgs);
-using BatchFn = void (*)(BatchArgs);
-
-// U1: the whole-tile all-reduce of 4-7 ranks with one vector per lane (the
-// planner halves its tiles); every other launch uses kUnroll.
-template <int NIN, class Op, bool NT, bool ACC, bool FULL, bool U1>
-FoldFn fold_ptr() {
-    if constexpr (FULL && U1 && NIN >= 4 && NIN < 8 && !ACC) return fold_full_kernel<NIN, Op, 1, NT, ACC>;
-    else if constexpr (FULL) return fold_full_kernel<NIN, Op, kUnroll<NIN, ACC>, NT, ACC>;
-    else return fold_kernel<NIN, Op, kUnroll<NIN, ACC>, NT, ACC>;
-}
-template <int NIN, class Op, bool NT, bool ACC>
-BatchFn batch_ptr() { return batch_kernel<NIN, Op, kUnroll<NIN, ACC>, NT, ACC>; }
-
-template <bool NT, bool FULL>
-struct CopyOf {
-    template <int NR>
-    struct At {
-        static FoldFn get() {
-            if constexpr (FULL) return copy_full_kernel<NR, kCopyUnroll, NT>;
-            else return copy_kernel<NR, kCopyUnroll, NT>;
-        }
-    };
-};
 
 // Kernel for nin = 1..16 ranks; Make<NIN>::get() names the instantiation.
 template <template <int> class Make, class Fn>
@@ -618,160 +477,5 @@ Fn pick_nin(int nin) {
     }
 }
 
-template <bool NT, bool FULL>
-FoldFn pick_copy(int nranks) {
-    return pick_nin<CopyOf<NT, FULL>::template At, FoldFn>(nranks);
-}
-
-template <class Op, bool NT, bool ACC, bool FULL, bool U1>
-struct FoldOf {
-    template <int NIN>
-    struct At {
-        static FoldFn get() { return fold_ptr<NIN, Op, NT, ACC, FULL, U1>(); }
-    };
-};
-template <class Op, bool NT, bool ACC>
-struct BatchOf {
-    template <int NIN>
-    struct At {
-        static BatchFn get() { return batch_ptr<NIN, Op, NT, ACC>(); }
-    };
-};
-
-// Accumulators exist for Sum and Mean only (validation refuses Max).
-template <bool NT, bool ACC, bool FULL, bool U1>
-FoldFn pick_fold_op(int dtype, int op, int nin) {
-    if (dtype == RC_F32) {
-        if (op == RC_MAX) {
-            if constexpr (ACC) return nullptr;
-            else return pick_nin<FoldOf<OpMaxF32, NT, false, FULL, U1>::template At, FoldFn>(nin);
-        }
-        return pick_nin<FoldOf<OpSumF32, NT, ACC, FULL, U1>::template At, FoldFn>(nin);
-    }
-    if (op == RC_MAX) {
-        if constexpr (ACC) return nullptr;
-        else return pick_nin<FoldOf<OpMaxI32, NT, false, FULL, U1>::template At, FoldFn>(nin);
-    }
-    return pick_nin<FoldOf<OpSumI32, NT, ACC, FULL, U1>::template At, FoldFn>(nin);
-}
-
-template <bool NT, bool ACC>
-BatchFn pick_batch_op(int dtype, int op, int nin) {
-    if (dtype == RC_F32) {
-        if (op == RC_MAX) {
-            if constexpr (ACC) return nullptr;
-            else return pick_nin<BatchOf<OpMaxF32, NT, false>::template At, BatchFn>(nin);
-        }
-        return pick_nin<BatchOf<OpSumF32, NT, ACC>::template At, BatchFn>(nin);
-    }
-    if (op == RC_MAX) {
-        if constexpr (ACC) return nullptr;
-        else return pick_nin<BatchOf<OpMaxI32, NT, false>::template At, BatchFn>(nin);
-    }
-    return pick_nin<BatchOf<OpSumI32, NT, ACC>::template At, BatchFn>(nin);
-}
-
-template <bool NT>
-struct CopyBatchOf {
-    template <int NR>
-    struct At {
-        static BatchFn get() { return copy_batch_kernel<NR, kCopyUnroll, NT>; }
-    };
-};
-
-using CopyArgsFn = void (*)(CopyArgs);
-template <bool NT, bool FULL>
-struct CopyArgsOf {
-    template <int NR>
-    struct At {
-        static CopyArgsFn get() {
-            if constexpr (FULL) return copy_args_full_kernel<NR, kCopyUnroll, NT>;
-            else return copy_args_kernel<NR, kCopyUnroll, NT>;
-        }
-    };
-};
-
-template <bool NT, bool FULL>
-FoldFn pick_fold_any(int dtype, int op, int nin, bool acc, bool u1) {
-    if (acc) return pick_fold_op<NT, true, FULL, false>(dtype, op, nin);
-    if constexpr (FULL) {
-        if (u1) return pick_fold_op<NT, false, true, true>(dtype, op, nin);
-    }
-    return pick_fold_op<NT, false, FULL, false>(dtype, op, nin);
-}
-template <bool NT>
-BatchFn pick_batch_any(int dtype, int op, int nin, bool acc) {
-    return acc ? pick_batch_op<NT, true>(dtype, op, nin) : pick_batch_op<NT, false>(dtype, op, nin);
-}
-
 }  // namespace
-
-hipError_t launch_jobs(const LaunchPlan& p, hipStream_t stream) {
-    const bool nt = p.args.nontemporal != 0;
-    const bool full = p.args.full_tiles != 0;
-    FoldFn fn;
-    if (p.args.in_mode == kInCopy) {
-        const int nr = p.args.nranks;
-        fn = nt ? (full ? pick_copy<true, true>(nr) : pick_copy<true, false>(nr))
-                : (full ? pick_copy<false, true>(nr) : pick_copy<false, false>(nr));
-    } else {
-        // the one-vector whole-tile all-reduce of 4-7 ranks (see plan)
-        const bool mid = !p.acc && p.nin >= 4 && p.nin < 8;
-        const bool u1 = full && mid && p.unroll == 1;
-        if (mid && !full && p.unroll != 2) return hipErrorInvalidValue;  // no general kernel with one vector
-        fn = nt ? (full ? pick_fold_any<true, true>(p.dtype, p.op, p.nin, p.acc, u1)
-                        : pick_fold_any<true, false>(p.dtype, p.op, p.nin, p.acc, false))
-                : (full ? pick_fold_any<false, true>(p.dtype, p.op, p.nin, p.acc, u1)
-                        : pick_fold_any<false, false>(p.dtype, p.op, p.nin, p.acc, false));
-    }
-    if (!fn) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fn, dim3(p.grid, p.grid_y), dim3(kBlock), p.lds_bytes, stream, p.args);
-    return hipGetLastError();
-}
-
-hipError_t launch_batch(const BatchJob* jobs, const int32_t* group_job, const void* const* ptrs,
-                        const BatchPlan& p, hipStream_t stream) {
-    const bool nt = p.nontemporal != 0;
-    BatchFn fn;
-    if (p.copy) fn = nt ? pick_nin<CopyBatchOf<true>::template At, BatchFn>(p.nout)
-                        : pick_nin<CopyBatchOf<false>::template At, BatchFn>(p.nout);
-    else fn = nt ? pick_batch_any<true>(p.dtype, p.op, p.nranks, p.acc)
-                 : pick_batch_any<false>(p.dtype, p.op, p.nranks, p.acc);
-    if (!fn) return hipErrorInvalidValue;
-    BatchArgs a;
-    a.jobs = jobs;
-    a.group_job = group_job;
-    a.ptrs = ptrs;
-    a.total_tiles = p.total_tiles;
-    a.ngroups = (int64_t)p.group_job.size();
-    a.njobs = (int32_t)p.jobs.size();
-    a.tile_elems = p.tile_elems;
-    a.mean = p.op == RC_MEAN ? 1 : 0;
-    a.grid_2d = p.grid_2d;
-    hipLaunchKernelGGL(fn, dim3(p.grid, p.grid_y), dim3(kBlock), p.lds_bytes, stream, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_copy_args(const BatchPlan& p, hipStream_t stream) {
-    if (!p.by_value || p.jobs.size() > (size_t)kMaxCopyArgJobs || p.ptrs.size() > (size_t)kMaxCopyArgPtrs)
-        return hipErrorInvalidValue;
-    const bool nt = p.nontemporal != 0;
-    const bool full = p.full_tiles;
-    CopyArgsFn fn = nt ? (full ? pick_nin<CopyArgsOf<true, true>::template At, CopyArgsFn>(p.nout)
-                               : pick_nin<CopyArgsOf<true, false>::template At, CopyArgsFn>(p.nout))
-                       : (full ? pick_nin<CopyArgsOf<false, true>::template At, CopyArgsFn>(p.nout)
-                               : pick_nin<CopyArgsOf<false, false>::template At, CopyArgsFn>(p.nout));
-    if (!fn) return hipErrorInvalidValue;
-    CopyArgs a{};
-    for (size_t i = 0; i < p.ptrs.size(); ++i) a.ptrs[i] = p.ptrs[i];
-    a.len = p.jobs[0].len;
-    a.tile_elems = p.tile_elems;
-    for (size_t j = 0; j < p.jobs.size(); ++j) {
-        if (p.jobs[j].len != a.len) return hipErrorInvalidValue;  // equal lengths only
-        a.phase[j] = (uint8_t)p.jobs[j].phase;
-    }
-    hipLaunchKernelGGL(fn, dim3(p.grid, p.grid_y), dim3(kBlock), p.lds_bytes, stream, a);
-    return hipGetLastError();
-}
-
 }  // namespace rc

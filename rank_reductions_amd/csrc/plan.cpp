@@ -32,23 +32,26 @@ uintptr_t addr(const void* p, int64_t elem_off, int64_t esize) {
     return reinterpret_cast<uintptr_t>(p) + (uintptr_t)(elem_off * esize);
 }
 
+// A job's streams at its first element: the inputs it reads, then the
+// outputs it writes.
+struct JobAddrs {
+    std::vector<uintptr_t> ins, outs;
+};
+
 // Fill per-job phase and tile counts of a single-launch plan.  Tile indices
 // are 32-bit in the kernels: tiles grow until the total stays below 2^31.
-void finish_jobs(LaunchPlan* p, const std::vector<std::vector<uintptr_t>>& job_addrs) {
+void finish_jobs(LaunchPlan* p, const std::vector<JobAddrs>& job_addrs) {
     JobArgs& a = p->args;
-    const int64_t es = 4;
     for (int c = 0; c < a.jobs; ++c) {
-        const int64_t len = std::max<int64_t>(0, std::min(a.seg, a.n - (int64_t)c * a.seg));
-        const auto& ad = job_addrs[c];
-        a.phase[c] = len ? job_phase(ad.data(), (int)ad.size(), es, len) : 0;
+        const JobAddrs& ad = job_addrs[c];
+        a.phase[c] = job_len(a.n, a.seg, c) ? job_phase(ad.ins.data(), (int)ad.ins.size(), ad.outs.data(),
+                                                         (int)ad.outs.size())
+                                            : 0;
     }
     int64_t prefix[kMaxRanks + 1];
     for (;;) {
         prefix[0] = 0;
-        for (int c = 0; c < a.jobs; ++c) {
-            const int64_t len = std::max<int64_t>(0, std::min(a.seg, a.n - (int64_t)c * a.seg));
-            prefix[c + 1] = prefix[c] + job_tiles(len, a.phase[c], a.tile_elems);
-        }
+        for (int c = 0; c < a.jobs; ++c) prefix[c + 1] = prefix[c] + tiles_of(job_len(a.n, a.seg, c), a.phase[c], a.tile_elems);
         if (prefix[a.jobs] < (int64_t(1) << 31)) break;
         a.tile_elems *= 2;
     }
@@ -85,26 +88,38 @@ int tile_elems_for(int unroll, const Config& cfg) {
     return (int)te;
 }
 
-uint8_t job_phase(const uintptr_t* addrs, int naddrs, int64_t esize, int64_t len) {
-    if (naddrs == 0) return 0;
-    const uintptr_t m = addrs[0] % 16;
-    for (int i = 1; i < naddrs; ++i)
-        if (addrs[i] % 16 != m) return kScalarOnly;
-    const int head = (int)(((16 - m) % 16) / (uintptr_t)esize);
-    const uintptr_t first_vec = addrs[0] + (uintptr_t)(head * esize);
+int job_reference(const uintptr_t* ins, int nin, const uintptr_t* outs, int nout) {
+    // weight of each stream's 256-byte class, counted over all streams
+    const int n = nin + nout;
+    int best = 0, best_w = -1;
+    for (int i = 0; i < n; ++i) {
+        const uintptr_t cls = (i < nin ? ins[i] : outs[i - nin]) % kTileAlignBytes;
+        bool seen = false;
+        for (int j = 0; j < i && !seen; ++j) seen = (j < nin ? ins[j] : outs[j - nin]) % kTileAlignBytes == cls;
+        if (seen) continue;
+        int w = 0;
+        for (int j = i; j < n; ++j)
+            if ((j < nin ? ins[j] : outs[j - nin]) % kTileAlignBytes == cls) w += j < nin ? 1 : 2;
+        if (w > best_w) {
+            best = i;
+            best_w = w;
+        }
+    }
+    return best;
+}
+
+uint8_t phase_of(uintptr_t ref) {
+    // elements are 4 bytes and 4-byte aligned (validation checks it)
+    const int head = (int)(((16 - ref % 16) % 16) / 4);
+    const uintptr_t first_vec = ref + (uintptr_t)(head * 4);
     const int lead = (int)(((kTileAlignBytes - first_vec % kTileAlignBytes) % kTileAlignBytes) / 16);
-    (void)len;
     return phase_code(head, lead);
 }
 
-int64_t job_tiles(int64_t len, uint8_t phase, int64_t te) {
-    if (len <= 0) return 0;
-    if (phase == kScalarOnly) return (len + te - 1) / te;
-    const int64_t head = std::min<int64_t>(phase_head(phase), len);
-    const int64_t nvec = (len - head) / kVec;
-    const int64_t lead = std::min<int64_t>(phase_lead(phase), nvec);
-    const int64_t tv = te / kVec;
-    return std::max<int64_t>(1, (lead > 0 ? 1 : 0) + (nvec - lead + tv - 1) / tv);
+uint8_t job_phase(const uintptr_t* ins, int nin, const uintptr_t* outs, int nout) {
+    if (nin + nout == 0) return 0;
+    const int r = job_reference(ins, nin, outs, nout);
+    return phase_of(r < nin ? ins[r] : outs[r - nin]);
 }
 
 int auto_waves_per_cu(int nin, int nout, int unroll, const InFlightRule& rule) {
@@ -179,7 +194,7 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceI
     p.dtype = ck.dtype;
     p.op = ck.op;
 
-    std::vector<std::vector<uintptr_t>> ad;
+    std::vector<JobAddrs> ad;
     auto fold_setup = [&](int64_t n, int64_t seg, int64_t in_stride, int64_t out_stride) {
         p.nin = R;
         p.acc = ck.has_acc;
@@ -207,12 +222,12 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceI
     auto fold_addrs = [&](uint32_t mask_for_owner_only, bool owner_only) {
         ad.assign(R, {});
         for (int c = 0; c < R; ++c) {
-            for (int r = 0; r < R; ++r) ad[c].push_back(addr(a.in[r], (int64_t)c * a.in_stride, es));
+            for (int r = 0; r < R; ++r) ad[c].ins.push_back(addr(a.in[r], (int64_t)c * a.in_stride, es));
             if (p.acc)
-                for (int r = 0; r < R; ++r) ad[c].push_back(addr(a.acc[r], (int64_t)c * a.in_stride, es));
+                for (int r = 0; r < R; ++r) ad[c].ins.push_back(addr(a.acc[r], (int64_t)c * a.in_stride, es));
             for (int r = 0; r < R; ++r) {
                 const bool writes = owner_only ? (r == c) : ((mask_for_owner_only >> r) & 1u);
-                if (writes) ad[c].push_back(addr(a.out[r], (int64_t)c * a.out_stride, es));
+                if (writes) ad[c].outs.push_back(addr(a.out[r], (int64_t)c * a.out_stride, es));
             }
         }
     };
@@ -259,8 +274,11 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceI
                 b.out[r] = ck.recv[r];
             }
             ad.assign(R, {});
-            for (int c = 0; c < R; ++c)
-                for (int r = 0; r < R; ++r) ad[c].push_back(addr(ck.recv[r], (int64_t)c * S, es));
+            for (int c = 0; c < R; ++c) {
+                ad[c].ins.push_back(addr(ck.recv[c], (int64_t)c * S, es));
+                for (int r = 0; r < R; ++r)
+                    if (r != c) ad[c].outs.push_back(addr(ck.recv[r], (int64_t)c * S, es));
+            }
             finish_jobs(&q, ad);
             out.push_back(q);
             break;
@@ -293,9 +311,9 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceI
             a.out_mask = mask;
             if (!mask) break;
             ad.assign(1, {});
-            ad[0].push_back(addr(a.in[0], 0, es));
+            ad[0].ins.push_back(addr(a.in[0], 0, es));
             for (int r = 0; r < R; ++r)
-                if ((mask >> r) & 1u) ad[0].push_back(addr(a.out[r], 0, es));
+                if ((mask >> r) & 1u) ad[0].outs.push_back(addr(a.out[r], 0, es));
             finish_jobs(&p, ad);
             out.push_back(p);
             break;
@@ -314,7 +332,9 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceI
             a.out[0] = ck.recv[0];
             a.out_mask = ck.send[0] != ck.recv[0] ? 1u : 0u;
             if (!a.out_mask) break;
-            ad.assign(1, {addr(a.in[0], 0, es), addr(a.out[0], 0, es)});
+            ad.assign(1, {});
+            ad[0].ins.push_back(addr(a.in[0], 0, es));
+            ad[0].outs.push_back(addr(a.out[0], 0, es));
             finish_jobs(&p, ad);
             out.push_back(p);
             break;
@@ -340,8 +360,8 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceI
             // in place: rank c's shard already sits at its place in rank c's output
             ad.assign(R, {});
             for (int c = 0; c < R; ++c) {
-                ad[c].push_back(addr(a.in[c], 0, es));
-                for (int r = 0; r < R; ++r) ad[c].push_back(addr(a.out[r], (int64_t)c * M, es));
+                ad[c].ins.push_back(addr(a.in[c], 0, es));
+                for (int r = 0; r < R; ++r) ad[c].outs.push_back(addr(a.out[r], (int64_t)c * M, es));
             }
             finish_jobs(&p, ad);
             out.push_back(p);
@@ -363,7 +383,7 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceI
         for (int c = 0; c < ja.jobs; ++c) widest = std::max<int64_t>(widest, ja.tile_prefix[c + 1] - ja.tile_prefix[c]);
         bool full = widest > 0 && ja.tile_elems == (int64_t)kBlock * kVec * lp.unroll;
         for (int c = 0; c < ja.jobs && full; ++c) {
-            const int64_t len = std::max<int64_t>(0, std::min(ja.seg, ja.n - (int64_t)c * ja.seg));
+            const int64_t len = job_len(ja.n, ja.seg, c);
             full = ja.phase[c] == 0 && ja.tile_prefix[c + 1] - ja.tile_prefix[c] == widest &&
                    len == widest * (int64_t)ja.tile_elems;
         }
@@ -420,8 +440,9 @@ BatchPlan plan_batch(const std::vector<Checked>& tensors, const Config& cfg, con
     bp.nontemporal = nontemporal_of(cfg);
     const int64_t es = element_size(bp.dtype);
     int64_t tiles = 0;
-    std::vector<uintptr_t> ad;
-    ad.reserve(3 * R);
+    std::vector<uintptr_t> ins, outs;
+    ins.reserve(2 * R);
+    outs.reserve(R);
     for (const Checked& ck : tensors) {
         if (ck.count == 0) continue;
         const int64_t S = (ck.count + R - 1) / R;
@@ -429,18 +450,20 @@ BatchPlan plan_batch(const std::vector<Checked>& tensors, const Config& cfg, con
             const int64_t start = (int64_t)c * S;
             const int64_t len = std::min(S, ck.count - start);
             if (len <= 0) continue;
-            ad.clear();
-            for (int k = 0; k < R; ++k) ad.push_back(addr(ck.send[(c + 1 + k) % R], start, es));
+            ins.clear();
+            outs.clear();
+            for (int k = 0; k < R; ++k) ins.push_back(addr(ck.send[fold_rank(c, k, R)], start, es));
             if (bp.acc)
-                for (int k = 0; k < R; ++k) ad.push_back(addr(ck.acc[(c + 1 + k) % R], start, es));
-            for (int r = 0; r < R; ++r) ad.push_back(addr(ck.recv[r], start, es));
+                for (int k = 0; k < R; ++k) ins.push_back(addr(ck.acc[fold_rank(c, k, R)], start, es));
+            for (int r = 0; r < R; ++r) outs.push_back(addr(ck.recv[r], start, es));
             BatchJob j{};
             j.tile_begin = tiles;
             j.len = len;
-            j.phase = job_phase(ad.data(), (int)ad.size(), es, len);
-            tiles += job_tiles(len, (uint8_t)j.phase, bp.tile_elems);
+            j.phase = job_phase(ins.data(), (int)ins.size(), outs.data(), (int)outs.size());
+            tiles += tiles_of(len, (uint8_t)j.phase, bp.tile_elems);
             bp.jobs.push_back(j);
-            for (uintptr_t a : ad) bp.ptrs.push_back(reinterpret_cast<const void*>(a));
+            for (uintptr_t a : ins) bp.ptrs.push_back(reinterpret_cast<const void*>(a));
+            for (uintptr_t a : outs) bp.ptrs.push_back(reinterpret_cast<const void*>(a));
         }
     }
     bp.total_tiles = tiles;
@@ -464,14 +487,14 @@ BatchPlan plan_copies(const Checked& ck, const Config& cfg, const DeviceInfo& de
     bp.op = RC_SUM;
     bp.nontemporal = nontemporal_of(cfg);
     bp.tile_elems = tile_elems_for(kCopyUnroll, cfg);
-    std::vector<uintptr_t> ad;
+    std::vector<uintptr_t> ad;  // the source, then the destinations
     int64_t tiles = 0;
     auto add_job = [&](int64_t len) {
         BatchJob j{};
         j.tile_begin = tiles;
         j.len = len;
-        j.phase = job_phase(ad.data(), (int)ad.size(), es, len);
-        tiles += job_tiles(len, (uint8_t)j.phase, bp.tile_elems);
+        j.phase = job_phase(ad.data(), 1, ad.data() + 1, (int)ad.size() - 1);
+        tiles += tiles_of(len, (uint8_t)j.phase, bp.tile_elems);
         bp.jobs.push_back(j);
         for (uintptr_t a : ad) bp.ptrs.push_back(reinterpret_cast<const void*>(a));
     };

@@ -9,24 +9,11 @@
 #include <vector>
 
 #include "rc.h"
+#include "tiling.h"
 
 namespace rc {
 
-constexpr int kMaxRanks = RC_MAX_RANKS;
-constexpr int kBlock = 64;           // threads per workgroup: one wave64
-constexpr int kVec = 4;              // elements per 16-byte vector
-constexpr uint8_t kScalarOnly = 0xFF;  // job phase: pointers not co-aligned
-// A job's phase packs how its elements split into accesses: bits 0-1 hold the
-// scalar elements before its first address reaches a 16-byte boundary (every
-// address agrees with it modulo 16), bits 2-5 the 16-byte vectors after that
-// before the first address reaches a kTileAlignBytes boundary.  Those vectors
-// form a short first tile, so that every full tile starts on the boundary:
-// tiles that share a 256-byte line with their neighbours measured 10-25%
-// slower.  kScalarOnly marks addresses that disagree modulo 16 bytes.
-constexpr int kTileAlignBytes = 256;
-constexpr uint8_t phase_code(int head, int lead) { return (uint8_t)(head | (lead << 2)); }
-constexpr int phase_head(uint8_t phase) { return phase & 3; }
-constexpr int phase_lead(uint8_t phase) { return (phase >> 2) & 15; }
+static_assert(kMaxRanks == RC_MAX_RANKS, "tiling.h and rc.h disagree on the rank limit");
 
 // The first five are reductions or fan-outs over ring segments; the rest are
 // the Communicator page's other methods: copies between ranks and a barrier.
@@ -36,13 +23,6 @@ enum class Coll { AllReduce, Reduce, Broadcast, ReduceScatter, AllGather, AllToA
 enum InMode : int32_t {
     kInFold = 0,  // fold R inputs: in[(c+1+k) % R] + c*in_stride, k = 0..R-1
     kInCopy = 1,  // copy one input: in[c] + c*in_stride
-};
-
-// Which ranks' outputs a job writes (each at out[r] + c*out_stride).
-enum OutMode : int32_t {
-    kOutMask = 0,       // the ranks in out_mask
-    kOutOwner = 1,      // only rank c
-    kOutMaskButOwner = 2,  // the ranks in out_mask except rank c
 };
 
 // Argument block of one launch that covers up to kMaxRanks jobs (segments).
@@ -71,20 +51,10 @@ struct JobArgs {
     int32_t full_tiles;
     int32_t total_tiles;                 // tile_prefix[jobs], below 2^31
     int32_t tile_prefix[kMaxRanks + 1];  // tiles before job j; past the last job: total_tiles
-    uint8_t phase[kMaxRanks];            // job phase (phase_code), or kScalarOnly
+    uint8_t phase[kMaxRanks];            // job phase (phase_code of its reference stream)
     // fold jobs with accumulators: operand k of a job is acc[r] + in[r] for
     // its rank r, added before the fold (kernels instantiated for it only)
     const void* acc[kMaxRanks];
-};
-
-// One segment of one tensor in a batched all-reduce (device descriptor).  Its
-// 2R pointers sit in a parallel table: the R fold operands in fold order,
-// then the R outputs, all already offset to the segment's first element.
-struct BatchJob {
-    int64_t tile_begin;  // first tile of this job in the launch's tile space
-    int64_t len;         // elements in the segment (> 0)
-    int32_t phase;       // job phase (phase_code), or kScalarOnly
-    int32_t pad;
 };
 
 struct DeviceInfo {
@@ -154,16 +124,18 @@ int64_t element_size(int dtype);
 constexpr int unroll_for(int nin) { return nin >= 8 ? 1 : (nin >= 4 ? 2 : (nin >= 2 ? 4 : 8)); }
 // Unroll of the copy kernel (one input, up to 16 outputs per element).
 constexpr int kCopyUnroll = 2;
-// Tiles of the batched all-reduce are indexed in groups of 2^kGroupShift: the
-// kernel finds a tile's job from its group's first job.
-constexpr int kGroupShift = 8;
 // Elements per tile for a kernel of the given unroll under the session's config.
 int tile_elems_for(int unroll, const Config& cfg);
-// Job phase (phase_code) of a job whose accesses start at addrs, or
-// kScalarOnly when the addresses disagree modulo 16 bytes.
-uint8_t job_phase(const uintptr_t* addrs, int naddrs, int64_t elem_size, int64_t len);
-// Tiles for one job of `len` elements.
-int64_t job_tiles(int64_t len, uint8_t phase, int64_t tile_elems);
+// The stream a job's tiles align to: of the job's streams (its nin inputs,
+// then its nout outputs, each at the job's first element), the one whose
+// 256-byte alignment class carries the most weight, an output counting twice
+// an input (a store sharing a line with a neighbouring tile costs more than a
+// load); ties go to the class met first.  Returns its index in ins ++ outs.
+int job_reference(const uintptr_t* ins, int nin, const uintptr_t* outs, int nout);
+// Phase (phase_code) of a job whose reference stream starts at `ref`.
+uint8_t phase_of(uintptr_t ref);
+// job_reference and phase_of together.
+uint8_t job_phase(const uintptr_t* ins, int nin, const uintptr_t* outs, int nout);
 
 struct LaunchPlan {
     JobArgs args;
@@ -281,6 +253,56 @@ struct TuneEntry {
 // *cand >= 0 asks the caller to time this launch and report it to tune_record.
 int tune_pick(TuneEntry& t, int rule_waves, int* cand);
 void tune_record(TuneEntry& t, int cand, float us);
+
+// ---------------------------------------------------------------- kernels_*.hip
+// Kernel argument blocks of the table-driven launches, passed by value.
+
+// A launch over a job table in device memory: tile t belongs to job
+// find_job(jobs, group_job, ngroups, njobs, t).
+struct BatchArgs {
+    const BatchJob* jobs;
+    const int32_t* group_job;
+    const void* const* ptrs;  // [job][2R], or [job][3R] with accumulators: operands, accumulators, outputs
+    int64_t total_tiles;
+    int64_t ngroups;
+    int32_t njobs;
+    int32_t tile_elems;
+    int32_t mean;
+    int32_t grid_2d;  // copies: y = job, x = tile of the job
+};
+
+// A copy batch whose table travels in the kernel arguments: job j =
+// blockIdx.y copies ptrs[j*(1+NR)] to the next NR pointers; every job has
+// len elements.
+struct CopyArgs {
+    const void* ptrs[kMaxCopyArgPtrs];
+    int64_t len;
+    int32_t tile_elems;
+    int32_t pad;
+    uint8_t phase[kMaxCopyArgJobs];
+};
+
+using FoldFn = void (*)(JobArgs);
+using BatchFn = void (*)(BatchArgs);
+using CopyArgsFn = void (*)(CopyArgs);
+
+// The kernel instantiation for a launch; nullptr if none exists.  Fold
+// kernels (kernels_fold.hip, built once per dtype and cache hint):
+// op RC_SUM / RC_MEAN / RC_MAX, acc (accumulators: Sum and Mean only), full
+// (whole-tile kernel), u1 (the whole-tile fold of 4-7 ranks with one vector
+// per lane), nin = ranks folded.
+FoldFn fold_fn_f32_nt(int op, bool acc, bool full, bool u1, int nin);
+FoldFn fold_fn_f32_cached(int op, bool acc, bool full, bool u1, int nin);
+FoldFn fold_fn_i32_nt(int op, bool acc, bool full, bool u1, int nin);
+FoldFn fold_fn_i32_cached(int op, bool acc, bool full, bool u1, int nin);
+// Batched folds (kernels_batch.hip, once per cache hint).
+BatchFn batch_fn_nt(int dtype, int op, bool acc, int nin);
+BatchFn batch_fn_cached(int dtype, int op, bool acc, int nin);
+// Copies to nr outputs (kernels_copy.hip): single copies, copy batches over
+// a device table, and copy batches by value.
+FoldFn copy_fn(bool nt, bool full, int nr);
+BatchFn copy_batch_fn(bool nt, int nr);
+CopyArgsFn copy_args_fn(bool nt, bool full, int nr);
 
 // ---------------------------------------------------------------- device.hip
 // All return RC_OK or RC_ERR_DEVICE with a message.

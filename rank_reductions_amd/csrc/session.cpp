@@ -284,6 +284,7 @@ Error launch_tuned(const TuneKey& key, int rule_waves, int64_t moved, void* stre
     return {};
 }
 
+// Enqueues one validated collective.
 Error launch(const Checked& ck, void* stream) {
     const int64_t es = element_size(ck.dtype);
     int capturing = -1;  // asked once, when a launch could be tuned

@@ -39,41 +39,51 @@ bool inside(uintptr_t a, int64_t bytes) {
     return a >= it->lo && a + (uintptr_t)bytes <= it->hi;
 }
 
-// Enumerate the elements tile lt of a job touches, as job_tile does.
+// Enumerate the elements tile lt of a job touches, in the kernels' loop
+// structure (job_tile: rounds of U vectors per lane over the tile's vectors,
+// then the job's scalars on tile 0), with the index arithmetic of tiling.h.
 template <class F>
 void tile_elements(int64_t len, int phase, int64_t lt, int64_t te, int unroll, F&& visit) {
-    if (phase == kScalarOnly) {
-        // rounds of 4*unroll elements per lane, kBlock apart, then the remainder
-        const int64_t e0 = lt * te, e1 = std::min(e0 + te, len);
-        const int64_t J = 4 * unroll;
-        int64_t e = e0;
-        for (; e + J * kBlock <= e1; e += J * kBlock)
-            for (int tid = 0; tid < kBlock; ++tid)
-                for (int64_t j = 0; j < J; ++j) visit(e + tid + j * kBlock, 4);
-        for (int tid = 0; tid < kBlock; ++tid)
-            for (int64_t x = e + tid; x < e1; x += kBlock) visit(x, 4);
-        return;
-    }
-    const int64_t head = std::min<int64_t>(phase_head((uint8_t)phase), len);
-    const int64_t nvec = (len - head) / kVec;
-    const int64_t tail0 = head + nvec * kVec;
-    const int64_t tv = te / kVec;
-    // a lead of L vectors is tile 0 on its own; tile t >= 1 starts at L + (t-1)*tv
-    const int64_t lead = std::min<int64_t>(phase_lead((uint8_t)phase), nvec);
-    const int64_t v0 = lead > 0 ? (lt == 0 ? 0 : lead + (lt - 1) * tv) : lt * tv;
-    const int64_t v1 = std::min(lead > 0 ? (lt == 0 ? lead : lead + lt * tv) : (lt + 1) * tv, nvec);
+    const JobSplit s = job_split(len, (uint8_t)phase, te);
+    int64_t v0, v1;
+    tile_vectors(s, lt, &v0, &v1);
     const int64_t step = (int64_t)kBlock * unroll;
     for (int64_t vb = v0; vb < v1; vb += step)
         for (int u = 0; u < unroll; ++u)
             for (int tid = 0; tid < kBlock; ++tid) {
                 const int64_t v = vb + (int64_t)u * kBlock + tid;
-                if (v < v1) visit(head + v * kVec, 16);
+                if (v < v1) visit(s.head + v * kVec, 16);
             }
-    if (lt == 0) {
-        const int64_t nscal = head + (len - tail0);
+    if (lt == 0)
         for (int tid = 0; tid < kBlock; ++tid)
-            if (tid < nscal) visit(tid < head ? tid : tail0 + (tid - head), 4);
+            if (tid < scalars_of(s, len)) visit(scalar_elem(s, tid), 4);
+}
+
+// The phase must put the job's tiles on the grid of a stream of the heaviest
+// 256-byte alignment class (outputs weigh 2, inputs 1): some stream of such a
+// class reaches a 16-byte boundary after `head` elements and a 256-byte one
+// `lead` vectors later.  Brute force over the classes, independent of the
+// planner's own choice.
+bool phase_fits_heaviest(const std::vector<uintptr_t>& ins, const std::vector<uintptr_t>& outs, uint8_t phase) {
+    std::vector<std::pair<uintptr_t, int>> w;  // class, weight
+    auto add = [&](uintptr_t a, int wt) {
+        for (auto& c : w)
+            if (c.first == a % kTileAlignBytes) {
+                c.second += wt;
+                return;
+            }
+        w.push_back({a % kTileAlignBytes, wt});
+    };
+    for (uintptr_t a : ins) add(a, 1);
+    for (uintptr_t a : outs) add(a, 2);
+    int best = 0;
+    for (auto& c : w) best = std::max(best, c.second);
+    for (auto& c : w) {
+        if (c.second != best) continue;
+        const uintptr_t v = c.first + (uintptr_t)phase_head(phase) * 4;
+        if (v % 16 == 0 && (v + (uintptr_t)phase_lead(phase) * 16) % kTileAlignBytes == 0) return true;
     }
+    return w.empty();
 }
 
 void check_plan(const LaunchPlan& p, const std::string& name) {
@@ -123,9 +133,7 @@ void check_plan(const LaunchPlan& p, const std::string& name) {
         const int64_t lt = visit.second;
         const int64_t start = (int64_t)c * a.seg;
         const int64_t len = std::min(a.seg, a.n - start);
-        uint32_t mask = a.out_mask;
-        if (a.out_mode == kOutOwner) mask = 1u << c;
-        else if (a.out_mode == kOutMaskButOwner) mask &= ~(1u << c);
+        const uint32_t mask = out_mask_of(a.out_mode, a.out_mask, c);
         auto visit_tile = [&](auto&& visit) {
             if (a.full_tiles) {
                 // fold_full_kernel / copy_full_kernel: one round of whole 16-byte vectors
@@ -141,34 +149,52 @@ void check_plan(const LaunchPlan& p, const std::string& name) {
                 if (e + i < 0 || e + i >= len) fail(name + ": element outside its job");
                 else seen[c][e + i] += 1;
             }
-            if (bytes == 16 && e % kVec != (a.phase[c] % kVec) % kVec) {
-                // vector accesses start at head + 4v: aligned by construction
-            }
+            // every access 4-byte aligned (vectors off the reference's grid
+            // rely on the unaligned access mode for the rest)
             if (a.in_mode == kInFold) {
                 for (int k = 0; k < p.nin; ++k) {
                     const uintptr_t base = (uintptr_t)a.in[(c + 1 + k) % p.nin] + (uintptr_t)(c * a.in_stride * 4);
                     const uintptr_t ad = base + (uintptr_t)(e * 4);
                     if (!inside(ad, bytes)) fail(name + ": input read outside its buffer");
-                    if (bytes == 16 && ad % 16) fail(name + ": misaligned vector read");
+                    if (ad % 4) fail(name + ": input read off the element grid");
                     if (p.acc) {
                         const uintptr_t aa = (uintptr_t)a.acc[(c + 1 + k) % p.nin] +
                                              (uintptr_t)(c * a.in_stride * 4) + (uintptr_t)(e * 4);
                         if (!inside(aa, bytes)) fail(name + ": accumulator read outside its buffer");
-                        if (bytes == 16 && aa % 16) fail(name + ": misaligned accumulator read");
+                        if (aa % 4) fail(name + ": accumulator read off the element grid");
                     }
                 }
             } else {
                 const uintptr_t ad = (uintptr_t)a.in[c] + (uintptr_t)(c * a.in_stride * 4) + (uintptr_t)(e * 4);
                 if (!inside(ad, bytes)) fail(name + ": copy read outside its buffer");
-                if (bytes == 16 && ad % 16) fail(name + ": misaligned vector read");
+                if (ad % 4) fail(name + ": copy read off the element grid");
             }
             for (int o = 0; o < a.nranks; ++o) {
                 if (!((mask >> o) & 1u)) continue;
                 const uintptr_t ad = (uintptr_t)a.out[o] + (uintptr_t)(c * a.out_stride * 4) + (uintptr_t)(e * 4);
                 if (!inside(ad, bytes)) fail(name + ": write outside its buffer");
-                if (bytes == 16 && ad % 16) fail(name + ": misaligned vector write");
+                if (ad % 4) fail(name + ": write off the element grid");
             }
         });
+    }
+    // each job's phase follows a stream of its heaviest alignment class
+    for (int c = 0; c < a.jobs; ++c) {
+        if (job_len(a.n, a.seg, c) == 0) continue;
+        uint32_t mask = out_mask_of(a.out_mode, a.out_mask, c);
+        std::vector<uintptr_t> ins, outs;
+        if (a.in_mode == kInFold) {
+            for (int k = 0; k < p.nin; ++k)
+                ins.push_back((uintptr_t)a.in[(c + 1 + k) % p.nin] + (uintptr_t)(c * a.in_stride * 4));
+            if (p.acc)
+                for (int k = 0; k < p.nin; ++k)
+                    ins.push_back((uintptr_t)a.acc[(c + 1 + k) % p.nin] + (uintptr_t)(c * a.in_stride * 4));
+        } else {
+            ins.push_back((uintptr_t)a.in[c] + (uintptr_t)(c * a.in_stride * 4));
+        }
+        for (int o = 0; o < a.nranks; ++o)
+            if ((mask >> o) & 1u) outs.push_back((uintptr_t)a.out[o] + (uintptr_t)(c * a.out_stride * 4));
+        if (!phase_fits_heaviest(ins, outs, a.phase[c]))
+            fail(name + ": job " + std::to_string(c) + " is not tiled on its heaviest alignment class");
     }
     for (int c = 0; c < a.jobs; ++c) {
         const int64_t len = std::max<int64_t>(0, std::min(a.seg, a.n - (int64_t)c * a.seg));
@@ -214,16 +240,22 @@ int main(int argc, char** argv) {
     dev.max_lds_per_block = 64 * 1024;
     int plans = 0;
     int full_plans = 0;  // plans whose kernels take the whole-tile path
-    // job_phase: the head reaches a 16-byte boundary, the lead a 256-byte one
+    // job_phase: the head reaches a 16-byte boundary and the lead a 256-byte
+    // one of a stream of the heaviest alignment class
     for (int i = 0; i < 20000; ++i) {
+        const int nin = 1 + (int)(rng() % 6), nout = (int)(rng() % 6);
+        std::vector<uintptr_t> ins, outs;
         const uintptr_t base = 0x10000 + (uintptr_t)(rng() % 8192) * 4;
-        uintptr_t addrs[3] = {base, base + 4096 * (1 + rng() % 5), base + 16 * (rng() % 1000)};
-        const uint8_t ph = job_phase(addrs, 3, 4, 1000);
-        const uintptr_t v = base + (uintptr_t)phase_head(ph) * 4;
-        if (ph == kScalarOnly || v % 16 || (v + (uintptr_t)phase_lead(ph) * 16) % kTileAlignBytes)
-            fail("job_phase: wrong head or lead for base " + std::to_string(base));
-        addrs[2] += 4;
-        if (job_phase(addrs, 3, 4, 1000) != kScalarOnly) fail("job_phase: mixed alignment not scalar-only");
+        for (int k = 0; k < nin + nout; ++k) {
+            // a few classes only, so that ties and majorities both occur
+            const uintptr_t a = base + 4096 * (uintptr_t)(1 + rng() % 5) + 4 * (uintptr_t)(rng() % 3);
+            (k < nin ? ins : outs).push_back(a);
+        }
+        const uint8_t ph = job_phase(ins.data(), nin, outs.data(), nout);
+        if (!phase_fits_heaviest(ins, outs, ph)) fail("job_phase: not on the heaviest class");
+        const int ref = job_reference(ins.data(), nin, outs.data(), nout);
+        if (ref < 0 || ref >= nin + nout || phase_of(ref < nin ? ins[ref] : outs[ref - nin]) != ph)
+            fail("job_reference and job_phase disagree");
     }
     for (int it = 0; it < iters; ++it) {
         g_bufs.clear();
@@ -334,19 +366,21 @@ int main(int argc, char** argv) {
         std::vector<std::vector<uint8_t>> seen(bp.jobs.size());
         for (size_t j = 0; j < bp.jobs.size(); ++j) seen[j].assign((size_t)bp.jobs[j].len, 0);
         const int64_t ngroups = (int64_t)bp.group_job.size();
+        for (size_t j = 0; j < bp.jobs.size(); ++j) {
+            const auto* tp = &bp.ptrs[j * ptrs_per_job];
+            const int nins = (with_acc ? 2 : 1) * R;
+            std::vector<uintptr_t> ins, outs;
+            for (int k = 0; k < ptrs_per_job; ++k) (k < nins ? ins : outs).push_back((uintptr_t)tp[k]);
+            if (!phase_fits_heaviest(ins, outs, (uint8_t)bp.jobs[j].phase))
+                fail("batched job not tiled on its heaviest alignment class");
+        }
         for (int64_t t = 0; t < bp.total_tiles; ++t) {
             const int64_t g = t >> kGroupShift;
             if (g >= ngroups) {
                 fail("group index out of range");
                 break;
             }
-            int lo = bp.group_job[g];
-            int hi = g + 1 < ngroups ? bp.group_job[g + 1] : (int)bp.jobs.size() - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (bp.jobs[mid].tile_begin <= t) lo = mid;
-                else hi = mid - 1;
-            }
+            const int lo = find_job(bp.jobs.data(), bp.group_job.data(), ngroups, (int)bp.jobs.size(), t);
             const BatchJob& jb = bp.jobs[lo];
             const int64_t next = lo + 1 < (int)bp.jobs.size() ? bp.jobs[lo + 1].tile_begin : bp.total_tiles;
             if (!(jb.tile_begin <= t && t < next)) fail("group lookup found the wrong job");
@@ -358,7 +392,7 @@ int main(int argc, char** argv) {
                 for (int k = 0; k < ptrs_per_job; ++k) {
                     const uintptr_t ad = (uintptr_t)bp.ptrs[(size_t)lo * ptrs_per_job + k] + (uintptr_t)(e * 4);
                     if (!inside(ad, bytes)) fail("batched access outside its buffer");
-                    if (bytes == 16 && ad % 16) fail("batched misaligned vector access");
+                    if (ad % 4) fail("batched access off the element grid");
                 }
             });
         }
@@ -423,6 +457,13 @@ int main(int argc, char** argv) {
         const int per_job = 1 + bp.nout;
         if (ck.count > 0 && (!bp.copy || bp.ptrs.size() != bp.jobs.size() * (size_t)per_job))
             fail("copy plan has the wrong shape");
+        for (size_t j = 0; j < bp.jobs.size(); ++j) {
+            const auto* tp = &bp.ptrs[j * per_job];
+            std::vector<uintptr_t> ins{(uintptr_t)tp[0]}, outs;
+            for (int k = 1; k < per_job; ++k) outs.push_back((uintptr_t)tp[k]);
+            if (!phase_fits_heaviest(ins, outs, (uint8_t)bp.jobs[j].phase))
+                fail("copy job not tiled on its heaviest alignment class");
+        }
         // the (job, tile) pairs the launch visits: one-shot 2-D grid (y = job,
         // tiles past the job's own count exit) or the 1-D group lookup
         std::vector<std::pair<int, int64_t>> visits;
@@ -430,7 +471,7 @@ int main(int argc, char** argv) {
             if (bp.grid_y != (int)bp.jobs.size()) fail("copy 2-D grid height is not the job count");
             for (int j = 0; j < bp.grid_y; ++j) {
                 const BatchJob& jb = bp.jobs[j];
-                const int64_t own = job_tiles(jb.len, (uint8_t)jb.phase, bp.tile_elems);
+                const int64_t own = tiles_of(jb.len, (uint8_t)jb.phase, bp.tile_elems);
                 if (own > bp.grid) fail("copy 2-D grid narrower than a job");
                 if (bp.full_tiles && (!bp.by_value || jb.phase != 0 || bp.tile_elems != kBlock * kVec * kCopyUnroll ||
                                       jb.len != bp.grid * (int64_t)bp.tile_elems))
@@ -442,14 +483,9 @@ int main(int argc, char** argv) {
         } else {
             const int64_t ngroups = (int64_t)bp.group_job.size();
             for (int64_t t = 0; t < bp.total_tiles; ++t) {
-                const int64_t g = t >> kGroupShift;
-                int lo = bp.group_job[g];
-                int hi = g + 1 < ngroups ? bp.group_job[g + 1] : (int)bp.jobs.size() - 1;
-                while (lo < hi) {
-                    const int mid = (lo + hi + 1) >> 1;
-                    if (bp.jobs[mid].tile_begin <= t) lo = mid;
-                    else hi = mid - 1;
-                }
+                const int lo = find_job(bp.jobs.data(), bp.group_job.data(), ngroups, (int)bp.jobs.size(), t);
+                const int64_t next = lo + 1 < (int)bp.jobs.size() ? bp.jobs[lo + 1].tile_begin : bp.total_tiles;
+                if (!(bp.jobs[lo].tile_begin <= t && t < next)) fail("copy group lookup found the wrong job");
                 visits.push_back({lo, t - bp.jobs[lo].tile_begin});
             }
         }
@@ -468,7 +504,7 @@ int main(int argc, char** argv) {
                 for (int k = 0; k < per_job; ++k) {
                     const uintptr_t ad = (uintptr_t)bp.ptrs[(size_t)lo * per_job + k] + (uintptr_t)(el * 4);
                     if (!inside(ad, bytes)) fail("copy access outside its buffer");
-                    if (bytes == 16 && ad % 16) fail("copy misaligned vector access");
+                    if (ad % 4) fail("copy access off the element grid");
                     if (k == 0) continue;
                     for (Dst& d : dsts)
                         if (ad >= d.lo && ad < d.lo + (uintptr_t)d.n * 4)
