@@ -43,12 +43,13 @@
  * Graphs.  Single collectives (all_reduce, reduce, broadcast, reduce_scatter,
  * all_gather, send/recv) and the copy batches of all_to_all_single and the
  * list-form all_gather (up to 12 and 16 ranks) enqueue nothing but kernels,
- * so they can be captured into a HIP graph and replayed.  Batched all-reduces
- * (rc_all_reduce_many, rc_all_reduce_params) with tensors under 64 MiB of
- * traffic, and copy batches beyond those sizes, upload descriptor tables
- * from reused host staging; on a capturing stream they return
- * RC_ERR_INVALID_ARGUMENT before enqueuing anything.  Per-rank calls join
- * several streams and are not meant for capture.
+ * so they can be captured into a HIP graph and replayed, and so can
+ * rc_all_reduce_many_static.  Batched all-reduces (rc_all_reduce_many,
+ * rc_all_reduce_params) with tensors under 64 MiB of traffic, and copy
+ * batches beyond those sizes, upload descriptor tables from reused host
+ * staging; on a capturing stream they return RC_ERR_INVALID_ARGUMENT before
+ * enqueuing anything.  Per-rank calls join several streams and are not meant
+ * for capture.
  *
  * Threads.  The library keeps one process-wide session behind a mutex; calls
  * from several threads are serialised.  A per-rank call blocks its thread,
@@ -65,7 +66,7 @@
 extern "C" {
 #endif
 
-#define RC_ABI_VERSION 2
+#define RC_ABI_VERSION 3
 #define RC_MAX_RANKS 16
 #define RC_MAX_DIMS 8
 
@@ -251,6 +252,23 @@ int rc_barrier(void* stream);
  * session keeps a descriptor arena for this (allocated on first use, freed by
  * rc_finish / rc_reset). */
 int rc_all_reduce_many(int num_tensors, const rc_buf* bufs, void* stream);
+
+/* rc_all_reduce_many for callers that cannot allocate device memory: code
+ * being captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, checks, launches and bits as
+ * rc_all_reduce_many, but nothing is allocated and only kernels are enqueued:
+ * the descriptor tables of the tensors that share the batched launch (those
+ * moving under 64 MiB) are written by a small kernel into a static device
+ * buffer of 1 MiB that the library holds on each GPU it runs on until the
+ * process ends, instead of the session's arena; tensors that get launches of
+ * their own use the occupancy tuner's choice so far without timing anything.
+ * A call whose tables need more than 1 MiB (about 11,900 ring segments at 4
+ * ranks, 3,700 at 16) returns RC_ERR_INVALID_ARGUMENT before enqueuing
+ * anything.  Every call on a GPU shares that GPU's buffer and leaves its
+ * tables there: calls that overlap on one GPU (from several threads, or on
+ * streams that run concurrently) race and give wrong results; calls ordered
+ * on one stream do not. */
+int rc_all_reduce_many_static(int num_tensors, const rc_buf* bufs, void* stream);
 
 /* One rank's entry of a gradient sync keyed by parameter ID.
  *   id   the parameter ID;

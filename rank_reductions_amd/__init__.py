@@ -32,7 +32,7 @@ __all__ = [
     "RC_OK", "RC_ERR_NOT_REGISTERED", "RC_ERR_DUPLICATE_REGISTRATION", "RC_ERR_SHAPE_MISMATCH",
     "RC_ERR_OP_MISMATCH", "RC_ERR_ROOT_MISMATCH", "RC_ERR_BROADCAST_SENDERS",
     "RC_ERR_DTYPE_MISMATCH", "RC_ERR_INVALID_ARGUMENT", "RC_ERR_DEVICE", "RC_ERR_PARAM_MISMATCH",
-    "all_reduce_params", "rank_register", "rank_finish", "rank_all_reduce", "rank_reduce",
+    "all_reduce_many_static", "all_reduce_params", "rank_register", "rank_finish", "rank_all_reduce", "rank_reduce",
     "rank_broadcast", "rank_reduce_scatter", "rank_all_gather", "rank_all_reduce_params",
     "all_gather_list", "all_to_all_single", "send_recv", "barrier", "rank_all_gather_list",
     "rank_all_to_all_single", "rank_send", "rank_recv", "rank_barrier", "rank_split", "rank_split_all",
@@ -40,7 +40,7 @@ __all__ = [
 ]
 
 RC_MAX_RANKS = 16
-RC_ABI_VERSION = 2  # the include/rc.h this binding is written against
+RC_ABI_VERSION = 3  # the include/rc.h this binding is written against
 RC_MAX_DIMS = 8
 
 RC_F32, RC_I32 = 0, 1
@@ -150,8 +150,9 @@ def _load():
         fn.restype = ctypes.c_int
     lib.rc_register.argtypes = [ctypes.c_int, ctypes.POINTER(RcConfig)]
     lib.rc_register.restype = ctypes.c_int
-    lib.rc_all_reduce_many.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-    lib.rc_all_reduce_many.restype = ctypes.c_int
+    for name in ("rc_all_reduce_many", "rc_all_reduce_many_static"):
+        getattr(lib, name).argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        getattr(lib, name).restype = ctypes.c_int
     for name in ("rc_finish", "rc_reset", "rc_abi_version"):
         getattr(lib, name).argtypes = []
         getattr(lib, name).restype = ctypes.c_int
@@ -459,6 +460,24 @@ def all_reduce_many(tensors, op="mean", out=None, stream=None):
     ref = tensors[0][0]
     check(library().rc_all_reduce_many(len(tensors), ctypes.c_void_p(arr.ctypes.data),
                                        ctypes.c_void_p(_stream(stream, ref))))
+    return out
+
+
+def all_reduce_many_static(tensors, op="mean", out=None, stream=None):
+    """all_reduce_many for callers that cannot allocate device memory (graph
+    capture, serving loops): the batched tensors' descriptor tables go to the
+    library's static device scratch (1 MiB per GPU) instead of its arena, and
+    only kernels are enqueued.  Same bits as all_reduce_many.  Calls that
+    overlap on one GPU race on the scratch."""
+    torch = _torch()
+    if out is None:
+        out = [[torch.empty_like(x) for x in per_rank] for per_rank in tensors]
+    if not tensors:
+        return out
+    arr = batch_bufs(tensors, out, _op(op))
+    ref = tensors[0][0]
+    check(library().rc_all_reduce_many_static(len(tensors), ctypes.c_void_p(arr.ctypes.data),
+                                              ctypes.c_void_p(_stream(stream, ref))))
     return out
 
 

@@ -1,5 +1,6 @@
-// HIP side of the session: device query, launches on the caller's stream, and
-// the descriptor arena of the batched all-reduce.
+// HIP side of the session: device query, launches on the caller's stream, the
+// descriptor arena of the batched all-reduce, and the static scratch of its
+// allocation-free variant.
 //
 // The arena holds the job and pointer tables of batched launches (the
 // gradient all-reduces, and copy batches too large for kernel arguments).
@@ -19,7 +20,17 @@
 
 namespace rc {
 
+// Device scratch of the allocation-free batched all-reduce: its job, group
+// and pointer tables are written here by kernels.  Each GPU holds its own
+// copy, at an address looked up once per device (resolve_scratch) and kept in
+// g_scratch_ptr; in host code the name is only a handle and is never passed
+// to a kernel or a copy.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices] = {};
 
 // ---------------------------------------------------------------- launches
 
@@ -203,7 +214,63 @@ void read_tables(const BatchPlan& p, const TableLayout& t, size_t off, size_t n,
 
 void write_tables(const BatchPlan& p, const TableLayout& t, char* dst) { read_tables(p, t, 0, t.bytes, dst); }
 
+// Looks up the address of GPU dev's copy of `scratch` once per device, with
+// that device current (rc_register's set-up of each session calls it).
+Error resolve_scratch(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return Error{RC_ERR_DEVICE, "device index beyond the scratch table"};
+    if (g_scratch_ptr[dev]) return {};
+    int prev = -1;
+    hipError_t e = hipGetDevice(&prev);
+    if (e == hipSuccess && prev != dev) e = hipSetDevice(dev);
+    if (e != hipSuccess) return hip_fail("hipSetDevice", e);
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (prev >= 0 && prev != dev) (void)hipSetDevice(prev);
+    if (e != hipSuccess) return hip_fail("hipGetSymbolAddress(scratch)", e);
+    if (!p) return Error{RC_ERR_DEVICE, "hipGetSymbolAddress(scratch) gave NULL"};
+    g_scratch_ptr[dev] = p;
+    return {};
+}
+
 }  // namespace
+
+size_t batch_table_bytes(const BatchPlan& p) { return table_layout(p).bytes; }
+
+Error device_launch_batch_static(const BatchPlan& p, void* stream) {
+    if (p.jobs.empty()) return {};
+    if (p.by_value) return Error{RC_ERR_INVALID_ARGUMENT, "device_launch_batch_static: by-value batch"};
+    const TableLayout t = table_layout(p);
+    if (t.bytes > kStaticScratchBytes)
+        return Error{RC_ERR_INVALID_ARGUMENT,
+                     "the batched tensors' descriptor tables need " + std::to_string(t.bytes) +
+                         " bytes, more than the " + std::to_string(kStaticScratchBytes) +
+                         " bytes of static scratch: use rc_all_reduce_many, or fewer small tensors per call"};
+    DeviceGuard guard;
+    if (guard.err != hipSuccess) return hip_fail("hipSetDevice", guard.err);
+    if (g.device < 0 || g.device >= kMaxDevices || !g_scratch_ptr[g.device])
+        return Error{RC_ERR_DEVICE, "static scratch not resolved for this device"};
+    char* base = static_cast<char*>(g_scratch_ptr[g.device]);
+    // the tables as 32-bit words (their size is a multiple of 8 bytes), in
+    // pieces small enough for kernel arguments
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t words = t.bytes / 4;
+    TableChunk c;
+    c.pad = 0;
+    for (size_t w0 = 0; w0 < words; w0 += kTableChunkWords) {
+        const size_t n = words - w0 < (size_t)kTableChunkWords ? words - w0 : (size_t)kTableChunkWords;
+        c.dst = reinterpret_cast<uint32_t*>(base) + w0;
+        c.nwords = (uint32_t)n;
+        read_tables(p, t, w0 * 4, n * 4, reinterpret_cast<char*>(c.words));
+        hipLaunchKernelGGL(table_write_fn(), dim3(1), dim3(kBlock), 0, s, c);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail("table writer launch", e);
+    }
+    const hipError_t e = launch_batch(reinterpret_cast<const BatchJob*>(base),
+                                      reinterpret_cast<const int32_t*>(base + t.group_off),
+                                      reinterpret_cast<const void* const*>(base + t.ptr_off), p, s);
+    if (e != hipSuccess) return hip_fail("kernel launch", e);
+    return {};
+}
 
 Error device_open(const Config& cfg, DeviceInfo* info) {
     int count = 0;
@@ -229,6 +296,8 @@ Error device_open(const Config& cfg, DeviceInfo* info) {
     info->lds_per_cu = (int64_t)prop.maxSharedMemoryPerMultiProcessor;
     info->max_lds_per_block = (int64_t)prop.sharedMemPerBlock;
     info->arch = arch;
+    Error err = resolve_scratch(dev);
+    if (err.code) return err;
     g.device = dev;
     g.next = 0;
     return {};

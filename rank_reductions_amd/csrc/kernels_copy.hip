@@ -1,5 +1,6 @@
 // Copy kernels (broadcast, all_gather, the ring's all-gather phase,
-// send/recv, all_to_all_single, the list form of all_gather).
+// send/recv, all_to_all_single, the list form of all_gather) and the table
+// writer of the allocation-free batched all-reduce.
 #include "kernels_impl.h"
 
 namespace rc {
@@ -35,6 +36,11 @@ struct CopyArgsOf {
     };
 };
 
+// Writes one piece of a descriptor table (c.nwords 32-bit words) to c.dst.
+__global__ __launch_bounds__(kBlock) void table_write_kernel(TableChunk c) {
+    for (uint32_t i = threadIdx.x; i < c.nwords; i += kBlock) c.dst[i] = c.words[i];
+}
+
 }  // namespace
 
 FoldFn copy_fn(bool nt, bool full, int nr) {
@@ -55,5 +61,7 @@ CopyArgsFn copy_args_fn(bool nt, bool full, int nr) {
     return full ? pick_nin<CopyArgsOf<false, true>::template At, CopyArgsFn>(nr)
                 : pick_nin<CopyArgsOf<false, false>::template At, CopyArgsFn>(nr);
 }
+
+TableFn table_write_fn() { return table_write_kernel; }
 
 }  // namespace rc

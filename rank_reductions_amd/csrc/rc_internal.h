@@ -282,9 +282,20 @@ struct CopyArgs {
     uint8_t phase[kMaxCopyArgJobs];
 };
 
+// A piece of a descriptor table written into device memory by a kernel (the
+// allocation-free batched all-reduce's way of placing its tables).
+constexpr int kTableChunkWords = 896;
+struct TableChunk {
+    uint32_t* dst;
+    uint32_t nwords;
+    uint32_t pad;
+    uint32_t words[kTableChunkWords];
+};
+
 using FoldFn = void (*)(JobArgs);
 using BatchFn = void (*)(BatchArgs);
 using CopyArgsFn = void (*)(CopyArgs);
+using TableFn = void (*)(TableChunk);
 
 // The kernel instantiation for a launch; nullptr if none exists.  Fold
 // kernels (kernels_fold.hip, built once per dtype and cache hint):
@@ -299,16 +310,25 @@ FoldFn fold_fn_i32_cached(int op, bool acc, bool full, bool u1, int nin);
 BatchFn batch_fn_nt(int dtype, int op, bool acc, int nin);
 BatchFn batch_fn_cached(int dtype, int op, bool acc, int nin);
 // Copies to nr outputs (kernels_copy.hip): single copies, copy batches over
-// a device table, and copy batches by value.
+// a device table, copy batches by value, and the table writer.
 FoldFn copy_fn(bool nt, bool full, int nr);
 BatchFn copy_batch_fn(bool nt, int nr);
 CopyArgsFn copy_args_fn(bool nt, bool full, int nr);
+TableFn table_write_fn();
 
 // ---------------------------------------------------------------- device.hip
 // All return RC_OK or RC_ERR_DEVICE with a message.
 Error device_open(const Config& cfg, DeviceInfo* info);
 Error device_launch(const LaunchPlan& p, void* stream);
 Error device_launch_batch(const BatchPlan& p, void* stream);
+// The same batch with its tables in the library's static device scratch
+// (kStaticScratchBytes per GPU, reserved when the library loads) instead of
+// the session's arena: no allocation, no host staging, nothing but kernel
+// launches (a table writer, then the batch).  RC_ERR_INVALID_ARGUMENT when
+// the tables exceed the scratch.  Calls that overlap on one GPU race on it.
+constexpr size_t kStaticScratchBytes = size_t(1) << 20;
+size_t batch_table_bytes(const BatchPlan& p);
+Error device_launch_batch_static(const BatchPlan& p, void* stream);
 Error device_finish();   // wait for the GPU, free scratch
 void device_reset();     // wait for kernels reading scratch, free scratch
 // Events that order the per-rank front end's streams around a launch.

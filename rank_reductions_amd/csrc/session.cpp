@@ -239,11 +239,19 @@ void log_tune_choice(const TuneKey& key, int rule_waves, const TuneEntry& t) {
 // CU, under the occupancy tuner when it applies: the entry `key` picks the
 // wave count, and a launch chosen for timing is bracketed by a timer.
 // run(-1) keeps the plan's own reservation.  `capturing` caches whether
-// `stream` is being captured (-1: not asked yet).
+// `stream` is being captured (-1: not asked yet).  With `timed` false the
+// launch makes no event or capture query at all: it takes the tuner's
+// choice for the shape if there is one, else the rule's wave count.
 template <class Run>
-Error launch_tuned(const TuneKey& key, int rule_waves, int64_t moved, void* stream, int* capturing, Run run) {
+Error launch_tuned(const TuneKey& key, int rule_waves, int64_t moved, void* stream, int* capturing, bool timed,
+                   Run run) {
     if (g_s.cfg.waves_per_cu > 0 || g_s.cfg.max_workgroups > 0 || rule_waves <= 0 || moved < kTuneMinBytes)
         return run(-1);
+    if (!timed) {
+        const auto it = g_s.tune.find(key);
+        const int w = it != g_s.tune.end() ? it->second.chosen : 0;
+        return run(w > 0 && w != rule_waves ? lds_for_waves(g_s.dev, w) : -1);
+    }
     if (*capturing < 0) {
         bool c = false;
         Error e = device_stream_capturing(stream, &c);
@@ -284,8 +292,9 @@ Error launch_tuned(const TuneKey& key, int rule_waves, int64_t moved, void* stre
     return {};
 }
 
-// Enqueues one validated collective.
-Error launch(const Checked& ck, void* stream) {
+// Enqueues one validated collective.  With `timed` false nothing but kernel
+// launches is enqueued (see launch_tuned).
+Error launch(const Checked& ck, void* stream, bool timed = true) {
     const int64_t es = element_size(ck.dtype);
     int capturing = -1;  // asked once, when a launch could be tuned
     if (runs_as_copies(ck.coll)) {
@@ -304,7 +313,7 @@ Error launch(const Checked& ck, void* stream) {
         for (const BatchJob& jb : bp.jobs) elems += jb.len;
         const int64_t moved = (1 + bp.nout) * elems * es;
         const TuneKey key{2, bp.full_tiles ? 1 : 0, 1, 0, bp.nout, kCopyUnroll, size_class(moved)};
-        return launch_tuned(key, bp.waves, moved, stream, &capturing, [&](int lds) {
+        return launch_tuned(key, bp.waves, moved, stream, &capturing, timed, [&](int lds) {
             if (lds >= 0) bp.lds_bytes = lds;
             return device_launch_batch(bp, stream);
         });
@@ -321,7 +330,7 @@ Error launch(const Checked& ck, void* stream) {
         }
         const TuneKey key{(int)p.args.in_mode, (int)p.args.full_tiles, p.nin, p.acc ? 1 : 0, p.nout, p.unroll,
                           size_class(moved)};
-        Error e = launch_tuned(key, p.waves, moved, stream, &capturing, [&](int lds) {
+        Error e = launch_tuned(key, p.waves, moved, stream, &capturing, timed, [&](int lds) {
             if (lds >= 0) p.lds_bytes = lds;
             return device_launch(p, stream);
         });
@@ -351,10 +360,39 @@ int collective(Coll coll, const rc_buf* bufs, void* stream, void* const* recv_li
 
 // A validated batch of all-reduces: tensors large enough get launches of
 // their own, the rest share one batched launch (one for tensors with
-// accumulators and one for tensors without, when both occur).
-Error launch_batch(const std::vector<Checked>& cks, void* stream) {
+// accumulators and one for tensors without, when both occur).  With
+// `use_static` the batched launches take their tables from the library's
+// static scratch, and nothing but kernels is enqueued.
+Error launch_batch(const std::vector<Checked>& cks, void* stream, bool use_static = false) {
     std::vector<Checked> own, batched;
     split_batch(cks, &own, &batched);
+    if (use_static) {
+        // every check before anything is enqueued
+        BatchPlan parts[2];
+        for (const bool acc : {false, true}) {
+            std::vector<Checked> part;
+            for (const Checked& ck : batched)
+                if (ck.has_acc == acc) part.push_back(ck);
+            parts[acc] = plan_batch(part, g_s.cfg, g_s.dev);
+            const size_t need = batch_table_bytes(parts[acc]);
+            if (parts[acc].total_tiles && need > kStaticScratchBytes)
+                return Error{RC_ERR_INVALID_ARGUMENT,
+                             "all_reduce_many_static: the tables of the " + std::to_string(part.size()) +
+                                 " tensors under 64 MiB of traffic need " + std::to_string(need) +
+                                 " bytes, more than the " + std::to_string(kStaticScratchBytes) +
+                                 " bytes of static scratch"};
+        }
+        for (const Checked& ck : own) {
+            Error e = launch(ck, stream, false);
+            if (e.code) return e;
+        }
+        for (const BatchPlan& bp : parts) {
+            if (bp.total_tiles == 0) continue;
+            Error e = device_launch_batch_static(bp, stream);
+            if (e.code) return e;
+        }
+        return {};
+    }
     if (!batched.empty()) {
         // the batched launch uploads its tables from host staging that later
         // calls reuse, so a graph replay would read stale tables: refuse
@@ -776,6 +814,19 @@ int rc_all_reduce_many(int num_tensors, const rc_buf* bufs, void* stream) {
     if (e.code) return report(e);
     if (g_s.cfg.validate_only) return ok();
     return report(launch_batch(cks, stream));
+}
+
+int rc_all_reduce_many_static(int num_tensors, const rc_buf* bufs, void* stream) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (g_s.mode == Mode::None)
+        return report(Error{RC_ERR_NOT_REGISTERED, "no session: call rc_register first"});
+    if (g_s.mode == Mode::PerRank)
+        return report(Error{RC_ERR_INVALID_ARGUMENT, "the session was opened per rank"});
+    std::vector<Checked> cks;
+    Error e = validate_batch(g_s.nranks, num_tensors, bufs, &cks);
+    if (e.code) return report(e);
+    if (g_s.cfg.validate_only) return ok();
+    return report(launch_batch(cks, stream, true));
 }
 
 int rc_all_reduce_params(const int* num_params, const rc_param* const* params, void* stream) {

@@ -20,6 +20,8 @@ namespace rc {
 Error device_open(const Config&, DeviceInfo*) { return Error{RC_ERR_DEVICE, "no device in this test"}; }
 Error device_launch(const LaunchPlan&, void*) { return Error{RC_ERR_DEVICE, "no device in this test"}; }
 Error device_launch_batch(const BatchPlan&, void*) { return Error{RC_ERR_DEVICE, "no device in this test"}; }
+size_t batch_table_bytes(const BatchPlan&) { return 0; }
+Error device_launch_batch_static(const BatchPlan&, void*) { return Error{RC_ERR_DEVICE, "no device in this test"}; }
 Error device_finish() { return {}; }
 void device_reset() {}
 Error device_event_create(void**) { return Error{RC_ERR_DEVICE, "no device in this test"}; }

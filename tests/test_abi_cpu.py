@@ -59,7 +59,7 @@ def test_library_exports_every_declared_symbol(lib):
     exported = set(re.findall(r"\bT (rc_\w+)", out))
     assert set(declared_functions()) <= exported
     header = re.search(r"#define RC_ABI_VERSION (\d+)", (ROOT / "include" / "rc.h").read_text())
-    assert lib.rc_abi_version() == int(header.group(1)) == rr.RC_ABI_VERSION == 2
+    assert lib.rc_abi_version() == int(header.group(1)) == rr.RC_ABI_VERSION == 3
 
 
 def test_struct_layout_matches_a_c_compiler(tmp_path):

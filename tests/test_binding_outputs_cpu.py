@@ -84,7 +84,7 @@ def test_all_gather_outputs():
 def test_batched_outputs():
     ts = [xs(N), xs(7)]
     good = [xs(N), xs(7)]
-    for fn in (rr.all_reduce_many,):
+    for fn in (rr.all_reduce_many, rr.all_reduce_many_static):
         assert code_of(lambda: fn(ts, out=[xs(N), xs(6)])) == SHAPE
         assert code_of(lambda: fn(ts, out=[xs(N), xs(7, torch.int32)])) == DTYPE
         assert code_of(lambda: fn(ts, out=[xs(N)])) == INVAL
