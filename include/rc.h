@@ -152,10 +152,12 @@ typedef struct rc_buf {
  *                  unit, in [1, 32]; 0: the library's choice per collective.
  *                  With 0, launches that move 256 MiB or more are tuned
  *                  online: the first launches of each launch shape and size
- *                  class try three caps (two timed launches each, HIP events
- *                  read once complete, never waited on; none while the stream
- *                  is being captured) and later ones use the fastest.  The
- *                  cap changes timing only, never the results.  With
+ *                  class try three caps (five timed launches each, HIP
+ *                  events read once complete, never waited on; none while
+ *                  the stream is being captured) and later ones use the cap
+ *                  with the lowest median time, the default cap unless
+ *                  another beats it by 3%.  The cap changes timing only,
+ *                  never the results.  With
  *                  RC_TUNE_LOG=1 in the environment each choice is printed
  *                  on stderr.
  *   reserved       must be 0 */

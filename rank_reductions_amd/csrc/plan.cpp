@@ -143,10 +143,8 @@ int lds_for_waves(const DeviceInfo& dev, int waves) {
 
 int tune_pick(TuneEntry& t, int rule_waves, int* cand) {
     *cand = -1;
-    if (t.ncand == 0) {
+    if (t.ncand == 0)
         for (int w = rule_waves; w >= std::max(2, rule_waves - (kTuneCands - 1)); --w) t.cand[t.ncand++] = w;
-        for (int i = 0; i < t.ncand; ++i) t.best_us[i] = 0.0f;
-    }
     if (t.chosen) return t.chosen;
     // candidates in turn, the one with the fewest timed launches first
     int pick = -1;
@@ -159,14 +157,20 @@ int tune_pick(TuneEntry& t, int rule_waves, int* cand) {
 }
 
 void tune_record(TuneEntry& t, int cand, float us) {
-    if (cand < 0 || cand >= t.ncand || t.chosen) return;
-    if (t.got[cand] == 0 || us < t.best_us[cand]) t.best_us[cand] = us;
-    ++t.got[cand];
+    if (cand < 0 || cand >= t.ncand || t.chosen || t.got[cand] >= kTuneSamples) return;
+    t.us[cand][t.got[cand]++] = us;
     for (int i = 0; i < t.ncand; ++i)
         if (t.got[i] < kTuneSamples) return;
-    int best = 0;  // ties keep the rule's value
+    for (int i = 0; i < t.ncand; ++i) {
+        float v[kTuneSamples];
+        std::copy(t.us[i], t.us[i] + kTuneSamples, v);
+        std::sort(v, v + kTuneSamples);
+        t.median_us[i] = v[kTuneSamples / 2];
+    }
+    int best = 0;  // candidate 0 is the rule's W
     for (int i = 1; i < t.ncand; ++i)
-        if (t.best_us[i] < t.best_us[best]) best = i;
+        if (t.median_us[i] < t.median_us[best]) best = i;
+    if (best != 0 && t.median_us[best] > (1.0 - kTuneMargin) * t.median_us[0]) best = 0;
     t.chosen = t.cand[best];
 }
 

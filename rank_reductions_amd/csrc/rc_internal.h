@@ -230,10 +230,17 @@ int lds_for_waves(const DeviceInfo& dev, int waves);
 // timing only, never results.  So the first launches of each large shape try
 // the rule's W and the two values below it, kTuneSamples timed launches each
 // (HIP events read once they have completed, never waited on), and every
-// later launch of that shape uses the fastest.  Used when waves_per_cu is
-// left to the library, for launches that move at least kTuneMinBytes.
+// later launch of that shape uses the candidate with the lowest median time
+// per byte.  A candidate other than the rule's W must beat the rule's median
+// by kTuneMargin: launch times of one shape spread by up to +-10%, a lucky
+// sample once sent a 4-rank all-reduce to a wave count that ran 30% slower
+// in steady state, and a switch 1.6% ahead in calibration ran 9% slower,
+// while the largest gain seen from a right switch is 3.6%.  Used when
+// waves_per_cu is left to the library, for launches that move at least
+// kTuneMinBytes.
 constexpr int kTuneCands = 3;
-constexpr int kTuneSamples = 2;
+constexpr int kTuneSamples = 5;
+constexpr double kTuneMargin = 0.03;
 constexpr int64_t kTuneMinBytes = int64_t(256) << 20;
 struct TunePending {
     int ticket;     // device timer
@@ -245,7 +252,8 @@ struct TuneEntry {
     int cand[kTuneCands] = {};
     int issued[kTuneCands] = {};
     int got[kTuneCands] = {};
-    float best_us[kTuneCands] = {};
+    float us[kTuneCands][kTuneSamples] = {};  // time per GiB of each timed launch
+    float median_us[kTuneCands] = {};         // set once every candidate has kTuneSamples times
     std::vector<TunePending> pending;  // timed launches not read yet
     int chosen = 0;  // 0 until every candidate has kTuneSamples times
 };

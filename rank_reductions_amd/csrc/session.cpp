@@ -213,7 +213,7 @@ void close_session() {
 
 // With RC_TUNE_LOG=1 in the environment, each choice of the occupancy tuner
 // is reported on stderr: the launch shape, the rule's wave count, and each
-// candidate's best time per GiB moved.
+// candidate's median time per GiB moved.
 void log_tune_choice(const TuneKey& key, int rule_waves, const TuneEntry& t) {
     static const bool on = [] {
         const char* v = std::getenv("RC_TUNE_LOG");
@@ -229,7 +229,7 @@ void log_tune_choice(const TuneKey& key, int rule_waves, const TuneEntry& t) {
                        " B: rule W=" + std::to_string(rule_waves) + ", chose W=" + std::to_string(t.chosen) + " (";
     for (int i = 0; i < t.ncand; ++i) {
         char buf[64];
-        std::snprintf(buf, sizeof buf, "%sW=%d %.1f us/GiB", i ? ", " : "", t.cand[i], (double)t.best_us[i]);
+        std::snprintf(buf, sizeof buf, "%sW=%d %.1f us/GiB", i ? ", " : "", t.cand[i], (double)t.median_us[i]);
         line += buf;
     }
     std::fprintf(stderr, "%s)\n", line.c_str());

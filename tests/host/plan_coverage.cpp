@@ -59,6 +59,43 @@ void tile_elements(int64_t len, int phase, int64_t lt, int64_t te, int unroll, F
             if (tid < scalars_of(s, len)) visit(scalar_elem(s, tid), 4);
 }
 
+// Elements of one output of one job written per (job-relative) element.
+struct WriteCount {
+    std::vector<uint8_t> hits;
+    bool bad = false;
+};
+
+// Checks one write of `bytes` at job element e of an output whose job starts
+// at address base: inside the buffer and 4-byte aligned (16-byte writes off
+// the 16-byte grid rely on the unaligned access mode); counts the elements.
+void count_write(WriteCount& wc, uintptr_t base, int64_t e, int bytes, int64_t len, const std::string& what) {
+    const uintptr_t ad = base + (uintptr_t)(e * 4);
+    if (!inside(ad, bytes)) {
+        if (!wc.bad) fail(what + ": write outside its buffer");
+        wc.bad = true;
+    }
+    if (ad % 4) {
+        if (!wc.bad) fail(what + ": write off the element grid");
+        wc.bad = true;
+    }
+    for (int i = 0; i < bytes / 4; ++i) {
+        if (e + i < 0 || e + i >= len) {
+            if (!wc.bad) fail(what + ": write outside its job");
+            wc.bad = true;
+        } else {
+            wc.hits[(size_t)(e + i)] += 1;
+        }
+    }
+}
+
+void expect_once(const WriteCount& wc, const std::string& what) {
+    for (size_t i = 0; i < wc.hits.size(); ++i)
+        if (wc.hits[i] != 1) {
+            fail(what + ": element " + std::to_string(i) + " written " + std::to_string(wc.hits[i]) + " times");
+            return;
+        }
+}
+
 // The phase must put the job's tiles on the grid of a stream of the heaviest
 // 256-byte alignment class (outputs weigh 2, inputs 1): some stream of such a
 // class reaches a 16-byte boundary after `head` elements and a 256-byte one
@@ -91,8 +128,11 @@ void check_plan(const LaunchPlan& p, const std::string& name) {
     if (a.tile_elems % (kBlock * kVec * p.unroll)) fail(name + ": tile not a multiple of a round");
     if (p.grid < 1 || p.grid > 0x7FFFFFFF) fail(name + ": grid out of range");
     std::vector<std::vector<uint8_t>> seen(a.jobs);
-    for (int c = 0; c < a.jobs; ++c)
-        seen[c].assign((size_t)std::max<int64_t>(0, std::min(a.seg, a.n - (int64_t)c * a.seg)), 0);
+    std::vector<std::vector<WriteCount>> writes(a.jobs, std::vector<WriteCount>(a.nranks));
+    for (int c = 0; c < a.jobs; ++c) {
+        seen[c].assign((size_t)job_len(a.n, a.seg, c), 0);
+        for (auto& wc : writes[c]) wc.hits.assign((size_t)job_len(a.n, a.seg, c), 0);
+    }
     const int64_t total = a.total_tiles;
     if (total != a.tile_prefix[a.jobs] || total != p.total_tiles) fail(name + ": tile totals disagree");
     for (int c = a.jobs; c <= kMaxRanks; ++c)
@@ -118,9 +158,8 @@ void check_plan(const LaunchPlan& p, const std::string& name) {
         if (p.grid_y != 1) fail(name + ": 1-D launch with a 2-D grid");
         for (int64_t b = 0; b < p.grid; ++b)
             for (int64_t t = b; t < total; t += p.grid) {
-                // the kernels' lookup: count job boundaries at or below t
-                int c = 0;
-                for (int j = 1; j < kMaxRanks; ++j) c += t >= a.tile_prefix[j] ? 1 : 0;
+                // the kernels' lookup (tiling.h)
+                const int c = job_of(a.tile_prefix, (int)t);
                 if (c >= a.jobs || t < a.tile_prefix[c] || t >= a.tile_prefix[c + 1]) {
                     fail(name + ": job index past the last job");
                     return;
@@ -169,14 +208,19 @@ void check_plan(const LaunchPlan& p, const std::string& name) {
                 if (!inside(ad, bytes)) fail(name + ": copy read outside its buffer");
                 if (ad % 4) fail(name + ": copy read off the element grid");
             }
-            for (int o = 0; o < a.nranks; ++o) {
-                if (!((mask >> o) & 1u)) continue;
-                const uintptr_t ad = (uintptr_t)a.out[o] + (uintptr_t)(c * a.out_stride * 4) + (uintptr_t)(e * 4);
-                if (!inside(ad, bytes)) fail(name + ": write outside its buffer");
-                if (ad % 4) fail(name + ": write off the element grid");
-            }
         });
+        // writes, output by output, as the kernel makes them
+        for (int o = 0; o < a.nranks; ++o) {
+            if (!((mask >> o) & 1u)) continue;
+            const uintptr_t base = (uintptr_t)a.out[o] + (uintptr_t)(c * a.out_stride * 4);
+            WriteCount& wc = writes[c][o];
+            visit_tile([&](int64_t e, int bytes) { count_write(wc, base, e, bytes, len, name); });
+        }
     }
+    for (int c = 0; c < a.jobs; ++c)
+        for (int o = 0; o < a.nranks; ++o)
+            if ((out_mask_of(a.out_mode, a.out_mask, c) >> o) & 1u)
+                expect_once(writes[c][o], name + ": job " + std::to_string(c) + " output " + std::to_string(o));
     // each job's phase follows a stream of its heaviest alignment class
     for (int c = 0; c < a.jobs; ++c) {
         if (job_len(a.n, a.seg, c) == 0) continue;
@@ -364,7 +408,11 @@ int main(int argc, char** argv) {
         const int ptrs_per_job = (with_acc ? 3 : 2) * R;
         if (bp.ptrs.size() != bp.jobs.size() * (size_t)ptrs_per_job) fail("batched pointer table has the wrong size");
         std::vector<std::vector<uint8_t>> seen(bp.jobs.size());
-        for (size_t j = 0; j < bp.jobs.size(); ++j) seen[j].assign((size_t)bp.jobs[j].len, 0);
+        std::vector<std::vector<WriteCount>> bwrites(bp.jobs.size(), std::vector<WriteCount>(R));
+        for (size_t j = 0; j < bp.jobs.size(); ++j) {
+            seen[j].assign((size_t)bp.jobs[j].len, 0);
+            for (auto& wc : bwrites[j]) wc.hits.assign((size_t)bp.jobs[j].len, 0);
+        }
         const int64_t ngroups = (int64_t)bp.group_job.size();
         for (size_t j = 0; j < bp.jobs.size(); ++j) {
             const auto* tp = &bp.ptrs[j * ptrs_per_job];
@@ -384,24 +432,33 @@ int main(int argc, char** argv) {
             const BatchJob& jb = bp.jobs[lo];
             const int64_t next = lo + 1 < (int)bp.jobs.size() ? bp.jobs[lo + 1].tile_begin : bp.total_tiles;
             if (!(jb.tile_begin <= t && t < next)) fail("group lookup found the wrong job");
+            const int nreads = (with_acc ? 2 : 1) * R;
             tile_elements(jb.len, jb.phase, t - jb.tile_begin, bp.tile_elems, unroll, [&](int64_t e, int bytes) {
                 for (int i = 0; i < bytes / 4; ++i) {
                     if (e + i >= jb.len) fail("batched element outside its job");
                     else seen[lo][e + i] += 1;
                 }
-                for (int k = 0; k < ptrs_per_job; ++k) {
+                for (int k = 0; k < nreads; ++k) {
                     const uintptr_t ad = (uintptr_t)bp.ptrs[(size_t)lo * ptrs_per_job + k] + (uintptr_t)(e * 4);
-                    if (!inside(ad, bytes)) fail("batched access outside its buffer");
-                    if (ad % 4) fail("batched access off the element grid");
+                    if (!inside(ad, bytes)) fail("batched read outside its buffer");
+                    if (ad % 4) fail("batched read off the element grid");
                 }
             });
+            for (int r = 0; r < R; ++r) {
+                const uintptr_t base = (uintptr_t)bp.ptrs[(size_t)lo * ptrs_per_job + nreads + r];
+                WriteCount& wc = bwrites[lo][r];
+                tile_elements(jb.len, jb.phase, t - jb.tile_begin, bp.tile_elems, unroll,
+                              [&](int64_t e, int bytes) { count_write(wc, base, e, bytes, jb.len, "batched"); });
+            }
         }
-        for (size_t j = 0; j < bp.jobs.size(); ++j)
+        for (size_t j = 0; j < bp.jobs.size(); ++j) {
             for (int64_t e = 0; e < bp.jobs[j].len; ++e)
                 if (seen[j][e] != 1) {
                     fail("batched job element not produced exactly once");
                     break;
                 }
+            for (int r = 0; r < R; ++r) expect_once(bwrites[j][r], "batched job output");
+        }
         ++batches;
     }
     // copy batches: all_to_all_single and the list form of all_gather; every
@@ -501,16 +558,28 @@ int main(int argc, char** argv) {
                 }
             };
             visit_copy_tile([&](int64_t el, int bytes) {
-                for (int k = 0; k < per_job; ++k) {
-                    const uintptr_t ad = (uintptr_t)bp.ptrs[(size_t)lo * per_job + k] + (uintptr_t)(el * 4);
-                    if (!inside(ad, bytes)) fail("copy access outside its buffer");
-                    if (ad % 4) fail("copy access off the element grid");
-                    if (k == 0) continue;
+                const uintptr_t ad = (uintptr_t)bp.ptrs[(size_t)lo * per_job] + (uintptr_t)(el * 4);
+                if (!inside(ad, bytes)) fail("copy read outside its buffer");
+                if (ad % 4) fail("copy read off the element grid");
+            });
+            for (int k = 1; k < per_job; ++k) {
+                const uintptr_t base = (uintptr_t)bp.ptrs[(size_t)lo * per_job + k];
+                auto write = [&](int64_t el, int bytes) {
+                    const uintptr_t ad = base + (uintptr_t)(el * 4);
+                    if (!inside(ad, bytes)) fail("copy write outside its buffer");
+                    if (ad % 4) fail("copy write off the element grid");
+                    if (el < 0 || el + bytes / 4 > jb.len) fail("copy write outside its job");
                     for (Dst& d : dsts)
                         if (ad >= d.lo && ad < d.lo + (uintptr_t)d.n * 4)
                             for (int i = 0; i < bytes / 4; ++i) d.hits[(ad - d.lo) / 4 + i] += 1;
+                };
+                if (bp.full_tiles) {
+                    for (int64_t el = v.second * bp.tile_elems; el < (v.second + 1) * bp.tile_elems; el += kVec)
+                        write(el, 16);
+                } else {
+                    tile_elements(jb.len, jb.phase, v.second, bp.tile_elems, kCopyUnroll, write);
                 }
-            });
+            }
         }
         for (const Dst& d : dsts)
             for (int64_t i = 0; i < d.n; ++i)
@@ -524,8 +593,8 @@ int main(int argc, char** argv) {
     if (iters >= 100 && full_plans == 0) fail("no plan took the whole-tile path");
     if (iters >= 100 && full_copy_batches == 0) fail("no copy batch took the whole-tile path");
     // occupancy tuner: candidates are the rule's W and the two below (never
-    // under 2), each timed kTuneSamples times in turn, and the fastest wins
-    // (ties keep the rule's value); nothing is timed once a value is chosen
+    // under 2), each timed kTuneSamples times in turn, and the lowest median
+    // wins (ties keep the rule's value); nothing is timed once a value is chosen
     for (int rule : {2, 3, 7, 10, 32}) {
         for (int fastest = 0; fastest < kTuneCands; ++fastest) {
             TuneEntry t;
@@ -557,6 +626,27 @@ int main(int argc, char** argv) {
             int c2 = 0;
             if (tune_pick(t, rule, &c2) != want || c2 != -1) fail("tuner still timing after its choice");
         }
+    }
+    {
+        // medians, not best samples: one lucky sample does not win, and a
+        // candidate must beat the rule's W by kTuneMargin
+        auto run = [](const std::vector<std::vector<float>>& samples) {  // [cand][sample], cand 0 = rule
+            TuneEntry t;
+            int c = 0;
+            std::vector<int> next(kTuneCands, 0);
+            for (int i = 0; i < kTuneCands * kTuneSamples; ++i) {
+                tune_pick(t, 7, &c);
+                tune_record(t, c, samples[c][next[c]++]);
+            }
+            return t.chosen;
+        };
+        static_assert(kTuneSamples == 5, "the cases below list five samples per candidate");
+        if (run({{110, 110, 110, 110, 110}, {115, 115, 115, 115, 115}, {90, 80, 130, 130, 130}}) != 7)
+            fail("tuner followed two lucky samples");
+        if (run({{110, 110, 110, 110, 110}, {107.5f, 107.5f, 107.5f, 107.5f, 107.5f}, {120, 120, 120, 120, 120}}) != 7)
+            fail("tuner switched for a gain inside the margin");
+        if (run({{110, 110, 110, 110, 110}, {104, 200, 104, 90, 104}, {120, 120, 120, 120, 120}}) != 6)
+            fail("tuner missed a clear gain");
     }
     {
         TuneEntry t;  // equal times: the rule's value stays

@@ -2,10 +2,11 @@
 (the one the benchmark times).
 
 Where the oracle can run on the whole output in seconds it does (8 x 64 MiB,
-4 x 64 MiB int32, 8 x 256 MiB reduce-scatter); for the 211 GB gradient list
-it checks sampled elements one by one, every segment boundary included, and
-the rest is checked through properties that hold at any size (all ranks
-bit-identical, batched bits equal to single-tensor bits).
+4 x 64 MiB int32, 8 x 256 MiB reduce-scatter and the all_gather of its
+shards); for the 211 GB gradient list it checks five whole tensors of every
+kind (the embedding among them) and sampled elements of all 289, every
+segment boundary included, and the rest through properties that hold at any
+size (all ranks bit-identical, batched bits equal to single-tensor bits).
 """
 
 import numpy as np
@@ -121,11 +122,16 @@ def test_ranks8_256MiB_reduce_scatter_all_gather():
         want = oracle.reduce_scatter(hx, "sum")
         for r in range(R):
             assert_bits(host(shards[r]), want[r], f"reduce_scatter shard {r}")
+        # every rank's whole gathered output against the oracle's all_gather of
+        # the oracle's shards
+        want_gathered = oracle.all_gather(want)
+        for r in range(R):
+            assert_bits(host(gathered[r]), want_gathered[r], f"all_gather rank {r}")
+        del want_gathered
+        # and the invariant all_gather(reduce_scatter(x)) == all_reduce(x)
         for r in range(R):
             assert torch.equal(gathered[r].view(torch.int32), ar[r].view(torch.int32)), \
                 f"all_gather(reduce_scatter(x)) != all_reduce(x) on rank {r}"
-        ranks_identical(gathered, "all_gather")
-        assert_bits(host(gathered[0][:M]), want[0], "gathered shard 0")
     del xs, shards, gathered, ar
     free()
 
@@ -149,6 +155,15 @@ def test_ranks4_llama32_grads_all_reduce_many():
             vals = np.stack([host(x.view(-1)[it]) for x in per])
             got = host(out[t % R].view(-1)[it])
             assert_bits(got, oracle.all_reduce_at_many(vals, idx, n, "mean"), f"tensor {t} {shapes[t]}")
+        # whole tensors against the oracle's fold, tensor by tensor: the
+        # embedding [32000, 4096], an MLP [11008, 4096], an attention
+        # [4096, 4096], the down projection [4096, 11008] and a norm [4096]
+        for t in (0, 5, 1, 7, 8):
+            hx = [host(x).reshape(-1) for x in ts[t]]
+            want = oracle.all_reduce_closed_form(hx, "mean")
+            for r in (0, R - 1):
+                assert_bits(host(outs[t][r]), want, f"tensor {t} {shapes[t]} rank {r}")
+            del hx, want
         # batched bits equal single-tensor bits (embedding, attention, MLP, norm)
         for t in (0, 1, 5, 7, 8, 9, 288):
             single = rr.all_reduce(ts[t], "mean")
