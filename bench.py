@@ -50,7 +50,7 @@ CSRC = ROOT / "rank_reductions_amd" / "csrc"
 KERNEL_SOURCES = [CSRC / n for n in ("tiling.h", "kernels_impl.h", "kernels_fold.hip", "kernels_batch.hip",
                                      "kernels_copy.hip")]
 PROFILES = ROOT / "profiles"
-METRIC_KERNEL = "fold_full_kernel<8, OpSumF32, 1, true, false>"
+METRIC_KERNEL = "fold_table_kernel<8, OpSumF32, 1, true>"
 
 
 def log(msg):
@@ -838,9 +838,9 @@ PROFILE_SETS = {
     "int32_r4_64MiB": {
         "what": "int32, 4 ranks x 16,777,216 (64 MiB) per rank: all_reduce Sum and Max, reduce Sum to root 2, "
                 "broadcast from rank 3",
-        "kernels": {"fold_full_kernel<4, OpSumI32, 1, true, false>": {"per_wg": (4 + 4) * 1024},
-                    "fold_full_kernel<4, OpMaxI32, 1, true, false>": {"per_wg": (4 + 4) * 1024},
-                    "fold_full_kernel<4, OpSumI32, 2, true, false>": {"per_wg": (4 + 1) * 2048},
+        "kernels": {"fold_table_kernel<4, OpSumI32, 1, true>": {"per_wg": (4 + 4) * 1024},
+                    "fold_table_kernel<4, OpMaxI32, 1, true>": {"per_wg": (4 + 4) * 1024},
+                    "fold_table_kernel<4, OpSumI32, 2, true>": {"per_wg": (4 + 1) * 2048},
                     "copy_full_kernel<4, 2, true>": {"per_wg": (1 + 3) * 2048}},
     },
     "rs_ag_r8_f32_256MiB": {
@@ -852,7 +852,7 @@ PROFILE_SETS = {
     "grads_r4_32layer_f32": {
         "what": "4 ranks, the 32-layer transformer gradient list (289 fp32 tensors, 26.4 GB per rank): "
                 "all_reduce_many Mean, then the parameter-keyed sync fused with gradient accumulation",
-        "kernels": {"fold_full_kernel<4, OpSumF32, 1, true, false>": {"per_wg": (4 + 4) * 1024},
+        "kernels": {"fold_table_kernel<4, OpSumF32, 1, true>": {"per_wg": (4 + 4) * 1024},
                     "fold_full_kernel<4, OpSumF32, 1, true, true>": {"per_wg": (8 + 4) * 1024},
                     "batch_kernel<4, OpSumF32, 2, true, false>": {"per_call": 64 * 4096 * 4 * 8},
                     "batch_kernel<4, OpSumF32, 1, true, true>": {"per_call": 64 * 4096 * 4 * 12}},
@@ -967,7 +967,7 @@ def run_profile_set(name, torch, rr, si, dev):
 
 def _short_name(name):
     s = name.replace("void ", "").replace("rc::(anonymous namespace)::", "").replace("rc::", "")
-    s = re.sub(r"\((JobArgs|BatchArgs|CopyArgs|TableChunk)\)$", "", s.strip())
+    s = re.sub(r"\((JobArgs|BatchArgs|CopyArgs|TableChunk|FoldTable)\)$", "", s.strip())
     return s.strip()
 
 

@@ -34,9 +34,34 @@ void* g_scratch_ptr[kMaxDevices] = {};
 
 // ---------------------------------------------------------------- launches
 
+// The FoldTable of a whole-tile fold without accumulators: job c's operands
+// in ring order at its first element, its output mask.
+FoldTable fold_table_of(const LaunchPlan& p) {
+    const JobArgs& a = p.args;
+    FoldTable t{};
+    for (int c = 0; c < a.jobs; ++c) {
+        for (int k = 0; k < p.nin; ++k)
+            t.in[c][k] = static_cast<const uint32_t*>(a.in[fold_rank(c, k, p.nin)]) + (int64_t)c * a.in_stride;
+        t.mask[c] = out_mask_of(a.out_mode, a.out_mask, c);
+    }
+    for (int r = 0; r < a.nranks; ++r) t.out[r] = a.out[r];
+    t.out_stride = a.out_stride;
+    t.mean = a.mean;
+    return t;
+}
+
 hipError_t launch_jobs(const LaunchPlan& p, hipStream_t stream) {
     const bool nt = p.args.nontemporal != 0;
     const bool full = p.args.full_tiles != 0;
+    if (full && p.args.in_mode == kInFold && !p.acc) {
+        const bool u1 = p.nin >= 4 && p.nin < 8 && p.unroll == 1;
+        FoldTableFn tf;
+        if (p.dtype == RC_F32) tf = nt ? fold_table_fn_f32_nt(p.op, u1, p.nin) : fold_table_fn_f32_cached(p.op, u1, p.nin);
+        else tf = nt ? fold_table_fn_i32_nt(p.op, u1, p.nin) : fold_table_fn_i32_cached(p.op, u1, p.nin);
+        if (!tf || p.unroll != (u1 ? 1 : unroll_for(p.nin))) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(tf, dim3(p.grid, p.grid_y), dim3(kBlock), p.lds_bytes, stream, fold_table_of(p));
+        return hipGetLastError();
+    }
     FoldFn fn;
     if (p.args.in_mode == kInCopy) {
         fn = copy_fn(nt, full, p.args.nranks);

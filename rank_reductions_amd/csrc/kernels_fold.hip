@@ -17,43 +17,70 @@ constexpr bool kNt = RC_KNT != 0;
 using SumOp = std::conditional_t<RC_KDT == RC_F32, OpSumF32, OpSumI32>;
 using MaxOp = std::conditional_t<RC_KDT == RC_F32, OpMaxF32, OpMaxI32>;
 
-// U1: the whole-tile all-reduce of 4-7 ranks with one vector per lane (the
-// planner halves its tiles); every other launch uses kUnroll.
-template <class Op, bool ACC, bool FULL, bool U1>
+// General folds (JobArgs), and whole-tile folds with accumulators; unroll kUnroll.
+template <class Op, bool ACC, bool FULL>
 struct FoldOf {
     template <int NIN>
     struct At {
         static FoldFn get() {
-            if constexpr (FULL && U1 && NIN >= 4 && NIN < 8 && !ACC) return fold_full_kernel<NIN, Op, 1, kNt, ACC>;
-            else if constexpr (FULL) return fold_full_kernel<NIN, Op, kUnroll<NIN, ACC>, kNt, ACC>;
+            if constexpr (FULL) return fold_full_kernel<NIN, Op, kUnroll<NIN, ACC>, kNt, ACC>;
             else return fold_kernel<NIN, Op, kUnroll<NIN, ACC>, kNt, ACC>;
         }
     };
 };
 
-template <bool FULL, bool U1>
+template <bool FULL>
 FoldFn pick(int op, bool acc, int nin) {
-    if (op == RC_MAX) return acc ? nullptr : pick_nin<FoldOf<MaxOp, false, FULL, U1>::template At, FoldFn>(nin);
-    if (acc) return pick_nin<FoldOf<SumOp, true, FULL, false>::template At, FoldFn>(nin);
-    return pick_nin<FoldOf<SumOp, false, FULL, U1>::template At, FoldFn>(nin);
+    if constexpr (FULL) {
+        // whole-tile folds without accumulators run fold_table_kernel
+        if (!acc || op == RC_MAX) return nullptr;
+        return pick_nin<FoldOf<SumOp, true, true>::template At, FoldFn>(nin);
+    } else {
+        if (op == RC_MAX) return acc ? nullptr : pick_nin<FoldOf<MaxOp, false, false>::template At, FoldFn>(nin);
+        if (acc) return pick_nin<FoldOf<SumOp, true, false>::template At, FoldFn>(nin);
+        return pick_nin<FoldOf<SumOp, false, false>::template At, FoldFn>(nin);
+    }
+}
+
+// U1: the whole-tile all-reduce of 4-7 ranks with one vector per lane (the
+// planner halves its tiles); every other whole-tile fold uses kUnroll.
+template <class Op, bool U1>
+struct TableOf {
+    template <int NIN>
+    struct At {
+        static FoldTableFn get() {
+            if constexpr (U1 && NIN >= 4 && NIN < 8) return fold_table_kernel<NIN, Op, 1, kNt>;
+            else return fold_table_kernel<NIN, Op, kUnroll<NIN, false>, kNt>;
+        }
+    };
+};
+
+FoldTableFn pick_table(int op, bool u1, int nin) {
+    if (op == RC_MAX) return u1 ? pick_nin<TableOf<MaxOp, true>::template At, FoldTableFn>(nin)
+                                : pick_nin<TableOf<MaxOp, false>::template At, FoldTableFn>(nin);
+    return u1 ? pick_nin<TableOf<SumOp, true>::template At, FoldTableFn>(nin)
+              : pick_nin<TableOf<SumOp, false>::template At, FoldTableFn>(nin);
 }
 
 FoldFn pick_any(int op, bool acc, bool full, bool u1, int nin) {
-    if (!full) return pick<false, false>(op, acc, nin);
-    if (u1 && !acc) return pick<true, true>(op, acc, nin);
-    return pick<true, false>(op, acc, nin);
+    (void)u1;
+    return full ? pick<true>(op, acc, nin) : pick<false>(op, acc, nin);
 }
 
 }  // namespace
 
 #if RC_KDT == RC_F32 && RC_KNT
 FoldFn fold_fn_f32_nt(int op, bool acc, bool full, bool u1, int nin) { return pick_any(op, acc, full, u1, nin); }
+FoldTableFn fold_table_fn_f32_nt(int op, bool u1, int nin) { return pick_table(op, u1, nin); }
 #elif RC_KDT == RC_F32
 FoldFn fold_fn_f32_cached(int op, bool acc, bool full, bool u1, int nin) { return pick_any(op, acc, full, u1, nin); }
+FoldTableFn fold_table_fn_f32_cached(int op, bool u1, int nin) { return pick_table(op, u1, nin); }
 #elif RC_KNT
 FoldFn fold_fn_i32_nt(int op, bool acc, bool full, bool u1, int nin) { return pick_any(op, acc, full, u1, nin); }
+FoldTableFn fold_table_fn_i32_nt(int op, bool u1, int nin) { return pick_table(op, u1, nin); }
 #else
 FoldFn fold_fn_i32_cached(int op, bool acc, bool full, bool u1, int nin) { return pick_any(op, acc, full, u1, nin); }
+FoldTableFn fold_table_fn_i32_cached(int op, bool u1, int nin) { return pick_table(op, u1, nin); }
 #endif
 
 }  // namespace rc

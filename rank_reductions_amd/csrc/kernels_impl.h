@@ -327,6 +327,22 @@ __global__ __launch_bounds__(kBlock) void fold_full_kernel(JobArgs a) {
                                              a.mean != 0);
 }
 
+// The whole-tile fold over a FoldTable: workgroup (x, y) = (tile, job).
+template <int NIN, class Op, int U, bool NT>
+__global__ __launch_bounds__(kBlock) void fold_table_kernel(FoldTable a) {
+    const int c = blockIdx.y;
+    const int64_t e0 = (int64_t)blockIdx.x * (kBlock * kVec * U);
+    const uint32_t* in[NIN];
+    const uint32_t* none[NIN];
+#pragma unroll
+    for (int k = 0; k < NIN; ++k) {
+        in[k] = static_cast<const uint32_t*>(a.in[c][k]) + e0;
+        none[k] = nullptr;
+    }
+    const Outs<NIN> out = outs_of<NIN>(a.out, (int64_t)c * a.out_stride + e0);
+    vec_round<NIN, NIN, Op, U, NT, false, true>(in, none, 0, 0, out, a.mask[c], a.mean != 0);
+}
+
 template <int NR, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void copy_full_kernel(JobArgs a) {
     const int c = blockIdx.y;
