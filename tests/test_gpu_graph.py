@@ -103,3 +103,48 @@ def test_batched_all_reduce_refuses_capture():
         for t in range(3):
             want = oracle.all_reduce_closed_form([host(x) for x in ts[t]], "mean")
             assert_bits(host(got[t][0]), want, f"tensor {t} after the refused capture")
+
+
+def test_static_batched_all_reduce_replays():
+    """rc_all_reduce_many_static captured into a graph: its table writes are
+    kernels whose words travel in the kernel arguments, so each replay
+    rewrites the static scratch before the batched fold reads it, even after
+    eager static calls of another batch have left their own tables there."""
+    R = 4
+    shapes = [(2048, 4096), (4096,), (4096,), (1000,), (257,), (3,), ()]  # the first gets its own launch
+    other = [(513,), (2048,), (9,)]
+
+    def make(shps, seed):
+        return [[si.torch_tensor_for(seed, t, R, r, s, device=DEV) for r in range(R)] for t, s in enumerate(shps)]
+
+    ts = make(shapes, 740)
+    outs = [[torch.empty_like(x) for x in per] for per in ts]
+    ots = make(other, 741)
+    with session(R, device=0):
+        rr.all_reduce_many_static(ts, "mean", out=outs)  # warm-up outside the capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            rr.all_reduce_many_static(ts, "mean", out=outs)
+        for rep in range(4):
+            fresh = make(shapes, 750 + rep)
+            for per, fper in zip(ts, fresh):
+                for x, f in zip(per, fper):
+                    x.copy_(f)
+            # eager static call of another batch: its tables overwrite the scratch
+            got_other = rr.all_reduce_many_static(ots, "sum")
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            eager = rr.all_reduce_many(ts, "mean")
+            torch.cuda.synchronize()
+            for t in range(len(shapes)):
+                for r in range(R):
+                    assert torch.equal(outs[t][r].view(torch.int32), eager[t][r].view(torch.int32)), (
+                        f"replay {rep} tensor {t} rank {r} differs from the eager batch")
+            for t in (0, 3, len(shapes) - 1):
+                hx = [host(x).reshape(-1) for x in ts[t]]
+                assert_bits(host(outs[t][rep % R]).reshape(-1), oracle.all_reduce(hx, "mean")[0],
+                            f"replay {rep} tensor {t} vs oracle")
+            hx = [host(x).reshape(-1) for x in ots[1]]
+            assert_bits(host(got_other[1][0]).reshape(-1), oracle.all_reduce(hx, "sum")[0], f"other batch {rep}")
