@@ -434,11 +434,13 @@ def prepared_all_gather_list(torch, rr, shards, outs):
     return call
 
 
-def small_latency(torch, rr, si, dev, calls=200):
+def small_latency(torch, rr, si, dev, scratch, sink, calls=200):
     """The pages' own example size (4 ranks x 257 fp32): launch-bound, so
     microseconds per call: device time of back-to-back calls, host time to
-    issue one call through the C ABI, and the device time per call when
-    `calls` calls are captured in one HIP graph and replayed."""
+    issue one call through the C ABI, the device time per call when `calls`
+    calls are captured in one HIP graph and replayed, and the median of
+    calls timed one at a time after a cache flush (HIP events around the
+    call alone: the fixed cost that every one-at-a-time timing carries)."""
     w = si.WORKLOADS["ranks4_257_f32"]
     R, n = w["R"], w["N"]
     xs = si.torch_rank_inputs(R, n, "f32", w["dist"], w["seed"], device=dev)
@@ -480,9 +482,11 @@ def small_latency(torch, rr, si, dev, calls=200):
             for _ in range(calls):
                 call(cap)
         replay_ms = time_calls(torch, g.replay, 10, warmup=2)
-        res[name] = {"us_per_call": round(dev_us, 2), "host_issue_us": round(host_us, 2),
-                     "graph_replay_us_per_call": round(replay_ms * 1e3 / calls, 2)}
         del g
+        single = cold_samples(torch, lambda: call(cur), 30, scratch, sink)
+        res[name] = {"us_per_call": round(dev_us, 2), "host_issue_us": round(host_us, 2),
+                     "graph_replay_us_per_call": round(replay_ms * 1e3 / calls, 2),
+                     "one_at_a_time_flushed_median_us": round(single[len(single) // 2] * 1e3, 2)}
     rr.finish()
     return res
 
@@ -492,10 +496,10 @@ def rows(torch, rr, si, dev, xs8, args):
     out = {}
     R, N = len(xs8), xs8[0].numel()
     b = N * 4
-    log("bench: rows: small-message latency (4 x 257), back to back and graph-replayed")
-    out["latency_r4_257_f32"] = small_latency(torch, rr, si, dev)
     scratch = torch.empty(128 << 20, dtype=torch.float32, device=dev)  # 512 MiB, twice the cache
     sink = torch.empty(1, dtype=torch.float32, device=dev)
+    log("bench: rows: small-message latency (4 x 257), back to back, graph-replayed and one at a time")
+    out["latency_r4_257_f32"] = small_latency(torch, rr, si, dev, scratch, sink)
 
     def flushed(fn, iters=15):
         s = cold_samples(torch, fn, iters, scratch, sink)
@@ -855,10 +859,13 @@ PROFILE_SETS = {
         # profiled as the metric is measured: the same timed loop, steps and warm-up
         "args": "--no-rows --no-cpu-baseline --steps 20 --warmup 5",
         "timed_launches": 40,  # the last launches of the metric kernel: 20 steps of Sum + Mean
+        "steady": 40,
     },
     "int32_r4_64MiB": {
         "what": "int32, 4 ranks x 16,777,216 (64 MiB) per rank: all_reduce Sum and Max, reduce Sum to root 2, "
-                "broadcast from rank 3",
+                "broadcast from rank 3; each back to back over rotating buffer sets (cold data), as the bench "
+                "rows time them",
+        "steady": 30,
         "kernels": {"fold_table_kernel<4, OpSumI32, 1, true>": {"per_wg": (4 + 4) * 1024},
                     "fold_table_kernel<4, OpMaxI32, 1, true>": {"per_wg": (4 + 4) * 1024},
                     "fold_table_kernel<4, OpSumI32, 2, true>": {"per_wg": (4 + 1) * 2048},
@@ -873,16 +880,18 @@ PROFILE_SETS = {
     "grads_r4_32layer_f32": {
         "what": "4 ranks, the 32-layer transformer gradient list (289 fp32 tensors, 26.4 GB per rank): "
                 "all_reduce_many Mean, then the parameter-keyed sync fused with gradient accumulation",
-        "kernels": {"fold_table_kernel<4, OpSumF32, 1, true>": {"per_wg": (4 + 4) * 1024},
-                    "fold_full_kernel<4, OpSumF32, 1, true, true>": {"per_wg": (8 + 4) * 1024},
-                    "batch_kernel<4, OpSumF32, 2, true, false>": {"per_call": 64 * 4096 * 4 * 8},
-                    "batch_kernel<4, OpSumF32, 1, true, true>": {"per_call": 64 * 4096 * 4 * 12}},
+        # steady: the launches of the last two calls (225 own launches per call of the list)
+        "kernels": {"fold_table_kernel<4, OpSumF32, 1, true>": {"per_wg": (4 + 4) * 1024, "steady": 450},
+                    "fold_full_kernel<4, OpSumF32, 1, true, true>": {"per_wg": (8 + 4) * 1024, "steady": 450},
+                    "batch_kernel<4, OpSumF32, 2, true, false>": {"per_call": 64 * 4096 * 4 * 8, "steady": 2},
+                    "batch_kernel<4, OpSumF32, 1, true, true>": {"per_call": 64 * 4096 * 4 * 12, "steady": 2}},
     },
     "copies_r8_f32_64MiB": {
-        "what": "send/recv of 64 MiB fp32, all_to_all_single of 8 x 64 MiB, the list all_gather of 8 shards "
-                "of 8 MiB, and an all_reduce of 8 x 64 MiB over views off the 16-byte grid (inputs at 0-3 "
-                "elements, outputs at 1-3-0 elements into their buffers: the whole-tile fold, most streams "
-                "off its reference's grid)",
+        "what": "send/recv of 64 MiB fp32 and the list all_gather of 8 shards of 8 MiB, each back to back over "
+                "rotating buffer sets (cold data), all_to_all_single of 8 x 64 MiB, and an all_reduce of 8 x 64 MiB "
+                "over views off the 16-byte grid (inputs at 0-3 elements, outputs at 1-3-0 elements into their "
+                "buffers: the whole-tile fold, most streams off its reference's grid)",
+        "steady": 30,
         "kernels": {"copy_full_kernel<1, 2, true>": {"per_wg": (1 + 1) * 2048},
                     "copy_args_full_kernel<1, 2, true>": {"per_wg": (1 + 1) * 2048},
                     "copy_args_full_kernel<8, 2, true>": {"per_wg": (1 + 8) * 2048},
@@ -909,10 +918,18 @@ def run_profile_set(name, torch, rr, si, dev):
         raise SystemExit(f"unknown profile set {name!r}; sets: {', '.join(PROFILE_SETS)}")
     log(f"bench: profile set {name}: {PROFILE_SETS[name]['what']}")
     reps, warm = 4, 18
+    steady = PROFILE_SETS[name].get("steady", reps)
 
     def rep(fn, n=reps):
         for _ in range(warm + n):
             fn()
+        torch.cuda.synchronize()
+
+    def rot(fns, n=steady):
+        """Back to back over rotating buffer sets, as the bench rows time
+        them: every call reads data that is not in the Infinity Cache."""
+        for i in range(warm + n):
+            fns[i % len(fns)]()
         torch.cuda.synchronize()
 
     if name == "all_reduce_r8_f32_64MiB":
@@ -923,15 +940,17 @@ def run_profile_set(name, torch, rr, si, dev):
         rep(lambda: (rr.all_reduce(xs, "sum", out=o), rr.all_reduce(xs, "mean", out=o)))
     elif name == "int32_r4_64MiB":
         w = si.WORKLOADS["ranks4_64MiB_i32"]
-        R = w["R"]
-        xs = si.torch_rank_inputs(R, w["N"], "i32", "int", w["seed"], device=dev)
-        o = [torch.empty_like(x) for x in xs]
+        R, N = w["R"], w["N"]
+        K = rotation_sets(2 * R * N * 4)
+        xi = [si.torch_rank_inputs(R, N, "i32", "int", w["seed"] + 100 * k, device=dev) for k in range(K)]
+        oi = [[torch.empty_like(x) for x in xk] for xk in xi]
         rr.register(R, device=0)
-        rep(lambda: rr.all_reduce(xs, "sum", out=o))
-        rep(lambda: rr.all_reduce(xs, "max", out=o))
-        rep(lambda: rr.reduce(xs, 2, "sum", out=[o[r] if r == 2 else None for r in range(R)]))
-        rep(lambda: rr.broadcast([xs[3] if r == 3 else None for r in range(R)],
-                                 out=[o[r] if r != 3 else None for r in range(R)]))
+        rot([prepared(torch, rr, "rc_all_reduce", xi[k], oi[k], "sum") for k in range(K)])
+        rot([prepared(torch, rr, "rc_all_reduce", xi[k], oi[k], "max") for k in range(K)])
+        rot([prepared(torch, rr, "rc_reduce", xi[k], [oi[k][r] if r == 2 else None for r in range(R)], "sum", 2)
+             for k in range(K)])
+        rot([prepared(torch, rr, "rc_broadcast", [xi[k][3] if r == 3 else None for r in range(R)],
+                      [oi[k][r] if r != 3 else None for r in range(R)], "sum", 3) for k in range(K)])
     elif name == "rs_ag_r8_f32_256MiB":
         w = si.WORKLOADS["ranks8_256MiB_f32_rs_ag"]
         R, N = w["R"], w["N"]
@@ -967,16 +986,24 @@ def run_profile_set(name, torch, rr, si, dev):
         xs = si.torch_rank_inputs(R, N, "f32", w["dist"], w["seed"], device=dev)
         o = [torch.empty_like(x) for x in xs]
         rr.register(R, device=0)
-        rep(lambda: rr.send_recv(xs[0], 0, 1, out=o[1]))
-        rep(lambda: rr.all_to_all_single(xs, out=o))
+        K = rotation_sets(2 * N * 4)
+        sx = [torch.empty(N, dtype=torch.float32, device=dev).normal_() for _ in range(K)]
+        sy = [torch.empty_like(x) for x in sx]
+        rot([prepared_send_recv(torch, rr, sx[k], sy[k], 0, 1) for k in range(K)], max(steady, 4 * K))
+        del sx, sy
+        rep(lambda: rr.all_to_all_single(xs, out=o), steady)
         M = N // R
-        lst = [[o[r][k * M:(k + 1) * M] for k in range(R)] for r in range(R)]
-        rep(lambda: rr.all_gather_list([x[:M] for x in xs], out=lst))
+        K = rotation_sets((R + R * R) * M * 4)
+        shards = [[torch.empty(M, dtype=torch.float32, device=dev).normal_() for _ in range(R)] for _ in range(K)]
+        lst = [[[torch.empty(M, dtype=torch.float32, device=dev) for _ in range(R)] for _ in range(R)]
+               for _ in range(K)]
+        rot([prepared_all_gather_list(torch, rr, shards[k], lst[k]) for k in range(K)])
+        del shards, lst
         base_in = si.torch_rank_inputs(R, N + 3, "f32", "normal", 1, device=dev)
         base_out = [torch.empty_like(x) for x in base_in]
         xm = [base_in[r][r % 4:r % 4 + N] for r in range(R)]
         om = [base_out[r][(r + 1) % 4:(r + 1) % 4 + N] for r in range(R)]
-        rep(lambda: rr.all_reduce(xm, "sum", out=om))
+        rep(lambda: rr.all_reduce(xm, "sum", out=om), steady)
     rr.finish()
     src = torch.empty(128 << 20, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
@@ -1055,8 +1082,12 @@ def summarize_profile(dir_, name):
           "Commands (MI355X, ROCm 7.2), then `python3 bench.py --summarize-profile "
           f"gpurun_out/prof_{name} --profile {name}` to write this file:", ""]
     md += [f"    {c}" for c in cmds]
-    md += ["", "| kernel | calls | avg us | min us | max us | alg. bytes per call | achieved GB/s | % of 8 TB/s |"
-               " counter bytes / alg. bytes |", "|---|---|---|---|---|---|---|---|---|"]
+    def steady_of(k):
+        return spec["kernels"][k].get("steady", spec.get("steady", 4))
+
+    md += ["", "| kernel | calls | avg us | min us | max us | last n | last n avg us | alg. bytes per call | "
+               "achieved GB/s (last n) | % of 8 TB/s | counter bytes / alg. bytes |",
+           "|---|---|---|---|---|---|---|---|---|---|---|"]
     tr = [f"# HBM traffic per launch of the {name} set's kernels, from rocprofv3 PMC counters.",
           "# FETCH_SIZE and WRITE_SIZE are KiB per dispatch; each is scaled by what it reads for a plain",
           f"# 512 MiB torch copy in the same run (FETCH_SIZE {calib['FETCH_SIZE']:.1f} KiB, WRITE_SIZE "
@@ -1066,11 +1097,13 @@ def summarize_profile(dir_, name):
     tr.append(f"write_scale = {scale['WRITE_SIZE']:.6f}" if scale["WRITE_SIZE"] else "write_scale = none")
     for k in spec["kernels"]:
         if k not in per:
-            md.append(f"| `{k}` | 0 | | | | | | | |")
+            md.append(f"| `{k}` | 0 | | | | | | | | | |")
             continue
         ds = [d for d, _ in per[k]]
-        alg = sum(alg_bytes(k, wg) for _, wg in per[k])
-        gbps = alg / (sum(ds) * 1e-6) / 1e9
+        last = per[k][-steady_of(k):]
+        last_avg = sum(d for d, _ in last) / len(last)
+        alg = sum(alg_bytes(k, wg) for _, wg in last)
+        gbps = alg / (sum(d for d, _ in last) * 1e-6) / 1e9
         ratio = ""
         fget, wget = counters["FETCH_SIZE"].get(k), counters["WRITE_SIZE"].get(k)
         if fget and wget and scale["FETCH_SIZE"] and scale["WRITE_SIZE"]:
@@ -1084,7 +1117,8 @@ def summarize_profile(dir_, name):
                    f"{k}.write_bytes_per_launch = {wb:.0f}",
                    f"{k}.traffic_over_algorithmic = {ratio}"]
         md.append(f"| `{k}` | {len(ds)} | {sum(ds) / len(ds):.1f} | {min(ds):.1f} | {max(ds):.1f} | "
-                  f"{alg / len(ds):.0f} | {gbps:.1f} | {100 * gbps / HBM_PEAK_GBPS:.1f}% | {ratio} |")
+                  f"{len(last)} | {last_avg:.1f} | {alg / len(last):.0f} | {gbps:.1f} | {100 * gbps / HBM_PEAK_GBPS:.1f}% | "
+                  f"{ratio} |")
     timed = spec.get("timed_launches")
     if timed and per.get(METRIC_KERNEL):
         last = [d for d, _ in per[METRIC_KERNEL][-timed:]]
@@ -1096,7 +1130,8 @@ def summarize_profile(dir_, name):
     if copy_us:
         md += ["", f"Torch copies in the traced run (host reads and the 512 MiB calibration copy): "
                    f"{len(copy_us)}, the longest {max(copy_us):.1f} us."]
-    md += ["", "Averages include every call of the run, the occupancy tuner's calibrating launches among them.",
+    md += ["", "`avg`, `min` and `max` cover every call of the run, the occupancy tuner's calibrating launches "
+               "among them; the achieved rate is over each kernel's last n launches, after the tuner settled.",
            "Algorithmic bytes: what the collective must read and write (each input element once, each output "
            "element once); the last column is the counters' scaled bytes over those.",
            f"Kernel sources sha256: {sha}"]
