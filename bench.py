@@ -890,12 +890,12 @@ PROFILE_SETS = {
         "what": "send/recv of 64 MiB fp32 and the list all_gather of 8 shards of 8 MiB, each back to back over "
                 "rotating buffer sets (cold data), all_to_all_single of 8 x 64 MiB, and an all_reduce of 8 x 64 MiB "
                 "over views off the 16-byte grid (inputs at 0-3 elements, outputs at 1-3-0 elements into their "
-                "buffers: the whole-tile fold, most streams off its reference's grid)",
+                "buffers: the whole-tile fold with outputs shifted onto their 64-byte bursts)",
         "steady": 30,
         "kernels": {"copy_full_kernel<1, 2, true>": {"per_wg": (1 + 1) * 2048},
                     "copy_args_full_kernel<1, 2, true>": {"per_wg": (1 + 1) * 2048},
                     "copy_args_full_kernel<8, 2, true>": {"per_wg": (1 + 8) * 2048},
-                    METRIC_KERNEL: {"per_wg": (8 + 8) * 1024}},
+                    "fold_table_shift_kernel<8, OpSumF32, 1, true>": {"per_wg": (8 + 8) * 1024}},
     },
 }
 

@@ -55,11 +55,16 @@ hipError_t launch_jobs(const LaunchPlan& p, hipStream_t stream) {
     const bool full = p.args.full_tiles != 0;
     if (full && p.args.in_mode == kInFold && !p.acc) {
         const bool u1 = p.nin >= 4 && p.nin < 8 && p.unroll == 1;
+        const bool sh = p.shift_out;
         FoldTableFn tf;
-        if (p.dtype == RC_F32) tf = nt ? fold_table_fn_f32_nt(p.op, u1, p.nin) : fold_table_fn_f32_cached(p.op, u1, p.nin);
-        else tf = nt ? fold_table_fn_i32_nt(p.op, u1, p.nin) : fold_table_fn_i32_cached(p.op, u1, p.nin);
+        if (p.dtype == RC_F32)
+            tf = nt ? fold_table_fn_f32_nt(p.op, u1, sh, p.nin) : fold_table_fn_f32_cached(p.op, u1, sh, p.nin);
+        else
+            tf = nt ? fold_table_fn_i32_nt(p.op, u1, sh, p.nin) : fold_table_fn_i32_cached(p.op, u1, sh, p.nin);
         if (!tf || p.unroll != (u1 ? 1 : unroll_for(p.nin))) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(tf, dim3(p.grid, p.grid_y), dim3(kBlock), p.lds_bytes, stream, fold_table_of(p));
+        // the shifted kernel stages a round in the LDS that caps occupancy
+        const int lds = sh ? std::max(p.lds_bytes, shift_lds_bytes(p.unroll)) : p.lds_bytes;
+        hipLaunchKernelGGL(tf, dim3(p.grid, p.grid_y), dim3(kBlock), lds, stream, fold_table_of(p));
         return hipGetLastError();
     }
     FoldFn fn;

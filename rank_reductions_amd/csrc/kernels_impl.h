@@ -343,6 +343,104 @@ __global__ __launch_bounds__(kBlock) void fold_table_kernel(FoldTable a) {
     vec_round<NIN, NIN, Op, U, NT, false, true>(in, none, 0, 0, out, a.mask[c], a.mean != 0);
 }
 
+// The whole-tile fold over a FoldTable when some written output starts its
+// job off a 64-byte write burst (tiling.h): outputs on a burst boundary are
+// written from registers as by fold_table_kernel, the others over
+// burst-aligned ranges from the round's values staged in LDS behind the
+// pre_vectors folded ahead of the tile.  Tiles go to the XCDs in groups of
+// consecutive ones (xcd_group_tile).  The stage is the dynamic LDS that
+// caps occupancy, at least shift_lds_bytes(U).  A tile writes up to
+// kBurstElems - 1 elements before its own, which the previous tile reads as
+// inputs if an output aliases an input: the planner never picks this kernel
+// for calls in place.
+template <int NIN, class Op, int U, bool NT>
+__global__ __launch_bounds__(kBlock) void fold_table_shift_kernel(FoldTable a) {
+    extern __shared__ uint32_t stage[];
+    constexpr int T = kBlock * kVec * U;
+    const int c = blockIdx.y;
+    const int64_t xt = xcd_group_tile(blockIdx.x, gridDim.x);
+    const int64_t e0 = xt * T;
+    const bool first = xt == 0;
+    const bool last = xt == (int64_t)gridDim.x - 1;
+    const int lane = (int)threadIdx.x;
+    const uint32_t mask = a.mask[c];
+    const bool mean = a.mean != 0;
+    const Outs<NIN> out = outs_of<NIN>(a.out, (int64_t)c * a.out_stride + e0);
+    int mmax = 0;
+#pragma unroll
+    for (int o = 0; o < NIN; ++o)
+        if ((mask >> o) & 1u) mmax = max(mmax, burst_offset(reinterpret_cast<uintptr_t>(out(o))));
+    const int npre = pre_vectors(mmax, first);
+    const uint32_t* in[NIN];
+#pragma unroll
+    for (int k = 0; k < NIN; ++k) in[k] = static_cast<const uint32_t*>(a.in[c][k]) + e0;
+    u32x4 x[U][NIN];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int k = 0; k < NIN; ++k) x[u][k] = ld4<NT>(in[k] + (size_t)((u * kBlock + lane) * kVec));
+    const bool pre = lane < npre;
+    u32x4 xp[NIN];
+    if (pre) {
+#pragma unroll
+        for (int k = 0; k < NIN; ++k) xp[k] = ld4<NT>(in[k] - (int64_t)(npre - lane) * kVec);
+    }
+    out.pin();
+    u32x4 acc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        acc[u] = fold<NIN, Op>(x[u]);
+        if constexpr (Op::kCanMean) {
+            if (mean) acc[u] = mean4<NIN>(acc[u]);
+        }
+    }
+    uint32_t shifted = 0;
+#pragma unroll
+    for (int o = 0; o < NIN; ++o) {
+        if (!((mask >> o) & 1u)) continue;
+        uint32_t* p = out(o);
+        if (burst_offset(reinterpret_cast<uintptr_t>(p))) {
+            shifted |= 1u << o;
+            continue;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) st4<NT>(p + (size_t)((u * kBlock + lane) * kVec), acc[u]);
+    }
+    if (!shifted) return;
+    // stage[j]: the value of element e0 - kBurstElems + j
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        *reinterpret_cast<u32x4*>(&stage[kBurstElems + (u * kBlock + lane) * kVec]) = acc[u];
+    if (pre) {
+        u32x4 ap = fold<NIN, Op>(xp);
+        if constexpr (Op::kCanMean) {
+            if (mean) ap = mean4<NIN>(ap);
+        }
+        *reinterpret_cast<u32x4*>(&stage[kBurstElems - (npre - lane) * kVec]) = ap;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int o = 0; o < NIN; ++o) {
+        if (!((shifted >> o) & 1u)) continue;
+        uint32_t* p = out(o);
+        const int m = burst_offset(reinterpret_cast<uintptr_t>(p));
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int w = (u * kBlock + lane) * kVec;  // the vector's first element in [e0 - m, e0 - m + T)
+            const u32x4 v = *reinterpret_cast<const u32x4m*>(&stage[kBurstElems - m + w]);
+            const int lo = shifted_first(first, w, m);
+            if (lo == 0) {
+                st4<NT>(p + (int64_t)(w - m), v);
+            } else {
+#pragma unroll
+                for (int i = 0; i < kVec; ++i)
+                    if (i >= lo) st1<NT>(p + (int64_t)(w - m + i), v[i]);
+            }
+        }
+        if (shifted_tail(last, m, lane)) st1<NT>(p + (T - m + lane), stage[kBurstElems + T - m + lane]);
+    }
+}
+
 template <int NR, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void copy_full_kernel(JobArgs a) {
     const int c = blockIdx.y;

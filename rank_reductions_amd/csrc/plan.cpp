@@ -183,6 +183,43 @@ void shape_launch(int64_t total_tiles, int nin, int nout, int unroll, const Conf
     *grid = std::max<int64_t>(1, std::min<int64_t>(g, 0x7FFFFFFF));
 }
 
+// Whether a whole-tile fold runs the shifted kernel (tiling.h): some output
+// it writes starts a job off a 64-byte write burst, and no output overlaps
+// an input.  The shifted kernel writes up to kBurstElems - 1 elements ahead
+// of each tile, which the previous tile reads when an output aliases an
+// input (a call in place).
+bool shifted_outputs_pay(const JobArgs& a, int64_t es) {
+    bool off = false;
+    for (int c = 0; c < a.jobs && !off; ++c) {
+        const uint32_t mask = out_mask_of(a.out_mode, a.out_mask, c);
+        for (int o = 0; o < a.nranks; ++o)
+            if (((mask >> o) & 1u) &&
+                burst_offset(reinterpret_cast<uintptr_t>(a.out[o]) + (uintptr_t)((int64_t)c * a.out_stride * es)))
+                off = true;
+    }
+    if (!off) return false;
+    // byte ranges: rank r's input as the jobs read it, output o as they write it
+    int64_t in_end = 0;
+    for (int c = 0; c < a.jobs; ++c)
+        in_end = std::max(in_end, ((int64_t)c * a.in_stride + job_len(a.n, a.seg, c)) * es);
+    for (int o = 0; o < a.nranks; ++o) {
+        int64_t lo = INT64_MAX, hi = INT64_MIN;
+        for (int c = 0; c < a.jobs; ++c) {
+            if (!((out_mask_of(a.out_mode, a.out_mask, c) >> o) & 1u)) continue;
+            lo = std::min(lo, (int64_t)c * a.out_stride * es);
+            hi = std::max(hi, ((int64_t)c * a.out_stride + job_len(a.n, a.seg, c)) * es);
+        }
+        if (lo >= hi) continue;
+        const uintptr_t olo = reinterpret_cast<uintptr_t>(a.out[o]) + (uintptr_t)lo;
+        const uintptr_t ohi = reinterpret_cast<uintptr_t>(a.out[o]) + (uintptr_t)hi;
+        for (int r = 0; r < a.nranks; ++r) {
+            const uintptr_t ilo = reinterpret_cast<uintptr_t>(a.in[r]);
+            if (olo < ilo + (uintptr_t)in_end && ilo < ohi) return false;
+        }
+    }
+    return true;
+}
+
 std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceInfo& dev) {
     std::vector<LaunchPlan> out;
     if (ck.count == 0) return out;
@@ -415,6 +452,7 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceI
         lp.args.full_tiles = full ? 1 : 0;
         lp.grid = std::max<int64_t>(1, widest);
         lp.grid_y = ja.jobs;
+        if (full && ja.in_mode == kInFold && !lp.acc) lp.shift_out = shifted_outputs_pay(lp.args, es);
     }
     return out;
 }

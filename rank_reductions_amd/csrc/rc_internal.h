@@ -150,11 +150,18 @@ struct LaunchPlan {
     int grid_y = 1;          // along y: the jobs, for one-shot launches
     int lds_bytes = 0;       // dynamic LDS per workgroup: caps workgroups per CU
     int waves = 0;           // workgroups (waves) per CU that lds_bytes allows; 0: no cap
+    // a whole-tile fold without accumulators some of whose written outputs
+    // start a job off a 64-byte write burst, and no output overlaps an input:
+    // it runs fold_table_shift_kernel (tiling.h)
+    bool shift_out = false;
 };
 
 // Builds the launches of one validated call: one for most collectives, two
 // for the ring all-reduce.  Empty when there is nothing to do.
 std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceInfo& dev);
+// Whether a whole-tile fold of these jobs (element size es) runs the
+// shifted kernel (LaunchPlan::shift_out).
+bool shifted_outputs_pay(const JobArgs& a, int64_t es);
 
 // Batched all-reduce: job and pointer tables for tensors [t0, t1).
 struct BatchPlan {
@@ -331,11 +338,13 @@ FoldFn fold_fn_f32_nt(int op, bool acc, bool full, bool u1, int nin);
 FoldFn fold_fn_f32_cached(int op, bool acc, bool full, bool u1, int nin);
 FoldFn fold_fn_i32_nt(int op, bool acc, bool full, bool u1, int nin);
 FoldFn fold_fn_i32_cached(int op, bool acc, bool full, bool u1, int nin);
-// Whole-tile folds without accumulators, over a FoldTable (same files).
-FoldTableFn fold_table_fn_f32_nt(int op, bool u1, int nin);
-FoldTableFn fold_table_fn_f32_cached(int op, bool u1, int nin);
-FoldTableFn fold_table_fn_i32_nt(int op, bool u1, int nin);
-FoldTableFn fold_table_fn_i32_cached(int op, bool u1, int nin);
+// Whole-tile folds without accumulators, over a FoldTable (same files);
+// shift: the kernel for launches with outputs off a 64-byte write burst
+// (LaunchPlan::shift_out).
+FoldTableFn fold_table_fn_f32_nt(int op, bool u1, bool shift, int nin);
+FoldTableFn fold_table_fn_f32_cached(int op, bool u1, bool shift, int nin);
+FoldTableFn fold_table_fn_i32_nt(int op, bool u1, bool shift, int nin);
+FoldTableFn fold_table_fn_i32_cached(int op, bool u1, bool shift, int nin);
 // Batched folds (kernels_batch.hip, once per cache hint).
 BatchFn batch_fn_nt(int dtype, int op, bool acc, int nin);
 BatchFn batch_fn_cached(int dtype, int op, bool acc, int nin);

@@ -103,7 +103,8 @@ struct Comm {
 };
 
 // Launch shape for the occupancy tuner: kernel family (fold, copy, copy
-// batch), whole tiles, inputs, accumulators, outputs, unroll and size class.
+// batch), whole tiles (2: whole tiles with outputs shifted onto 64-byte
+// bursts), inputs, accumulators, outputs, unroll and size class.
 using TuneKey = std::tuple<int, int, int, int, int, int, int>;
 
 struct Session {
@@ -328,8 +329,8 @@ Error launch(const Checked& ck, void* stream, bool timed = true) {
             if (e.code) return e;
             continue;
         }
-        const TuneKey key{(int)p.args.in_mode, (int)p.args.full_tiles, p.nin, p.acc ? 1 : 0, p.nout, p.unroll,
-                          size_class(moved)};
+        const TuneKey key{(int)p.args.in_mode, (int)p.args.full_tiles + (p.shift_out ? 1 : 0), p.nin,
+                          p.acc ? 1 : 0, p.nout, p.unroll, size_class(moved)};
         Error e = launch_tuned(key, p.waves, moved, stream, &capturing, timed, [&](int lds) {
             if (lds >= 0) p.lds_bytes = lds;
             return device_launch(p, stream);

@@ -123,6 +123,55 @@ RC_HD int fold_rank(int c, int k, int nranks) {
     return r >= nranks ? r - nranks : r;
 }
 
+// Whole-tile folds with outputs off a 64-byte write burst.  HBM is written
+// in 64-byte bursts: a store that covers part of one costs the memory a
+// read-modify-write.  A job's tiles are whole multiples of 64 bytes, so an
+// output that starts the job m elements past a burst boundary starts every
+// tile m elements past one (burst_offset), and with straight tiles the burst
+// at each tile boundary would be written half by each of two waves.  The
+// shifted whole-tile kernel writes such an output over burst-aligned ranges
+// instead: tile x of T elements writes its elements [x*T - m, (x+1)*T - m),
+// taking the values before its tile from pre_vectors extra vectors that it
+// folds ahead of the tile; the job's first tile skips the elements before
+// the job (lanes whose vector starts fewer than m elements into the shifted
+// range write from element shifted_first on), and its last tile also writes
+// the job's last m elements, lane l < m taking element T - m + l.  Outputs on
+// a boundary are written straight, as by the unshifted kernel.
+constexpr int kBurstBytes = 64;
+constexpr int kBurstElems = kBurstBytes / 4;
+
+RC_HD int burst_offset(uintptr_t addr) { return (int)((addr % kBurstBytes) / 4); }
+
+// Vectors before the tile that a tile folds for outputs up to mmax elements
+// past a burst boundary (none on the job's first tile).
+RC_HD int pre_vectors(int mmax, bool first) { return first ? 0 : (mmax + kVec - 1) / kVec; }
+
+// The first element, of the 4 in the vector w elements into the shifted
+// range [x*T - m, ...), that the tile writes (4: none of them).
+RC_HD int shifted_first(bool first, int64_t w, int m) { return first ? (int)min64(max64(m - w, 0), kVec) : 0; }
+
+// Whether `lane` writes one of the job's last m elements.
+RC_HD bool shifted_tail(bool last, int m, int lane) { return last && lane < m; }
+
+// The shifted kernel's tile for workgroup bx of a job's nx: groups of
+// kXcdGroup consecutive tiles per XCD.  Workgroups go to the 8 XCDs in turn,
+// so without the grouping a tile's neighbour runs on another XCD and the
+// 128-byte line of each operand that the tile reads ahead of itself comes
+// from HBM a second time; grouped, the neighbour that read it a moment
+// before shares the XCD's L2.  Tiles past the last whole group of
+// 8*kXcdGroup keep their place.  A permutation of [0, nx).
+constexpr int kXcdCount = 8;
+constexpr int kXcdGroup = 4;
+RC_HD int64_t xcd_group_tile(int64_t bx, int64_t nx) {
+    constexpr int64_t span = (int64_t)kXcdCount * kXcdGroup;
+    if (bx >= nx / span * span) return bx;
+    return bx / span * span + (bx % kXcdCount) * kXcdGroup + (bx / kXcdCount) % kXcdGroup;
+}
+
+// LDS the shifted kernel stages a round in: the round and the kBurstElems
+// elements before it.
+RC_HD constexpr int shift_lds_bytes(int unroll) { return (kBurstElems + kBlock * kVec * unroll) * 4; }
+
 // One job of a launch over a job table in device memory (the batched
 // all-reduce, and copy batches too large for kernel arguments).
 struct BatchJob {

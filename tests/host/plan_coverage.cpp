@@ -59,6 +59,23 @@ void tile_elements(int64_t len, int phase, int64_t lt, int64_t te, int unroll, F
             if (tid < scalars_of(s, len)) visit(scalar_elem(s, tid), 4);
 }
 
+// fold_table_shift_kernel's writes of one output whose job starts m elements
+// past a 64-byte burst boundary (tiling.h): tile lt of ntiles whole tiles of
+// T elements, shifted onto the output's bursts.
+template <class F>
+void shifted_tile_writes(int64_t lt, int64_t ntiles, int64_t T, int m, F&& visit) {
+    const bool first = lt == 0, last = lt == ntiles - 1;
+    const int64_t e0 = lt * T;
+    for (int64_t w = 0; w < T; w += kVec) {
+        const int lo = shifted_first(first, w, m);
+        if (lo == 0) visit(e0 + w - m, 16);
+        else
+            for (int i = lo; i < kVec; ++i) visit(e0 + w - m + i, 4);
+    }
+    for (int lane = 0; lane < kBlock; ++lane)
+        if (shifted_tail(last, m, lane)) visit(e0 + T - m + lane, 4);
+}
+
 // Elements of one output of one job written per (job-relative) element.
 struct WriteCount {
     std::vector<uint8_t> hits;
@@ -135,6 +152,25 @@ void check_plan(const LaunchPlan& p, const std::string& name) {
     }
     const int64_t total = a.total_tiles;
     if (total != a.tile_prefix[a.jobs] || total != p.total_tiles) fail(name + ": tile totals disagree");
+    if (p.shift_out) {
+        // the shifted kernel only for whole-tile folds, and never where an
+        // output's bytes overlap an input's (its writes ahead of a tile would
+        // race the previous tile's reads)
+        if (!a.full_tiles || a.in_mode != kInFold || p.acc) fail(name + ": shifted kernel off a whole-tile fold");
+        for (int c = 0; c < a.jobs; ++c) {
+            const int64_t len = job_len(a.n, a.seg, c);
+            for (int o = 0; o < a.nranks; ++o) {
+                if (!((out_mask_of(a.out_mode, a.out_mask, c) >> o) & 1u)) continue;
+                const uintptr_t olo = (uintptr_t)a.out[o] + (uintptr_t)(c * a.out_stride * 4);
+                for (int d = 0; d < a.jobs; ++d)
+                    for (int r = 0; r < a.nranks; ++r) {
+                        const uintptr_t ilo = (uintptr_t)a.in[r] + (uintptr_t)(d * a.in_stride * 4);
+                        if (olo < ilo + (uintptr_t)(job_len(a.n, a.seg, d) * 4) && ilo < olo + (uintptr_t)(len * 4))
+                            fail(name + ": shifted kernel with an output over an input");
+                    }
+            }
+        }
+    }
     for (int c = a.jobs; c <= kMaxRanks; ++c)
         if (a.tile_prefix[c] != total) fail(name + ": prefix past the last job is not the total");
     // the (job, tile) pairs the launch visits
@@ -142,8 +178,12 @@ void check_plan(const LaunchPlan& p, const std::string& name) {
     if (a.grid_2d) {
         if (p.grid_y != a.jobs) fail(name + ": 2-D grid height is not the job count");
         for (int c = 0; c < p.grid_y; ++c)
-            for (int64_t lt = 0; lt < p.grid; ++lt)
+            for (int64_t bx = 0; bx < p.grid; ++bx) {
+                // the shifted kernel's workgroup bx takes tile xcd_group_tile(bx)
+                const int64_t lt = p.shift_out ? xcd_group_tile(bx, p.grid) : bx;
+                if (lt < 0 || lt >= p.grid) fail(name + ": grouped tile out of range");
                 if (a.full_tiles || lt < a.tile_prefix[c + 1] - a.tile_prefix[c]) visits.push_back({c, lt});
+            }
         if (a.full_tiles) {
             // the kernels then take every tile as whole: check that it is
             for (int c = 0; c < a.jobs; ++c) {
@@ -209,12 +249,40 @@ void check_plan(const LaunchPlan& p, const std::string& name) {
                 if (ad % 4) fail(name + ": copy read off the element grid");
             }
         });
+        // the shifted kernel's reads ahead of the tile: pre_vectors vectors
+        // of every operand, inside the job and the operand's buffer
+        if (p.shift_out) {
+            int mmax = 0;
+            for (int o = 0; o < a.nranks; ++o)
+                if ((mask >> o) & 1u)
+                    mmax = std::max(mmax, burst_offset((uintptr_t)a.out[o] + (uintptr_t)(c * a.out_stride * 4)));
+            const int npre = pre_vectors(mmax, lt == 0);
+            for (int lane = 0; lane < npre; ++lane) {
+                const int64_t e = lt * a.tile_elems - (int64_t)(npre - lane) * kVec;
+                if (e < 0 || e + kVec > len) fail(name + ": read ahead of a tile outside its job");
+                for (int k = 0; k < p.nin; ++k) {
+                    const uintptr_t ad = (uintptr_t)a.in[(c + 1 + k) % p.nin] + (uintptr_t)(c * a.in_stride * 4) +
+                                         (uintptr_t)(e * 4);
+                    if (!inside(ad, 16)) fail(name + ": read ahead of a tile outside its buffer");
+                }
+            }
+        }
         // writes, output by output, as the kernel makes them
         for (int o = 0; o < a.nranks; ++o) {
             if (!((mask >> o) & 1u)) continue;
             const uintptr_t base = (uintptr_t)a.out[o] + (uintptr_t)(c * a.out_stride * 4);
             WriteCount& wc = writes[c][o];
-            visit_tile([&](int64_t e, int bytes) { count_write(wc, base, e, bytes, len, name); });
+            const int m = p.shift_out ? burst_offset(base) : 0;
+            if (m) {
+                shifted_tile_writes(lt, p.grid, a.tile_elems, m,
+                                    [&](int64_t e, int bytes) { count_write(wc, base, e, bytes, len, name); });
+                // burst-aligned: every 16-byte write starts on a 16-byte boundary
+                shifted_tile_writes(lt, p.grid, a.tile_elems, m, [&](int64_t e, int bytes) {
+                    if (bytes == 16 && (base + (uintptr_t)(e * 4)) % 16) fail(name + ": shifted vector write off grid");
+                });
+            } else {
+                visit_tile([&](int64_t e, int bytes) { count_write(wc, base, e, bytes, len, name); });
+            }
         }
     }
     for (int c = 0; c < a.jobs; ++c)
@@ -368,6 +436,41 @@ int main(int argc, char** argv) {
             if (!p.args.full_tiles || p.unroll != 1 || p.args.tile_elems != kBlock * kVec)
                 fail("whole-tile all-reduce of 4-7 ranks does not run one vector per lane");
         }
+        }
+    }
+    // whole-tile folds with outputs off a 64-byte burst (offsets 0..15
+    // elements): the shifted kernel, except in place
+    int shifted_plans = 0;
+    for (int it = 0; it < iters; ++it) {
+        g_bufs.clear();
+        const int R = 1 + (int)(rng() % 16);
+        // up to 128 tiles per job: several whole groups of tiles per XCD and a partial one
+        const int64_t n = (int64_t)R * 4096 * (int64_t)(1 + rng() % 8);
+        const int coll = (int)(rng() % 3);  // all_reduce, reduce, reduce_scatter
+        const bool in_place = coll == 0 && rng() % 4 == 0;
+        const int op = rng() % 2 ? RC_SUM : RC_MEAN;
+        std::vector<rc_buf> bufs(R);
+        for (int r = 0; r < R; ++r) {
+            const int64_t out_n = coll == 2 ? n / R : n;
+            void* sb = (void*)alloc(n * 4, rng() % 2 ? 0 : (int)(rng() % 16));
+            void* ob = in_place ? sb : (void*)alloc(out_n * 4, (int)(rng() % 16));
+            bufs[r] = make(sb, ob, n, op, coll == 1 ? (int)(it % R) : 0);
+        }
+        Checked ck;
+        const Coll kind = coll == 0 ? Coll::AllReduce : (coll == 1 ? Coll::Reduce : Coll::ReduceScatter);
+        const Error ve = validate(kind, R, bufs.data(), &ck);
+        if (ve.code) {
+            fail("whole-tile fold with outputs off a burst rejected: " + ve.msg);
+            continue;
+        }
+        Config cfg;
+        cfg.algo = rng() % 4 == 0 ? RC_ALGO_RING : RC_ALGO_DIRECT;
+        for (const LaunchPlan& p : plan(ck, cfg, dev)) {
+            check_plan(p, "outputs off a burst: coll " + std::to_string(coll) + " R=" + std::to_string(R) +
+                              (in_place ? " in place" : ""));
+            ++plans;
+            if (p.shift_out) ++shifted_plans;
+            if (in_place && p.shift_out) fail("shifted kernel chosen for a call in place");
         }
     }
     // batched plans: job lookup through the group index, and coverage
@@ -591,6 +694,7 @@ int main(int argc, char** argv) {
         ++copies;
     }
     if (iters >= 100 && full_plans == 0) fail("no plan took the whole-tile path");
+    if (iters >= 100 && shifted_plans == 0) fail("no plan took the shifted whole-tile kernel");
     if (iters >= 100 && full_copy_batches == 0) fail("no copy batch took the whole-tile path");
     // occupancy tuner: candidates are the rule's W and the two below (never
     // under 2), each timed kTuneSamples times in turn, and the lowest median
@@ -657,7 +761,8 @@ int main(int argc, char** argv) {
         }
         if (t.chosen != 7) fail("tuner left the rule's value on a tie");
     }
-    std::printf("checked %d plans (%d whole-tile), %d batches and %d copy batches (%d whole-tile): %d failures\n",
-                plans, full_plans, batches, copies, full_copy_batches, g_fail);
+    std::printf("checked %d plans (%d whole-tile, %d shifted), %d batches and %d copy batches (%d whole-tile): "
+                "%d failures\n",
+                plans, full_plans, shifted_plans, batches, copies, full_copy_batches, g_fail);
     return g_fail ? 1 : 0;
 }

@@ -164,6 +164,73 @@ def test_all_reduce_misaligned_views(R):
                     assert_bits(host(outs[r]), want, f"offsets {offsets} {op} rank {r}")
 
 
+@pytest.mark.parametrize("R", [2, 3, 4, 5, 8, 16])
+@pytest.mark.parametrize("dtype,op", OPS)
+def test_whole_tile_outputs_off_bursts(R, dtype, op):
+    """Whole-tile folds whose outputs start 1-15 elements past a 64-byte
+    boundary (inputs aligned, so the jobs stay whole tiles): the shifted
+    kernel writes each such output over burst-aligned ranges, reaching back
+    up to 15 elements into the previous tile's range and writing a job's
+    last elements from its last tile.  all_reduce (direct and ring), reduce
+    to one root and reduce_scatter, with every byte around the outputs
+    holding a sentinel that must survive; in place runs the unshifted
+    kernel.  Bits against the oracle."""
+    N = R * 8192  # whole tiles of every unroll, several per segment
+    M = N // R
+    PAD = 32
+    offs = [(5 * r) % 16 for r in range(R)]  # rank 0 on a boundary: the aligned class stays the heaviest
+    dist = "int" if dtype == "i32" else "normal"
+    seed = 4500 + 10 * R + OPS.index((dtype, op))
+    xs = gen(R, N, dtype, dist, seed=seed)
+    hx = [host(x).copy() for x in xs]
+    want = oracle.all_reduce_closed_form(hx, op)
+
+    def padded(n):
+        bases = [sentinel_like(torch, torch.empty(n + PAD, dtype=xs[0].dtype, device=DEV)) for _ in range(R)]
+        return bases, [b[o:o + n] for b, o in zip(bases, offs)]
+
+    def check_pads(bases, n, what, written=None):
+        for r, (b, o) in enumerate(zip(bases, offs)):
+            hb = host(b).view(np.uint32)
+            if written is not None and r not in written:
+                assert np.all(hb == SENTINEL), f"{what}: rank {r} written"
+                continue
+            assert np.all(hb[:o] == SENTINEL) and np.all(hb[o + n:] == SENTINEL), \
+                f"{what}: rank {r} written outside its output (offset {o})"
+
+    for algo in ("direct", "ring"):
+        with session(R, algo=algo):
+            bases, outs = padded(N)
+            rr.all_reduce(xs, op, out=outs)
+            sync()
+            for r in range(R):
+                assert_bits(host(outs[r]), want, f"all_reduce {algo} R={R} {dtype} {op} rank {r}")
+            check_pads(bases, N, f"all_reduce {algo}")
+    with session(R):
+        root = R - 1
+        bases, outs = padded(N)
+        rr.reduce(xs, root, op, out=[o if r == root else None for r, o in enumerate(outs)])
+        sync()
+        assert_bits(host(outs[root]), want, f"reduce R={R} {dtype} {op}")
+        check_pads(bases, N, "reduce", written={root})
+        bases, shards = padded(M)
+        rr.reduce_scatter(xs, op, out=shards)
+        sync()
+        for r in range(R):
+            assert_bits(host(shards[r]), want[r * M:(r + 1) * M], f"reduce_scatter R={R} {op} rank {r}")
+        check_pads(bases, M, "reduce_scatter")
+        # in place at the same offsets: the unshifted kernel
+        bases, views = padded(N)
+        for v, x in zip(views, xs):
+            v.copy_(x)
+        rr.all_reduce(views, op, out=views)
+        sync()
+        for r in range(R):
+            assert_bits(host(views[r]), want, f"in place R={R} {op} rank {r}")
+        check_pads(bases, N, "in place")
+    check_unchanged(xs, hx, f"outputs off bursts R={R}")
+
+
 def test_all_reduce_in_place():
     R, N = 8, 200_003
     with session(R):
