@@ -69,7 +69,7 @@ hipError_t launch_jobs(const LaunchPlan& p, hipStream_t stream) {
     }
     FoldFn fn;
     if (p.args.in_mode == kInCopy) {
-        fn = copy_fn(nt, full, p.args.nranks);
+        fn = copy_fn(nt, full, p.shift_out, p.args.nranks);
     } else {
         // the one-vector whole-tile all-reduce of 4-7 ranks (see plan)
         const bool mid = !p.acc && p.nin >= 4 && p.nin < 8;
@@ -80,7 +80,9 @@ hipError_t launch_jobs(const LaunchPlan& p, hipStream_t stream) {
         else fn = nt ? fold_fn_i32_nt(p.op, p.acc, full, u1, p.nin) : fold_fn_i32_cached(p.op, p.acc, full, u1, p.nin);
     }
     if (!fn) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fn, dim3(p.grid, p.grid_y), dim3(kBlock), p.lds_bytes, stream, p.args);
+    // the shifted copy stages a round in the LDS that caps occupancy
+    const int lds = p.shift_out ? std::max(p.lds_bytes, shift_lds_bytes(p.unroll)) : p.lds_bytes;
+    hipLaunchKernelGGL(fn, dim3(p.grid, p.grid_y), dim3(kBlock), lds, stream, p.args);
     return hipGetLastError();
 }
 
@@ -108,7 +110,7 @@ hipError_t launch_batch(const BatchJob* jobs, const int32_t* group_job, const vo
 hipError_t launch_copy_args(const BatchPlan& p, hipStream_t stream) {
     if (!p.by_value || p.jobs.size() > (size_t)kMaxCopyArgJobs || p.ptrs.size() > (size_t)kMaxCopyArgPtrs)
         return hipErrorInvalidValue;
-    CopyArgsFn fn = copy_args_fn(p.nontemporal != 0, p.full_tiles, p.nout);
+    CopyArgsFn fn = copy_args_fn(p.nontemporal != 0, p.full_tiles, p.shift_out, p.nout);
     if (!fn) return hipErrorInvalidValue;
     CopyArgs a{};
     for (size_t i = 0; i < p.ptrs.size(); ++i) a.ptrs[i] = p.ptrs[i];
@@ -118,7 +120,8 @@ hipError_t launch_copy_args(const BatchPlan& p, hipStream_t stream) {
         if (p.jobs[j].len != a.len) return hipErrorInvalidValue;  // equal lengths only
         a.phase[j] = (uint8_t)p.jobs[j].phase;
     }
-    hipLaunchKernelGGL(fn, dim3(p.grid, p.grid_y), dim3(kBlock), p.lds_bytes, stream, a);
+    const int lds = p.shift_out ? std::max(p.lds_bytes, shift_lds_bytes(kCopyUnroll)) : p.lds_bytes;
+    hipLaunchKernelGGL(fn, dim3(p.grid, p.grid_y), dim3(kBlock), lds, stream, a);
     return hipGetLastError();
 }
 

@@ -6,12 +6,15 @@
 namespace rc {
 namespace {
 
-template <bool NT, bool FULL>
+// SHIFT: the whole-tile kernel for launches with outputs off a 64-byte
+// write burst.
+template <bool NT, bool FULL, bool SHIFT = false>
 struct CopyOf {
     template <int NR>
     struct At {
         static FoldFn get() {
-            if constexpr (FULL) return copy_full_kernel<NR, kCopyUnroll, NT>;
+            if constexpr (SHIFT) return copy_full_shift_kernel<NR, kCopyUnroll, NT>;
+            else if constexpr (FULL) return copy_full_kernel<NR, kCopyUnroll, NT>;
             else return copy_kernel<NR, kCopyUnroll, NT>;
         }
     };
@@ -25,12 +28,13 @@ struct CopyBatchOf {
     };
 };
 
-template <bool NT, bool FULL>
+template <bool NT, bool FULL, bool SHIFT = false>
 struct CopyArgsOf {
     template <int NR>
     struct At {
         static CopyArgsFn get() {
-            if constexpr (FULL) return copy_args_full_kernel<NR, kCopyUnroll, NT>;
+            if constexpr (SHIFT) return copy_args_full_shift_kernel<NR, kCopyUnroll, NT>;
+            else if constexpr (FULL) return copy_args_full_kernel<NR, kCopyUnroll, NT>;
             else return copy_args_kernel<NR, kCopyUnroll, NT>;
         }
     };
@@ -43,7 +47,12 @@ __global__ __launch_bounds__(kBlock) void table_write_kernel(TableChunk c) {
 
 }  // namespace
 
-FoldFn copy_fn(bool nt, bool full, int nr) {
+FoldFn copy_fn(bool nt, bool full, bool shift, int nr) {
+    if (shift) {
+        if (!full) return nullptr;
+        return nt ? pick_nin<CopyOf<true, true, true>::template At, FoldFn>(nr)
+                  : pick_nin<CopyOf<false, true, true>::template At, FoldFn>(nr);
+    }
     if (nt) return full ? pick_nin<CopyOf<true, true>::template At, FoldFn>(nr)
                         : pick_nin<CopyOf<true, false>::template At, FoldFn>(nr);
     return full ? pick_nin<CopyOf<false, true>::template At, FoldFn>(nr)
@@ -55,7 +64,12 @@ BatchFn copy_batch_fn(bool nt, int nr) {
               : pick_nin<CopyBatchOf<false>::template At, BatchFn>(nr);
 }
 
-CopyArgsFn copy_args_fn(bool nt, bool full, int nr) {
+CopyArgsFn copy_args_fn(bool nt, bool full, bool shift, int nr) {
+    if (shift) {
+        if (!full) return nullptr;
+        return nt ? pick_nin<CopyArgsOf<true, true, true>::template At, CopyArgsFn>(nr)
+                  : pick_nin<CopyArgsOf<false, true, true>::template At, CopyArgsFn>(nr);
+    }
     if (nt) return full ? pick_nin<CopyArgsOf<true, true>::template At, CopyArgsFn>(nr)
                         : pick_nin<CopyArgsOf<true, false>::template At, CopyArgsFn>(nr);
     return full ? pick_nin<CopyArgsOf<false, true>::template At, CopyArgsFn>(nr)

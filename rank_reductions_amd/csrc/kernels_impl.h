@@ -343,37 +343,27 @@ __global__ __launch_bounds__(kBlock) void fold_table_kernel(FoldTable a) {
     vec_round<NIN, NIN, Op, U, NT, false, true>(in, none, 0, 0, out, a.mask[c], a.mean != 0);
 }
 
-// The whole-tile fold over a FoldTable when some written output starts its
-// job off a 64-byte write burst (tiling.h): outputs on a burst boundary are
-// written from registers as by fold_table_kernel, the others over
-// burst-aligned ranges from the round's values staged in LDS behind the
-// pre_vectors folded ahead of the tile.  Tiles go to the XCDs in groups of
-// consecutive ones (xcd_group_tile).  The stage is the dynamic LDS that
-// caps occupancy, at least shift_lds_bytes(U).  A tile writes up to
-// kBurstElems - 1 elements before its own, which the previous tile reads as
-// inputs if an output aliases an input: the planner never picks this kernel
-// for calls in place.
-template <int NIN, class Op, int U, bool NT>
-__global__ __launch_bounds__(kBlock) void fold_table_shift_kernel(FoldTable a) {
+// One whole-tile round of a launch in which some written output starts its
+// job off a 64-byte write burst (tiling.h): in[k] and out(o) are at the
+// tile's first element.  Outputs on a burst boundary are written from
+// registers as by vec_round; the others over burst-aligned ranges, from the
+// round's values staged in LDS (at least shift_lds_bytes(U): the dynamic
+// allocation that caps occupancy) behind the pre_vectors folded ahead of the
+// tile.  A tile writes up to kBurstElems - 1 elements before its own, which
+// the previous tile reads as inputs if an output aliases an input: the
+// planners never pick this path for calls in place.  NIN = 1 with OpSumI32
+// is a copy.
+template <int NIN, int NR, class Op, int U, bool NT>
+__device__ __forceinline__ void shifted_round(const uint32_t* const (&in)[NIN], const Outs<NR>& out,
+                                              uint32_t mask, bool first, bool last, bool mean) {
     extern __shared__ uint32_t stage[];
     constexpr int T = kBlock * kVec * U;
-    const int c = blockIdx.y;
-    const int64_t xt = xcd_group_tile(blockIdx.x, gridDim.x);
-    const int64_t e0 = xt * T;
-    const bool first = xt == 0;
-    const bool last = xt == (int64_t)gridDim.x - 1;
     const int lane = (int)threadIdx.x;
-    const uint32_t mask = a.mask[c];
-    const bool mean = a.mean != 0;
-    const Outs<NIN> out = outs_of<NIN>(a.out, (int64_t)c * a.out_stride + e0);
     int mmax = 0;
 #pragma unroll
-    for (int o = 0; o < NIN; ++o)
+    for (int o = 0; o < NR; ++o)
         if ((mask >> o) & 1u) mmax = max(mmax, burst_offset(reinterpret_cast<uintptr_t>(out(o))));
     const int npre = pre_vectors(mmax, first);
-    const uint32_t* in[NIN];
-#pragma unroll
-    for (int k = 0; k < NIN; ++k) in[k] = static_cast<const uint32_t*>(a.in[c][k]) + e0;
     u32x4 x[U][NIN];
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -396,7 +386,7 @@ __global__ __launch_bounds__(kBlock) void fold_table_shift_kernel(FoldTable a) {
     }
     uint32_t shifted = 0;
 #pragma unroll
-    for (int o = 0; o < NIN; ++o) {
+    for (int o = 0; o < NR; ++o) {
         if (!((mask >> o) & 1u)) continue;
         uint32_t* p = out(o);
         if (burst_offset(reinterpret_cast<uintptr_t>(p))) {
@@ -407,7 +397,7 @@ __global__ __launch_bounds__(kBlock) void fold_table_shift_kernel(FoldTable a) {
         for (int u = 0; u < U; ++u) st4<NT>(p + (size_t)((u * kBlock + lane) * kVec), acc[u]);
     }
     if (!shifted) return;
-    // stage[j]: the value of element e0 - kBurstElems + j
+    // stage[j]: the value of element e0 - kBurstElems + j (e0: the tile's first)
 #pragma unroll
     for (int u = 0; u < U; ++u)
         *reinterpret_cast<u32x4*>(&stage[kBurstElems + (u * kBlock + lane) * kVec]) = acc[u];
@@ -420,7 +410,7 @@ __global__ __launch_bounds__(kBlock) void fold_table_shift_kernel(FoldTable a) {
     }
     __syncthreads();
 #pragma unroll
-    for (int o = 0; o < NIN; ++o) {
+    for (int o = 0; o < NR; ++o) {
         if (!((shifted >> o) & 1u)) continue;
         uint32_t* p = out(o);
         const int m = burst_offset(reinterpret_cast<uintptr_t>(p));
@@ -441,6 +431,22 @@ __global__ __launch_bounds__(kBlock) void fold_table_shift_kernel(FoldTable a) {
     }
 }
 
+// The whole-tile fold over a FoldTable with outputs shifted onto their
+// 64-byte bursts (shifted_round); tiles go to the XCDs in groups of
+// consecutive ones (xcd_group_tile).
+template <int NIN, class Op, int U, bool NT>
+__global__ __launch_bounds__(kBlock) void fold_table_shift_kernel(FoldTable a) {
+    constexpr int T = kBlock * kVec * U;
+    const int c = blockIdx.y;
+    const int64_t xt = xcd_group_tile(blockIdx.x, gridDim.x);
+    const int64_t e0 = xt * T;
+    const uint32_t* in[NIN];
+#pragma unroll
+    for (int k = 0; k < NIN; ++k) in[k] = static_cast<const uint32_t*>(a.in[c][k]) + e0;
+    const Outs<NIN> out = outs_of<NIN>(a.out, (int64_t)c * a.out_stride + e0);
+    shifted_round<NIN, NIN, Op, U, NT>(in, out, a.mask[c], xt == 0, xt == (int64_t)gridDim.x - 1, a.mean != 0);
+}
+
 template <int NR, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void copy_full_kernel(JobArgs a) {
     const int c = blockIdx.y;
@@ -450,6 +456,20 @@ __global__ __launch_bounds__(kBlock) void copy_full_kernel(JobArgs a) {
     const Outs<NR> out = outs_of<NR>(a.out, (int64_t)c * a.out_stride + e0);
     vec_round<1, NR, OpSumI32, U, NT, false, true>(in, none, 0, 0, out, out_mask_of(a.out_mode, a.out_mask, c),
                                                    false);
+}
+
+// copy_full_kernel with outputs shifted onto their 64-byte bursts
+// (shifted_round, tiles grouped per XCD).
+template <int NR, int U, bool NT>
+__global__ __launch_bounds__(kBlock) void copy_full_shift_kernel(JobArgs a) {
+    constexpr int T = kBlock * kVec * U;
+    const int c = blockIdx.y;
+    const int64_t xt = xcd_group_tile(blockIdx.x, gridDim.x);
+    const int64_t e0 = xt * T;
+    const uint32_t* in[1] = {static_cast<const uint32_t*>(a.in[c]) + (int64_t)c * a.in_stride + e0};
+    const Outs<NR> out = outs_of<NR>(a.out, (int64_t)c * a.out_stride + e0);
+    shifted_round<1, NR, OpSumI32, U, NT>(in, out, out_mask_of(a.out_mode, a.out_mask, c), xt == 0,
+                                          xt == (int64_t)gridDim.x - 1, false);
 }
 
 // Launch shapes: one-shot launches use a 2-D grid, blockIdx.y = job and
@@ -558,6 +578,19 @@ __global__ __launch_bounds__(kBlock) void copy_args_full_kernel(CopyArgs a) {
     const uint32_t* none[1] = {nullptr};
     const Outs<NR> out = outs_of<NR>(const_cast<void* const*>(tp + 1), e0);
     vec_round<1, NR, OpSumI32, U, NT, false, true>(in, none, 0, 0, out, 0xFFFFFFFFu >> (32 - NR), false);
+}
+
+// copy_args_full_kernel with outputs shifted onto their 64-byte bursts.
+template <int NR, int U, bool NT>
+__global__ __launch_bounds__(kBlock) void copy_args_full_shift_kernel(CopyArgs a) {
+    constexpr int T = kBlock * kVec * U;
+    const void* const* tp = a.ptrs + blockIdx.y * (1 + NR);
+    const int64_t xt = xcd_group_tile(blockIdx.x, gridDim.x);
+    const int64_t e0 = xt * T;
+    const uint32_t* in[1] = {static_cast<const uint32_t*>(tp[0]) + e0};
+    const Outs<NR> out = outs_of<NR>(const_cast<void* const*>(tp + 1), e0);
+    shifted_round<1, NR, OpSumI32, U, NT>(in, out, 0xFFFFFFFFu >> (32 - NR), xt == 0,
+                                          xt == (int64_t)gridDim.x - 1, false);
 }
 
 // ---------------------------------------------------------------- dispatch helpers

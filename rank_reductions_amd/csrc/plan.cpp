@@ -183,41 +183,68 @@ void shape_launch(int64_t total_tiles, int nin, int nout, int unroll, const Conf
     *grid = std::max<int64_t>(1, std::min<int64_t>(g, 0x7FFFFFFF));
 }
 
-// Whether a whole-tile fold runs the shifted kernel (tiling.h): some output
-// it writes starts a job off a 64-byte write burst, and no output overlaps
-// an input.  The shifted kernel writes up to kBurstElems - 1 elements ahead
-// of each tile, which the previous tile reads when an output aliases an
-// input (a call in place).
+namespace {
+
+// A byte range [lo, hi).
+struct Span {
+    uintptr_t lo, hi;
+};
+
+// Whether shifting pays and is safe (tiling.h): some destination starts its
+// job off a 64-byte write burst, and no destination overlaps a source.  The
+// shifted kernels write up to kBurstElems - 1 elements ahead of each tile,
+// which the previous tile reads when an output aliases an input (a call in
+// place).
+bool shift_pays(bool off_burst, const std::vector<Span>& srcs, const std::vector<Span>& dsts) {
+    if (!off_burst) return false;
+    for (const Span& d : dsts)
+        for (const Span& r : srcs)
+            if (d.lo < r.hi && r.lo < d.hi) return false;
+    return true;
+}
+
+}  // namespace
+
 bool shifted_outputs_pay(const JobArgs& a, int64_t es) {
     bool off = false;
-    for (int c = 0; c < a.jobs && !off; ++c) {
+    std::vector<Span> srcs, dsts;
+    auto at = [](const void* p, int64_t bytes) { return reinterpret_cast<uintptr_t>(p) + (uintptr_t)bytes; };
+    for (int c = 0; c < a.jobs; ++c) {
+        const int64_t len = job_len(a.n, a.seg, c);
+        if (len == 0) continue;
+        // a fold reads every rank's input at the job's place, a copy its own
+        if (a.in_mode == kInFold) {
+            for (int r = 0; r < a.nranks; ++r)
+                srcs.push_back({at(a.in[r], c * a.in_stride * es), at(a.in[r], (c * a.in_stride + len) * es)});
+        } else {
+            srcs.push_back({at(a.in[c], c * a.in_stride * es), at(a.in[c], (c * a.in_stride + len) * es)});
+        }
         const uint32_t mask = out_mask_of(a.out_mode, a.out_mask, c);
-        for (int o = 0; o < a.nranks; ++o)
-            if (((mask >> o) & 1u) &&
-                burst_offset(reinterpret_cast<uintptr_t>(a.out[o]) + (uintptr_t)((int64_t)c * a.out_stride * es)))
-                off = true;
-    }
-    if (!off) return false;
-    // byte ranges: rank r's input as the jobs read it, output o as they write it
-    int64_t in_end = 0;
-    for (int c = 0; c < a.jobs; ++c)
-        in_end = std::max(in_end, ((int64_t)c * a.in_stride + job_len(a.n, a.seg, c)) * es);
-    for (int o = 0; o < a.nranks; ++o) {
-        int64_t lo = INT64_MAX, hi = INT64_MIN;
-        for (int c = 0; c < a.jobs; ++c) {
-            if (!((out_mask_of(a.out_mode, a.out_mask, c) >> o) & 1u)) continue;
-            lo = std::min(lo, (int64_t)c * a.out_stride * es);
-            hi = std::max(hi, ((int64_t)c * a.out_stride + job_len(a.n, a.seg, c)) * es);
-        }
-        if (lo >= hi) continue;
-        const uintptr_t olo = reinterpret_cast<uintptr_t>(a.out[o]) + (uintptr_t)lo;
-        const uintptr_t ohi = reinterpret_cast<uintptr_t>(a.out[o]) + (uintptr_t)hi;
-        for (int r = 0; r < a.nranks; ++r) {
-            const uintptr_t ilo = reinterpret_cast<uintptr_t>(a.in[r]);
-            if (olo < ilo + (uintptr_t)in_end && ilo < ohi) return false;
+        for (int o = 0; o < a.nranks; ++o) {
+            if (!((mask >> o) & 1u)) continue;
+            const uintptr_t lo = at(a.out[o], c * a.out_stride * es);
+            dsts.push_back({lo, lo + (uintptr_t)(len * es)});
+            if (burst_offset(lo)) off = true;
         }
     }
-    return true;
+    return shift_pays(off, srcs, dsts);
+}
+
+// The same for a copy batch: ptrs[j * (1 + nout)] is job j's source, the
+// next nout its destinations, each at the job's first element.
+bool shifted_copies_pay(const BatchPlan& bp, int64_t es) {
+    bool off = false;
+    std::vector<Span> srcs, dsts;
+    const size_t per = 1 + (size_t)bp.nout;
+    for (size_t j = 0; j < bp.jobs.size(); ++j) {
+        const uintptr_t bytes = (uintptr_t)(bp.jobs[j].len * es);
+        for (size_t i = 0; i < per; ++i) {
+            const uintptr_t lo = reinterpret_cast<uintptr_t>(bp.ptrs[j * per + i]);
+            (i == 0 ? srcs : dsts).push_back({lo, lo + bytes});
+            if (i > 0 && burst_offset(lo)) off = true;
+        }
+    }
+    return shift_pays(off, srcs, dsts);
 }
 
 std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceInfo& dev) {
@@ -452,7 +479,7 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceI
         lp.args.full_tiles = full ? 1 : 0;
         lp.grid = std::max<int64_t>(1, widest);
         lp.grid_y = ja.jobs;
-        if (full && ja.in_mode == kInFold && !lp.acc) lp.shift_out = shifted_outputs_pay(lp.args, es);
+        if (full && !lp.acc) lp.shift_out = shifted_outputs_pay(lp.args, es);
     }
     return out;
 }
@@ -577,6 +604,7 @@ BatchPlan plan_copies(const Checked& ck, const Config& cfg, const DeviceInfo& de
         for (const BatchJob& jb : bp.jobs)
             full = full && jb.phase == 0 && jb.len == bp.grid * (int64_t)bp.tile_elems;
         bp.full_tiles = full;
+        bp.shift_out = full && shifted_copies_pay(bp, es);
     }
     return bp;
 }

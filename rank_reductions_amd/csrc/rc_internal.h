@@ -150,16 +150,17 @@ struct LaunchPlan {
     int grid_y = 1;          // along y: the jobs, for one-shot launches
     int lds_bytes = 0;       // dynamic LDS per workgroup: caps workgroups per CU
     int waves = 0;           // workgroups (waves) per CU that lds_bytes allows; 0: no cap
-    // a whole-tile fold without accumulators some of whose written outputs
-    // start a job off a 64-byte write burst, and no output overlaps an input:
-    // it runs fold_table_shift_kernel (tiling.h)
+    // a whole-tile fold without accumulators, or a whole-tile copy, some of
+    // whose written outputs start a job off a 64-byte write burst, and no
+    // output overlaps an input: it runs fold_table_shift_kernel or
+    // copy_full_shift_kernel (tiling.h)
     bool shift_out = false;
 };
 
 // Builds the launches of one validated call: one for most collectives, two
 // for the ring all-reduce.  Empty when there is nothing to do.
 std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceInfo& dev);
-// Whether a whole-tile fold of these jobs (element size es) runs the
+// Whether a whole-tile fold or copy of these jobs (element size es) runs the
 // shifted kernel (LaunchPlan::shift_out).
 bool shifted_outputs_pay(const JobArgs& a, int64_t es);
 
@@ -192,7 +193,14 @@ struct BatchPlan {
     // by value, and every job whole one-round tiles on a 256-byte boundary
     // (phase 0, len = grid * tile_elems): the whole-tile copy kernel
     bool full_tiles = false;
+    // whole tiles, some destination starts its job off a 64-byte write
+    // burst, and no destination overlaps a source: the shifted copy kernel
+    // (tiling.h)
+    bool shift_out = false;
 };
+// Whether a whole-tile copy batch runs the shifted kernel
+// (BatchPlan::shift_out; element size es).
+bool shifted_copies_pay(const BatchPlan& bp, int64_t es);
 // Capacity of the by-value copy table: all_to_all_single up to 12 ranks
 // (R*R jobs of 2 pointers) and every list-form all_gather (R jobs of 1+R).
 constexpr int kMaxCopyArgJobs = 256;
@@ -349,10 +357,12 @@ FoldTableFn fold_table_fn_i32_cached(int op, bool u1, bool shift, int nin);
 BatchFn batch_fn_nt(int dtype, int op, bool acc, int nin);
 BatchFn batch_fn_cached(int dtype, int op, bool acc, int nin);
 // Copies to nr outputs (kernels_copy.hip): single copies, copy batches over
-// a device table, copy batches by value, and the table writer.
-FoldFn copy_fn(bool nt, bool full, int nr);
+// a device table, copy batches by value, and the table writer; shift (with
+// full only): the whole-tile kernel that writes outputs off a 64-byte burst
+// over burst-aligned ranges.
+FoldFn copy_fn(bool nt, bool full, bool shift, int nr);
 BatchFn copy_batch_fn(bool nt, int nr);
-CopyArgsFn copy_args_fn(bool nt, bool full, int nr);
+CopyArgsFn copy_args_fn(bool nt, bool full, bool shift, int nr);
 TableFn table_write_fn();
 
 // ---------------------------------------------------------------- device.hip

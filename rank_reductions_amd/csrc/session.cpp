@@ -313,7 +313,8 @@ Error launch(const Checked& ck, void* stream, bool timed = true) {
         int64_t elems = 0;  // every job reads len elements and writes them nout times
         for (const BatchJob& jb : bp.jobs) elems += jb.len;
         const int64_t moved = (1 + bp.nout) * elems * es;
-        const TuneKey key{2, bp.full_tiles ? 1 : 0, 1, 0, bp.nout, kCopyUnroll, size_class(moved)};
+        const TuneKey key{2, (bp.full_tiles ? 1 : 0) + (bp.shift_out ? 1 : 0), 1, 0, bp.nout, kCopyUnroll,
+                          size_class(moved)};
         return launch_tuned(key, bp.waves, moved, stream, &capturing, timed, [&](int lds) {
             if (lds >= 0) bp.lds_bytes = lds;
             return device_launch_batch(bp, stream);

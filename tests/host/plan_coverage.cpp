@@ -156,7 +156,7 @@ void check_plan(const LaunchPlan& p, const std::string& name) {
         // the shifted kernel only for whole-tile folds, and never where an
         // output's bytes overlap an input's (its writes ahead of a tile would
         // race the previous tile's reads)
-        if (!a.full_tiles || a.in_mode != kInFold || p.acc) fail(name + ": shifted kernel off a whole-tile fold");
+        if (!a.full_tiles || p.acc) fail(name + ": shifted kernel off a whole-tile launch");
         for (int c = 0; c < a.jobs; ++c) {
             const int64_t len = job_len(a.n, a.seg, c);
             for (int o = 0; o < a.nranks; ++o) {
@@ -164,6 +164,7 @@ void check_plan(const LaunchPlan& p, const std::string& name) {
                 const uintptr_t olo = (uintptr_t)a.out[o] + (uintptr_t)(c * a.out_stride * 4);
                 for (int d = 0; d < a.jobs; ++d)
                     for (int r = 0; r < a.nranks; ++r) {
+                        if (a.in_mode != kInFold && r != d) continue;  // a copy job reads its own source
                         const uintptr_t ilo = (uintptr_t)a.in[r] + (uintptr_t)(d * a.in_stride * 4);
                         if (olo < ilo + (uintptr_t)(job_len(a.n, a.seg, d) * 4) && ilo < olo + (uintptr_t)(len * 4))
                             fail(name + ": shifted kernel with an output over an input");
@@ -261,8 +262,8 @@ void check_plan(const LaunchPlan& p, const std::string& name) {
                 const int64_t e = lt * a.tile_elems - (int64_t)(npre - lane) * kVec;
                 if (e < 0 || e + kVec > len) fail(name + ": read ahead of a tile outside its job");
                 for (int k = 0; k < p.nin; ++k) {
-                    const uintptr_t ad = (uintptr_t)a.in[(c + 1 + k) % p.nin] + (uintptr_t)(c * a.in_stride * 4) +
-                                         (uintptr_t)(e * 4);
+                    const void* src = a.in_mode == kInFold ? a.in[(c + 1 + k) % p.nin] : a.in[c];
+                    const uintptr_t ad = (uintptr_t)src + (uintptr_t)(c * a.in_stride * 4) + (uintptr_t)(e * 4);
                     if (!inside(ad, 16)) fail(name + ": read ahead of a tile outside its buffer");
                 }
             }
@@ -389,7 +390,7 @@ int main(int argc, char** argv) {
         if (coll == 3) n = (n / R) * R;  // reduce_scatter needs R | n
         for (int r = 0; r < R; ++r) {
             const int64_t out_n = coll == 3 ? n / R : (coll == 4 ? n * R : n);
-            void* s = (void*)alloc(std::max<int64_t>(n, 1) * 4, mis(r));
+            void* s = (void*)alloc(std::max<int64_t>(n, 1) * 4, mis_mode == 3 ? 0 : mis(r));
             void* o = (void*)alloc(std::max<int64_t>(out_n, 1) * 4, mis(r + 1));
             bufs[r] = make(s, o, n, RC_SUM, coll == 2 ? -1 : (int)(it % R));
         }
@@ -446,18 +447,22 @@ int main(int argc, char** argv) {
         const int R = 1 + (int)(rng() % 16);
         // up to 128 tiles per job: several whole groups of tiles per XCD and a partial one
         const int64_t n = (int64_t)R * 4096 * (int64_t)(1 + rng() % 8);
-        const int coll = (int)(rng() % 3);  // all_reduce, reduce, reduce_scatter
-        const bool in_place = coll == 0 && rng() % 4 == 0;
-        const int op = rng() % 2 ? RC_SUM : RC_MEAN;
+        // all_reduce, reduce, reduce_scatter, broadcast, all_gather (of shards of n / R)
+        const int coll = (int)(rng() % 5);
+        const bool in_place = (coll == 0 || coll == 3) && rng() % 4 == 0;
+        const int op = coll >= 3 ? RC_SUM : (rng() % 2 ? RC_SUM : RC_MEAN);
+        const int root = (int)(it % R);
+        const int64_t in_n = coll == 4 ? n / R : n;
         std::vector<rc_buf> bufs(R);
         for (int r = 0; r < R; ++r) {
             const int64_t out_n = coll == 2 ? n / R : n;
-            void* sb = (void*)alloc(n * 4, rng() % 2 ? 0 : (int)(rng() % 16));
+            void* sb = (void*)alloc(in_n * 4, rng() % 2 ? 0 : (int)(rng() % 16));
             void* ob = in_place ? sb : (void*)alloc(out_n * 4, (int)(rng() % 16));
-            bufs[r] = make(sb, ob, n, op, coll == 1 ? (int)(it % R) : 0);
+            bufs[r] = make(coll == 3 && r != root ? nullptr : sb, ob, in_n, op, coll == 1 || coll == 3 ? root : 0);
         }
         Checked ck;
-        const Coll kind = coll == 0 ? Coll::AllReduce : (coll == 1 ? Coll::Reduce : Coll::ReduceScatter);
+        const Coll kinds[] = {Coll::AllReduce, Coll::Reduce, Coll::ReduceScatter, Coll::Broadcast, Coll::AllGather};
+        const Coll kind = kinds[coll];
         const Error ve = validate(kind, R, bufs.data(), &ck);
         if (ve.code) {
             fail("whole-tile fold with outputs off a burst rejected: " + ve.msg);
@@ -470,7 +475,12 @@ int main(int argc, char** argv) {
                               (in_place ? " in place" : ""));
             ++plans;
             if (p.shift_out) ++shifted_plans;
-            if (in_place && p.shift_out) fail("shifted kernel chosen for a call in place");
+            // in place an all-reduce's fold writes over its inputs (the ring's
+            // all-gather phase reads only the owner's segment and writes the
+            // other ranks', and a broadcast sender's own buffer is not
+            // written: those may shift)
+            if (in_place && p.args.in_mode == kInFold && p.shift_out)
+                fail("shifted fold chosen for an all-reduce in place");
         }
     }
     // batched plans: job lookup through the group index, and coverage
@@ -567,15 +577,29 @@ int main(int argc, char** argv) {
     // copy batches: all_to_all_single and the list form of all_gather; every
     // destination element written exactly once, every access in bounds
     int copies = 0;
-    int full_copy_batches = 0;  // copy batches on the whole-tile kernel
+    int full_copy_batches = 0;     // copy batches on the whole-tile kernel
+    int shifted_copy_batches = 0;  // and on its shifted form
     for (int it = 0; it < iters / 2; ++it) {
         g_bufs.clear();
         const int R = 1 + (int)(rng() % 16);
-        const bool a2a = rng() % 2;
+        bool a2a = rng() % 2;
         int64_t m = (int64_t)(rng() % 3 == 0 ? rng() % 40000 : rng() % 300);
         if (rng() % 4 == 0) m = 2048 * (1 + (int64_t)(rng() % 3));  // whole tiles for every tile size tried
-        const int mis_mode = (int)(rng() % 3);
+        if (rng() % 4 == 0) m = 512 * (1 + (int64_t)(rng() % 80));  // whole tiles, several groups per XCD
+        // 3: the list all_gather in whole tiles with the destinations of odd
+        // ranks off their 64-byte bursts (the shifted copy kernel; sources and
+        // even ranks' destinations aligned keep the aligned class the heaviest)
+        const int mis_mode = (int)(rng() % 4);
+        if (mis_mode == 3) {
+            m = 512 * (1 + (int64_t)(rng() % 80));
+            a2a = false;
+        }
         auto mis = [&](int r) { return mis_mode == 0 ? 0 : (mis_mode == 1 ? 1 : (r * 3 + it) % 4); };
+        auto dst_mis = [&](int i) {  // destination i = r * R + k of the list
+            if (mis_mode != 3) return mis(i + 2);
+            const int r = i / R;
+            return r % 2 == 0 ? 0 : 1 + (r * 5 + it) % 15;
+        };
         std::vector<rc_buf> bufs(R);
         std::vector<void*> recv_list;
         // destination buffers, with per-element write counts
@@ -587,7 +611,7 @@ int main(int argc, char** argv) {
         std::vector<Dst> dsts;
         const int64_t n = a2a ? m * R : m;
         for (int r = 0; r < R; ++r) {
-            void* s = (void*)alloc(std::max<int64_t>(n, 1) * 4, mis(r));
+            void* s = (void*)alloc(std::max<int64_t>(n, 1) * 4, mis_mode == 3 ? 0 : mis(r));
             void* o = nullptr;
             if (a2a) {
                 o = (void*)alloc(std::max<int64_t>(n, 1) * 4, mis(r + 1));
@@ -597,7 +621,7 @@ int main(int argc, char** argv) {
         }
         if (!a2a)
             for (int i = 0; i < R * R; ++i) {
-                void* o = (void*)alloc(std::max<int64_t>(m, 1) * 4, mis(i + 2));
+                void* o = (void*)alloc(std::max<int64_t>(m, 1) * 4, dst_mis(i));
                 recv_list.push_back(o);
                 dsts.push_back({(uintptr_t)o, m, std::vector<uint8_t>((size_t)m, 0)});
             }
@@ -610,9 +634,9 @@ int main(int argc, char** argv) {
         }
         Config cfg;
         cfg.waves_per_cu = (int)(rng() % 9);
-        cfg.max_workgroups = rng() % 3 == 0 ? (int)(1 + rng() % 50) : 0;
+        cfg.max_workgroups = rng() % 3 == 0 && mis_mode != 3 ? (int)(1 + rng() % 50) : 0;
         const int64_t tes[] = {0, 0, 2048, 8192};
-        cfg.tile_elems = tes[rng() % 4];
+        cfg.tile_elems = mis_mode == 3 ? 0 : tes[rng() % 4];
         const BatchPlan bp = plan_copies(ck, cfg, dev);
         const int per_job = 1 + bp.nout;
         if (ck.count > 0 && (!bp.copy || bp.ptrs.size() != bp.jobs.size() * (size_t)per_job))
@@ -636,10 +660,26 @@ int main(int argc, char** argv) {
                 if (bp.full_tiles && (!bp.by_value || jb.phase != 0 || bp.tile_elems != kBlock * kVec * kCopyUnroll ||
                                       jb.len != bp.grid * (int64_t)bp.tile_elems))
                     fail("whole-tile copy batch on a job that is not whole tiles");
-                for (int64_t lt = 0; lt < bp.grid; ++lt)
+                for (int64_t bx = 0; bx < bp.grid; ++bx) {
+                    const int64_t lt = bp.shift_out ? xcd_group_tile(bx, bp.grid) : bx;
                     if (bp.full_tiles || lt < own) visits.push_back({j, lt});
+                }
             }
             if (bp.full_tiles) ++full_copy_batches;
+            if (bp.shift_out) {
+                ++shifted_copy_batches;
+                if (!bp.full_tiles) fail("shifted copy batch off whole tiles");
+                const size_t per = (size_t)per_job;
+                for (size_t j = 0; j < bp.jobs.size(); ++j)
+                    for (size_t k = 1; k < per; ++k) {
+                        const uintptr_t d = (uintptr_t)bp.ptrs[j * per + k];
+                        for (size_t i = 0; i < bp.jobs.size(); ++i) {
+                            const uintptr_t sp = (uintptr_t)bp.ptrs[i * per];
+                            if (d < sp + (uintptr_t)(bp.jobs[i].len * 4) && sp < d + (uintptr_t)(bp.jobs[j].len * 4))
+                                fail("shifted copy batch with a destination over a source");
+                        }
+                    }
+            }
         } else {
             const int64_t ngroups = (int64_t)bp.group_job.size();
             for (int64_t t = 0; t < bp.total_tiles; ++t) {
@@ -665,6 +705,17 @@ int main(int argc, char** argv) {
                 if (!inside(ad, bytes)) fail("copy read outside its buffer");
                 if (ad % 4) fail("copy read off the element grid");
             });
+            if (bp.shift_out) {  // the source read ahead of the tile
+                int mmax = 0;
+                for (int k = 1; k < per_job; ++k)
+                    mmax = std::max(mmax, burst_offset((uintptr_t)bp.ptrs[(size_t)lo * per_job + k]));
+                const int npre = pre_vectors(mmax, v.second == 0);
+                for (int lane = 0; lane < npre; ++lane) {
+                    const int64_t el = v.second * bp.tile_elems - (int64_t)(npre - lane) * kVec;
+                    const uintptr_t ad = (uintptr_t)bp.ptrs[(size_t)lo * per_job] + (uintptr_t)(el * 4);
+                    if (el < 0 || !inside(ad, 16)) fail("copy read ahead of a tile outside its job or buffer");
+                }
+            }
             for (int k = 1; k < per_job; ++k) {
                 const uintptr_t base = (uintptr_t)bp.ptrs[(size_t)lo * per_job + k];
                 auto write = [&](int64_t el, int bytes) {
@@ -676,7 +727,13 @@ int main(int argc, char** argv) {
                         if (ad >= d.lo && ad < d.lo + (uintptr_t)d.n * 4)
                             for (int i = 0; i < bytes / 4; ++i) d.hits[(ad - d.lo) / 4 + i] += 1;
                 };
-                if (bp.full_tiles) {
+                const int msh = bp.shift_out ? burst_offset(base) : 0;
+                if (msh) {
+                    shifted_tile_writes(v.second, bp.grid, bp.tile_elems, msh, write);
+                    shifted_tile_writes(v.second, bp.grid, bp.tile_elems, msh, [&](int64_t el, int bytes) {
+                        if (bytes == 16 && (base + (uintptr_t)(el * 4)) % 16) fail("shifted copy write off grid");
+                    });
+                } else if (bp.full_tiles) {
                     for (int64_t el = v.second * bp.tile_elems; el < (v.second + 1) * bp.tile_elems; el += kVec)
                         write(el, 16);
                 } else {
@@ -695,6 +752,7 @@ int main(int argc, char** argv) {
     }
     if (iters >= 100 && full_plans == 0) fail("no plan took the whole-tile path");
     if (iters >= 100 && shifted_plans == 0) fail("no plan took the shifted whole-tile kernel");
+    if (iters >= 100 && shifted_copy_batches == 0) fail("no copy batch took the shifted whole-tile kernel");
     if (iters >= 100 && full_copy_batches == 0) fail("no copy batch took the whole-tile path");
     // occupancy tuner: candidates are the rule's W and the two below (never
     // under 2), each timed kTuneSamples times in turn, and the lowest median
@@ -761,8 +819,8 @@ int main(int argc, char** argv) {
         }
         if (t.chosen != 7) fail("tuner left the rule's value on a tie");
     }
-    std::printf("checked %d plans (%d whole-tile, %d shifted), %d batches and %d copy batches (%d whole-tile): "
-                "%d failures\n",
-                plans, full_plans, shifted_plans, batches, copies, full_copy_batches, g_fail);
+    std::printf("checked %d plans (%d whole-tile, %d shifted), %d batches and %d copy batches (%d whole-tile, "
+                "%d shifted): %d failures\n",
+                plans, full_plans, shifted_plans, batches, copies, full_copy_batches, shifted_copy_batches, g_fail);
     return g_fail ? 1 : 0;
 }

@@ -252,3 +252,88 @@ def test_rank_barrier_orders_streams():
     finally:
         for r in range(R):
             rr.rank_finish(r)
+
+
+# ---------------------------------------------------------------- destinations off their bursts
+
+PAD = 32
+
+
+def padded(n, offset, dtype=torch.float32):
+    """(base, view): n elements `offset` into a buffer of sentinels."""
+    from gpu_util import SENTINEL
+    base = torch.full((n + PAD,), SENTINEL, dtype=torch.int32, device=DEV)
+    base = base.view(dtype) if dtype == torch.float32 else base
+    return base, base[offset:offset + n]
+
+
+def pads_intact(base, offset, n, what):
+    from gpu_util import SENTINEL
+    hb = host(base).view(np.uint32)
+    assert np.all(hb[:offset] == SENTINEL) and np.all(hb[offset + n:] == SENTINEL), \
+        f"{what}: written outside its destination (offset {offset})"
+
+
+@pytest.mark.parametrize("R", [2, 3, 4, 8, 16])
+def test_copies_to_destinations_off_bursts(R):
+    """Whole-tile copies whose destinations start 1-15 elements past a 64-byte
+    boundary (sources and rank 0's destination aligned, so the jobs stay whole
+    tiles): the shifted copy kernels write those destinations over
+    burst-aligned ranges.  broadcast (also from a sender whose own buffer is
+    its output), all_gather, the list all_gather (odd ranks' destinations
+    off), and the ring all-reduce's copy phase; sentinels around every
+    destination; bits against the oracle."""
+    M = 8192  # whole tiles of the copy kernels (512 elements), several per job
+    N = R * M
+    offs = [0] + [1 + (5 * r) % 15 for r in range(1, R)]
+    xs = inputs(R, N, torch.float32, 900 + R)
+    hx = [host(x).copy() for x in xs]
+    with session(R):
+        for root in (0, R - 1):
+            bufs = [padded(N, o) for o in offs]
+            sends = [xs[r] if r == root else None for r in range(R)]
+            rr.broadcast(sends, out=[v if r != root else None for r, (_, v) in enumerate(bufs)])
+            torch.cuda.synchronize()
+            for r, (b, v) in enumerate(bufs):
+                if r == root:
+                    continue
+                assert_bits(host(v), hx[root], f"broadcast R={R} from {root} rank {r}")
+                pads_intact(b, offs[r], N, f"broadcast rank {r}")
+        # the sender's own output is its input: only the receivers are written
+        root = R - 1
+        sb, sv = padded(N, 0)
+        sv.copy_(xs[root])
+        bufs = [padded(N, o) for o in offs]
+        outs = [v for _, v in bufs]
+        outs[root] = sv
+        rr.broadcast([sv if r == root else None for r in range(R)], out=outs)
+        torch.cuda.synchronize()
+        for r in range(R):
+            assert_bits(host(outs[r]), hx[root], f"broadcast in place R={R} rank {r}")
+        shards = [x[:M].clone() for x in xs]
+        hs = [host(s) for s in shards]
+        bufs = [padded(N, o) for o in offs]
+        rr.all_gather(shards, out=[v for _, v in bufs])
+        torch.cuda.synchronize()
+        want = oracle.all_gather(hs)
+        for r, (b, v) in enumerate(bufs):
+            assert_bits(host(v), want[r], f"all_gather R={R} rank {r}")
+            pads_intact(b, offs[r], N, f"all_gather rank {r}")
+        lst_bufs = [[padded(M, 0 if r % 2 == 0 else 1 + (3 * r + 7 * k) % 15) for k in range(R)] for r in range(R)]
+        rr.all_gather_list(shards, out=[[v for _, v in row] for row in lst_bufs])
+        torch.cuda.synchronize()
+        for r in range(R):
+            for k in range(R):
+                b, v = lst_bufs[r][k]
+                assert_bits(host(v), hs[k], f"all_gather_list R={R} rank {r} shard {k}")
+                pads_intact(b, 0 if r % 2 == 0 else 1 + (3 * r + 7 * k) % 15, M, f"all_gather_list {r}/{k}")
+    with session(R, algo="ring"):
+        bufs = [padded(N, o) for o in offs]
+        rr.all_reduce(xs, "sum", out=[v for _, v in bufs])
+        torch.cuda.synchronize()
+        want = oracle.all_reduce_closed_form(hx, "sum")
+        for r, (b, v) in enumerate(bufs):
+            assert_bits(host(v), want, f"ring all_reduce R={R} rank {r}")
+            pads_intact(b, offs[r], N, f"ring all_reduce rank {r}")
+    for r in range(R):
+        assert_bits(host(xs[r]), hx[r], f"input of rank {r} changed")
