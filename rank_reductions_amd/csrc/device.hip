@@ -40,10 +40,17 @@ FoldTable fold_table_of(const LaunchPlan& p) {
     const JobArgs& a = p.args;
     FoldTable t{};
     for (int c = 0; c < a.jobs; ++c) {
+        // the interior of a split fold starts job_off[c] elements into the job
+        const int64_t off = (int64_t)c * a.in_stride + p.job_off[c];
         for (int k = 0; k < p.nin; ++k)
-            t.in[c][k] = static_cast<const uint32_t*>(a.in[fold_rank(c, k, p.nin)]) + (int64_t)c * a.in_stride;
+            t.in[c][k] = static_cast<const uint32_t*>(a.in[fold_rank(c, k, p.nin)]) + off;
         t.mask[c] = out_mask_of(a.out_mode, a.out_mask, c);
+        t.out_off[c] = p.job_off[c];
+        t.len[c] = job_len(a.n, a.seg, c);
+        t.phase[c] = a.phase[c];
     }
+    t.edges = p.split ? p.edges : 0;
+    t.interior = (int32_t)(p.split ? p.interior : p.grid);
     for (int r = 0; r < a.nranks; ++r) t.out[r] = a.out[r];
     t.out_stride = a.out_stride;
     t.mean = a.mean;
@@ -53,14 +60,15 @@ FoldTable fold_table_of(const LaunchPlan& p) {
 hipError_t launch_jobs(const LaunchPlan& p, hipStream_t stream) {
     const bool nt = p.args.nontemporal != 0;
     const bool full = p.args.full_tiles != 0;
-    if (full && p.args.in_mode == kInFold && !p.acc) {
+    if ((full || p.split) && p.args.in_mode == kInFold && !p.acc) {
         const bool u1 = p.nin >= 4 && p.nin < 8 && p.unroll == 1;
         const bool sh = p.shift_out;
+        const bool ed = p.split;
         FoldTableFn tf;
         if (p.dtype == RC_F32)
-            tf = nt ? fold_table_fn_f32_nt(p.op, u1, sh, p.nin) : fold_table_fn_f32_cached(p.op, u1, sh, p.nin);
+            tf = nt ? fold_table_fn_f32_nt(p.op, u1, sh, ed, p.nin) : fold_table_fn_f32_cached(p.op, u1, sh, ed, p.nin);
         else
-            tf = nt ? fold_table_fn_i32_nt(p.op, u1, sh, p.nin) : fold_table_fn_i32_cached(p.op, u1, sh, p.nin);
+            tf = nt ? fold_table_fn_i32_nt(p.op, u1, sh, ed, p.nin) : fold_table_fn_i32_cached(p.op, u1, sh, ed, p.nin);
         if (!tf || p.unroll != (u1 ? 1 : unroll_for(p.nin))) return hipErrorInvalidValue;
         // the shifted kernel stages a round in the LDS that caps occupancy
         const int lds = sh ? std::max(p.lds_bytes, shift_lds_bytes(p.unroll)) : p.lds_bytes;

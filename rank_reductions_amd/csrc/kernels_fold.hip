@@ -44,28 +44,31 @@ FoldFn pick(int op, bool acc, int nin) {
 
 // U1: the whole-tile all-reduce of 4-7 ranks with one vector per lane (the
 // planner halves its tiles); every other whole-tile fold uses kUnroll.
-// SHIFT: the kernel for launches with outputs off a 64-byte write burst.
-template <class Op, bool U1, bool SHIFT>
+// SHIFT: the kernel for launches with outputs off a 64-byte write burst;
+// EDGES: the form of split folds (kUnroll only).
+template <class Op, bool U1, bool SHIFT, bool EDGES>
 struct TableOf {
     template <int NIN>
     struct At {
         static constexpr int kU = (U1 && NIN >= 4 && NIN < 8) ? 1 : kUnroll<NIN, false>;
         static FoldTableFn get() {
-            if constexpr (SHIFT) return fold_table_shift_kernel<NIN, Op, kU, kNt>;
-            else return fold_table_kernel<NIN, Op, kU, kNt>;
+            if constexpr (SHIFT) return fold_table_shift_kernel<NIN, Op, kU, kNt, EDGES>;
+            else return fold_table_kernel<NIN, Op, kU, kNt, EDGES>;
         }
     };
 };
 
 template <class Op, bool SHIFT>
-FoldTableFn pick_table_op(bool u1, int nin) {
-    return u1 ? pick_nin<TableOf<Op, true, SHIFT>::template At, FoldTableFn>(nin)
-              : pick_nin<TableOf<Op, false, SHIFT>::template At, FoldTableFn>(nin);
+FoldTableFn pick_table_op(bool u1, bool edges, int nin) {
+    if (edges) return u1 ? nullptr : pick_nin<TableOf<Op, false, SHIFT, true>::template At, FoldTableFn>(nin);
+    return u1 ? pick_nin<TableOf<Op, true, SHIFT, false>::template At, FoldTableFn>(nin)
+              : pick_nin<TableOf<Op, false, SHIFT, false>::template At, FoldTableFn>(nin);
 }
 
-FoldTableFn pick_table(int op, bool u1, bool shift, int nin) {
-    if (op == RC_MAX) return shift ? pick_table_op<MaxOp, true>(u1, nin) : pick_table_op<MaxOp, false>(u1, nin);
-    return shift ? pick_table_op<SumOp, true>(u1, nin) : pick_table_op<SumOp, false>(u1, nin);
+FoldTableFn pick_table(int op, bool u1, bool shift, bool edges, int nin) {
+    if (op == RC_MAX)
+        return shift ? pick_table_op<MaxOp, true>(u1, edges, nin) : pick_table_op<MaxOp, false>(u1, edges, nin);
+    return shift ? pick_table_op<SumOp, true>(u1, edges, nin) : pick_table_op<SumOp, false>(u1, edges, nin);
 }
 
 FoldFn pick_any(int op, bool acc, bool full, bool u1, int nin) {
@@ -77,16 +80,24 @@ FoldFn pick_any(int op, bool acc, bool full, bool u1, int nin) {
 
 #if RC_KDT == RC_F32 && RC_KNT
 FoldFn fold_fn_f32_nt(int op, bool acc, bool full, bool u1, int nin) { return pick_any(op, acc, full, u1, nin); }
-FoldTableFn fold_table_fn_f32_nt(int op, bool u1, bool shift, int nin) { return pick_table(op, u1, shift, nin); }
+FoldTableFn fold_table_fn_f32_nt(int op, bool u1, bool shift, bool edges, int nin) {
+    return pick_table(op, u1, shift, edges, nin);
+}
 #elif RC_KDT == RC_F32
 FoldFn fold_fn_f32_cached(int op, bool acc, bool full, bool u1, int nin) { return pick_any(op, acc, full, u1, nin); }
-FoldTableFn fold_table_fn_f32_cached(int op, bool u1, bool shift, int nin) { return pick_table(op, u1, shift, nin); }
+FoldTableFn fold_table_fn_f32_cached(int op, bool u1, bool shift, bool edges, int nin) {
+    return pick_table(op, u1, shift, edges, nin);
+}
 #elif RC_KNT
 FoldFn fold_fn_i32_nt(int op, bool acc, bool full, bool u1, int nin) { return pick_any(op, acc, full, u1, nin); }
-FoldTableFn fold_table_fn_i32_nt(int op, bool u1, bool shift, int nin) { return pick_table(op, u1, shift, nin); }
+FoldTableFn fold_table_fn_i32_nt(int op, bool u1, bool shift, bool edges, int nin) {
+    return pick_table(op, u1, shift, edges, nin);
+}
 #else
 FoldFn fold_fn_i32_cached(int op, bool acc, bool full, bool u1, int nin) { return pick_any(op, acc, full, u1, nin); }
-FoldTableFn fold_table_fn_i32_cached(int op, bool u1, bool shift, int nin) { return pick_table(op, u1, shift, nin); }
+FoldTableFn fold_table_fn_i32_cached(int op, bool u1, bool shift, bool edges, int nin) {
+    return pick_table(op, u1, shift, edges, nin);
+}
 #endif
 
 }  // namespace rc

@@ -327,11 +327,42 @@ __global__ __launch_bounds__(kBlock) void fold_full_kernel(JobArgs a) {
                                              a.mean != 0);
 }
 
-// The whole-tile fold over a FoldTable: workgroup (x, y) = (tile, job).
+// A split fold's edge tile: workgroup x < a.edges of job c does the job's
+// tile skipped_tile(x, 1, a.interior) (its tile 0, with the scalars, or one
+// past its interior) on the general path, from the job's first element.
 template <int NIN, class Op, int U, bool NT>
+__device__ __forceinline__ void table_edge_tile(const FoldTable& a, int c, int x) {
+    constexpr int T = kBlock * kVec * U;
+    const int64_t lt = skipped_tile(x, 1, a.interior);
+    if (lt >= tiles_of(a.len[c], a.phase[c], T)) return;
+    const uint32_t* in[NIN];
+    const uint32_t* none[NIN];
+#pragma unroll
+    for (int k = 0; k < NIN; ++k) {
+        in[k] = static_cast<const uint32_t*>(a.in[c][k]) - a.out_off[c];
+        none[k] = nullptr;
+    }
+    const Outs<NIN> out = outs_of<NIN>(a.out, (int64_t)c * a.out_stride);
+    job_tile<NIN, NIN, Op, U, NT, false>(in, none, out, a.mask[c], a.len[c], a.phase[c], lt, T, a.mean != 0);
+}
+
+// The whole-tile fold over a FoldTable: workgroup (x, y) = (tile, job); job
+// c's inputs start at in[c][k] and its outputs out_off[c] elements into its
+// place.  EDGES (a split fold): the first a.edges workgroups of each job do
+// its edge tiles (table_edge_tile), dispatched first so that their latency
+// overlaps the interior's, and the rest the interior from out_off[c].
+template <int NIN, class Op, int U, bool NT, bool EDGES = false>
 __global__ __launch_bounds__(kBlock) void fold_table_kernel(FoldTable a) {
     const int c = blockIdx.y;
-    const int64_t e0 = (int64_t)blockIdx.x * (kBlock * kVec * U);
+    int64_t x = blockIdx.x;
+    if constexpr (EDGES) {
+        if (x < a.edges) {
+            table_edge_tile<NIN, Op, U, NT>(a, c, (int)x);
+            return;
+        }
+        x -= a.edges;
+    }
+    const int64_t e0 = x * (kBlock * kVec * U);
     const uint32_t* in[NIN];
     const uint32_t* none[NIN];
 #pragma unroll
@@ -339,7 +370,7 @@ __global__ __launch_bounds__(kBlock) void fold_table_kernel(FoldTable a) {
         in[k] = static_cast<const uint32_t*>(a.in[c][k]) + e0;
         none[k] = nullptr;
     }
-    const Outs<NIN> out = outs_of<NIN>(a.out, (int64_t)c * a.out_stride + e0);
+    const Outs<NIN> out = outs_of<NIN>(a.out, (int64_t)c * a.out_stride + a.out_off[c] + e0);
     vec_round<NIN, NIN, Op, U, NT, false, true>(in, none, 0, 0, out, a.mask[c], a.mean != 0);
 }
 
@@ -434,17 +465,27 @@ __device__ __forceinline__ void shifted_round(const uint32_t* const (&in)[NIN], 
 // The whole-tile fold over a FoldTable with outputs shifted onto their
 // 64-byte bursts (shifted_round); tiles go to the XCDs in groups of
 // consecutive ones (xcd_group_tile).
-template <int NIN, class Op, int U, bool NT>
+template <int NIN, class Op, int U, bool NT, bool EDGES = false>
 __global__ __launch_bounds__(kBlock) void fold_table_shift_kernel(FoldTable a) {
     constexpr int T = kBlock * kVec * U;
     const int c = blockIdx.y;
-    const int64_t xt = xcd_group_tile(blockIdx.x, gridDim.x);
+    int64_t x = blockIdx.x;
+    int64_t nx = gridDim.x;
+    if constexpr (EDGES) {
+        if (x < a.edges) {
+            table_edge_tile<NIN, Op, U, NT>(a, c, (int)x);
+            return;
+        }
+        x -= a.edges;
+        nx = a.interior;
+    }
+    const int64_t xt = xcd_group_tile(x, nx);
     const int64_t e0 = xt * T;
     const uint32_t* in[NIN];
 #pragma unroll
     for (int k = 0; k < NIN; ++k) in[k] = static_cast<const uint32_t*>(a.in[c][k]) + e0;
-    const Outs<NIN> out = outs_of<NIN>(a.out, (int64_t)c * a.out_stride + e0);
-    shifted_round<NIN, NIN, Op, U, NT>(in, out, a.mask[c], xt == 0, xt == (int64_t)gridDim.x - 1, a.mean != 0);
+    const Outs<NIN> out = outs_of<NIN>(a.out, (int64_t)c * a.out_stride + a.out_off[c] + e0);
+    shifted_round<NIN, NIN, Op, U, NT>(in, out, a.mask[c], xt == 0, xt == nx - 1, a.mean != 0);
 }
 
 template <int NR, int U, bool NT>

@@ -205,7 +205,7 @@ bool shift_pays(bool off_burst, const std::vector<Span>& srcs, const std::vector
 
 }  // namespace
 
-bool shifted_outputs_pay(const JobArgs& a, int64_t es) {
+bool shifted_outputs_pay(const JobArgs& a, int64_t es, const int64_t* job_off) {
     bool off = false;
     std::vector<Span> srcs, dsts;
     auto at = [](const void* p, int64_t bytes) { return reinterpret_cast<uintptr_t>(p) + (uintptr_t)bytes; };
@@ -224,7 +224,8 @@ bool shifted_outputs_pay(const JobArgs& a, int64_t es) {
             if (!((mask >> o) & 1u)) continue;
             const uintptr_t lo = at(a.out[o], c * a.out_stride * es);
             dsts.push_back({lo, lo + (uintptr_t)(len * es)});
-            if (burst_offset(lo)) off = true;
+            // where the launch starts writing the job (its interior, if split)
+            if (burst_offset(lo + (uintptr_t)((job_off ? job_off[c] : 0) * es))) off = true;
         }
     }
     return shift_pays(off, srcs, dsts);
@@ -245,6 +246,47 @@ bool shifted_copies_pay(const BatchPlan& bp, int64_t es) {
         }
     }
     return shift_pays(off, srcs, dsts);
+}
+
+// A fold launch whose jobs are not whole tiles (segment lengths or buffers
+// off the 256-byte grid) runs its round inside the general kernel, 2-3%
+// slower than the whole-tile kernels, plus the lead tiles.  When it moves
+// kSplitMinBytes or more and every job has whole tiles after its first, it
+// runs on the edge form of the FoldTable kernels instead (LaunchPlan::split):
+// per job, `edges` workgroups for the tiles outside the interior (tile 0,
+// with the scalars and the lead, and those past the interior) and
+// `interior` workgroups for the first whole tiles after tile 0 (the fewest
+// any job has), from element job_interior_start.  Each element is still
+// folded once, in the same order.
+bool split_fold(LaunchPlan* lp, const Config& cfg, const DeviceInfo& dev, int64_t es) {
+    const JobArgs& a = lp->args;
+    if (!a.grid_2d || a.full_tiles || a.in_mode != kInFold || lp->acc || cfg.max_workgroups > 0 ||
+        a.tile_elems != kBlock * kVec * lp->unroll || lp->unroll != unroll_for(lp->nin) || a.jobs < 1)
+        return false;
+    int64_t elems = 0, interior = INT64_MAX;
+    int64_t widest = 0;
+    int64_t off[kMaxRanks] = {};
+    for (int c = 0; c < a.jobs; ++c) {
+        const int64_t len = job_len(a.n, a.seg, c);
+        const JobSplit s = job_split(len, a.phase[c], a.tile_elems);
+        interior = std::min(interior, job_interior_tiles(s));
+        off[c] = job_interior_start(s);
+        elems += len;
+        widest = std::max<int64_t>(widest, a.tile_prefix[c + 1] - a.tile_prefix[c]);
+    }
+    const int64_t min_bytes = cfg.split_min_bytes >= 0 ? cfg.split_min_bytes : kSplitMinBytes;
+    if (interior < 1 || (int64_t)(lp->nin + lp->nout) * elems * es < min_bytes) return false;
+    lp->split = true;
+    lp->interior = interior;
+    lp->edges = (int)(widest - interior);
+    for (int c = 0; c < a.jobs; ++c) lp->job_off[c] = off[c];
+    // the interior carries the launch: the whole-tile occupancy rule
+    int64_t grid = 0;
+    shape_launch(a.jobs * interior, lp->nin, lp->nout, lp->unroll, cfg, dev, &grid, &lp->lds_bytes, kFullFoldRule);
+    lp->waves = cfg.waves_per_cu > 0 ? cfg.waves_per_cu : auto_waves_per_cu(lp->nin, lp->nout, lp->unroll, kFullFoldRule);
+    lp->grid = lp->edges + interior;
+    lp->shift_out = shifted_outputs_pay(lp->args, es, lp->job_off);
+    return true;
 }
 
 std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceInfo& dev) {
@@ -479,8 +521,11 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceI
         lp.args.full_tiles = full ? 1 : 0;
         lp.grid = std::max<int64_t>(1, widest);
         lp.grid_y = ja.jobs;
-        if (full && !lp.acc) lp.shift_out = shifted_outputs_pay(lp.args, es);
+        if (full && !lp.acc) lp.shift_out = shifted_outputs_pay(lp.args, es, lp.job_off);
     }
+    // folds whose jobs are not whole tiles: their aligned interiors on the
+    // FoldTable kernels, the edges in the same launch
+    for (LaunchPlan& lp : out) split_fold(&lp, cfg, dev, es);
     return out;
 }
 

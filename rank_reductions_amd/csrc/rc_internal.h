@@ -74,6 +74,10 @@ struct Config {
     int max_workgroups = 0;
     int cache_hint = RC_CACHE_AUTO;
     int waves_per_cu = 0;
+    // folds moving this many bytes or more split off their aligned interior
+    // (split_fold); not in rc_config: kSplitMinBytes, lowered by the CPU
+    // replay of the planner to reach the split at small sizes
+    int64_t split_min_bytes = -1;
 };
 
 // Result of validating one collective call.
@@ -155,14 +159,27 @@ struct LaunchPlan {
     // output overlaps an input: it runs fold_table_shift_kernel or
     // copy_full_shift_kernel (tiling.h)
     bool shift_out = false;
+    // A fold whose jobs are not whole tiles, split (split_fold): the FoldTable
+    // kernels' edge form, whose first `edges` workgroups of each job do the
+    // job's head, lead and what follows its interior on the general path,
+    // and the next `interior` the whole tiles of its aligned interior, job c's
+    // starting job_off[c] elements in.  grid = edges + interior.
+    bool split = false;
+    int edges = 0;
+    int64_t interior = 0;
+    int64_t job_off[kMaxRanks] = {};
 };
 
 // Builds the launches of one validated call: one for most collectives, two
 // for the ring all-reduce.  Empty when there is nothing to do.
 std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceInfo& dev);
 // Whether a whole-tile fold or copy of these jobs (element size es) runs the
-// shifted kernel (LaunchPlan::shift_out).
-bool shifted_outputs_pay(const JobArgs& a, int64_t es);
+// shifted kernel (LaunchPlan::shift_out); job_off: where the launch starts
+// in each job (LaunchPlan::job_off).
+bool shifted_outputs_pay(const JobArgs& a, int64_t es, const int64_t* job_off);
+// Turns a fold launch whose jobs are not whole tiles into a split one
+// (LaunchPlan::split); false: it stays on the general kernel.
+bool split_fold(LaunchPlan* lp, const Config& cfg, const DeviceInfo& dev, int64_t es);
 
 // Batched all-reduce: job and pointer tables for tensors [t0, t1).
 struct BatchPlan {
@@ -257,6 +274,10 @@ constexpr int kTuneCands = 3;
 constexpr int kTuneSamples = 5;
 constexpr double kTuneMargin = 0.03;
 constexpr int64_t kTuneMinBytes = int64_t(256) << 20;
+// Fold launches that move this much or more split off their aligned
+// interior onto the whole-tile kernels (split_fold): the second launch costs
+// a few microseconds, a few percent of a launch this size.
+constexpr int64_t kSplitMinBytes = int64_t(256) << 20;
 struct TunePending {
     int ticket;     // device timer
     int cand;       // candidate index
@@ -313,12 +334,21 @@ struct CopyArgs {
 // with no index or stride arithmetic before its HBM loads; the JobArgs form
 // measured 3% slower on the 8-rank all-reduce.
 struct FoldTable {
-    const void* in[kMaxRanks][kMaxRanks];  // [job][k]: operand k at the job's first element
+    const void* in[kMaxRanks][kMaxRanks];  // [job][k]: operand k at the first element the launch folds
     void* out[kMaxRanks];                  // output bases; job c's outputs start c*out_stride elements in
+    int64_t out_off[kMaxRanks];            // ... and the launch writes from out_off[c] elements further
     int64_t out_stride;
     uint32_t mask[kMaxRanks];              // outputs job c writes
     int32_t mean;                          // divide the finished fold by the rank count
     int32_t pad;
+    // A split fold (LaunchPlan::split): workgroups x < edges of job c do the
+    // job's tiles outside its interior on the general path (job c has len[c]
+    // elements and phase[c]; its tile skipped_tile(x, 1, interior)); the next
+    // `interior` do the whole tiles of its interior.  Unused otherwise.
+    int64_t len[kMaxRanks];
+    uint8_t phase[kMaxRanks];
+    int32_t edges;
+    int32_t interior;
 };
 
 // A piece of a descriptor table written into device memory by a kernel (the
@@ -348,11 +378,12 @@ FoldFn fold_fn_i32_nt(int op, bool acc, bool full, bool u1, int nin);
 FoldFn fold_fn_i32_cached(int op, bool acc, bool full, bool u1, int nin);
 // Whole-tile folds without accumulators, over a FoldTable (same files);
 // shift: the kernel for launches with outputs off a 64-byte write burst
-// (LaunchPlan::shift_out).
-FoldTableFn fold_table_fn_f32_nt(int op, bool u1, bool shift, int nin);
-FoldTableFn fold_table_fn_f32_cached(int op, bool u1, bool shift, int nin);
-FoldTableFn fold_table_fn_i32_nt(int op, bool u1, bool shift, int nin);
-FoldTableFn fold_table_fn_i32_cached(int op, bool u1, bool shift, int nin);
+// (LaunchPlan::shift_out); edges: the form of split folds (LaunchPlan::split,
+// unroll kUnroll only).
+FoldTableFn fold_table_fn_f32_nt(int op, bool u1, bool shift, bool edges, int nin);
+FoldTableFn fold_table_fn_f32_cached(int op, bool u1, bool shift, bool edges, int nin);
+FoldTableFn fold_table_fn_i32_nt(int op, bool u1, bool shift, bool edges, int nin);
+FoldTableFn fold_table_fn_i32_cached(int op, bool u1, bool shift, bool edges, int nin);
 // Batched folds (kernels_batch.hip, once per cache hint).
 BatchFn batch_fn_nt(int dtype, int op, bool acc, int nin);
 BatchFn batch_fn_cached(int dtype, int op, bool acc, int nin);

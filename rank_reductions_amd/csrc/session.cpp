@@ -330,7 +330,8 @@ Error launch(const Checked& ck, void* stream, bool timed = true) {
             if (e.code) return e;
             continue;
         }
-        const TuneKey key{(int)p.args.in_mode, (int)p.args.full_tiles + (p.shift_out ? 1 : 0), p.nin,
+        // a split fold runs the whole-tile kernels: tuned with them
+        const TuneKey key{(int)p.args.in_mode, (p.args.full_tiles || p.split ? 1 : 0) + (p.shift_out ? 1 : 0), p.nin,
                           p.acc ? 1 : 0, p.nout, p.unroll, size_class(moved)};
         Error e = launch_tuned(key, p.waves, moved, stream, &capturing, timed, [&](int lds) {
             if (lds >= 0) p.lds_bytes = lds;

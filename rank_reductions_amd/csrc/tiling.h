@@ -103,6 +103,23 @@ RC_HD int job_of(const int32_t* prefix, int t) {
     return c;
 }
 
+// The job's tile that workgroup x of a 2-D grid takes when the job's tiles
+// [from, from + count) belong to another launch (the interior of a split
+// fold, done on the whole-tile kernels).
+RC_HD int skipped_tile(int x, int from, int count) { return x < from ? x : x + count; }
+
+// A fold job's aligned interior, for a split launch: the job's tiles from 1
+// on that are whole (tile 0, which also does the job's scalars, stays with
+// the general kernel).  Tile t >= 1 starts at vector job_interior_vec +
+// (t - 1) * tv, on a kTileAlignBytes boundary of the reference stream;
+// job_interior_tiles of them are whole, from element job_interior_start.
+RC_HD int64_t job_interior_vec(const JobSplit& s) { return s.lead > 0 ? s.lead : s.tv; }
+RC_HD int64_t job_interior_start(const JobSplit& s) { return s.head + job_interior_vec(s) * kVec; }
+RC_HD int64_t job_interior_tiles(const JobSplit& s) {
+    const int64_t v = job_interior_vec(s);
+    return s.tv > 0 && s.nvec > v ? (s.nvec - v) / s.tv : 0;
+}
+
 // Which ranks' outputs a job writes (each at out[r] + c*out_stride).
 enum OutMode : int32_t {
     kOutMask = 0,          // the ranks in out_mask

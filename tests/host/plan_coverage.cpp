@@ -150,13 +150,42 @@ void check_plan(const LaunchPlan& p, const std::string& name) {
         seen[c].assign((size_t)job_len(a.n, a.seg, c), 0);
         for (auto& wc : writes[c]) wc.hits.assign((size_t)job_len(a.n, a.seg, c), 0);
     }
+    if (p.split) {
+        // the interior: whole tiles from job_off[c], inside the job, starting on
+        // a 256-byte boundary of a stream of the job's heaviest class, after
+        // the general kernel's tile 0; edges: the job's other general tiles
+        if (a.full_tiles || a.in_mode != kInFold || p.acc || !a.grid_2d) fail(name + ": split off a plain fold");
+        if (p.grid != p.edges + p.interior || p.interior < 1) fail(name + ": split grid is not edges + interior");
+        int64_t widest = 0;
+        for (int c = 0; c < a.jobs; ++c) widest = std::max<int64_t>(widest, a.tile_prefix[c + 1] - a.tile_prefix[c]);
+        if (p.edges != widest - p.interior) fail(name + ": split edges do not reach the widest job");
+        for (int c = 0; c < a.jobs; ++c) {
+            const int64_t len = job_len(a.n, a.seg, c);
+            const JobSplit sp = job_split(len, a.phase[c], a.tile_elems);
+            if (p.job_off[c] != job_interior_start(sp) || p.job_off[c] + p.interior * a.tile_elems > len ||
+                p.interior > job_interior_tiles(sp))
+                fail(name + ": split interior past its job");
+            std::vector<uintptr_t> ins, outs;
+            for (int k = 0; k < p.nin; ++k)
+                ins.push_back((uintptr_t)a.in[(c + 1 + k) % p.nin] + (uintptr_t)(c * a.in_stride * 4));
+            for (int o = 0; o < a.nranks; ++o)
+                if ((out_mask_of(a.out_mode, a.out_mask, c) >> o) & 1u)
+                    outs.push_back((uintptr_t)a.out[o] + (uintptr_t)(c * a.out_stride * 4));
+            // the phase that makes the interior start element a 256-byte
+            // boundary of the heaviest class: (job_off * 4) mod 256 = 0 there
+            bool aligned = false;
+            for (uintptr_t x : ins) aligned |= (x + (uintptr_t)(p.job_off[c] * 4)) % kTileAlignBytes == 0;
+            for (uintptr_t x : outs) aligned |= (x + (uintptr_t)(p.job_off[c] * 4)) % kTileAlignBytes == 0;
+            if (!aligned) fail(name + ": split interior of job " + std::to_string(c) + " on no stream's boundary");
+        }
+    }
     const int64_t total = a.total_tiles;
     if (total != a.tile_prefix[a.jobs] || total != p.total_tiles) fail(name + ": tile totals disagree");
     if (p.shift_out) {
         // the shifted kernel only for whole-tile folds, and never where an
         // output's bytes overlap an input's (its writes ahead of a tile would
         // race the previous tile's reads)
-        if (!a.full_tiles || p.acc) fail(name + ": shifted kernel off a whole-tile launch");
+        if (!(a.full_tiles || p.split) || p.acc) fail(name + ": shifted kernel off a whole-tile launch");
         for (int c = 0; c < a.jobs; ++c) {
             const int64_t len = job_len(a.n, a.seg, c);
             for (int o = 0; o < a.nranks; ++o) {
@@ -174,16 +203,34 @@ void check_plan(const LaunchPlan& p, const std::string& name) {
     }
     for (int c = a.jobs; c <= kMaxRanks; ++c)
         if (a.tile_prefix[c] != total) fail(name + ": prefix past the last job is not the total");
-    // the (job, tile) pairs the launch visits
-    std::vector<std::pair<int, int64_t>> visits;
+    // the tiles the launch visits: (job, tile, whole) with whole tiles from
+    // job_off[c] (the whole-tile kernels, a split fold's interior) or the
+    // general kernel's tile of the job
+    struct Visit {
+        int c;
+        int64_t lt;
+        bool whole;
+    };
+    std::vector<Visit> visits;
+    const int64_t nwhole = p.split ? p.interior : p.grid;  // whole tiles per job
     if (a.grid_2d) {
         if (p.grid_y != a.jobs) fail(name + ": 2-D grid height is not the job count");
         for (int c = 0; c < p.grid_y; ++c)
             for (int64_t bx = 0; bx < p.grid; ++bx) {
-                // the shifted kernel's workgroup bx takes tile xcd_group_tile(bx)
-                const int64_t lt = p.shift_out ? xcd_group_tile(bx, p.grid) : bx;
-                if (lt < 0 || lt >= p.grid) fail(name + ": grouped tile out of range");
-                if (a.full_tiles || lt < a.tile_prefix[c + 1] - a.tile_prefix[c]) visits.push_back({c, lt});
+                if (p.split && bx < p.edges) {  // an edge tile, on the general path
+                    const int64_t lt = skipped_tile((int)bx, 1, (int)p.interior);
+                    if (lt < a.tile_prefix[c + 1] - a.tile_prefix[c]) visits.push_back({c, lt, false});
+                    continue;
+                }
+                if (!a.full_tiles && !p.split) {
+                    if (bx < a.tile_prefix[c + 1] - a.tile_prefix[c]) visits.push_back({c, bx, false});
+                    continue;
+                }
+                // a whole tile; the shifted kernel's workgroup takes tile xcd_group_tile
+                const int64_t x = p.split ? bx - p.edges : bx;
+                const int64_t lt = p.shift_out ? xcd_group_tile(x, nwhole) : x;
+                if (lt < 0 || lt >= nwhole) fail(name + ": grouped tile out of range");
+                visits.push_back({c, lt, true});
             }
         if (a.full_tiles) {
             // the kernels then take every tile as whole: check that it is
@@ -205,20 +252,21 @@ void check_plan(const LaunchPlan& p, const std::string& name) {
                     fail(name + ": job index past the last job");
                     return;
                 }
-                visits.push_back({c, t - a.tile_prefix[c]});
+                visits.push_back({c, t - a.tile_prefix[c], false});
             }
     }
-    for (const auto& visit : visits) {
-        const int c = visit.first;
-        const int64_t lt = visit.second;
+    for (const Visit& vis : visits) {
+        const int c = vis.c;
+        const int64_t lt = vis.lt;
         const int64_t start = (int64_t)c * a.seg;
         const int64_t len = std::min(a.seg, a.n - start);
         const uint32_t mask = out_mask_of(a.out_mode, a.out_mask, c);
+        const int64_t joff = p.job_off[c];  // where a split interior starts in the job
         auto visit_tile = [&](auto&& visit) {
-            if (a.full_tiles) {
-                // fold_full_kernel / copy_full_kernel: one round of whole 16-byte vectors
-                // from lt*tile_elems
-                for (int64_t e = lt * a.tile_elems; e < (lt + 1) * a.tile_elems; e += kVec) visit(e, 16);
+            if (vis.whole) {
+                // the whole-tile kernels: one round of whole 16-byte vectors
+                // from joff + lt*tile_elems
+                for (int64_t e = joff + lt * a.tile_elems; e < joff + (lt + 1) * a.tile_elems; e += kVec) visit(e, 16);
             } else {
                 tile_elements(len, a.phase[c], lt, a.tile_elems, p.unroll, visit);
             }
@@ -252,14 +300,14 @@ void check_plan(const LaunchPlan& p, const std::string& name) {
         });
         // the shifted kernel's reads ahead of the tile: pre_vectors vectors
         // of every operand, inside the job and the operand's buffer
-        if (p.shift_out) {
+        if (p.shift_out && vis.whole) {
             int mmax = 0;
             for (int o = 0; o < a.nranks; ++o)
                 if ((mask >> o) & 1u)
-                    mmax = std::max(mmax, burst_offset((uintptr_t)a.out[o] + (uintptr_t)(c * a.out_stride * 4)));
+                    mmax = std::max(mmax, burst_offset((uintptr_t)a.out[o] + (uintptr_t)((c * a.out_stride + joff) * 4)));
             const int npre = pre_vectors(mmax, lt == 0);
             for (int lane = 0; lane < npre; ++lane) {
-                const int64_t e = lt * a.tile_elems - (int64_t)(npre - lane) * kVec;
+                const int64_t e = joff + lt * a.tile_elems - (int64_t)(npre - lane) * kVec;
                 if (e < 0 || e + kVec > len) fail(name + ": read ahead of a tile outside its job");
                 for (int k = 0; k < p.nin; ++k) {
                     const void* src = a.in_mode == kInFold ? a.in[(c + 1 + k) % p.nin] : a.in[c];
@@ -273,13 +321,15 @@ void check_plan(const LaunchPlan& p, const std::string& name) {
             if (!((mask >> o) & 1u)) continue;
             const uintptr_t base = (uintptr_t)a.out[o] + (uintptr_t)(c * a.out_stride * 4);
             WriteCount& wc = writes[c][o];
-            const int m = p.shift_out ? burst_offset(base) : 0;
+            const int m = p.shift_out && vis.whole ? burst_offset(base + (uintptr_t)(joff * 4)) : 0;
             if (m) {
-                shifted_tile_writes(lt, p.grid, a.tile_elems, m,
-                                    [&](int64_t e, int bytes) { count_write(wc, base, e, bytes, len, name); });
+                shifted_tile_writes(lt, nwhole, a.tile_elems, m, [&](int64_t e, int bytes) {
+                    count_write(wc, base, joff + e, bytes, len, name);
+                });
                 // burst-aligned: every 16-byte write starts on a 16-byte boundary
-                shifted_tile_writes(lt, p.grid, a.tile_elems, m, [&](int64_t e, int bytes) {
-                    if (bytes == 16 && (base + (uintptr_t)(e * 4)) % 16) fail(name + ": shifted vector write off grid");
+                shifted_tile_writes(lt, nwhole, a.tile_elems, m, [&](int64_t e, int bytes) {
+                    if (bytes == 16 && (base + (uintptr_t)((joff + e) * 4)) % 16)
+                        fail(name + ": shifted vector write off grid");
                 });
             } else {
                 visit_tile([&](int64_t e, int bytes) { count_write(wc, base, e, bytes, len, name); });
@@ -353,6 +403,7 @@ int main(int argc, char** argv) {
     dev.max_lds_per_block = 64 * 1024;
     int plans = 0;
     int full_plans = 0;  // plans whose kernels take the whole-tile path
+    int split_plans = 0;  // folds split into a whole-tile interior and edges
     // job_phase: the head reaches a 16-byte boundary and the lead a 256-byte
     // one of a stream of the heaviest alignment class
     for (int i = 0; i < 20000; ++i) {
@@ -383,6 +434,7 @@ int main(int argc, char** argv) {
         cfg.tile_elems = tiles[rng() % 5];
         cfg.max_workgroups = rng() % 3 == 0 ? (int)(1 + rng() % 50) : 0;
         cfg.waves_per_cu = (int)(rng() % 9);
+        if (rng() % 2) cfg.split_min_bytes = 0;  // split folds whatever their size
         const int mis_mode = (int)(rng() % 3);  // 0 aligned, 1 common offset, 2 mixed offsets
         auto mis = [&](int r) { return mis_mode == 0 ? 0 : (mis_mode == 1 ? 1 + (int)(it % 3) : (r * 3 + it) % 4); };
         const int coll = (int)(rng() % 5);
@@ -418,6 +470,7 @@ int main(int argc, char** argv) {
                               " mis=" + std::to_string(mis_mode) + (ck.has_acc ? " acc" : ""));
             ++plans;
             if (p.args.full_tiles) ++full_plans;
+            if (p.split) ++split_plans;
         }
     }
     {
@@ -445,8 +498,10 @@ int main(int argc, char** argv) {
     for (int it = 0; it < iters; ++it) {
         g_bufs.clear();
         const int R = 1 + (int)(rng() % 16);
-        // up to 128 tiles per job: several whole groups of tiles per XCD and a partial one
-        const int64_t n = (int64_t)R * 4096 * (int64_t)(1 + rng() % 8);
+        // up to 128 tiles per job: several whole groups of tiles per XCD and a
+        // partial one; sometimes a ragged length (split: the interior shifted)
+        int64_t n = (int64_t)R * 4096 * (int64_t)(1 + rng() % 8);
+        if (rng() % 3 == 0) n += (int64_t)R * (1 + (int64_t)(rng() % 40));
         // all_reduce, reduce, reduce_scatter, broadcast, all_gather (of shards of n / R)
         const int coll = (int)(rng() % 5);
         const bool in_place = (coll == 0 || coll == 3) && rng() % 4 == 0;
@@ -470,7 +525,9 @@ int main(int argc, char** argv) {
         }
         Config cfg;
         cfg.algo = rng() % 4 == 0 ? RC_ALGO_RING : RC_ALGO_DIRECT;
+        cfg.split_min_bytes = 0;
         for (const LaunchPlan& p : plan(ck, cfg, dev)) {
+            if (p.split) ++split_plans;
             check_plan(p, "outputs off a burst: coll " + std::to_string(coll) + " R=" + std::to_string(R) +
                               (in_place ? " in place" : ""));
             ++plans;
@@ -752,6 +809,7 @@ int main(int argc, char** argv) {
     }
     if (iters >= 100 && full_plans == 0) fail("no plan took the whole-tile path");
     if (iters >= 100 && shifted_plans == 0) fail("no plan took the shifted whole-tile kernel");
+    if (iters >= 100 && split_plans == 0) fail("no fold was split");
     if (iters >= 100 && shifted_copy_batches == 0) fail("no copy batch took the shifted whole-tile kernel");
     if (iters >= 100 && full_copy_batches == 0) fail("no copy batch took the whole-tile path");
     // occupancy tuner: candidates are the rule's W and the two below (never
@@ -819,8 +877,9 @@ int main(int argc, char** argv) {
         }
         if (t.chosen != 7) fail("tuner left the rule's value on a tie");
     }
-    std::printf("checked %d plans (%d whole-tile, %d shifted), %d batches and %d copy batches (%d whole-tile, "
-                "%d shifted): %d failures\n",
-                plans, full_plans, shifted_plans, batches, copies, full_copy_batches, shifted_copy_batches, g_fail);
+    std::printf("checked %d plans (%d whole-tile, %d shifted, %d split), %d batches and %d copy batches "
+                "(%d whole-tile, %d shifted): %d failures\n",
+                plans, full_plans, shifted_plans, split_plans, batches, copies, full_copy_batches,
+                shifted_copy_batches, g_fail);
     return g_fail ? 1 : 0;
 }

@@ -616,3 +616,70 @@ def test_shapes_are_flattened(shape):
         want_rs = oracle.reduce_scatter([h.reshape(-1) for h in hx], "max")
         for r in range(R):
             assert_bits(host(rs[r]), want_rs[r], f"{shape} reduce_scatter rank {r}")
+
+
+# ---------------------------------------------------------------- split folds
+
+@pytest.mark.parametrize("case", ["r8_f32_plus8", "r4_i32_plus12", "reduce_r4_plus20", "rs_r8_shards_plus3",
+                                  "r8_in_place", "r8_outputs_off_bursts", "r8_ring"])
+def test_split_folds(case):
+    """Folds of 256 MiB and more whose jobs are not whole tiles (segment
+    lengths off the 256-byte grid, so each job has its own head and lead)
+    run as two launches: the whole tiles of each job's aligned interior on
+    the table kernels (shifted when outputs are off their bursts), then the
+    head, lead and tail on the general kernel.  Bits against the oracle at
+    those sizes, in place too, and through the ring's first phase."""
+    algo = "ring" if case == "r8_ring" else "direct"
+    if case.startswith("r4_i32"):
+        R, N, dtype, ops = 4, 2**24 + 12, "i32", ("sum", "max")
+    elif case.startswith("reduce"):
+        R, N, dtype, ops = 4, 2**24 + 20, "f32", ("sum",)
+    elif case.startswith("rs_"):
+        R, N, dtype, ops = 8, 8 * (2**21 + 3), "f32", ("sum", "mean")
+    else:
+        R, N, dtype, ops = 8, 2**24 + 8, "f32", ("sum", "mean")
+    dist = "int" if dtype == "i32" else "normal"
+    xs = gen(R, N, dtype, dist, seed=6000 + len(case))
+    hx = [host(x).copy() for x in xs]
+    with session(R, algo=algo):
+        for op in ops:
+            want = oracle.all_reduce_closed_form(hx, op)
+            if case.startswith("reduce"):
+                outs = [sentinel_like(torch, x) for x in xs]
+                rr.reduce(xs, 2, op, out=[o if r == 2 else None for r, o in enumerate(outs)])
+                sync()
+                assert_bits(host(outs[2]), want, f"{case} {op} root")
+                for r in (0, 1, 3):
+                    assert np.all(host(outs[r]).view(np.uint32) == SENTINEL), f"{case}: non-root {r} written"
+            elif case.startswith("rs_"):
+                M = N // R
+                shards = rr.reduce_scatter(xs, op)
+                sync()
+                for r in range(R):
+                    assert_bits(host(shards[r]), want[r * M:(r + 1) * M], f"{case} {op} shard {r}")
+            elif case == "r8_in_place":
+                ys = [x.clone() for x in xs]
+                rr.all_reduce(ys, op, out=ys)
+                sync()
+                for r in (0, 3, R - 1):
+                    assert_bits(host(ys[r]), want, f"{case} {op} rank {r}")
+                del ys
+            elif case == "r8_outputs_off_bursts":
+                offs = [(5 * r) % 16 for r in range(R)]
+                bases = [sentinel_like(torch, torch.empty(N + 32, device=DEV)) for _ in range(R)]
+                outs = [b[o:o + N] for b, o in zip(bases, offs)]
+                rr.all_reduce(xs, op, out=outs)
+                sync()
+                for r, (b, o) in enumerate(zip(bases, offs)):
+                    hb = host(b)
+                    assert_bits(hb[o:o + N], want, f"{case} {op} rank {r}")
+                    assert np.all(hb.view(np.uint32)[:o] == SENTINEL) and \
+                        np.all(hb.view(np.uint32)[o + N:] == SENTINEL), f"{case}: rank {r} written outside"
+                del bases, outs
+            else:
+                outs = rr.all_reduce(xs, op)
+                sync()
+                for r in range(R):
+                    assert_bits(host(outs[r]), want, f"{case} {op} rank {r}")
+                del outs
+    check_unchanged(xs, hx, case)
