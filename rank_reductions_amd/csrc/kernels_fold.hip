@@ -52,8 +52,10 @@ struct TableOf {
     struct At {
         static constexpr int kU = (U1 && NIN >= 4 && NIN < 8) ? 1 : kUnroll<NIN, false>;
         static FoldTableFn get() {
-            if constexpr (SHIFT) return fold_table_shift_kernel<NIN, Op, kU, kNt, EDGES>;
-            else return fold_table_kernel<NIN, Op, kU, kNt, EDGES>;
+            if constexpr (SHIFT && EDGES) return fold_table_shift_edges_kernel<NIN, Op, kU, kNt>;
+            else if constexpr (SHIFT) return fold_table_shift_kernel<NIN, Op, kU, kNt>;
+            else if constexpr (EDGES) return fold_table_edges_kernel<NIN, Op, kU, kNt>;
+            else return fold_table_kernel<NIN, Op, kU, kNt>;
         }
     };
 };

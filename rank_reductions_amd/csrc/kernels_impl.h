@@ -347,12 +347,13 @@ __device__ __forceinline__ void table_edge_tile(const FoldTable& a, int c, int x
 }
 
 // The whole-tile fold over a FoldTable: workgroup (x, y) = (tile, job); job
-// c's inputs start at in[c][k] and its outputs out_off[c] elements into its
-// place.  EDGES (a split fold): the first a.edges workgroups of each job do
-// its edge tiles (table_edge_tile), dispatched first so that their latency
-// overlaps the interior's, and the rest the interior from out_off[c].
-template <int NIN, class Op, int U, bool NT, bool EDGES = false>
-__global__ __launch_bounds__(kBlock) void fold_table_kernel(FoldTable a) {
+// c's inputs start at in[c][k] and its outputs at its place.  EDGES (a split
+// fold): the first a.edges workgroups of each job do its edge tiles
+// (table_edge_tile), dispatched first so that their latency overlaps the
+// interior's, and the rest the interior, whose outputs start out_off[c]
+// elements into the job.
+template <int NIN, class Op, int U, bool NT, bool EDGES>
+__device__ __forceinline__ void table_round(const FoldTable& a) {
     const int c = blockIdx.y;
     int64_t x = blockIdx.x;
     if constexpr (EDGES) {
@@ -370,8 +371,22 @@ __global__ __launch_bounds__(kBlock) void fold_table_kernel(FoldTable a) {
         in[k] = static_cast<const uint32_t*>(a.in[c][k]) + e0;
         none[k] = nullptr;
     }
-    const Outs<NIN> out = outs_of<NIN>(a.out, (int64_t)c * a.out_stride + a.out_off[c] + e0);
+    // only a split fold's interior starts off the job's first element
+    const int64_t ooff = EDGES ? a.out_off[c] : 0;
+    const Outs<NIN> out = outs_of<NIN>(a.out, (int64_t)c * a.out_stride + ooff + e0);
     vec_round<NIN, NIN, Op, U, NT, false, true>(in, none, 0, 0, out, a.mask[c], a.mean != 0);
+}
+
+template <int NIN, class Op, int U, bool NT>
+__global__ __launch_bounds__(kBlock) void fold_table_kernel(FoldTable a) {
+    table_round<NIN, Op, U, NT, false>(a);
+}
+
+// The edge form: a split fold (the first a.edges workgroups of each job do
+// its edge tiles).
+template <int NIN, class Op, int U, bool NT>
+__global__ __launch_bounds__(kBlock) void fold_table_edges_kernel(FoldTable a) {
+    table_round<NIN, Op, U, NT, true>(a);
 }
 
 // One whole-tile round of a launch in which some written output starts its
@@ -465,8 +480,8 @@ __device__ __forceinline__ void shifted_round(const uint32_t* const (&in)[NIN], 
 // The whole-tile fold over a FoldTable with outputs shifted onto their
 // 64-byte bursts (shifted_round); tiles go to the XCDs in groups of
 // consecutive ones (xcd_group_tile).
-template <int NIN, class Op, int U, bool NT, bool EDGES = false>
-__global__ __launch_bounds__(kBlock) void fold_table_shift_kernel(FoldTable a) {
+template <int NIN, class Op, int U, bool NT, bool EDGES>
+__device__ __forceinline__ void table_shift_round(const FoldTable& a) {
     constexpr int T = kBlock * kVec * U;
     const int c = blockIdx.y;
     int64_t x = blockIdx.x;
@@ -484,8 +499,19 @@ __global__ __launch_bounds__(kBlock) void fold_table_shift_kernel(FoldTable a) {
     const uint32_t* in[NIN];
 #pragma unroll
     for (int k = 0; k < NIN; ++k) in[k] = static_cast<const uint32_t*>(a.in[c][k]) + e0;
-    const Outs<NIN> out = outs_of<NIN>(a.out, (int64_t)c * a.out_stride + a.out_off[c] + e0);
+    const int64_t ooff = EDGES ? a.out_off[c] : 0;
+    const Outs<NIN> out = outs_of<NIN>(a.out, (int64_t)c * a.out_stride + ooff + e0);
     shifted_round<NIN, NIN, Op, U, NT>(in, out, a.mask[c], xt == 0, xt == nx - 1, a.mean != 0);
+}
+
+template <int NIN, class Op, int U, bool NT>
+__global__ __launch_bounds__(kBlock) void fold_table_shift_kernel(FoldTable a) {
+    table_shift_round<NIN, Op, U, NT, false>(a);
+}
+
+template <int NIN, class Op, int U, bool NT>
+__global__ __launch_bounds__(kBlock) void fold_table_shift_edges_kernel(FoldTable a) {
+    table_shift_round<NIN, Op, U, NT, true>(a);
 }
 
 template <int NR, int U, bool NT>
