@@ -882,7 +882,7 @@ PROFILE_SETS = {
                 "all_reduce_many Mean, then the parameter-keyed sync fused with gradient accumulation",
         # steady: the launches of the last two calls (225 own launches per call of the list)
         "kernels": {"fold_table_kernel<4, OpSumF32, 1, true>": {"per_wg": (4 + 4) * 1024, "steady": 450},
-                    "fold_full_kernel<4, OpSumF32, 1, true, true>": {"per_wg": (8 + 4) * 1024, "steady": 450},
+                    "fold_table_acc_kernel<4, OpSumF32, 1, true>": {"per_wg": (8 + 4) * 1024, "steady": 450},
                     "batch_kernel<4, OpSumF32, 2, true, false>": {"per_call": 64 * 4096 * 4 * 8, "steady": 2},
                     "batch_kernel<4, OpSumF32, 1, true, true>": {"per_call": 64 * 4096 * 4 * 12, "steady": 2}},
     },

@@ -34,32 +34,19 @@ void* g_scratch_ptr[kMaxDevices] = {};
 
 // ---------------------------------------------------------------- launches
 
-// The FoldTable of a whole-tile fold without accumulators: job c's operands
-// in ring order at its first element, its output mask.
-FoldTable fold_table_of(const LaunchPlan& p) {
-    const JobArgs& a = p.args;
-    FoldTable t{};
-    for (int c = 0; c < a.jobs; ++c) {
-        // the interior of a split fold starts job_off[c] elements into the job
-        const int64_t off = (int64_t)c * a.in_stride + p.job_off[c];
-        for (int k = 0; k < p.nin; ++k)
-            t.in[c][k] = static_cast<const uint32_t*>(a.in[fold_rank(c, k, p.nin)]) + off;
-        t.mask[c] = out_mask_of(a.out_mode, a.out_mask, c);
-        t.out_off[c] = p.job_off[c];
-        t.len[c] = job_len(a.n, a.seg, c);
-        t.phase[c] = a.phase[c];
-    }
-    t.edges = p.split ? p.edges : 0;
-    t.interior = (int32_t)(p.split ? p.interior : p.grid);
-    for (int r = 0; r < a.nranks; ++r) t.out[r] = a.out[r];
-    t.out_stride = a.out_stride;
-    t.mean = a.mean;
-    return t;
-}
-
 hipError_t launch_jobs(const LaunchPlan& p, hipStream_t stream) {
     const bool nt = p.args.nontemporal != 0;
     const bool full = p.args.full_tiles != 0;
+    if (full && p.args.in_mode == kInFold && p.acc && p.nin <= kAccSlot) {
+        FoldTableFn tf;
+        if (p.dtype == RC_F32)
+            tf = nt ? fold_table_acc_fn_f32_nt(p.op, p.nin) : fold_table_acc_fn_f32_cached(p.op, p.nin);
+        else
+            tf = nt ? fold_table_acc_fn_i32_nt(p.op, p.nin) : fold_table_acc_fn_i32_cached(p.op, p.nin);
+        if (!tf || p.split || p.shift_out || p.unroll != unroll_for(2 * p.nin)) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(tf, dim3(p.grid, p.grid_y), dim3(kBlock), p.lds_bytes, stream, fold_table_of(p));
+        return hipGetLastError();
+    }
     if ((full || p.split) && p.args.in_mode == kInFold && !p.acc) {
         const bool u1 = p.nin >= 4 && p.nin < 8 && p.unroll == 1;
         const bool sh = p.shift_out;

@@ -17,13 +17,15 @@ constexpr bool kNt = RC_KNT != 0;
 using SumOp = std::conditional_t<RC_KDT == RC_F32, OpSumF32, OpSumI32>;
 using MaxOp = std::conditional_t<RC_KDT == RC_F32, OpMaxF32, OpMaxI32>;
 
-// General folds (JobArgs), and whole-tile folds with accumulators; unroll kUnroll.
+// General folds (JobArgs), and whole-tile folds with accumulators of more
+// than kAccSlot ranks; unroll kUnroll.
 template <class Op, bool ACC, bool FULL>
 struct FoldOf {
     template <int NIN>
     struct At {
         static FoldFn get() {
-            if constexpr (FULL) return fold_full_kernel<NIN, Op, kUnroll<NIN, ACC>, kNt, ACC>;
+            if constexpr (FULL && NIN <= kAccSlot) return nullptr;  // fold_table_acc_kernel
+            else if constexpr (FULL) return fold_full_kernel<NIN, Op, kUnroll<NIN, ACC>, kNt, ACC>;
             else return fold_kernel<NIN, Op, kUnroll<NIN, ACC>, kNt, ACC>;
         }
     };
@@ -32,7 +34,8 @@ struct FoldOf {
 template <bool FULL>
 FoldFn pick(int op, bool acc, int nin) {
     if constexpr (FULL) {
-        // whole-tile folds without accumulators run fold_table_kernel
+        // whole-tile folds without accumulators run fold_table_kernel, and
+        // those with accumulators of up to kAccSlot ranks fold_table_acc_kernel
         if (!acc || op == RC_MAX) return nullptr;
         return pick_nin<FoldOf<SumOp, true, true>::template At, FoldFn>(nin);
     } else {
@@ -73,6 +76,20 @@ FoldTableFn pick_table(int op, bool u1, bool shift, bool edges, int nin) {
     return shift ? pick_table_op<SumOp, true>(u1, edges, nin) : pick_table_op<SumOp, false>(u1, edges, nin);
 }
 
+// Whole-tile folds with accumulators of up to kAccSlot ranks (Sum; Mean is
+// Sum with the table's mean flag).
+template <int NIN>
+struct AccTableAt {
+    static FoldTableFn get() {
+        if constexpr (NIN <= kAccSlot) return fold_table_acc_kernel<NIN, SumOp, kUnroll<NIN, true>, kNt>;
+        else return nullptr;
+    }
+};
+
+FoldTableFn pick_acc_table(int op, int nin) {
+    return op == RC_MAX ? nullptr : pick_nin<AccTableAt, FoldTableFn>(nin);
+}
+
 FoldFn pick_any(int op, bool acc, bool full, bool u1, int nin) {
     (void)u1;
     return full ? pick<true>(op, acc, nin) : pick<false>(op, acc, nin);
@@ -85,21 +102,25 @@ FoldFn fold_fn_f32_nt(int op, bool acc, bool full, bool u1, int nin) { return pi
 FoldTableFn fold_table_fn_f32_nt(int op, bool u1, bool shift, bool edges, int nin) {
     return pick_table(op, u1, shift, edges, nin);
 }
+FoldTableFn fold_table_acc_fn_f32_nt(int op, int nin) { return pick_acc_table(op, nin); }
 #elif RC_KDT == RC_F32
 FoldFn fold_fn_f32_cached(int op, bool acc, bool full, bool u1, int nin) { return pick_any(op, acc, full, u1, nin); }
 FoldTableFn fold_table_fn_f32_cached(int op, bool u1, bool shift, bool edges, int nin) {
     return pick_table(op, u1, shift, edges, nin);
 }
+FoldTableFn fold_table_acc_fn_f32_cached(int op, int nin) { return pick_acc_table(op, nin); }
 #elif RC_KNT
 FoldFn fold_fn_i32_nt(int op, bool acc, bool full, bool u1, int nin) { return pick_any(op, acc, full, u1, nin); }
 FoldTableFn fold_table_fn_i32_nt(int op, bool u1, bool shift, bool edges, int nin) {
     return pick_table(op, u1, shift, edges, nin);
 }
+FoldTableFn fold_table_acc_fn_i32_nt(int op, int nin) { return pick_acc_table(op, nin); }
 #else
 FoldFn fold_fn_i32_cached(int op, bool acc, bool full, bool u1, int nin) { return pick_any(op, acc, full, u1, nin); }
 FoldTableFn fold_table_fn_i32_cached(int op, bool u1, bool shift, bool edges, int nin) {
     return pick_table(op, u1, shift, edges, nin);
 }
+FoldTableFn fold_table_acc_fn_i32_cached(int op, int nin) { return pick_acc_table(op, nin); }
 #endif
 
 }  // namespace rc

@@ -351,9 +351,11 @@ __device__ __forceinline__ void table_edge_tile(const FoldTable& a, int c, int x
 // fold): the first a.edges workgroups of each job do its edge tiles
 // (table_edge_tile), dispatched first so that their latency overlaps the
 // interior's, and the rest the interior, whose outputs start out_off[c]
-// elements into the job.
-template <int NIN, class Op, int U, bool NT, bool EDGES>
+// elements into the job.  ACC: operand k is in[c][kAccSlot + k] (its
+// accumulator) plus in[c][k].
+template <int NIN, class Op, int U, bool NT, bool EDGES, bool ACC = false>
 __device__ __forceinline__ void table_round(const FoldTable& a) {
+    static_assert(!ACC || (NIN <= kAccSlot && !EDGES), "accumulators: up to kAccSlot ranks, whole tiles");
     const int c = blockIdx.y;
     int64_t x = blockIdx.x;
     if constexpr (EDGES) {
@@ -365,21 +367,28 @@ __device__ __forceinline__ void table_round(const FoldTable& a) {
     }
     const int64_t e0 = x * (kBlock * kVec * U);
     const uint32_t* in[NIN];
-    const uint32_t* none[NIN];
+    const uint32_t* ac[NIN];
 #pragma unroll
     for (int k = 0; k < NIN; ++k) {
         in[k] = static_cast<const uint32_t*>(a.in[c][k]) + e0;
-        none[k] = nullptr;
+        ac[k] = ACC ? static_cast<const uint32_t*>(a.in[c][kAccSlot + k]) + e0 : nullptr;
     }
     // only a split fold's interior starts off the job's first element
     const int64_t ooff = EDGES ? a.out_off[c] : 0;
     const Outs<NIN> out = outs_of<NIN>(a.out, (int64_t)c * a.out_stride + ooff + e0);
-    vec_round<NIN, NIN, Op, U, NT, false, true>(in, none, 0, 0, out, a.mask[c], a.mean != 0);
+    vec_round<NIN, NIN, Op, U, NT, ACC, true>(in, ac, 0, 0, out, a.mask[c], a.mean != 0);
 }
 
 template <int NIN, class Op, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void fold_table_kernel(FoldTable a) {
     table_round<NIN, Op, U, NT, false>(a);
+}
+
+// Whole-tile folds with accumulators of up to kAccSlot ranks (a gradient
+// sync that adds the last microbatch's gradients into the accumulators).
+template <int NIN, class Op, int U, bool NT>
+__global__ __launch_bounds__(kBlock) void fold_table_acc_kernel(FoldTable a) {
+    table_round<NIN, Op, U, NT, false, true>(a);
 }
 
 // The edge form: a split fold (the first a.edges workgroups of each job do

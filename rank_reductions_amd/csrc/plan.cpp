@@ -289,6 +289,30 @@ bool split_fold(LaunchPlan* lp, const Config& cfg, const DeviceInfo& dev, int64_
     return true;
 }
 
+FoldTable fold_table_of(const LaunchPlan& p) {
+    const JobArgs& a = p.args;
+    FoldTable t{};
+    for (int c = 0; c < a.jobs; ++c) {
+        // the interior of a split fold starts job_off[c] elements into the job
+        const int64_t off = (int64_t)c * a.in_stride + p.job_off[c];
+        for (int k = 0; k < p.nin; ++k) {
+            const int r = fold_rank(c, k, p.nin);
+            t.in[c][k] = static_cast<const uint32_t*>(a.in[r]) + off;
+            if (p.acc && k < kAccSlot) t.in[c][kAccSlot + k] = static_cast<const uint32_t*>(a.acc[r]) + off;
+        }
+        t.mask[c] = out_mask_of(a.out_mode, a.out_mask, c);
+        t.out_off[c] = p.job_off[c];
+        t.len[c] = job_len(a.n, a.seg, c);
+        t.phase[c] = a.phase[c];
+    }
+    t.edges = p.split ? p.edges : 0;
+    t.interior = (int32_t)(p.split ? p.interior : p.grid);
+    for (int r = 0; r < a.nranks; ++r) t.out[r] = a.out[r];
+    t.out_stride = a.out_stride;
+    t.mean = a.mean;
+    return t;
+}
+
 std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceInfo& dev) {
     std::vector<LaunchPlan> out;
     if (ck.count == 0) return out;
@@ -501,6 +525,10 @@ std::vector<LaunchPlan> plan(const Checked& ck, const Config& cfg, const DeviceI
         const InFlightRule& rule = !full ? kFoldRule : (ja.in_mode == kInCopy ? kCopyBatchRule : kFullFoldRule);
         shape_launch(lp.total_tiles, loads, lp.nout, lp.unroll, cfg, dev, &lp.grid, &lp.lds_bytes, rule);
         lp.waves = cfg.waves_per_cu > 0 ? cfg.waves_per_cu : auto_waves_per_cu(loads, lp.nout, lp.unroll, rule);
+        if (full && lp.acc && lp.nin <= kAccSlot && cfg.waves_per_cu <= 0 && lp.waves > kAccTableMaxWaves) {
+            lp.waves = kAccTableMaxWaves;
+            lp.lds_bytes = lds_for_waves(dev, lp.waves);
+        }
         // A whole-tile all-reduce of 4-7 ranks runs one vector per lane:
         // 4 x 64 MiB 82.1-82.2 us at W=7 against 83.3-83.6 at the best W with
         // two (three boxes); 5, 6 and 7 ranks of 2^21 elements per segment

@@ -247,6 +247,12 @@ struct InFlightRule {
 constexpr InFlightRule kFoldRule{110.0, 0.65};     // general fold and copy kernels
 constexpr InFlightRule kCopyBatchRule{60.0, 0.5};  // batched copies; whole-tile copies
 constexpr InFlightRule kFullFoldRule{85.0, 0.52};  // whole-tile folds
+// Whole-tile folds with accumulators (fold_table_acc_kernel) run at most this
+// many waves per CU.  Sweeps of W = 4..10, in place and not, two runs each:
+// 2 and 4 ranks (8 KiB of loads per wave either way) peak at 6 (4 x 64 MiB
+// 122.3-123.1 us against 126.7-128.0 at the rule's 8, 128-130 at 4 and 5),
+// 8 ranks at 4-5, where the rule already lands.
+constexpr int kAccTableMaxWaves = 6;
 int auto_waves_per_cu(int nin, int nout, int unroll, const InFlightRule& rule = kFoldRule);
 // Grid and LDS reservation of a launch of `total_tiles` tiles.
 void shape_launch(int64_t total_tiles, int nin, int nout, int unroll, const Config& cfg,
@@ -275,9 +281,10 @@ constexpr int kTuneSamples = 5;
 constexpr double kTuneMargin = 0.03;
 constexpr int64_t kTuneMinBytes = int64_t(256) << 20;
 // Fold launches that move this much or more split off their aligned
-// interior onto the whole-tile kernels (split_fold): the second launch costs
-// a few microseconds, a few percent of a launch this size.
-constexpr int64_t kSplitMinBytes = int64_t(256) << 20;
+// interior onto the whole-tile kernels (split_fold).  Ragged 4- and 8-rank
+// all-reduces of 64 and 128 MiB ran 1-8% faster split, same box; at 32 MiB,
+// latency-bound (about 10 us a call), the two forms were within noise.
+constexpr int64_t kSplitMinBytes = int64_t(64) << 20;
 struct TunePending {
     int ticket;     // device timer
     int cand;       // candidate index
@@ -326,13 +333,16 @@ struct CopyArgs {
     uint8_t phase[kMaxCopyArgJobs];
 };
 
-// Argument block of a whole-tile fold without accumulators (the all-reduce,
-// reduce and reduce_scatter of whole, aligned tiles: every large workload's
-// launch).  Job c's fold operands are listed in ring order and already
-// offset to its first element, so a workgroup fetches its R input pointers,
-// the output bases and its job's output mask in one round of scalar loads,
-// with no index or stride arithmetic before its HBM loads; the JobArgs form
-// measured 3% slower on the 8-rank all-reduce.
+// Argument block of a whole-tile fold (the all-reduce, reduce and
+// reduce_scatter of whole, aligned tiles: every large workload's launch; a
+// gradient sync's fold with accumulators of up to kAccSlot ranks).  Job c's
+// fold operands are listed in ring order and already offset to its first
+// element, so a workgroup fetches its R input pointers, the output bases and
+// its job's output mask in one round of scalar loads, with no index or
+// stride arithmetic before its HBM loads; the JobArgs form measured 3%
+// slower on the 8-rank all-reduce.  With accumulators, operand k's
+// accumulator sits in slot kAccSlot + k of the job's row.
+constexpr int kAccSlot = kMaxRanks / 2;
 struct FoldTable {
     const void* in[kMaxRanks][kMaxRanks];  // [job][k]: operand k at the first element the launch folds
     void* out[kMaxRanks];                  // output bases; job c's outputs start c*out_stride elements in
@@ -350,6 +360,12 @@ struct FoldTable {
     int32_t edges;
     int32_t interior;
 };
+
+// The FoldTable of a whole-tile fold (full_tiles or split, kInFold; with
+// accumulators only for nin <= kAccSlot and full_tiles): job c's operands in
+// ring order from the element its launch starts at (job_off[c] for a split),
+// its output mask and, for a split, its length, phase and edge tiles.
+FoldTable fold_table_of(const LaunchPlan& p);
 
 // A piece of a descriptor table written into device memory by a kernel (the
 // allocation-free batched all-reduce's way of placing its tables).
@@ -384,6 +400,12 @@ FoldTableFn fold_table_fn_f32_nt(int op, bool u1, bool shift, bool edges, int ni
 FoldTableFn fold_table_fn_f32_cached(int op, bool u1, bool shift, bool edges, int nin);
 FoldTableFn fold_table_fn_i32_nt(int op, bool u1, bool shift, bool edges, int nin);
 FoldTableFn fold_table_fn_i32_cached(int op, bool u1, bool shift, bool edges, int nin);
+// Whole-tile folds with accumulators of nin <= kAccSlot ranks, over a
+// FoldTable (same files; Sum and Mean, unroll unroll_for(2 * nin)).
+FoldTableFn fold_table_acc_fn_f32_nt(int op, int nin);
+FoldTableFn fold_table_acc_fn_f32_cached(int op, int nin);
+FoldTableFn fold_table_acc_fn_i32_nt(int op, int nin);
+FoldTableFn fold_table_acc_fn_i32_cached(int op, int nin);
 // Batched folds (kernels_batch.hip, once per cache hint).
 BatchFn batch_fn_nt(int dtype, int op, bool acc, int nin);
 BatchFn batch_fn_cached(int dtype, int op, bool acc, int nin);

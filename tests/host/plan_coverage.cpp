@@ -140,6 +140,9 @@ bool phase_fits_heaviest(const std::vector<uintptr_t>& ins, const std::vector<ui
     return w.empty();
 }
 
+int g_table_plans = 0;      // plans whose launch carries a FoldTable
+int g_acc_table_plans = 0;  // ... with accumulators
+
 void check_plan(const LaunchPlan& p, const std::string& name) {
     const JobArgs& a = p.args;
     if (a.tile_elems % (kBlock * kVec * p.unroll)) fail(name + ": tile not a multiple of a round");
@@ -203,6 +206,33 @@ void check_plan(const LaunchPlan& p, const std::string& name) {
     }
     for (int c = a.jobs; c <= kMaxRanks; ++c)
         if (a.tile_prefix[c] != total) fail(name + ": prefix past the last job is not the total");
+    // the FoldTable of a whole-tile or split fold (built by the launch layer's
+    // own host code): every job's operands, and accumulators, at the ranks of
+    // the ring order from the element the launch starts at; its mask, length,
+    // phase and edge tiles.  The replay below takes its addresses from the
+    // JobArgs, so the two must agree.
+    if (a.in_mode == kInFold && a.grid_2d && (a.full_tiles || p.split) && (!p.acc || p.nin <= kAccSlot)) {
+        const FoldTable t = fold_table_of(p);
+        for (int c = 0; c < a.jobs; ++c) {
+            const uintptr_t off = (uintptr_t)((c * a.in_stride + p.job_off[c]) * 4);
+            for (int k = 0; k < p.nin; ++k) {
+                if ((uintptr_t)t.in[c][k] != (uintptr_t)a.in[(c + 1 + k) % p.nin] + off)
+                    fail(name + ": table operand " + std::to_string(k) + " of job " + std::to_string(c));
+                if (p.acc && (uintptr_t)t.in[c][kAccSlot + k] != (uintptr_t)a.acc[(c + 1 + k) % p.nin] + off)
+                    fail(name + ": table accumulator " + std::to_string(k) + " of job " + std::to_string(c));
+            }
+            if (t.mask[c] != out_mask_of(a.out_mode, a.out_mask, c) || t.out_off[c] != p.job_off[c] ||
+                t.len[c] != job_len(a.n, a.seg, c) || t.phase[c] != a.phase[c])
+                fail(name + ": table row of job " + std::to_string(c));
+        }
+        for (int r = 0; r < a.nranks; ++r)
+            if (t.out[r] != a.out[r]) fail(name + ": table output base");
+        if (t.out_stride != a.out_stride || t.mean != a.mean || t.edges != (p.split ? p.edges : 0) ||
+            t.interior != (p.split ? p.interior : p.grid))
+            fail(name + ": table launch fields");
+        ++g_table_plans;
+        if (p.acc) ++g_acc_table_plans;
+    }
     // the tiles the launch visits: (job, tile, whole) with whole tiles from
     // job_off[c] (the whole-tile kernels, a split fold's interior) or the
     // general kernel's tile of the job
@@ -491,6 +521,39 @@ int main(int argc, char** argv) {
                 fail("whole-tile all-reduce of 4-7 ranks does not run one vector per lane");
         }
         }
+    }
+    {
+        // whole-tile gradient syncs with accumulators, in place into them and
+        // not, direct and ring: up to kAccSlot ranks on the table kernel
+        for (int R = 1; R <= 10; ++R)
+            for (int variant = 0; variant < 4; ++variant) {
+                g_bufs.clear();
+                const int64_t n = (int64_t)R * 4096 * 2;
+                const bool in_place = variant & 1;
+                std::vector<rc_buf> bufs(R);
+                std::vector<const void*> accs(R);
+                for (int r = 0; r < R; ++r) {
+                    accs[r] = (const void*)alloc(n * 4, 0);
+                    void* o = in_place ? (void*)accs[r] : (void*)alloc(n * 4, 0);
+                    bufs[r] = make((void*)alloc(n * 4, 0), o, n);
+                }
+                Checked ck;
+                if (validate(Coll::AllReduce, R, bufs.data(), &ck).code) fail("all-reduce rejected");
+                ck.has_acc = true;
+                for (int r = 0; r < R; ++r) ck.acc[r] = accs[r];
+                Config cfg;
+                cfg.algo = variant & 2 ? RC_ALGO_RING : RC_ALGO_DIRECT;
+                const int before = g_acc_table_plans;
+                for (const LaunchPlan& p : plan(ck, cfg, dev)) {
+                    check_plan(p, "whole-tile sync with accumulators, R=" + std::to_string(R) +
+                                      (in_place ? " in place" : "") + (variant & 2 ? " ring" : ""));
+                    ++plans;
+                    if (p.acc && !p.args.full_tiles) fail("whole-tile sync with accumulators off the whole-tile path");
+                }
+                if ((g_acc_table_plans > before) != (R <= kAccSlot))
+                    fail("sync with accumulators of " + std::to_string(R) + " ranks: table kernel " +
+                         (R <= kAccSlot ? "not taken" : "taken"));
+            }
     }
     // whole-tile folds with outputs off a 64-byte burst (offsets 0..15
     // elements): the shifted kernel, except in place
@@ -810,6 +873,7 @@ int main(int argc, char** argv) {
     if (iters >= 100 && full_plans == 0) fail("no plan took the whole-tile path");
     if (iters >= 100 && shifted_plans == 0) fail("no plan took the shifted whole-tile kernel");
     if (iters >= 100 && split_plans == 0) fail("no fold was split");
+    if (iters >= 100 && g_acc_table_plans == 0) fail("no fold with accumulators took the table kernel");
     if (iters >= 100 && shifted_copy_batches == 0) fail("no copy batch took the shifted whole-tile kernel");
     if (iters >= 100 && full_copy_batches == 0) fail("no copy batch took the whole-tile path");
     // occupancy tuner: candidates are the rule's W and the two below (never
@@ -877,9 +941,9 @@ int main(int argc, char** argv) {
         }
         if (t.chosen != 7) fail("tuner left the rule's value on a tie");
     }
-    std::printf("checked %d plans (%d whole-tile, %d shifted, %d split), %d batches and %d copy batches "
-                "(%d whole-tile, %d shifted): %d failures\n",
-                plans, full_plans, shifted_plans, split_plans, batches, copies, full_copy_batches,
-                shifted_copy_batches, g_fail);
+    std::printf("checked %d plans (%d whole-tile, %d shifted, %d split; %d tables, %d with accumulators), "
+                "%d batches and %d copy batches (%d whole-tile, %d shifted): %d failures\n",
+                plans, full_plans, shifted_plans, split_plans, g_table_plans, g_acc_table_plans, batches, copies,
+                full_copy_batches, shifted_copy_batches, g_fail);
     return g_fail ? 1 : 0;
 }

@@ -621,16 +621,25 @@ def test_shapes_are_flattened(shape):
 # ---------------------------------------------------------------- split folds
 
 @pytest.mark.parametrize("case", ["r8_f32_plus8", "r4_i32_plus12", "reduce_r4_plus20", "rs_r8_shards_plus3",
-                                  "r8_in_place", "r8_outputs_off_bursts", "r8_ring"])
+                                  "r8_in_place", "r8_outputs_off_bursts", "r8_ring", "r8_128MiB_plus8",
+                                  "r4_64MiB_plus4", "r4_under_64MiB"])
 def test_split_folds(case):
-    """Folds of 256 MiB and more whose jobs are not whole tiles (segment
+    """Folds of 64 MiB and more whose jobs are not whole tiles (segment
     lengths off the 256-byte grid, so each job has its own head and lead)
-    run as two launches: the whole tiles of each job's aligned interior on
-    the table kernels (shifted when outputs are off their bursts), then the
-    head, lead and tail on the general kernel.  Bits against the oracle at
-    those sizes, in place too, and through the ring's first phase."""
+    run split, in one launch: per job, the first workgroups do the head,
+    lead and tail on the general path and the rest the whole tiles of its
+    aligned interior on the table kernels (shifted when outputs are off
+    their bursts).  Bits against the oracle at those sizes, at the smallest
+    split size and just below it (the general kernel), in place too, and
+    through the ring's first phase."""
     algo = "ring" if case == "r8_ring" else "direct"
-    if case.startswith("r4_i32"):
+    if case == "r8_128MiB_plus8":
+        R, N, dtype, ops = 8, 2**21 + 8, "f32", ("sum", "mean")
+    elif case == "r4_64MiB_plus4":
+        R, N, dtype, ops = 4, 2**21 + 4, "f32", ("sum", "max")
+    elif case == "r4_under_64MiB":
+        R, N, dtype, ops = 4, 2**21 - 4, "f32", ("sum", "mean")
+    elif case.startswith("r4_i32"):
         R, N, dtype, ops = 4, 2**24 + 12, "i32", ("sum", "max")
     elif case.startswith("reduce"):
         R, N, dtype, ops = 4, 2**24 + 20, "f32", ("sum",)
