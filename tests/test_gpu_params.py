@@ -183,6 +183,41 @@ def test_params_accumulated_whole_tiles(R):
     check(got, want, f"accumulated whole tiles R={R}")
 
 
+# elements per ring segment: whole tiles of every unroll, 64 MiB and more moved
+ACC_TABLE_SEG = {1: 2**23, 2: 2**21, 3: 2**20, 4: 2**19, 5: 2**18, 6: 2**18, 7: 2**17, 8: 2**17, 9: 2**17}
+
+
+@pytest.mark.parametrize("R", list(range(1, 10)))
+@pytest.mark.parametrize("case", ["f32_mean_in_place", "i32_sum"])
+def test_params_accumulated_table_kernels(R, case):
+    """Whole-tile folds with accumulators on their pointer-table kernel (up
+    to 8 ranks: each operand's accumulator in the table row's upper half) and
+    past it (9 ranks), for every rank count and so every unroll: float32 Mean
+    written in place into the accumulators, int32 Sum into new outputs, next
+    to a parameter that is not whole tiles."""
+    if case == "i32_sum" and R not in (1, 4, 7, 9):
+        pytest.skip("int32 at a few rank counts")
+    seg = ACC_TABLE_SEG[R]
+    specs = {21: (R * seg,), 22: (R * seg + 3,)}
+    dtype = "i32" if case == "i32_sum" else "f32"
+    op = "sum" if case == "i32_sum" else "mean"
+    seed = 140 + R
+    maps = [{k: si.torch_tensor_for(seed, k, R, r, specs[k], dtype=dtype, device=DEV) for k in specs}
+            for r in range(R)]
+    accs = [{k: si.torch_tensor_for(seed + 50, k, R, r, specs[k], dtype=dtype, device=DEV) for k in specs}
+            for r in range(R)]
+    torch.cuda.synchronize()
+    want = oracle.all_reduce_params(host_maps(maps), op, acc=host_maps(accs))
+    with session(R, device=0):
+        if case == "f32_mean_in_place":
+            rr.all_reduce_params(maps, op, out=accs, acc=accs)
+            got = accs
+        else:
+            got = rr.all_reduce_params(maps, op, acc=accs)
+        torch.cuda.synchronize()
+    check(got, want, f"accumulated table kernels R={R} {case}")
+
+
 @pytest.mark.parametrize("algo", ["direct", "ring"])
 def test_params_accumulated_own_launch_in_place(algo):
     """A parameter large enough for its own fold launch (direct, or the ring's
