@@ -300,7 +300,7 @@ def main():
     if not args.no_rows:
         scratch = torch.empty(128 << 20, dtype=torch.float32, device=dev)
         sink = torch.empty(1, dtype=torch.float32, device=dev)
-        cold = cold_samples(torch, lambda: call(p_sum), 30, scratch, sink)
+        cold = cold_samples(torch, lambda: call(p_sum), 50, scratch, sink)
         del scratch, sink
         cold_med, cold_best = cold[len(cold) // 2], cold[0]
         log(f"bench: one call at a time, cache flushed: median {cold_med * 1e3:.1f} us, "
