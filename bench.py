@@ -805,15 +805,15 @@ def cpu_baseline(torch, xs, out_sum, seconds):
     edges = [S * i // T for i in range(T + 1)]
     full = np.empty(N, dtype=np.float32)
 
-    def block(i):
+    def block(i, src=hx, dst=full):
         lo, hi = edges[i], edges[i + 1]
         if lo == hi:
             return
-        sub = [np.concatenate([h[c * S + lo:c * S + hi] for c in range(R)]) for h in hx]
+        sub = [np.concatenate([h[c * S + lo:c * S + hi] for c in range(R)]) for h in src]
         got = oracle.all_reduce(sub, "sum")[0]
         wdt = hi - lo
         for c in range(R):
-            full[c * S + lo:c * S + hi] = got[c * wdt:(c + 1) * wdt]
+            dst[c * S + lo:c * S + hi] = got[c * wdt:(c + 1) * wdt]
 
     pcalls = 0
     with ThreadPoolExecutor(T) as ex:
@@ -826,6 +826,40 @@ def cpu_baseline(torch, xs, out_sum, seconds):
                 break
     all_match = bool(np.array_equal(full.view(np.uint32), gpu))
     allc = pcalls * N * 4 / pel / 1e9
+
+    # Context only: an all-reduce staged through the host, as the pages' own
+    # transfer path is (ruCCL README, section 5), with the all-cores oracle
+    # as its compute: the R inputs copied to pinned host memory, folded, and
+    # the result copied to every rank's output.
+    log("bench: timing a host-staged all-reduce (context)")
+    pin_in = [torch.empty(N, dtype=torch.float32, pin_memory=True) for _ in range(R)]
+    pin_out = torch.empty(N, dtype=torch.float32, pin_memory=True)
+    dev_out = [torch.empty_like(x) for x in xs]
+    src, dst = [p.numpy() for p in pin_in], pin_out.numpy()
+    phases = []
+    with ThreadPoolExecutor(T) as ex:
+        for _ in range(3):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for p, x in zip(pin_in, xs):
+                p.copy_(x)
+            t1 = time.perf_counter()
+            list(ex.map(lambda i: block(i, src, dst), range(T)))
+            t2 = time.perf_counter()
+            for o in dev_out:
+                o.copy_(pin_out, non_blocking=True)
+            torch.cuda.synchronize()
+            phases.append((t1 - t0, t2 - t1, time.perf_counter() - t2))
+    staged_match = bool(np.array_equal(dev_out[R - 1].cpu().numpy().view(np.uint32), gpu))
+    best = min(phases, key=sum)
+    del pin_in, pin_out, dev_out, src, dst
+    host_staged = {
+        "value": round(N * 4 / sum(best) / 1e9, 4), "unit": "GB/s",
+        "what": "context, not a baseline of this path: device-to-host copies of the R inputs into pinned "
+                "memory, the oracle on all cores, host-to-device copies of the result to every rank; "
+                "best of 3 calls",
+        "d2h_ms": round(best[0] * 1e3, 2), "oracle_ms": round(best[1] * 1e3, 2),
+        "h2d_ms": round(best[2] * 1e3, 2), "matches_gpu_bits": staged_match}
     return {
         "value": round(allc, 4),
         "unit": "GB/s",
@@ -841,6 +875,7 @@ def cpu_baseline(torch, xs, out_sum, seconds):
                      "seconds": round(el, 2), "matches_gpu_bits": one_match},
         "all_cores": {"value": round(allc, 4), "unit": "GB/s", "cores": T, "calls": pcalls,
                       "seconds": round(pel, 2), "matches_gpu_bits": all_match},
+        "host_staged_context": host_staged,
     }
 
 
