@@ -5,6 +5,7 @@ synchronisation in between, so the results are only right if the library
 orders the kernels after every rank's producer and every consumer after the
 kernels.  Bits are compared with the CPU oracle."""
 
+import random
 import threading
 
 import numpy as np
@@ -227,6 +228,140 @@ def test_split_groups_reduce_in_their_own_rank_order():
                     assert_bits(host(got[w][2]), want_mean, f"group {g} reduce at its rank 1")
                 else:
                     assert got[w][2] is None
+    finally:
+        for r in range(R):
+            rr.rank_finish(r)
+
+
+def _plan_sequence(rng, R, count):
+    """`count` collectives of random kinds, sizes, types and roots, the same
+    for every rank (a send/recv pair involves two ranks only)."""
+    kinds = ["all_reduce", "reduce", "broadcast", "reduce_scatter", "all_gather", "all_gather_list",
+             "all_to_all_single", "barrier", "params", "send_recv"]
+    plan = []
+    for _ in range(count):
+        kind = rng.choice(kinds)
+        dtype = rng.choice(["f32", "i32"])
+        op = rng.choice(["sum", "max"] if dtype == "i32" else ["sum", "mean", "max"])
+        n = rng.choice([1, 257, 4099, R * 2048, rng.randint(1, 150_000)])
+        if kind in ("reduce_scatter", "all_to_all_single"):
+            n = max(R, n - n % R)
+        if kind == "params":
+            op = "sum" if dtype == "i32" else rng.choice(["sum", "mean"])
+        pair = rng.sample(range(R), 2)
+        plan.append({"kind": kind, "dtype": dtype, "op": op, "n": n, "root": rng.randrange(R),
+                     "pair": pair, "acc": rng.random() < 0.5})
+    return plan
+
+
+@pytest.mark.parametrize("seed", [1, 2, 4, 5, 6, 9, 21, 24, 25, 30])
+def test_rank_threads_random_sequences(seed):
+    """A seeded sequence of 24 collectives of every kind, issued by R rank
+    threads in the same order, with the ranks spread over 1 to R streams
+    (seeds chosen for 2 to 8 ranks on one stream, on some shared streams and
+    on a stream each).
+    Each rank produces its input on its stream right before each call,
+    consumes the output right after, and then overwrites its input: every
+    consumed output equals the oracle's, so every call ran after every
+    rank's producer and before every rank's later work."""
+    rng = random.Random(7_000 + seed)
+    R = rng.choice([2, 3, 4, 5, 8])
+    S = rng.choice(sorted({1, 2, R}))
+    plan = _plan_sequence(rng, R, 24)
+    gen_ = torch.Generator(device=DEV).manual_seed(seed)
+    srcs, accs = [], []
+    for p in plan:
+        if p["dtype"] == "i32":
+            draw = [torch.randint(-2 ** 20, 2 ** 20 + 1, (p["n"],), dtype=torch.int32, device=DEV, generator=gen_)
+                    for _ in range(R)]
+            dacc = [torch.randint(-2 ** 20, 2 ** 20 + 1, (p["n"],), dtype=torch.int32, device=DEV, generator=gen_)
+                    for _ in range(R)]
+        else:
+            draw = [torch.randn(p["n"], device=DEV, generator=gen_) for _ in range(R)]
+            dacc = [torch.randn(p["n"], device=DEV, generator=gen_) for _ in range(R)]
+        srcs.append(draw)
+        accs.append(dacc)
+    torch.cuda.synchronize()
+    hx = [[host(x) for x in xs] for xs in srcs]
+    ha = [[host(a) for a in xs] for xs in accs]
+    pool = [torch.cuda.Stream() for _ in range(S)]
+    for r in range(R):
+        rr.rank_register(r, R)
+
+    def body(r):
+        s = pool[r % S]
+        got = []
+        with torch.cuda.stream(s):
+            for i, p in enumerate(plan):
+                kind, op, n = p["kind"], p["op"], p["n"]
+                x = slow_copy(srcs[i][r]) if p["dtype"] == "f32" else srcs[i][r].clone()  # producer
+                res = None
+                if kind == "all_reduce":
+                    res = rr.rank_all_reduce(r, x, op, stream=s)
+                elif kind == "reduce":
+                    res = rr.rank_reduce(r, x, p["root"], op, stream=s)
+                elif kind == "broadcast":
+                    src = p["root"]
+                    res = rr.rank_broadcast(r, x if r == src else None,
+                                            out=None if r == src else torch.empty_like(x), stream=s)
+                elif kind == "reduce_scatter":
+                    res = rr.rank_reduce_scatter(r, x, R, op, stream=s)
+                elif kind == "all_gather":
+                    res = rr.rank_all_gather(r, x, R, stream=s)
+                elif kind == "all_gather_list":
+                    res = torch.cat(rr.rank_all_gather_list(r, x, R, stream=s))
+                elif kind == "all_to_all_single":
+                    res = rr.rank_all_to_all_single(r, x, stream=s)
+                elif kind == "barrier":
+                    rr.rank_barrier(r, stream=s)
+                elif kind == "params":
+                    acc = {5: accs[i][r].clone()} if p["acc"] else None
+                    res = rr.rank_all_reduce_params(r, {5: x}, op, stream=s, acc=acc)[5]
+                else:
+                    a, b = p["pair"]
+                    if r == a:
+                        rr.rank_send(r, x, b, stream=s)
+                    elif r == b:
+                        res = rr.rank_recv(r, torch.empty_like(x), a, stream=s)
+                got.append(res.clone() if res is not None else None)  # consumer
+                x.mul_(0)  # the rank's next use of its input buffer
+        return got
+
+    try:
+        got = run_ranks(R, body)
+        torch.cuda.synchronize()
+        for i, p in enumerate(plan):
+            kind, op, xs = p["kind"], p["op"], hx[i]
+            what = f"seed {seed} R={R} S={S} call {i}: {kind} {p['dtype']} {op} n={p['n']}"
+            if kind == "all_reduce":
+                want = oracle.all_reduce(xs, op)
+            elif kind == "reduce":
+                want = oracle.reduce(xs, p["root"], op)
+            elif kind == "broadcast":
+                want = oracle.broadcast([x if r == p["root"] else None for r, x in enumerate(xs)])
+                want[p["root"]] = None  # the sender asked for no output
+            elif kind == "reduce_scatter":
+                want = oracle.reduce_scatter(xs, op)
+            elif kind == "all_gather":
+                want = oracle.all_gather(xs)
+            elif kind == "all_gather_list":
+                want = [np.concatenate(w) for w in oracle.all_gather_list(xs)]
+            elif kind == "all_to_all_single":
+                want = oracle.all_to_all_single(xs)
+            elif kind == "barrier":
+                want = [None] * R
+            elif kind == "params":
+                acc = [{5: a} for a in ha[i]] if p["acc"] else None
+                w = oracle.all_reduce_params([{5: x} for x in xs], op, acc=acc)
+                want = [m[5] for m in w]
+            else:
+                a, b = p["pair"]
+                want = [oracle.send_recv(xs[a]) if r == b else None for r in range(R)]
+            for r in range(R):
+                if want[r] is None:
+                    assert got[r][i] is None, f"{what}: rank {r} got an output"
+                else:
+                    assert_bits(host(got[r][i]), want[r], f"{what}: rank {r}")
     finally:
         for r in range(R):
             rr.rank_finish(r)
