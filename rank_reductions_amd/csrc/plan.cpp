@@ -298,7 +298,9 @@ FoldTable fold_table_of(const LaunchPlan& p) {
         for (int k = 0; k < p.nin; ++k) {
             const int r = fold_rank(c, k, p.nin);
             t.in[c][k] = static_cast<const uint32_t*>(a.in[r]) + off;
-            if (p.acc && k < kAccSlot) t.in[c][kAccSlot + k] = static_cast<const uint32_t*>(a.acc[r]) + off;
+            // accumulators only where they fit beside the operands (the
+            // table kernels' case); past kAccSlot ranks the table is unused
+            if (p.acc && p.nin <= kAccSlot) t.in[c][kAccSlot + k] = static_cast<const uint32_t*>(a.acc[r]) + off;
         }
         t.mask[c] = out_mask_of(a.out_mode, a.out_mask, c);
         t.out_off[c] = p.job_off[c];
