@@ -936,12 +936,16 @@ PROFILE_SETS = {
 
 
 def profile_commands(name, dir_):
+    """The three rocprofv3 runs of a profile set, as run from the repository
+    root: rocprofv3 itself starts from /tmp ($OLDPWD is then the root), and
+    writes under dir_ (relative to the root)."""
     base = "cd /tmp && export TMPDIR=/tmp && "
-    run = f"-- python3 $GRAFT_REPO_ROOT/bench.py {PROFILE_SETS[name].get('args', '--profile ' + name)}"
+    run = f"-- python3 $OLDPWD/bench.py {PROFILE_SETS[name].get('args', '--profile ' + name)}"
+    out = f"$OLDPWD/{dir_}"
     return [
-        f"{base}rocprofv3 --kernel-trace --stats --output-format csv -d {dir_}/trace -o run {run}",
-        f"{base}rocprofv3 --pmc FETCH_SIZE --output-format csv -d {dir_}/fetch -o run {run}",
-        f"{base}rocprofv3 --pmc WRITE_SIZE --output-format csv -d {dir_}/write -o run {run}",
+        f"{base}rocprofv3 --kernel-trace --stats --output-format csv -d {out}/trace -o run {run}",
+        f"{base}rocprofv3 --pmc FETCH_SIZE --output-format csv -d {out}/fetch -o run {run}",
+        f"{base}rocprofv3 --pmc WRITE_SIZE --output-format csv -d {out}/write -o run {run}",
     ]
 
 
@@ -1111,11 +1115,12 @@ def summarize_profile(dir_, name):
     scale = {c: (copy_kib / calib[c] if calib[c] else None) for c in calib}
 
     sha = kernels_sha()
-    cmds = profile_commands(name, f"$GRAFT_REPO_ROOT/gpurun_out/prof_{name}")
+    rel = os.path.relpath(dir_, ROOT) if dir_.is_absolute() else str(dir_)
+    cmds = profile_commands(name, rel)
     md = [f"# Kernel time and HBM traffic: {name}", "",
           f"Workload: {spec['what']}.", "",
-          "Commands (MI355X, ROCm 7.2), then `python3 bench.py --summarize-profile "
-          f"gpurun_out/prof_{name} --profile {name}` to write this file:", ""]
+          "Commands (MI355X, ROCm 7.2; each run from the repository root), then `python3 bench.py "
+          f"--summarize-profile {rel} --profile {name}` to write this file:", ""]
     md += [f"    {c}" for c in cmds]
     def steady_of(k):
         return spec["kernels"][k].get("steady", spec.get("steady", 4))
