@@ -89,6 +89,12 @@ MUTATIONS = {
     "accumulate_aliases": ("        return grad.copy()", "        return grad"),
     "accumulate_replaces": ("return combine(_flat(acc), _flat(grad), SUM).reshape(acc.shape)",
                             "return grad.copy()"),
+    "send_recv_aliases": ("    _check_dtype(x)\n    return x.copy()", "    _check_dtype(x)\n    return x"),
+    "reduce_fills_non_roots": ("    out = [None] * R\n    out[root] = result.reshape(shape)",
+                               "    out = [result.reshape(shape)] * R"),
+    "broadcast_accepts_two_senders": ("    if len(senders) != 1:", "    if len(senders) < 1:"),
+    "a2a_accepts_ragged": ('    if n % R:\n        raise OracleError("all_to_all_single input length must be a multiple of R")',
+                           "    if False:\n        pass"),
 }
 
 
